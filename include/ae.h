@@ -1,0 +1,188 @@
+/*
+ * ae.h -- C-ABI of the MI355X (gfx950) flow-matching action-expert library.
+ *
+ * What it computes. A VLM prefix (images, text, robot state) is encoded once
+ * into a per-layer key/value cache; each of N Euler steps then runs only the
+ * action suffix of the expert: action_in_proj plus a sinusoidal time
+ * embedding through time_mlp_in / time_mlp_out, L Gemma-style decoder blocks
+ * (RMSNorm, grouped-query attention of the suffix rows over
+ * [cached prefix KV ; suffix KV] with rotary positions, GeGLU MLP), a final
+ * RMSNorm and action_out_proj giving the velocity v, then x += dt * v.
+ *   - "DM0.5: high-performance embodied VLA and OpenDM guide", section 5.1
+ *     (prefix once, KV cache reused by every step), section 5.2 (suffix
+ *     modules), section 5.3 (flow-matching path and Euler sampling, 10 steps,
+ *     action chunk), section 6.3 (FP8 E4M3 MLP weights with scales),
+ *     section 6.5 (fixed shapes, static buffers, one graph replay).
+ *   - "Realtime-VLA FLASH" article, sections 02-03: speculative verification
+ *     of a draft chunk at several flow times in one batched pass, endpoint
+ *     reconstruction, delta-prefix acceptance, gripper-switch fallback.
+ *
+ * Conventions (the pages leave these open; the library and its tests use them):
+ *   - time runs 0 (noise) -> 1 (action); step k evaluates v at t_k = k/N and
+ *     applies x += (1/N) v; the velocity is never evaluated at t = 1;
+ *   - time embedding phi(t) = [sin(2 pi t / p_i) | cos(2 pi t / p_i)],
+ *     p_i geometric from 4e-3 to 4 over width/2 entries; temb =
+ *     time_out(silu(time_in(phi))) is added to every action_in_proj row;
+ *   - RMSNorm y = x / sqrt(mean(x^2) + eps) * gain; GELU is the tanh form;
+ *   - RoPE rotates pairs (d, d + head_dim/2) by pos * base^(-2d/head_dim), suffix
+ *     row i sits at position prefix_len + i; the cached prefix K is used as given;
+ *   - suffix rows see every prefix key and every suffix key of their own
+ *     sequence (no mask); scale 1/sqrt(head_dim); query head h reads kv head
+ *     h * n_kv_heads / n_q_heads;
+ *   - decoder linears have no bias; action_in/out and time_mlp_in/out do.
+ *
+ * Layouts. Every matrix is row-major [out][in]. bf16 tensors are uint16 bit
+ * patterns; fp8 tensors are OCP E4M3 (e4m3fn) bytes with one fp32 scale per
+ * output row (value = scale[row] * e4m3(code)). Gains and biases are fp32.
+ * Prefix caches are [n_layers][prefix_len][n_kv_heads][head_dim] in kv_dtype.
+ * Action chunks are [batch][horizon][action_dim] fp32.
+ *
+ * Ownership. Device memory belongs to the library. Host buffers belong to the
+ * caller and are only read (or written) during the call. Weights and caches
+ * are copied; the caller may free them after the call returns.
+ *
+ * Errors. Every int-returning call returns AE_OK (0) or a negative AE_ERR_*
+ * code and never throws; ae_last_error() describes the last failure. On error
+ * the outputs are not written. A handle is not re-entrant: calls on one
+ * handle must not overlap. Separate handles are independent.
+ */
+#ifndef AE_H_
+#define AE_H_
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AE_OK 0
+#define AE_ERR_INVALID_ARG (-1)  /* null pointer, bad size, out-of-range slot/batch/steps */
+#define AE_ERR_UNSUPPORTED (-2)  /* shape or dtype combination the kernels do not cover */
+#define AE_ERR_NOT_READY (-3)    /* a prefix slot used before ae_load_prefix_kv */
+#define AE_ERR_OOM (-4)          /* device allocation failed */
+#define AE_ERR_HIP (-5)          /* a HIP runtime call failed (no device, launch error, ...) */
+
+enum ae_dtype { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 };
+
+typedef struct ae_config {
+  int n_layers;     /* L decoder blocks */
+  int width;        /* hidden size w (multiple of 64) */
+  int n_q_heads;    /* query heads */
+  int n_kv_heads;   /* key/value heads (divides n_q_heads) */
+  int head_dim;     /* dh (multiple of 32) */
+  int mlp_dim;      /* GeGLU inner size F (multiple of 32) */
+  int action_dim;   /* A (1..64) */
+  int horizon;      /* H chunk rows (1..256) */
+  int prefix_len;   /* P cached prefix tokens (>= 0) */
+  int max_batch;    /* prefix slots = robots advanced together by ae_denoise (>= 1) */
+  int max_taus;     /* verification times per ae_verify call (0 disables ae_verify) */
+  float rope_base;  /* e.g. 10000 */
+  float rms_eps;    /* e.g. 1e-6 */
+  int weight_dtype; /* AE_F32 | AE_BF16: q/k/v/o, action in/out, time MLP */
+  int mlp_dtype;    /* AE_F32 | AE_BF16 | AE_FP8_E4M3: gate / up / down */
+  int kv_dtype;     /* AE_F32 | AE_BF16: prefix cache */
+  int gripper_dim;  /* action dim holding the +-1 gripper channel, -1 = none */
+} ae_config;
+
+/* One decoder block. wq [n_q*dh][w], wk/wv [n_kv*dh][w], wo [w][n_q*dh],
+ * wg/wu [F][w], wd [w][F]; *_scale are fp32 per output row, fp8 only (NULL otherwise). */
+typedef struct ae_layer_weights {
+  const float* ln1;
+  const void* wq;
+  const void* wk;
+  const void* wv;
+  const void* wo;
+  const float* ln2;
+  const void* wg;
+  const void* wu;
+  const void* wd;
+  const float* wg_scale;
+  const float* wu_scale;
+  const float* wd_scale;
+} ae_layer_weights;
+
+/* time_in_w/time_out_w [w][w], action_in_w [w][A], action_out_w [A][w], all host pointers. */
+typedef struct ae_weights {
+  const void* time_in_w;
+  const float* time_in_b;
+  const void* time_out_w;
+  const float* time_out_b;
+  const void* action_in_w;
+  const float* action_in_b;
+  const ae_layer_weights* layers; /* n_layers entries */
+  const float* final_ln;
+  const void* action_out_w;
+  const float* action_out_b;
+} ae_weights;
+
+typedef struct ae_handle ae_handle;
+
+/* Validate cfg, allocate device memory on the current HIP device, pack and
+ * upload the weights (host pointers; copied). *out receives the handle.
+ * The shape contract is fixed for the handle's lifetime (DM0.5 guide 6.1 and
+ * 6.5: fixed image count, token length and chunk shape). Returns
+ * AE_ERR_INVALID_ARG / AE_ERR_UNSUPPORTED before touching the GPU when cfg is
+ * not covered, AE_ERR_HIP if no device is usable, AE_ERR_OOM on allocation failure. */
+int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
+
+/* Copy one robot's prefix cache into slot (0 <= slot < max_batch). k and v are
+ * host [n_layers][prefix_len][n_kv_heads][head_dim] in kv_dtype, keys already
+ * position-rotated by the prefix encoder (DM0.5 guide 5.1). Synchronous. */
+int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v);
+
+/* Denoise `batch` robots (slots 0..batch-1) from host noise [batch][H][A]
+ * with `steps` uniform Euler steps (DM0.5 guide 5.3); writes the host action
+ * chunks [batch][H][A]. Synchronous. The first call for a new (steps, batch)
+ * builds and captures a graph of the whole step loop (slow, once). */
+int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* actions_out);
+
+/* Same as ae_denoise with device pointers (d_noise, d_actions_out: device
+ * [batch][H][A] fp32), enqueued on `stream` (a hipStream_t; NULL = the
+ * library's own stream). Returns after enqueueing; the caller synchronises. */
+int ae_denoise_async(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out,
+                     void* stream);
+
+/* Speculative verification of a draft chunk against the expert (Realtime-VLA
+ * FLASH, sections 02-03). Host inputs: draft [H][A], noise [H][A] (one draw
+ * shared by every tau), taus [n_tau] in [0, 1). The expert velocity v_j is
+ * evaluated at x_j = (1 - tau_j) noise + tau_j draft for all j in one batched
+ * pass over prefix slot `slot`; endpoints a_j = x_j + (1 - tau_j) v_j;
+ * D[j][i] = ||a_j[i] - draft[i]||_2. *accept_len = longest k with D[j][i] < delta
+ * for all i < k and all j, forced to 0 when *gripper_switch = 1 (the gripper
+ * channel changes sign between consecutive rows). dist_out (nullable) receives
+ * D [n_tau][H]. Synchronous. Requires 1 <= n_tau <= max_taus. */
+int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, const float* taus, int n_tau,
+              float delta, int* accept_len, int* gripper_switch, float* dist_out);
+
+/* Same as ae_verify with device pointers for every array (d_dist_out
+ * nullable), enqueued on `stream` (NULL = the library's stream). */
+int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d_noise, const float* d_taus,
+                    int n_tau, float delta, int* d_accept_len, int* d_gripper_switch, float* d_dist_out,
+                    void* stream);
+
+/* Free every device resource of the handle. NULL is a no-op. */
+void ae_destroy(ae_handle* h);
+
+/* Text of the last error on this handle ("" if none); h == NULL gives the
+ * last ae_create failure of this thread. Valid until the next call. */
+const char* ae_last_error(const ae_handle* h);
+
+/* GPU time in ms of the last synchronous ae_denoise / ae_verify graph replay,
+ * measured with HIP events around the launch on the library's stream. */
+int ae_last_gpu_ms(const ae_handle* h, float* ms);
+
+/* Per-kernel timing. Runs one ae_denoise (mode 0, slots 0..batch-1, `steps`)
+ * or one ae_verify pass (mode 1, slot 0, batch = n_tau) eagerly `iters`
+ * times with HIP events around every kernel launch on the library's stream,
+ * using the inputs of the last call of that mode. Writes up to max_stats
+ * entries {kernel name, launches, total ms} and the number written to *n_stats. */
+typedef struct ae_kernel_stat {
+  char name[48];
+  int launches;
+  float total_ms;
+} ae_kernel_stat;
+int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats,
+                    int max_stats, int* n_stats);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* AE_H_ */

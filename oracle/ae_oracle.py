@@ -1,0 +1,293 @@
+"""CPU oracle for the flow-matching action-expert denoise loop (fp64, numpy).
+
+TEST INFRASTRUCTURE ONLY. Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` may import this module. The product library
+never calls it, and it shares no code with the GPU path: it decodes bf16 and
+FP8 itself, and it computes every step plainly, in float64, with numpy's
+matmul as the only library primitive.
+
+Sources (page title, then section):
+
+* "DM0.5: high-performance embodied VLA and OpenDM guide" (the DM0.5 guide):
+  section 5.1 (prefix encoded once into a KV cache), section 5.2 (action
+  expert modules: action_in_proj, time_mlp_in/out, prefix KV, action_out_proj,
+  built on the Gemma3 text stack), section 5.3 (linear flow path, velocity
+  target, Euler integration, 10 steps, action chunk), section 6.3 (FP8 E4M3
+  with scales).
+* "Realtime-VLA FLASH" article, section 02 (interpolate a draft with noise at
+  several flow times, evaluate the expert's velocity there, rebuild endpoints,
+  compare with the draft) and section 03 (delta-prefix acceptance at all
+  verification times, fall back on length 0; a gripper switch in the candidate
+  chunk forces the full path).
+
+Readings where the pages are silent or garbled (listed with reasons in the
+design notes):
+
+* Time runs from 0 (noise) to 1 (action): x_t = (1 - t) eps + t a, the exact
+  velocity is a - eps, and Euler steps x <- x + (1/N) v(x, k/N), k = 0..N-1.
+  The DM0.5 guide writes the path with noise at t = 1 and prints the update
+  as x_{t-dt} = x_t + v dt; both describe the same integration under
+  t -> 1 - t, v -> -v.
+* Time embedding: [sin | cos] of 2 pi t / p_i with periods geometric from
+  4e-3 to 4, then time_mlp_in -> SiLU -> time_mlp_out, added to every
+  action_in_proj row.
+* Decoder block (Gemma-style, pre-norm): RMSNorm (eps inside the root, gain
+  multiplies), GQA attention of the suffix rows over [prefix KV ; suffix KV]
+  with no mask among the suffix rows, half-split RoPE at positions P + i on
+  the suffix q and k (prefix K is used as cached), scale 1/sqrt(head_dim),
+  GeGLU MLP with the tanh GELU, residual adds. Decoder linears have no bias;
+  action_in/out and time_mlp_in/out have biases.
+* Verification: one noise draw shared by all tau; endpoint a_hat = x + (1 - tau) v;
+  Euclidean distance per chunk row over all action dims; strict < delta.
+"""
+import numpy as np
+
+# ----------------------------------------------------------------------------
+# storage-format decoders (own implementation, from the format definitions)
+# ----------------------------------------------------------------------------
+
+
+def decode_bf16(bits):
+    """bf16 bit patterns (uint16) -> float64: the 16 bits are the top half of an IEEE binary32."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    with np.errstate(invalid="ignore"):  # NaN payloads are kept as NaN
+        return u32.view(np.float32).astype(np.float64)
+
+
+def _e4m3_value(code):
+    """OCP FP8 E4M3 (e4m3fn) code -> value: 1 sign, 4 exponent (bias 7), 3 mantissa bits.
+
+    Exponent 0 is subnormal (m/8 * 2^-6); exponent 15 with mantissa 7 is NaN;
+    there is no infinity, so exponent 15 with mantissa 0..6 is a normal number.
+    """
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return np.nan
+    if e == 0:
+        return s * (m / 8.0) * 2.0 ** -6
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_e4m3(codes):
+    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
+def decode(arr, dtype, scale=None):
+    """Storage array -> float64. fp8 rows are multiplied by their per-row scale."""
+    if dtype == "f32":
+        return np.asarray(arr, dtype=np.float32).astype(np.float64)
+    if dtype == "bf16":
+        return decode_bf16(arr)
+    if dtype == "fp8":
+        return decode_e4m3(arr) * np.asarray(scale, np.float64)[:, None]
+    raise ValueError(dtype)
+
+
+def dequantize_weights(cfg, W):
+    """Decode every tensor of a weight dict (workload storage formats) to float64."""
+    out = {}
+    for name, arr in W.items():
+        if name.endswith(".scale"):
+            continue
+        if arr.dtype == np.float32:
+            out[name] = arr.astype(np.float64)
+        elif name.split(".")[-1] in ("wg", "wu", "wd"):
+            out[name] = decode(arr, cfg.mlp_dtype, W.get(name + ".scale"))
+        else:
+            out[name] = decode(arr, cfg.weight_dtype)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+# ----------------------------------------------------------------------------
+
+
+def silu(x):
+    return x / (1.0 + np.exp(-x))
+
+
+def gelu_tanh(x):
+    """GELU, tanh form: 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))."""
+    return 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+
+
+def rmsnorm(x, gain, eps):
+    """x / sqrt(mean(x^2) + eps) * gain over the last axis."""
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * gain
+
+
+def linear(x, w, b=None):
+    """x @ w^T (+ b); w is [out][in]."""
+    y = x @ w.T
+    return y if b is None else y + b
+
+
+# ----------------------------------------------------------------------------
+# time embedding (DM0.5 guide 5.2: time_mlp_in / time_mlp_out)
+# ----------------------------------------------------------------------------
+
+MIN_PERIOD = 4e-3
+MAX_PERIOD = 4.0
+
+
+def sinusoid(t, width):
+    """phi(t): first half sin(2 pi t / p_i), second half cos(2 pi t / p_i),
+    p_i = MIN_PERIOD * (MAX_PERIOD / MIN_PERIOD) ** (i / (width/2 - 1))."""
+    half = width // 2
+    frac = np.arange(half, dtype=np.float64) / (half - 1)
+    period = MIN_PERIOD * (MAX_PERIOD / MIN_PERIOD) ** frac
+    ang = 2.0 * np.pi * float(t) / period
+    return np.concatenate([np.sin(ang), np.cos(ang)])
+
+
+def time_embedding(Wd, t, width):
+    """temb(t) = W_out silu(W_in phi(t) + b_in) + b_out."""
+    hid = silu(linear(sinusoid(t, width), Wd["time_in_w"], Wd["time_in_b"]))
+    return linear(hid, Wd["time_out_w"], Wd["time_out_b"])
+
+
+# ----------------------------------------------------------------------------
+# rotary position embedding and attention
+# ----------------------------------------------------------------------------
+
+
+def rope(x, positions, base):
+    """Rotate pairs (d, d + dh/2) of the last axis by pos * base^(-2d/dh).
+
+    x: [..., n_pos, n_heads, dh]; positions: [n_pos].
+    """
+    dh = x.shape[-1]
+    half = dh // 2
+    inv_freq = base ** (-2.0 * np.arange(half, dtype=np.float64) / dh)
+    ang = np.asarray(positions, np.float64)[:, None] * inv_freq[None, :]  # [n_pos][half]
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * cos - x2 * sin, x1 * sin + x2 * cos], axis=-1)
+
+
+def attention(q, k, v):
+    """softmax(q k^T / sqrt(dh)) v per query head, GQA head map kv = head * n_kv // n_q.
+
+    q: [n_rows][n_q][dh]; k, v: [n_keys][n_kv][dh] -> [n_rows][n_q][dh].
+    """
+    n_q, dh = q.shape[1], q.shape[2]
+    n_kv = k.shape[1]
+    out = np.empty_like(q)
+    for hq in range(n_q):
+        hk = hq * n_kv // n_q
+        s = q[:, hq, :] @ k[:, hk, :].T / np.sqrt(dh)
+        s = s - s.max(axis=1, keepdims=True)
+        p = np.exp(s)
+        p = p / p.sum(axis=1, keepdims=True)
+        out[:, hq, :] = p @ v[:, hk, :]
+    return out
+
+
+# ----------------------------------------------------------------------------
+# the action expert (velocity field) and its two uses
+# ----------------------------------------------------------------------------
+
+
+def decoder_layer(cfg, Wd, l, h, k_pre, v_pre):
+    """One Gemma-style block over one sequence. h: [H][w]; k_pre, v_pre: [P][n_kv][dh]."""
+    p = f"layers.{l}."
+    H = h.shape[0]
+    nq, nkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    n = rmsnorm(h, Wd[p + "ln1"], cfg.rms_eps)
+    q = linear(n, Wd[p + "wq"]).reshape(H, nq, dh)
+    k = linear(n, Wd[p + "wk"]).reshape(H, nkv, dh)
+    v = linear(n, Wd[p + "wv"]).reshape(H, nkv, dh)
+    pos = cfg.prefix_len + np.arange(H)
+    q = rope(q, pos, cfg.rope_base)
+    k = rope(k, pos, cfg.rope_base)
+    o = attention(q, np.concatenate([k_pre, k], axis=0), np.concatenate([v_pre, v], axis=0))
+    h = h + linear(o.reshape(H, nq * dh), Wd[p + "wo"])
+    n2 = rmsnorm(h, Wd[p + "ln2"], cfg.rms_eps)
+    u = gelu_tanh(linear(n2, Wd[p + "wg"])) * linear(n2, Wd[p + "wu"])
+    return h + linear(u, Wd[p + "wd"])
+
+
+def velocity(cfg, Wd, kv_k, kv_v, x, t):
+    """v_theta(x_t, t | c) for one sequence (DM0.5 guide 5.2).
+
+    x: [H][A] float64, t: scalar flow time, kv_k / kv_v: [L][P][n_kv][dh] float64.
+    """
+    h = linear(x, Wd["action_in_w"], Wd["action_in_b"]) + time_embedding(Wd, t, cfg.width)[None, :]
+    for l in range(cfg.n_layers):
+        h = decoder_layer(cfg, Wd, l, h, kv_k[l], kv_v[l])
+    return linear(rmsnorm(h, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
+
+
+def euler_integrate(x0, steps, vfield):
+    """Integrate dx/dt = vfield(x, t) from t = 0 to t = 1 in ``steps`` uniform Euler steps.
+
+    The field is evaluated at t_k = k / steps, k = 0 .. steps-1 (never at t = 1).
+    """
+    x = np.array(x0, dtype=np.float64)
+    dt = 1.0 / steps
+    for k in range(steps):
+        x = x + dt * vfield(x, k * dt)
+    return x
+
+
+def denoise(cfg, Wd, kv_k, kv_v, noise, steps):
+    """Noise [H][A] -> action chunk [H][A] for one robot with its own prefix cache."""
+    return euler_integrate(noise, steps, lambda x, t: velocity(cfg, Wd, kv_k, kv_v, x, t))
+
+
+def denoise_batch(cfg, Wd, kvs, noise, steps):
+    """Robots are independent: robot r uses cache kvs[r] = (K, V) and noise[r]."""
+    return np.stack([denoise(cfg, Wd, kvs[r][0], kvs[r][1], noise[r], steps) for r in range(noise.shape[0])])
+
+
+def interpolate(draft, noise, taus):
+    """x_j = (1 - tau_j) eps + tau_j d: the draft placed on the linear flow path at each tau_j."""
+    taus = np.asarray(taus, np.float64)[:, None, None]
+    return (1.0 - taus) * np.asarray(noise, np.float64)[None] + taus * np.asarray(draft, np.float64)[None]
+
+
+def gripper_switch(draft, gripper_dim):
+    """1 if the gripper channel changes sign between two consecutive chunk rows, else 0."""
+    if gripper_dim < 0:
+        return 0
+    g = np.asarray(draft, np.float64)[:, gripper_dim]
+    return int(np.any(g[1:] * g[:-1] < 0))
+
+
+def accept_from_velocity(draft, x_tau, v_tau, taus, delta, gripper_dim):
+    """FLASH acceptance given the expert velocity at each verification time.
+
+    a_hat_j = x_j + (1 - tau_j) v_j; D[j, i] = || a_hat_j[i] - d[i] ||_2;
+    accept = longest prefix k with D[j, i] < delta for all i < k and all j,
+    forced to 0 when the draft contains a gripper switch.
+    Returns (accept, switch, D).
+    """
+    taus = np.asarray(taus, np.float64)
+    a_hat = x_tau + (1.0 - taus)[:, None, None] * v_tau
+    D = np.sqrt(np.sum((a_hat - np.asarray(draft, np.float64)[None]) ** 2, axis=-1))
+    ok = np.all(D < delta, axis=0)
+    accept = 0
+    while accept < ok.shape[0] and ok[accept]:
+        accept += 1
+    switch = gripper_switch(draft, gripper_dim)
+    if switch:
+        accept = 0
+    return accept, switch, D
+
+
+def verify(cfg, Wd, kv_k, kv_v, draft, noise, taus, delta):
+    """Speculative verification of one draft chunk against the expert (FLASH section 03)."""
+    x_tau = interpolate(draft, noise, taus)
+    v_tau = np.stack([velocity(cfg, Wd, kv_k, kv_v, x_tau[j], float(taus[j])) for j in range(len(taus))])
+    return accept_from_velocity(draft, x_tau, v_tau, taus, delta, cfg.gripper_dim)
+
+
+def decode_kv(cfg, k, v):
+    return decode(k, cfg.kv_dtype), decode(v, cfg.kv_dtype)

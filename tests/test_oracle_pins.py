@@ -1,0 +1,409 @@
+"""Pins for the CPU oracle: each oracle function checked against something other
+than itself (library routines, closed forms, invariants, brute force on tiny
+inputs), so that a dropped term, a wrong sign or index, or a transposed
+operand fails at least one test."""
+import math
+
+import numpy as np
+import pytest
+import scipy.special as sps
+import torch
+
+from oracle import ae_oracle as O
+from workload import configs as C
+from workload import gen as G
+
+
+# ---------------------------------------------------------------- decoders
+
+def test_bf16_decoder_matches_torch():
+    rng = np.random.default_rng(1)
+    bits = rng.integers(0, 1 << 16, size=20000, dtype=np.uint32).astype(np.uint16)
+    bits = np.concatenate([bits, np.array([0x0000, 0x8000, 0x3f80, 0xbf80, 0x7f7f, 0x0001], np.uint16)])
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = O.decode_bf16(bits)
+    both_nan = np.isnan(ref) & np.isnan(got)
+    assert np.all(both_nan | (ref == got))
+
+
+def test_e4m3_decoder_exhaustive_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    got = O.decode_e4m3(codes)
+    assert np.array_equal(np.isnan(ref), np.isnan(got))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ref[ok], got[ok])
+    # OCP E4M3: largest finite 448, smallest subnormal 2^-9, NaN only at 0x7f / 0xff
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF]) and np.sum(np.isnan(got)) == 2
+
+
+def test_fp8_rows_roundtrip_within_half_ulp():
+    rng = np.random.default_rng(2)
+    w = rng.standard_normal((16, 64)).astype(np.float32) * 0.02
+    codes, scale = G._to_fp8_rows(w)
+    deq = O.decode(codes, "fp8", scale)
+    # every row's max maps to +-448 exactly; relative error of E4M3 RNE is <= 2^-4
+    assert np.allclose(np.abs(deq).max(axis=1), np.abs(w).max(axis=1), rtol=1e-6)
+    big = np.abs(w) > scale[:, None] * 2.0 ** -6 * 8
+    assert np.all(np.abs(deq - w)[big] <= np.abs(w)[big] * 2.0 ** -4 + 1e-12)
+
+
+# ---------------------------------------------------------------- elementwise
+
+def test_gelu_tanh_against_erf_gelu():
+    x = np.linspace(-6, 6, 2001)
+    exact = 0.5 * x * (1.0 + sps.erf(x / math.sqrt(2.0)))
+    assert np.max(np.abs(O.gelu_tanh(x) - exact)) < 5e-4
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    assert abs(O.gelu_tanh(np.array([8.0]))[0] - 8.0) < 1e-9
+    assert abs(O.gelu_tanh(np.array([-8.0]))[0]) < 1e-9
+
+
+def test_silu_against_expit():
+    x = np.linspace(-20, 20, 401)
+    assert np.allclose(O.silu(x), x * sps.expit(x), rtol=1e-12, atol=1e-15)
+
+
+def test_rmsnorm_output_rms_is_gain_and_scale_invariant():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((5, 64)) * 3.0
+    y = O.rmsnorm(x, np.full(64, 2.5), 0.0)
+    assert np.allclose(np.sqrt(np.mean(y * y, axis=-1)), 2.5)
+    assert np.allclose(O.rmsnorm(7.0 * x, 1.0, 0.0), O.rmsnorm(x, 1.0, 0.0))
+    # eps sits inside the root: a zero row stays zero, a tiny row is damped
+    z = O.rmsnorm(np.zeros((1, 8)), 1.0, 1e-6)
+    assert np.all(z == 0)
+
+
+def test_linear_orientation():
+    w = np.array([[1.0, 2.0, 3.0], [0.0, -1.0, 0.0]])  # [out=2][in=3]
+    x = np.array([[1.0, 1.0, 1.0]])
+    assert np.array_equal(O.linear(x, w, np.array([10.0, 20.0])), np.array([[16.0, 19.0]]))
+
+
+# ---------------------------------------------------------------- time embedding
+
+def test_sinusoid_special_values():
+    w = 64
+    half = w // 2
+    phi0 = O.sinusoid(0.0, w)
+    assert np.array_equal(phi0, np.concatenate([np.zeros(half), np.ones(half)]))
+    phi1 = O.sinusoid(1.0, w)
+    # slowest component has period 4: at t = 1 it is a quarter turn
+    assert abs(phi1[half - 1] - 1.0) < 1e-12 and abs(phi1[w - 1]) < 1e-12
+    # fastest component has period 4e-3: t = 1 is 250 full turns, t = 1e-3 a quarter turn
+    assert abs(phi1[0]) < 1e-9 and abs(phi1[half] - 1.0) < 1e-9
+    assert abs(O.sinusoid(1e-3, w)[0] - 1.0) < 1e-12
+    t = 0.37
+    p = O.sinusoid(t, w)
+    assert np.allclose(p[:half] ** 2 + p[half:] ** 2, 1.0)
+    # periods are geometric: log-frequencies equally spaced
+    ang = np.arctan2(O.sinusoid(1e-4, w)[:half], O.sinusoid(1e-4, w)[half:])
+    ratio = ang[:-1] / ang[1:]
+    assert np.allclose(ratio, (4.0 / 4e-3) ** (1.0 / (half - 1)))
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_closed_form_on_basis_vectors():
+    dh, half, base = 16, 8, 10000.0
+    for d in (0, 3, 7):
+        e = np.zeros((1, 1, dh))
+        e[0, 0, d] = 1.0
+        pos = 5
+        r = O.rope(e, np.array([pos]), base)[0, 0]
+        theta = pos * base ** (-2.0 * d / dh)
+        expect = np.zeros(dh)
+        expect[d] = math.cos(theta)
+        expect[d + half] = math.sin(theta)
+        assert np.allclose(r, expect, atol=1e-15)
+
+
+def test_rope_norm_and_relative_position():
+    rng = np.random.default_rng(4)
+    dh = 32
+    q = rng.standard_normal((1, 1, dh))
+    k = rng.standard_normal((1, 1, dh))
+    for m in (0, 3, 50):
+        assert np.isclose(np.linalg.norm(O.rope(q, np.array([m]), 10000.0)), np.linalg.norm(q))
+    def dot(m, n):
+        return float(np.sum(O.rope(q, np.array([m]), 10000.0) * O.rope(k, np.array([n]), 10000.0)))
+    assert np.isclose(dot(10, 3), dot(817, 810))
+    assert np.isclose(dot(0, 0), float(np.sum(q * k)))
+
+
+# ---------------------------------------------------------------- attention
+
+def _attention_bruteforce(q, k, v):
+    """Scalar triple loop: out[r][h][:] = sum_j softmax_j(q.k_j / sqrt(dh)) v_j, kv head = h * n_kv // n_q."""
+    n_rows, n_q, dh = q.shape
+    n_keys, n_kv, _ = k.shape
+    out = np.zeros_like(q)
+    for r in range(n_rows):
+        for h in range(n_q):
+            g = (h * n_kv) // n_q
+            scores = []
+            for j in range(n_keys):
+                s = 0.0
+                for d in range(dh):
+                    s += q[r, h, d] * k[j, g, d]
+                scores.append(s / math.sqrt(dh))
+            mx = max(scores)
+            ws = [math.exp(s - mx) for s in scores]
+            tot = sum(ws)
+            for d in range(dh):
+                out[r, h, d] = sum(ws[j] * v[j, g, d] for j in range(n_keys)) / tot
+    return out
+
+
+def test_attention_bruteforce_gqa():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((3, 4, 8))
+    k = rng.standard_normal((7, 2, 8))
+    v = rng.standard_normal((7, 2, 8))
+    assert np.allclose(O.attention(q, k, v), _attention_bruteforce(q, k, v), atol=1e-12)
+
+
+def test_attention_gqa_equals_mha_with_repeated_kv_and_shift_invariance():
+    rng = np.random.default_rng(6)
+    q = rng.standard_normal((5, 8, 16))
+    k = rng.standard_normal((11, 1, 16))
+    v = rng.standard_normal((11, 1, 16))
+    a = O.attention(q, k, v)
+    assert np.allclose(a, O.attention(q, np.repeat(k, 8, axis=1), np.repeat(v, 8, axis=1)))
+    c = rng.standard_normal(16)
+    assert np.allclose(a, O.attention(q, k + c, v))          # constant key shift: softmax invariant
+    z = O.attention(np.zeros_like(q), k, v)                   # zero query: uniform weights
+    assert np.allclose(z, np.broadcast_to(v.mean(axis=0), z.shape))
+
+
+# ---------------------------------------------------------------- Euler integration
+
+@pytest.mark.parametrize("steps", [1, 2, 4, 10])
+def test_euler_recovers_target_under_exact_linear_field(steps):
+    rng = np.random.default_rng(7)
+    a = rng.standard_normal((8, 8))
+    eps = rng.standard_normal((8, 8))
+    seen = []
+
+    def exact(x, t):
+        assert t < 1.0
+        seen.append(t)
+        return (a - x) / (1.0 - t)
+
+    x = O.euler_integrate(eps, steps, exact)
+    assert np.allclose(x, a, atol=1e-12)
+    assert np.allclose(seen, np.arange(steps) / steps)
+
+
+def test_interpolation_endpoints_and_exact_velocity():
+    rng = np.random.default_rng(8)
+    d = rng.standard_normal((6, 4))
+    e = rng.standard_normal((6, 4))
+    x = O.interpolate(d, e, [0.0, 1.0, 0.25])
+    assert np.allclose(x[0], e) and np.allclose(x[1], d)
+    # on the linear path the exact velocity is d - eps and the endpoint rebuild returns d
+    a_hat = x[2] + (1 - 0.25) * (d - e)
+    assert np.allclose(a_hat, d)
+
+
+# ---------------------------------------------------------------- verification
+
+def _exact_velocity(a, x_tau, taus):
+    return np.stack([(a - x_tau[j]) / (1.0 - taus[j]) for j in range(len(taus))])
+
+
+def test_verify_full_accept_when_draft_is_exact_target():
+    rng = np.random.default_rng(9)
+    H, A = 50, 32
+    a = rng.standard_normal((H, A))
+    a[:, 31] = 1.0
+    eps = rng.standard_normal((H, A))
+    taus = np.array([0.2, 0.4, 0.6, 0.8])
+    x = O.interpolate(a, eps, taus)
+    acc, sw, D = O.accept_from_velocity(a, x, _exact_velocity(a, x, taus), taus, 0.05, 31)
+    assert acc == H and sw == 0 and np.max(D) < 1e-12
+    acc0, _, _ = O.accept_from_velocity(a, x, _exact_velocity(a, x, taus), taus, 0.0, 31)
+    assert acc0 == 0  # strict < delta
+
+
+@pytest.mark.parametrize("k", [0, 1, 17, 49])
+def test_verify_prefix_length_closed_form(k):
+    rng = np.random.default_rng(10 + k)
+    H, A = 50, 32
+    a = rng.standard_normal((H, A))
+    a[:, 31] = -1.0
+    d = a.copy()
+    d[k:, 0] += 0.1 + rng.random(H - k)  # distance >= 0.1 = 2 delta from row k on
+    eps = rng.standard_normal((H, A))
+    taus = np.array([0.2, 0.4, 0.6, 0.8])
+    x = O.interpolate(d, eps, taus)
+    acc, sw, D = O.accept_from_velocity(d, x, _exact_velocity(a, x, taus), taus, 0.05, 31)
+    assert acc == k and sw == 0
+    # the exact field makes every rebuilt endpoint a, so D is tau-independent ||a_i - d_i||
+    assert np.allclose(D, np.linalg.norm(a - d, axis=1)[None, :].repeat(4, axis=0))
+
+
+def test_verify_gripper_switch_forces_zero():
+    rng = np.random.default_rng(11)
+    H, A = 50, 32
+    a = rng.standard_normal((H, A))
+    a[:, 31] = 1.0
+    a[30:, 31] = -1.0
+    eps = rng.standard_normal((H, A))
+    taus = np.array([0.2, 0.4, 0.6, 0.8])
+    x = O.interpolate(a, eps, taus)
+    acc, sw, _ = O.accept_from_velocity(a, x, _exact_velocity(a, x, taus), taus, 0.05, 31)
+    assert sw == 1 and acc == 0
+    assert O.gripper_switch(a, -1) == 0
+
+
+def test_draft_generator_switches_on_odd_seeds_only():
+    cfg = C.PI0_VERIFY
+    for s in range(16):
+        d = G.make_draft(cfg, s)
+        assert set(np.unique(d[:, 31])) <= {-1.0, 1.0}
+        assert O.gripper_switch(d, 31) == (s % 2)
+
+
+# ---------------------------------------------------------------- whole-network composition
+
+def _tiny_cfg(**kw):
+    base = C.TINY.with_(n_layers=2, width=32, n_q_heads=4, n_kv_heads=1, head_dim=8, mlp_dim=64,
+                        action_dim=4, horizon=5, prefix_len=6)
+    return base.with_(**kw)
+
+
+def _tiny_inputs(cfg, seed=0):
+    W = G.make_weights(cfg, seed)
+    Wd = O.dequantize_weights(cfg, W)
+    k, v = G.make_prefix_kv(cfg, 100 + seed)
+    kk, vv = O.decode_kv(cfg, k, v)
+    noise = G.make_noise(cfg, 200 + seed, 1)[0].astype(np.float64)
+    return Wd, kk, vv, noise
+
+
+def test_zero_out_proj_gives_constant_velocity():
+    cfg = _tiny_cfg()
+    Wd, kk, vv, noise = _tiny_inputs(cfg)
+    Wd["action_out_w"][:] = 0.0
+    c = np.array([0.5, -1.0, 2.0, 0.25])
+    Wd["action_out_b"] = c
+    for steps in (1, 3, 10):
+        x = O.denoise(cfg, Wd, kk, vv, noise, steps)
+        assert np.allclose(x, noise + c, atol=1e-12)
+
+
+def test_identity_layers_when_output_projections_are_zero():
+    cfg = _tiny_cfg()
+    Wd, kk, vv, noise = _tiny_inputs(cfg)
+    for l in range(cfg.n_layers):
+        Wd[f"layers.{l}.wo"][:] = 0.0
+        Wd[f"layers.{l}.wd"][:] = 0.0
+    v = O.velocity(cfg, Wd, kk, vv, noise, 0.3)
+    h0 = O.linear(noise, Wd["action_in_w"], Wd["action_in_b"]) + O.time_embedding(Wd, 0.3, cfg.width)
+    expect = O.linear(O.rmsnorm(h0, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
+    assert np.allclose(v, expect)
+    kk2 = np.random.default_rng(1).standard_normal(kk.shape)
+    assert np.allclose(O.velocity(cfg, Wd, kk2, vv, noise, 0.3), expect)
+
+
+def test_attention_uses_prefix_and_suffix_keys_of_its_own_layer():
+    """q = 0 and suffix v = 0 make every head output mean(prefix V) * P / (P + H)."""
+    cfg = _tiny_cfg(n_layers=2)
+    Wd, kk, vv, noise = _tiny_inputs(cfg)
+    for l in range(cfg.n_layers):
+        Wd[f"layers.{l}.wq"][:] = 0.0
+        Wd[f"layers.{l}.wv"][:] = 0.0
+        Wd[f"layers.{l}.wd"][:] = 0.0
+    P, H = cfg.prefix_len, cfg.horizon
+    h = O.linear(noise, Wd["action_in_w"], Wd["action_in_b"]) + O.time_embedding(Wd, 0.6, cfg.width)
+    for l in range(cfg.n_layers):
+        head_out = vv[l, :, 0, :].sum(axis=0) / (P + H)                  # [dh], single kv head
+        o = np.tile(head_out, cfg.n_q_heads)                              # every query head, same kv head
+        h = h + O.linear(o[None, :], Wd[f"layers.{l}.wo"])
+    expect = O.linear(O.rmsnorm(h, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
+    assert np.allclose(O.velocity(cfg, Wd, kk, vv, noise, 0.6), expect)
+
+
+def test_batched_robot_equals_robot_alone_and_verify_rows_equal_velocity():
+    cfg = _tiny_cfg(gripper_dim=3, max_batch=2, batch=2)
+    W = G.make_weights(cfg, 0)
+    Wd = O.dequantize_weights(cfg, W)
+    kvs = [O.decode_kv(cfg, *G.make_prefix_kv(cfg, 100 + r)) for r in range(2)]
+    noise = G.make_noise(cfg, 200, 2).astype(np.float64)
+    xb = O.denoise_batch(cfg, Wd, kvs, noise, 3)
+    assert np.array_equal(xb[1], O.denoise(cfg, Wd, kvs[1][0], kvs[1][1], noise[1], 3))
+    d = noise[0] * 0.1
+    taus = np.array([0.2, 0.6])
+    acc, sw, D = O.verify(cfg, Wd, kvs[0][0], kvs[0][1], d, noise[1], taus, 10.0)
+    x1 = O.interpolate(d, noise[1], taus)[1]
+    a1 = x1 + 0.4 * O.velocity(cfg, Wd, kvs[0][0], kvs[0][1], x1, 0.6)
+    assert np.allclose(D[1], np.linalg.norm(a1 - d, axis=1))
+
+
+def test_rmsnorm_eps_inside_root():
+    c = 1e-4
+    y = O.rmsnorm(np.full((1, 4), c), 1.0, 1e-6)
+    assert np.allclose(y, c / math.sqrt(c * c + 1e-6))
+
+
+def test_time_mlp_composition_order():
+    """time_in -> SiLU -> time_out: with W_in = 0 the hidden layer is silu(b_in) for every t."""
+    w = 8
+    rng = np.random.default_rng(12)
+    Wd = {"time_in_w": np.zeros((w, w)), "time_in_b": rng.standard_normal(w),
+          "time_out_w": rng.standard_normal((w, w)), "time_out_b": rng.standard_normal(w)}
+    expect = Wd["time_out_w"] @ (Wd["time_in_b"] * sps.expit(Wd["time_in_b"])) + Wd["time_out_b"]
+    for t in (0.0, 0.5):
+        assert np.allclose(O.time_embedding(Wd, t, w), expect)
+    # with W_out = I and b = 0 the output is silu(W_in phi(t)): phi(0) = [0.., 1..]
+    Wd = {"time_in_w": np.eye(w), "time_in_b": np.zeros(w), "time_out_w": np.eye(w), "time_out_b": np.zeros(w)}
+    phi = np.concatenate([np.zeros(w // 2), np.ones(w // 2)])
+    assert np.allclose(O.time_embedding(Wd, 0.0, w), phi * sps.expit(phi))
+
+
+def _one_layer_weights(w, dh, nq, F):
+    z = lambda *s: np.zeros(s)
+    return {"layers.0.ln1": np.ones(w), "layers.0.ln2": np.ones(w),
+            "layers.0.wq": z(nq * dh, w), "layers.0.wk": z(dh, w), "layers.0.wv": z(dh, w),
+            "layers.0.wo": z(w, nq * dh), "layers.0.wg": z(F, w), "layers.0.wu": z(F, w), "layers.0.wd": z(w, F)}
+
+
+def test_geglu_gate_is_the_gelu_branch():
+    """h += W_d (gelu(W_g n) * (W_u n)): gate row reads n[0], up row reads n[1]."""
+    cfg = _tiny_cfg(n_layers=1, width=4, n_q_heads=1, head_dim=4, mlp_dim=2, prefix_len=2, horizon=1)
+    Wd = _one_layer_weights(4, 4, 1, 2)
+    Wd["layers.0.wg"][0, 0] = 3.0
+    Wd["layers.0.wu"][0, 1] = 2.0
+    Wd["layers.0.wd"][2, 0] = 1.0
+    h0 = np.array([[1.0, -0.5, 0.25, 2.0]])
+    n2 = h0 / np.sqrt(np.mean(h0 ** 2) + cfg.rms_eps)
+    kp = np.zeros((2, 1, 4))
+    h1 = O.decoder_layer(cfg, Wd, 0, h0, kp, kp)
+    g = 3.0 * n2[0, 0]
+    erf_gelu = 0.5 * g * (1 + sps.erf(g / math.sqrt(2)))
+    assert np.allclose(h1[0, [0, 1, 3]], h0[0, [0, 1, 3]])
+    assert abs(h1[0, 2] - (h0[0, 2] + erf_gelu * 2.0 * n2[0, 1])) < 1e-3
+
+
+@pytest.mark.parametrize("P", [1, 3])
+def test_suffix_rope_position_is_prefix_len_plus_row(P):
+    """One suffix row at position P attends a prefix key (0, kappa): its score is n0 kappa sin(P) / sqrt(2)."""
+    cfg = _tiny_cfg(n_layers=1, width=2, n_q_heads=1, head_dim=2, mlp_dim=2, prefix_len=P, horizon=1, rope_base=10000.0)
+    Wd = _one_layer_weights(2, 2, 1, 2)
+    Wd["layers.0.wq"][0, 0] = 1.0          # q = (n0, 0); suffix k = v = 0
+    Wd["layers.0.wo"][:] = np.eye(2)
+    kappa = 3.0
+    kp = np.zeros((P, 1, 2))
+    kp[:, 0, 1] = kappa
+    vp = np.zeros((P, 1, 2))
+    vp[:, 0, 0], vp[:, 0, 1] = 1.0, 2.0
+    h0 = np.array([[0.8, -0.3]])
+    n0 = (h0 / np.sqrt(np.mean(h0 ** 2) + cfg.rms_eps))[0, 0]
+    s = n0 * kappa * math.sin(P) / math.sqrt(2)
+    w_pre = P * math.exp(s) / (P * math.exp(s) + 1.0)    # P equal prefix keys, one zero suffix key
+    expect = h0 + w_pre * np.array([[1.0, 2.0]])             # every prefix value row is (1, 2)
+    got = O.decoder_layer(cfg, Wd, 0, h0, kp, vp)
+    assert np.allclose(got, expect)
