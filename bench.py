@@ -1,0 +1,175 @@
+#!/usr/bin/env python
+"""Benchmark: ms per 10-step action chunk and denoise steps/s of the Pi0-scale
+action expert (bf16 weights, fp32 accumulate, batch 1, 816-token prefix KV,
+chunk 50 x 32) on one MI355X.
+
+One bench step = one whole action chunk: `steps` Euler steps of the suffix
+(in_proj + time embedding, 18 decoder blocks over [prefix KV ; suffix],
+out_proj, Euler update), replayed as one captured graph with the noise
+already resident in HBM. Prints one JSON line.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
+
+
+def kernel_bytes(cfg):
+    """Algorithmic HBM bytes per launch of each kernel: weights (and KV) read once."""
+    w, F, dh, nq, nkv, A = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.action_dim
+    wb = 2 if cfg.weight_dtype == "bf16" else 4
+    mb = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.mlp_dtype]
+    sc = 4 if cfg.mlp_dtype == "fp8" else 0
+    kvb = 2 if cfg.kv_dtype == "bf16" else 4
+    return {
+        "qkv_rope": (nq + 2 * nkv) * dh * w * wb,
+        "attn": 2 * (cfg.prefix_len + cfg.horizon) * nkv * dh * kvb,
+        "o_proj_resid": w * nq * dh * wb,
+        "gate_up_geglu": 2 * F * w * mb + 2 * F * sc,
+        "down_resid": w * F * mb + w * sc,
+        "in_proj": w * A * wb,
+        "out_proj_euler": A * w * wb,
+    }
+
+
+def step_bytes(cfg, batch):
+    kb = kernel_bytes(cfg)
+    per_layer = kb["qkv_rope"] + kb["o_proj_resid"] + kb["gate_up_geglu"] + kb["down_resid"]
+    kv = batch * (kb["attn"] - 2 * cfg.horizon * cfg.n_kv_heads * cfg.head_dim * (2 if cfg.kv_dtype == "bf16" else 4))
+    return cfg.n_layers * (per_layer + kv) + kb["in_proj"] + kb["out_proj_euler"]
+
+
+def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0):
+    """The oracle as it stands, timed on this host: Euler steps of one robot until the budget is spent."""
+    from oracle import ae_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    Wd = O.dequantize_weights(cfg, W)
+    kk, vv = O.decode_kv(cfg, k, v)
+    x = noise[0].astype(np.float64)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        x = x + (1.0 / cfg.steps) * O.velocity(cfg, Wd, kk, vv, x, (n % cfg.steps) / cfg.steps)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 40:
+            break
+    return {"value": n / el, "unit": "denoise steps/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} Euler steps of one robot ({cfg.name}, P={cfg.prefix_len}, H={cfg.horizon}), fp64 numpy, "
+                      f"{el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20, help="timed action chunks")
+    ap.add_argument("--warmup", type=int, default=15)
+    ap.add_argument("--config", default="pi0_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-iters", type=int, default=3)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no multi-GPU leg)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from flow_matching_action_euler_amd import ActionExpert
+    from workload import configs as C
+    from workload import gen as G
+
+    cfg = C.config_by_name(args.config)
+    B = cfg.batch
+    t_setup = time.perf_counter()
+    W = G.make_weights(cfg)
+    kvs = [G.make_prefix_kv(cfg, cfg.kv_seed + r) for r in range(B)]
+    noise = G.make_noise(cfg, batch=B)
+    torch.cuda.set_device(0)
+    ex = ActionExpert(cfg, W)
+    for r in range(B):
+        ex.load_prefix_kv(r, *kvs[r])
+    d_noise = torch.from_numpy(noise).cuda()
+    d_out = torch.empty_like(d_noise)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    print(f"setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        ex.denoise_async(B, d_noise.data_ptr(), cfg.steps, d_out.data_ptr(), sp)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        ex.denoise_async(B, d_noise.data_ptr(), cfg.steps, d_out.data_ptr(), sp)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    chunk_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    ms_per_chunk = elapsed * 1e3 / args.steps
+    out = d_out.cpu().numpy()
+    assert np.all(np.isfinite(out))
+
+    # per-kernel HIP-event timing on the library's stream (eager launches of the same kernels)
+    stats = ex.kernel_times(0, B, cfg.steps, args.kernel_iters)
+    kb = kernel_bytes(cfg)
+    kernels = {}
+    for name, launches, total in stats:
+        avg_us = total * 1e3 / launches
+        entry = {"launches_per_chunk": launches // args.kernel_iters, "avg_us": round(avg_us, 3),
+                 "ms_per_chunk": round(total / args.kernel_iters, 4)}
+        if name in kb:
+            per_launch = kb[name] * (B if name == "attn" else 1)
+            entry["alg_bytes"] = per_launch
+            entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+        kernels[name] = entry
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_chunk"])
+    sb = step_bytes(cfg, B)
+    achieved = kernels[dom].get("GBs")
+    result = {
+        "metric": "ms per 10-step action chunk & denoise steps/s (Pi0-scale expert, bs1)",
+        "value": round(args.steps * cfg.steps / elapsed, 2),
+        "unit": "denoise steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_chunk, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.mlp_dtype == "bf16" else ("fp8+bf16" if cfg.mlp_dtype == "fp8" else "f32"),
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix KV and noise)",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "width": cfg.width, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv",
+                   "head_dim": cfg.head_dim, "mlp_dim": cfg.mlp_dim, "prefix_len": cfg.prefix_len,
+                   "chunk": f"{cfg.horizon}x{cfg.action_dim}", "euler_steps": cfg.steps, "robots": B},
+        "chunk_ms_median": round(float(np.median(chunk_ms)), 4),
+        "chunk_ms_p90": round(float(np.percentile(chunk_ms, 90)), 4),
+        "step_alg_bytes": sb,
+        "whole_chunk_GBs": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9, 1),
+        "whole_chunk_hbm_frac": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, W, kvs[0][0], kvs[0][1], noise)
+    ex.close()
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,813 @@
+// Host runtime of the action-expert library: implements include/ae.h.
+//
+// ae_create validates the shape contract, packs the weights into MFMA lane
+// order and uploads them once; ae_load_prefix_kv fills a prefix slot;
+// ae_denoise / ae_verify copy their small inputs into static device buffers
+// and replay one captured hipGraph of the whole pass (DM0.5 guide, section
+// 6.5: static buffers, fixed step count, one replay per request). Graphs are
+// cached per (mode, steps or n_tau, batch).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/ae.h"
+#include "ae_kernels.hpp"
+
+using namespace ae;
+
+namespace {
+
+thread_local std::string g_create_error;
+
+struct Timer {  // per-launch HIP events for ae_kernel_times
+  hipStream_t stream;
+  std::vector<std::pair<std::string, std::pair<hipEvent_t, hipEvent_t>>> rec;
+  void begin(const char* name) {
+    hipEvent_t a, b;
+    (void)hipEventCreate(&a);
+    (void)hipEventCreate(&b);
+    (void)hipEventRecord(a, stream);
+    rec.push_back({name, {a, b}});
+  }
+  void end() { (void)hipEventRecord(rec.back().second.second, stream); }
+};
+
+size_t dtype_size(int dt) { return dt == AE_F32 ? 4 : dt == AE_BF16 ? 2 : 1; }
+
+struct PhaseCfg {
+  int S;  // k-splits
+};
+
+}  // namespace
+
+struct ae_handle {
+  ae_config c{};
+  int dev = 0;
+  hipStream_t stream = nullptr;
+  std::string err;
+  int at = AT_BF16;      // activation type
+  int wt = WT_BF16;      // attention / projection weight type
+  int mt = WT_BF16;      // MLP weight type
+  int M_max = 0, Mp_max = 0;
+  int ld_h = 0, ld_q = 0, ld_kv = 0, ld_u = 0;  // padded row strides (elements) of hb/o, q, k/v, u
+  std::vector<void*> allocs;
+
+  // weights (device)
+  void *time_in_w = nullptr, *time_out_w = nullptr, *action_in_w = nullptr, *action_out_p = nullptr;
+  float *time_in_b = nullptr, *time_out_b = nullptr, *action_in_b = nullptr, *action_out_b = nullptr;
+  std::vector<void*> qkv_p, o_p, gu_p, d_p;
+  std::vector<float*> gu_s, d_s;   // fp8 scales in packed order
+  std::vector<float*> ln1, ln2;
+  float* final_ln = nullptr;
+  int qkv_tiles = 0, gu_tiles = 0, out_tiles = 0;
+
+  // activations and scratch
+  float *x = nullptr, *h = nullptr, *ssp_a = nullptr, *ssp_b = nullptr, *vout = nullptr;
+  void *hb = nullptr, *q = nullptr, *sk = nullptr, *sv = nullptr, *o = nullptr, *u = nullptr;
+  float* part = nullptr;
+  size_t part_floats = 0;
+  unsigned* counters = nullptr;
+  size_t n_counters = 0;
+  float *opart = nullptr, *mlpart = nullptr;
+  float* rope_cs = nullptr;
+  void *kcache = nullptr, *vcache = nullptr;
+  size_t slot_elems = 0;
+  std::vector<int> slot_ready;
+  int *denoise_slots = nullptr, *verify_slots = nullptr;
+  // verify inputs / outputs
+  float *draft = nullptr, *vnoise = nullptr, *taus = nullptr, *temb_tau = nullptr, *phi = nullptr, *hid = nullptr,
+        *dist = nullptr, *params = nullptr;
+  int *accept = nullptr, *gswitch = nullptr;
+  std::map<int, float*> temb_steps;  // steps -> [steps][width]
+  std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
+  float last_ms = 0.f;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  // inputs of the last call per mode, for ae_kernel_times
+  int last_verify_slot = 0;
+  float last_delta = 0.f;
+};
+
+namespace {
+
+int fail(ae_handle* h, int code, const std::string& msg) {
+  if (h) h->err = msg;
+  else g_create_error = msg;
+  return code;
+}
+
+#define HIP_TRY(h, expr)                                                                  \
+  do {                                                                                    \
+    hipError_t e_ = (expr);                                                               \
+    if (e_ != hipSuccess) {                                                               \
+      return fail(h, e_ == hipErrorOutOfMemory ? AE_ERR_OOM : AE_ERR_HIP,                 \
+                  std::string(#expr) + ": " + hipGetErrorString(e_));                     \
+    }                                                                                     \
+  } while (0)
+
+int dalloc(ae_handle* h, void** p, size_t bytes) {
+  if (bytes == 0) bytes = 16;
+  hipError_t e = hipMalloc(p, bytes);
+  if (e != hipSuccess) return fail(h, AE_ERR_OOM, "hipMalloc(" + std::to_string(bytes) + "): " + hipGetErrorString(e));
+  h->allocs.push_back(*p);
+  e = hipMemset(*p, 0, bytes);
+  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("hipMemset: ") + hipGetErrorString(e));
+  return AE_OK;
+}
+
+template <class T>
+int dalloc_t(ae_handle* h, T** p, size_t count) {
+  return dalloc(h, (void**)p, count * sizeof(T));
+}
+
+int upload(ae_handle* h, void** dst, const void* src, size_t bytes) {
+  int rc = dalloc(h, dst, bytes);
+  if (rc) return rc;
+  HIP_TRY(h, hipMemcpy(*dst, src, bytes, hipMemcpyHostToDevice));
+  return AE_OK;
+}
+
+// Pack rows (row_ptr[p] = source row of packed channel p, or null for a zero row)
+// of K elements of size es into [tiles][K/32][64 lanes][8].
+void pack_rows(const std::vector<const unsigned char*>& row_ptr, int K, size_t es, std::vector<unsigned char>& out) {
+  const int tiles = (int)row_ptr.size() / 16, KB = K / 32;
+  out.assign((size_t)tiles * KB * 64 * 8 * es, 0);
+  for (int t = 0; t < tiles; ++t)
+    for (int kb = 0; kb < KB; ++kb)
+      for (int lane = 0; lane < 64; ++lane) {
+        const unsigned char* src = row_ptr[t * 16 + (lane & 15)];
+        unsigned char* dst = out.data() + (((size_t)t * KB + kb) * 64 + lane) * 8 * es;
+        if (src) memcpy(dst, src + ((size_t)kb * 32 + (lane >> 4) * 8) * es, 8 * es);
+      }
+}
+
+int validate(const ae_config* c, const ae_weights* w) {
+  if (!c || !w) return fail(nullptr, AE_ERR_INVALID_ARG, "null config or weights");
+  if (c->n_layers < 1 || c->width <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
+      c->mlp_dim <= 0 || c->action_dim <= 0 || c->horizon <= 0 || c->prefix_len < 0 || c->max_batch < 1 ||
+      c->max_taus < 0 || c->max_taus > 64 || !(c->rms_eps >= 0.f) || !(c->rope_base > 0.f))
+    return fail(nullptr, AE_ERR_INVALID_ARG, "non-positive size in ae_config");
+  if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, AE_ERR_INVALID_ARG, "n_kv_heads must divide n_q_heads");
+  if (c->gripper_dim >= c->action_dim || c->gripper_dim < -1) return fail(nullptr, AE_ERR_INVALID_ARG, "gripper_dim out of range");
+  for (int d : {c->weight_dtype, c->mlp_dtype, c->kv_dtype})
+    if (d != AE_F32 && d != AE_BF16 && d != AE_FP8_E4M3) return fail(nullptr, AE_ERR_INVALID_ARG, "unknown dtype");
+  if (c->width % 64 || c->head_dim % 32 || c->mlp_dim % 32 || c->head_dim > 256)
+    return fail(nullptr, AE_ERR_UNSUPPORTED, "width must be a multiple of 64, head_dim of 32 (<= 256), mlp_dim of 32");
+  if (c->action_dim > 64 || c->horizon > 256) return fail(nullptr, AE_ERR_UNSUPPORTED, "action_dim <= 64 and horizon <= 256");
+  if (c->weight_dtype == AE_FP8_E4M3) return fail(nullptr, AE_ERR_UNSUPPORTED, "fp8 is supported for the MLP only");
+  if (c->kv_dtype != c->weight_dtype) return fail(nullptr, AE_ERR_UNSUPPORTED, "kv_dtype must equal weight_dtype");
+  if (c->weight_dtype == AE_F32 && c->mlp_dtype != AE_F32)
+    return fail(nullptr, AE_ERR_UNSUPPORTED, "fp32 attention weights need fp32 MLP weights");
+  if (c->weight_dtype == AE_BF16 && c->mlp_dtype == AE_F32)
+    return fail(nullptr, AE_ERR_UNSUPPORTED, "bf16 attention weights need bf16 or fp8 MLP weights");
+  if (!w->time_in_w || !w->time_in_b || !w->time_out_w || !w->time_out_b || !w->action_in_w || !w->action_in_b ||
+      !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b)
+    return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
+  for (int l = 0; l < c->n_layers; ++l) {
+    const ae_layer_weights& L = w->layers[l];
+    if (!L.ln1 || !L.wq || !L.wk || !L.wv || !L.wo || !L.ln2 || !L.wg || !L.wu || !L.wd)
+      return fail(nullptr, AE_ERR_INVALID_ARG, "null layer weight pointer");
+    if (c->mlp_dtype == AE_FP8_E4M3 && (!L.wg_scale || !L.wu_scale || !L.wd_scale))
+      return fail(nullptr, AE_ERR_INVALID_ARG, "fp8 MLP needs per-row scales");
+  }
+  return AE_OK;
+}
+
+PhaseCfg pick(int KB, int want, int n_z) {
+  int S = n_z == 1 ? want : 1;
+  while (S > 1 && (KB % S)) --S;
+  return {S};
+}
+
+template <int WT, int AT, int EPI, int NT>
+hipError_t launch_gemm(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+  size_t lds = (size_t)(5 * NT * TOKG * 16 + TOKG) * sizeof(float);
+  constexpr int KBW = AT == AT_F32 ? 4 : 8;
+  hipLaunchKernelGGL((gemm_kernel<WT, AT, EPI, NT, KBW>), dim3(n_groups, a.S, n_z), dim3(256), lds, st, a);
+  return hipGetLastError();
+}
+
+// k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group;
+// AE_SPLITS="q,o,g,d,u" overrides them for tuning.
+struct Splits {
+  int qkv = 1, o = 2, gu = 1, down = 4, out = 1;
+  Splits() {
+    if (const char* e = getenv("AE_SPLITS")) sscanf(e, "%d,%d,%d,%d,%d", &qkv, &o, &gu, &down, &out);
+  }
+};
+const Splits& splits() { static Splits s; return s; }
+
+template <int AT>
+hipError_t set_attrs(size_t bytes) {
+  return hipFuncSetAttribute((const void*)attn_kernel<AT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+size_t attn_lds_bytes(int at, int dh) {
+  const int KC = at == AT_BF16 ? 64 : 32, pad = at == AT_BF16 ? 8 : 4;
+  const size_t es = at == AT_BF16 ? 2 : 4;
+  return ((size_t)KC * (dh + pad) + (size_t)dh * (KC + pad) + 64 * (size_t)(KC + pad)) * es;
+}
+
+struct Dispatch {
+  // one launcher per (phase) bound to the handle's dtypes
+  static hipError_t gemm(ae_handle* h, int epi, bool mlp, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+    if (h->at == AT_F32) {
+      switch (epi) {
+        case EPI_QKV: return launch_gemm<WT_F32, AT_F32, EPI_QKV, 1>(a, n_groups, n_z, st);
+        case EPI_RESID: return launch_gemm<WT_F32, AT_F32, EPI_RESID, 1>(a, n_groups, n_z, st);
+        case EPI_GEGLU: return launch_gemm<WT_F32, AT_F32, EPI_GEGLU, 2>(a, n_groups, n_z, st);
+        default: return launch_gemm<WT_F32, AT_F32, EPI_OUT, 1>(a, n_groups, n_z, st);
+      }
+    }
+    if (mlp && h->mt == WT_FP8) {
+      if (epi == EPI_GEGLU) return launch_gemm<WT_FP8, AT_BF16, EPI_GEGLU, 2>(a, n_groups, n_z, st);
+      return launch_gemm<WT_FP8, AT_BF16, EPI_RESID, 1>(a, n_groups, n_z, st);
+    }
+    switch (epi) {
+      case EPI_QKV: return launch_gemm<WT_BF16, AT_BF16, EPI_QKV, 1>(a, n_groups, n_z, st);
+      case EPI_RESID: return launch_gemm<WT_BF16, AT_BF16, EPI_RESID, 1>(a, n_groups, n_z, st);
+      case EPI_GEGLU: return launch_gemm<WT_BF16, AT_BF16, EPI_GEGLU, 2>(a, n_groups, n_z, st);
+      default: return launch_gemm<WT_BF16, AT_BF16, EPI_OUT, 1>(a, n_groups, n_z, st);
+    }
+  }
+};
+
+#define LAUNCH_CHECK(h, name, expr)                                                          \
+  do {                                                                                       \
+    if (tm) tm->begin(name);                                                                 \
+    expr;                                                                                    \
+    if (tm) tm->end();                                                                       \
+    hipError_t e_ = hipGetLastError();                                                       \
+    if (e_ != hipSuccess) return fail(h, AE_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
+// temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
+int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, float dt,
+                     hipStream_t st, Timer* tm) {
+  const ae_config& c = h->c;
+  const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
+  const int nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
+  const int M = n_seq * H, Mp = (M + 15) / 16 * 16, n_z = (Mp + TOKG - 1) / TOKG;
+
+  LAUNCH_CHECK(h, "in_proj", {
+    if (h->at == AT_F32)
+      hipLaunchKernelGGL((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
+                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
+    else
+      hipLaunchKernelGGL((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
+                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
+  });
+
+  const int gq = nq / nkv, R = gq * H;
+  const int KC = h->at == AT_BF16 ? 64 : 32;
+  AttnArgs aa{};
+  aa.q = h->q; aa.ks = h->sk; aa.vs = h->sv; aa.kcache = h->kcache; aa.vcache = h->vcache;
+  aa.seq_slot = seq_slot; aa.slot_stride = h->slot_elems;
+  aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh; aa.KC = KC;
+  aa.ldq = h->ld_q; aa.ldkv = h->ld_kv; aa.ldo = h->ld_q;
+  aa.n_qt = (R + 63) / 64; aa.n_chunks = (c.prefix_len + H + KC - 1) / KC;
+  aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
+  aa.opart = h->opart; aa.mlpart = h->mlpart;
+  const size_t attn_lds = attn_lds_bytes(h->at, dh);
+
+  for (int l = 0; l < c.n_layers; ++l) {
+    GemmArgs g{};
+    g.inv_width = 1.f / (float)w; g.eps = c.rms_eps; g.M = M; g.M_pad = Mp;
+    g.part = h->part; g.counters = h->counters;
+    // --- norm1 + QKV + RoPE
+    {
+      GemmArgs a = g;
+      a.w = h->qkv_p[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_q; a.ldkv = h->ld_kv;
+      a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
+      a.S = pick(w / 32, splits().qkv, n_z).S;
+      a.q_out = h->q; a.k_out = h->sk; a.v_out = h->sv; a.rope_cs = h->rope_cs;
+      a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
+      LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, EPI_QKV, false, a, h->qkv_tiles, n_z, st));
+    }
+    // --- attention over [prefix ; suffix]
+    aa.layer_off = (size_t)l * c.prefix_len * nkv * dh;
+    LAUNCH_CHECK(h, "attn", {
+      if (h->at == AT_BF16)
+        hipLaunchKernelGGL(attn_kernel<AT_BF16>, dim3(aa.n_chunks, aa.n_qt, n_seq * nkv), dim3(256), attn_lds, st, aa);
+      else
+        hipLaunchKernelGGL(attn_kernel<AT_F32>, dim3(aa.n_chunks, aa.n_qt, n_seq * nkv), dim3(256), attn_lds, st, aa);
+    });
+    LAUNCH_CHECK(h, "attn_combine", {
+      if (h->at == AT_BF16)
+        hipLaunchKernelGGL(attn_combine<AT_BF16>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa, h->o);
+      else
+        hipLaunchKernelGGL(attn_combine<AT_F32>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa, h->o);
+    });
+    // --- o_proj + residual; hb <- h * ln2
+    {
+      GemmArgs a = g;
+      a.w = h->o_p[l]; a.x = h->o; a.ldx = h->ld_q; a.ldo = h->ld_h; a.ssp_in = nullptr; a.K = nq * dh;
+      a.S = pick(nq * dh / 32, splits().o, n_z).S;
+      a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
+      LAUNCH_CHECK(h, "o_proj_resid", (void)Dispatch::gemm(h, EPI_RESID, false, a, w / 16, n_z, st));
+    }
+    // --- norm2 + gate/up + GeGLU
+    {
+      GemmArgs a = g;
+      a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_u;
+      a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
+      a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
+      LAUNCH_CHECK(h, "gate_up_geglu", (void)Dispatch::gemm(h, EPI_GEGLU, true, a, h->gu_tiles / 2, n_z, st));
+    }
+    // --- down + residual; hb <- h * next gain
+    {
+      GemmArgs a = g;
+      a.w = h->d_p[l]; a.wscale = h->d_s[l]; a.x = h->u; a.ldx = h->ld_u; a.ldo = h->ld_h; a.ssp_in = nullptr; a.K = F;
+      a.S = pick(F / 32, splits().down, n_z).S;
+      a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
+      a.ssp_out = h->ssp_a; a.N = w;
+      LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, EPI_RESID, true, a, w / 16, n_z, st));
+    }
+  }
+  // --- final norm + action_out_proj (+ Euler update)
+  {
+    GemmArgs a{};
+    a.inv_width = 1.f / (float)w; a.eps = c.rms_eps; a.M = M; a.M_pad = Mp;
+    a.part = h->part; a.counters = h->counters;
+    a.w = h->action_out_p; a.x = h->hb; a.ldx = h->ld_h; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
+    a.S = pick(w / 32, splits().out, n_z).S;
+    a.bias = h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
+    LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, EPI_OUT, false, a, h->out_tiles, n_z, st));
+  }
+  return AE_OK;
+}
+
+// temb for n_t times in device array t_dev -> out [n_t][width].
+int enqueue_temb(ae_handle* h, const float* t_dev, int n_t, float* out, hipStream_t st, Timer* tm) {
+  const int w = h->c.width;
+  LAUNCH_CHECK(h, "time_sinusoid", hipLaunchKernelGGL(sinusoid_kernel, dim3(std::max(1, w / 2 / 256), n_t), dim3(256), 0, st, t_dev, w, h->phi));
+  LAUNCH_CHECK(h, "time_mlp", {
+    if (h->at == AT_F32) {
+      hipLaunchKernelGGL(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid);
+      hipLaunchKernelGGL(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out);
+    } else {
+      hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid);
+      hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out);
+    }
+  });
+  return AE_OK;
+}
+
+int get_temb_steps(ae_handle* h, int steps, float** out) {
+  auto it = h->temb_steps.find(steps);
+  if (it != h->temb_steps.end()) { *out = it->second; return AE_OK; }
+  const int w = h->c.width;
+  float* buf = nullptr;
+  int rc = dalloc_t(h, &buf, (size_t)steps * w);
+  if (rc) return rc;
+  std::vector<float> ts(steps);
+  for (int k = 0; k < steps; ++k) ts[k] = (float)((double)k / steps);
+  // the sinusoid/hidden scratch holds max(steps, max_taus) rows
+  float *tdev = nullptr, *phi = nullptr, *hid = nullptr;
+  rc = dalloc_t(h, &tdev, steps); if (rc) return rc;
+  rc = dalloc_t(h, &phi, (size_t)steps * w); if (rc) return rc;
+  rc = dalloc_t(h, &hid, (size_t)steps * w); if (rc) return rc;
+  HIP_TRY(h, hipMemcpy(tdev, ts.data(), steps * sizeof(float), hipMemcpyHostToDevice));
+  float* save_phi = h->phi; float* save_hid = h->hid;
+  h->phi = phi; h->hid = hid;
+  rc = enqueue_temb(h, tdev, steps, buf, h->stream, nullptr);
+  h->phi = save_phi; h->hid = save_hid;
+  if (rc) return rc;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  h->temb_steps[steps] = buf;
+  *out = buf;
+  return AE_OK;
+}
+
+int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t st, Timer* tm) {
+  const float dt = 1.f / (float)steps;
+  for (int k = 0; k < steps; ++k) {
+    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, h->denoise_slots, dt, st, tm);
+    if (rc) return rc;
+  }
+  return AE_OK;
+}
+
+int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
+  const ae_config& c = h->c;
+  const int H = c.horizon, A = c.action_dim;
+  LAUNCH_CHECK(h, "verify_interp", hipLaunchKernelGGL(interp_kernel, dim3((n_tau * H * A + 255) / 256), dim3(256), 0, st,
+                                                      h->draft, h->vnoise, h->taus, n_tau, H, A, h->x));
+  int rc = enqueue_temb(h, h->taus, n_tau, h->temb_tau, st, tm);
+  if (rc) return rc;
+  rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0.f, st, tm);
+  if (rc) return rc;
+  LAUNCH_CHECK(h, "verify_accept", hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(256), (size_t)n_tau * H * sizeof(float), st,
+                                                      h->x, h->vout, h->draft, h->taus, n_tau, H, A, h->params,
+                                                      c.gripper_dim, h->dist, h->accept, h->gswitch));
+  return AE_OK;
+}
+
+int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
+  auto key = std::make_tuple(mode, a, b);
+  auto it = h->graphs.find(key);
+  if (it != h->graphs.end()) { *out = it->second; return AE_OK; }
+  float* temb = nullptr;
+  if (mode == 0) {
+    int rc = get_temb_steps(h, a, &temb);
+    if (rc) return rc;
+  }
+  HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+  int rc = mode == 0 ? enqueue_denoise(h, b, a, temb, h->stream, nullptr) : enqueue_verify(h, a, h->stream, nullptr);
+  hipGraph_t graph = nullptr;
+  hipError_t e = hipStreamEndCapture(h->stream, &graph);
+  if (rc) { if (graph) hipGraphDestroy(graph); return rc; }
+  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  hipGraphExec_t exec = nullptr;
+  e = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  hipGraphDestroy(graph);
+  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(e));
+  h->graphs[key] = exec;
+  *out = exec;
+  return AE_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+extern "C" {
+
+int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
+  g_create_error.clear();
+  if (!out) return fail(nullptr, AE_ERR_INVALID_ARG, "null output handle pointer");
+  *out = nullptr;
+  int rc = validate(cfg, wts);
+  if (rc) return rc;
+  int ndev = 0;
+  hipError_t e = hipGetDeviceCount(&ndev);
+  if (e != hipSuccess || ndev == 0) return fail(nullptr, AE_ERR_HIP, "no HIP device available");
+
+  ae_handle* h = new ae_handle();
+  h->c = *cfg;
+  const ae_config& c = h->c;
+  if (hipGetDevice(&h->dev) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipGetDevice failed"); }
+  if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
+  hipEventCreate(&h->ev0);
+  hipEventCreate(&h->ev1);
+  h->at = c.weight_dtype == AE_F32 ? AT_F32 : AT_BF16;
+  h->wt = c.weight_dtype == AE_F32 ? WT_F32 : WT_BF16;
+  h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
+  const size_t lds_need = attn_lds_bytes(h->at, cfg->head_dim);
+  if ((h->at == AT_BF16 ? set_attrs<AT_BF16>(lds_need) : set_attrs<AT_F32>(lds_need)) != hipSuccess) {
+    std::string m = "hipFuncSetAttribute failed";
+    ae_destroy(h);
+    return fail(nullptr, AE_ERR_HIP, m);
+  }
+
+  const int w = c.width, A = c.action_dim, F = c.mlp_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
+  const int L = c.n_layers, H = c.horizon, P = c.prefix_len;
+  const size_t wes = dtype_size(c.weight_dtype), mes = dtype_size(c.mlp_dtype), kes = dtype_size(c.kv_dtype);
+  const int aes = h->at == AT_F32 ? 4 : 2;
+  h->M_max = std::max(c.max_batch, std::max(1, c.max_taus)) * H;
+  h->Mp_max = (h->M_max + 15) / 16 * 16;
+  const int Mp = h->Mp_max;
+  std::string msg;
+#define TRY(x) do { int r_ = (x); if (r_) { msg = h->err; ae_destroy(h); return fail(nullptr, r_, msg); } } while (0)
+
+  // ---- small weights (row-major, used by the time MLP and in_proj kernels)
+  TRY(upload(h, &h->time_in_w, wts->time_in_w, (size_t)w * w * wes));
+  TRY(upload(h, (void**)&h->time_in_b, wts->time_in_b, (size_t)w * 4));
+  TRY(upload(h, &h->time_out_w, wts->time_out_w, (size_t)w * w * wes));
+  TRY(upload(h, (void**)&h->time_out_b, wts->time_out_b, (size_t)w * 4));
+  TRY(upload(h, &h->action_in_w, wts->action_in_w, (size_t)w * A * wes));
+  TRY(upload(h, (void**)&h->action_in_b, wts->action_in_b, (size_t)w * 4));
+  TRY(upload(h, (void**)&h->action_out_b, wts->action_out_b, (size_t)A * 4));
+  TRY(upload(h, (void**)&h->final_ln, wts->final_ln, (size_t)w * 4));
+  {
+    h->out_tiles = (A + 15) / 16;
+    std::vector<const unsigned char*> rows(h->out_tiles * 16, nullptr);
+    for (int r = 0; r < A; ++r) rows[r] = (const unsigned char*)wts->action_out_w + (size_t)r * w * wes;
+    std::vector<unsigned char> buf;
+    pack_rows(rows, w, wes, buf);
+    TRY(upload(h, &h->action_out_p, buf.data(), buf.size()));
+  }
+  // ---- decoder layers, packed
+  h->qkv_tiles = (nq + 2 * nkv) * dh / 16;
+  h->gu_tiles = 2 * F / 16;
+  for (int l = 0; l < L; ++l) {
+    const ae_layer_weights& Lw = wts->layers[l];
+    std::vector<unsigned char> buf;
+    // q heads, k heads: tile = 8 channels d..d+7 and their RoPE partners d+dh/2..; then v
+    std::vector<const unsigned char*> rows;
+    auto head_rows = [&](const void* base, int nh) {
+      for (int hh = 0; hh < nh; ++hh)
+        for (int p = 0; p < dh / 16; ++p)
+          for (int cc = 0; cc < 16; ++cc) {
+            int d = cc < 8 ? p * 8 + cc : dh / 2 + p * 8 + (cc - 8);
+            rows.push_back((const unsigned char*)base + ((size_t)hh * dh + d) * w * wes);
+          }
+    };
+    head_rows(Lw.wq, nq);
+    head_rows(Lw.wk, nkv);
+    for (int r = 0; r < nkv * dh; ++r) rows.push_back((const unsigned char*)Lw.wv + (size_t)r * w * wes);
+    pack_rows(rows, w, wes, buf);
+    void* p = nullptr;
+    TRY(upload(h, &p, buf.data(), buf.size()));
+    h->qkv_p.push_back(p);
+    rows.clear();
+    for (int r = 0; r < w; ++r) rows.push_back((const unsigned char*)Lw.wo + (size_t)r * nq * dh * wes);
+    pack_rows(rows, nq * dh, wes, buf);
+    TRY(upload(h, &p, buf.data(), buf.size()));
+    h->o_p.push_back(p);
+    // gate/up interleaved by 16-row tiles
+    rows.clear();
+    std::vector<float> gus;
+    for (int j = 0; j < F / 16; ++j) {
+      for (int cc = 0; cc < 16; ++cc) rows.push_back((const unsigned char*)Lw.wg + ((size_t)j * 16 + cc) * w * mes);
+      for (int cc = 0; cc < 16; ++cc) rows.push_back((const unsigned char*)Lw.wu + ((size_t)j * 16 + cc) * w * mes);
+      if (c.mlp_dtype == AE_FP8_E4M3) {
+        for (int cc = 0; cc < 16; ++cc) gus.push_back(Lw.wg_scale[j * 16 + cc]);
+        for (int cc = 0; cc < 16; ++cc) gus.push_back(Lw.wu_scale[j * 16 + cc]);
+      }
+    }
+    pack_rows(rows, w, mes, buf);
+    TRY(upload(h, &p, buf.data(), buf.size()));
+    h->gu_p.push_back(p);
+    rows.clear();
+    for (int r = 0; r < w; ++r) rows.push_back((const unsigned char*)Lw.wd + (size_t)r * F * mes);
+    pack_rows(rows, F, mes, buf);
+    TRY(upload(h, &p, buf.data(), buf.size()));
+    h->d_p.push_back(p);
+    float *gs = nullptr, *ds = nullptr;
+    if (c.mlp_dtype == AE_FP8_E4M3) {
+      TRY(upload(h, (void**)&gs, gus.data(), gus.size() * 4));
+      TRY(upload(h, (void**)&ds, Lw.wd_scale, (size_t)w * 4));
+    }
+    h->gu_s.push_back(gs);
+    h->d_s.push_back(ds);
+    float *g1 = nullptr, *g2 = nullptr;
+    TRY(upload(h, (void**)&g1, Lw.ln1, (size_t)w * 4));
+    TRY(upload(h, (void**)&g2, Lw.ln2, (size_t)w * 4));
+    h->ln1.push_back(g1);
+    h->ln2.push_back(g2);
+  }
+  // ---- activations and scratch (padding rows stay zero)
+  TRY(dalloc_t(h, &h->x, (size_t)Mp * A));
+  TRY(dalloc_t(h, &h->vout, (size_t)Mp * A));
+  TRY(dalloc_t(h, &h->h, (size_t)Mp * w));
+  // activation rows padded by 128 bytes so the rows of one MFMA fragment spread over L2 channels
+  const int pad = 128 / aes;
+  h->ld_h = w + pad; h->ld_q = nq * dh + pad; h->ld_kv = nkv * dh + pad; h->ld_u = F + pad;
+  TRY(dalloc(h, &h->hb, (size_t)Mp * h->ld_h * aes));
+  TRY(dalloc_t(h, &h->ssp_a, (size_t)(w / 16) * Mp));
+  TRY(dalloc_t(h, &h->ssp_b, (size_t)(w / 16) * Mp));
+  TRY(dalloc(h, &h->q, (size_t)Mp * h->ld_q * aes));
+  TRY(dalloc(h, &h->sk, (size_t)Mp * h->ld_kv * aes));
+  TRY(dalloc(h, &h->sv, (size_t)Mp * h->ld_kv * aes));
+  TRY(dalloc(h, &h->o, (size_t)Mp * h->ld_q * aes));
+  TRY(dalloc(h, &h->u, (size_t)Mp * h->ld_u * aes));
+  {
+    const int n_z = (Mp + TOKG - 1) / TOKG;
+    size_t maxg = std::max({(size_t)h->qkv_tiles, (size_t)(w / 16), (size_t)h->gu_tiles, (size_t)h->out_tiles});
+    h->part_floats = 4 * maxg * 2 * TOKG * 16 * (size_t)n_z;
+    TRY(dalloc_t(h, &h->part, h->part_floats));
+    h->n_counters = maxg * n_z;
+    TRY(dalloc_t(h, &h->counters, h->n_counters));
+    const int KC = h->at == AT_BF16 ? 64 : 32;
+    const int R = nq / nkv * H;
+    const size_t n_qt = (R + 63) / 64, n_chunks = (P + H + KC - 1) / KC;
+    const size_t n_zz = (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv;
+    TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_chunks * 64 * dh));
+    TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_chunks * 64 * 2));
+  }
+  {
+    std::vector<float> cs((size_t)H * (dh / 2) * 2);
+    for (int t = 0; t < H; ++t)
+      for (int d = 0; d < dh / 2; ++d) {
+        double ang = (double)(P + t) * std::pow((double)c.rope_base, -2.0 * d / dh);
+        cs[((size_t)t * (dh / 2) + d) * 2 + 0] = (float)std::cos(ang);
+        cs[((size_t)t * (dh / 2) + d) * 2 + 1] = (float)std::sin(ang);
+      }
+    TRY(upload(h, (void**)&h->rope_cs, cs.data(), cs.size() * 4));
+  }
+  h->slot_elems = (size_t)L * P * nkv * dh;
+  TRY(dalloc(h, &h->kcache, h->slot_elems * c.max_batch * kes));
+  TRY(dalloc(h, &h->vcache, h->slot_elems * c.max_batch * kes));
+  h->slot_ready.assign(c.max_batch, 0);
+  {
+    std::vector<int> ids(c.max_batch);
+    for (int i = 0; i < c.max_batch; ++i) ids[i] = i;
+    TRY(upload(h, (void**)&h->denoise_slots, ids.data(), ids.size() * 4));
+  }
+  const int ntau = std::max(1, c.max_taus);
+  TRY(dalloc_t(h, &h->verify_slots, ntau));
+  TRY(dalloc_t(h, &h->draft, (size_t)H * A));
+  TRY(dalloc_t(h, &h->vnoise, (size_t)H * A));
+  TRY(dalloc_t(h, &h->taus, ntau));
+  TRY(dalloc_t(h, &h->temb_tau, (size_t)ntau * w));
+  TRY(dalloc_t(h, &h->phi, (size_t)ntau * w));
+  TRY(dalloc_t(h, &h->hid, (size_t)ntau * w));
+  TRY(dalloc_t(h, &h->dist, (size_t)ntau * H));
+  TRY(dalloc_t(h, &h->params, 4));
+  TRY(dalloc_t(h, &h->accept, 1));
+  TRY(dalloc_t(h, &h->gswitch, 1));
+  if (hipDeviceSynchronize() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "device sync after upload failed"); }
+#undef TRY
+  *out = h;
+  return AE_OK;
+}
+
+int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
+  if (!h) return AE_ERR_INVALID_ARG;
+  if (!k || !v) return fail(h, AE_ERR_INVALID_ARG, "null cache pointer");
+  if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
+  const size_t bytes = h->slot_elems * dtype_size(h->c.kv_dtype);
+  if (bytes) {
+    HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * bytes, k, bytes, hipMemcpyHostToDevice));
+    HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * bytes, v, bytes, hipMemcpyHostToDevice));
+  }
+  h->slot_ready[slot] = 1;
+  return AE_OK;
+}
+
+static int check_denoise(ae_handle* h, int batch, int steps) {
+  if (!h) return AE_ERR_INVALID_ARG;
+  if (batch < 1 || batch > h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "batch out of range");
+  if (steps < 1 || steps > 1000) return fail(h, AE_ERR_INVALID_ARG, "steps out of range (1..1000)");
+  for (int b = 0; b < batch; ++b)
+    if (!h->slot_ready[b]) return fail(h, AE_ERR_NOT_READY, "prefix slot " + std::to_string(b) + " not loaded");
+  return AE_OK;
+}
+
+int ae_denoise_async(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out, void* stream) {
+  int rc = check_denoise(h, batch, steps);
+  if (rc) return rc;
+  if (!d_noise || !d_actions_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  hipStream_t st = stream ? (hipStream_t)stream : h->stream;
+  hipGraphExec_t g;
+  rc = get_graph(h, 0, steps, batch, &g);
+  if (rc) return rc;
+  const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
+  HIP_TRY(h, hipMemcpyAsync(h->x, d_noise, bytes, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(h, hipGraphLaunch(g, st));
+  HIP_TRY(h, hipMemcpyAsync(d_actions_out, h->x, bytes, hipMemcpyDeviceToDevice, st));
+  return AE_OK;
+}
+
+int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* actions_out) {
+  int rc = check_denoise(h, batch, steps);
+  if (rc) return rc;
+  if (!noise || !actions_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  hipGraphExec_t g;
+  rc = get_graph(h, 0, steps, batch, &g);
+  if (rc) return rc;
+  const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
+  HIP_TRY(h, hipMemcpyAsync(h->x, noise, bytes, hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(g, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  std::vector<float> tmp(bytes / sizeof(float));
+  HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  memcpy(actions_out, tmp.data(), bytes);
+  return AE_OK;
+}
+
+static int check_verify(ae_handle* h, int slot, int n_tau) {
+  if (!h) return AE_ERR_INVALID_ARG;
+  if (h->c.max_taus < 1) return fail(h, AE_ERR_UNSUPPORTED, "handle created with max_taus = 0");
+  if (n_tau < 1 || n_tau > h->c.max_taus) return fail(h, AE_ERR_INVALID_ARG, "n_tau out of range");
+  if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
+  if (!h->slot_ready[slot]) return fail(h, AE_ERR_NOT_READY, "prefix slot not loaded");
+  return AE_OK;
+}
+
+static int verify_common(ae_handle* h, int slot, int n_tau, float delta, hipStream_t st, hipMemcpyKind kind,
+                         const float* draft, const float* noise, const float* taus) {
+  const size_t ha = (size_t)h->c.horizon * h->c.action_dim * sizeof(float);
+  HIP_TRY(h, hipMemcpyAsync(h->draft, draft, ha, kind, st));
+  HIP_TRY(h, hipMemcpyAsync(h->vnoise, noise, ha, kind, st));
+  HIP_TRY(h, hipMemcpyAsync(h->taus, taus, n_tau * sizeof(float), kind, st));
+  hipLaunchKernelGGL(set_verify_params_kernel, dim3(1), dim3(64), 0, st, h->verify_slots, n_tau, slot, h->params, delta);
+  HIP_TRY(h, hipGetLastError());
+  h->last_verify_slot = slot;
+  h->last_delta = delta;
+  return AE_OK;
+}
+
+int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d_noise, const float* d_taus, int n_tau,
+                    float delta, int* d_accept_len, int* d_gripper_switch, float* d_dist_out, void* stream) {
+  int rc = check_verify(h, slot, n_tau);
+  if (rc) return rc;
+  if (!d_draft || !d_noise || !d_taus || !d_accept_len || !d_gripper_switch) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  hipStream_t st = stream ? (hipStream_t)stream : h->stream;
+  hipGraphExec_t g;
+  rc = get_graph(h, 1, n_tau, 1, &g);
+  if (rc) return rc;
+  rc = verify_common(h, slot, n_tau, delta, st, hipMemcpyDeviceToDevice, d_draft, d_noise, d_taus);
+  if (rc) return rc;
+  HIP_TRY(h, hipGraphLaunch(g, st));
+  HIP_TRY(h, hipMemcpyAsync(d_accept_len, h->accept, sizeof(int), hipMemcpyDeviceToDevice, st));
+  HIP_TRY(h, hipMemcpyAsync(d_gripper_switch, h->gswitch, sizeof(int), hipMemcpyDeviceToDevice, st));
+  if (d_dist_out)
+    HIP_TRY(h, hipMemcpyAsync(d_dist_out, h->dist, (size_t)n_tau * h->c.horizon * sizeof(float), hipMemcpyDeviceToDevice, st));
+  return AE_OK;
+}
+
+int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, const float* taus, int n_tau, float delta,
+              int* accept_len, int* gripper_switch, float* dist_out) {
+  int rc = check_verify(h, slot, n_tau);
+  if (rc) return rc;
+  if (!draft || !noise || !taus || !accept_len || !gripper_switch) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  for (int j = 0; j < n_tau; ++j)
+    if (!(taus[j] >= 0.f && taus[j] < 1.f)) return fail(h, AE_ERR_INVALID_ARG, "tau must lie in [0, 1)");
+  hipGraphExec_t g;
+  rc = get_graph(h, 1, n_tau, 1, &g);
+  if (rc) return rc;
+  rc = verify_common(h, slot, n_tau, delta, h->stream, hipMemcpyHostToDevice, draft, noise, taus);
+  if (rc) return rc;
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(g, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  int acc = 0, sw = 0;
+  std::vector<float> d((size_t)n_tau * h->c.horizon);
+  HIP_TRY(h, hipMemcpyAsync(&acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipMemcpyAsync(&sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipMemcpyAsync(d.data(), h->dist, d.size() * sizeof(float), hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  *accept_len = acc;
+  *gripper_switch = sw;
+  if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
+  return AE_OK;
+}
+
+void ae_destroy(ae_handle* h) {
+  if (!h) return;
+  if (h->stream) hipStreamSynchronize(h->stream);
+  for (auto& kv : h->graphs) hipGraphExecDestroy(kv.second);
+  for (void* p : h->allocs) hipFree(p);
+  if (h->ev0) hipEventDestroy(h->ev0);
+  if (h->ev1) hipEventDestroy(h->ev1);
+  if (h->stream) hipStreamDestroy(h->stream);
+  delete h;
+}
+
+const char* ae_last_error(const ae_handle* h) { return h ? h->err.c_str() : g_create_error.c_str(); }
+
+int ae_last_gpu_ms(const ae_handle* h, float* ms) {
+  if (!h || !ms) return AE_ERR_INVALID_ARG;
+  *ms = h->last_ms;
+  return AE_OK;
+}
+
+int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats, int max_stats,
+                    int* n_stats) {
+  if (!h || !stats || !n_stats || iters < 1) return AE_ERR_INVALID_ARG;
+  int rc;
+  if (mode == 0) {
+    rc = check_denoise(h, batch, steps);
+    if (rc) return rc;
+  } else {
+    rc = check_verify(h, h->last_verify_slot, batch);
+    if (rc) return rc;
+  }
+  float* temb = nullptr;
+  if (mode == 0) { rc = get_temb_steps(h, steps, &temb); if (rc) return rc; }
+  Timer tm{h->stream, {}};
+  for (int it = 0; it < iters; ++it) {
+    rc = mode == 0 ? enqueue_denoise(h, batch, steps, temb, h->stream, &tm) : enqueue_verify(h, batch, h->stream, &tm);
+    if (rc) break;
+  }
+  hipError_t e = hipStreamSynchronize(h->stream);
+  std::vector<std::string> names;
+  std::map<std::string, std::pair<int, float>> agg;
+  for (auto& r : tm.rec) {
+    float ms = 0.f;
+    if (e == hipSuccess) hipEventElapsedTime(&ms, r.second.first, r.second.second);
+    if (!agg.count(r.first)) names.push_back(r.first);
+    agg[r.first].first += 1;
+    agg[r.first].second += ms;
+    hipEventDestroy(r.second.first);
+    hipEventDestroy(r.second.second);
+  }
+  if (rc) return rc;
+  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing: ") + hipGetErrorString(e));
+  int n = 0;
+  for (auto& nm : names) {
+    if (n >= max_stats) break;
+    memset(stats[n].name, 0, sizeof(stats[n].name));
+    strncpy(stats[n].name, nm.c_str(), sizeof(stats[n].name) - 1);
+    stats[n].launches = agg[nm].first;
+    stats[n].total_ms = agg[nm].second;
+    ++n;
+  }
+  *n_stats = n;
+  return AE_OK;
+}
+
+}  // extern "C"

@@ -261,6 +261,15 @@ def gripper_switch(draft, gripper_dim):
     return int(np.any(g[1:] * g[:-1] < 0))
 
 
+def accept_from_distances(D, delta, switch):
+    """Longest prefix k with D[j, i] < delta for all i < k and all j; 0 when switch is set."""
+    ok = np.all(np.asarray(D) < delta, axis=0)
+    accept = 0
+    while accept < ok.shape[0] and ok[accept]:
+        accept += 1
+    return 0 if switch else accept
+
+
 def accept_from_velocity(draft, x_tau, v_tau, taus, delta, gripper_dim):
     """FLASH acceptance given the expert velocity at each verification time.
 
@@ -272,14 +281,8 @@ def accept_from_velocity(draft, x_tau, v_tau, taus, delta, gripper_dim):
     taus = np.asarray(taus, np.float64)
     a_hat = x_tau + (1.0 - taus)[:, None, None] * v_tau
     D = np.sqrt(np.sum((a_hat - np.asarray(draft, np.float64)[None]) ** 2, axis=-1))
-    ok = np.all(D < delta, axis=0)
-    accept = 0
-    while accept < ok.shape[0] and ok[accept]:
-        accept += 1
     switch = gripper_switch(draft, gripper_dim)
-    if switch:
-        accept = 0
-    return accept, switch, D
+    return accept_from_distances(D, delta, switch), switch, D
 
 
 def verify(cfg, Wd, kv_k, kv_v, draft, noise, taus, delta):

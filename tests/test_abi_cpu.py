@@ -1,0 +1,121 @@
+"""C-ABI checks that need no GPU: exported symbols, struct layouts, and the
+argument validation that ae_create does before touching a device."""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+from flow_matching_action_euler_amd import binding as B
+from workload import configs as C
+from workload import gen as G
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ae.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ae_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    lib = B.load_library()
+    names = _declared()
+    assert len(names) == 10
+    assert sorted(B.EXPORTS) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    prog = tmp_path / "layout.c"
+    prog.write_text(r'''
+#include <stdio.h>
+#include <stddef.h>
+#include "ae.h"
+int main(void) {
+  printf("%zu %zu %zu %zu\n", sizeof(ae_config), sizeof(ae_layer_weights), sizeof(ae_weights), sizeof(ae_kernel_stat));
+  printf("%zu %zu %zu %zu\n", offsetof(ae_config, rope_base), offsetof(ae_config, gripper_dim),
+         offsetof(ae_weights, layers), offsetof(ae_kernel_stat, total_ms));
+  return 0;
+}
+''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-I", os.path.dirname(HEADER), str(prog), "-o", str(exe)], check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.split()
+    got = [int(x) for x in out]
+    exp = [ctypes.sizeof(B.ae_config), ctypes.sizeof(B.ae_layer_weights), ctypes.sizeof(B.ae_weights),
+           ctypes.sizeof(B.ae_kernel_stat), B.ae_config.rope_base.offset, B.ae_config.gripper_dim.offset,
+           B.ae_weights.layers.offset, B.ae_kernel_stat.total_ms.offset]
+    assert got == exp
+
+
+def _create_rc(cfg, W):
+    lib = B.load_library()
+    keep = []
+
+    def p(a):
+        if a is None:
+            return None
+        a = np.ascontiguousarray(a)
+        keep.append(a)
+        return a.ctypes.data
+
+    L = cfg.n_layers
+    layers = (B.ae_layer_weights * L)()
+    for l in range(L):
+        for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "wg", "wu", "wd"):
+            setattr(layers[l], f, p(W.get(f"layers.{l}.{f}")))
+        for f in ("wg", "wu", "wd"):
+            setattr(layers[l], f + "_scale", p(W.get(f"layers.{l}.{f}.scale")))
+    w = B.ae_weights(time_in_w=p(W["time_in_w"]), time_in_b=p(W["time_in_b"]), time_out_w=p(W["time_out_w"]),
+                     time_out_b=p(W["time_out_b"]), action_in_w=p(W["action_in_w"]), action_in_b=p(W["action_in_b"]),
+                     layers=layers, final_ln=p(W["final_ln"]), action_out_w=p(W["action_out_w"]),
+                     action_out_b=p(W["action_out_b"]))
+    c = B.make_config(cfg)
+    h = ctypes.c_void_p()
+    rc = lib.ae_create(ctypes.byref(c), ctypes.byref(w), ctypes.byref(h))
+    msg = lib.ae_last_error(None).decode()
+    if rc == 0:
+        lib.ae_destroy(h)
+    return rc, msg
+
+
+@pytest.fixture(scope="module")
+def tiny_weights():
+    return G.make_weights(C.TINY)
+
+
+@pytest.mark.parametrize("change,code", [
+    (dict(width=0), -1),
+    (dict(n_kv_heads=3), -1),           # does not divide n_q_heads
+    (dict(gripper_dim=8), -1),           # outside action_dim
+    (dict(width=200), -2),               # not a multiple of 64
+    (dict(head_dim=48), -2),             # not a multiple of 32
+    (dict(action_dim=65), -2),
+    (dict(kv_dtype="bf16"), -2),         # cache type differs from the attention weights
+    (dict(mlp_dtype="fp8"), -2),         # fp8 MLP needs bf16 attention weights
+])
+def test_create_rejects_bad_config_before_any_device_call(tiny_weights, change, code):
+    rc, msg = _create_rc(C.TINY.with_(**change), tiny_weights)
+    assert rc == code and msg
+
+
+def test_create_rejects_missing_weight(tiny_weights):
+    W = dict(tiny_weights)
+    W["layers.1.wd"] = None
+    rc, msg = _create_rc(C.TINY, W)
+    assert rc == -1 and "null" in msg
+
+
+def test_binding_raises_without_library(tmp_path):
+    with pytest.raises(OSError):
+        B._lib, saved = None, B._lib
+        try:
+            B.load_library(str(tmp_path / "missing.so"))
+        finally:
+            B._lib = saved

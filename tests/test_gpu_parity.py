@@ -1,0 +1,218 @@
+"""GPU path (libae.so through the C-ABI) against the CPU oracle, element by element.
+
+Floating-point chunks must satisfy max|gpu - oracle| <= tol * RMS(oracle):
+tol = 1e-4 (fp32), 2e-2 (bf16 weights, fp32 accumulate), 6e-2 (fp8 E4M3 MLP).
+Integers (accepted prefix length, gripper-switch flag) must match exactly.
+"""
+import numpy as np
+import pytest
+
+from flow_matching_action_euler_amd import ActionExpert, AEError
+from oracle import ae_oracle as O
+from workload import configs as C
+from workload import gen as G
+
+from helpers import SMALL_BF16, SMALL_F32, SMALL_FP8, Case, rel_err, tol_for
+
+pytestmark = pytest.mark.gpu
+
+
+def _expert(case, slots=None):
+    ex = ActionExpert(case.cfg, case.W)
+    for r in range(case.cfg.max_batch if slots is None else slots):
+        ex.load_prefix_kv(r, *case.kv[r])
+    return ex
+
+
+# ------------------------------------------------------------------ small shapes, several tiles, ragged tails
+
+@pytest.mark.parametrize("cfg", [C.TINY, SMALL_F32, SMALL_BF16, SMALL_FP8], ids=lambda c: c.name)
+def test_denoise_small_matches_oracle(cfg):
+    case = Case(cfg)
+    ex = _expert(case)
+    B = cfg.max_batch
+    noise = case.noise(B)
+    for steps in (1, cfg.steps):
+        got = ex.denoise(noise, steps)
+        ref = case.oracle_denoise(noise, steps)
+        err = rel_err(got, ref)
+        print(f"{cfg.name} B={B} steps={steps} rel_err={err:.3e}")
+        assert err <= tol_for(cfg), err
+    ex.close()
+
+
+@pytest.mark.parametrize("cfg", [SMALL_F32, SMALL_BF16, SMALL_FP8], ids=lambda c: c.name)
+def test_verify_small_matches_oracle(cfg):
+    case = Case(cfg)
+    ex = _expert(case)
+    for seed in range(4):
+        draft = G.make_draft(cfg, seed)
+        noise = case.noise(1, 300 + seed)[0]
+        taus = np.array([0.2, 0.5, 0.8], np.float32)
+        acc, sw, D = ex.verify(1, draft, noise, taus, 0.05)
+        acc_o, sw_o, D_o = case.oracle_verify(1, draft, noise, taus, 0.05)
+        assert sw == sw_o == seed % 2
+        assert acc == acc_o
+        assert rel_err(D, D_o) <= tol_for(cfg)
+    ex.close()
+
+
+def test_batched_robot_equals_robot_alone():
+    case = Case(SMALL_BF16)
+    ex = _expert(case)
+    noise = case.noise(3)
+    xb = ex.denoise(noise, 3)
+    # robot 0 alone shares slot 0 and its noise
+    x0 = ex.denoise(noise[:1], 3)
+    assert rel_err(x0[0], xb[0]) <= 1e-3
+    # repeated calls are bitwise reproducible (no float atomics anywhere)
+    assert np.array_equal(ex.denoise(noise, 3), xb)
+    ex.close()
+
+
+def test_zero_output_projection_gives_constant_velocity():
+    """W_out = 0, b_out = c: every Euler step adds dt * c, so x_N = x_0 + c for any N."""
+    cfg = SMALL_BF16
+    case = Case(cfg)
+    W = dict(case.W)
+    W["action_out_w"] = np.zeros_like(W["action_out_w"])
+    c = np.linspace(-1.0, 1.0, cfg.action_dim).astype(np.float32)
+    W["action_out_b"] = c
+    ex = ActionExpert(cfg, W)
+    for r in range(cfg.max_batch):
+        ex.load_prefix_kv(r, *case.kv[r])
+    noise = case.noise(2)
+    for steps in (1, 4, 10):
+        x = ex.denoise(noise, steps)
+        assert np.allclose(x, noise + c[None, None, :], atol=2e-6), steps
+    ex.close()
+
+
+def test_verify_closed_form_exact_endpoint():
+    """v = c everywhere (W_out = 0): with noise = d0 - c the rebuilt endpoints equal d0,
+    so a draft d0 + p (p = 0 before row k, |p| = 1 from row k) has D[j,i] = (1 - tau_j)|p_i|
+    and the accepted length is exactly k; a gripper switch forces 0."""
+    cfg = SMALL_BF16
+    case = Case(cfg)
+    W = dict(case.W)
+    W["action_out_w"] = np.zeros_like(W["action_out_w"])
+    c = np.linspace(-0.5, 0.5, cfg.action_dim).astype(np.float32)
+    W["action_out_b"] = c
+    ex = ActionExpert(cfg, W)
+    ex.load_prefix_kv(0, *case.kv[0])
+    H, A = cfg.horizon, cfg.action_dim
+    rng = np.random.default_rng(0)
+    d0 = rng.standard_normal((H, A)).astype(np.float32)
+    d0[:, cfg.gripper_dim] = 1.0
+    noise = (d0 - c[None, :]).astype(np.float32)
+    taus = np.array([0.2, 0.5, 0.8], np.float32)
+    for k in (0, 1, 7, H):
+        d = d0.copy()
+        d[k:, 0] += 1.0
+        acc, sw, D = ex.verify(0, d, noise, taus, 0.05)
+        assert (acc, sw) == (k, 0)
+        expect = (1.0 - taus[:, None]) * np.where(np.arange(H) >= k, 1.0, 0.0)[None, :]
+        assert np.allclose(D, expect, atol=1e-5)
+    d = d0.copy()
+    d[5:, cfg.gripper_dim] = -1.0
+    noise_g = (d - c[None, :]).astype(np.float32)
+    acc, sw, D = ex.verify(0, d, noise_g, taus, 0.05)
+    assert (acc, sw) == (0, 1) and np.max(D) < 1e-5
+    ex.close()
+
+
+def test_error_codes():
+    cfg = SMALL_BF16
+    case = Case(cfg)
+    ex = ActionExpert(cfg, case.W)
+    noise = case.noise(1)
+    with pytest.raises(AEError) as e:
+        ex.denoise(noise, 3)  # slot 0 not loaded
+    assert e.value.code == -3
+    ex.load_prefix_kv(0, *case.kv[0])
+    with pytest.raises(AEError) as e:
+        ex.denoise(np.zeros((4, cfg.horizon, cfg.action_dim), np.float32), 3)  # batch > max_batch
+    assert e.value.code == -1
+    with pytest.raises(AEError) as e:
+        ex.verify(0, noise[0], noise[0], np.zeros(4, np.float32), 0.05)  # n_tau > max_taus
+    assert e.value.code == -1
+    with pytest.raises(AEError) as e:
+        ex.load_prefix_kv(5, *case.kv[0])
+    assert e.value.code == -1
+    ex.close()
+
+
+# ------------------------------------------------------------------ full Pi0-scale shapes
+
+@pytest.fixture(scope="module")
+def pi0_case():
+    return Case(C.PI0_BATCH16, n_slots=16)
+
+
+def test_pi0_bf16_denoise_full(pi0_case):
+    cfg = C.PI0
+    ex = ActionExpert(cfg, pi0_case.W)
+    ex.load_prefix_kv(0, *pi0_case.kv[0])
+    noise = pi0_case.noise(1)
+    got = ex.denoise(noise, 10)
+    ref = pi0_case.oracle_denoise(noise, 10)
+    err = rel_err(got, ref)
+    print(f"pi0 bf16 10 steps rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+    assert err <= 2e-2
+    ex.close()
+
+
+def test_pi0_fp8_mlp_two_view_full():
+    cfg = C.PI0_FP8
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(1)
+    got = ex.denoise(noise, 10)
+    ref = case.oracle_denoise(noise, 10)
+    err = rel_err(got, ref)
+    print(f"pi0 fp8 10 steps rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+    assert err <= 6e-2
+    ex.close()
+
+
+def test_pi0_verify_full(pi0_case):
+    cfg = C.PI0_VERIFY
+    ex = ActionExpert(cfg, pi0_case.W)
+    ex.load_prefix_kv(0, *pi0_case.kv[0])
+    taus = np.asarray(C.VERIFY_TAUS, np.float32)
+    margins = []
+    for seed in range(16):
+        draft, noise, _ = G.make_verify_case(cfg, seed)
+        acc, sw, D = ex.verify(0, draft, noise, taus, C.VERIFY_DELTA)
+        acc_o, sw_o, D_o = pi0_case.oracle_verify(0, draft, noise, taus, C.VERIFY_DELTA, cfg)
+        assert (acc, sw) == (acc_o, sw_o), seed
+        assert sw == seed % 2
+        err = rel_err(D, D_o)
+        assert err <= 2e-2, (seed, err)
+        # delta-midpoint sweep: running max of D over rows; accept = k for delta between maxima k-1 and k
+        if sw == 0:
+            run = np.maximum.accumulate(D_o.max(axis=0))
+            for k in range(1, cfg.horizon):
+                gap = run[k] - run[k - 1]
+                if gap > 0.2 * run[k]:   # keep decisions far from the float tolerance
+                    delta = float(0.5 * (run[k] + run[k - 1]))
+                    acc_k, _, _ = ex.verify(0, draft, noise, taus, delta)
+                    assert O.accept_from_distances(D_o, delta, 0) == k
+                    assert acc_k == k, (seed, k, acc_k)
+                    margins.append(k)
+    print("nontrivial accept lengths checked:", sorted(set(margins)))
+    ex.close()
+
+
+def test_pi0_batch16_sampled_robots(pi0_case):
+    cfg = C.PI0_BATCH16
+    ex = _expert(pi0_case, slots=16)
+    noise = pi0_case.noise(16)
+    got = ex.denoise(noise, 10)
+    robots = [0, 7, 15]
+    ref = pi0_case.oracle_denoise(noise, 10, robots)
+    for i, r in enumerate(robots):
+        err = rel_err(got[r], ref[i])
+        print(f"batch16 robot {r} rel_err={err:.3e}")
+        assert err <= 2e-2
+    ex.close()
