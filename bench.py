@@ -79,7 +79,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=15)
     ap.add_argument("--config", default="pi0_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-iters", type=int, default=3)
+    ap.add_argument("--kernel-iters", type=int, default=3, help="replays of each per-kernel timing graph")
+    ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel timing pass")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no multi-GPU leg)",
@@ -103,8 +104,9 @@ def main():
         ex.load_prefix_kv(r, *kvs[r])
     d_noise = torch.from_numpy(noise).cuda()
     d_out = torch.empty_like(d_noise)
-    stream = torch.cuda.current_stream()
+    stream = torch.cuda.Stream()  # the library enqueues on this stream; the events below bracket it
     sp = stream.cuda_stream
+    torch.cuda.synchronize()
     print(f"setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
     for _ in range(args.warmup):
@@ -124,22 +126,31 @@ def main():
     out = d_out.cpu().numpy()
     assert np.all(np.isfinite(out))
 
-    # per-kernel HIP-event timing on the library's stream (eager launches of the same kernels)
-    stats = ex.kernel_times(0, B, cfg.steps, args.kernel_iters)
+    # Per-kernel timing on the library's stream. "in place": the chunk's launches in their
+    # normal order, each with a HIP start/stop event pair bound to its dispatch, so a kernel is
+    # timed in the cache state the whole chunk gives it (weights streamed from HBM); this is the
+    # figure the roofline uses. "isolated": every launch of one kernel back to back in a graph of
+    # its own (one kernel's weights for all layers may then stay in the 256 MB MALL).
     kb = kernel_bytes(cfg)
     kernels = {}
-    for name, launches, total in stats:
-        avg_us = total * 1e3 / launches
-        entry = {"launches_per_chunk": launches // args.kernel_iters, "avg_us": round(avg_us, 3),
-                 "ms_per_chunk": round(total / args.kernel_iters, 4)}
-        if name in kb:
-            per_launch = kb[name] * (B if name == "attn" else 1)
-            entry["alg_bytes"] = per_launch
-            entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
-        kernels[name] = entry
-    dom = max(kernels, key=lambda n: kernels[n]["ms_per_chunk"])
+    if not args.no_kernel_times:
+        iso = {n: (l, t) for n, l, t in ex.kernel_times(0, B, cfg.steps, args.kernel_iters)}
+        for name, launches, total in ex.kernel_times(2, B, cfg.steps, args.kernel_iters):
+            if launches == 0:
+                continue
+            avg_us = total * 1e3 / launches
+            entry = {"launches_per_chunk": launches // args.kernel_iters, "avg_us": round(avg_us, 3),
+                     "ms_per_chunk": round(total / args.kernel_iters, 4)}
+            if name in iso and iso[name][0]:
+                entry["isolated_avg_us"] = round(iso[name][1] * 1e3 / iso[name][0], 3)
+            if name in kb:
+                per_launch = kb[name] * (B if name == "attn" else 1)
+                entry["alg_bytes"] = per_launch
+                entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+            kernels[name] = entry
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_chunk"]) if kernels else None
     sb = step_bytes(cfg, B)
-    achieved = kernels[dom].get("GBs")
+    achieved = kernels[dom].get("GBs") if dom else None
     result = {
         "metric": "ms per 10-step action chunk & denoise steps/s (Pi0-scale expert, bs1)",
         "value": round(args.steps * cfg.steps / elapsed, 2),

@@ -7,6 +7,7 @@
 // 6.5: static buffers, fixed step count, one replay per request). Graphs are
 // cached per (mode, steps or n_tau, batch).
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <algorithm>
 #include <cmath>
@@ -27,17 +28,51 @@ namespace {
 
 thread_local std::string g_create_error;
 
-struct Timer {  // per-launch HIP events for ae_kernel_times
-  hipStream_t stream;
-  std::vector<std::pair<std::string, std::pair<hipEvent_t, hipEvent_t>>> rec;
-  void begin(const char* name) {
-    hipEvent_t a, b;
-    (void)hipEventCreate(&a);
-    (void)hipEventCreate(&b);
-    (void)hipEventRecord(a, stream);
-    rec.push_back({name, {a, b}});
+// Dispatch-bound timing events: when `start` is set, the next AE_LAUNCH binds
+// this pair to its dispatch (hipExtLaunchKernel records the kernel's own start
+// and end) and clears it.
+struct DispatchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+thread_local DispatchEvents t_dispatch_ev;
+
+#define AE_LAUNCH(kernel, grid, block, lds, st, ...)                                               \
+  do {                                                                                             \
+    if (t_dispatch_ev.start) {                                                                     \
+      hipExtLaunchKernelGGL(kernel, grid, block, (std::uint32_t)(lds), st, t_dispatch_ev.start,    \
+                            t_dispatch_ev.stop, 0, __VA_ARGS__);                                   \
+      t_dispatch_ev = DispatchEvents{};                                                            \
+    } else {                                                                                       \
+      hipLaunchKernelGGL(kernel, grid, block, lds, st, __VA_ARGS__);                               \
+    }                                                                                              \
+  } while (0)
+
+// Kernel filter and per-dispatch timing for ae_kernel_times. An enqueue pass
+// launches only the kernels named `only` (all of them when empty) and records
+// the names it meets; with `pairs` set, every launch gets the next event pair.
+struct Timer {
+  std::string only;
+  int count = 0;
+  std::vector<std::string> seen;
+  std::vector<hipEvent_t>* pairs = nullptr;  // 2 per launch: start, stop
+  std::vector<std::string> launched;         // name of each timed launch, in order
+  bool overflow = false;
+  bool take(const char* name) {
+    if (std::find(seen.begin(), seen.end(), name) == seen.end()) seen.push_back(name);
+    if (!only.empty() && only != name) return false;
+    ++count;
+    if (pairs) {
+      size_t i = launched.size();
+      if (2 * i + 1 < pairs->size()) {
+        t_dispatch_ev.start = (*pairs)[2 * i];
+        t_dispatch_ev.stop = (*pairs)[2 * i + 1];
+        launched.push_back(name);
+      } else {
+        overflow = true;
+      }
+    }
+    return true;
   }
-  void end() { (void)hipEventRecord(rec.back().second.second, stream); }
 };
 
 size_t dtype_size(int dt) { return dt == AE_F32 ? 4 : dt == AE_BF16 ? 2 : 1; }
@@ -77,9 +112,14 @@ struct ae_handle {
   unsigned* counters = nullptr;
   size_t n_counters = 0;
   float *opart = nullptr, *mlpart = nullptr;
+  unsigned *qt_counter = nullptr, *err_flag = nullptr;
+  void* vsT = nullptr;       // suffix values transposed [seq][n_kv][dh][ld_vt]
+  int ld_vt = 0, ld_p = 0;   // padded key strides of the transposed suffix / prefix V
+  int n_cu = 0;
   float* rope_cs = nullptr;
   void *kcache = nullptr, *vcache = nullptr;
-  size_t slot_elems = 0;
+  size_t slot_elems = 0;     // elements of one slot's K cache (= V cache without padding)
+  size_t vslot_elems = 0;    // elements of one slot's transposed V cache
   std::vector<int> slot_ready;
   int *denoise_slots = nullptr, *verify_slots = nullptr;
   // verify inputs / outputs
@@ -158,8 +198,10 @@ int validate(const ae_config* c, const ae_weights* w) {
   if (c->gripper_dim >= c->action_dim || c->gripper_dim < -1) return fail(nullptr, AE_ERR_INVALID_ARG, "gripper_dim out of range");
   for (int d : {c->weight_dtype, c->mlp_dtype, c->kv_dtype})
     if (d != AE_F32 && d != AE_BF16 && d != AE_FP8_E4M3) return fail(nullptr, AE_ERR_INVALID_ARG, "unknown dtype");
-  if (c->width % 64 || c->head_dim % 32 || c->mlp_dim % 32 || c->head_dim > 256)
-    return fail(nullptr, AE_ERR_UNSUPPORTED, "width must be a multiple of 64, head_dim of 32 (<= 256), mlp_dim of 32");
+  if (c->width % 256 || (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) ||
+      c->mlp_dim % 256 || (c->n_q_heads * c->head_dim) % 256)
+    return fail(nullptr, AE_ERR_UNSUPPORTED,
+                "width, mlp_dim and n_q_heads*head_dim must be multiples of 256; head_dim one of 32, 64, 128, 256");
   if (c->action_dim > 64 || c->horizon > 256) return fail(nullptr, AE_ERR_UNSUPPORTED, "action_dim <= 64 and horizon <= 256");
   if (c->weight_dtype == AE_FP8_E4M3) return fail(nullptr, AE_ERR_UNSUPPORTED, "fp8 is supported for the MLP only");
   if (c->kv_dtype != c->weight_dtype) return fail(nullptr, AE_ERR_UNSUPPORTED, "kv_dtype must equal weight_dtype");
@@ -182,70 +224,130 @@ int validate(const ae_config* c, const ae_weights* w) {
 
 PhaseCfg pick(int KB, int want, int n_z) {
   int S = n_z == 1 ? want : 1;
-  while (S > 1 && (KB % S)) --S;
+  while (S > 1 && (KB % S || (KB / S) % GW)) --S;
   return {S};
 }
 
-template <int WT, int AT, int EPI, int NT>
-hipError_t launch_gemm(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
-  size_t lds = (size_t)(5 * NT * TOKG * 16 + TOKG) * sizeof(float);
-  constexpr int KBW = AT == AT_F32 ? 4 : 8;
-  hipLaunchKernelGGL((gemm_kernel<WT, AT, EPI, NT, KBW>), dim3(n_groups, a.S, n_z), dim3(256), lds, st, a);
+template <int WT, int AT, int ROLE, int KPW>
+hipError_t launch_gemm_k(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+  constexpr size_t lds = gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>();
+  AE_LAUNCH((gemm_entry<ROLE, WT, AT, KPW>()), dim3(n_groups, a.S, n_z), dim3(GTHREADS), lds, st, a);
   return hipGetLastError();
+}
+
+// Pick k-blocks per wave per pass (largest of 4, 2, 1 dividing the split) and launch.
+template <int WT, int AT, int ROLE>
+hipError_t launch_gemm(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+  const int kb_split = a.K / KBLK / a.S;
+  if constexpr (AT == AT_BF16) {  // fp32 staging of 4 k-blocks per wave would not fit in LDS
+    if (kb_split % (GW * 4) == 0) { a.passes = kb_split / (GW * 4); return launch_gemm_k<WT, AT, ROLE, 4>(a, n_groups, n_z, st); }
+  }
+  if (kb_split % (GW * 2) == 0) { a.passes = kb_split / (GW * 2); return launch_gemm_k<WT, AT, ROLE, 2>(a, n_groups, n_z, st); }
+  a.passes = kb_split / GW;
+  return launch_gemm_k<WT, AT, ROLE, 1>(a, n_groups, n_z, st);
+}
+
+template <int WT, int AT, int ROLE, int KPW>
+hipError_t set_gemm_attr_k() {
+  return hipFuncSetAttribute((const void*)gemm_entry<ROLE, WT, AT, KPW>(), hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>());
+}
+template <int WT, int AT, int ROLE>
+hipError_t set_gemm_attr() {
+  hipError_t e = hipSuccess;
+  if constexpr (AT == AT_BF16) e = set_gemm_attr_k<WT, AT, ROLE, 4>();
+  if (e == hipSuccess) e = set_gemm_attr_k<WT, AT, ROLE, 2>();
+  if (e == hipSuccess) e = set_gemm_attr_k<WT, AT, ROLE, 1>();
+  return e;
+}
+hipError_t set_all_gemm_attrs() {
+  hipError_t e = hipSuccess;
+  auto acc = [&](hipError_t r) { if (e == hipSuccess) e = r; };
+  acc(set_gemm_attr<WT_F32, AT_F32, R_QKV_ROPE>()); acc(set_gemm_attr<WT_F32, AT_F32, R_O_PROJ>());
+  acc(set_gemm_attr<WT_F32, AT_F32, R_GATE_UP>()); acc(set_gemm_attr<WT_F32, AT_F32, R_DOWN>());
+  acc(set_gemm_attr<WT_F32, AT_F32, R_OUT_PROJ>());
+  acc(set_gemm_attr<WT_BF16, AT_BF16, R_QKV_ROPE>()); acc(set_gemm_attr<WT_BF16, AT_BF16, R_O_PROJ>());
+  acc(set_gemm_attr<WT_BF16, AT_BF16, R_GATE_UP>()); acc(set_gemm_attr<WT_BF16, AT_BF16, R_DOWN>());
+  acc(set_gemm_attr<WT_BF16, AT_BF16, R_OUT_PROJ>());
+  acc(set_gemm_attr<WT_FP8, AT_BF16, R_GATE_UP>()); acc(set_gemm_attr<WT_FP8, AT_BF16, R_DOWN>());
+  return e;
 }
 
 // k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group;
 // AE_SPLITS="q,o,g,d,u" overrides them for tuning.
 struct Splits {
-  int qkv = 1, o = 2, gu = 1, down = 4, out = 1;
+  int qkv = 1, o = 2, gu = 1, down = 2, out = 1;
   Splits() {
     if (const char* e = getenv("AE_SPLITS")) sscanf(e, "%d,%d,%d,%d,%d", &qkv, &o, &gu, &down, &out);
   }
 };
 const Splits& splits() { static Splits s; return s; }
 
+// Attention kernels are instantiated per (activation type, key chunk, head_dim).
+template <int AT, int KC>
+hipError_t attn_dispatch(int dh, bool set_attr, size_t lds, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  const void* fn = nullptr;
+  switch (dh) {
+    case 32: fn = (const void*)attn_kernel<AT, KC, 32>; break;
+    case 64: fn = (const void*)attn_kernel<AT, KC, 64>; break;
+    case 128: fn = (const void*)attn_kernel<AT, KC, 128>; break;
+    case 256: fn = (const void*)attn_kernel<AT, KC, 256>; break;
+    default: return hipErrorInvalidValue;
+  }
+  if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  switch (dh) {
+    case 32: AE_LAUNCH((attn_kernel<AT, KC, 32>), grid, dim3(256), lds, st, aa); break;
+    case 64: AE_LAUNCH((attn_kernel<AT, KC, 64>), grid, dim3(256), lds, st, aa); break;
+    case 128: AE_LAUNCH((attn_kernel<AT, KC, 128>), grid, dim3(256), lds, st, aa); break;
+    default: AE_LAUNCH((attn_kernel<AT, KC, 256>), grid, dim3(256), lds, st, aa); break;
+  }
+  return hipGetLastError();
+}
+
 template <int AT>
-hipError_t set_attrs(size_t bytes) {
-  return hipFuncSetAttribute((const void*)attn_kernel<AT>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+hipError_t set_attrs(size_t bytes, int dh) {
+  return AT == AT_BF16 ? attn_dispatch<AT_BF16, 64>(dh, true, bytes, dim3(), nullptr, AttnArgs{})
+                       : attn_dispatch<AT_F32, 32>(dh, true, bytes, dim3(), nullptr, AttnArgs{});
 }
 
 size_t attn_lds_bytes(int at, int dh) {
   const int KC = at == AT_BF16 ? 64 : 32, pad = at == AT_BF16 ? 8 : 4;
   const size_t es = at == AT_BF16 ? 2 : 4;
-  return ((size_t)KC * (dh + pad) + (size_t)dh * (KC + pad) + 64 * (size_t)(KC + pad)) * es;
+  return ((size_t)KC * (dh + pad) + (size_t)dh * (KC + pad)) * es + 16;
 }
 
 struct Dispatch {
-  // one launcher per (phase) bound to the handle's dtypes
-  static hipError_t gemm(ae_handle* h, int epi, bool mlp, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+  // one launcher per role bound to the handle's dtypes (fp8 weights: MLP roles only)
+  static hipError_t gemm(ae_handle* h, int role, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
     if (h->at == AT_F32) {
-      switch (epi) {
-        case EPI_QKV: return launch_gemm<WT_F32, AT_F32, EPI_QKV, 1>(a, n_groups, n_z, st);
-        case EPI_RESID: return launch_gemm<WT_F32, AT_F32, EPI_RESID, 1>(a, n_groups, n_z, st);
-        case EPI_GEGLU: return launch_gemm<WT_F32, AT_F32, EPI_GEGLU, 2>(a, n_groups, n_z, st);
-        default: return launch_gemm<WT_F32, AT_F32, EPI_OUT, 1>(a, n_groups, n_z, st);
+      switch (role) {
+        case R_QKV_ROPE: return launch_gemm<WT_F32, AT_F32, R_QKV_ROPE>(a, n_groups, n_z, st);
+        case R_O_PROJ: return launch_gemm<WT_F32, AT_F32, R_O_PROJ>(a, n_groups, n_z, st);
+        case R_GATE_UP: return launch_gemm<WT_F32, AT_F32, R_GATE_UP>(a, n_groups, n_z, st);
+        case R_DOWN: return launch_gemm<WT_F32, AT_F32, R_DOWN>(a, n_groups, n_z, st);
+        default: return launch_gemm<WT_F32, AT_F32, R_OUT_PROJ>(a, n_groups, n_z, st);
       }
     }
-    if (mlp && h->mt == WT_FP8) {
-      if (epi == EPI_GEGLU) return launch_gemm<WT_FP8, AT_BF16, EPI_GEGLU, 2>(a, n_groups, n_z, st);
-      return launch_gemm<WT_FP8, AT_BF16, EPI_RESID, 1>(a, n_groups, n_z, st);
-    }
-    switch (epi) {
-      case EPI_QKV: return launch_gemm<WT_BF16, AT_BF16, EPI_QKV, 1>(a, n_groups, n_z, st);
-      case EPI_RESID: return launch_gemm<WT_BF16, AT_BF16, EPI_RESID, 1>(a, n_groups, n_z, st);
-      case EPI_GEGLU: return launch_gemm<WT_BF16, AT_BF16, EPI_GEGLU, 2>(a, n_groups, n_z, st);
-      default: return launch_gemm<WT_BF16, AT_BF16, EPI_OUT, 1>(a, n_groups, n_z, st);
+    if (h->mt == WT_FP8 && role == R_GATE_UP) return launch_gemm<WT_FP8, AT_BF16, R_GATE_UP>(a, n_groups, n_z, st);
+    if (h->mt == WT_FP8 && role == R_DOWN) return launch_gemm<WT_FP8, AT_BF16, R_DOWN>(a, n_groups, n_z, st);
+    switch (role) {
+      case R_QKV_ROPE: return launch_gemm<WT_BF16, AT_BF16, R_QKV_ROPE>(a, n_groups, n_z, st);
+      case R_O_PROJ: return launch_gemm<WT_BF16, AT_BF16, R_O_PROJ>(a, n_groups, n_z, st);
+      case R_GATE_UP: return launch_gemm<WT_BF16, AT_BF16, R_GATE_UP>(a, n_groups, n_z, st);
+      case R_DOWN: return launch_gemm<WT_BF16, AT_BF16, R_DOWN>(a, n_groups, n_z, st);
+      default: return launch_gemm<WT_BF16, AT_BF16, R_OUT_PROJ>(a, n_groups, n_z, st);
     }
   }
 };
 
 #define LAUNCH_CHECK(h, name, expr)                                                          \
   do {                                                                                       \
-    if (tm) tm->begin(name);                                                                 \
-    expr;                                                                                    \
-    if (tm) tm->end();                                                                       \
-    hipError_t e_ = hipGetLastError();                                                       \
-    if (e_ != hipSuccess) return fail(h, AE_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e_)); \
+    if (!tm || tm->take(name)) {                                                             \
+      expr;                                                                                  \
+      hipError_t e_ = hipGetLastError();                                                     \
+      if (e_ != hipSuccess) return fail(h, AE_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e_)); \
+      t_dispatch_ev = DispatchEvents{};                                                      \
+    }                                                                                        \
   } while (0)
 
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
@@ -255,27 +357,35 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
-  const int M = n_seq * H, Mp = (M + 15) / 16 * 16, n_z = (Mp + TOKG - 1) / TOKG;
+  const int M = n_seq * H, Mp = (M + TOKG - 1) / TOKG * TOKG, n_z = Mp / TOKG;
 
   LAUNCH_CHECK(h, "in_proj", {
     if (h->at == AT_F32)
-      hipLaunchKernelGGL((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
+      AE_LAUNCH((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
                          h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
     else
-      hipLaunchKernelGGL((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
+      AE_LAUNCH((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
                          h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
   });
 
   const int gq = nq / nkv, R = gq * H;
   const int KC = h->at == AT_BF16 ? 64 : 32;
   AttnArgs aa{};
-  aa.q = h->q; aa.ks = h->sk; aa.vs = h->sv; aa.kcache = h->kcache; aa.vcache = h->vcache;
-  aa.seq_slot = seq_slot; aa.slot_stride = h->slot_elems;
+  aa.q = h->q; aa.ks = h->sk; aa.vsT = h->vsT; aa.kcache = h->kcache; aa.vcacheT = h->vcache;
+  aa.seq_slot = seq_slot;
+  aa.kslot_stride = h->slot_elems; aa.vslot_stride = h->vslot_elems;
   aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh; aa.KC = KC;
-  aa.ldq = h->ld_q; aa.ldkv = h->ld_kv; aa.ldo = h->ld_q;
+  aa.ldq = h->ld_q; aa.ldkv = h->ld_kv; aa.ldvt = h->ld_vt; aa.ldp = h->ld_p; aa.ldo = h->ld_q;
   aa.n_qt = (R + 63) / 64; aa.n_chunks = (c.prefix_len + H + KC - 1) / KC;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
-  aa.opart = h->opart; aa.mlpart = h->mlpart;
+  aa.opart = h->opart; aa.mlpart = h->mlpart; aa.qt_counter = h->qt_counter; aa.err = h->err_flag; aa.o = h->o;
+  const int attn_wgs = aa.n_chunks * aa.n_qt * n_seq * nkv;
+  aa.trace_id = 1;
+  aa.p_aligned = (c.prefix_len % (h->at == AT_BF16 ? 8 : 4)) == 0;
+  // In-kernel combine (AE_ATTN_FUSED=1) only when every workgroup is co-resident, so the wait is
+  // safe; measured slower than a separate combine launch on MI355X, hence off by default.
+  aa.fused = 0;
+  if (const char* e = getenv("AE_ATTN_FUSED")) aa.fused = (attn_wgs <= h->n_cu && atoi(e) != 0) ? 1 : 0;
   const size_t attn_lds = attn_lds_bytes(h->at, dh);
 
   for (int l = 0; l < c.n_layers; ++l) {
@@ -288,31 +398,35 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->qkv_p[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_q; a.ldkv = h->ld_kv;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().qkv, n_z).S;
-      a.q_out = h->q; a.k_out = h->sk; a.v_out = h->sv; a.rope_cs = h->rope_cs;
+      a.q_out = h->q; a.k_out = h->sk; a.v_out = h->vsT; a.ldvt = h->ld_vt; a.rope_cs = h->rope_cs;
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
-      LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, EPI_QKV, false, a, h->qkv_tiles, n_z, st));
+      a.trace_id = 0;
+      LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
     // --- attention over [prefix ; suffix]
-    aa.layer_off = (size_t)l * c.prefix_len * nkv * dh;
+    aa.klayer_off = (size_t)l * c.prefix_len * nkv * dh;
+    aa.vlayer_off = (size_t)l * nkv * dh * h->ld_p;
+    const dim3 attn_grid(aa.n_chunks, aa.n_qt, n_seq * nkv);
     LAUNCH_CHECK(h, "attn", {
-      if (h->at == AT_BF16)
-        hipLaunchKernelGGL(attn_kernel<AT_BF16>, dim3(aa.n_chunks, aa.n_qt, n_seq * nkv), dim3(256), attn_lds, st, aa);
-      else
-        hipLaunchKernelGGL(attn_kernel<AT_F32>, dim3(aa.n_chunks, aa.n_qt, n_seq * nkv), dim3(256), attn_lds, st, aa);
+      if (h->at == AT_BF16) (void)(attn_dispatch<AT_BF16, 64>)(dh, false, attn_lds, attn_grid, st, aa);
+      else (void)(attn_dispatch<AT_F32, 32>)(dh, false, attn_lds, attn_grid, st, aa);
     });
-    LAUNCH_CHECK(h, "attn_combine", {
-      if (h->at == AT_BF16)
-        hipLaunchKernelGGL(attn_combine<AT_BF16>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa, h->o);
-      else
-        hipLaunchKernelGGL(attn_combine<AT_F32>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa, h->o);
-    });
+    if (!aa.fused) {
+      LAUNCH_CHECK(h, "attn_combine", {
+        if (h->at == AT_BF16)
+          AE_LAUNCH(attn_combine<AT_BF16>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa);
+        else
+          AE_LAUNCH(attn_combine<AT_F32>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa);
+      });
+    }
     // --- o_proj + residual; hb <- h * ln2
     {
       GemmArgs a = g;
       a.w = h->o_p[l]; a.x = h->o; a.ldx = h->ld_q; a.ldo = h->ld_h; a.ssp_in = nullptr; a.K = nq * dh;
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
-      LAUNCH_CHECK(h, "o_proj_resid", (void)Dispatch::gemm(h, EPI_RESID, false, a, w / 16, n_z, st));
+      a.trace_id = 2;
+      LAUNCH_CHECK(h, "o_proj_resid", (void)Dispatch::gemm(h, R_O_PROJ, a, w / 16, n_z, st));
     }
     // --- norm2 + gate/up + GeGLU
     {
@@ -320,7 +434,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_u;
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
-      LAUNCH_CHECK(h, "gate_up_geglu", (void)Dispatch::gemm(h, EPI_GEGLU, true, a, h->gu_tiles / 2, n_z, st));
+      a.trace_id = 3;
+      LAUNCH_CHECK(h, "gate_up_geglu", (void)Dispatch::gemm(h, R_GATE_UP, a, h->gu_tiles / 2, n_z, st));
     }
     // --- down + residual; hb <- h * next gain
     {
@@ -329,7 +444,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.S = pick(F / 32, splits().down, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
       a.ssp_out = h->ssp_a; a.N = w;
-      LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, EPI_RESID, true, a, w / 16, n_z, st));
+      a.trace_id = 4;
+      LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, R_DOWN, a, w / 16, n_z, st));
     }
   }
   // --- final norm + action_out_proj (+ Euler update)
@@ -340,7 +456,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.w = h->action_out_p; a.x = h->hb; a.ldx = h->ld_h; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, splits().out, n_z).S;
     a.bias = h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
-    LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, EPI_OUT, false, a, h->out_tiles, n_z, st));
+    a.trace_id = 5;
+    LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, R_OUT_PROJ, a, h->out_tiles, n_z, st));
   }
   return AE_OK;
 }
@@ -348,16 +465,14 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
 // temb for n_t times in device array t_dev -> out [n_t][width].
 int enqueue_temb(ae_handle* h, const float* t_dev, int n_t, float* out, hipStream_t st, Timer* tm) {
   const int w = h->c.width;
-  LAUNCH_CHECK(h, "time_sinusoid", hipLaunchKernelGGL(sinusoid_kernel, dim3(std::max(1, w / 2 / 256), n_t), dim3(256), 0, st, t_dev, w, h->phi));
-  LAUNCH_CHECK(h, "time_mlp", {
-    if (h->at == AT_F32) {
-      hipLaunchKernelGGL(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid);
-      hipLaunchKernelGGL(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out);
-    } else {
-      hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid);
-      hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out);
-    }
-  });
+  LAUNCH_CHECK(h, "time_sinusoid", AE_LAUNCH(sinusoid_kernel, dim3(std::max(1, w / 2 / 256), n_t), dim3(256), 0, st, t_dev, w, h->phi));
+  if (h->at == AT_F32) {
+    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid));
+    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out));
+  } else {
+    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid));
+    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out));
+  }
   return AE_OK;
 }
 
@@ -399,13 +514,13 @@ int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t
 int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim;
-  LAUNCH_CHECK(h, "verify_interp", hipLaunchKernelGGL(interp_kernel, dim3((n_tau * H * A + 255) / 256), dim3(256), 0, st,
+  LAUNCH_CHECK(h, "verify_interp", AE_LAUNCH(interp_kernel, dim3((n_tau * H * A + 255) / 256), dim3(256), 0, st,
                                                       h->draft, h->vnoise, h->taus, n_tau, H, A, h->x));
   int rc = enqueue_temb(h, h->taus, n_tau, h->temb_tau, st, tm);
   if (rc) return rc;
   rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0.f, st, tm);
   if (rc) return rc;
-  LAUNCH_CHECK(h, "verify_accept", hipLaunchKernelGGL(verify_kernel, dim3(1), dim3(256), (size_t)n_tau * H * sizeof(float), st,
+  LAUNCH_CHECK(h, "verify_accept", AE_LAUNCH(verify_kernel, dim3(1), dim3(256), (size_t)n_tau * H * sizeof(float), st,
                                                       h->x, h->vout, h->draft, h->taus, n_tau, H, A, h->params,
                                                       c.gripper_dim, h->dist, h->accept, h->gswitch));
   return AE_OK;
@@ -454,6 +569,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->c = *cfg;
   const ae_config& c = h->c;
   if (hipGetDevice(&h->dev) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipGetDevice failed"); }
+  if (hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->dev) != hipSuccess) h->n_cu = 0;
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
   hipEventCreate(&h->ev0);
   hipEventCreate(&h->ev1);
@@ -461,7 +577,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->wt = c.weight_dtype == AE_F32 ? WT_F32 : WT_BF16;
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
   const size_t lds_need = attn_lds_bytes(h->at, cfg->head_dim);
-  if ((h->at == AT_BF16 ? set_attrs<AT_BF16>(lds_need) : set_attrs<AT_F32>(lds_need)) != hipSuccess) {
+  if ((h->at == AT_BF16 ? set_attrs<AT_BF16>(lds_need, cfg->head_dim) : set_attrs<AT_F32>(lds_need, cfg->head_dim)) != hipSuccess ||
+      set_all_gemm_attrs() != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
     return fail(nullptr, AE_ERR_HIP, m);
@@ -472,7 +589,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   const size_t wes = dtype_size(c.weight_dtype), mes = dtype_size(c.mlp_dtype), kes = dtype_size(c.kv_dtype);
   const int aes = h->at == AT_F32 ? 4 : 2;
   h->M_max = std::max(c.max_batch, std::max(1, c.max_taus)) * H;
-  h->Mp_max = (h->M_max + 15) / 16 * 16;
+  h->Mp_max = (h->M_max + TOKG - 1) / TOKG * TOKG;
   const int Mp = h->Mp_max;
   std::string msg;
 #define TRY(x) do { int r_ = (x); if (r_) { msg = h->err; ae_destroy(h); return fail(nullptr, r_, msg); } } while (0)
@@ -566,7 +683,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc_t(h, &h->ssp_b, (size_t)(w / 16) * Mp));
   TRY(dalloc(h, &h->q, (size_t)Mp * h->ld_q * aes));
   TRY(dalloc(h, &h->sk, (size_t)Mp * h->ld_kv * aes));
-  TRY(dalloc(h, &h->sv, (size_t)Mp * h->ld_kv * aes));
+  h->ld_vt = (H + 7) / 8 * 8;
+  TRY(dalloc(h, &h->vsT, (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv * dh * h->ld_vt * aes));
   TRY(dalloc(h, &h->o, (size_t)Mp * h->ld_q * aes));
   TRY(dalloc(h, &h->u, (size_t)Mp * h->ld_u * aes));
   {
@@ -582,6 +700,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     const size_t n_zz = (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv;
     TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_chunks * 64 * dh));
     TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_chunks * 64 * 2));
+    TRY(dalloc_t(h, &h->qt_counter, n_zz * n_qt));
+    TRY(dalloc_t(h, &h->err_flag, 1));
   }
   {
     std::vector<float> cs((size_t)H * (dh / 2) * 2);
@@ -594,8 +714,10 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(upload(h, (void**)&h->rope_cs, cs.data(), cs.size() * 4));
   }
   h->slot_elems = (size_t)L * P * nkv * dh;
+  h->ld_p = (P + 7) / 8 * 8;
+  h->vslot_elems = (size_t)L * nkv * dh * h->ld_p;
   TRY(dalloc(h, &h->kcache, h->slot_elems * c.max_batch * kes));
-  TRY(dalloc(h, &h->vcache, h->slot_elems * c.max_batch * kes));
+  TRY(dalloc(h, &h->vcache, h->vslot_elems * c.max_batch * kes));
   h->slot_ready.assign(c.max_batch, 0);
   {
     std::vector<int> ids(c.max_batch);
@@ -624,12 +746,34 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (!k || !v) return fail(h, AE_ERR_INVALID_ARG, "null cache pointer");
   if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
-  const size_t bytes = h->slot_elems * dtype_size(h->c.kv_dtype);
-  if (bytes) {
-    HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * bytes, k, bytes, hipMemcpyHostToDevice));
-    HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * bytes, v, bytes, hipMemcpyHostToDevice));
+  const ae_config& c = h->c;
+  const size_t es = dtype_size(c.kv_dtype);
+  const size_t kbytes = h->slot_elems * es;
+  if (kbytes) {
+    HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * kbytes, k, kbytes, hipMemcpyHostToDevice));
+    // V is kept transposed per layer and kv head: [L][n_kv][dh][ld_p], keys contiguous
+    const int L = c.n_layers, P = c.prefix_len, nkv = c.n_kv_heads, dh = c.head_dim, ldp = h->ld_p;
+    std::vector<unsigned char> vt(h->vslot_elems * es, 0);
+    const unsigned char* src = (const unsigned char*)v;
+    for (int l = 0; l < L; ++l)
+      for (int j = 0; j < P; ++j)
+        for (int g = 0; g < nkv; ++g)
+          for (int d = 0; d < dh; ++d)
+            memcpy(&vt[((((size_t)l * nkv + g) * dh + d) * ldp + j) * es], src + ((((size_t)l * P + j) * nkv + g) * dh + d) * es, es);
+    HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * vt.size(), vt.data(), vt.size(), hipMemcpyHostToDevice));
   }
   h->slot_ready[slot] = 1;
+  return AE_OK;
+}
+
+// A fused attention combine whose wait timed out (workgroups not co-resident) leaves a flag.
+static int check_err_flag(ae_handle* h) {
+  unsigned e = 0;
+  HIP_TRY(h, hipMemcpy(&e, h->err_flag, sizeof(e), hipMemcpyDeviceToHost));
+  if (e) {
+    HIP_TRY(h, hipMemset(h->err_flag, 0, sizeof(e)));
+    return fail(h, AE_ERR_HIP, "attention combine wait timed out");
+  }
   return AE_OK;
 }
 
@@ -673,6 +817,8 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  int rc2 = check_err_flag(h);
+  if (rc2) return rc2;
   memcpy(actions_out, tmp.data(), bytes);
   return AE_OK;
 }
@@ -740,6 +886,8 @@ int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, co
   HIP_TRY(h, hipMemcpyAsync(d.data(), h->dist, d.size() * sizeof(float), hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  int rc2 = check_err_flag(h);
+  if (rc2) return rc2;
   *accept_len = acc;
   *gripper_switch = sw;
   if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
@@ -765,9 +913,78 @@ int ae_last_gpu_ms(const ae_handle* h, float* ms) {
   return AE_OK;
 }
 
+}  // extern "C"
+
+namespace {
+// The pass launched eagerly in its normal order (so each kernel sees the cache
+// state and neighbours it has inside the graph), with a start/stop event pair
+// bound to every dispatch: the kernel's own execution time, summed per name
+// over `iters` passes.
+template <class Enq>
+int kernel_times_in_place(ae_handle* h, Enq& enqueue, const std::vector<std::string>& names, int iters,
+                          ae_kernel_stat* stats, int max_stats, int* n_stats) {
+  // count the pass's launches: a capture that is never instantiated
+  int n_launch = 0;
+  {
+    Timer probe;
+    HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+    int rc = enqueue(&probe);
+    hipGraph_t g0 = nullptr;
+    hipError_t e = hipStreamEndCapture(h->stream, &g0);
+    if (g0) hipGraphDestroy(g0);
+    if (rc) return rc;
+    if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("in-place timing (launch count): ") + hipGetErrorString(e));
+    n_launch = probe.count;
+  }
+  std::vector<hipEvent_t> ev;
+  auto cleanup = [&]() { for (hipEvent_t x : ev) hipEventDestroy(x); };
+  hipError_t e = hipSuccess;
+  ev.reserve(2 * (size_t)n_launch);
+  for (int i = 0; i < 2 * n_launch && e == hipSuccess; ++i) {
+    hipEvent_t x;
+    e = hipEventCreate(&x);
+    if (e == hipSuccess) ev.push_back(x);
+  }
+  if (e != hipSuccess) { cleanup(); return fail(h, AE_ERR_HIP, std::string("in-place timing events: ") + hipGetErrorString(e)); }
+  std::vector<double> tot(names.size(), 0.0);
+  std::vector<int> cnt(names.size(), 0);
+  for (int it = 0; it <= iters && e == hipSuccess; ++it) {  // pass 0 warms up
+    Timer tm;
+    tm.pairs = &ev;
+    int rc = enqueue(&tm);
+    t_dispatch_ev = DispatchEvents{};
+    if (rc) { hipStreamSynchronize(h->stream); cleanup(); return rc; }
+    if (tm.overflow) { hipStreamSynchronize(h->stream); cleanup(); return fail(h, AE_ERR_HIP, "in-place timing: launch count changed"); }
+    e = hipStreamSynchronize(h->stream);
+    for (size_t i = 0; i < tm.launched.size() && e == hipSuccess && it > 0; ++i) {
+      float ms = 0.f;
+      e = hipEventElapsedTime(&ms, ev[2 * i], ev[2 * i + 1]);
+      size_t k = std::find(names.begin(), names.end(), tm.launched[i]) - names.begin();
+      if (e == hipSuccess && k < names.size()) { tot[k] += ms; ++cnt[k]; }
+    }
+  }
+  cleanup();
+  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("in-place timing: ") + hipGetErrorString(e));
+  int n = 0;
+  for (size_t k = 0; k < names.size() && n < max_stats; ++k) {
+    memset(stats[n].name, 0, sizeof(stats[n].name));
+    strncpy(stats[n].name, names[k].c_str(), sizeof(stats[n].name) - 1);
+    stats[n].launches = cnt[k];
+    stats[n].total_ms = (float)tot[k];
+    ++n;
+  }
+  *n_stats = n;
+  return check_err_flag(h);
+}
+}  // namespace
+
+extern "C" {
+
 int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats, int max_stats,
                     int* n_stats) {
-  if (!h || !stats || !n_stats || iters < 1) return AE_ERR_INVALID_ARG;
+  if (!h || !stats || !n_stats || iters < 1 || mode < 0 || mode > 3) return AE_ERR_INVALID_ARG;
+  const bool in_place = (mode & 2) != 0;
+  mode &= 1;
   int rc;
   if (mode == 0) {
     rc = check_denoise(h, batch, steps);
@@ -778,36 +995,70 @@ int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_
   }
   float* temb = nullptr;
   if (mode == 0) { rc = get_temb_steps(h, steps, &temb); if (rc) return rc; }
-  Timer tm{h->stream, {}};
-  for (int it = 0; it < iters; ++it) {
-    rc = mode == 0 ? enqueue_denoise(h, batch, steps, temb, h->stream, &tm) : enqueue_verify(h, batch, h->stream, &tm);
-    if (rc) break;
-  }
-  hipError_t e = hipStreamSynchronize(h->stream);
+  auto enqueue = [&](Timer* tm) {
+    return mode == 0 ? enqueue_denoise(h, batch, steps, temb, h->stream, tm) : enqueue_verify(h, batch, h->stream, tm);
+  };
+  // kernel names in launch order: a pass under capture that launches nothing
   std::vector<std::string> names;
-  std::map<std::string, std::pair<int, float>> agg;
-  for (auto& r : tm.rec) {
-    float ms = 0.f;
-    if (e == hipSuccess) hipEventElapsedTime(&ms, r.second.first, r.second.second);
-    if (!agg.count(r.first)) names.push_back(r.first);
-    agg[r.first].first += 1;
-    agg[r.first].second += ms;
-    hipEventDestroy(r.second.first);
-    hipEventDestroy(r.second.second);
+  {
+    Timer probe;
+    probe.only = "\x01";
+    HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+    rc = enqueue(&probe);
+    hipGraph_t g0 = nullptr;
+    hipError_t e = hipStreamEndCapture(h->stream, &g0);
+    if (g0) hipGraphDestroy(g0);
+    if (rc) return rc;
+    if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing capture: ") + hipGetErrorString(e));
+    names = probe.seen;
   }
-  if (rc) return rc;
-  if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing: ") + hipGetErrorString(e));
+  if (in_place) return kernel_times_in_place(h, enqueue, names, iters, stats, max_stats, n_stats);
+  // per kernel: one graph holding every launch of that kernel in the pass, back to back,
+  // replayed `iters` times between two HIP events on the library's stream
   int n = 0;
-  for (auto& nm : names) {
+  for (const std::string& nm : names) {
     if (n >= max_stats) break;
+    Timer tm;
+    tm.only = nm;
+    HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+    rc = enqueue(&tm);
+    hipGraph_t g = nullptr;
+    hipError_t e = hipStreamEndCapture(h->stream, &g);
+    if (rc) { if (g) hipGraphDestroy(g); return rc; }
+    if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing capture: ") + hipGetErrorString(e));
+    hipGraphExec_t ge = nullptr;
+    e = hipGraphInstantiate(&ge, g, nullptr, nullptr, 0);
+    hipGraphDestroy(g);
+    if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing instantiate: ") + hipGetErrorString(e));
+    float ms = 0.f;
+    e = hipGraphLaunch(ge, h->stream);
+    if (e == hipSuccess) e = hipEventRecord(h->ev0, h->stream);
+    for (int it = 0; it < iters && e == hipSuccess; ++it) e = hipGraphLaunch(ge, h->stream);
+    if (e == hipSuccess) e = hipEventRecord(h->ev1, h->stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, h->ev0, h->ev1);
+    hipGraphExecDestroy(ge);
+    if (e != hipSuccess) return fail(h, AE_ERR_HIP, std::string("kernel timing: ") + hipGetErrorString(e));
     memset(stats[n].name, 0, sizeof(stats[n].name));
     strncpy(stats[n].name, nm.c_str(), sizeof(stats[n].name) - 1);
-    stats[n].launches = agg[nm].first;
-    stats[n].total_ms = agg[nm].second;
+    stats[n].launches = tm.count * iters;
+    stats[n].total_ms = ms;
     ++n;
   }
   *n_stats = n;
-  return AE_OK;
+  return check_err_flag(h);
 }
+
+#ifdef AE_TRACE
+// Debug export of the traced build only: copies the per-workgroup timestamps.
+int ae_debug_trace(unsigned long long* out) {
+  if (!out) return AE_ERR_INVALID_ARG;
+  return hipMemcpyFromSymbol(out, HIP_SYMBOL(ae_trace_buf), sizeof(unsigned long long) * 8 * 2048 * 8) == hipSuccess ? AE_OK : AE_ERR_HIP;
+}
+int ae_debug_trace_clear() {
+  static unsigned long long zeros[8][2048][8];
+  return hipMemcpyToSymbol(HIP_SYMBOL(ae_trace_buf), zeros, sizeof(zeros)) == hipSuccess ? AE_OK : AE_ERR_HIP;
+}
+#endif
 
 }  // extern "C"

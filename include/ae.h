@@ -169,11 +169,19 @@ const char* ae_last_error(const ae_handle* h);
  * measured with HIP events around the launch on the library's stream. */
 int ae_last_gpu_ms(const ae_handle* h, float* ms);
 
-/* Per-kernel timing. Runs one ae_denoise (mode 0, slots 0..batch-1, `steps`)
- * or one ae_verify pass (mode 1, slot 0, batch = n_tau) eagerly `iters`
- * times with HIP events around every kernel launch on the library's stream,
- * using the inputs of the last call of that mode. Writes up to max_stats
- * entries {kernel name, launches, total ms} and the number written to *n_stats. */
+/* Per-kernel timing of one ae_denoise pass (mode bit 0 clear: slots
+ * 0..batch-1, `steps` Euler steps) or one ae_verify pass (bit 0 set: the slot
+ * and inputs of the last ae_verify call, batch = n_tau).
+ *   bit 1 clear (isolated): for each kernel, a graph holding every launch of
+ *     that kernel in the pass, back to back, is replayed `iters` times between
+ *     two HIP events on the library's stream;
+ *   bit 1 set (in place): the pass is launched eagerly in its normal order,
+ *     `iters` times after one warm-up pass, with a start/stop event pair bound
+ *     to every dispatch (hipExtLaunchKernel), so each launch is timed by its
+ *     own execution in the cache state the full pass gives it.
+ * Writes up to max_stats entries {kernel name, launches (per pass x iters),
+ * total ms} in launch order and the number written to *n_stats. Leaves the
+ * activation buffers in an unspecified state (the next call reinitialises them). */
 typedef struct ae_kernel_stat {
   char name[48];
   int launches;
