@@ -3,7 +3,7 @@
 // One Euler step of the suffix (DM0.5 guide, sections 5.2-5.3) runs as:
 //   in_proj   : h = x W_in^T + b_in + temb(t)                      (tiny, FMA)
 //   per layer : qkv  = rmsnorm(h) W_qkv^T, RoPE on q/k             (qkv_rope_kernel)      
-//               attn = softmax(q [Kp;k]^T / sqrt(dh)) [Vp;v]        (attn_kernel + attn_combine)
+//               attn = softmax(q [Kp;k]^T / sqrt(dh)) [Vp;v]        (attn_kernel + attn_merge)
 //               h   += o W_o^T                                       (o_proj_resid_kernel)
 //               u    = gelu(rmsnorm(h) W_g^T) * (rmsnorm(h) W_u^T)  (gate_up_geglu_kernel)  
 //               h   += u W_d^T                                       (down_resid_kernel)
@@ -122,11 +122,11 @@ struct GemmArgs {
   float* part;          // split-K partials [S][n_z][n_groups][NT*64*16]
   unsigned* counters;   // [n_z][n_groups], zero between launches
   // EPI_QKV
-  void* q_out; void* k_out; void* v_out;   // [rows][ldo], [rows][ldkv] x2
+  void* q_out; void* k_out; void* v_out;   // attention operands in fragment order (see the attention section)
   const float* rope_cs;                    // [H][dh/2][2] cos, sin at positions P + t
   int n_q, n_kv, dh, H;
-  int ldkv;                                // row stride of the suffix k buffer
-  int ldvt;                                // row stride of the transposed suffix v buffer
+  int n_qt;                                // 16-row query tiles per (sequence, kv head)
+  int nbs;                                 // 32-key suffix blocks per (sequence, kv head)
   // EPI_RESID
   float* h;              // [M_pad][N] residual, updated in place
   void* hb;              // [rows][ldo] copy h * gain_next for the next consumer
@@ -426,14 +426,26 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         if (c < 8) { out = val * cs.x - partner * cs.y; dfull = d; }
         else { out = partner * cs.y + val * cs.x; dfull = half + d; }
         if (valid) {
-          if (is_q) Act<AT>::st((XT*)a.q_out, (size_t)tok * a.ldo + head * a.dh + dfull, out);
-          else Act<AT>::st((XT*)a.k_out, (size_t)tok * a.ldkv + head * a.dh + dfull, out);
+          const int sq = tok / a.H, t = tok % a.H;
+          const int nkb = a.dh / KBLK, lgrp = ((dfull % KBLK) >> 3) << 4, e8 = dfull & 7, kb = dfull / KBLK;
+          if (is_q) {  // query B fragments: row r = j*H + t of the tile, dims kb*32 + (lane/16)*8
+            const int gq = a.n_q / a.n_kv, g = head / gq, r = (head % gq) * a.H + t;
+            const size_t fr = ((((size_t)sq * a.n_kv + g) * a.n_qt + r / 16) * nkb + kb);
+            Act<AT>::st((XT*)a.q_out, fr * 512 + (lgrp + (r & 15)) * 8 + e8, out);
+          } else {     // key A fragments of 32-key block t/32, keys in the order the attention expects
+            const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+            const size_t fr = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb);
+            Act<AT>::st((XT*)a.k_out, fr * 512 + (lgrp + m) * 8 + e8, out);
+          }
         }
       } else {
-        // suffix values transposed: [seq][kv head][dh][ldvt]
+        // value A fragments (of V^T) of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
         const int col = (t_in - q_tiles - k_tiles) * 16 + c;
-        if (valid)
-          Act<AT>::st((XT*)a.v_out, ((size_t)(tok / a.H) * a.n_kv * a.dh + col) * a.ldvt + tok % a.H, val);
+        if (valid) {
+          const int sq = tok / a.H, t = tok % a.H, hd = col / a.dh, d = col % a.dh, kk = t & 31;
+          const size_t fr = ((((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d / 16);
+          Act<AT>::st((XT*)a.v_out, fr * 512 + (((kk >> 3) << 4) + (d & 15)) * 8 + (kk & 7), val);
+        }
       }
     } else if constexpr (EPI == EPI_RESID) {
       const int n = (int)tile * 16 + c;
@@ -503,363 +515,335 @@ constexpr void (*gemm_entry())(GemmArgs) {
 
 // ------------------------------------------------------------------ attention
 
+// Attention operands live in MFMA fragment order, one 1 KB (bf16) or 2 KB (fp32)
+// contiguous run per fragment, so every load instruction of a wave reads whole
+// cache lines (scattered 16-byte pieces of 16 rows cost several times more):
+//   Q  [seq][kv head][16-row tile][dh/32][64 lanes][8]: lane = (d%32/8)*16 + row%16,
+//      row r = j*H + t for query head g*gq + j and chunk row t;
+//   K  [..][32-key block][2][dh/32][64][8]: half kt, lane = (d%32/8)*16 + m holds key
+//      8*(m/4) + 4*kt + m%4 of the block, so that the S^T accumulators of a lane
+//      cover keys 8*(lane/16) .. +8 of the block in order;
+//   V  [..][32-key block][dh/16][64][8]: lane = (key/8)*16 + d%16, element key%8
+//      (the A operand of O^T = V^T P^T over the same 8 keys).
+// The prefix cache is packed this way at load time, per slot and layer, with
+// ceil(P/32) blocks (keys past P zero); the suffix operands are written in
+// this order by the QKV epilogue with ceil(H/32) blocks per sequence.
 struct AttnArgs {
-  const void* q;          // [rows][ldq] (rotated)
-  const void* ks;         // suffix keys [rows][ldkv] (rotated)
-  const void* vsT;        // suffix values transposed [seq][n_kv][dh][ldvt]
-  const void* kcache;     // prefix K [slots][L][P][n_kv][dh]
-  const void* vcacheT;    // prefix V transposed [slots][L][n_kv][dh][ldp]
+  const void* q;          // packed queries
+  const void* ks;         // packed suffix K
+  const void* vs;         // packed suffix V
+  const void* kcache;     // packed prefix K [slot][L][n_kv][nbp][2][dh/32][64][8]
+  const void* vcache;     // packed prefix V [slot][L][n_kv][nbp][dh/16][64][8]
   const int* seq_slot;    // prefix slot of each sequence
-  size_t kslot_stride, klayer_off;  // elements
-  size_t vslot_stride, vlayer_off;  // elements
-  int P, H, n_q, n_kv, dh, KC;
-  int ldq, ldkv, ldvt, ldp, ldo;
-  int n_qt, n_chunks;
+  size_t slot_stride, layer_off;  // elements (same for K and V)
+  int P, H, n_q, n_kv, dh;
+  int nbp, nbs;           // 32-key prefix / suffix blocks
+  int ldo;                // row stride of o
+  int n_qt;               // 16-row query tiles per (sequence, kv head)
+  int n_split;            // key splits (workgroups) per query tile
   float scale_log2;       // log2(e) / sqrt(dh)
-  float* opart;           // [z][qt][chunk][64][dh]
-  float* mlpart;          // [z][qt][chunk][64][2]  (row max in log2 units, row sum)
-  unsigned* qt_counter;   // [z][qt] arrival counters (monotonic) for the fused combine
-  unsigned* err;          // set when a fused-combine wait times out
+  float* opart;           // [zz][qt][split][16][dh] merged split partials
+  float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum)
   void* o;                // [rows][ldo] output
-  int fused;              // 1: combine inside the kernel (whole grid co-resident)
-  int p_aligned;          // prefix_len is a multiple of the 16-byte vector width
   int trace_id;
 };
 
-// Combine the chunk partials of one query row r (of sequence s, kv head g) for dims d:
-// o = sum_c 2^(m_c - M) O_c / sum_c 2^(m_c - M) l_c, 16 chunks per batch, all loads of a batch in flight.
-template <int AT, bool COHERENT>
-__device__ __forceinline__ void attn_combine_row(const AttnArgs& a, int zz, int qt, int row, int d, int s, int g) {
-  typedef typename Act<AT>::T XT;
-  const size_t base = ((size_t)zz * a.n_qt + qt) * a.n_chunks;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
-  float M = -INFINITY, num = 0.f, den = 0.f;
-  for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
-    float mc[16], lc[16], oc[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int c = c0 + i;
-      if (c < a.n_chunks) {
-        const size_t mi = ((base + c) * 64 + row) * 2, oi = ((base + c) * 64 + row) * a.dh + d;
-        if constexpr (COHERENT) {
-          mc[i] = ld_coherent_buf(rm, (unsigned)(mi * 4));
-          lc[i] = ld_coherent_buf(rm, (unsigned)(mi * 4 + 4));
-          oc[i] = ld_coherent_buf(ro, (unsigned)(oi * 4));
-        } else {
-          mc[i] = a.mlpart[mi];
-          lc[i] = a.mlpart[mi + 1];
-          oc[i] = a.opart[oi];
-        }
-      } else {
-        mc[i] = -INFINITY; lc[i] = 0.f; oc[i] = 0.f;
-      }
-    }
-    float Mn = M;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) Mn = fmaxf(Mn, mc[i]);
-    const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
-    num *= sc;
-    den *= sc;
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float wgt = (mc[i] == -INFINITY) ? 0.f : exp2f(mc[i] - Mn);
-      num += wgt * oc[i];
-      den += wgt * lc[i];
-    }
-    M = Mn;
-  }
-  const int gq = a.n_q / a.n_kv;
-  const int r = qt * 64 + row;
-  const int jh = r / a.H, t = r % a.H;
-  Act<AT>::st((XT*)a.o, (size_t)(s * a.H + t) * a.ldo + (size_t)(g * gq + jh) * a.dh + d, num / den);
+constexpr int ATT_ROWS = 16;   // query rows per workgroup
+constexpr int ATT_KB = 32;     // keys per wave block
+constexpr int ATT_WAVES = 8;   // waves per workgroup
+constexpr int ATT_IT = 1;      // key blocks per wave (a split covers ATT_WAVES * ATT_IT blocks)
+
+template <int DH>
+constexpr size_t attn_lds_size() {  // per-wave O and (m, l), then the query tile (fp32 at most)
+  return (size_t)ATT_WAVES * ATT_ROWS * (DH + 4) * 4 + (size_t)ATT_WAVES * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4;
 }
 
-// One workgroup: 64 query rows (4 waves x 16; row r = j*H + t is query head
-// g*gq + j, chunk row t of one sequence) against one chunk of KC keys of
-// [prefix ; suffix]. S^T = K Q^T puts 16 keys x 16 rows in each MFMA tile,
-// so a lane's accumulators hold 8 keys of one row per 32-key block: they are
-// the B operand of O^T = V^T P^T directly (k index permuted identically for
-// V^T), and the softmax never leaves registers. K and V^T are staged in LDS
-// with 16-byte loads (V is cached transposed). The chunk's partial (m, l, O)
-// is written write-through; with fused = 1 the n_chunks workgroups of a
-// query tile then meet at a counter and each combines a share of the rows.
-template <int AT, int KC, int DH>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 2))) void attn_kernel(AttnArgs a) {
+// Attention of suffix query rows over [prefix ; suffix] keys. Grid (n_split,
+// n_qt, n_seq * n_kv), block = 8 waves. A query tile is 16 rows; GQA folds the
+// gq heads of a kv head into rows, so each key is read once per tile. The key
+// blocks of a split (prefix blocks first, then the sequence's suffix blocks)
+// are dealt to the 8 waves round robin; a wave runs an online softmax over its
+// blocks. S^T = K Q^T leaves per lane 8 scores of one row that are exactly the
+// B operand of O^T = V^T P^T, so the softmax stays in registers. Loads are
+// pipelined without extra registers: a block's K fragments are reissued for
+// the next block as soon as its S^T is done, its V fragments as soon as its
+// O^T is done. The waves merge (m, l, O) in LDS; with one split the workgroup
+// writes o, with several it stores its partial for attn_merge.
+template <int AT, int DH>
+__global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT_BF16, AT> F;
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];  // no static LDS: aligned 16-byte accesses
-  constexpr int dh = DH;
-  constexpr int VE = 16 / sizeof(XT);      // elements per 16-byte vector
-  constexpr int ldk = DH + VE;             // padded LDS row strides (elements)
-  constexpr int ldv = KC + VE;
-  XT* Ks = (XT*)smem_raw;                  // [KC][ldk]
-  XT* VT = Ks + (size_t)KC * ldk;          // [dh][ldv]
+  constexpr int NKB = DH / KBLK;   // 32-dim blocks of a head
+  constexpr int NDT = DH / 16;     // 16-dim tiles of a head
+  constexpr int LDO = DH + 4;      // LDS row stride of a wave's O (floats)
+  constexpr int FR = 512;          // elements per fragment (64 lanes x 8)
+  extern __shared__ __attribute__((aligned(16))) float att_smem[];
+  float* Ow = att_smem;                                    // [waves][16][LDO]
+  float* MLw = Ow + ATT_WAVES * ATT_ROWS * LDO;            // [waves][16][2]
+  XT* Qs = (XT*)(MLw + ATT_WAVES * ATT_ROWS * 2);          // [NKB][64][8] query fragments
 
   AE_TR(0);
-  const int chunk = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
+  const int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
   const int s = zz / a.n_kv, g = zz % a.n_kv;
   const int gq = a.n_q / a.n_kv;
   const int R = gq * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int j0 = chunk * KC;
-  const int n_keys = a.P + a.H;
   const int slot = a.seq_slot[s];
-  const XT* kc = (const XT*)a.kcache + (size_t)slot * a.kslot_stride + a.klayer_off;
-  const XT* vcT = (const XT*)a.vcacheT + (size_t)slot * a.vslot_stride + a.vlayer_off + (size_t)g * DH * a.ldp;
-  const XT* ks = (const XT*)a.ks;
-  const XT* vsT = (const XT*)a.vsT + ((size_t)s * a.n_kv + g) * dh * a.ldvt;
-
-  // query fragments (B operand of S^T): row r of this lane, 8 inputs per 32-block
-  const int r_lane = qt * 64 + wave * 16 + (lane & 15);
-  const bool r_ok = r_lane < R;
-  const int jh = r_ok ? r_lane / a.H : 0, t_lane = r_ok ? r_lane % a.H : 0;
-  const XT* qrow = (const XT*)a.q + (size_t)(s * a.H + t_lane) * a.ldq + (size_t)(g * gq + jh) * dh + (lane >> 4) * 8;
-  typename F::B qb[8];
-#pragma unroll
-  for (int kb = 0; kb < 8; ++kb)
-    if (kb < dh / KBLK) qb[kb] = r_ok ? F::load_b(qrow + kb * KBLK) : typename F::B();
-
-  // stage K rows [j0, j0+KC) and V^T columns: every global load of the thread is
-  // issued before the first LDS store (one memory round trip). Sources are
-  // selected, not branched on: key indices are clamped into range and keys
-  // past the last one are zeroed after the load.
-  constexpr int vpr = DH / VE, kpr = KC / VE;
-  constexpr int KIT = KC * vpr / 256, VIT = DH * kpr / 256;  // vectors per thread
-  static_assert(KIT >= 1 && VIT >= 1 && KIT <= 8 && VIT <= 8, "attention tile shape");
-  i32x4 kreg[KIT], vreg[VIT];
-#pragma unroll
-  for (int i = 0; i < KIT; ++i) {
-    const int e = threadIdx.x + 256 * i;
-    const int kr = e / vpr, d0 = (e % vpr) * VE, j = j0 + kr;
-    const int jc = min(j, n_keys - 1);
-    const XT* src = jc < a.P ? kc + ((size_t)jc * a.n_kv + g) * DH + d0
-                             : ks + (size_t)(s * a.H + (jc - a.P)) * a.ldkv + (size_t)g * DH + d0;
-    kreg[i] = *(const i32x4*)src;
-  }
-  if (a.p_aligned) {  // every 16-byte key vector lies wholly in the prefix or wholly in the suffix
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int d = e / kpr, jb = j0 + (e % kpr) * VE;
-      const int jc = min(jb, a.P + a.ldvt - VE);  // suffix rows are zero-padded to ldvt
-      const XT* src = jc < a.P ? vcT + (size_t)d * a.ldp + jc : vsT + (size_t)d * a.ldvt + (jc - a.P);
-      vreg[i] = *(const i32x4*)src;
+  const int nb = a.nbp + a.nbs;
+  const int bps = (nb + a.n_split - 1) / a.n_split;         // blocks per split
+  const int b_begin = split * bps, b_end = min(nb, b_begin + bps);
+  const size_t pre_base = (size_t)slot * a.slot_stride + a.layer_off + (size_t)g * a.nbp * (2 * NKB * FR);
+  const size_t suf_base = ((size_t)s * a.n_kv + g) * a.nbs * (2 * NKB * FR);
+  // fragment base and valid keys of block b (a prefix or a suffix block)
+  auto block_src = [&](int b, const XT*& kf, const XT*& vf, int& n_valid) {
+    if (b < a.nbp) {
+      const size_t base = pre_base + (size_t)b * (2 * NKB * FR);
+      kf = (const XT*)a.kcache + base;
+      vf = (const XT*)a.vcache + base;
+      n_valid = min(ATT_KB, a.P - b * ATT_KB);
+    } else {
+      const size_t base = suf_base + (size_t)(b - a.nbp) * (2 * NKB * FR);
+      kf = (const XT*)a.ks + base;
+      vf = (const XT*)a.vs + base;
+      n_valid = min(ATT_KB, a.H - (b - a.nbp) * ATT_KB);
     }
-  } else {
+  };
+  const XT* qf = (const XT*)a.q + (((size_t)s * a.n_kv + g) * a.n_qt + qt) * NKB * FR;
+
+  // the query tile goes to LDS once (it is the same for every wave and block): its loads are
+  // issued first, the LDS stores wait only for them while the K/V loads below stay in flight
+  constexpr int QVEC = 16 / sizeof(XT);  // elements per 16-byte vector
+  constexpr int QNV = NKB * FR / QVEC;
+  constexpr int QIT = (QNV + ATT_WAVES * 64 - 1) / (ATT_WAVES * 64);
+  i32x4 qtmp[QIT];
 #pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int e = threadIdx.x + 256 * i;
-      const int d = e / kpr, jb = j0 + (e % kpr) * VE;
-      XT tmp[VE];
-#pragma unroll
-      for (int t = 0; t < VE; ++t) {
-        const int j = jb + t;
-        tmp[t] = j < a.P ? vcT[(size_t)d * a.ldp + j] : (j < n_keys ? vsT[(size_t)d * a.ldvt + (j - a.P)] : (XT)0);
-      }
-      vreg[i] = *(const i32x4*)tmp;
-    }
+  for (int i = 0; i < QIT; ++i) {
+    const int e = threadIdx.x + ATT_WAVES * 64 * i;
+    qtmp[i] = e < QNV ? *(const i32x4*)(qf + e * QVEC) : i32x4{0, 0, 0, 0};
   }
-  __builtin_amdgcn_sched_barrier(0);  // all staging loads in flight before the first LDS store
+  __builtin_amdgcn_sched_barrier(0);
+  // this wave's blocks: b_begin + wave + 8 it for it < ATT_IT (the runtime keeps a split within
+  // ATT_IT blocks per wave); a slot past the split's end reads the split's first block, masked.
+  // The loop is unrolled with no data-dependent branch so every wait covers exactly the loads it needs.
+  const XT* kfs[ATT_IT];
+  const XT* vfs[ATT_IT];
+  int nvs[ATT_IT];
 #pragma unroll
-  for (int i = 0; i < KIT; ++i) {
-    const int e = threadIdx.x + 256 * i;
-    const int kr = e / vpr;
-    const i32x4 z = {0, 0, 0, 0};
-    *(i32x4*)(Ks + (size_t)kr * ldk + (e % vpr) * VE) = (j0 + kr < n_keys) ? kreg[i] : z;
+  for (int it = 0; it < ATT_IT; ++it) {
+    const int bb = b_begin + wave + ATT_WAVES * it;
+    block_src(bb < b_end ? bb : b_begin, kfs[it], vfs[it], nvs[it]);
+    if (bb >= b_end) nvs[it] = 0;
   }
+  typename F::A ka[2][NKB];
 #pragma unroll
-  for (int i = 0; i < VIT; ++i) {
-    const int e = threadIdx.x + 256 * i;
-    const int jb = j0 + (e % kpr) * VE;
-    const i32x4 z = {0, 0, 0, 0};
-    *(i32x4*)(VT + (size_t)(e / kpr) * ldv + (e % kpr) * VE) = (jb < n_keys) ? vreg[i] : z;
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) ka[kt][kb] = F::load_b(kfs[0] + (kt * NKB + kb) * FR + lane * 8);
+  typename F::A va[NDT];
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) va[dt] = F::load_b(vfs[0] + dt * FR + lane * 8);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < QIT; ++i) {
+    const int e = threadIdx.x + ATT_WAVES * 64 * i;
+    if (e < QNV) *(i32x4*)(Qs + e * QVEC) = qtmp[i];
   }
-  __syncthreads();
   AE_TR(1);
+  __syncthreads();  // query tile staged
 
-  // S^T tiles: sacc[kt][v] = score(key kt*16 + 4*(lane/16) + v, row lane%16)
-  const int n_kt = KC / 16;
-  f32x4 sacc[8];
+  const int k8 = 8 * (lane >> 4);
+  float m_run = -INFINITY, l_run = 0.f;
+  f32x4 oacc[NDT];
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) sacc[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int dt = 0; dt < NDT; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kt = 0; kt < 8; ++kt) {
-    if (kt < n_kt) {
-      const XT* kp = Ks + (size_t)(kt * 16 + (lane & 15)) * ldk + (lane >> 4) * 8;
+  for (int it = 0; it < ATT_IT; ++it) {
+    // S^T: sacc[kt][v] = score(block key 8*(lane/16) + 4*kt + v, row lane%16)
+    f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-      for (int kb = 0; kb < 8; ++kb)
-        if (kb < dh / KBLK) {
-          typename F::A ka;
-          if constexpr (AT == AT_BF16) ka = __builtin_bit_cast(bf16x8, *(const uint4*)(kp + kb * KBLK));
-          else ka = typename F::A{((const float4*)(kp + kb * KBLK))[0], ((const float4*)(kp + kb * KBLK))[1]};
-          sacc[kt] = F::mma(ka, qb[kb], sacc[kt]);
-        }
+    for (int kb = 0; kb < NKB; ++kb) {
+      const typename F::B qb = F::load_b(Qs + kb * FR + lane * 8);
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) sacc[kt] = F::mma(ka[kt][kb], qb, sacc[kt]);
     }
+    __builtin_amdgcn_sched_barrier(0);  // ka consumed before the next block's K overwrites it
+    if (it + 1 < ATT_IT) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) ka[kt][kb] = F::load_b(kfs[it + 1] + (kt * NKB + kb) * FR + lane * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // online softmax over this block for row lane%16
+    const int n_valid = nvs[it];
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float sv = (k8 + 4 * kt + v < n_valid) ? sacc[kt][v] * a.scale_log2 : -INFINITY;
+        sacc[kt][v] = sv;
+        mb = fmaxf(mb, sv);
+      }
+    mb = fmaxf(mb, __shfl_xor(mb, 16));
+    mb = fmaxf(mb, __shfl_xor(mb, 32));
+    const float m_new = fmaxf(m_run, mb);
+    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    float lb = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float p = (m_new == -INFINITY) ? 0.f : exp2f(sacc[kt][v] - m_new);
+        sacc[kt][v] = p;
+        lb += p;
+      }
+    lb += __shfl_xor(lb, 16);
+    lb += __shfl_xor(lb, 32);
+    l_run = l_run * alpha + lb;
+    m_run = m_new;
+    typename F::B pb;
+    if constexpr (AT == AT_BF16) {
+      pb = bf16x8{(__bf16)sacc[0][0], (__bf16)sacc[0][1], (__bf16)sacc[0][2], (__bf16)sacc[0][3],
+                  (__bf16)sacc[1][0], (__bf16)sacc[1][1], (__bf16)sacc[1][2], (__bf16)sacc[1][3]};
+    } else {
+      pb = typename F::B{make_float4(sacc[0][0], sacc[0][1], sacc[0][2], sacc[0][3]),
+                         make_float4(sacc[1][0], sacc[1][1], sacc[1][2], sacc[1][3])};
+    }
+    // O^T = alpha O^T + V^T P^T: element (dim dt*16 + 4*(lane/16) + v, row lane%16)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oacc[dt] = F::mma(va[dt], pb, oacc[dt] * alpha);
+    __builtin_amdgcn_sched_barrier(0);  // va consumed before the next block's V overwrites it
+    if (it + 1 < ATT_IT) {
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) va[dt] = F::load_b(vfs[it + 1] + dt * FR + lane * 8);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
+  // this wave's (m, l, O) to LDS: O[row lane%16][dt*16 + 4*(lane/16) + v]
+  float* ow = Ow + (size_t)wave * ATT_ROWS * LDO + (lane & 15) * LDO + 4 * (lane >> 4);
+#pragma unroll
+  for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(ow + dt * 16) = oacc[dt];
+  if (lane < 16) *(float2*)(MLw + (wave * ATT_ROWS + lane) * 2) = make_float2(m_run, l_run);
+  __syncthreads();
   AE_TR(2);
-  // softmax over this chunk's keys for row lane%16: reduce over kt, v and the 4 lane groups
-  float m = -INFINITY;
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int j = j0 + kt * 16 + 4 * (lane >> 4) + v;
-      const float sv = (kt < n_kt && j < n_keys) ? sacc[kt][v] * a.scale_log2 : -INFINITY;
-      sacc[kt][v] = sv;
-      m = fmaxf(m, sv);
-    }
-  m = fmaxf(m, __shfl_xor(m, 16));
-  m = fmaxf(m, __shfl_xor(m, 32));
-  float lsum = 0.f;
-#pragma unroll
-  for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const float p = (m == -INFINITY) ? 0.f : exp2f(sacc[kt][v] - m);
-      sacc[kt][v] = p;
-      lsum += p;
-    }
-  lsum += __shfl_xor(lsum, 16);
-  lsum += __shfl_xor(lsum, 32);
 
-  // O^T = V^T P^T: dims dt*16 + lane%16 (A from LDS, keys permuted like the B operand), rows lane%16
-  const int q4 = 4 * (lane >> 4);
-  f32x4 oacc[16];
+  // ---- merge the waves: thread -> row, DPT consecutive dims (threads past 16 rows idle)
+  constexpr int DPT = DH / 16 >= 4 ? DH / 16 : 4;   // dims per thread, a multiple of 4
+  constexpr int TPR = DH / DPT;                      // threads per row
+  const bool active = threadIdx.x < ATT_ROWS * TPR;
+  const int row = active ? threadIdx.x / TPR : 0, d0 = (threadIdx.x % TPR) * DPT;
+  float mw[ATT_WAVES], lw[ATT_WAVES];
+  float M = -INFINITY;
 #pragma unroll
-  for (int dt = 0; dt < 16; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int w = 0; w < ATT_WAVES; ++w) {
+    const float2 ml = *(const float2*)(MLw + (w * ATT_ROWS + row) * 2);
+    mw[w] = ml.x;
+    lw[w] = ml.y;
+    M = fmaxf(M, ml.x);
+  }
+  float L = 0.f, O[DPT];
 #pragma unroll
-  for (int kb2 = 0; kb2 < 4; ++kb2) {
-    if (kb2 < KC / KBLK) {
-      typename F::B pb;
-      if constexpr (AT == AT_BF16) {
-        pb = bf16x8{(__bf16)sacc[2 * kb2][0], (__bf16)sacc[2 * kb2][1], (__bf16)sacc[2 * kb2][2], (__bf16)sacc[2 * kb2][3],
-                    (__bf16)sacc[2 * kb2 + 1][0], (__bf16)sacc[2 * kb2 + 1][1], (__bf16)sacc[2 * kb2 + 1][2],
-                    (__bf16)sacc[2 * kb2 + 1][3]};
-      } else {
-        pb = typename F::B{make_float4(sacc[2 * kb2][0], sacc[2 * kb2][1], sacc[2 * kb2][2], sacc[2 * kb2][3]),
-                           make_float4(sacc[2 * kb2 + 1][0], sacc[2 * kb2 + 1][1], sacc[2 * kb2 + 1][2], sacc[2 * kb2 + 1][3])};
-      }
+  for (int i = 0; i < DPT; ++i) O[i] = 0.f;
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt) {
-        if (dt < dh / 16) {
-          const XT* vp = VT + (size_t)(dt * 16 + (lane & 15)) * ldv + kb2 * KBLK + q4;
-          typename F::A va;
-          if constexpr (AT == AT_BF16) {
-            const uint2 lo = *(const uint2*)vp, hi = *(const uint2*)(vp + 16);
-            va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-          } else {
-            va = typename F::A{*(const float4*)vp, *(const float4*)(vp + 16)};
-          }
-          oacc[dt] = F::mma(va, pb, oacc[dt]);
-        }
-      }
+  for (int w = 0; w < ATT_WAVES; ++w) {
+    const float wt = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
+    L += wt * lw[w];
+    const float* src = Ow + ((size_t)w * ATT_ROWS + row) * LDO + d0;
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) {
+      const float4 v = *(const float4*)(src + i);
+      O[i] += wt * v.x; O[i + 1] += wt * v.y; O[i + 2] += wt * v.z; O[i + 3] += wt * v.w;
     }
   }
-
   AE_TR(3);
-  // publish the chunk partial: row lane%16 holds dims dt*16 + q4 .. +4
-  const int prow = wave * 16 + (lane & 15);
-  const size_t pidx = ((size_t)zz * a.n_qt + qt) * a.n_chunks + chunk;
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
-  if (a.fused) {  // read by other workgroups of this launch: write through
+
+  const int r = qt * ATT_ROWS + row;
+  const bool row_ok = active && r < R;
+  XT* op = (XT*)a.o + (size_t)(s * a.H + (row_ok ? r % a.H : 0)) * a.ldo + (size_t)(g * gq + (row_ok ? r / a.H : 0)) * DH + d0;
+  if (a.n_split == 1) {
+    if (row_ok) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < dh / 16; ++dt)
-      st16_coherent(ro, (unsigned)(((pidx * 64 + prow) * dh + dt * 16 + q4) * 4),
-                    make_float4(oacc[dt][0], oacc[dt][1], oacc[dt][2], oacc[dt][3]));
-    if (lane < 16) {
-      __hip_atomic_store(a.mlpart + (pidx * 64 + prow) * 2, m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(a.mlpart + (pidx * 64 + prow) * 2 + 1, lsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < DPT; ++i) Act<AT>::st(op, i, O[i] * inv);
     }
-  } else {  // read by the combine kernel after the launch boundary
+    return;
+  }
+
+  // ---- several splits: store this split's partial; attn_merge combines them after the launch boundary
+  if (active) {
+    const size_t tile = (size_t)zz * a.n_qt + qt;
+    const size_t pbase = ((tile * a.n_split + split) * ATT_ROWS + row) * DH + d0;
 #pragma unroll
-    for (int dt = 0; dt < dh / 16; ++dt)
-      *(f32x4*)(a.opart + (pidx * 64 + prow) * dh + dt * 16 + q4) = oacc[dt];
-    if (lane < 16) *(float2*)(a.mlpart + (pidx * 64 + prow) * 2) = make_float2(m, lsum);
+    for (int i = 0; i < DPT; i += 4) *(float4*)(a.opart + pbase + i) = make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]);
+    if (threadIdx.x % TPR == 0)
+      *(float2*)(a.mlpart + ((tile * a.n_split + split) * ATT_ROWS + row) * 2) = make_float2(M, L);
   }
 #ifdef AE_TRACE
   wait_mem();
   AE_TR(4);
 #endif
-  if (!a.fused) return;
-
-  // fused combine: wait for the n_chunks workgroups of this query tile (bounded spin)
-  wait_mem();
-  __syncthreads();
-  int* go = (int*)(VT + (size_t)dh * ldv);  // one int past the staged tiles
-  if (threadIdx.x == 0) {
-    unsigned* cnt = a.qt_counter + (size_t)zz * a.n_qt + qt;
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned target = (old / a.n_chunks + 1) * a.n_chunks;
-    int ok = 0;
-    for (int it = 0; it < (1 << 22); ++it) {
-      if ((int)(ldu_coherent(cnt) - target) >= 0) { ok = 1; break; }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (!ok) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *go = ok;
-  }
-  __syncthreads();
-  AE_TR(5);
-  if (!*go) return;
-  // this workgroup's share of the tile: units (row, 4 dims), strided over the n_chunks workgroups
-  const int rows_here = min(64, R - qt * 64);
-  const int units = rows_here * (dh / 4);
-  const size_t base = ((size_t)zz * a.n_qt + qt) * a.n_chunks;
-  for (int u = chunk * 256 + threadIdx.x; u < units; u += a.n_chunks * 256) {
-    const int row = u / (dh / 4), d4 = (u % (dh / 4)) * 4;
-    float M = -INFINITY;
-    float4 num = make_float4(0.f, 0.f, 0.f, 0.f);
-    float den = 0.f;
-    for (int c0 = 0; c0 < a.n_chunks; c0 += 16) {
-      float mc[16], lc[16];
-      float4 oc[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int c = c0 + i;
-        if (c < a.n_chunks) {
-          const size_t mi = ((base + c) * 64 + row) * 2, oi = ((base + c) * 64 + row) * dh + d4;
-          mc[i] = ld_coherent_buf(rm, (unsigned)(mi * 4));
-          lc[i] = ld_coherent_buf(rm, (unsigned)(mi * 4 + 4));
-          oc[i] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(ro, (unsigned)(oi * 4), 0, 0x10));
-        } else {
-          mc[i] = -INFINITY; lc[i] = 0.f; oc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-        }
-      }
-      float Mn = M;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) Mn = fmaxf(Mn, mc[i]);
-      const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
-      num.x *= sc; num.y *= sc; num.z *= sc; num.w *= sc;
-      den *= sc;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float wgt = (mc[i] == -INFINITY) ? 0.f : exp2f(mc[i] - Mn);
-        num.x += wgt * oc[i].x; num.y += wgt * oc[i].y; num.z += wgt * oc[i].z; num.w += wgt * oc[i].w;
-        den += wgt * lc[i];
-      }
-      M = Mn;
-    }
-    const int r = qt * 64 + row;
-    const int jr = r / a.H, tr = r % a.H;
-    XT* op = (XT*)a.o + (size_t)(s * a.H + tr) * a.ldo + (size_t)(g * gq + jr) * dh + d4;
-    const float inv = 1.f / den;
-    Act<AT>::st(op, 0, num.x * inv);
-    Act<AT>::st(op, 1, num.y * inv);
-    Act<AT>::st(op, 2, num.z * inv);
-    Act<AT>::st(op, 3, num.w * inv);
-  }
-#ifdef AE_TRACE
-  wait_mem();
-  AE_TR(6);
-#endif
 }
 
-// Separate combine (grid not co-resident): grid (R rows, n_seq * n_kv); block = dh threads.
-template <int AT>
-__global__ __launch_bounds__(256) void attn_combine(AttnArgs a) {
-  const int r = blockIdx.x, zz = blockIdx.y;
-  if ((int)threadIdx.x >= a.dh) return;
-  attn_combine_row<AT, false>(a, zz, r / 64, r % 64, threadIdx.x, zz / a.n_kv, zz % a.n_kv);
+// Merge of the key-split partials of attn_kernel: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Grid (n_qt, n_seq * n_kv), block = 16 rows x TPR threads, each DPT consecutive dims; the
+// partials of up to 8 splits are loaded at once, in split order (deterministic).
+template <int AT, int DH>
+__global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
+  typedef typename Act<AT>::T XT;
+  constexpr int DPT = DH / 16 >= 4 ? DH / 16 : 4;
+  constexpr int TPR = DH / DPT;
+  const int qt = blockIdx.x, zz = blockIdx.y;
+  if ((int)threadIdx.x >= ATT_ROWS * TPR) return;
+  AE_TR(0);
+  const int row = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DPT;
+  const int s = zz / a.n_kv, g = zz % a.n_kv, gq = a.n_q / a.n_kv;
+  const int r = qt * ATT_ROWS + row;
+  if (r >= gq * a.H) return;
+  const size_t tile = (size_t)zz * a.n_qt + qt;
+  float M = -INFINITY, L = 0.f, O[DPT];
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) O[i] = 0.f;
+  for (int c0 = 0; c0 < a.n_split; c0 += 8) {
+    float mc[8], lc[8];
+    float4 oc[8][DPT / 4];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int sp = c0 + c < a.n_split ? c0 + c : 0;
+      const float2 ml = *(const float2*)(a.mlpart + ((tile * a.n_split + sp) * ATT_ROWS + row) * 2);
+      mc[c] = c0 + c < a.n_split ? ml.x : -INFINITY;
+      lc[c] = ml.y;
+      const float* src = a.opart + ((tile * a.n_split + sp) * ATT_ROWS + row) * DH + d0;
+#pragma unroll
+      for (int i = 0; i < DPT / 4; ++i) oc[c][i] = *(const float4*)(src + 4 * i);
+    }
+    float Mn = M;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Mn = fmaxf(Mn, mc[c]);
+    const float sc = (M == -INFINITY) ? 0.f : exp2f(M - Mn);
+    L *= sc;
+#pragma unroll
+    for (int i = 0; i < DPT; ++i) O[i] *= sc;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float wt = (mc[c] == -INFINITY) ? 0.f : exp2f(mc[c] - Mn);
+      L += wt * lc[c];
+#pragma unroll
+      for (int i = 0; i < DPT / 4; ++i) {
+        O[4 * i] += wt * oc[c][i].x; O[4 * i + 1] += wt * oc[c][i].y;
+        O[4 * i + 2] += wt * oc[c][i].z; O[4 * i + 3] += wt * oc[c][i].w;
+      }
+    }
+    M = Mn;
+  }
+  XT* op = (XT*)a.o + (size_t)(s * a.H + r % a.H) * a.ldo + (size_t)(g * gq + r / a.H) * DH + d0;
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+  for (int i = 0; i < DPT; ++i) Act<AT>::st(op, i, O[i] * inv);
+#ifdef AE_TRACE
+  wait_mem();
+  AE_TR(1);
+#endif
 }
 
 // ------------------------------------------------------------------ in_proj, time embedding, verify

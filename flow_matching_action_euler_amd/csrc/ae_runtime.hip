@@ -92,7 +92,7 @@ struct ae_handle {
   int wt = WT_BF16;      // attention / projection weight type
   int mt = WT_BF16;      // MLP weight type
   int M_max = 0, Mp_max = 0;
-  int ld_h = 0, ld_q = 0, ld_kv = 0, ld_u = 0;  // padded row strides (elements) of hb/o, q, k/v, u
+  int ld_h = 0, ld_q = 0, ld_u = 0;  // padded row strides (elements) of hb, o, u
   std::vector<void*> allocs;
 
   // weights (device)
@@ -106,20 +106,18 @@ struct ae_handle {
 
   // activations and scratch
   float *x = nullptr, *h = nullptr, *ssp_a = nullptr, *ssp_b = nullptr, *vout = nullptr;
-  void *hb = nullptr, *q = nullptr, *sk = nullptr, *sv = nullptr, *o = nullptr, *u = nullptr;
+  void *hb = nullptr, *o = nullptr, *u = nullptr;
+  void *q = nullptr, *ks = nullptr, *vs = nullptr;  // attention operands of the suffix, fragment order
   float* part = nullptr;
   size_t part_floats = 0;
   unsigned* counters = nullptr;
   size_t n_counters = 0;
   float *opart = nullptr, *mlpart = nullptr;
-  unsigned *qt_counter = nullptr, *err_flag = nullptr;
-  void* vsT = nullptr;       // suffix values transposed [seq][n_kv][dh][ld_vt]
-  int ld_vt = 0, ld_p = 0;   // padded key strides of the transposed suffix / prefix V
+  int n_qt = 0, nbp = 0, nbs = 0;  // 16-row query tiles, 32-key prefix / suffix blocks
   int n_cu = 0;
   float* rope_cs = nullptr;
   void *kcache = nullptr, *vcache = nullptr;
-  size_t slot_elems = 0;     // elements of one slot's K cache (= V cache without padding)
-  size_t vslot_elems = 0;    // elements of one slot's transposed V cache
+  size_t slot_elems = 0;     // elements of one slot's packed K (and V) cache
   std::vector<int> slot_ready;
   int *denoise_slots = nullptr, *verify_slots = nullptr;
   // verify inputs / outputs
@@ -223,7 +221,7 @@ int validate(const ae_config* c, const ae_weights* w) {
 }
 
 PhaseCfg pick(int KB, int want, int n_z) {
-  int S = n_z == 1 ? want : 1;
+  int S = n_z == 1 ? std::min(std::max(want, 1), 4) : 1;  // the split-K reduction sums at most 4 partials
   while (S > 1 && (KB % S || (KB / S) % GW)) --S;
   return {S};
 }
@@ -276,44 +274,48 @@ hipError_t set_all_gemm_attrs() {
 // k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group;
 // AE_SPLITS="q,o,g,d,u" overrides them for tuning.
 struct Splits {
-  int qkv = 1, o = 2, gu = 1, down = 2, out = 1;
+  int qkv = 1, o = 4, gu = 1, down = 4, out = 1;
   Splits() {
     if (const char* e = getenv("AE_SPLITS")) sscanf(e, "%d,%d,%d,%d,%d", &qkv, &o, &gu, &down, &out);
   }
 };
 const Splits& splits() { static Splits s; return s; }
 
-// Attention kernels are instantiated per (activation type, key chunk, head_dim).
-template <int AT, int KC>
-hipError_t attn_dispatch(int dh, bool set_attr, size_t lds, dim3 grid, hipStream_t st, const AttnArgs& aa) {
-  const void* fn = nullptr;
+// Key splits of the attention: one workgroup per query tile runs up to ATT_IT blocks of 32 keys
+// per wave; longer contexts are split and merged by attn_merge.
+int attn_splits(int n_blocks) { return std::max(1, (n_blocks + ATT_IT * ATT_WAVES - 1) / (ATT_IT * ATT_WAVES)); }
+
+// Attention kernels are instantiated per (activation type, head_dim).
+template <int AT>
+hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   switch (dh) {
-    case 32: fn = (const void*)attn_kernel<AT, KC, 32>; break;
-    case 64: fn = (const void*)attn_kernel<AT, KC, 64>; break;
-    case 128: fn = (const void*)attn_kernel<AT, KC, 128>; break;
-    case 256: fn = (const void*)attn_kernel<AT, KC, 256>; break;
-    default: return hipErrorInvalidValue;
-  }
-  if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  switch (dh) {
-    case 32: AE_LAUNCH((attn_kernel<AT, KC, 32>), grid, dim3(256), lds, st, aa); break;
-    case 64: AE_LAUNCH((attn_kernel<AT, KC, 64>), grid, dim3(256), lds, st, aa); break;
-    case 128: AE_LAUNCH((attn_kernel<AT, KC, 128>), grid, dim3(256), lds, st, aa); break;
-    default: AE_LAUNCH((attn_kernel<AT, KC, 256>), grid, dim3(256), lds, st, aa); break;
+    case 32: AE_LAUNCH((attn_merge<AT, 32>), grid, dim3(256), 0, st, aa); break;
+    case 64: AE_LAUNCH((attn_merge<AT, 64>), grid, dim3(256), 0, st, aa); break;
+    case 128: AE_LAUNCH((attn_merge<AT, 128>), grid, dim3(256), 0, st, aa); break;
+    default: AE_LAUNCH((attn_merge<AT, 256>), grid, dim3(256), 0, st, aa); break;
   }
   return hipGetLastError();
 }
 
 template <int AT>
-hipError_t set_attrs(size_t bytes, int dh) {
-  return AT == AT_BF16 ? attn_dispatch<AT_BF16, 64>(dh, true, bytes, dim3(), nullptr, AttnArgs{})
-                       : attn_dispatch<AT_F32, 32>(dh, true, bytes, dim3(), nullptr, AttnArgs{});
-}
-
-size_t attn_lds_bytes(int at, int dh) {
-  const int KC = at == AT_BF16 ? 64 : 32, pad = at == AT_BF16 ? 8 : 4;
-  const size_t es = at == AT_BF16 ? 2 : 4;
-  return ((size_t)KC * (dh + pad) + (size_t)dh * (KC + pad)) * es + 16;
+hipError_t attn_dispatch(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  const void* fn = nullptr;
+  size_t lds = 0;
+  switch (dh) {
+    case 32: fn = (const void*)attn_kernel<AT, 32>; lds = attn_lds_size<32>(); break;
+    case 64: fn = (const void*)attn_kernel<AT, 64>; lds = attn_lds_size<64>(); break;
+    case 128: fn = (const void*)attn_kernel<AT, 128>; lds = attn_lds_size<128>(); break;
+    case 256: fn = (const void*)attn_kernel<AT, 256>; lds = attn_lds_size<256>(); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  switch (dh) {
+    case 32: AE_LAUNCH((attn_kernel<AT, 32>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    case 64: AE_LAUNCH((attn_kernel<AT, 64>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    case 128: AE_LAUNCH((attn_kernel<AT, 128>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    default: AE_LAUNCH((attn_kernel<AT, 256>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+  }
+  return hipGetLastError();
 }
 
 struct Dispatch {
@@ -369,24 +371,17 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   });
 
   const int gq = nq / nkv, R = gq * H;
-  const int KC = h->at == AT_BF16 ? 64 : 32;
   AttnArgs aa{};
-  aa.q = h->q; aa.ks = h->sk; aa.vsT = h->vsT; aa.kcache = h->kcache; aa.vcacheT = h->vcache;
+  aa.q = h->q; aa.ks = h->ks; aa.vs = h->vs; aa.kcache = h->kcache; aa.vcache = h->vcache;
   aa.seq_slot = seq_slot;
-  aa.kslot_stride = h->slot_elems; aa.vslot_stride = h->vslot_elems;
-  aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh; aa.KC = KC;
-  aa.ldq = h->ld_q; aa.ldkv = h->ld_kv; aa.ldvt = h->ld_vt; aa.ldp = h->ld_p; aa.ldo = h->ld_q;
-  aa.n_qt = (R + 63) / 64; aa.n_chunks = (c.prefix_len + H + KC - 1) / KC;
+  aa.slot_stride = h->slot_elems;
+  aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh;
+  aa.nbp = h->nbp; aa.nbs = h->nbs; aa.ldo = h->ld_q;
+  aa.n_qt = h->n_qt;
+  aa.n_split = attn_splits(h->nbp + h->nbs);
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
-  aa.opart = h->opart; aa.mlpart = h->mlpart; aa.qt_counter = h->qt_counter; aa.err = h->err_flag; aa.o = h->o;
-  const int attn_wgs = aa.n_chunks * aa.n_qt * n_seq * nkv;
+  aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
   aa.trace_id = 1;
-  aa.p_aligned = (c.prefix_len % (h->at == AT_BF16 ? 8 : 4)) == 0;
-  // In-kernel combine (AE_ATTN_FUSED=1) only when every workgroup is co-resident, so the wait is
-  // safe; measured slower than a separate combine launch on MI355X, hence off by default.
-  aa.fused = 0;
-  if (const char* e = getenv("AE_ATTN_FUSED")) aa.fused = (attn_wgs <= h->n_cu && atoi(e) != 0) ? 1 : 0;
-  const size_t attn_lds = attn_lds_bytes(h->at, dh);
 
   for (int l = 0; l < c.n_layers; ++l) {
     GemmArgs g{};
@@ -395,28 +390,25 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     // --- norm1 + QKV + RoPE
     {
       GemmArgs a = g;
-      a.w = h->qkv_p[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_q; a.ldkv = h->ld_kv;
+      a.w = h->qkv_p[l]; a.x = h->hb; a.ldx = h->ld_h;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().qkv, n_z).S;
-      a.q_out = h->q; a.k_out = h->sk; a.v_out = h->vsT; a.ldvt = h->ld_vt; a.rope_cs = h->rope_cs;
+      a.q_out = h->q; a.k_out = h->ks; a.v_out = h->vs; a.n_qt = h->n_qt; a.nbs = h->nbs; a.rope_cs = h->rope_cs;
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
       a.trace_id = 0;
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
     // --- attention over [prefix ; suffix]
-    aa.klayer_off = (size_t)l * c.prefix_len * nkv * dh;
-    aa.vlayer_off = (size_t)l * nkv * dh * h->ld_p;
-    const dim3 attn_grid(aa.n_chunks, aa.n_qt, n_seq * nkv);
+    aa.layer_off = (size_t)l * nkv * h->nbp * ATT_KB * dh;
+    const dim3 attn_grid(aa.n_split, aa.n_qt, n_seq * nkv);
     LAUNCH_CHECK(h, "attn", {
-      if (h->at == AT_BF16) (void)(attn_dispatch<AT_BF16, 64>)(dh, false, attn_lds, attn_grid, st, aa);
-      else (void)(attn_dispatch<AT_F32, 32>)(dh, false, attn_lds, attn_grid, st, aa);
+      if (h->at == AT_BF16) (void)attn_dispatch<AT_BF16>(dh, false, attn_grid, st, aa);
+      else (void)attn_dispatch<AT_F32>(dh, false, attn_grid, st, aa);
     });
-    if (!aa.fused) {
-      LAUNCH_CHECK(h, "attn_combine", {
-        if (h->at == AT_BF16)
-          AE_LAUNCH(attn_combine<AT_BF16>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa);
-        else
-          AE_LAUNCH(attn_combine<AT_F32>, dim3(R, n_seq * nkv), dim3(dh), 0, st, aa);
+    if (aa.n_split > 1) {
+      LAUNCH_CHECK(h, "attn_merge", {
+        if (h->at == AT_BF16) (void)attn_merge_dispatch<AT_BF16>(dh, dim3(aa.n_qt, n_seq * nkv), st, aa);
+        else (void)attn_merge_dispatch<AT_F32>(dh, dim3(aa.n_qt, n_seq * nkv), st, aa);
       });
     }
     // --- o_proj + residual; hb <- h * ln2
@@ -576,8 +568,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->at = c.weight_dtype == AE_F32 ? AT_F32 : AT_BF16;
   h->wt = c.weight_dtype == AE_F32 ? WT_F32 : WT_BF16;
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
-  const size_t lds_need = attn_lds_bytes(h->at, cfg->head_dim);
-  if ((h->at == AT_BF16 ? set_attrs<AT_BF16>(lds_need, cfg->head_dim) : set_attrs<AT_F32>(lds_need, cfg->head_dim)) != hipSuccess ||
+  if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, dim3(), nullptr, AttnArgs{})
+                        : attn_dispatch<AT_F32>(cfg->head_dim, true, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
       set_all_gemm_attrs() != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
@@ -677,14 +669,19 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc_t(h, &h->h, (size_t)Mp * w));
   // activation rows padded by 128 bytes so the rows of one MFMA fragment spread over L2 channels
   const int pad = 128 / aes;
-  h->ld_h = w + pad; h->ld_q = nq * dh + pad; h->ld_kv = nkv * dh + pad; h->ld_u = F + pad;
+  h->ld_h = w + pad; h->ld_q = nq * dh + pad; h->ld_u = F + pad;
   TRY(dalloc(h, &h->hb, (size_t)Mp * h->ld_h * aes));
   TRY(dalloc_t(h, &h->ssp_a, (size_t)(w / 16) * Mp));
   TRY(dalloc_t(h, &h->ssp_b, (size_t)(w / 16) * Mp));
-  TRY(dalloc(h, &h->q, (size_t)Mp * h->ld_q * aes));
-  TRY(dalloc(h, &h->sk, (size_t)Mp * h->ld_kv * aes));
-  h->ld_vt = (H + 7) / 8 * 8;
-  TRY(dalloc(h, &h->vsT, (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv * dh * h->ld_vt * aes));
+  {
+    const size_t seqs = (size_t)std::max(c.max_batch, std::max(1, c.max_taus));
+    h->n_qt = (nq / nkv * H + ATT_ROWS - 1) / ATT_ROWS;
+    h->nbs = (H + ATT_KB - 1) / ATT_KB;
+    h->nbp = (P + ATT_KB - 1) / ATT_KB;
+    TRY(dalloc(h, &h->q, seqs * nkv * h->n_qt * ATT_ROWS * dh * aes));
+    TRY(dalloc(h, &h->ks, seqs * nkv * h->nbs * ATT_KB * dh * aes));
+    TRY(dalloc(h, &h->vs, seqs * nkv * h->nbs * ATT_KB * dh * aes));
+  }
   TRY(dalloc(h, &h->o, (size_t)Mp * h->ld_q * aes));
   TRY(dalloc(h, &h->u, (size_t)Mp * h->ld_u * aes));
   {
@@ -694,14 +691,12 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc_t(h, &h->part, h->part_floats));
     h->n_counters = maxg * n_z;
     TRY(dalloc_t(h, &h->counters, h->n_counters));
-    const int KC = h->at == AT_BF16 ? 64 : 32;
     const int R = nq / nkv * H;
-    const size_t n_qt = (R + 63) / 64, n_chunks = (P + H + KC - 1) / KC;
+    const size_t n_qt = (R + ATT_ROWS - 1) / ATT_ROWS;
+    const size_t n_split = attn_splits((P + ATT_KB - 1) / ATT_KB + (H + ATT_KB - 1) / ATT_KB);
     const size_t n_zz = (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv;
-    TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_chunks * 64 * dh));
-    TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_chunks * 64 * 2));
-    TRY(dalloc_t(h, &h->qt_counter, n_zz * n_qt));
-    TRY(dalloc_t(h, &h->err_flag, 1));
+    TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_split * ATT_ROWS * dh));
+    TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_split * ATT_ROWS * 2));
   }
   {
     std::vector<float> cs((size_t)H * (dh / 2) * 2);
@@ -713,11 +708,9 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
       }
     TRY(upload(h, (void**)&h->rope_cs, cs.data(), cs.size() * 4));
   }
-  h->slot_elems = (size_t)L * P * nkv * dh;
-  h->ld_p = (P + 7) / 8 * 8;
-  h->vslot_elems = (size_t)L * nkv * dh * h->ld_p;
+  h->slot_elems = (size_t)L * nkv * h->nbp * ATT_KB * dh;
   TRY(dalloc(h, &h->kcache, h->slot_elems * c.max_batch * kes));
-  TRY(dalloc(h, &h->vcache, h->vslot_elems * c.max_batch * kes));
+  TRY(dalloc(h, &h->vcache, h->slot_elems * c.max_batch * kes));
   h->slot_ready.assign(c.max_batch, 0);
   {
     std::vector<int> ids(c.max_batch);
@@ -748,32 +741,32 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
   const ae_config& c = h->c;
   const size_t es = dtype_size(c.kv_dtype);
-  const size_t kbytes = h->slot_elems * es;
-  if (kbytes) {
-    HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * kbytes, k, kbytes, hipMemcpyHostToDevice));
-    // V is kept transposed per layer and kv head: [L][n_kv][dh][ld_p], keys contiguous
-    const int L = c.n_layers, P = c.prefix_len, nkv = c.n_kv_heads, dh = c.head_dim, ldp = h->ld_p;
-    std::vector<unsigned char> vt(h->vslot_elems * es, 0);
-    const unsigned char* src = (const unsigned char*)v;
+  const size_t bytes = h->slot_elems * es;
+  if (bytes) {
+    // repack into the attention's fragment order (see the attention section of the kernels):
+    // per layer and kv head, 32-key blocks; keys past prefix_len stay zero
+    const int L = c.n_layers, P = c.prefix_len, nkv = c.n_kv_heads, dh = c.head_dim, nbp = h->nbp;
+    const int nkb = dh / 32;
+    std::vector<unsigned char> kp(bytes, 0), vp(bytes, 0);
+    const unsigned char* ksrc = (const unsigned char*)k;
+    const unsigned char* vsrc = (const unsigned char*)v;
     for (int l = 0; l < L; ++l)
       for (int j = 0; j < P; ++j)
-        for (int g = 0; g < nkv; ++g)
-          for (int d = 0; d < dh; ++d)
-            memcpy(&vt[((((size_t)l * nkv + g) * dh + d) * ldp + j) * es], src + ((((size_t)l * P + j) * nkv + g) * dh + d) * es, es);
-    HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * vt.size(), vt.data(), vt.size(), hipMemcpyHostToDevice));
+        for (int g = 0; g < nkv; ++g) {
+          const size_t blk = (((size_t)l * nkv + g) * nbp + j / 32) * 32 * dh;  // block base (elements)
+          const int kk = j % 32, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+          const size_t srow = (((size_t)l * P + j) * nkv + g) * dh;
+          for (int d = 0; d < dh; ++d) {
+            const size_t kidx = blk + ((size_t)(kt * nkb + d / 32) * 64 + ((d % 32) / 8) * 16 + m) * 8 + (d & 7);
+            const size_t vidx = blk + ((size_t)(d / 16) * 64 + (kk / 8) * 16 + (d & 15)) * 8 + (kk & 7);
+            memcpy(&kp[kidx * es], ksrc + (srow + d) * es, es);
+            memcpy(&vp[vidx * es], vsrc + (srow + d) * es, es);
+          }
+        }
+    HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * bytes, kp.data(), bytes, hipMemcpyHostToDevice));
+    HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * bytes, vp.data(), bytes, hipMemcpyHostToDevice));
   }
   h->slot_ready[slot] = 1;
-  return AE_OK;
-}
-
-// A fused attention combine whose wait timed out (workgroups not co-resident) leaves a flag.
-static int check_err_flag(ae_handle* h) {
-  unsigned e = 0;
-  HIP_TRY(h, hipMemcpy(&e, h->err_flag, sizeof(e), hipMemcpyDeviceToHost));
-  if (e) {
-    HIP_TRY(h, hipMemset(h->err_flag, 0, sizeof(e)));
-    return fail(h, AE_ERR_HIP, "attention combine wait timed out");
-  }
   return AE_OK;
 }
 
@@ -817,8 +810,6 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  int rc2 = check_err_flag(h);
-  if (rc2) return rc2;
   memcpy(actions_out, tmp.data(), bytes);
   return AE_OK;
 }
@@ -886,8 +877,6 @@ int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, co
   HIP_TRY(h, hipMemcpyAsync(d.data(), h->dist, d.size() * sizeof(float), hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  int rc2 = check_err_flag(h);
-  if (rc2) return rc2;
   *accept_len = acc;
   *gripper_switch = sw;
   if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
@@ -974,7 +963,7 @@ int kernel_times_in_place(ae_handle* h, Enq& enqueue, const std::vector<std::str
     ++n;
   }
   *n_stats = n;
-  return check_err_flag(h);
+  return AE_OK;
 }
 }  // namespace
 
@@ -1046,7 +1035,7 @@ int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_
     ++n;
   }
   *n_stats = n;
-  return check_err_flag(h);
+  return AE_OK;
 }
 
 #ifdef AE_TRACE
