@@ -105,6 +105,63 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   return 0.5f * x * (1.0f + tanhf(u));
 }
 
+// ------------------------------------------------------------------ L2 prefetch of the next kernel's operands
+//
+// A kernel's working set arrives from HBM about 2 us after it asks; the same
+// bytes already in its XCD's L2 arrive in a fraction of that, and L2 contents
+// survive kernel boundaries. A GEMM whose HBM traffic is over once its main
+// loop is done (no split-K exchange follows) therefore touches, one dword per
+// 128-byte line, what the next kernel will read while it reduces and runs its
+// epilogue, placing each line in the L2 of the XCD where the consumer
+// workgroup will run (workgroup i of a launch runs on XCD i % 8). A fixed
+// number of touches per thread, no branch: unused slots reread a line of the
+// kernel's own weights.
+struct Prefetch {
+  const char* base;         // kind 1: first region; kind 2: next kernel's packed weights
+  const char* base2;        // kind 1: second region
+  const char* dummy;        // a line this kernel reads anyway
+  unsigned long long bytes; // kind 1: bytes of each region
+  int kind;                 // 0: none, 1: whole regions into every XCD's L2, 2: next GEMM's weights
+  int next_groups, next_S, NT, KB, frag_bytes;  // kind 2: next launch's tiling
+};
+
+template <int NL>
+__device__ __forceinline__ int prefetch_issue(const Prefetch& pf, unsigned wg, unsigned n_wg, unsigned tid, unsigned nthr) {
+  const unsigned c8 = n_wg >= 8 ? n_wg / 8 : 1;  // this launch's workgroups per XCD
+  const unsigned xcd = wg % 8, j0 = wg / 8;
+  const bool wg_ok = pf.kind != 0 && wg < c8 * 8;
+  int acc = 0;
+#pragma unroll
+  for (int k = 0; k < NL; ++k) {
+    const unsigned L = tid + nthr * k;  // this workgroup's k-th touch slot
+    bool ok = wg_ok;
+    const char* a1;
+    if (pf.kind == 1) {  // every XCD gets every line: the c8 workgroups of an XCD interleave them
+      const unsigned long long lines1 = pf.bytes / 128;
+      const unsigned long long Lg = j0 + (unsigned long long)c8 * L;
+      ok = ok && Lg < 2 * lines1;
+      a1 = Lg < lines1 ? pf.base + Lg * 128 : pf.base2 + (Lg - lines1) * 128;
+    } else {  // the lines of next-launch workgroups i = xcd + 8 (j0 + m c8), m = 0, 1, ...
+      const unsigned kbs = pf.KB / max(pf.next_S, 1);
+      const unsigned lpt = max(kbs * pf.frag_bytes / 128, 1u);  // lines per tile range
+      const unsigned lpw = max(pf.NT, 1) * lpt;                 // lines per next workgroup
+      const unsigned m = L / lpw, r = L % lpw;
+      const unsigned i = xcd + 8 * (j0 + m * c8);
+      ok = ok && pf.kind == 2 && i < (unsigned)(pf.next_groups * pf.next_S);
+      const unsigned g = i % max(pf.next_groups, 1), sp = i / max(pf.next_groups, 1);
+      const unsigned long long off =
+          ((unsigned long long)(g * pf.NT + r / lpt) * pf.KB + (unsigned long long)sp * kbs) * pf.frag_bytes +
+          (unsigned long long)(r % lpt) * 128;
+      a1 = pf.base + off;
+    }
+    acc ^= *(const int*)(ok ? a1 : pf.dummy);
+  }
+  return acc;
+}
+
+// Consume the prefetch values: forces their completion, nothing else.
+__device__ __forceinline__ void prefetch_done(int acc) { asm volatile("" ::"v"(acc)); }
+
 // ------------------------------------------------------------------ GEMM
 
 struct GemmArgs {
@@ -141,6 +198,7 @@ struct GemmArgs {
   int A;
   float dt;              // > 0: x += dt * v; 0: store v
   int trace_id;          // kernel kind for the optional phase trace
+  Prefetch pf;           // next kernel's operands to place in L2 (QKV and gate/up launches only)
 };
 
 constexpr int GW = 8;         // waves per GEMM workgroup
@@ -219,9 +277,9 @@ constexpr size_t gemm_lds_size() {
 // pass wave w owns KPW consecutive k-blocks: it issues its weight fragments
 // and the 64 x (KPW*32) activation slice as whole 128-byte lines (half the
 // L2 requests of fragment-shaped loads), parks the slice in its own LDS
-// region and reads the MFMA B fragments from there. No predication:
-// activation buffers hold whole 64-row groups. The 8 partial tiles are summed
-// in LDS.
+// region and reads the MFMA B fragments from there. Rows past M are not
+// read (zeros are staged instead), so the padding of the last 64-row group
+// costs no traffic. The 8 partial tiles are summed in LDS.
 template <int WT, int AT, int EPI, int NT, int KPW>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   typedef typename Act<AT>::T XT;
@@ -301,9 +359,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < KPW; ++j) wa[nt][j] = F::load_a(a.w, ((size_t)g * NT + nt) * KB + kb0 + j, lane);
+    // activation rows past M (padding of the last token group) are not read: zeros go to LDS
     i32x4 xr[NI];
 #pragma unroll
-    for (int i = 0; i < NI; ++i) xr[i] = *(const i32x4*)(xg + i * xrow_step + (size_t)kb0 * KBLK * sizeof(XT));
+    for (int i = 0; i < NI; ++i)
+      xr[i] = (tok0 + lr + i * RPI < a.M) ? *(const i32x4*)(xg + i * xrow_step + (size_t)kb0 * KBLK * sizeof(XT))
+                                          : i32x4{0, 0, 0, 0};
     __builtin_amdgcn_sched_barrier(0);  // keep every load of the pass in flight before the first LDS store
 #pragma unroll
     for (int i = 0; i < NI; ++i) *(i32x4*)(xs + (size_t)(i * RPI + lr) * RS + lc * 16) = xr[i];
@@ -317,6 +378,12 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       }
   }
 
+  // next kernel's operands into L2 while this one reduces and runs its epilogue (no
+  // split-K exchange in these roles, so nothing below waits on memory before the end)
+  int pf_acc = 0;
+  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
+    pf_acc = prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                               gridDim.x * gridDim.y * gridDim.z, threadIdx.x, GTHREADS);
   AE_TR(1);
   float ssq = 0.f;
 #pragma unroll
@@ -475,6 +542,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       }
     }
   }
+  prefetch_done(pf_acc);
 #ifdef AE_TRACE
   wait_mem();
   AE_TR(4);
