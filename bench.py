@@ -41,6 +41,27 @@ def kernel_bytes(cfg):
     }
 
 
+def measured_traffic():
+    """HBM bytes per launch of each kernel from the committed rocprofv3 counter summary, or {} when
+    the kernel sources have changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_pi0_bf16_kernels.md")
+    if not os.path.exists(path):
+        return {}
+    sha = hashlib.sha256()
+    for f in ("ae_kernels.hpp", "ae_runtime.hip"):
+        with open(os.path.join(ROOT, "flow_matching_action_euler_amd", "csrc", f), "rb") as fh:
+            sha.update(fh.read())
+    want, table = None, {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("traffic_source_sha256_16:"):
+                want = line.split(":", 1)[1].strip()
+            elif line.startswith("traffic_bytes_per_launch:"):
+                table = json.loads(line.split(":", 1)[1])
+    return table if want == sha.hexdigest()[:16] else {}
+
+
 def step_bytes(cfg, batch):
     kb = kernel_bytes(cfg)
     per_layer = kb["qkv_rope"] + kb["o_proj_resid"] + kb["gate_up_geglu"] + kb["down_resid"]
@@ -81,6 +102,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-iters", type=int, default=3, help="replays of each per-kernel timing graph")
     ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel timing pass")
+    ap.add_argument("--copy-kernel-mib", type=int, default=0,
+                    help="after the timed loop, run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported (the path has no multi-GPU leg)",
@@ -125,6 +148,13 @@ def main():
     ms_per_chunk = elapsed * 1e3 / args.steps
     out = d_out.cpu().numpy()
     assert np.all(np.isfinite(out))
+    if args.copy_kernel_mib > 0:  # known traffic: reads and writes copy_kernel_mib MiB once per copy
+        src = torch.ones(args.copy_kernel_mib << 18, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     # Per-kernel timing on the library's stream. "in place": the chunk's launches in their
     # normal order, each with a HIP start/stop event pair bound to its dispatch, so a kernel is
@@ -148,6 +178,10 @@ def main():
                 entry["alg_bytes"] = per_launch
                 entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
             kernels[name] = entry
+    traffic = measured_traffic() if cfg.name == "pi0_bf16" else {}
+    for name, entry in kernels.items():
+        if name in traffic:
+            entry["traffic_bytes"] = traffic[name]
     dom = max(kernels, key=lambda n: kernels[n]["ms_per_chunk"]) if kernels else None
     sb = step_bytes(cfg, B)
     achieved = kernels[dom].get("GBs") if dom else None
@@ -173,7 +207,8 @@ def main():
         "whole_chunk_GBs": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9, 1),
         "whole_chunk_hbm_frac": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
+                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
+                     "traffic": traffic.get(dom) if dom else None},
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:
