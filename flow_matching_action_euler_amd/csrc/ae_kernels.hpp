@@ -619,7 +619,7 @@ struct AttnArgs {
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
 constexpr int ATT_KB = 32;     // keys per wave block
 constexpr int ATT_WAVES = 8;   // waves per workgroup
-constexpr int ATT_IT = 1;      // key blocks per wave (a split covers ATT_WAVES * ATT_IT blocks)
+constexpr int ATT_IT = 4;      // key blocks per wave (a split covers ATT_WAVES * ATT_IT blocks)
 
 template <int DH>
 constexpr size_t attn_lds_size() {  // per-wave O and (m, l), then the query tile (fp32 at most)
