@@ -612,6 +612,9 @@ struct AttnArgs {
   float scale_log2;       // log2(e) / sqrt(dh)
   float* opart;           // [zz][qt][split][16][dh] merged split partials
   float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum)
+  unsigned* qt_counter;   // [zz][qt] split arrivals (monotonic), co-resident merge only
+  unsigned* err;          // set if a co-resident merge wait timed out
+  int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
   void* o;                // [rows][ldo] output
   int trace_id;
 };
@@ -619,11 +622,12 @@ struct AttnArgs {
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
 constexpr int ATT_KB = 32;     // keys per wave block
 constexpr int ATT_WAVES = 8;   // waves per workgroup
-constexpr int ATT_IT = 4;      // key blocks per wave (a split covers ATT_WAVES * ATT_IT blocks)
+constexpr int ATT_IT_SPLIT = 1;   // key blocks per wave when the splits merge in-kernel
+constexpr int ATT_IT_WHOLE = 4;   // key blocks per wave otherwise (a split covers 8 * 4 blocks)
 
 template <int DH>
-constexpr size_t attn_lds_size() {  // per-wave O and (m, l), then the query tile (fp32 at most)
-  return (size_t)ATT_WAVES * ATT_ROWS * (DH + 4) * 4 + (size_t)ATT_WAVES * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4;
+constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp32 at most), a flag
+  return (size_t)ATT_WAVES * ATT_ROWS * (DH + 4) * 4 + (size_t)ATT_WAVES * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4 + 16;
 }
 
 // Attention of suffix query rows over [prefix ; suffix] keys. Grid (n_split,
@@ -637,7 +641,7 @@ constexpr size_t attn_lds_size() {  // per-wave O and (m, l), then the query til
 // the next block as soon as its S^T is done, its V fragments as soon as its
 // O^T is done. The waves merge (m, l, O) in LDS; with one split the workgroup
 // writes o, with several it stores its partial for attn_merge.
-template <int AT, int DH>
+template <int AT, int DH, int ATT_IT>
 __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT_BF16, AT> F;
@@ -838,18 +842,101 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- several splits: store this split's partial; attn_merge combines them after the launch boundary
+  const size_t tile = (size_t)zz * a.n_qt + qt;
+  if (!a.coresident) {
+    // ---- several splits: store this split's partial; attn_merge combines them after the launch boundary
+    if (active) {
+      const size_t pbase = ((tile * a.n_split + split) * ATT_ROWS + row) * DH + d0;
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) *(float4*)(a.opart + pbase + i) = make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]);
+      if (threadIdx.x % TPR == 0)
+        *(float2*)(a.mlpart + ((tile * a.n_split + split) * ATT_ROWS + row) * 2) = make_float2(M, L);
+    }
+#ifdef AE_TRACE
+    wait_mem();
+    AE_TR(4);
+#endif
+    return;
+  }
+
+  // ---- co-resident splits: publish the partial write-through, meet the other splits of this
+  // query tile at a counter (bounded wait), then each split merges a share of the 16 rows
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
   if (active) {
-    const size_t tile = (size_t)zz * a.n_qt + qt;
     const size_t pbase = ((tile * a.n_split + split) * ATT_ROWS + row) * DH + d0;
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4) *(float4*)(a.opart + pbase + i) = make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]);
-    if (threadIdx.x % TPR == 0)
-      *(float2*)(a.mlpart + ((tile * a.n_split + split) * ATT_ROWS + row) * 2) = make_float2(M, L);
+    for (int i = 0; i < DPT; i += 4)
+      st16_coherent(ro, (unsigned)((pbase + i) * 4), make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
+    if (threadIdx.x % TPR == 0) {
+      const size_t mi = ((tile * a.n_split + split) * ATT_ROWS + row) * 2;
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(M), rm, (unsigned)(mi * 4), 0, 0x10);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(L), rm, (unsigned)(mi * 4 + 4), 0, 0x10);
+    }
   }
+  wait_mem();
+  __syncthreads();
+  int* go = (int*)(Qs + NKB * FR);  // flag past the query tile
+  if (threadIdx.x == 0) {
+    unsigned* cnt = a.qt_counter + tile;
+    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const unsigned target = (old / a.n_split + 1) * a.n_split;
+    int ok = 0;
+    for (int it = 0; it < (1 << 20); ++it) {
+      if ((int)(ldu_coherent(cnt) - target) >= 0) { ok = 1; break; }
+      __builtin_amdgcn_s_sleep(1);
+    }
+    if (!ok) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *go = ok;
+  }
+  __syncthreads();
+  AE_TR(4);
+  if (!*go) return;
+  // rows [split * rps, +rps) of the tile: thread -> (row, 4 dims)
+  const int rps = (ATT_ROWS + a.n_split - 1) / a.n_split;
+  const int t4 = threadIdx.x % (DH / 4), rr = split * rps + (int)threadIdx.x / (DH / 4);
+  if ((int)threadIdx.x >= rps * (DH / 4) || rr >= ATT_ROWS) return;
+  const int r2 = qt * ATT_ROWS + rr;
+  if (r2 >= R) return;
+  float M2 = -INFINITY, L2 = 0.f;
+  float4 O2 = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int c0 = 0; c0 < a.n_split; c0 += 8) {
+    float mc[8], lc[8];
+    float4 oc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {  // unconditional loads: indices past n_split reread split 0, weighted 0
+      const int sp = c0 + c < a.n_split ? c0 + c : 0;
+      const size_t mi = ((tile * a.n_split + sp) * ATT_ROWS + rr) * 2;
+      mc[c] = ld_coherent_buf(rm, (unsigned)(mi * 4));
+      lc[c] = ld_coherent_buf(rm, (unsigned)(mi * 4 + 4));
+      oc[c] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ro, (unsigned)((((tile * a.n_split + sp) * ATT_ROWS + rr) * DH + t4 * 4) * 4), 0, 0x10));
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c0 + c >= a.n_split) mc[c] = -INFINITY;
+    float Mn = M2;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) Mn = fmaxf(Mn, mc[c]);
+    const float sc = (M2 == -INFINITY) ? 0.f : exp2f(M2 - Mn);
+    L2 *= sc;
+    O2.x *= sc; O2.y *= sc; O2.z *= sc; O2.w *= sc;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const float wt = (mc[c] == -INFINITY) ? 0.f : exp2f(mc[c] - Mn);
+      L2 += wt * lc[c];
+      O2.x += wt * oc[c].x; O2.y += wt * oc[c].y; O2.z += wt * oc[c].z; O2.w += wt * oc[c].w;
+    }
+    M2 = Mn;
+  }
+  XT* op2 = (XT*)a.o + (size_t)(s * a.H + r2 % a.H) * a.ldo + (size_t)(g * gq + r2 / a.H) * DH + t4 * 4;
+  const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
+  Act<AT>::st(op2, 0, O2.x * inv);
+  Act<AT>::st(op2, 1, O2.y * inv);
+  Act<AT>::st(op2, 2, O2.z * inv);
+  Act<AT>::st(op2, 3, O2.w * inv);
 #ifdef AE_TRACE
   wait_mem();
-  AE_TR(4);
+  AE_TR(5);
 #endif
 }
 

@@ -113,6 +113,9 @@ struct ae_handle {
   unsigned* counters = nullptr;
   size_t n_counters = 0;
   float *opart = nullptr, *mlpart = nullptr;
+  unsigned* qt_counter = nullptr;   // co-resident attention merge arrivals [zz][qt]
+  unsigned* err_flag = nullptr;     // set by a kernel whose bounded wait timed out
+  size_t n_qt_counters = 0;
   int n_qt = 0, nbp = 0, nbs = 0;  // 16-row query tiles, 32-key prefix / suffix blocks
   int n_cu = 0;
   float* rope_cs = nullptr;
@@ -282,11 +285,40 @@ struct Splits {
 };
 const Splits& splits() { static Splits s; return s; }
 
-// Key splits of the attention: one workgroup per query tile runs up to ATT_IT blocks of 32 keys
-// per wave; longer contexts are split and merged by attn_merge.
-int attn_splits(int n_blocks) { return std::max(1, (n_blocks + ATT_IT * ATT_WAVES - 1) / (ATT_IT * ATT_WAVES)); }
+// Key splits when each wave walks `it` blocks of ATT_KB keys.
+int attn_splits(int n_blocks, int it) { return std::max(1, (n_blocks + it * ATT_WAVES - 1) / (it * ATT_WAVES)); }
 
-// Attention kernels are instantiated per (activation type, head_dim).
+// Attention kernels are instantiated per (activation type, head_dim, blocks per wave).
+template <int AT, int IT>
+hipError_t attn_dispatch_it(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  const void* fn = nullptr;
+  size_t lds = 0;
+  switch (dh) {
+    case 32: fn = (const void*)attn_kernel<AT, 32, IT>; lds = attn_lds_size<32>(); break;
+    case 64: fn = (const void*)attn_kernel<AT, 64, IT>; lds = attn_lds_size<64>(); break;
+    case 128: fn = (const void*)attn_kernel<AT, 128, IT>; lds = attn_lds_size<128>(); break;
+    case 256: fn = (const void*)attn_kernel<AT, 256, IT>; lds = attn_lds_size<256>(); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  switch (dh) {
+    case 32: AE_LAUNCH((attn_kernel<AT, 32, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    case 64: AE_LAUNCH((attn_kernel<AT, 64, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    case 128: AE_LAUNCH((attn_kernel<AT, 128, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    default: AE_LAUNCH((attn_kernel<AT, 256, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+  }
+  return hipGetLastError();
+}
+template <int AT>
+hipError_t attn_dispatch(int dh, bool set_attr, bool split_it, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  if (set_attr) {
+    hipError_t e = attn_dispatch_it<AT, ATT_IT_SPLIT>(dh, true, grid, st, aa);
+    return e != hipSuccess ? e : attn_dispatch_it<AT, ATT_IT_WHOLE>(dh, true, grid, st, aa);
+  }
+  return split_it ? attn_dispatch_it<AT, ATT_IT_SPLIT>(dh, false, grid, st, aa)
+                  : attn_dispatch_it<AT, ATT_IT_WHOLE>(dh, false, grid, st, aa);
+}
+
 template <int AT>
 hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   switch (dh) {
@@ -298,25 +330,22 @@ hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs
   return hipGetLastError();
 }
 
-template <int AT>
-hipError_t attn_dispatch(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
-  const void* fn = nullptr;
-  size_t lds = 0;
-  switch (dh) {
-    case 32: fn = (const void*)attn_kernel<AT, 32>; lds = attn_lds_size<32>(); break;
-    case 64: fn = (const void*)attn_kernel<AT, 64>; lds = attn_lds_size<64>(); break;
-    case 128: fn = (const void*)attn_kernel<AT, 128>; lds = attn_lds_size<128>(); break;
-    case 256: fn = (const void*)attn_kernel<AT, 256>; lds = attn_lds_size<256>(); break;
-    default: return hipErrorInvalidValue;
-  }
-  if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  switch (dh) {
-    case 32: AE_LAUNCH((attn_kernel<AT, 32>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    case 64: AE_LAUNCH((attn_kernel<AT, 64>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    case 128: AE_LAUNCH((attn_kernel<AT, 128>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    default: AE_LAUNCH((attn_kernel<AT, 256>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-  }
-  return hipGetLastError();
+// How the attention covers the keys: n_split workgroups per query tile and blocks per wave.
+// Splits of one block per wave merge in-kernel when every workgroup of the launch fits on
+// the device at once (one per compute unit); otherwise a workgroup walks up to 4 blocks per
+// wave and longer contexts fall back to attn_merge.
+struct AttnPlan {
+  int n_split, split_it, coresident;
+};
+AttnPlan attn_plan(const ae_handle* h, int n_seq) {
+  static const bool allow = [] {
+    const char* e = getenv("AE_ATTN_CORESIDENT");
+    return !e || atoi(e) != 0;
+  }();
+  const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
+  const int ns = attn_splits(nb, ATT_IT_SPLIT);
+  if (allow && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, 1, 1};
+  return {attn_splits(nb, ATT_IT_WHOLE), 0, 0};
 }
 
 struct Dispatch {
@@ -390,7 +419,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh;
   aa.nbp = h->nbp; aa.nbs = h->nbs; aa.ldo = h->ld_q;
   aa.n_qt = h->n_qt;
-  aa.n_split = attn_splits(h->nbp + h->nbs);
+  const AttnPlan plan = attn_plan(h, n_seq);
+  aa.n_split = plan.n_split;
+  aa.coresident = plan.coresident;
+  aa.qt_counter = h->qt_counter;
+  aa.err = h->err_flag;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
   aa.trace_id = 1;
@@ -420,10 +453,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     aa.layer_off = (size_t)l * nkv * h->nbp * ATT_KB * dh;
     const dim3 attn_grid(aa.n_split, aa.n_qt, n_seq * nkv);
     LAUNCH_CHECK(h, "attn", {
-      if (h->at == AT_BF16) (void)attn_dispatch<AT_BF16>(dh, false, attn_grid, st, aa);
-      else (void)attn_dispatch<AT_F32>(dh, false, attn_grid, st, aa);
+      if (h->at == AT_BF16) (void)attn_dispatch<AT_BF16>(dh, false, plan.split_it, attn_grid, st, aa);
+      else (void)attn_dispatch<AT_F32>(dh, false, plan.split_it, attn_grid, st, aa);
     });
-    if (aa.n_split > 1) {
+    if (aa.n_split > 1 && !aa.coresident) {
       LAUNCH_CHECK(h, "attn_merge", {
         if (h->at == AT_BF16) (void)attn_merge_dispatch<AT_BF16>(dh, dim3(aa.n_qt, n_seq * nkv), st, aa);
         else (void)attn_merge_dispatch<AT_F32>(dh, dim3(aa.n_qt, n_seq * nkv), st, aa);
@@ -591,8 +624,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->at = c.weight_dtype == AE_F32 ? AT_F32 : AT_BF16;
   h->wt = c.weight_dtype == AE_F32 ? WT_F32 : WT_BF16;
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
-  if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, dim3(), nullptr, AttnArgs{})
-                        : attn_dispatch<AT_F32>(cfg->head_dim, true, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
+  if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})
+                        : attn_dispatch<AT_F32>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
       set_all_gemm_attrs() != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
@@ -716,10 +749,13 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc_t(h, &h->counters, h->n_counters));
     const int R = nq / nkv * H;
     const size_t n_qt = (R + ATT_ROWS - 1) / ATT_ROWS;
-    const size_t n_split = attn_splits((P + ATT_KB - 1) / ATT_KB + (H + ATT_KB - 1) / ATT_KB);
+    const size_t n_split = attn_splits((P + ATT_KB - 1) / ATT_KB + (H + ATT_KB - 1) / ATT_KB, ATT_IT_SPLIT);
     const size_t n_zz = (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv;
     TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_split * ATT_ROWS * dh));
     TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_split * ATT_ROWS * 2));
+    TRY(dalloc_t(h, &h->qt_counter, n_zz * n_qt));
+    h->n_qt_counters = n_zz * n_qt;
+    TRY(dalloc_t(h, &h->err_flag, 1));
   }
   {
     std::vector<float> cs((size_t)H * (dh / 2) * 2);
@@ -793,6 +829,18 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   return AE_OK;
 }
 
+// A co-resident attention merge whose wait timed out (its workgroups were not all resident)
+// leaves a flag: report it and reset the arrival counters, which are then out of step.
+static int check_err_flag(ae_handle* h) {
+  unsigned e = 0;
+  HIP_TRY(h, hipMemcpy(&e, h->err_flag, sizeof(e), hipMemcpyDeviceToHost));
+  if (!e) return AE_OK;
+  HIP_TRY(h, hipMemset(h->err_flag, 0, sizeof(e)));
+  HIP_TRY(h, hipMemset(h->qt_counter, 0, h->n_qt_counters * sizeof(unsigned)));
+  return fail(h, AE_ERR_HIP, "attention split merge: workgroups were not co-resident (wait timed out); "
+                             "set AE_ATTN_CORESIDENT=0");
+}
+
 static int check_denoise(ae_handle* h, int batch, int steps) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (batch < 1 || batch > h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "batch out of range");
@@ -833,6 +881,10 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  {
+    const int rc_err = check_err_flag(h);
+    if (rc_err) return rc_err;
+  }
   memcpy(actions_out, tmp.data(), bytes);
   return AE_OK;
 }
@@ -900,6 +952,10 @@ int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, co
   HIP_TRY(h, hipMemcpyAsync(d.data(), h->dist, d.size() * sizeof(float), hipMemcpyDeviceToHost, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  {
+    const int rc_err = check_err_flag(h);
+    if (rc_err) return rc_err;
+  }
   *accept_len = acc;
   *gripper_switch = sw;
   if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
