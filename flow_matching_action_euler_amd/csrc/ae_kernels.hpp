@@ -462,6 +462,65 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   }
 
   AE_TR(3);
+  if constexpr (EPI == EPI_QKV) {
+    // q and k tiles: thread -> (token, half of the tile's 16 channels) = 8 consecutive head dims,
+    // rotated and stored as one 16-byte run of a fragment row
+    const int tiles_per_head = a.dh / 16, half = a.dh / 2;
+    const int q_tiles = a.n_q * tiles_per_head, k_tiles = a.n_kv * tiles_per_head;
+    const int t_in = (int)g;  // one tile per workgroup
+    if (t_in < q_tiles + k_tiles) {
+      const int tl = threadIdx.x >> 1, hf = threadIdx.x & 1, tok = tok0 + tl;
+      if (threadIdx.x < 2 * TOKG && tok < a.M) {
+        const bool is_q = t_in < q_tiles;
+        const int tt2 = is_q ? t_in : t_in - q_tiles;
+        const int head = tt2 / tiles_per_head, pair = tt2 % tiles_per_head;
+        const int sq = tok / a.H, t = tok % a.H;
+        const float ir = inv_rms[tl];
+        const float* rr = res + tl * 16;
+        const float4* csp = (const float4*)(a.rope_cs + ((size_t)t * half + pair * 8) * 2);
+        float out[8];
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+          const float4 cs2 = csp[j / 2];  // (cos, sin) of dims pair*8 + j and + j + 1
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const float cs_c = u ? cs2.z : cs2.x, cs_s = u ? cs2.w : cs2.y;
+            const float x1 = rr[j + u] * ir, x2 = rr[8 + j + u] * ir;  // dims d and d + dh/2
+            out[j + u] = hf ? x1 * cs_s + x2 * cs_c : x1 * cs_c - x2 * cs_s;
+          }
+        }
+        const int dfull = hf * half + pair * 8;
+        const int nkb = a.dh / KBLK, lgrp = ((dfull % KBLK) >> 3) << 4, kb = dfull / KBLK;
+        size_t off;
+        if (is_q) {  // query B fragments: row r = j*H + t of the tile, dims kb*32 + (lane/16)*8
+          const int gq = a.n_q / a.n_kv, gg = head / gq, r = (head % gq) * a.H + t;
+          off = ((((size_t)sq * a.n_kv + gg) * a.n_qt + r / 16) * nkb + kb) * 512 + (lgrp + (r & 15)) * 8;
+        } else {     // key A fragments of 32-key block t/32, keys in the order the attention expects
+          const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+          off = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb) * 512 + (lgrp + m) * 8;
+        }
+        XT* dst = (XT*)(is_q ? a.q_out : a.k_out) + off;
+        if constexpr (AT == AT_BF16) {
+          uint4 v;
+          v.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+          v.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+          v.z = (uint32_t)f32_to_bf16(out[4]) | ((uint32_t)f32_to_bf16(out[5]) << 16);
+          v.w = (uint32_t)f32_to_bf16(out[6]) | ((uint32_t)f32_to_bf16(out[7]) << 16);
+          *(uint4*)dst = v;
+        } else {
+          ((float4*)dst)[0] = make_float4(out[0], out[1], out[2], out[3]);
+          ((float4*)dst)[1] = make_float4(out[4], out[5], out[6], out[7]);
+        }
+      }
+      prefetch_done(pf_acc);
+#ifdef AE_TRACE
+      wait_mem();
+      AE_TR(4);
+      AE_TRC(7);
+#endif
+      return;
+    }
+  }
   // ---------------- epilogues: element e -> (nt = e / 1024, token tl = (e / 16) % 64, channel c = e % 16)
 #pragma unroll
   for (int i = 0; i < 2 * NT; ++i) {
