@@ -32,6 +32,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
 
 enum WType { WT_BF16 = 0, WT_FP8 = 1, WT_F32 = 2 };
 enum AType { AT_BF16 = 0, AT_F32 = 1 };
@@ -57,9 +58,17 @@ __device__ unsigned long long ae_trace_buf[8][2048][8];  // [kernel kind][workgr
       if (wg_ < 2048) ae_trace_buf[a.trace_id & 7][wg_][i] = clock64();                                  \
     }                                                                                                    \
   } while (0)
+#define AE_TRV(i, v)                                                                                     \
+  do {                                                                                                   \
+    if (threadIdx.x == 0) {                                                                              \
+      const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);               \
+      if (wg_ < 2048) ae_trace_buf[a.trace_id & 7][wg_][i] = (v);                                        \
+    }                                                                                                    \
+  } while (0)
 #else
 #define AE_TR(i) do { } while (0)
 #define AE_TRC(i) do { } while (0)
+#define AE_TRV(i, v) do { } while (0)
 #endif
 constexpr int KBLK = 32;   // inputs per k-block
 
@@ -176,8 +185,10 @@ struct GemmArgs {
   int passes;           // k-passes per wave: K/32/S = passes * GW * KPW
   int ldx;              // row stride of x in elements (K plus a 128-byte pad)
   int ldo;              // row stride of the activation written by the epilogue
-  float* part;          // split-K partials [S][n_z][n_groups][NT*64*16]
-  unsigned* counters;   // [n_z][n_groups], zero between launches
+  float* part;          // split-K partials [S][n_z][n_groups][NT*64*16], EXCH_EMPTY between launches
+  unsigned* counters;   // [n_z][n_groups], zero between launches (arrival tickets)
+  int exch_poll;        // 1: every workgroup is resident at once; split S-1 polls the others' partials
+  unsigned* err;        // set if a poll gave up
   // EPI_QKV
   void* q_out; void* k_out; void* v_out;   // attention operands in fragment order (see the attention section)
   const float* rope_cs;                    // [H][dh/2][2] cos, sin at positions P + t
@@ -223,6 +234,31 @@ __device__ __forceinline__ void st16_coherent(__amdgpu_buffer_rsrc_t r, unsigned
 }
 __device__ __forceinline__ float ld_coherent_buf(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, byte_off, 0, 0x10));
+}
+__device__ __forceinline__ f32x4 ld16_coherent(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0x10));
+}
+__device__ __forceinline__ void st4_coherent(__amdgpu_buffer_rsrc_t r, unsigned byte_off, unsigned v) {
+  __builtin_amdgcn_raw_buffer_store_b32((int)v, r, byte_off, 0, 0x10);
+}
+
+// Partials exchanged inside one launch (split-K tiles, attention key splits) go
+// to buffers that hold EXCH_EMPTY in every word between launches. A consumer
+// polls the words it needs until none holds it, so it sees each partial arrive
+// in the data itself: the producer neither waits for its stores to be
+// acknowledged nor takes a counter, which saves two dependent round trips
+// across XCDs. The consumer then writes EXCH_EMPTY back over what it read
+// (complete before the next launch starts). EXCH_EMPTY is a NaN that no
+// arithmetic on finite inputs produces; a word is tested on its own, so a
+// 16-byte store seen half-written still reads as not arrived.
+constexpr unsigned EXCH_EMPTY = 0xffffffffu;
+constexpr unsigned long long EXCH_WAIT = 2000000;  // constant-clock ticks (100 MHz: 20 ms) before a poll gives up
+__device__ __forceinline__ bool exch_arrived(float v) { return __float_as_uint(v) != EXCH_EMPTY; }
+__device__ __forceinline__ bool exch_arrived(f32x4 v) {
+  return exch_arrived(v[0]) && exch_arrived(v[1]) && exch_arrived(v[2]) && exch_arrived(v[3]);
+}
+__device__ __forceinline__ void st16_empty(__amdgpu_buffer_rsrc_t r, unsigned byte_off) {
+  __builtin_amdgcn_raw_buffer_store_b128(i32x4{-1, -1, -1, -1}, r, byte_off, 0, 0x10);
 }
 
 
@@ -424,41 +460,90 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 
   AE_TR(2);
   if (a.S > 1) {
-    // split-K: publish the partial (write-through), count arrivals; the last
-    // arriver of (z, g) sums the S partials in split order (deterministic).
     const int n_z = gridDim.z;
     const int tile_elems = NT * 1024;
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part);
+    auto poff = [&](int ss, int qd) {
+      return (unsigned)(((((size_t)ss * n_z + z) * n_groups + g) * tile_elems + qd * 4) * 4);
+    };
+    if (a.exch_poll) {
+      // split-K, all workgroups resident: splits 0..S-2 publish their partial write-through and
+      // leave; split S-1 (the highest workgroup ids of the tile) adds them as they land, in split
+      // order (deterministic), and empties them
+      if (s != a.S - 1) {
 #pragma unroll
-    for (int i = 0; i < (NT + 1) / 2; ++i) {
-      const int qd = threadIdx.x + GTHREADS * i;
-      if (qd < NT * 256)
-        st16_coherent(rp, (unsigned)(((((size_t)s * n_z + z) * n_groups + g) * tile_elems + qd * 4) * 4),
-                      *(const float4*)(res + qd * 4));
-    }
-    wait_mem();
-    __syncthreads();
-    unsigned* cnt = a.counters + z * n_groups + g;
-    if (threadIdx.x == 0) {
-      *ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      if (*ticket == (unsigned)a.S - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    if (*ticket != (unsigned)a.S - 1) return;
-#pragma unroll
-    for (int i = 0; i < (NT + 1) / 2; ++i) {
-      const int qd = threadIdx.x + GTHREADS * i;
-      if (qd < NT * 256) {
-        f32x4 v[4];
-#pragma unroll
-        for (int ss = 0; ss < 4; ++ss)
-          v[ss] = ss < a.S ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                 rp, (unsigned)(((((size_t)ss * n_z + z) * n_groups + g) * tile_elems + qd * 4) * 4), 0, 0x10))
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
-        *(f32x4*)(res + qd * 4) = ((v[0] + v[1]) + v[2]) + v[3];
+        for (int i = 0; i < (NT + 1) / 2; ++i) {
+          const int qd = threadIdx.x + GTHREADS * i;
+          if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
+        }
+        return;
       }
+      bool gave_up = false;
+#pragma unroll
+      for (int i = 0; i < (NT + 1) / 2; ++i) {
+        const int qd = threadIdx.x + GTHREADS * i;
+        if (qd < NT * 256) {
+          f32x4 v[3];
+          const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
+          int polls = 0;
+          for (;; ++polls) {
+            bool ok = true;
+#pragma unroll
+            for (int ss = 0; ss < 3; ++ss) {
+              v[ss] = ss < a.S - 1 ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
+              ok = ok && exch_arrived(v[ss]);
+            }
+            if (ok) break;
+            if (wall_clock64() > t_end) { gave_up = true; break; }
+            __builtin_amdgcn_s_sleep(1);
+          }
+          if (i == 0) AE_TRV(5, polls + 1);
+          const f32x4 own = *(const f32x4*)(res + qd * 4);
+          const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+          f32x4 sum = v[0] + (a.S == 2 ? own : v[1]);
+          sum = sum + (a.S == 3 ? own : v[2]);
+          sum = sum + (a.S == 4 ? own : zero);
+          *(f32x4*)(res + qd * 4) = sum;
+#pragma unroll
+          for (int ss = 0; ss < 3; ++ss)
+            if (ss < a.S - 1) st16_empty(rp, poff(ss, qd));
+        }
+      }
+      if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+    } else {
+      // split-K, more workgroups than fit at once: publish the partial, count arrivals; the
+      // last arriver of (z, g) sums the S partials in split order and empties them
+#pragma unroll
+      for (int i = 0; i < (NT + 1) / 2; ++i) {
+        const int qd = threadIdx.x + GTHREADS * i;
+        if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
+      }
+      wait_mem();
+      __syncthreads();
+      unsigned* cnt = a.counters + z * n_groups + g;
+      if (threadIdx.x == 0) {
+        *ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (*ticket == (unsigned)a.S - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();
+      if (*ticket != (unsigned)a.S - 1) return;
+#pragma unroll
+      for (int i = 0; i < (NT + 1) / 2; ++i) {
+        const int qd = threadIdx.x + GTHREADS * i;
+        if (qd < NT * 256) {
+          f32x4 v[4];
+#pragma unroll
+          for (int ss = 0; ss < 4; ++ss)
+            v[ss] = ss < a.S ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
+          *(f32x4*)(res + qd * 4) = ((v[0] + v[1]) + v[2]) + v[3];
+#pragma unroll
+          for (int ss = 0; ss < 4; ++ss)
+            if (ss < a.S) st16_empty(rp, poff(ss, qd));
+        }
+      }
+      __syncthreads();
     }
-    __syncthreads();
   }
 
   AE_TR(3);
@@ -669,10 +754,9 @@ struct AttnArgs {
   int n_qt;               // 16-row query tiles per (sequence, kv head)
   int n_split;            // key splits (workgroups) per query tile
   float scale_log2;       // log2(e) / sqrt(dh)
-  float* opart;           // [zz][qt][split][16][dh] merged split partials
-  float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum)
-  unsigned* qt_counter;   // [zz][qt] split arrivals (monotonic), co-resident merge only
-  unsigned* err;          // set if a co-resident merge wait timed out
+  float* opart;           // [zz][qt][split][16][dh] split partials, EXCH_EMPTY between launches
+  float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum), same
+  unsigned* err;          // set if a co-resident merge poll gave up
   int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
   void* o;                // [rows][ldo] output
   int trace_id;
@@ -680,28 +764,30 @@ struct AttnArgs {
 
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
 constexpr int ATT_KB = 32;     // keys per wave block
-constexpr int ATT_WAVES = 8;   // waves per workgroup
-constexpr int ATT_IT_SPLIT = 1;   // key blocks per wave when the splits merge in-kernel
-constexpr int ATT_IT_WHOLE = 4;   // key blocks per wave otherwise (a split covers 8 * 4 blocks)
+// Two shapes: splits that merge inside the launch give each of 8 waves one key block
+// (measured: 4 waves x 7 splits read less per compute unit but lose more to the larger
+// exchange); otherwise 8 waves walk up to 4 blocks each (a split covers 32 blocks).
+constexpr int ATT_WAVES_SPLIT = 8, ATT_IT_SPLIT = 1;
+constexpr int ATT_WAVES_WHOLE = 8, ATT_IT_WHOLE = 4;
 
-template <int DH>
-constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp32 at most), a flag
-  return (size_t)ATT_WAVES * ATT_ROWS * (DH + 4) * 4 + (size_t)ATT_WAVES * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4 + 16;
+template <int DH, int NW>
+constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp32 at most)
+  return (size_t)NW * ATT_ROWS * (DH + 4) * 4 + (size_t)NW * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4;
 }
 
 // Attention of suffix query rows over [prefix ; suffix] keys. Grid (n_split,
-// n_qt, n_seq * n_kv), block = 8 waves. A query tile is 16 rows; GQA folds the
+// n_qt, n_seq * n_kv), block = NW waves. A query tile is 16 rows; GQA folds the
 // gq heads of a kv head into rows, so each key is read once per tile. The key
 // blocks of a split (prefix blocks first, then the sequence's suffix blocks)
-// are dealt to the 8 waves round robin; a wave runs an online softmax over its
+// are dealt to the NW waves round robin; a wave runs an online softmax over its
 // blocks. S^T = K Q^T leaves per lane 8 scores of one row that are exactly the
 // B operand of O^T = V^T P^T, so the softmax stays in registers. Loads are
 // pipelined without extra registers: a block's K fragments are reissued for
 // the next block as soon as its S^T is done, its V fragments as soon as its
 // O^T is done. The waves merge (m, l, O) in LDS; with one split the workgroup
 // writes o, with several it stores its partial for attn_merge.
-template <int AT, int DH, int ATT_IT>
-__global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
+template <int AT, int DH, int ATT_IT, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT_BF16, AT> F;
   constexpr int NKB = DH / KBLK;   // 32-dim blocks of a head
@@ -710,8 +796,8 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   constexpr int FR = 512;          // elements per fragment (64 lanes x 8)
   extern __shared__ __attribute__((aligned(16))) float att_smem[];
   float* Ow = att_smem;                                    // [waves][16][LDO]
-  float* MLw = Ow + ATT_WAVES * ATT_ROWS * LDO;            // [waves][16][2]
-  XT* Qs = (XT*)(MLw + ATT_WAVES * ATT_ROWS * 2);          // [NKB][64][8] query fragments
+  float* MLw = Ow + NW * ATT_ROWS * LDO;                   // [waves][16][2]
+  XT* Qs = (XT*)(MLw + NW * ATT_ROWS * 2);                 // [NKB][64][8] query fragments
 
   AE_TR(0);
   const int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
@@ -745,15 +831,15 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   // issued first, the LDS stores wait only for them while the K/V loads below stay in flight
   constexpr int QVEC = 16 / sizeof(XT);  // elements per 16-byte vector
   constexpr int QNV = NKB * FR / QVEC;
-  constexpr int QIT = (QNV + ATT_WAVES * 64 - 1) / (ATT_WAVES * 64);
+  constexpr int QIT = (QNV + NW * 64 - 1) / (NW * 64);
   i32x4 qtmp[QIT];
 #pragma unroll
   for (int i = 0; i < QIT; ++i) {
-    const int e = threadIdx.x + ATT_WAVES * 64 * i;
+    const int e = threadIdx.x + NW * 64 * i;
     qtmp[i] = e < QNV ? *(const i32x4*)(qf + e * QVEC) : i32x4{0, 0, 0, 0};
   }
   __builtin_amdgcn_sched_barrier(0);
-  // this wave's blocks: b_begin + wave + 8 it for it < ATT_IT (the runtime keeps a split within
+  // this wave's blocks: b_begin + wave + NW it for it < ATT_IT (the runtime keeps a split within
   // ATT_IT blocks per wave); a slot past the split's end reads the split's first block, masked.
   // The loop is unrolled with no data-dependent branch so every wait covers exactly the loads it needs.
   const XT* kfs[ATT_IT];
@@ -761,7 +847,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   int nvs[ATT_IT];
 #pragma unroll
   for (int it = 0; it < ATT_IT; ++it) {
-    const int bb = b_begin + wave + ATT_WAVES * it;
+    const int bb = b_begin + wave + NW * it;
     block_src(bb < b_end ? bb : b_begin, kfs[it], vfs[it], nvs[it]);
     if (bb >= b_end) nvs[it] = 0;
   }
@@ -776,7 +862,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int i = 0; i < QIT; ++i) {
-    const int e = threadIdx.x + ATT_WAVES * 64 * i;
+    const int e = threadIdx.x + NW * 64 * i;
     if (e < QNV) *(i32x4*)(Qs + e * QVEC) = qtmp[i];
   }
   AE_TR(1);
@@ -864,10 +950,10 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
   constexpr int TPR = DH / DPT;                      // threads per row
   const bool active = threadIdx.x < ATT_ROWS * TPR;
   const int row = active ? threadIdx.x / TPR : 0, d0 = (threadIdx.x % TPR) * DPT;
-  float mw[ATT_WAVES], lw[ATT_WAVES];
+  float mw[NW], lw[NW];
   float M = -INFINITY;
 #pragma unroll
-  for (int w = 0; w < ATT_WAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float2 ml = *(const float2*)(MLw + (w * ATT_ROWS + row) * 2);
     mw[w] = ml.x;
     lw[w] = ml.y;
@@ -877,7 +963,7 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
 #pragma unroll
   for (int i = 0; i < DPT; ++i) O[i] = 0.f;
 #pragma unroll
-  for (int w = 0; w < ATT_WAVES; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const float wt = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
     L += wt * lw[w];
     const float* src = Ow + ((size_t)w * ATT_ROWS + row) * LDO + d0;
@@ -918,81 +1004,94 @@ __global__ __launch_bounds__(ATT_WAVES * 64) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- co-resident splits: publish the partial write-through, meet the other splits of this
-  // query tile at a counter (bounded wait), then each split merges a share of the 16 rows
+  // ---- co-resident splits: publish the partial write-through; split c then merges rows
+  // [c * rps, +rps) of the tile from every split's partial as the words land (see EXCH_EMPTY)
+  // and empties them. A partial row is DH/4 16-byte chunks; chunk i * TPR + t holds dims
+  // t * DPT + 4 i .. +4, so every store and load instruction covers whole 256-byte runs.
+  // A row's consumer threads share one wave, whose polls end together.
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
+  const size_t prow = (tile * a.n_split + split) * ATT_ROWS;  // this split's first partial row
+  float2* MLs = (float2*)Qs;  // merged (m, l) per row; the query tile is dead by now
   if (active) {
-    const size_t pbase = ((tile * a.n_split + split) * ATT_ROWS + row) * DH + d0;
+    const int tp = threadIdx.x % TPR;
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4)
-      st16_coherent(ro, (unsigned)((pbase + i) * 4), make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]));
-    if (threadIdx.x % TPR == 0) {
-      const size_t mi = ((tile * a.n_split + split) * ATT_ROWS + row) * 2;
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(M), rm, (unsigned)(mi * 4), 0, 0x10);
-      __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(L), rm, (unsigned)(mi * 4 + 4), 0, 0x10);
-    }
-  }
-  wait_mem();
-  __syncthreads();
-  int* go = (int*)(Qs + NKB * FR);  // flag past the query tile
-  if (threadIdx.x == 0) {
-    unsigned* cnt = a.qt_counter + tile;
-    const unsigned old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const unsigned target = (old / a.n_split + 1) * a.n_split;
-    int ok = 0;
-    for (int it = 0; it < (1 << 20); ++it) {
-      if ((int)(ldu_coherent(cnt) - target) >= 0) { ok = 1; break; }
-      __builtin_amdgcn_s_sleep(1);
-    }
-    if (!ok) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *go = ok;
+    for (int i = 0; i < DPT / 4; ++i)
+      st16_coherent(ro, (unsigned)(((prow + row) * DH + (i * TPR + tp) * 4) * 4),
+                    make_float4(O[4 * i], O[4 * i + 1], O[4 * i + 2], O[4 * i + 3]));
+    if (tp == 0) MLs[row] = make_float2(M, L);
   }
   __syncthreads();
-  AE_TR(4);
-  if (!*go) return;
-  // rows [split * rps, +rps) of the tile: thread -> (row, 4 dims)
+  if (threadIdx.x < ATT_ROWS)  // the 16 rows' (m, l) as one 128-byte run
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, MLs[threadIdx.x]), rm,
+                                          (unsigned)((prow + threadIdx.x) * 8), 0, 0x10);
+  AE_TR(6);
   const int rps = (ATT_ROWS + a.n_split - 1) / a.n_split;
-  const int t4 = threadIdx.x % (DH / 4), rr = split * rps + (int)threadIdx.x / (DH / 4);
-  if ((int)threadIdx.x >= rps * (DH / 4) || rr >= ATT_ROWS) return;
-  const int r2 = qt * ATT_ROWS + rr;
-  if (r2 >= R) return;
-  float M2 = -INFINITY, L2 = 0.f;
-  float4 O2 = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int c0 = 0; c0 < a.n_split; c0 += 8) {
-    float mc[8], lc[8];
-    float4 oc[8];
+  constexpr int TPC = DH / 4;            // consumer threads per row, one 16-byte chunk each
+  constexpr int RPP = NW * 64 / TPC;     // rows per pass
+  const int kc = threadIdx.x % TPC;
+  const int dim = (kc % TPR) * DPT + 4 * (kc / TPR);
+  bool gave_up = false;
+  for (int rb = 0; rb < rps; rb += RPP) {
+    const int rl = rb + (int)threadIdx.x / TPC, rr = split * rps + rl;
+    if (rl >= rps || rr >= ATT_ROWS) continue;
+    const int r2 = qt * ATT_ROWS + rr;
+    float M2 = -INFINITY, L2 = 0.f;
+    float4 O2 = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int c0 = 0; c0 < a.n_split; c0 += 8) {
+      const int nc = min(8, a.n_split - c0);
+      float2 ml[8];
+      f32x4 oc[8];
+      auto moff = [&](int c) { return (unsigned)(((tile * a.n_split + c) * ATT_ROWS + rr) * 8); };
+      auto ooff = [&](int c) { return (unsigned)((((tile * a.n_split + c) * ATT_ROWS + rr) * DH + kc * 4) * 4); };
+      const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
+      int polls = 0;
+      for (;; ++polls) {
+        bool ok = true;
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {  // unconditional loads: indices past n_split reread split 0, weighted 0
-      const int sp = c0 + c < a.n_split ? c0 + c : 0;
-      const size_t mi = ((tile * a.n_split + sp) * ATT_ROWS + rr) * 2;
-      mc[c] = ld_coherent_buf(rm, (unsigned)(mi * 4));
-      lc[c] = ld_coherent_buf(rm, (unsigned)(mi * 4 + 4));
-      oc[c] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             ro, (unsigned)((((tile * a.n_split + sp) * ATT_ROWS + rr) * DH + t4 * 4) * 4), 0, 0x10));
+        for (int c = 0; c < 8; ++c)
+          if (c < nc) {
+            ml[c] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(rm, moff(c0 + c), 0, 0x10));
+            oc[c] = ld16_coherent(ro, ooff(c0 + c));
+            ok = ok && exch_arrived(ml[c].x) && exch_arrived(ml[c].y) && exch_arrived(oc[c]);
+          }
+        if (__all(ok)) break;
+        if (wall_clock64() > t_end) { gave_up = true; break; }
+        __builtin_amdgcn_s_sleep(1);
+      }
+      AE_TR(4);
+      if (c0 == 0) AE_TRV(7, polls + 1);
+      float Mn = M2;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < nc) Mn = fmaxf(Mn, ml[c].x);
+      const float sc = (M2 == -INFINITY) ? 0.f : exp2f(M2 - Mn);
+      L2 *= sc;
+      O2.x *= sc; O2.y *= sc; O2.z *= sc; O2.w *= sc;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < nc) {
+          const float wt = (ml[c].x == -INFINITY) ? 0.f : exp2f(ml[c].x - Mn);
+          L2 += wt * ml[c].y;
+          O2.x += wt * oc[c][0]; O2.y += wt * oc[c][1]; O2.z += wt * oc[c][2]; O2.w += wt * oc[c][3];
+        }
+      M2 = Mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        if (c < nc) {
+          st16_empty(ro, ooff(c0 + c));
+          if (kc == 0) __builtin_amdgcn_raw_buffer_store_b64(i32x2{-1, -1}, rm, moff(c0 + c), 0, 0x10);
+        }
     }
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      if (c0 + c >= a.n_split) mc[c] = -INFINITY;
-    float Mn = M2;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) Mn = fmaxf(Mn, mc[c]);
-    const float sc = (M2 == -INFINITY) ? 0.f : exp2f(M2 - Mn);
-    L2 *= sc;
-    O2.x *= sc; O2.y *= sc; O2.z *= sc; O2.w *= sc;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const float wt = (mc[c] == -INFINITY) ? 0.f : exp2f(mc[c] - Mn);
-      L2 += wt * lc[c];
-      O2.x += wt * oc[c].x; O2.y += wt * oc[c].y; O2.z += wt * oc[c].z; O2.w += wt * oc[c].w;
+    if (r2 < R) {
+      XT* op2 = (XT*)a.o + (size_t)(s * a.H + r2 % a.H) * a.ldo + (size_t)(g * gq + r2 / a.H) * DH + dim;
+      const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
+      Act<AT>::st(op2, 0, O2.x * inv);
+      Act<AT>::st(op2, 1, O2.y * inv);
+      Act<AT>::st(op2, 2, O2.z * inv);
+      Act<AT>::st(op2, 3, O2.w * inv);
     }
-    M2 = Mn;
   }
-  XT* op2 = (XT*)a.o + (size_t)(s * a.H + r2 % a.H) * a.ldo + (size_t)(g * gq + r2 / a.H) * DH + t4 * 4;
-  const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
-  Act<AT>::st(op2, 0, O2.x * inv);
-  Act<AT>::st(op2, 1, O2.y * inv);
-  Act<AT>::st(op2, 2, O2.z * inv);
-  Act<AT>::st(op2, 3, O2.w * inv);
+  if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 #ifdef AE_TRACE
   wait_mem();
   AE_TR(5);
@@ -1013,8 +1112,8 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   const int row = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DPT;
   const int s = zz / a.n_kv, g = zz % a.n_kv, gq = a.n_q / a.n_kv;
   const int r = qt * ATT_ROWS + row;
-  if (r >= gq * a.H) return;
   const size_t tile = (size_t)zz * a.n_qt + qt;
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
   float M = -INFINITY, L = 0.f, O[DPT];
 #pragma unroll
   for (int i = 0; i < DPT; ++i) O[i] = 0.f;
@@ -1049,7 +1148,20 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
       }
     }
     M = Mn;
+    // the partials read (rows past the last query row too) go back to EXCH_EMPTY
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      if (c0 + c < a.n_split) {
+        const size_t pi = (tile * a.n_split + c0 + c) * ATT_ROWS + row;
+#pragma unroll
+        for (int i = 0; i < DPT / 4; ++i) st16_empty(ro, (unsigned)((pi * DH + d0 + 4 * i) * 4));
+        if (d0 == 0) {
+          st4_coherent(rm, (unsigned)(pi * 2 * 4), EXCH_EMPTY);
+          st4_coherent(rm, (unsigned)(pi * 2 * 4 + 4), EXCH_EMPTY);
+        }
+      }
   }
+  if (r >= gq * a.H) return;
   XT* op = (XT*)a.o + (size_t)(s * a.H + r % a.H) * a.ldo + (size_t)(g * gq + r / a.H) * DH + d0;
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll

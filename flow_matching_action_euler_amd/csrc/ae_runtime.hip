@@ -113,11 +113,13 @@ struct ae_handle {
   unsigned* counters = nullptr;
   size_t n_counters = 0;
   float *opart = nullptr, *mlpart = nullptr;
-  unsigned* qt_counter = nullptr;   // co-resident attention merge arrivals [zz][qt]
-  unsigned* err_flag = nullptr;     // set by a kernel whose bounded wait timed out
-  size_t n_qt_counters = 0;
+  size_t opart_floats = 0, mlpart_floats = 0;
+  unsigned* err_flag = nullptr;     // set by a kernel whose bounded poll gave up
   int n_qt = 0, nbp = 0, nbs = 0;  // 16-row query tiles, 32-key prefix / suffix blocks
   int n_cu = 0;
+  // in-kernel partial exchanges (read from AE_ATTN_CORESIDENT / AE_EXCH_POLL at creation, 0 = off):
+  // attention key splits merged by co-resident workgroups, split-K partials polled by split S-1
+  bool coresident_attn = true, poll_splitk = true;
   float* rope_cs = nullptr;
   void *kcache = nullptr, *vcache = nullptr;
   size_t slot_elems = 0;     // elements of one slot's packed K (and V) cache
@@ -166,6 +168,17 @@ int dalloc(ae_handle* h, void** p, size_t bytes) {
 template <class T>
 int dalloc_t(ae_handle* h, T** p, size_t count) {
   return dalloc(h, (void**)p, count * sizeof(T));
+}
+
+// The split partial buffers hold EXCH_EMPTY in every word between launches (all bytes 0xff);
+// the GEMM arrival tickets hold zero. Synchronous.
+int reset_exchange(ae_handle* h) {
+  if (h->part) HIP_TRY(h, hipMemset(h->part, 0xff, h->part_floats * sizeof(float)));
+  if (h->opart) HIP_TRY(h, hipMemset(h->opart, 0xff, h->opart_floats * sizeof(float)));
+  if (h->mlpart) HIP_TRY(h, hipMemset(h->mlpart, 0xff, h->mlpart_floats * sizeof(float)));
+  if (h->counters) HIP_TRY(h, hipMemset(h->counters, 0, h->n_counters * sizeof(unsigned)));
+  HIP_TRY(h, hipDeviceSynchronize());
+  return AE_OK;
 }
 
 int upload(ae_handle* h, void** dst, const void* src, size_t bytes) {
@@ -285,38 +298,38 @@ struct Splits {
 };
 const Splits& splits() { static Splits s; return s; }
 
-// Key splits when each wave walks `it` blocks of ATT_KB keys.
-int attn_splits(int n_blocks, int it) { return std::max(1, (n_blocks + it * ATT_WAVES - 1) / (it * ATT_WAVES)); }
+// Key splits when each of nw waves walks `it` blocks of ATT_KB keys.
+int attn_splits(int n_blocks, int it, int nw) { return std::max(1, (n_blocks + it * nw - 1) / (it * nw)); }
 
-// Attention kernels are instantiated per (activation type, head_dim, blocks per wave).
-template <int AT, int IT>
+// Attention kernels are instantiated per (activation type, head_dim, blocks per wave, waves).
+template <int AT, int IT, int NW>
 hipError_t attn_dispatch_it(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   const void* fn = nullptr;
   size_t lds = 0;
   switch (dh) {
-    case 32: fn = (const void*)attn_kernel<AT, 32, IT>; lds = attn_lds_size<32>(); break;
-    case 64: fn = (const void*)attn_kernel<AT, 64, IT>; lds = attn_lds_size<64>(); break;
-    case 128: fn = (const void*)attn_kernel<AT, 128, IT>; lds = attn_lds_size<128>(); break;
-    case 256: fn = (const void*)attn_kernel<AT, 256, IT>; lds = attn_lds_size<256>(); break;
+    case 32: fn = (const void*)attn_kernel<AT, 32, IT, NW>; lds = attn_lds_size<32, NW>(); break;
+    case 64: fn = (const void*)attn_kernel<AT, 64, IT, NW>; lds = attn_lds_size<64, NW>(); break;
+    case 128: fn = (const void*)attn_kernel<AT, 128, IT, NW>; lds = attn_lds_size<128, NW>(); break;
+    case 256: fn = (const void*)attn_kernel<AT, 256, IT, NW>; lds = attn_lds_size<256, NW>(); break;
     default: return hipErrorInvalidValue;
   }
   if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   switch (dh) {
-    case 32: AE_LAUNCH((attn_kernel<AT, 32, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    case 64: AE_LAUNCH((attn_kernel<AT, 64, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    case 128: AE_LAUNCH((attn_kernel<AT, 128, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
-    default: AE_LAUNCH((attn_kernel<AT, 256, IT>), grid, dim3(ATT_WAVES * 64), lds, st, aa); break;
+    case 32: AE_LAUNCH((attn_kernel<AT, 32, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
+    case 64: AE_LAUNCH((attn_kernel<AT, 64, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
+    case 128: AE_LAUNCH((attn_kernel<AT, 128, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
+    default: AE_LAUNCH((attn_kernel<AT, 256, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
   }
   return hipGetLastError();
 }
 template <int AT>
 hipError_t attn_dispatch(int dh, bool set_attr, bool split_it, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   if (set_attr) {
-    hipError_t e = attn_dispatch_it<AT, ATT_IT_SPLIT>(dh, true, grid, st, aa);
-    return e != hipSuccess ? e : attn_dispatch_it<AT, ATT_IT_WHOLE>(dh, true, grid, st, aa);
+    hipError_t e = attn_dispatch_it<AT, ATT_IT_SPLIT, ATT_WAVES_SPLIT>(dh, true, grid, st, aa);
+    return e != hipSuccess ? e : attn_dispatch_it<AT, ATT_IT_WHOLE, ATT_WAVES_WHOLE>(dh, true, grid, st, aa);
   }
-  return split_it ? attn_dispatch_it<AT, ATT_IT_SPLIT>(dh, false, grid, st, aa)
-                  : attn_dispatch_it<AT, ATT_IT_WHOLE>(dh, false, grid, st, aa);
+  return split_it ? attn_dispatch_it<AT, ATT_IT_SPLIT, ATT_WAVES_SPLIT>(dh, false, grid, st, aa)
+                  : attn_dispatch_it<AT, ATT_IT_WHOLE, ATT_WAVES_WHOLE>(dh, false, grid, st, aa);
 }
 
 template <int AT>
@@ -331,26 +344,24 @@ hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs
 }
 
 // How the attention covers the keys: n_split workgroups per query tile and blocks per wave.
-// Splits of one block per wave merge in-kernel when every workgroup of the launch fits on
-// the device at once (one per compute unit); otherwise a workgroup walks up to 4 blocks per
-// wave and longer contexts fall back to attn_merge.
+// Splits of 8 waves x one block merge in-kernel when every workgroup of the launch fits on
+// the device at once (one per compute unit); otherwise 8 waves walk up to 4 blocks each and
+// longer contexts fall back to attn_merge.
 struct AttnPlan {
   int n_split, split_it, coresident;
 };
 AttnPlan attn_plan(const ae_handle* h, int n_seq) {
-  static const bool allow = [] {
-    const char* e = getenv("AE_ATTN_CORESIDENT");
-    return !e || atoi(e) != 0;
-  }();
   const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
-  const int ns = attn_splits(nb, ATT_IT_SPLIT);
-  if (allow && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, 1, 1};
-  return {attn_splits(nb, ATT_IT_WHOLE), 0, 0};
+  const int ns = attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT);
+  if (h->coresident_attn && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, 1, 1};
+  return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 
 struct Dispatch {
   // one launcher per role bound to the handle's dtypes (fp8 weights: MLP roles only)
   static hipError_t gemm(ae_handle* h, int role, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+    a.exch_poll = h->poll_splitk && (long long)n_groups * a.S * n_z <= h->n_cu;  // one workgroup per CU fits them all
+    a.err = h->err_flag;
     if (h->at == AT_F32) {
       switch (role) {
         case R_QKV_ROPE: return launch_gemm<WT_F32, AT_F32, R_QKV_ROPE>(a, n_groups, n_z, st);
@@ -422,7 +433,6 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const AttnPlan plan = attn_plan(h, n_seq);
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
-  aa.qt_counter = h->qt_counter;
   aa.err = h->err_flag;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
@@ -618,6 +628,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   const ae_config& c = h->c;
   if (hipGetDevice(&h->dev) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipGetDevice failed"); }
   if (hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->dev) != hipSuccess) h->n_cu = 0;
+  if (const char* e = getenv("AE_ATTN_CORESIDENT")) h->coresident_attn = atoi(e) != 0;
+  if (const char* e = getenv("AE_EXCH_POLL")) h->poll_splitk = atoi(e) != 0;
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
   hipEventCreate(&h->ev0);
   hipEventCreate(&h->ev1);
@@ -749,13 +761,15 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc_t(h, &h->counters, h->n_counters));
     const int R = nq / nkv * H;
     const size_t n_qt = (R + ATT_ROWS - 1) / ATT_ROWS;
-    const size_t n_split = attn_splits((P + ATT_KB - 1) / ATT_KB + (H + ATT_KB - 1) / ATT_KB, ATT_IT_SPLIT);
+    const int nb = (P + ATT_KB - 1) / ATT_KB + (H + ATT_KB - 1) / ATT_KB;
+    const size_t n_split = std::max(attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT), attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE));
     const size_t n_zz = (size_t)std::max(c.max_batch, std::max(1, c.max_taus)) * nkv;
-    TRY(dalloc_t(h, &h->opart, n_zz * n_qt * n_split * ATT_ROWS * dh));
-    TRY(dalloc_t(h, &h->mlpart, n_zz * n_qt * n_split * ATT_ROWS * 2));
-    TRY(dalloc_t(h, &h->qt_counter, n_zz * n_qt));
-    h->n_qt_counters = n_zz * n_qt;
+    h->opart_floats = n_zz * n_qt * n_split * ATT_ROWS * dh;
+    h->mlpart_floats = n_zz * n_qt * n_split * ATT_ROWS * 2;
+    TRY(dalloc_t(h, &h->opart, h->opart_floats));
+    TRY(dalloc_t(h, &h->mlpart, h->mlpart_floats));
     TRY(dalloc_t(h, &h->err_flag, 1));
+    TRY(reset_exchange(h));
   }
   {
     std::vector<float> cs((size_t)H * (dh / 2) * 2);
@@ -829,16 +843,18 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   return AE_OK;
 }
 
-// A co-resident attention merge whose wait timed out (its workgroups were not all resident)
-// leaves a flag: report it and reset the arrival counters, which are then out of step.
+// A kernel whose poll for another workgroup's partial gave up (the workgroups of the launch
+// were not all resident) leaves a flag: report it and restore the exchange buffers, which
+// may then hold partials nobody consumed.
 static int check_err_flag(ae_handle* h) {
   unsigned e = 0;
   HIP_TRY(h, hipMemcpy(&e, h->err_flag, sizeof(e), hipMemcpyDeviceToHost));
   if (!e) return AE_OK;
   HIP_TRY(h, hipMemset(h->err_flag, 0, sizeof(e)));
-  HIP_TRY(h, hipMemset(h->qt_counter, 0, h->n_qt_counters * sizeof(unsigned)));
-  return fail(h, AE_ERR_HIP, "attention split merge: workgroups were not co-resident (wait timed out); "
-                             "set AE_ATTN_CORESIDENT=0");
+  const int rc = reset_exchange(h);
+  if (rc) return rc;
+  return fail(h, AE_ERR_HIP, "split partial exchange: workgroups were not co-resident (poll gave up); "
+                             "set AE_ATTN_CORESIDENT=0 and AE_EXCH_POLL=0");
 }
 
 static int check_denoise(ae_handle* h, int batch, int steps) {
@@ -1046,11 +1062,8 @@ int kernel_times_in_place(ae_handle* h, Enq& enqueue, const std::vector<std::str
 }
 }  // namespace
 
-extern "C" {
-
-int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats, int max_stats,
-                    int* n_stats) {
-  if (!h || !stats || !n_stats || iters < 1 || mode < 0 || mode > 3) return AE_ERR_INVALID_ARG;
+static int kernel_times_impl(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats,
+                             int max_stats, int* n_stats) {
   const bool in_place = (mode & 2) != 0;
   mode &= 1;
   int rc;
@@ -1115,6 +1128,18 @@ int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_
   }
   *n_stats = n;
   return AE_OK;
+}
+
+extern "C" {
+
+int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_kernel_stat* stats, int max_stats,
+                    int* n_stats) {
+  if (!h || !stats || !n_stats || iters < 1 || mode < 0 || mode > 3) return AE_ERR_INVALID_ARG;
+  const int rc = kernel_times_impl(h, mode, batch, steps, iters, stats, max_stats, n_stats);
+  // a graph of one kernel's launches alone can leave partials that no launch consumed
+  hipStreamSynchronize(h->stream);
+  const int rc2 = reset_exchange(h);
+  return rc ? rc : rc2;
 }
 
 #ifdef AE_TRACE

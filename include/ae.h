@@ -43,7 +43,10 @@
  *
  * Errors. Every int-returning call returns AE_OK (0) or a negative AE_ERR_*
  * code and never throws; ae_last_error() describes the last failure. On error
- * the outputs are not written. A handle is not re-entrant: calls on one
+ * the outputs are not written. A bounded wait inside a kernel that gave up
+ * (partials of other workgroups never arrived) is reported as AE_ERR_HIP by the
+ * synchronous ae_denoise / ae_verify of that pass, or by the next one after an
+ * asynchronous call. A handle is not re-entrant: calls on one
  * handle must not overlap. Separate handles are independent.
  */
 #ifndef AE_H_
@@ -120,7 +123,12 @@ typedef struct ae_handle ae_handle;
  * The shape contract is fixed for the handle's lifetime (DM0.5 guide 6.1 and
  * 6.5: fixed image count, token length and chunk shape). Returns
  * AE_ERR_INVALID_ARG / AE_ERR_UNSUPPORTED before touching the GPU when cfg is
- * not covered, AE_ERR_HIP if no device is usable, AE_ERR_OOM on allocation failure. */
+ * not covered, AE_ERR_HIP if no device is usable, AE_ERR_OOM on allocation failure.
+ * Read here from the environment: AE_ATTN_CORESIDENT=0 (attention key splits
+ * merge in a separate launch instead of inside the attention launch) and
+ * AE_EXCH_POLL=0 (split-K partials meet through arrival tickets instead of being
+ * polled); both in-kernel exchanges assume every workgroup of the launch is
+ * resident at once, which holds on an otherwise idle device. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 
 /* Copy one robot's prefix cache into slot (0 <= slot < max_batch). k and v are

@@ -70,6 +70,38 @@ def test_batched_robot_equals_robot_alone():
     ex.close()
 
 
+def test_exchange_paths_agree(monkeypatch):
+    """Split partials meet three ways: polled inside the launch (default), through arrival
+    tickets (GEMM split-K, AE_EXCH_POLL=0) and in a merge launch (attention,
+    AE_ATTN_CORESIDENT=0). A 1,100-token prefix gives the attention 5 key splits (2 without
+    co-residency) and the down projection 2 k-splits. Every path matches the oracle; the GEMM
+    paths add the same partials in the same order (bitwise equal), the attention paths split
+    the keys differently (bf16-level agreement); per-kernel timing, whose
+    graphs of one kernel alone leave partials unconsumed, leaves the next result unchanged."""
+    cfg = SMALL_BF16.with_(name="small_bf16_long_prefix", prefix_len=1100)
+    case = Case(cfg)
+    noise = case.noise(cfg.max_batch)
+    ref = case.oracle_denoise(noise, 3)
+    outs = []
+    for env in ({}, {"AE_EXCH_POLL": "0"}, {"AE_ATTN_CORESIDENT": "0"}):
+        with monkeypatch.context() as m:
+            for k, v in env.items():
+                m.setenv(k, v)
+            ex = _expert(case)
+        got = ex.denoise(noise, 3)
+        err = rel_err(got, ref)
+        print(f"{env or 'default'} rel_err={err:.3e}")
+        assert err <= tol_for(cfg), (env, err)
+        for mode in (0, 2):  # isolated, then in place
+            ex.kernel_times(mode, cfg.max_batch, 3, 1)
+            assert np.array_equal(ex.denoise(noise, 3), got), (env, mode)
+        outs.append(got)
+        ex.close()
+    assert np.array_equal(outs[0], outs[1])
+    # 5 vs 2 key splits round the bf16 attention output differently: bf16-level agreement
+    assert rel_err(outs[2], outs[0]) <= tol_for(cfg)
+
+
 def test_zero_output_projection_gives_constant_velocity():
     """W_out = 0, b_out = c: every Euler step adds dt * c, so x_N = x_0 + c for any N."""
     cfg = SMALL_BF16
