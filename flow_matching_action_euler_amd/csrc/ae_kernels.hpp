@@ -72,6 +72,14 @@ __device__ unsigned long long ae_trace_buf[8][2048][8];  // [kernel kind][workgr
 #endif
 constexpr int KBLK = 32;   // inputs per k-block
 
+// Activations passed between kernels (hb, o, u: M_pad tokens x K inputs) are stored in the
+// MFMA B-operand order of the GEMM that reads them: [K/32][M_pad/16][64 lanes][8], lane =
+// 16 * (k % 32 / 8) + token % 16, element k % 8 (bf16 and fp32 alike). A wave then loads
+// each 16-token x 32-input fragment as one contiguous run straight into registers.
+__device__ __forceinline__ size_t act_idx(int tok, int k, int ntt) {
+  return ((((size_t)(k >> 5) * ntt + (tok >> 4)) * 64 + (((k & 31) >> 3) << 4) + (tok & 15)) << 3) + (k & 7);
+}
+
 // ------------------------------------------------------------------ small helpers
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -176,15 +184,13 @@ __device__ __forceinline__ void prefetch_done(int acc) { asm volatile("" ::"v"(a
 struct GemmArgs {
   const void* w;        // packed weights [n_tiles][KB][64][8]
   const float* wscale;  // fp8: scale per packed channel (tile*16 + c); else null
-  const void* x;        // activations [rows][ldx], gain-scaled, not normalised
+  const void* x;        // activations in fragment order (act_idx), gain-scaled, not normalised
   const float* ssp_in;  // [g_in][M_pad] partial sums of h^2 (null: no RMS scaling)
   int g_in;
   float inv_width;      // 1 / width of the normalised vector
   float eps;
   int M, M_pad, K, S;   // rows, padded rows, inputs, k-splits
   int passes;           // k-passes per wave: K/32/S = passes * GW * KPW
-  int ldx;              // row stride of x in elements (K plus a 128-byte pad)
-  int ldo;              // row stride of the activation written by the epilogue
   float* part;          // split-K partials [S][n_z][n_groups][NT*64*16], EXCH_EMPTY between launches
   unsigned* counters;   // [n_z][n_groups], zero between launches (arrival tickets)
   int exch_poll;        // 1: every workgroup is resident at once; split S-1 polls the others' partials
@@ -197,12 +203,12 @@ struct GemmArgs {
   int nbs;                                 // 32-key suffix blocks per (sequence, kv head)
   // EPI_RESID
   float* h;              // [M_pad][N] residual, updated in place
-  void* hb;              // [rows][ldo] copy h * gain_next for the next consumer
+  void* hb;              // h * gain_next for the next consumer, fragment order (act_idx)
   const float* gain_next;
   float* ssp_out;        // [N/16][M_pad]
   int N;                 // logical outputs
   // EPI_GEGLU
-  void* u_out;           // [rows][ldo]
+  void* u_out;           // fragment order (act_idx)
   // EPI_OUT
   const float* bias;     // [A]
   float* xio;            // denoise: x [M_pad][A] updated in place; verify: v out
@@ -272,6 +278,7 @@ template <int WT> struct Frag<WT, AT_BF16> {
     else return __builtin_bit_cast(bf16x8, ((const uint4*)w)[blk * 64 + lane]);
   }
   __device__ static __forceinline__ B load_b(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const uint4*)p); }
+  __device__ static __forceinline__ B zero_b() { return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u}); }
   __device__ static __forceinline__ f32x4 mma(const A& a, const B& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -285,6 +292,7 @@ template <int WT> struct Frag<WT, AT_F32> {
     return A{p[0], p[1]};
   }
   __device__ static __forceinline__ B load_b(const float* p) { return B{((const float4*)p)[0], ((const float4*)p)[1]}; }
+  __device__ static __forceinline__ B zero_b() { return B{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)}; }
   __device__ static __forceinline__ f32x4 mma(const A& a, const B& b, f32x4 c) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
@@ -298,38 +306,31 @@ template <int WT> struct Frag<WT, AT_F32> {
   }
 };
 
-// LDS bytes of the GEMM kernels: per-wave activation staging (reused for the
-// cross-wave reduction), the reduced tile, inverse RMS and RMS partials.
+// LDS bytes of the GEMM kernels: the cross-wave reduction, the reduced tile,
+// inverse RMS and RMS partials.
 template <int AT, int NT, int KPW>
 constexpr size_t gemm_lds_size() {
-  constexpr size_t RS = KPW * KBLK * (AT == AT_BF16 ? 2 : 4) + 16;
-  constexpr size_t stage = (size_t)GW * 64 * RS;
-  constexpr size_t red = (size_t)GW * NT * 1024 * 4;
-  return (stage > red ? stage : red) + (size_t)NT * 1024 * 4 + 64 * 4 + 512 * 4 + 16;
+  // reduction tiles, summed tile, 1/rms, h^2 partials, ticket; at least 81 KB so that a compute
+  // unit holds one workgroup and a launch of up to 256 workgroups spreads over all of them
+  constexpr size_t need = (size_t)GW * NT * 1024 * 4 + (size_t)NT * 1024 * 4 + 64 * 4 + 512 * 4 + 16;
+  return need > 81 * 1024 ? need : 81 * 1024;
 }
 
 // Y = X W^T over the workgroup's channel tiles [g*NT, g*NT+NT), k-split s and
 // token group z (64 rows), then the epilogue EPI. Block = 8 waves. In each
 // pass wave w owns KPW consecutive k-blocks: it issues its weight fragments
-// and the 64 x (KPW*32) activation slice as whole 128-byte lines (half the
-// L2 requests of fragment-shaped loads), parks the slice in its own LDS
-// region and reads the MFMA B fragments from there. Rows past M are not
-// read (zeros are staged instead), so the padding of the last 64-row group
-// costs no traffic. The 8 partial tiles are summed in LDS.
+// and the matching 4 x KPW activation fragments (each one contiguous run, see
+// act_idx) straight into registers, then runs the MFMAs; no LDS staging.
+// Lanes of tokens past M load nothing (zeros), so the padding of the last
+// 64-row group costs no traffic. The 8 partial tiles are summed in LDS.
 template <int WT, int AT, int EPI, int NT, int KPW>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT, AT> F;
-  constexpr int RB = KPW * KBLK * (int)sizeof(XT);  // bytes of one staged row slice
-  constexpr int RS = RB + 16;                        // LDS row stride
-  constexpr int LPR = RB / 16;                       // lanes per row in a 16-byte load
-  constexpr int RPI = 64 / LPR;                      // rows per load instruction
-  constexpr int NI = 64 / RPI;                       // load instructions per slice
-  constexpr size_t STAGE = (size_t)GW * 64 * RS;
   constexpr size_t REDB = (size_t)GW * NT * 1024 * 4;
   extern __shared__ __attribute__((aligned(16))) float smem[];  // no static LDS: keeps 16-byte accesses aligned
-  float* red = smem;                                          // [GW][NT][64][16], reuses the staging area
-  float* res = (float*)((char*)smem + (STAGE > REDB ? STAGE : REDB));  // [NT][64][16]
+  float* red = smem;                                          // [GW][NT][64][16] cross-wave reduction
+  float* res = (float*)((char*)smem + REDB);                  // [NT][64][16]
   float* inv_rms = res + NT * 1024;                           // [64]
   float* ssq8 = inv_rms + 64;                                 // [8][64]
   unsigned* ticket = (unsigned*)(ssq8 + 512);                 // split-K arrival ticket
@@ -383,11 +384,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) acc[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  unsigned char* xs = (unsigned char*)smem + (size_t)wave * 64 * RS;
-  const int lr = lane / LPR, lc = lane % LPR;
-  const char* xg = (const char*)a.x + ((size_t)(tok0 + lr) * a.ldx) * sizeof(XT) + lc * 16;
-  const size_t xrow_step = (size_t)RPI * a.ldx * sizeof(XT);
-  const unsigned char* xf = xs + (lane & 15) * RS + (lane >> 4) * 8 * sizeof(XT);
+  const int ntt = a.M_pad / 16;
+  const XT* xg = (const XT*)a.x + ((size_t)z * 4 * 64 + lane) * 8;  // this lane's slot of token tile 4z
   for (int p = 0; p < a.passes; ++p) {
     const int kb0 = s * (KB / a.S) + (p * GW + wave) * KPW;
     typename F::A wa[NT][KPW];
@@ -395,23 +393,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < KPW; ++j) wa[nt][j] = F::load_a(a.w, ((size_t)g * NT + nt) * KB + kb0 + j, lane);
-    // activation rows past M (padding of the last token group) are not read: zeros go to LDS
-    i32x4 xr[NI];
-#pragma unroll
-    for (int i = 0; i < NI; ++i)
-      xr[i] = (tok0 + lr + i * RPI < a.M) ? *(const i32x4*)(xg + i * xrow_step + (size_t)kb0 * KBLK * sizeof(XT))
-                                          : i32x4{0, 0, 0, 0};
-    __builtin_amdgcn_sched_barrier(0);  // keep every load of the pass in flight before the first LDS store
-#pragma unroll
-    for (int i = 0; i < NI; ++i) *(i32x4*)(xs + (size_t)(i * RPI + lr) * RS + lc * 16) = xr[i];
+    // activation fragments; lanes of tokens past M (padding of the last token group) load nothing
+    typename F::B xb[KPW][4];
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        typename F::B xb = F::load_b((const XT*)(xf + (size_t)tt * 16 * RS + j * KBLK * sizeof(XT)));
+      for (int tt = 0; tt < 4; ++tt)
+        xb[j][tt] = (tok0 + tt * 16 + (lane & 15) < a.M) ? F::load_b(xg + ((size_t)(kb0 + j) * ntt + tt) * 512)
+                                                         : F::zero_b();
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][tt] = F::mma(wa[nt][j], xb, acc[nt][tt]);
-      }
+    for (int j = 0; j < KPW; ++j)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[nt][tt] = F::mma(wa[nt][j], xb[j][tt], acc[nt][tt]);
   }
 
   // next kernel's operands into L2 while this one reduces and runs its epilogue (no
@@ -426,7 +422,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   for (int i = 0; i < 8; ++i) ssq += ssv[i];
   if (a.ssp_in != nullptr)
     for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
-  __syncthreads();  // every wave is done with its staging region before it becomes the reduction buffer
   // cross-wave reduction: red[wave][nt][tok][c], one 16-byte write per (nt, tt) per lane
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
@@ -664,7 +659,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       if (valid) {
         hn = pre0[i] + val;
         a.h[(size_t)tok * a.N + n] = hn;
-        Act<AT>::st((XT*)a.hb, (size_t)tok * a.ldo + n, hn * pre1[i]);
+        Act<AT>::st((XT*)a.hb, act_idx(tok, n, a.M_pad / 16), hn * pre1[i]);
       }
       float sq = hn * hn;
       sq += __shfl_xor(sq, 1, 16);
@@ -676,7 +671,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       float up = res[e + 1024] * inv_rms[tl];
       if constexpr (WT == WT_FP8) up *= a.wscale[(tile + 1) * 16 + c];
       const int f = (int)(tile / 2) * 16 + c;
-      if (valid) Act<AT>::st((XT*)a.u_out, (size_t)tok * a.ldo + f, gelu_tanh(val) * up);
+      if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
     } else {  // EPI_OUT
       const int n = (int)tile * 16 + c;
       if (valid && n < a.A) {
@@ -750,7 +745,7 @@ struct AttnArgs {
   size_t slot_stride, layer_off;  // elements (same for K and V)
   int P, H, n_q, n_kv, dh;
   int nbp, nbs;           // 32-key prefix / suffix blocks
-  int ldo;                // row stride of o
+  int ntt;                // 16-token tiles of o (fragment order, act_idx)
   int n_qt;               // 16-row query tiles per (sequence, kv head)
   int n_split;            // key splits (workgroups) per query tile
   float scale_log2;       // log2(e) / sqrt(dh)
@@ -977,12 +972,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
 
   const int r = qt * ATT_ROWS + row;
   const bool row_ok = active && r < R;
-  XT* op = (XT*)a.o + (size_t)(s * a.H + (row_ok ? r % a.H : 0)) * a.ldo + (size_t)(g * gq + (row_ok ? r / a.H : 0)) * DH + d0;
   if (a.n_split == 1) {
     if (row_ok) {
+      const int tok = s * a.H + r % a.H, col = (g * gq + r / a.H) * DH + d0;
       const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) Act<AT>::st(op, i, O[i] * inv);
+      for (int i = 0; i < DPT; ++i) Act<AT>::st((XT*)a.o, act_idx(tok, col + i, a.ntt), O[i] * inv);
     }
     return;
   }
@@ -1083,12 +1078,12 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         }
     }
     if (r2 < R) {
-      XT* op2 = (XT*)a.o + (size_t)(s * a.H + r2 % a.H) * a.ldo + (size_t)(g * gq + r2 / a.H) * DH + dim;
+      const int tok = s * a.H + r2 % a.H, col = (g * gq + r2 / a.H) * DH + dim;
       const float inv = L2 > 0.f ? 1.f / L2 : 0.f;
-      Act<AT>::st(op2, 0, O2.x * inv);
-      Act<AT>::st(op2, 1, O2.y * inv);
-      Act<AT>::st(op2, 2, O2.z * inv);
-      Act<AT>::st(op2, 3, O2.w * inv);
+      Act<AT>::st((XT*)a.o, act_idx(tok, col, a.ntt), O2.x * inv);
+      Act<AT>::st((XT*)a.o, act_idx(tok, col + 1, a.ntt), O2.y * inv);
+      Act<AT>::st((XT*)a.o, act_idx(tok, col + 2, a.ntt), O2.z * inv);
+      Act<AT>::st((XT*)a.o, act_idx(tok, col + 3, a.ntt), O2.w * inv);
     }
   }
   if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1162,10 +1157,10 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
       }
   }
   if (r >= gq * a.H) return;
-  XT* op = (XT*)a.o + (size_t)(s * a.H + r % a.H) * a.ldo + (size_t)(g * gq + r / a.H) * DH + d0;
+  const int tok = s * a.H + r % a.H, col = (g * gq + r / a.H) * DH + d0;
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) Act<AT>::st(op, i, O[i] * inv);
+  for (int i = 0; i < DPT; ++i) Act<AT>::st((XT*)a.o, act_idx(tok, col + i, a.ntt), O[i] * inv);
 #ifdef AE_TRACE
   wait_mem();
   AE_TR(1);
@@ -1180,7 +1175,7 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
 template <int WT_IN, int AT>
 __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void* w_in, const float* b_in,
                                                       const float* temb, int temb_stride, int M, int M_pad,
-                                                      int A, int H, int width, float* h, void* hb, int ldh,
+                                                      int A, int H, int width, float* h, void* hb,
                                                       const float* gain, float* ssp) {
   typedef typename Act<AT>::T XT;
   __shared__ float xs[16][65];
@@ -1215,7 +1210,7 @@ __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void
       acc = bias + tv[i];
       for (int k = 0; k < A; ++k) acc += xs[rl][k] * ws[nl][k];
       h[(size_t)tok * width + n] = acc;
-      Act<AT>::st((XT*)hb, (size_t)tok * ldh + n, acc * gn);
+      Act<AT>::st((XT*)hb, act_idx(tok, n, M_pad / 16), acc * gn);
     }
     float sq = acc * acc;
     sq += __shfl_xor(sq, 1, 16);

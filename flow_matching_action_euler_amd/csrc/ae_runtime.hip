@@ -92,7 +92,6 @@ struct ae_handle {
   int wt = WT_BF16;      // attention / projection weight type
   int mt = WT_BF16;      // MLP weight type
   int M_max = 0, Mp_max = 0;
-  int ld_h = 0, ld_q = 0, ld_u = 0;  // padded row strides (elements) of hb, o, u
   std::vector<void*> allocs;
 
   // weights (device)
@@ -416,10 +415,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   LAUNCH_CHECK(h, "in_proj", {
     if (h->at == AT_F32)
       AE_LAUNCH((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
+                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ln1[0], h->ssp_a);
     else
       AE_LAUNCH((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ld_h, h->ln1[0], h->ssp_a);
+                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ln1[0], h->ssp_a);
   });
 
   const int gq = nq / nkv, R = gq * H;
@@ -428,7 +427,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.seq_slot = seq_slot;
   aa.slot_stride = h->slot_elems;
   aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh;
-  aa.nbp = h->nbp; aa.nbs = h->nbs; aa.ldo = h->ld_q;
+  aa.nbp = h->nbp; aa.nbs = h->nbs; aa.ntt = Mp / 16;
   aa.n_qt = h->n_qt;
   const AttnPlan plan = attn_plan(h, n_seq);
   aa.n_split = plan.n_split;
@@ -445,7 +444,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     // --- norm1 + QKV + RoPE
     {
       GemmArgs a = g;
-      a.w = h->qkv_p[l]; a.x = h->hb; a.ldx = h->ld_h;
+      a.w = h->qkv_p[l]; a.x = h->hb;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().qkv, n_z).S;
       if ((prefetch_mask() & 1) && n_seq == 1 && h->slot_elems) {  // this layer's prefix K/V (one robot: slot 0)
@@ -475,7 +474,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     // --- o_proj + residual; hb <- h * ln2
     {
       GemmArgs a = g;
-      a.w = h->o_p[l]; a.x = h->o; a.ldx = h->ld_q; a.ldo = h->ld_h; a.ssp_in = nullptr; a.K = nq * dh;
+      a.w = h->o_p[l]; a.x = h->o; a.ssp_in = nullptr; a.K = nq * dh;
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
       a.trace_id = 2;
@@ -484,7 +483,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     // --- norm2 + gate/up + GeGLU
     {
       GemmArgs a = g;
-      a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb; a.ldx = h->ld_h; a.ldo = h->ld_u;
+      a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb;
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
       if (prefetch_mask() & 2) {  // down's weights, tiled as down is launched below
@@ -498,7 +497,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     // --- down + residual; hb <- h * next gain
     {
       GemmArgs a = g;
-      a.w = h->d_p[l]; a.wscale = h->d_s[l]; a.x = h->u; a.ldx = h->ld_u; a.ldo = h->ld_h; a.ssp_in = nullptr; a.K = F;
+      a.w = h->d_p[l]; a.wscale = h->d_s[l]; a.x = h->u; a.ssp_in = nullptr; a.K = F;
       a.S = pick(F / 32, splits().down, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
       a.ssp_out = h->ssp_a; a.N = w;
@@ -511,7 +510,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     GemmArgs a{};
     a.inv_width = 1.f / (float)w; a.eps = c.rms_eps; a.M = M; a.M_pad = Mp;
     a.part = h->part; a.counters = h->counters;
-    a.w = h->action_out_p; a.x = h->hb; a.ldx = h->ld_h; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
+    a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, splits().out, n_z).S;
     a.bias = h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
     a.trace_id = 5;
@@ -735,10 +734,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc_t(h, &h->x, (size_t)Mp * A));
   TRY(dalloc_t(h, &h->vout, (size_t)Mp * A));
   TRY(dalloc_t(h, &h->h, (size_t)Mp * w));
-  // activation rows padded by 128 bytes so the rows of one MFMA fragment spread over L2 channels
-  const int pad = 128 / aes;
-  h->ld_h = w + pad; h->ld_q = nq * dh + pad; h->ld_u = F + pad;
-  TRY(dalloc(h, &h->hb, (size_t)Mp * h->ld_h * aes));
+  // activations between kernels in the GEMMs' fragment order (act_idx): Mp tokens x K inputs
+  TRY(dalloc(h, &h->hb, (size_t)Mp * w * aes));
   TRY(dalloc_t(h, &h->ssp_a, (size_t)(w / 16) * Mp));
   TRY(dalloc_t(h, &h->ssp_b, (size_t)(w / 16) * Mp));
   {
@@ -750,8 +747,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc(h, &h->ks, seqs * nkv * h->nbs * ATT_KB * dh * aes));
     TRY(dalloc(h, &h->vs, seqs * nkv * h->nbs * ATT_KB * dh * aes));
   }
-  TRY(dalloc(h, &h->o, (size_t)Mp * h->ld_q * aes));
-  TRY(dalloc(h, &h->u, (size_t)Mp * h->ld_u * aes));
+  TRY(dalloc(h, &h->o, (size_t)Mp * nq * dh * aes));
+  TRY(dalloc(h, &h->u, (size_t)Mp * F * aes));
   {
     const int n_z = (Mp + TOKG - 1) / TOKG;
     size_t maxg = std::max({(size_t)h->qkv_tiles, (size_t)(w / 16), (size_t)h->gu_tiles, (size_t)h->out_tiles});
