@@ -940,58 +940,68 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   __syncthreads();
   AE_TR(2);
 
-  // ---- merge the waves: thread -> row, DPT consecutive dims (threads past 16 rows idle)
-  constexpr int DPT = DH / 16 >= 4 ? DH / 16 : 4;   // dims per thread, a multiple of 4
-  constexpr int TPR = DH / DPT;                      // threads per row
-  const bool active = threadIdx.x < ATT_ROWS * TPR;
-  const int row = active ? threadIdx.x / TPR : 0, d0 = (threadIdx.x % TPR) * DPT;
-  float mw[NW], lw[NW];
-  float M = -INFINITY;
+  // ---- merge the waves: thread -> (row, 4-dim chunk) pairs q = t + 64 NW i; a wave reads whole
+  // 1 KB rows of the wave partials, so the LDS reads have no bank conflicts
+  constexpr int CPR = DH / 4;                              // 16-byte chunks per row
+  constexpr int NTH = NW * 64;
+  constexpr int PPT = (ATT_ROWS * CPR + NTH - 1) / NTH;    // pairs per thread
+  const int c4 = threadIdx.x % CPR;                        // same chunk for every pair of a thread
+  float Mq[PPT], Lq[PPT];
+  f32x4 Oq[PPT];
 #pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float2 ml = *(const float2*)(MLw + (w * ATT_ROWS + row) * 2);
-    mw[w] = ml.x;
-    lw[w] = ml.y;
-    M = fmaxf(M, ml.x);
-  }
-  float L = 0.f, O[DPT];
+  for (int i = 0; i < PPT; ++i) {
+    const int q = threadIdx.x + NTH * i;
+    const int row = q < ATT_ROWS * CPR ? q / CPR : 0;
+    float mw[NW], lw[NW];
+    float M = -INFINITY;
 #pragma unroll
-  for (int i = 0; i < DPT; ++i) O[i] = 0.f;
-#pragma unroll
-  for (int w = 0; w < NW; ++w) {
-    const float wt = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
-    L += wt * lw[w];
-    const float* src = Ow + ((size_t)w * ATT_ROWS + row) * LDO + d0;
-#pragma unroll
-    for (int i = 0; i < DPT; i += 4) {
-      const float4 v = *(const float4*)(src + i);
-      O[i] += wt * v.x; O[i + 1] += wt * v.y; O[i + 2] += wt * v.z; O[i + 3] += wt * v.w;
+    for (int w = 0; w < NW; ++w) {
+      const float2 ml = *(const float2*)(MLw + (w * ATT_ROWS + row) * 2);
+      mw[w] = ml.x;
+      lw[w] = ml.y;
+      M = fmaxf(M, ml.x);
     }
+    float L = 0.f;
+    f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const float wt = (mw[w] == -INFINITY) ? 0.f : exp2f(mw[w] - M);
+      L += wt * lw[w];
+      O += wt * *(const f32x4*)(Ow + ((size_t)w * ATT_ROWS + row) * LDO + 4 * c4);
+    }
+    Mq[i] = M;
+    Lq[i] = L;
+    Oq[i] = O;
   }
   AE_TR(3);
 
-  const int r = qt * ATT_ROWS + row;
-  const bool row_ok = active && r < R;
+  auto pair_row = [&](int i) { return (int)(threadIdx.x + NTH * i) / CPR; };
+  auto pair_ok = [&](int i) { return (int)(threadIdx.x + NTH * i) < ATT_ROWS * CPR; };
   if (a.n_split == 1) {
-    if (row_ok) {
-      const int tok = s * a.H + r % a.H, col = (g * gq + r / a.H) * DH + d0;
-      const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-      for (int i = 0; i < DPT; ++i) Act<AT>::st((XT*)a.o, act_idx(tok, col + i, a.ntt), O[i] * inv);
+    for (int i = 0; i < PPT; ++i) {
+      const int r = qt * ATT_ROWS + pair_row(i);
+      if (pair_ok(i) && r < R) {
+        const int tok = s * a.H + r % a.H, col = (g * gq + r / a.H) * DH + 4 * c4;
+        const float inv = Lq[i] > 0.f ? 1.f / Lq[i] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) Act<AT>::st((XT*)a.o, act_idx(tok, col + j, a.ntt), Oq[i][j] * inv);
+      }
     }
     return;
   }
 
+  // partial rows are row-major [dims]; (m, l) per row
   const size_t tile = (size_t)zz * a.n_qt + qt;
+  const size_t prow = (tile * a.n_split + split) * ATT_ROWS;  // this split's first partial row
   if (!a.coresident) {
     // ---- several splits: store this split's partial; attn_merge combines them after the launch boundary
-    if (active) {
-      const size_t pbase = ((tile * a.n_split + split) * ATT_ROWS + row) * DH + d0;
 #pragma unroll
-      for (int i = 0; i < DPT; i += 4) *(float4*)(a.opart + pbase + i) = make_float4(O[i], O[i + 1], O[i + 2], O[i + 3]);
-      if (threadIdx.x % TPR == 0)
-        *(float2*)(a.mlpart + ((tile * a.n_split + split) * ATT_ROWS + row) * 2) = make_float2(M, L);
-    }
+    for (int i = 0; i < PPT; ++i)
+      if (pair_ok(i)) {
+        *(f32x4*)(a.opart + (prow + pair_row(i)) * DH + 4 * c4) = Oq[i];
+        if (c4 == 0) *(float2*)(a.mlpart + (prow + pair_row(i)) * 2) = make_float2(Mq[i], Lq[i]);
+      }
 #ifdef AE_TRACE
     wait_mem();
     AE_TR(4);
@@ -999,24 +1009,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     return;
   }
 
-  // ---- co-resident splits: publish the partial write-through; split c then merges rows
-  // [c * rps, +rps) of the tile from every split's partial as the words land (see EXCH_EMPTY)
-  // and empties them. A partial row is DH/4 16-byte chunks; chunk i * TPR + t holds dims
-  // t * DPT + 4 i .. +4, so every store and load instruction covers whole 256-byte runs.
-  // A row's consumer threads share one wave, whose polls end together.
+  // ---- co-resident splits: publish the partial write-through (a wave stores whole 1 KB rows,
+  // the 16 rows' (m, l) go out as one 128-byte run); split c then merges rows [c * rps, +rps)
+  // of the tile from every split's partial as the words land (see EXCH_EMPTY) and empties
+  // them. A row's consumer threads share one wave, whose polls end together.
   const __amdgpu_buffer_rsrc_t ro = make_rsrc(a.opart), rm = make_rsrc(a.mlpart);
-  const size_t prow = (tile * a.n_split + split) * ATT_ROWS;  // this split's first partial row
   float2* MLs = (float2*)Qs;  // merged (m, l) per row; the query tile is dead by now
-  if (active) {
-    const int tp = threadIdx.x % TPR;
 #pragma unroll
-    for (int i = 0; i < DPT / 4; ++i)
-      st16_coherent(ro, (unsigned)(((prow + row) * DH + (i * TPR + tp) * 4) * 4),
-                    make_float4(O[4 * i], O[4 * i + 1], O[4 * i + 2], O[4 * i + 3]));
-    if (tp == 0) MLs[row] = make_float2(M, L);
-  }
+  for (int i = 0; i < PPT; ++i)
+    if (pair_ok(i)) {
+      st16_coherent(ro, (unsigned)(((prow + pair_row(i)) * DH + 4 * c4) * 4),
+                    make_float4(Oq[i][0], Oq[i][1], Oq[i][2], Oq[i][3]));
+      if (c4 == 0) MLs[pair_row(i)] = make_float2(Mq[i], Lq[i]);
+    }
   __syncthreads();
-  if (threadIdx.x < ATT_ROWS)  // the 16 rows' (m, l) as one 128-byte run
+  if (threadIdx.x < ATT_ROWS)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, MLs[threadIdx.x]), rm,
                                           (unsigned)((prow + threadIdx.x) * 8), 0, 0x10);
   AE_TR(6);
@@ -1024,7 +1031,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   constexpr int TPC = DH / 4;            // consumer threads per row, one 16-byte chunk each
   constexpr int RPP = NW * 64 / TPC;     // rows per pass
   const int kc = threadIdx.x % TPC;
-  const int dim = (kc % TPR) * DPT + 4 * (kc / TPR);
+  const int dim = 4 * kc;
   bool gave_up = false;
   for (int rb = 0; rb < rps; rb += RPP) {
     const int rl = rb + (int)threadIdx.x / TPC, rr = split * rps + rl;
