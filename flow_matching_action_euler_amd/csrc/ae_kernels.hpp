@@ -140,6 +140,7 @@ struct Prefetch {
   unsigned long long bytes; // kind 1: bytes of each region
   int kind;                 // 0: none, 1: whole regions into every XCD's L2, 2: next GEMM's weights
   int next_groups, next_S, NT, KB, frag_bytes;  // kind 2: next launch's tiling
+  int kb_lead;              // kind 2: leading k-blocks of each tile's k-range to place (0: all)
 };
 
 template <int NL>
@@ -160,7 +161,8 @@ __device__ __forceinline__ int prefetch_issue(const Prefetch& pf, unsigned wg, u
       a1 = Lg < lines1 ? pf.base + Lg * 128 : pf.base2 + (Lg - lines1) * 128;
     } else {  // the lines of next-launch workgroups i = xcd + 8 (j0 + m c8), m = 0, 1, ...
       const unsigned kbs = pf.KB / max(pf.next_S, 1);
-      const unsigned lpt = max(kbs * pf.frag_bytes / 128, 1u);  // lines per tile range
+      const unsigned kbl = pf.kb_lead > 0 && (unsigned)pf.kb_lead < kbs ? (unsigned)pf.kb_lead : kbs;
+      const unsigned lpt = max(kbl * pf.frag_bytes / 128, 1u);  // lines per tile range
       const unsigned lpw = max(pf.NT, 1) * lpt;                 // lines per next workgroup
       const unsigned m = L / lpw, r = L % lpw;
       const unsigned i = xcd + 8 * (j0 + m * c8);
@@ -471,6 +473,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
           const int qd = threadIdx.x + GTHREADS * i;
           if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
         }
+        // this workgroup's HBM reads are over while split S-1 still merges: place the next
+        // GEMM's weights in L2 (producers are workgroup ids below n_groups * (S-1) * n_z)
+        if (a.pf.kind == 2)
+          prefetch_done(prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                          gridDim.x * (gridDim.y - 1) * gridDim.z, threadIdx.x, GTHREADS));
         return;
       }
       bool gave_up = false;

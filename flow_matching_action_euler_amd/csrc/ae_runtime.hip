@@ -395,12 +395,26 @@ struct Dispatch {
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
 // temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
 // Which GEMMs prefetch for the kernel after them (bit 0: QKV -> the attention's prefix K/V,
-// bit 1: gate/up -> down weights; measured: bit 0 saves ~1 us per layer for free, bit 1 moves
-// ~1 us from down to gate/up); AE_PREFETCH=mask overrides it for tuning.
+// bit 1: gate/up -> down weights, bit 3: o_proj's split-K producers -> gate/up weights, bit 4:
+// down's split-K producers -> the next layer's QKV weights). Measured for Pi0 per layer: bit 0
+// saves ~1 us, bit 4 ~1.1 us, bit 3 (half of each k-range) ~0.6 us; bit 1 moves ~1 us from
+// down to gate/up. Default 1 | 8 | 16; AE_PREFETCH=mask overrides it.
+// Leading k-blocks of each gate/up tile that o_proj's producers place in L2 (bit 3): half the
+// k-range, so that the prefetch ends within o_proj's own tail (measured for Pi0: all of it
+// lengthens o_proj as much as it shortens gate/up; 12-16 of 32 blocks gain 0.1 ms per chunk);
+// AE_PF_GU_LEAD overrides it.
+int prefetch_gu_lead(int kb) {
+  static int n = [] {
+    const char* e = getenv("AE_PF_GU_LEAD");
+    return e ? atoi(e) : -1;
+  }();
+  return n >= 0 ? n : kb / 2;
+}
+
 int prefetch_mask() {
   static int m = [] {
     const char* e = getenv("AE_PREFETCH");
-    return e ? atoi(e) : 1;
+    return e ? atoi(e) : 1 | 8 | 16;
   }();
   return m;
 }
@@ -477,6 +491,12 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->o_p[l]; a.x = h->o; a.ssp_in = nullptr; a.K = nq * dh;
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
+      if (prefetch_mask() & 8) {  // gate/up's weights, tiled as gate/up is launched below
+        a.pf.kind = 2; a.pf.base = (const char*)h->gu_p[l];
+        a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, splits().gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
+        a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
+        a.pf.kb_lead = prefetch_gu_lead(w / KBLK / a.pf.next_S);
+      }
       a.trace_id = 2;
       LAUNCH_CHECK(h, "o_proj_resid", (void)Dispatch::gemm(h, R_O_PROJ, a, w / 16, n_z, st));
     }
@@ -501,6 +521,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.S = pick(F / 32, splits().down, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
       a.ssp_out = h->ssp_a; a.N = w;
+      if ((prefetch_mask() & 16) && l + 1 < c.n_layers) {  // the next layer's QKV weights
+        a.pf.kind = 2; a.pf.base = (const char*)h->qkv_p[l + 1];
+        a.pf.next_groups = h->qkv_tiles; a.pf.next_S = pick(w / 32, splits().qkv, n_z).S; a.pf.NT = 1; a.pf.KB = w / KBLK;
+        a.pf.frag_bytes = h->wt == WT_F32 ? 2048 : 1024;
+      }
       a.trace_id = 4;
       LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, R_DOWN, a, w / 16, n_z, st));
     }
