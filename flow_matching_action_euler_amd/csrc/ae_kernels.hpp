@@ -143,12 +143,16 @@ struct Prefetch {
   int kb_lead;              // kind 2: leading k-blocks of each tile's k-range to place (0: all)
 };
 
+// The touched values stay in registers until prefetch_done: combining them any earlier would
+// make the wave wait for HBM at the next scheduling boundary (a barrier), mid-kernel.
+template <int NL> struct PfVals { int v[NL]; };
+
 template <int NL>
-__device__ __forceinline__ int prefetch_issue(const Prefetch& pf, unsigned wg, unsigned n_wg, unsigned tid, unsigned nthr) {
+__device__ __forceinline__ PfVals<NL> prefetch_issue(const Prefetch& pf, unsigned wg, unsigned n_wg, unsigned tid, unsigned nthr) {
   const unsigned c8 = n_wg >= 8 ? n_wg / 8 : 1;  // this launch's workgroups per XCD
   const unsigned xcd = wg % 8, j0 = wg / 8;
   const bool wg_ok = pf.kind != 0 && wg < c8 * 8;
-  int acc = 0;
+  PfVals<NL> out;
 #pragma unroll
   for (int k = 0; k < NL; ++k) {
     const unsigned L = tid + nthr * k;  // this workgroup's k-th touch slot
@@ -173,13 +177,19 @@ __device__ __forceinline__ int prefetch_issue(const Prefetch& pf, unsigned wg, u
           (unsigned long long)(r % lpt) * 128;
       a1 = pf.base + off;
     }
-    acc ^= *(const int*)(ok ? a1 : pf.dummy);
+    out.v[k] = *(const int*)(ok ? a1 : pf.dummy);
   }
-  return acc;
+  return out;
 }
 
-// Consume the prefetch values: forces their completion, nothing else.
-__device__ __forceinline__ void prefetch_done(int acc) { asm volatile("" ::"v"(acc)); }
+// Consume the prefetch values (call once, at the end): forces their completion, nothing else.
+template <int NL>
+__device__ __forceinline__ void prefetch_done(const PfVals<NL>& p) {
+  int acc = 0;
+#pragma unroll
+  for (int k = 0; k < NL; ++k) acc ^= p.v[k];
+  asm volatile("" ::"v"(acc));
+}
 
 // ------------------------------------------------------------------ GEMM
 
@@ -414,7 +424,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 
   // next kernel's operands into L2 while this one reduces and runs its epilogue (no
   // split-K exchange in these roles, so nothing below waits on memory before the end)
-  int pf_acc = 0;
+  PfVals<2> pf_acc{};
   if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
     pf_acc = prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
                                gridDim.x * gridDim.y * gridDim.z, threadIdx.x, GTHREADS);
@@ -424,15 +434,16 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   for (int i = 0; i < 8; ++i) ssq += ssv[i];
   if (a.ssp_in != nullptr)
     for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
-  // cross-wave reduction: red[wave][nt][tok][c], one 16-byte write per (nt, tt) per lane
+  // cross-wave reduction: red[wave][nt][tt][channel quad][token % 16][4], so the 16 lanes of a
+  // write phase cover 256 consecutive bytes (no bank conflicts); res is [nt][token][channel]
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
-      *(f32x4*)(red + ((wave * NT + nt) * TOKG + tt * 16 + (lane & 15)) * 16 + 4 * (lane >> 4)) = acc[nt][tt];
+      *(f32x4*)(red + ((((wave * NT + nt) * 4 + tt) * 4 + (lane >> 4)) * 16 + (lane & 15)) * 4) = acc[nt][tt];
   ssq8[threadIdx.x] = ssq;
   __syncthreads();
-  // quads of 4 consecutive elements: NT * 256 quads over 512 threads
+  // NT * 256 quads over 512 threads; quad qd = ((nt * 4 + tt) * 4 + cq) * 16 + t
 #pragma unroll
   for (int i = 0; i < (NT + 1) / 2; ++i) {
     const int qd = threadIdx.x + GTHREADS * i;
@@ -440,7 +451,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       f32x4 sum = *(const f32x4*)(red + qd * 4);
 #pragma unroll
       for (int w = 1; w < GW; ++w) sum += *(const f32x4*)(red + w * NT * 1024 + qd * 4);
-      *(f32x4*)(res + qd * 4) = sum;
+      const int nt = qd >> 8, tt = (qd >> 6) & 3, cq = (qd >> 4) & 3, t = qd & 15;
+      *(f32x4*)(res + nt * 1024 + (tt * 16 + t) * 16 + cq * 4) = sum;
     }
   }
   if (threadIdx.x < TOKG) {
@@ -760,7 +772,7 @@ struct AttnArgs {
   float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum), same
   unsigned* err;          // set if a co-resident merge poll gave up
   int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
-  void* o;                // [rows][ldo] output
+  void* o;                // output, fragment order (act_idx)
   int trace_id;
 };
 

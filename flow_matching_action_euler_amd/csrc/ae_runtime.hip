@@ -392,13 +392,21 @@ struct Dispatch {
     }                                                                                        \
   } while (0)
 
-// One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
-// temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
-// Which GEMMs prefetch for the kernel after them (bit 0: QKV -> the attention's prefix K/V,
-// bit 1: gate/up -> down weights, bit 3: o_proj's split-K producers -> gate/up weights, bit 4:
-// down's split-K producers -> the next layer's QKV weights). Measured for Pi0 per layer: bit 0
-// saves ~1 us, bit 4 ~1.1 us, bit 3 (half of each k-range) ~0.6 us; bit 1 moves ~1 us from
-// down to gate/up. Default 1 | 8 | 16; AE_PREFETCH=mask overrides it.
+// Which kernels place the next kernel's operands in L2 (bit 0: QKV -> the attention's prefix
+// K/V, bit 1: gate/up -> down weights, bit 3: o_proj's split-K producers -> gate/up weights,
+// bit 4: down's split-K producers -> the next layer's QKV weights). Measured for Pi0 per chunk:
+// bit 0 saves 0.32 ms, bit 4 0.19 ms, bit 3 (half of each k-range) 0.1 ms, bit 1 0.04 ms (it
+// moves ~1.3 us per layer from down to gate/up). The attention placing o_proj's weights
+// costs it ~1 us per launch (its exchange shares the memory path) and is not offered.
+// Default 1 | 2 | 8 | 16; AE_PREFETCH=mask overrides it.
+int prefetch_mask() {
+  static int m = [] {
+    const char* e = getenv("AE_PREFETCH");
+    return e ? atoi(e) : 1 | 2 | 8 | 16;
+  }();
+  return m;
+}
+
 // Leading k-blocks of each gate/up tile that o_proj's producers place in L2 (bit 3): half the
 // k-range, so that the prefetch ends within o_proj's own tail (measured for Pi0: all of it
 // lengthens o_proj as much as it shortens gate/up; 12-16 of 32 blocks gain 0.1 ms per chunk);
@@ -411,14 +419,18 @@ int prefetch_gu_lead(int kb) {
   return n >= 0 ? n : kb / 2;
 }
 
-int prefetch_mask() {
-  static int m = [] {
-    const char* e = getenv("AE_PREFETCH");
-    return e ? atoi(e) : 1 | 8 | 16;
+// Leading k-blocks of each down tile that gate/up places in L2 (bit 1; 0 = all);
+// AE_PF_DOWN_LEAD overrides it.
+int prefetch_down_lead() {
+  static int n = [] {
+    const char* e = getenv("AE_PF_DOWN_LEAD");
+    return e ? atoi(e) : 0;
   }();
-  return m;
+  return n;
 }
 
+// One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
+// temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
 int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, float dt,
                      hipStream_t st, Timer* tm) {
   const ae_config& c = h->c;
@@ -510,6 +522,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
         a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, splits().down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
+        a.pf.kb_lead = prefetch_down_lead();
       }
       a.trace_id = 3;
       LAUNCH_CHECK(h, "gate_up_geglu", (void)Dispatch::gemm(h, R_GATE_UP, a, h->gu_tiles / 2, n_z, st));
