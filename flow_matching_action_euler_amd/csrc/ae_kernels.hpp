@@ -355,14 +355,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   const int KB = a.K / KBLK;
   const int tok0 = z * TOKG;
 
-  // partial sums of h^2: thread -> token t & 63, groups (t >> 6) + 8 i; loaded now, summed after the MFMAs
+  // partial sums of h^2: thread -> token t & 63, groups (t >> 6) + 8 i; loaded right after the
+  // first pass's weights and activations (loads retire in order, so the MFMAs do not wait for
+  // them), summed after the MFMAs. The loads are unconditional (a valid fallback address,
+  // masked at the sum): a conditional load let the compiler start the sum, and wait for it,
+  // before the main loads were issued.
   float ssv[8];
-  const float* sp = a.ssp_in + tok0 + (threadIdx.x & 63);
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int gi = (threadIdx.x >> 6) + 8 * i;
-    ssv[i] = (a.ssp_in != nullptr && gi < a.g_in) ? sp[(size_t)gi * a.M_pad] : 0.f;
-  }
+  const bool has_ssp = a.ssp_in != nullptr;
+  const float* sp = has_ssp ? a.ssp_in + tok0 + (threadIdx.x & 63) : (const float*)a.w;
 
   // epilogue operands that do not depend on the product, loaded before the main loads:
   // element e = t + 512 i -> (nt = e / 1024, token (e / 16) % 64, channel e % 16)
@@ -413,6 +413,13 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       for (int tt = 0; tt < 4; ++tt)
         xb[j][tt] = (tok0 + tt * 16 + (lane & 15) < a.M) ? F::load_b(xg + ((size_t)(kb0 + j) * ntt + tt) * 512)
                                                          : F::zero_b();
+    if (p == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int gi = (threadIdx.x >> 6) + 8 * i;
+        ssv[i] = sp[(has_ssp && gi < a.g_in) ? (size_t)gi * a.M_pad : 0];
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
@@ -431,7 +438,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   AE_TR(1);
   float ssq = 0.f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ssq += ssv[i];
+  for (int i = 0; i < 8; ++i) ssq += (has_ssp && (int)(threadIdx.x >> 6) + 8 * i < a.g_in) ? ssv[i] : 0.f;
   if (a.ssp_in != nullptr)
     for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
   // cross-wave reduction: red[wave][nt][tt][channel quad][token % 16][4], so the 16 lanes of a
