@@ -290,7 +290,6 @@ template <int WT> struct Frag<WT, AT_BF16> {
     else return __builtin_bit_cast(bf16x8, ((const uint4*)w)[blk * 64 + lane]);
   }
   __device__ static __forceinline__ B load_b(const uint16_t* p) { return __builtin_bit_cast(bf16x8, *(const uint4*)p); }
-  __device__ static __forceinline__ B zero_b() { return __builtin_bit_cast(bf16x8, uint4{0u, 0u, 0u, 0u}); }
   __device__ static __forceinline__ f32x4 mma(const A& a, const B& b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
   }
@@ -304,7 +303,6 @@ template <int WT> struct Frag<WT, AT_F32> {
     return A{p[0], p[1]};
   }
   __device__ static __forceinline__ B load_b(const float* p) { return B{((const float4*)p)[0], ((const float4*)p)[1]}; }
-  __device__ static __forceinline__ B zero_b() { return B{make_float4(0.f, 0.f, 0.f, 0.f), make_float4(0.f, 0.f, 0.f, 0.f)}; }
   __device__ static __forceinline__ f32x4 mma(const A& a, const B& b, f32x4 c) {
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.x, b.lo.x, c, 0, 0, 0);
     c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.lo.y, b.lo.y, c, 0, 0, 0);
@@ -333,8 +331,7 @@ constexpr size_t gemm_lds_size() {
 // pass wave w owns KPW consecutive k-blocks: it issues its weight fragments
 // and the matching 4 x KPW activation fragments (each one contiguous run, see
 // act_idx) straight into registers, then runs the MFMAs; no LDS staging.
-// Lanes of tokens past M load nothing (zeros), so the padding of the last
-// 64-row group costs no traffic. The 8 partial tiles are summed in LDS.
+// The 8 partial tiles are summed in LDS.
 template <int WT, int AT, int EPI, int NT, int KPW>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   typedef typename Act<AT>::T XT;
@@ -378,16 +375,28 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     if constexpr (EPI == EPI_RESID) {
       if (tok < a.M) pre0[i] = a.h[(size_t)tok * a.N + tile * 16 + c];
       pre1[i] = a.gain_next[tile * 16 + c];
-    } else if constexpr (EPI == EPI_QKV) {
-      const int tiles_per_head = a.dh / 16, half = a.dh / 2;
-      const int t_in = (int)tile;
-      if (t_in < (a.n_q + a.n_kv) * tiles_per_head) {
-        const int pair = (t_in % tiles_per_head);
-        const float2 cs = *(const float2*)(a.rope_cs + ((size_t)(tok % a.H) * half + pair * 8 + (c & 7)) * 2);
-        pre0[i] = cs.x;
-        pre1[i] = cs.y;
-      }
+    } else if constexpr (EPI == EPI_OUT) {
+      const int n = (int)tile * 16 + c;
+      const bool ok = n < a.A && tok < a.M;  // unconditional loads (clamped), masked at use
+      pre0[i] = a.bias[n < a.A ? n : 0];
+      pre1[i] = a.dt > 0.f ? a.xio[ok ? (size_t)tok * a.A + n : 0] : 0.f;
     }
+  }
+  // fp8 weights: the per-row scale of each epilogue element, loaded now
+  float psc[2 * NT];
+#pragma unroll
+  for (int i = 0; i < 2 * NT; ++i) {
+    const int e = threadIdx.x + GTHREADS * i;
+    psc[i] = WT == WT_FP8 ? a.wscale[((size_t)g * NT + (e >> 10)) * 16 + (e & 15)] : 1.f;
+  }
+  // QKV: the (cos, sin) of the 8 head dims this thread rotates in the epilogue (thread ->
+  // token (t >> 1) % 64, tile pair g % (dh/16)); loaded with the first pass, so the epilogue
+  // waits for nothing (threads past 128 repeat the addresses of threads 0..127: L1 hits)
+  float4 cs_pre[4];
+  const float4* csp = (const float4*)a.rope_cs;
+  if constexpr (EPI == EPI_QKV) {
+    const int tl = (threadIdx.x >> 1) & (TOKG - 1), tok = min(tok0 + tl, a.M - 1);
+    csp += ((size_t)(tok % a.H) * (a.dh / 2) + (g % (a.dh / 16)) * 8) / 2;
   }
 
   f32x4 acc[NT][4];
@@ -398,35 +407,53 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 
   const int ntt = a.M_pad / 16;
   const XT* xg = (const XT*)a.x + ((size_t)z * 4 * 64 + lane) * 8;  // this lane's slot of token tile 4z
-  for (int p = 0; p < a.passes; ++p) {
+  // pass p: wave w owns k-blocks kb0 .. kb0 + KPW
+  auto issue = [&](int p, typename F::A (&wa)[NT][KPW], typename F::B (&xb)[KPW][4]) {
     const int kb0 = s * (KB / a.S) + (p * GW + wave) * KPW;
-    typename F::A wa[NT][KPW];
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < KPW; ++j) wa[nt][j] = F::load_a(a.w, ((size_t)g * NT + nt) * KB + kb0 + j, lane);
-    // activation fragments; lanes of tokens past M (padding of the last token group) load nothing
-    typename F::B xb[KPW][4];
+    // activation fragments, unconditional: the padding tokens of the last group are in bounds
+    // (buffers hold M_pad rows) and only reach output columns that are never stored (tokens are
+    // MFMA columns, nothing mixes across them); a per-lane condition here made the compiler wait
+    // for each load before issuing the next
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-        xb[j][tt] = (tok0 + tt * 16 + (lane & 15) < a.M) ? F::load_b(xg + ((size_t)(kb0 + j) * ntt + tt) * 512)
-                                                         : F::zero_b();
-    if (p == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gi = (threadIdx.x >> 6) + 8 * i;
-        ssv[i] = sp[(has_ssp && gi < a.g_in) ? (size_t)gi * a.M_pad : 0];
-      }
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
+      for (int tt = 0; tt < 4; ++tt) xb[j][tt] = F::load_b(xg + ((size_t)(kb0 + j) * ntt + tt) * 512);
+  };
+  auto compute = [&](const typename F::A (&wa)[NT][KPW], const typename F::B (&xb)[KPW][4]) {
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][tt] = F::mma(wa[nt][j], xb[j][tt], acc[nt][tt]);
+  };
+  {
+    typename F::A wa[NT][KPW];
+    typename F::B xb[KPW][4];
+    issue(0, wa, xb);
+    // after the first pass's loads (they retire in order, so the MFMAs do not wait for these)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int gi = (threadIdx.x >> 6) + 8 * i;
+      ssv[i] = sp[(has_ssp && gi < a.g_in) ? (size_t)gi * a.M_pad : 0];
+    }
+    if constexpr (EPI == EPI_QKV) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) cs_pre[j] = csp[j];
+    }
+    __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
+    compute(wa, xb);
+  }
+  for (int p = 1; p < a.passes; ++p) {
+    typename F::A wa[NT][KPW];
+    typename F::B xb[KPW][4];
+    issue(p, wa, xb);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(wa, xb);
   }
 
   // next kernel's operands into L2 while this one reduces and runs its epilogue (no
@@ -583,11 +610,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         const int sq = tok / a.H, t = tok % a.H;
         const float ir = inv_rms[tl];
         const float* rr = res + tl * 16;
-        const float4* csp = (const float4*)(a.rope_cs + ((size_t)t * half + pair * 8) * 2);
         float out[8];
 #pragma unroll
         for (int j = 0; j < 8; j += 2) {
-          const float4 cs2 = csp[j / 2];  // (cos, sin) of dims pair*8 + j and + j + 1
+          const float4 cs2 = cs_pre[j / 2];  // (cos, sin) of dims pair*8 + j and + j + 1
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
             const float cs_c = u ? cs2.z : cs2.x, cs_s = u ? cs2.w : cs2.y;
@@ -639,45 +665,15 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       if (nt & 1) continue;
     }
     float val = res[e] * inv_rms[tl];
-    if constexpr (WT == WT_FP8) val *= a.wscale[tile * 16 + c];
+    if constexpr (WT == WT_FP8) val *= psc[i];
     if constexpr (EPI == EPI_QKV) {
-      // packed tiles: q heads, then k heads (RoPE pairs d, d+dh/2 share a tile), then v
-      const int tiles_per_head = a.dh / 16;
-      const int q_tiles = a.n_q * tiles_per_head, k_tiles = a.n_kv * tiles_per_head;
-      const int half = a.dh / 2;
-      const int t_in = (int)tile;
-      if (t_in < q_tiles + k_tiles) {
-        const bool is_q = t_in < q_tiles;
-        const int tt2 = is_q ? t_in : t_in - q_tiles;
-        const int head = tt2 / tiles_per_head, pair = tt2 % tiles_per_head;
-        const int d = pair * 8 + (c & 7);
-        const float partner = res[e ^ 8] * inv_rms[tl];
-        const float2 cs = make_float2(pre0[i], pre1[i]);
-        float out;
-        int dfull;
-        if (c < 8) { out = val * cs.x - partner * cs.y; dfull = d; }
-        else { out = partner * cs.y + val * cs.x; dfull = half + d; }
-        if (valid) {
-          const int sq = tok / a.H, t = tok % a.H;
-          const int nkb = a.dh / KBLK, lgrp = ((dfull % KBLK) >> 3) << 4, e8 = dfull & 7, kb = dfull / KBLK;
-          if (is_q) {  // query B fragments: row r = j*H + t of the tile, dims kb*32 + (lane/16)*8
-            const int gq = a.n_q / a.n_kv, g = head / gq, r = (head % gq) * a.H + t;
-            const size_t fr = ((((size_t)sq * a.n_kv + g) * a.n_qt + r / 16) * nkb + kb);
-            Act<AT>::st((XT*)a.q_out, fr * 512 + (lgrp + (r & 15)) * 8 + e8, out);
-          } else {     // key A fragments of 32-key block t/32, keys in the order the attention expects
-            const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
-            const size_t fr = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb);
-            Act<AT>::st((XT*)a.k_out, fr * 512 + (lgrp + m) * 8 + e8, out);
-          }
-        }
-      } else {
-        // value A fragments (of V^T) of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
-        const int col = (t_in - q_tiles - k_tiles) * 16 + c;
-        if (valid) {
-          const int sq = tok / a.H, t = tok % a.H, hd = col / a.dh, d = col % a.dh, kk = t & 31;
-          const size_t fr = ((((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d / 16);
-          Act<AT>::st((XT*)a.v_out, fr * 512 + (((kk >> 3) << 4) + (d & 15)) * 8 + (kk & 7), val);
-        }
+      // v tiles only (q and k tiles took the vectorised path above): value A fragments (of V^T)
+      // of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
+      const int col = ((int)tile - (a.n_q + a.n_kv) * (a.dh / 16)) * 16 + c;
+      if (valid) {
+        const int sq = tok / a.H, t = tok % a.H, hd = col / a.dh, d = col % a.dh, kk = t & 31;
+        const size_t fr = ((((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d / 16);
+        Act<AT>::st((XT*)a.v_out, fr * 512 + (((kk >> 3) << 4) + (d & 15)) * 8 + (kk & 7), val);
       }
     } else if constexpr (EPI == EPI_RESID) {
       const int n = (int)tile * 16 + c;
@@ -695,15 +691,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       if (c == 0) a.ssp_out[tile * a.M_pad + tok] = sq;
     } else if constexpr (EPI == EPI_GEGLU) {
       float up = res[e + 1024] * inv_rms[tl];
-      if constexpr (WT == WT_FP8) up *= a.wscale[(tile + 1) * 16 + c];
+      if constexpr (WT == WT_FP8) up *= psc[(i + 2) & (2 * NT - 1)];  // the up tile of this gate element
       const int f = (int)(tile / 2) * 16 + c;
       if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
-    } else {  // EPI_OUT
+    } else {  // EPI_OUT: bias and x were loaded at the start (pre0, pre1)
       const int n = (int)tile * 16 + c;
       if (valid && n < a.A) {
-        const float v = val + a.bias[n];
-        if (a.dt > 0.f) a.xio[(size_t)tok * a.A + n] += a.dt * v;
-        else a.xio[(size_t)tok * a.A + n] = v;
+        const float v = val + pre0[i];
+        a.xio[(size_t)tok * a.A + n] = a.dt > 0.f ? pre1[i] + a.dt * v : v;
       }
     }
   }
@@ -767,7 +762,7 @@ struct AttnArgs {
   const void* vs;         // packed suffix V
   const void* kcache;     // packed prefix K [slot][L][n_kv][nbp][2][dh/32][64][8]
   const void* vcache;     // packed prefix V [slot][L][n_kv][nbp][dh/16][64][8]
-  const int* seq_slot;    // prefix slot of each sequence
+  const int* seq_slot;    // prefix slot of each sequence; null: sequence s uses slot s (no load)
   size_t slot_stride, layer_off;  // elements (same for K and V)
   int P, H, n_q, n_kv, dh;
   int nbp, nbs;           // 32-key prefix / suffix blocks
@@ -826,7 +821,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int gq = a.n_q / a.n_kv;
   const int R = gq * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = a.seq_slot[s];
+  const int slot = a.seq_slot ? a.seq_slot[s] : s;
   const int nb = a.nbp + a.nbs;
   const int bps = (nb + a.n_split - 1) / a.n_split;         // blocks per split
   const int b_begin = split * bps, b_end = min(nb, b_begin + bps);

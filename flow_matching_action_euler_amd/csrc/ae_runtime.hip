@@ -123,7 +123,7 @@ struct ae_handle {
   void *kcache = nullptr, *vcache = nullptr;
   size_t slot_elems = 0;     // elements of one slot's packed K (and V) cache
   std::vector<int> slot_ready;
-  int *denoise_slots = nullptr, *verify_slots = nullptr;
+  int* verify_slots = nullptr;
   // verify inputs / outputs
   float *draft = nullptr, *vnoise = nullptr, *taus = nullptr, *temb_tau = nullptr, *phi = nullptr, *hid = nullptr,
         *dist = nullptr, *params = nullptr;
@@ -600,7 +600,8 @@ int get_temb_steps(ae_handle* h, int steps, float** out) {
 int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t st, Timer* tm) {
   const float dt = 1.f / (float)steps;
   for (int k = 0; k < steps; ++k) {
-    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, h->denoise_slots, dt, st, tm);
+    // robot b uses prefix slot b: no slot table (the attention then reads no slot from memory)
+    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, nullptr, dt, st, tm);
     if (rc) return rc;
   }
   return AE_OK;
@@ -820,11 +821,6 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc(h, &h->kcache, h->slot_elems * c.max_batch * kes));
   TRY(dalloc(h, &h->vcache, h->slot_elems * c.max_batch * kes));
   h->slot_ready.assign(c.max_batch, 0);
-  {
-    std::vector<int> ids(c.max_batch);
-    for (int i = 0; i < c.max_batch; ++i) ids[i] = i;
-    TRY(upload(h, (void**)&h->denoise_slots, ids.data(), ids.size() * 4));
-  }
   const int ntau = std::max(1, c.max_taus);
   TRY(dalloc_t(h, &h->verify_slots, ntau));
   TRY(dalloc_t(h, &h->draft, (size_t)H * A));
