@@ -206,6 +206,7 @@ struct GemmArgs {
   float* part;          // split-K partials [S][n_z][n_groups][NT*64*16], EXCH_EMPTY between launches
   unsigned* counters;   // [n_z][n_groups], zero between launches (arrival tickets)
   int exch_poll;        // 1: every workgroup is resident at once; split S-1 polls the others' partials
+  int poll_delay;       // ~0.2 us steps split S-1 waits before its first poll (the partials' flight time)
   unsigned* err;        // set if a poll gave up
   // EPI_QKV
   void* q_out; void* k_out; void* v_out;   // attention operands in fragment order (see the attention section)
@@ -527,6 +528,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         return;
       }
       bool gave_up = false;
+      for (int d = 0; d < a.poll_delay; ++d) __builtin_amdgcn_s_sleep(8);
 #pragma unroll
       for (int i = 0; i < (NT + 1) / 2; ++i) {
         const int qd = threadIdx.x + GTHREADS * i;

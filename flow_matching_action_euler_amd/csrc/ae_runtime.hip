@@ -356,10 +356,22 @@ AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 
+// Steps of ~0.2 us that a split-K consumer sleeps before its first poll, so that the poll
+// finds the other splits' partials landed instead of costing a second round trip (measured
+// for Pi0: 1 step saves 0.16 ms per chunk, 2-6 steps less); AE_POLL_DELAY overrides it.
+int poll_delay() {
+  static int n = [] {
+    const char* e = getenv("AE_POLL_DELAY");
+    return e ? atoi(e) : 1;
+  }();
+  return n;
+}
+
 struct Dispatch {
   // one launcher per role bound to the handle's dtypes (fp8 weights: MLP roles only)
   static hipError_t gemm(ae_handle* h, int role, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
     a.exch_poll = h->poll_splitk && (long long)n_groups * a.S * n_z <= h->n_cu;  // one workgroup per CU fits them all
+    a.poll_delay = poll_delay();
     a.err = h->err_flag;
     if (h->at == AT_F32) {
       switch (role) {
