@@ -93,6 +93,105 @@ def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0):
                       f"{el:.1f} s"}
 
 
+def bench_verify(args, cfg, W, kvs, ex, stream):
+    """Verify passes: every flow time of one draft in one batched pass (M = n_tau * H), timed
+    like the chunks (warm-up, then events around each pass on the library's stream)."""
+    import torch
+    from workload import gen as G
+    sp = stream.cuda_stream
+    draft, noise, taus = G.make_verify_case(cfg, 0)
+    n_tau = len(taus)
+    d_draft = torch.from_numpy(draft).cuda()
+    d_noise = torch.from_numpy(noise).cuda()
+    d_taus = torch.from_numpy(taus).cuda()
+    d_acc = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_sw = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_dist = torch.zeros((n_tau, cfg.horizon), dtype=torch.float32, device="cuda")
+    args_v = (0, d_draft.data_ptr(), d_noise.data_ptr(), d_taus.data_ptr(), n_tau, 0.05, d_acc.data_ptr(),
+              d_sw.data_ptr(), d_dist.data_ptr(), sp)
+    ex.verify(0, draft, noise, taus, 0.05)  # captures the graph; sets the inputs ae_kernel_times reuses
+    for _ in range(args.warmup):
+        ex.verify_async(*args_v)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        ex.verify_async(*args_v)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    pass_ms = np.array([a.elapsed_time(b) for a, b in evs])
+    assert np.all(np.isfinite(d_dist.cpu().numpy()))
+    kb = kernel_bytes(cfg)
+    kernels = {}
+    if not args.no_kernel_times:
+        for name, launches, total in ex.kernel_times(3, n_tau, cfg.steps, args.kernel_iters):
+            if launches == 0:
+                continue
+            avg_us = total * 1e3 / launches
+            entry = {"launches_per_pass": launches // args.kernel_iters, "avg_us": round(avg_us, 3),
+                     "ms_per_pass": round(total / args.kernel_iters, 4)}
+            if name in kb:
+                kvb = 2 if cfg.kv_dtype == "bf16" else 4
+                suffix = 2 * cfg.horizon * cfg.n_kv_heads * cfg.head_dim * kvb  # every flow time shares the prefix
+                per_launch = kb[name] + (n_tau - 1) * suffix if name == "attn" else kb[name]
+                entry["alg_bytes"] = per_launch
+                entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+            kernels[name] = entry
+    dom = max(kernels, key=lambda n: kernels[n]["ms_per_pass"]) if kernels else None
+    achieved = kernels[dom].get("GBs") if dom else None
+    sb = step_bytes(cfg, 1)
+    ms = elapsed * 1e3 / args.steps
+    result = {
+        "metric": "verify passes/s (all flow times of one draft, Pi0-scale expert)",
+        "value": round(args.steps / elapsed, 2),
+        "unit": "verify passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix KV, random-walk draft, N(0,1) noise)",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "width": cfg.width, "prefix_len": cfg.prefix_len,
+                   "chunk": f"{cfg.horizon}x{cfg.action_dim}", "flow_times": n_tau, "rows": n_tau * cfg.horizon},
+        "pass_ms_median": round(float(np.median(pass_ms)), 4),
+        "pass_ms_p90": round(float(np.percentile(pass_ms, 90)), 4),
+        "pass_alg_bytes": sb,
+        "pass_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
+        "kernels": kernels,
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_verify(cfg, W, kvs[0][0], kvs[0][1])
+    ex.close()
+    print(json.dumps(result))
+
+
+def cpu_baseline_verify(cfg, W, k, v, budget_s=12.0):
+    """The oracle as it stands, timed on this host: verify passes (all flow times) of one draft."""
+    from oracle import ae_oracle as O
+    from workload import gen as G
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:
+        cores = os.cpu_count()
+    Wd = O.dequantize_weights(cfg, W)
+    kk, vv = O.decode_kv(cfg, k, v)
+    draft, noise, taus = G.make_verify_case(cfg, 0)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        O.verify(cfg, Wd, kk, vv, draft, noise, taus, 0.05)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 20:
+            break
+    return {"value": n / el, "unit": "verify passes/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} verify passes of one draft ({cfg.name}, {len(taus)} flow times, P={cfg.prefix_len}, "
+                      f"H={cfg.horizon}), fp64 numpy, {el:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +231,8 @@ def main():
     torch.cuda.synchronize()
     print(f"setup {time.perf_counter() - t_setup:.1f} s", file=sys.stderr, flush=True)
 
+    if cfg.max_taus > 0 and cfg.batch == 1 and cfg.name.endswith("verify"):
+        return bench_verify(args, cfg, W, kvs, ex, stream)
     for _ in range(args.warmup):
         ex.denoise_async(B, d_noise.data_ptr(), cfg.steps, d_out.data_ptr(), sp)
     torch.cuda.synchronize()
@@ -201,6 +302,7 @@ def main():
         "config": {"workload": cfg.name, "layers": cfg.n_layers, "width": cfg.width, "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv",
                    "head_dim": cfg.head_dim, "mlp_dim": cfg.mlp_dim, "prefix_len": cfg.prefix_len,
                    "chunk": f"{cfg.horizon}x{cfg.action_dim}", "euler_steps": cfg.steps, "robots": B},
+        "robot_steps_per_s": round(B * args.steps * cfg.steps / elapsed, 2),
         "chunk_ms_median": round(float(np.median(chunk_ms)), 4),
         "chunk_ms_p90": round(float(np.percentile(chunk_ms, 90)), 4),
         "step_alg_bytes": sb,
