@@ -202,6 +202,7 @@ struct GemmArgs {
   float inv_width;      // 1 / width of the normalised vector
   float eps;
   int M, M_pad, K, S;   // rows, padded rows, inputs, k-splits
+  int n_zt, zpw;        // 64-token groups in all, and per workgroup (grid z = ceil(n_zt / zpw); zpw = 1 if S > 1)
   int passes;           // k-passes per wave: K/32/S = passes * GW * KPW
   float* part;          // split-K partials [S][n_z][n_groups][NT*64*16], EXCH_EMPTY between launches
   unsigned* counters;   // [n_z][n_groups], zero between launches (arrival tickets)
@@ -333,7 +334,7 @@ constexpr size_t gemm_lds_size() {
 // and the matching 4 x KPW activation fragments (each one contiguous run, see
 // act_idx) straight into registers, then runs the MFMAs; no LDS staging.
 // The 8 partial tiles are summed in LDS.
-template <int WT, int AT, int EPI, int NT, int KPW>
+template <int WT, int AT, int EPI, int NT, int KPW, bool LOOP>
 __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT, AT> F;
@@ -347,83 +348,34 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 
   AE_TR(0);
   AE_TRC(6);
-  const int g = blockIdx.x, s = blockIdx.y, z = blockIdx.z;
+  const int g = blockIdx.x, s = blockIdx.y;
   const int n_groups = gridDim.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int KB = a.K / KBLK;
-  const int tok0 = z * TOKG;
-
-  // partial sums of h^2: thread -> token t & 63, groups (t >> 6) + 8 i; loaded right after the
-  // first pass's weights and activations (loads retire in order, so the MFMAs do not wait for
-  // them), summed after the MFMAs. The loads are unconditional (a valid fallback address,
-  // masked at the sum): a conditional load let the compiler start the sum, and wait for it,
-  // before the main loads were issued.
-  float ssv[8];
   const bool has_ssp = a.ssp_in != nullptr;
-  const float* sp = has_ssp ? a.ssp_in + tok0 + (threadIdx.x & 63) : (const float*)a.w;
-
-  // epilogue operands that do not depend on the product, loaded before the main loads:
-  // element e = t + 512 i -> (nt = e / 1024, token (e / 16) % 64, channel e % 16)
-  float pre0[2 * NT], pre1[2 * NT];
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    const int e = threadIdx.x + GTHREADS * i;
-    const int nt = e >> 10, tl = (e >> 4) & 63, c = e & 15;
-    const size_t tile = (size_t)g * NT + nt;
-    const int tok = tok0 + tl;
-    pre0[i] = 0.f;
-    pre1[i] = 0.f;
-    if constexpr (EPI == EPI_RESID) {
-      if (tok < a.M) pre0[i] = a.h[(size_t)tok * a.N + tile * 16 + c];
-      pre1[i] = a.gain_next[tile * 16 + c];
-    } else if constexpr (EPI == EPI_OUT) {
-      const int n = (int)tile * 16 + c;
-      const bool ok = n < a.A && tok < a.M;  // unconditional loads (clamped), masked at use
-      pre0[i] = a.bias[n < a.A ? n : 0];
-      pre1[i] = a.dt > 0.f ? a.xio[ok ? (size_t)tok * a.A + n : 0] : 0.f;
-    }
-  }
-  // fp8 weights: the per-row scale of each epilogue element, loaded now
-  float psc[2 * NT];
-#pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    const int e = threadIdx.x + GTHREADS * i;
-    psc[i] = WT == WT_FP8 ? a.wscale[((size_t)g * NT + (e >> 10)) * 16 + (e & 15)] : 1.f;
-  }
-  // QKV: the (cos, sin) of the 8 head dims this thread rotates in the epilogue (thread ->
-  // token (t >> 1) % 64, tile pair g % (dh/16)); loaded with the first pass, so the epilogue
-  // waits for nothing (threads past 128 repeat the addresses of threads 0..127: L1 hits)
-  float4 cs_pre[4];
-  const float4* csp = (const float4*)a.rope_cs;
-  if constexpr (EPI == EPI_QKV) {
-    const int tl = (threadIdx.x >> 1) & (TOKG - 1), tok = min(tok0 + tl, a.M - 1);
-    csp += ((size_t)(tok % a.H) * (a.dh / 2) + (g % (a.dh / 16)) * 8) / 2;
-  }
-
-  f32x4 acc[NT][4];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt) acc[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int ntt = a.M_pad / 16;
-  const XT* xg = (const XT*)a.x + ((size_t)z * 4 * 64 + lane) * 8;  // this lane's slot of token tile 4z
   // pass p: wave w owns k-blocks kb0 .. kb0 + KPW
-  auto issue = [&](int p, typename F::A (&wa)[NT][KPW], typename F::B (&xb)[KPW][4]) {
+  auto issue_w = [&](int p, typename F::A (&wa)[NT][KPW]) {
     const int kb0 = s * (KB / a.S) + (p * GW + wave) * KPW;
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int j = 0; j < KPW; ++j) wa[nt][j] = F::load_a(a.w, ((size_t)g * NT + nt) * KB + kb0 + j, lane);
-    // activation fragments, unconditional: the padding tokens of the last group are in bounds
-    // (buffers hold M_pad rows) and only reach output columns that are never stored (tokens are
-    // MFMA columns, nothing mixes across them); a per-lane condition here made the compiler wait
-    // for each load before issuing the next
+  };
+  // activation fragments of token group z, unconditional: the padding tokens of the last group
+  // are in bounds (buffers hold M_pad rows) and only reach output columns that are never stored
+  // (tokens are MFMA columns, nothing mixes across them); a per-lane condition here made the
+  // compiler wait for each load before issuing the next
+  auto issue_x = [&](int p, int z, typename F::B (&xb)[KPW][4]) {
+    const int kb0 = s * (KB / a.S) + (p * GW + wave) * KPW;
+    const XT* xg = (const XT*)a.x + ((size_t)z * 4 * 64 + lane) * 8;  // this lane's slot of token tile 4z
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
 #pragma unroll
       for (int tt = 0; tt < 4; ++tt) xb[j][tt] = F::load_b(xg + ((size_t)(kb0 + j) * ntt + tt) * 512);
   };
+  f32x4 acc[NT][4];
   auto compute = [&](const typename F::A (&wa)[NT][KPW], const typename F::B (&xb)[KPW][4]) {
 #pragma unroll
     for (int j = 0; j < KPW; ++j)
@@ -432,277 +384,347 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[nt][tt] = F::mma(wa[nt][j], xb[j][tt], acc[nt][tt]);
   };
-  {
-    typename F::A wa[NT][KPW];
-    typename F::B xb[KPW][4];
-    issue(0, wa, xb);
-    // after the first pass's loads (they retire in order, so the MFMAs do not wait for these)
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int gi = (threadIdx.x >> 6) + 8 * i;
-      ssv[i] = sp[(has_ssp && gi < a.g_in) ? (size_t)gi * a.M_pad : 0];
-    }
-    if constexpr (EPI == EPI_QKV) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) cs_pre[j] = csp[j];
-    }
-    __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
-    compute(wa, xb);
-  }
-  for (int p = 1; p < a.passes; ++p) {
-    typename F::A wa[NT][KPW];
-    typename F::B xb[KPW][4];
-    issue(p, wa, xb);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(wa, xb);
-  }
 
-  // next kernel's operands into L2 while this one reduces and runs its epilogue (no
-  // split-K exchange in these roles, so nothing below waits on memory before the end)
   PfVals<2> pf_acc{};
-  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
-    pf_acc = prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                               gridDim.x * gridDim.y * gridDim.z, threadIdx.x, GTHREADS);
-  AE_TR(1);
-  float ssq = 0.f;
+  // token group z (the zi-th of this workgroup); true when the workgroup has nothing more to do
+  // (a split-K producer that handed over its partial)
+  typename F::A wa0[NT][KPW];  // LOOP: the first pass's weights, kept for every token group
+  auto group = [&](const int z, const int zi) __attribute__((always_inline)) -> bool {
+    const int tok0 = z * TOKG;
+    // epilogue operands of this workgroup's channels (reloaded per token group: L2 hits)
+    float gn[2 * NT];  // EPI_RESID: next gain; EPI_OUT: bias
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ssq += (has_ssp && (int)(threadIdx.x >> 6) + 8 * i < a.g_in) ? ssv[i] : 0.f;
-  if (a.ssp_in != nullptr)
-    for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
-  // cross-wave reduction: red[wave][nt][tt][channel quad][token % 16][4], so the 16 lanes of a
-  // write phase cover 256 consecutive bytes (no bank conflicts); res is [nt][token][channel]
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int tt = 0; tt < 4; ++tt)
-      *(f32x4*)(red + ((((wave * NT + nt) * 4 + tt) * 4 + (lane >> 4)) * 16 + (lane & 15)) * 4) = acc[nt][tt];
-  ssq8[threadIdx.x] = ssq;
-  __syncthreads();
-  // NT * 256 quads over 512 threads; quad qd = ((nt * 4 + tt) * 4 + cq) * 16 + t
-#pragma unroll
-  for (int i = 0; i < (NT + 1) / 2; ++i) {
-    const int qd = threadIdx.x + GTHREADS * i;
-    if (qd < NT * 256) {
-      f32x4 sum = *(const f32x4*)(red + qd * 4);
-#pragma unroll
-      for (int w = 1; w < GW; ++w) sum += *(const f32x4*)(red + w * NT * 1024 + qd * 4);
-      const int nt = qd >> 8, tt = (qd >> 6) & 3, cq = (qd >> 4) & 3, t = qd & 15;
-      *(f32x4*)(res + nt * 1024 + (tt * 16 + t) * 16 + cq * 4) = sum;
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int e = threadIdx.x + GTHREADS * i;
+      const int n = (int)((size_t)g * NT + (e >> 10)) * 16 + (e & 15);
+      gn[i] = 0.f;
+      if constexpr (EPI == EPI_RESID) gn[i] = a.gain_next[n];
+      else if constexpr (EPI == EPI_OUT) gn[i] = a.bias[n < a.A ? n : 0];
     }
-  }
-  if (threadIdx.x < TOKG) {
-    float r = 1.f;
-    if (a.ssp_in != nullptr) {
-      float t8 = 0.f;
+    // fp8 weights: the per-row scale of each epilogue element, loaded now
+    float psc[2 * NT];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) t8 += ssq8[q * 64 + threadIdx.x];
-      r = rsqrtf(t8 * a.inv_width + a.eps);
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int e = threadIdx.x + GTHREADS * i;
+      psc[i] = WT == WT_FP8 ? a.wscale[((size_t)g * NT + (e >> 10)) * 16 + (e & 15)] : 1.f;
     }
-    inv_rms[threadIdx.x] = r;
-  }
-  __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt) acc[nt][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  AE_TR(2);
-  if (a.S > 1) {
-    const int n_z = gridDim.z;
-    const int tile_elems = NT * 1024;
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part);
-    auto poff = [&](int ss, int qd) {
-      return (unsigned)(((((size_t)ss * n_z + z) * n_groups + g) * tile_elems + qd * 4) * 4);
-    };
-    if (a.exch_poll) {
-      // split-K, all workgroups resident: splits 0..S-2 publish their partial write-through and
-      // leave; split S-1 (the highest workgroup ids of the tile) adds them as they land, in split
-      // order (deterministic), and empties them
-      if (s != a.S - 1) {
+    // partial sums of h^2 (thread -> token t & 63, groups (t >> 6) + 8 i), the residual or x
+    // (element e = t + 512 i -> (nt = e / 1024, token (e / 16) % 64, channel e % 16)) and the
+    // RoPE (cos, sin) of the 8 head dims this thread rotates (thread -> token (t >> 1) % 64,
+    // pair g % (dh/16); threads past 128 repeat addresses: L1 hits): loaded right after the
+    // first pass's activations (loads retire in order, so the MFMAs do not wait for them). The
+    // loads are unconditional (clamped or fallback addresses, masked at use): a conditional load
+    // let the compiler wait for it before the main loads were issued, and so did a 64-bit offset
+    // product for ssv (its register pair overlapped a load in flight), hence 32-bit offsets there.
+    float ssv[8];
+    const float* sp = has_ssp ? a.ssp_in + tok0 + (threadIdx.x & 63) : (const float*)a.w;
+    float pre0[2 * NT];  // EPI_RESID: h; EPI_OUT: x
+    float4 cs_pre[4];
+    {
+      typename F::A wa[NT][KPW];
+      typename F::B xb[KPW][4];
+      if constexpr (!LOOP) issue_w(0, wa);
+      issue_x(0, z, xb);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int gi = (threadIdx.x >> 6) + 8 * i;
+        ssv[i] = sp[(has_ssp && gi < a.g_in) ? gi * a.M_pad : 0];
+      }
+#pragma unroll
+      for (int i = 0; i < 2 * NT; ++i) {
+        const int e = threadIdx.x + GTHREADS * i;
+        const int tok = min(tok0 + ((e >> 4) & 63), a.M - 1);
+        const int n = (int)((size_t)g * NT + (e >> 10)) * 16 + (e & 15);
+        pre0[i] = 0.f;
+        if constexpr (EPI == EPI_RESID) pre0[i] = a.h[(size_t)tok * a.N + n];
+        else if constexpr (EPI == EPI_OUT) pre0[i] = a.dt > 0.f ? a.xio[(size_t)tok * a.A + (n < a.A ? n : 0)] : 0.f;
+      }
+      if constexpr (EPI == EPI_QKV) {
+        const int tok = min(tok0 + ((threadIdx.x >> 1) & (TOKG - 1)), a.M - 1);
+        const float4* csp = (const float4*)a.rope_cs + ((size_t)(tok % a.H) * (a.dh / 2) + (g % (a.dh / 16)) * 8) / 2;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) cs_pre[j] = csp[j];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // every load of the pass in flight before the first MFMA
+      if constexpr (LOOP) compute(wa0, xb);
+      else compute(wa, xb);
+    }
+    for (int p = 1; p < a.passes; ++p) {
+      typename F::A wa[NT][KPW];
+      typename F::B xb[KPW][4];
+      issue_w(p, wa);
+      issue_x(p, z, xb);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa, xb);
+    }
+
+    // next kernel's operands into L2 while this one reduces and runs its epilogue (no
+    // split-K exchange in these roles, so nothing below waits on memory before the end)
+    if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
+      if (zi == 0)
+        pf_acc = prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                   gridDim.x * gridDim.y * gridDim.z, threadIdx.x, GTHREADS);
+    AE_TR(1);
+    float ssq = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ssq += (has_ssp && (int)(threadIdx.x >> 6) + 8 * i < a.g_in) ? ssv[i] : 0.f;
+    if (a.ssp_in != nullptr)
+      for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
+#ifdef AE_TRACE
+    if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
+      asm volatile("" ::"v"(ssq));
+      AE_TR(5);
+    }
+#endif
+    // cross-wave reduction: red[wave][nt][tt][channel quad][token % 16][4], so the 16 lanes of a
+    // write phase cover 256 consecutive bytes (no bank conflicts); res is [nt][token][channel]
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int tt = 0; tt < 4; ++tt)
+        *(f32x4*)(red + ((((wave * NT + nt) * 4 + tt) * 4 + (lane >> 4)) * 16 + (lane & 15)) * 4) = acc[nt][tt];
+    ssq8[threadIdx.x] = ssq;
+    __syncthreads();
+    // NT * 256 quads over 512 threads; quad qd = ((nt * 4 + tt) * 4 + cq) * 16 + t
+#pragma unroll
+    for (int i = 0; i < (NT + 1) / 2; ++i) {
+      const int qd = threadIdx.x + GTHREADS * i;
+      if (qd < NT * 256) {
+        f32x4 sum = *(const f32x4*)(red + qd * 4);
+#pragma unroll
+        for (int w = 1; w < GW; ++w) sum += *(const f32x4*)(red + w * NT * 1024 + qd * 4);
+        const int nt = qd >> 8, tt = (qd >> 6) & 3, cq = (qd >> 4) & 3, t = qd & 15;
+        *(f32x4*)(res + nt * 1024 + (tt * 16 + t) * 16 + cq * 4) = sum;
+      }
+    }
+    if (threadIdx.x < TOKG) {
+      float r = 1.f;
+      if (a.ssp_in != nullptr) {
+        float t8 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) t8 += ssq8[q * 64 + threadIdx.x];
+        r = rsqrtf(t8 * a.inv_width + a.eps);
+      }
+      inv_rms[threadIdx.x] = r;
+    }
+    __syncthreads();
+
+    AE_TR(2);
+    if (a.S > 1) {  // one token group (zpw = 1)
+      const int n_z = a.n_zt;
+      const int tile_elems = NT * 1024;
+      const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.part);
+      auto poff = [&](int ss, int qd) {
+        return (unsigned)(((((size_t)ss * n_z + z) * n_groups + g) * tile_elems + qd * 4) * 4);
+      };
+      if (a.exch_poll) {
+        // split-K, all workgroups resident: splits 0..S-2 publish their partial write-through and
+        // leave; split S-1 (the highest workgroup ids of the tile) adds them as they land, in split
+        // order (deterministic), and empties them
+        if (s != a.S - 1) {
+#pragma unroll
+          for (int i = 0; i < (NT + 1) / 2; ++i) {
+            const int qd = threadIdx.x + GTHREADS * i;
+            if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
+          }
+          // this workgroup's HBM reads are over while split S-1 still merges: place the next
+          // GEMM's weights in L2 (producers are workgroup ids below n_groups * (S-1) * n_z)
+          if (a.pf.kind == 2)
+            prefetch_done(prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
+                                            gridDim.x * (gridDim.y - 1) * gridDim.z, threadIdx.x, GTHREADS));
+          return true;
+        }
+        bool gave_up = false;
+        for (int d = 0; d < a.poll_delay; ++d) __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+        for (int i = 0; i < (NT + 1) / 2; ++i) {
+          const int qd = threadIdx.x + GTHREADS * i;
+          if (qd < NT * 256) {
+            f32x4 v[3];
+            const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
+            int polls = 0;
+            for (;; ++polls) {
+              bool ok = true;
+#pragma unroll
+              for (int ss = 0; ss < 3; ++ss) {
+                v[ss] = ss < a.S - 1 ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
+                ok = ok && exch_arrived(v[ss]);
+              }
+              if (ok) break;
+              if (wall_clock64() > t_end) { gave_up = true; break; }
+              __builtin_amdgcn_s_sleep(1);
+            }
+            if (i == 0) AE_TRV(5, polls + 1);
+            const f32x4 own = *(const f32x4*)(res + qd * 4);
+            const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 sum = v[0] + (a.S == 2 ? own : v[1]);
+            sum = sum + (a.S == 3 ? own : v[2]);
+            sum = sum + (a.S == 4 ? own : zero);
+            *(f32x4*)(res + qd * 4) = sum;
+#pragma unroll
+            for (int ss = 0; ss < 3; ++ss)
+              if (ss < a.S - 1) st16_empty(rp, poff(ss, qd));
+          }
+        }
+        if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+      } else {
+        // split-K, more workgroups than fit at once: publish the partial, count arrivals; the
+        // last arriver of (z, g) sums the S partials in split order and empties them
 #pragma unroll
         for (int i = 0; i < (NT + 1) / 2; ++i) {
           const int qd = threadIdx.x + GTHREADS * i;
           if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
         }
-        // this workgroup's HBM reads are over while split S-1 still merges: place the next
-        // GEMM's weights in L2 (producers are workgroup ids below n_groups * (S-1) * n_z)
-        if (a.pf.kind == 2)
-          prefetch_done(prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
-                                          gridDim.x * (gridDim.y - 1) * gridDim.z, threadIdx.x, GTHREADS));
-        return;
-      }
-      bool gave_up = false;
-      for (int d = 0; d < a.poll_delay; ++d) __builtin_amdgcn_s_sleep(8);
+        wait_mem();
+        __syncthreads();
+        unsigned* cnt = a.counters + z * n_groups + g;
+        if (threadIdx.x == 0) {
+          *ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (*ticket == (unsigned)a.S - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        if (*ticket != (unsigned)a.S - 1) return true;
 #pragma unroll
-      for (int i = 0; i < (NT + 1) / 2; ++i) {
-        const int qd = threadIdx.x + GTHREADS * i;
-        if (qd < NT * 256) {
-          f32x4 v[3];
-          const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
-          int polls = 0;
-          for (;; ++polls) {
-            bool ok = true;
+        for (int i = 0; i < (NT + 1) / 2; ++i) {
+          const int qd = threadIdx.x + GTHREADS * i;
+          if (qd < NT * 256) {
+            f32x4 v[4];
 #pragma unroll
-            for (int ss = 0; ss < 3; ++ss) {
-              v[ss] = ss < a.S - 1 ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
-              ok = ok && exch_arrived(v[ss]);
-            }
-            if (ok) break;
-            if (wall_clock64() > t_end) { gave_up = true; break; }
-            __builtin_amdgcn_s_sleep(1);
+            for (int ss = 0; ss < 4; ++ss)
+              v[ss] = ss < a.S ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
+            *(f32x4*)(res + qd * 4) = ((v[0] + v[1]) + v[2]) + v[3];
+#pragma unroll
+            for (int ss = 0; ss < 4; ++ss)
+              if (ss < a.S) st16_empty(rp, poff(ss, qd));
           }
-          if (i == 0) AE_TRV(5, polls + 1);
-          const f32x4 own = *(const f32x4*)(res + qd * 4);
-          const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
-          f32x4 sum = v[0] + (a.S == 2 ? own : v[1]);
-          sum = sum + (a.S == 3 ? own : v[2]);
-          sum = sum + (a.S == 4 ? own : zero);
-          *(f32x4*)(res + qd * 4) = sum;
-#pragma unroll
-          for (int ss = 0; ss < 3; ++ss)
-            if (ss < a.S - 1) st16_empty(rp, poff(ss, qd));
         }
+        __syncthreads();
       }
-      if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __syncthreads();
-    } else {
-      // split-K, more workgroups than fit at once: publish the partial, count arrivals; the
-      // last arriver of (z, g) sums the S partials in split order and empties them
-#pragma unroll
-      for (int i = 0; i < (NT + 1) / 2; ++i) {
-        const int qd = threadIdx.x + GTHREADS * i;
-        if (qd < NT * 256) st16_coherent(rp, poff(s, qd), *(const float4*)(res + qd * 4));
-      }
-      wait_mem();
-      __syncthreads();
-      unsigned* cnt = a.counters + z * n_groups + g;
-      if (threadIdx.x == 0) {
-        *ticket = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (*ticket == (unsigned)a.S - 1) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-      __syncthreads();
-      if (*ticket != (unsigned)a.S - 1) return;
-#pragma unroll
-      for (int i = 0; i < (NT + 1) / 2; ++i) {
-        const int qd = threadIdx.x + GTHREADS * i;
-        if (qd < NT * 256) {
-          f32x4 v[4];
-#pragma unroll
-          for (int ss = 0; ss < 4; ++ss)
-            v[ss] = ss < a.S ? ld16_coherent(rp, poff(ss, qd)) : f32x4{0.f, 0.f, 0.f, 0.f};
-          *(f32x4*)(res + qd * 4) = ((v[0] + v[1]) + v[2]) + v[3];
-#pragma unroll
-          for (int ss = 0; ss < 4; ++ss)
-            if (ss < a.S) st16_empty(rp, poff(ss, qd));
-        }
-      }
-      __syncthreads();
     }
-  }
 
-  AE_TR(3);
-  if constexpr (EPI == EPI_QKV) {
-    // q and k tiles: thread -> (token, half of the tile's 16 channels) = 8 consecutive head dims,
-    // rotated and stored as one 16-byte run of a fragment row
-    const int tiles_per_head = a.dh / 16, half = a.dh / 2;
-    const int q_tiles = a.n_q * tiles_per_head, k_tiles = a.n_kv * tiles_per_head;
-    const int t_in = (int)g;  // one tile per workgroup
-    if (t_in < q_tiles + k_tiles) {
-      const int tl = threadIdx.x >> 1, hf = threadIdx.x & 1, tok = tok0 + tl;
-      if (threadIdx.x < 2 * TOKG && tok < a.M) {
-        const bool is_q = t_in < q_tiles;
-        const int tt2 = is_q ? t_in : t_in - q_tiles;
-        const int head = tt2 / tiles_per_head, pair = tt2 % tiles_per_head;
-        const int sq = tok / a.H, t = tok % a.H;
-        const float ir = inv_rms[tl];
-        const float* rr = res + tl * 16;
-        float out[8];
+    AE_TR(3);
+    if constexpr (EPI == EPI_QKV) {
+      // q and k tiles: thread -> (token, half of the tile's 16 channels) = 8 consecutive head dims,
+      // rotated and stored as one 16-byte run of a fragment row
+      const int tiles_per_head = a.dh / 16, half = a.dh / 2;
+      const int q_tiles = a.n_q * tiles_per_head, k_tiles = a.n_kv * tiles_per_head;
+      const int t_in = (int)g;  // one tile per workgroup
+      if (t_in < q_tiles + k_tiles) {
+        const int tl = threadIdx.x >> 1, hf = threadIdx.x & 1, tok = tok0 + tl;
+        if (threadIdx.x < 2 * TOKG && tok < a.M) {
+          const bool is_q = t_in < q_tiles;
+          const int tt2 = is_q ? t_in : t_in - q_tiles;
+          const int head = tt2 / tiles_per_head, pair = tt2 % tiles_per_head;
+          const int sq = tok / a.H, t = tok % a.H;
+          const float ir = inv_rms[tl];
+          const float* rr = res + tl * 16;
+          float out[8];
 #pragma unroll
-        for (int j = 0; j < 8; j += 2) {
-          const float4 cs2 = cs_pre[j / 2];  // (cos, sin) of dims pair*8 + j and + j + 1
+          for (int j = 0; j < 8; j += 2) {
+            const float4 cs2 = cs_pre[j / 2];  // (cos, sin) of dims pair*8 + j and + j + 1
 #pragma unroll
-          for (int u = 0; u < 2; ++u) {
-            const float cs_c = u ? cs2.z : cs2.x, cs_s = u ? cs2.w : cs2.y;
-            const float x1 = rr[j + u] * ir, x2 = rr[8 + j + u] * ir;  // dims d and d + dh/2
-            out[j + u] = hf ? x1 * cs_s + x2 * cs_c : x1 * cs_c - x2 * cs_s;
+            for (int u = 0; u < 2; ++u) {
+              const float cs_c = u ? cs2.z : cs2.x, cs_s = u ? cs2.w : cs2.y;
+              const float x1 = rr[j + u] * ir, x2 = rr[8 + j + u] * ir;  // dims d and d + dh/2
+              out[j + u] = hf ? x1 * cs_s + x2 * cs_c : x1 * cs_c - x2 * cs_s;
+            }
+          }
+          const int dfull = hf * half + pair * 8;
+          const int nkb = a.dh / KBLK, lgrp = ((dfull % KBLK) >> 3) << 4, kb = dfull / KBLK;
+          size_t off;
+          if (is_q) {  // query B fragments: row r = j*H + t of the tile, dims kb*32 + (lane/16)*8
+            const int gq = a.n_q / a.n_kv, gg = head / gq, r = (head % gq) * a.H + t;
+            off = ((((size_t)sq * a.n_kv + gg) * a.n_qt + r / 16) * nkb + kb) * 512 + (lgrp + (r & 15)) * 8;
+          } else {     // key A fragments of 32-key block t/32, keys in the order the attention expects
+            const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+            off = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb) * 512 + (lgrp + m) * 8;
+          }
+          XT* dst = (XT*)(is_q ? a.q_out : a.k_out) + off;
+          if constexpr (AT == AT_BF16) {
+            uint4 v;
+            v.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+            v.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+            v.z = (uint32_t)f32_to_bf16(out[4]) | ((uint32_t)f32_to_bf16(out[5]) << 16);
+            v.w = (uint32_t)f32_to_bf16(out[6]) | ((uint32_t)f32_to_bf16(out[7]) << 16);
+            *(uint4*)dst = v;
+          } else {
+            ((float4*)dst)[0] = make_float4(out[0], out[1], out[2], out[3]);
+            ((float4*)dst)[1] = make_float4(out[4], out[5], out[6], out[7]);
           }
         }
-        const int dfull = hf * half + pair * 8;
-        const int nkb = a.dh / KBLK, lgrp = ((dfull % KBLK) >> 3) << 4, kb = dfull / KBLK;
-        size_t off;
-        if (is_q) {  // query B fragments: row r = j*H + t of the tile, dims kb*32 + (lane/16)*8
-          const int gq = a.n_q / a.n_kv, gg = head / gq, r = (head % gq) * a.H + t;
-          off = ((((size_t)sq * a.n_kv + gg) * a.n_qt + r / 16) * nkb + kb) * 512 + (lgrp + (r & 15)) * 8;
-        } else {     // key A fragments of 32-key block t/32, keys in the order the attention expects
-          const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
-          off = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb) * 512 + (lgrp + m) * 8;
-        }
-        XT* dst = (XT*)(is_q ? a.q_out : a.k_out) + off;
-        if constexpr (AT == AT_BF16) {
-          uint4 v;
-          v.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
-          v.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
-          v.z = (uint32_t)f32_to_bf16(out[4]) | ((uint32_t)f32_to_bf16(out[5]) << 16);
-          v.w = (uint32_t)f32_to_bf16(out[6]) | ((uint32_t)f32_to_bf16(out[7]) << 16);
-          *(uint4*)dst = v;
-        } else {
-          ((float4*)dst)[0] = make_float4(out[0], out[1], out[2], out[3]);
-          ((float4*)dst)[1] = make_float4(out[4], out[5], out[6], out[7]);
-        }
+        return false;
       }
-      prefetch_done(pf_acc);
-#ifdef AE_TRACE
-      wait_mem();
-      AE_TR(4);
-      AE_TRC(7);
-#endif
-      return;
     }
-  }
-  // ---------------- epilogues: element e -> (nt = e / 1024, token tl = (e / 16) % 64, channel c = e % 16)
+    // ---------------- epilogues: element e -> (nt = e / 1024, token tl = (e / 16) % 64, channel c = e % 16)
 #pragma unroll
-  for (int i = 0; i < 2 * NT; ++i) {
-    const int e = threadIdx.x + GTHREADS * i;
-    const int nt = e >> 10, tl = (e >> 4) & 63, c = e & 15;
-    const size_t tile = (size_t)g * NT + nt;
-    const int tok = tok0 + tl;
-    const bool valid = tok < a.M;
-    if constexpr (EPI == EPI_GEGLU) {
-      if (nt & 1) continue;
+    for (int i = 0; i < 2 * NT; ++i) {
+      const int e = threadIdx.x + GTHREADS * i;
+      const int nt = e >> 10, tl = (e >> 4) & 63, c = e & 15;
+      const size_t tile = (size_t)g * NT + nt;
+      const int tok = tok0 + tl;
+      const bool valid = tok < a.M;
+      if constexpr (EPI == EPI_GEGLU) {
+        if (nt & 1) continue;
+      }
+      float val = res[e] * inv_rms[tl];
+      if constexpr (WT == WT_FP8) val *= psc[i];
+      if constexpr (EPI == EPI_QKV) {
+        // v tiles only (q and k tiles took the vectorised path above): value A fragments (of V^T)
+        // of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
+        const int col = ((int)tile - (a.n_q + a.n_kv) * (a.dh / 16)) * 16 + c;
+        if (valid) {
+          const int sq = tok / a.H, t = tok % a.H, hd = col / a.dh, d = col % a.dh, kk = t & 31;
+          const size_t fr = ((((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d / 16);
+          Act<AT>::st((XT*)a.v_out, fr * 512 + (((kk >> 3) << 4) + (d & 15)) * 8 + (kk & 7), val);
+        }
+      } else if constexpr (EPI == EPI_RESID) {
+        const int n = (int)tile * 16 + c;
+        float hn = 0.f;
+        if (valid) {
+          hn = pre0[i] + val;
+          a.h[(size_t)tok * a.N + n] = hn;
+          Act<AT>::st((XT*)a.hb, act_idx(tok, n, a.M_pad / 16), hn * gn[i]);
+        }
+        float sq = hn * hn;
+        sq += __shfl_xor(sq, 1, 16);
+        sq += __shfl_xor(sq, 2, 16);
+        sq += __shfl_xor(sq, 4, 16);
+        sq += __shfl_xor(sq, 8, 16);
+        if (c == 0) a.ssp_out[tile * a.M_pad + tok] = sq;
+      } else if constexpr (EPI == EPI_GEGLU) {
+        float up = res[e + 1024] * inv_rms[tl];
+        if constexpr (WT == WT_FP8) up *= psc[(i + 2) & (2 * NT - 1)];  // the up tile of this gate element
+        const int f = (int)(tile / 2) * 16 + c;
+        if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
+      } else {  // EPI_OUT: bias (gn) and x (pre0) were loaded before the MFMAs
+        const int n = (int)tile * 16 + c;
+        if (valid && n < a.A) {
+          const float v = val + gn[i];
+          a.xio[(size_t)tok * a.A + n] = a.dt > 0.f ? pre0[i] + a.dt * v : v;
+        }
+      }
     }
-    float val = res[e] * inv_rms[tl];
-    if constexpr (WT == WT_FP8) val *= psc[i];
-    if constexpr (EPI == EPI_QKV) {
-      // v tiles only (q and k tiles took the vectorised path above): value A fragments (of V^T)
-      // of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
-      const int col = ((int)tile - (a.n_q + a.n_kv) * (a.dh / 16)) * 16 + c;
-      if (valid) {
-        const int sq = tok / a.H, t = tok % a.H, hd = col / a.dh, d = col % a.dh, kk = t & 31;
-        const size_t fr = ((((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d / 16);
-        Act<AT>::st((XT*)a.v_out, fr * 512 + (((kk >> 3) << 4) + (d & 15)) * 8 + (kk & 7), val);
+    return false;
+  };
+  // LOOP = false: one token group per workgroup (zpw = 1) in straight-line code: at a loop head
+  // the compiler waits for every load in flight, which would hold up the first pass
+  if constexpr (LOOP) {
+    // the first group peeled off, so that its MFMAs wait for their own loads only
+    const int z0 = blockIdx.z * a.zpw;  // < n_zt: the grid holds ceil(n_zt / zpw) rows
+    issue_w(0, wa0);
+    if (!group(z0, 0))
+      for (int zi = 1; zi < a.zpw; ++zi) {
+        const int z = z0 + zi;
+        if (z >= a.n_zt || group(z, zi)) break;
       }
-    } else if constexpr (EPI == EPI_RESID) {
-      const int n = (int)tile * 16 + c;
-      float hn = 0.f;
-      if (valid) {
-        hn = pre0[i] + val;
-        a.h[(size_t)tok * a.N + n] = hn;
-        Act<AT>::st((XT*)a.hb, act_idx(tok, n, a.M_pad / 16), hn * pre1[i]);
-      }
-      float sq = hn * hn;
-      sq += __shfl_xor(sq, 1, 16);
-      sq += __shfl_xor(sq, 2, 16);
-      sq += __shfl_xor(sq, 4, 16);
-      sq += __shfl_xor(sq, 8, 16);
-      if (c == 0) a.ssp_out[tile * a.M_pad + tok] = sq;
-    } else if constexpr (EPI == EPI_GEGLU) {
-      float up = res[e + 1024] * inv_rms[tl];
-      if constexpr (WT == WT_FP8) up *= psc[(i + 2) & (2 * NT - 1)];  // the up tile of this gate element
-      const int f = (int)(tile / 2) * 16 + c;
-      if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
-    } else {  // EPI_OUT: bias and x were loaded at the start (pre0, pre1)
-      const int n = (int)tile * 16 + c;
-      if (valid && n < a.A) {
-        const float v = val + pre0[i];
-        a.xio[(size_t)tok * a.A + n] = a.dt > 0.f ? pre1[i] + a.dt * v : v;
-      }
-    }
+  } else if (group(blockIdx.z, 0)) {
+    return;
   }
   prefetch_done(pf_acc);
 #ifdef AE_TRACE
@@ -723,9 +745,9 @@ template <> struct RoleTraits<R_DOWN> { static constexpr int EPI = EPI_RESID, NT
 template <> struct RoleTraits<R_OUT_PROJ> { static constexpr int EPI = EPI_OUT, NT = 1; };
 
 #define AE_GEMM_ENTRY(NAME, ROLE)                                                                         \
-  template <int WT, int AT, int KPW>                                                                      \
+  template <int WT, int AT, int KPW, bool LOOP>                                                           \
   __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void NAME(GemmArgs a) {   \
-    gemm_body<WT, AT, RoleTraits<ROLE>::EPI, RoleTraits<ROLE>::NT, KPW>(a);                              \
+    gemm_body<WT, AT, RoleTraits<ROLE>::EPI, RoleTraits<ROLE>::NT, KPW, LOOP>(a);                        \
   }
 AE_GEMM_ENTRY(qkv_rope_kernel, R_QKV_ROPE)
 AE_GEMM_ENTRY(o_proj_resid_kernel, R_O_PROJ)
@@ -734,13 +756,13 @@ AE_GEMM_ENTRY(down_resid_kernel, R_DOWN)
 AE_GEMM_ENTRY(out_proj_euler_kernel, R_OUT_PROJ)
 #undef AE_GEMM_ENTRY
 
-template <int ROLE, int WT, int AT, int KPW>
+template <int ROLE, int WT, int AT, int KPW, bool LOOP>
 constexpr void (*gemm_entry())(GemmArgs) {
-  if constexpr (ROLE == R_QKV_ROPE) return qkv_rope_kernel<WT, AT, KPW>;
-  else if constexpr (ROLE == R_O_PROJ) return o_proj_resid_kernel<WT, AT, KPW>;
-  else if constexpr (ROLE == R_GATE_UP) return gate_up_geglu_kernel<WT, AT, KPW>;
-  else if constexpr (ROLE == R_DOWN) return down_resid_kernel<WT, AT, KPW>;
-  else return out_proj_euler_kernel<WT, AT, KPW>;
+  if constexpr (ROLE == R_QKV_ROPE) return qkv_rope_kernel<WT, AT, KPW, LOOP>;
+  else if constexpr (ROLE == R_O_PROJ) return o_proj_resid_kernel<WT, AT, KPW, LOOP>;
+  else if constexpr (ROLE == R_GATE_UP) return gate_up_geglu_kernel<WT, AT, KPW, LOOP>;
+  else if constexpr (ROLE == R_DOWN) return down_resid_kernel<WT, AT, KPW, LOOP>;
+  else return out_proj_euler_kernel<WT, AT, KPW, LOOP>;
 }
 
 // ------------------------------------------------------------------ attention

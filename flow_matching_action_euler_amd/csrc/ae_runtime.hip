@@ -245,7 +245,9 @@ template <int WT, int AT, int ROLE, int KPW>
 hipError_t launch_gemm_k(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
   if (!a.pf.dummy) a.pf.dummy = (const char*)a.w;  // unused prefetch slots reread the kernel's own weights
   constexpr size_t lds = gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>();
-  AE_LAUNCH((gemm_entry<ROLE, WT, AT, KPW>()), dim3(n_groups, a.S, n_z), dim3(GTHREADS), lds, st, a);
+  const dim3 grid(n_groups, a.S, (a.n_zt + a.zpw - 1) / a.zpw);
+  if (a.zpw > 1) AE_LAUNCH((gemm_entry<ROLE, WT, AT, KPW, true>()), grid, dim3(GTHREADS), lds, st, a);
+  else AE_LAUNCH((gemm_entry<ROLE, WT, AT, KPW, false>()), grid, dim3(GTHREADS), lds, st, a);
   return hipGetLastError();
 }
 
@@ -263,8 +265,11 @@ hipError_t launch_gemm(GemmArgs a, int n_groups, int n_z, hipStream_t st) {
 
 template <int WT, int AT, int ROLE, int KPW>
 hipError_t set_gemm_attr_k() {
-  return hipFuncSetAttribute((const void*)gemm_entry<ROLE, WT, AT, KPW>(), hipFuncAttributeMaxDynamicSharedMemorySize,
-                             (int)gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>());
+  const int lds = (int)gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>();
+  hipError_t e = hipFuncSetAttribute((const void*)gemm_entry<ROLE, WT, AT, KPW, false>(),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute((const void*)gemm_entry<ROLE, WT, AT, KPW, true>(), hipFuncAttributeMaxDynamicSharedMemorySize, lds);
 }
 template <int WT, int AT, int ROLE>
 hipError_t set_gemm_attr() {
@@ -356,6 +361,16 @@ AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 
+// Whether a GEMM workgroup loops over several 64-token groups (M > 64) with its weights in
+// registers instead of one workgroup per group; AE_TOKEN_LOOP=0 turns it off.
+bool tokens_per_wg_loop() {
+  static bool on = [] {
+    const char* e = getenv("AE_TOKEN_LOOP");
+    return !e || atoi(e) != 0;
+  }();
+  return on;
+}
+
 // Steps of ~0.2 us that a split-K consumer sleeps before its first poll, so that the poll
 // finds the other splits' partials landed instead of costing a second round trip (measured
 // for Pi0: 1 step saves 0.16 ms per chunk, 2-6 steps less); AE_POLL_DELAY overrides it.
@@ -370,6 +385,14 @@ int poll_delay() {
 struct Dispatch {
   // one launcher per role bound to the handle's dtypes (fp8 weights: MLP roles only)
   static hipError_t gemm(ae_handle* h, int role, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
+    // token groups per workgroup: enough that the launch fits one round of compute units
+    // (each workgroup then loads its weights once for all its groups); split-K: one group
+    a.n_zt = n_z;
+    a.zpw = 1;
+    if (a.S == 1 && n_z > 1 && h->n_cu > 0 && tokens_per_wg_loop()) {
+      const int gz = std::max(1, std::min(n_z, h->n_cu / std::max(n_groups, 1)));
+      a.zpw = (n_z + gz - 1) / gz;
+    }
     a.exch_poll = h->poll_splitk && (long long)n_groups * a.S * n_z <= h->n_cu;  // one workgroup per CU fits them all
     a.poll_delay = poll_delay();
     a.err = h->err_flag;

@@ -127,7 +127,8 @@ typedef struct ae_handle ae_handle;
  * Read here from the environment: AE_ATTN_CORESIDENT=0 (attention key splits
  * merge in a separate launch instead of inside the attention launch) and
  * AE_EXCH_POLL=0 (split-K partials meet through arrival tickets instead of being
- * polled); both in-kernel exchanges assume every workgroup of the launch is
+ * polled); AE_TOKEN_LOOP=0 (one GEMM workgroup per 64-token group instead of
+ * workgroups that loop over several groups with their weights held); both in-kernel exchanges assume every workgroup of the launch is
  * resident at once, which holds on an otherwise idle device. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 
