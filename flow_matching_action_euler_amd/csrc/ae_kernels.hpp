@@ -121,6 +121,13 @@ __device__ __forceinline__ float gelu_tanh(float x) {
   float u = k0 * (x + 0.044715f * x * x * x);
   return 0.5f * x * (1.0f + tanhf(u));
 }
+// The same function through 0.5 (1 + tanh u) = 1 / (1 + exp(-2u)): one exp2 and one reciprocal
+// (relative error ~1e-6, far inside the bf16 rounding of its output)
+__device__ __forceinline__ float gelu_tanh_fast(float x) {
+  const float k2 = -2.f * 0.7978845608028654f * 1.4426950408889634f;  // -2 sqrt(2/pi) log2(e)
+  const float e = __builtin_amdgcn_exp2f(k2 * (x + 0.044715f * x * x * x));
+  return x * __builtin_amdgcn_rcpf(1.f + e);
+}
 
 // ------------------------------------------------------------------ L2 prefetch of the next kernel's operands
 //
@@ -230,6 +237,7 @@ struct GemmArgs {
   float dt;              // > 0: x += dt * v; 0: store v
   int trace_id;          // kernel kind for the optional phase trace
   Prefetch pf;           // next kernel's operands to place in L2 (QKV and gate/up launches only)
+  int tn_blocks, tm_blocks;  // token-tiled launches: channel and token panels of the output
 };
 
 constexpr int GW = 8;         // waves per GEMM workgroup
@@ -763,6 +771,315 @@ constexpr void (*gemm_entry())(GemmArgs) {
   else if constexpr (ROLE == R_GATE_UP) return gate_up_geglu_kernel<WT, AT, KPW, LOOP>;
   else if constexpr (ROLE == R_DOWN) return down_resid_kernel<WT, AT, KPW, LOOP>;
   else return out_proj_euler_kernel<WT, AT, KPW, LOOP>;
+}
+
+// ------------------------------------------------------------------ GEMM, many tokens
+
+// For a few hundred tokens and more (verification passes, batched robots) a workgroup owns an
+// output tile of TN = 64*WN channels x TM = 64*WM tokens, so that each operand byte it brings in
+// feeds TM (weights) or TN (activations) outputs; the kernel above re-reads every activation in
+// each 16- or 32-channel group. The 8 waves are WN x WM x WK: wave (wn, wm, wk) accumulates the
+// 64 x 64 sub-tile (wn, wm) (4 x 4 MFMA tiles) over the k-blocks of each chunk that belong to its
+// k-group wk; with WK > 1 the partial sub-tiles meet in LDS and each wave finishes 1/WK of the
+// tiles. Operands are staged in LDS as whole 1 KB fragments in the packed order (lane-major, so
+// fragment reads are conflict-free), double-buffered: the next chunk's global loads are in flight
+// in registers while the MFMAs consume the current chunk. bf16 weights and activations.
+template <int WN, int WM, int WK>
+struct TileCfg {
+  static_assert(WN * WM * WK == GW, "8 waves");
+  static constexpr int NT = 4 * WN, MT = 4 * WM;                   // 16-channel, 16-token tiles
+  static constexpr int KPT = 64 / ((NT + MT) * WK) >= 2 ? 2 : 1;  // k-blocks per wave per chunk
+  static constexpr int CK = WK * KPT;                              // k-blocks per chunk
+  static constexpr int NA = NT * CK, NB = MT * CK;                 // fragments per chunk
+  static constexpr int LOADS = (NA + NB) / GW;                     // 16-byte loads per thread
+  static constexpr size_t CHUNK = (size_t)(NA + NB) * 1024;
+  // operand double buffer; with WK > 1 it then holds the 8 waves' partial sub-tiles (16 KB each)
+  static constexpr size_t STAGE = WK > 1 && 2 * CHUNK < (size_t)GW * 16384 ? (size_t)GW * 16384 : 2 * CHUNK;
+  static constexpr int GPT = GTHREADS / (MT * 16);                 // RMS partial groups per token
+  static constexpr int NRD = 64 / GPT;                             // RMS partial loads per thread
+  static constexpr size_t LDS = STAGE + (size_t)MT * 16 * 4 + GTHREADS * 4;
+  static_assert(NA % GW == 0 && NB % GW == 0 && 2 * CHUNK <= 128 * 1024, "chunk shape");
+};
+constexpr int TILED_MAX_GIN = 64;  // RMS partial groups the prologue reads (width <= 1024)
+
+template <int EPI, int WN, int WM, int WK>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_tiled_kernel(GemmArgs a) {
+  typedef TileCfg<WN, WM, WK> C;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  char* stage = (char*)smem;                                  // [2][CHUNK] operands; then partials
+  float* inv_rms = (float*)(stage + C::STAGE);                // [TM]
+  float* ssq = inv_rms + C::MT * 16;                          // [512]
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // wave: scalar
+  const int wk = wave % WK, wn = (wave / WK) % WN, wm = wave / (WK * WN);
+  const int KB = a.K / KBLK, ntt = a.M_pad / 16;
+
+  // workgroup i runs on XCD i % 8: each XCD takes a contiguous run of output tiles in
+  // channel-major order, so the workgroups that share a weight panel share one L2
+  const int T = a.tn_blocks * a.tm_blocks;
+  const int xcd = blockIdx.x & 7;
+  const int item = xcd * (T >> 3) + min(xcd, T & 7) + (int)(blockIdx.x >> 3);
+  const int nb = item / a.tm_blocks, mb = item % a.tm_blocks;
+  const int ct0 = nb * C::NT, tt0 = mb * C::MT;  // first 16-channel tile, first 16-token tile
+
+  // fragment f of chunk c: weights [ct][kk] for f < NA, then activations [kk][tt]; the token
+  // tiles past the buffer's rows read its last tile (their outputs are never stored)
+  const i32x4* wsrc = (const i32x4*)a.w;
+  const i32x4* xsrc = (const i32x4*)a.x;
+  // three chunks in flight in registers (a vector type: arrays of HIP's uint4 structs stayed in
+  // scratch memory); load i of a thread is fragment wave + 8 i, weights for i < NA / 8
+  i32x4 r0[C::LOADS], r1[C::LOADS], r2[C::LOADS];
+  auto gload = [&](i32x4 (&r)[C::LOADS], int c) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::NA / GW; ++i) {
+      const int f = wave + GW * i;
+      r[i] = wsrc[((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane];
+    }
+#pragma unroll
+    for (int i = C::NA / GW; i < C::LOADS; ++i) {
+      const int f = wave + GW * i - C::NA;
+      r[i] = xsrc[((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane];
+    }
+  };
+  auto lstore = [&](const i32x4 (&r)[C::LOADS], int b) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < C::LOADS; ++i)
+      *(i32x4*)(stage + b * C::CHUNK + (size_t)(wave + GW * i) * 1024 + lane * 16) = r[i];
+  };
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // every fragment of the chunk is read before the first MFMA (LDS returns in order, so the
+  // MFMAs of k-block 0 wait only for their own fragments)
+  auto compute = [&](int b) __attribute__((always_inline)) {
+    const char* buf = stage + b * C::CHUNK + lane * 16;
+    bf16x8 af[C::KPT][4], bfr[C::KPT][4];
+#pragma unroll
+    for (int kp = 0; kp < C::KPT; ++kp) {
+      const int kk = wk * C::KPT + kp;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[kp][i] = *(const bf16x8*)(buf + (size_t)((wn * 4 + i) * C::CK + kk) * 1024);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[kp][j] = *(const bf16x8*)(buf + (size_t)(C::NA + kk * C::MT + wm * 4 + j) * 1024);
+    }
+#pragma unroll
+    for (int kp = 0; kp < C::KPT; ++kp)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kp][i], bfr[kp][j], acc[i][j], 0, 0, 0);
+  };
+
+  const int nc = KB / C::CK;
+  gload(r0, 0);
+  gload(r1, min(1, nc - 1));
+  gload(r2, min(2, nc - 1));
+  // 1/rms of this tile's tokens from the producer's partial sums of h^2 (QKV, gate/up):
+  // thread -> token t % TM, partial groups t / TM + GPT * q; clamped loads, masked sums
+  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
+    const int tl = threadIdx.x % (C::MT * 16), g0 = threadIdx.x / (C::MT * 16);
+    const float* sp = a.ssp_in + min(tt0 * 16 + tl, a.M_pad - 1);
+    float sv[C::NRD];
+#pragma unroll
+    for (int q = 0; q < C::NRD; ++q) sv[q] = sp[(size_t)min(g0 + C::GPT * q, a.g_in - 1) * a.M_pad];
+    float sum = 0.f;
+#pragma unroll
+    for (int q = 0; q < C::NRD; ++q) sum += g0 + C::GPT * q < a.g_in ? sv[q] : 0.f;
+    ssq[threadIdx.x] = sum;
+  }
+  lstore(r0, 0);
+  __syncthreads();
+  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
+    if (threadIdx.x < C::MT * 16) {
+      float t = 0.f;
+#pragma unroll
+      for (int q = 0; q < C::GPT; ++q) t += ssq[q * C::MT * 16 + threadIdx.x];
+      inv_rms[threadIdx.x] = rsqrtf(t * a.inv_width + a.eps);
+    }
+  }
+  // chunk c: LDS buffer c % 2 holds it, registers hold chunks c + 1 and c + 2 and take c + 3 into
+  // the set chunk c came from; then chunk c + 1 moves to the other LDS buffer. Every step issues
+  // the same loads and stores (chunk indices clamped; steps past the end skip only the MFMAs, and
+  // what they store lands in a buffer nobody reads again): the compiler then sees the same loads
+  // in flight on every path and waits only for the set it stores (a conditional load made it
+  // wait for all of them).
+  auto step = [&](int c, i32x4 (&rf)[C::LOADS], const i32x4 (&rn)[C::LOADS]) __attribute__((always_inline)) {
+    gload(rf, min(c + 3, nc - 1));
+    __builtin_amdgcn_sched_barrier(0);  // the loads in flight before the MFMAs
+    if (c < nc) compute(c & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    lstore(rn, (c + 1) & 1);
+    __syncthreads();
+  };
+  for (int c = 0; c < nc; c += 3) {
+    step(c, r0, r1);
+    step(c + 1, r1, r2);
+    step(c + 2, r2, r0);
+  }
+
+  // partial sub-tiles of the WK k-groups meet in LDS: [wave][tile q = 4 i + j][lane][4]
+  if constexpr (WK > 1) {
+    __syncthreads();  // every wave is done reading the operand stage
+    float* red = (float*)stage;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) *(f32x4*)(red + (((size_t)wave * 16 + i * 4 + j) * 64 + lane) * 4) = acc[i][j];
+    __syncthreads();
+  }
+  // the sum of tile (i, j) of this wave's sub-tile over the k-groups, in k-group order
+  auto tile_sum = [&](int i, int j) __attribute__((always_inline)) -> f32x4 {
+    if constexpr (WK == 1) {
+      return acc[i][j];
+    } else {
+      const float* red = (const float*)stage;
+      f32x4 v = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int g = 0; g < WK; ++g) {
+        const int w = (wm * WN + wn) * WK + g;
+        v += *(const f32x4*)(red + (((size_t)w * 16 + i * 4 + j) * 64 + lane) * 4);
+      }
+      return v;
+    }
+  };
+
+  // ---------------- epilogues: lane -> token tt*16 + lane % 16, channels 4 (lane / 16) + v of a tile
+  const int cq = lane >> 4, tq = lane & 15;
+  if constexpr (EPI == EPI_GEGLU) {
+    // gate tile 2p and up tile 2p + 1 hold the same 16 outputs f
+#pragma unroll
+    for (int u = 0; u < 8 / WK; ++u) {
+      const int pq = wk + WK * u, p = pq >> 2, j = pq & 3;
+      const f32x4 gv = tile_sum(2 * p, j), uv = tile_sum(2 * p + 1, j);
+      const int tl = (wm * 4 + j) * 16 + tq, tok = tt0 * 16 + tl;
+      const float ir = inv_rms[tl];
+      const int f = ((ct0 + wn * 4) / 2 + p) * 16 + cq * 4;
+      if (tok < a.M) {
+        uint2 o;
+        o.x = (uint32_t)f32_to_bf16(gelu_tanh_fast(gv[0] * ir) * (uv[0] * ir)) |
+              ((uint32_t)f32_to_bf16(gelu_tanh_fast(gv[1] * ir) * (uv[1] * ir)) << 16);
+        o.y = (uint32_t)f32_to_bf16(gelu_tanh_fast(gv[2] * ir) * (uv[2] * ir)) |
+              ((uint32_t)f32_to_bf16(gelu_tanh_fast(gv[3] * ir) * (uv[3] * ir)) << 16);
+        *(uint2*)((uint16_t*)a.u_out + act_idx(tok, f, ntt)) = o;
+      }
+    }
+  } else if constexpr (EPI == EPI_RESID) {
+    // groups of up to 8 tiles: their residual rows are loaded before any is stored
+    constexpr int PER = 16 / WK, GRP = PER < 8 ? PER : 8;
+#pragma unroll
+    for (int u0 = 0; u0 < PER; u0 += GRP) {
+      float4 hv[GRP], gv[GRP];
+      f32x4 val[GRP];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = wk + WK * (u0 + u), i = q >> 2, j = q & 3;
+        const int tok = tt0 * 16 + (wm * 4 + j) * 16 + tq;
+        const int n = (ct0 + wn * 4 + i) * 16 + cq * 4;
+        hv[u] = *(const float4*)(a.h + (size_t)min(tok, a.M - 1) * a.N + n);
+        gv[u] = *(const float4*)(a.gain_next + n);
+        val[u] = tile_sum(i, j);
+      }
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = wk + WK * (u0 + u), i = q >> 2, j = q & 3;
+        const int tok = tt0 * 16 + (wm * 4 + j) * 16 + tq;
+        const int tile = ct0 + wn * 4 + i, n = tile * 16 + cq * 4;
+        const bool valid = tok < a.M;
+        float4 hn = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (valid) {
+          hn = make_float4(hv[u].x + val[u][0], hv[u].y + val[u][1], hv[u].z + val[u][2], hv[u].w + val[u][3]);
+          *(float4*)(a.h + (size_t)tok * a.N + n) = hn;
+          uint2 o;
+          o.x = (uint32_t)f32_to_bf16(hn.x * gv[u].x) | ((uint32_t)f32_to_bf16(hn.y * gv[u].y) << 16);
+          o.y = (uint32_t)f32_to_bf16(hn.z * gv[u].z) | ((uint32_t)f32_to_bf16(hn.w * gv[u].w) << 16);
+          *(uint2*)((uint16_t*)a.hb + act_idx(tok, n, ntt)) = o;
+        }
+        float sq = hn.x * hn.x + hn.y * hn.y + hn.z * hn.z + hn.w * hn.w;
+        sq += __shfl_xor(sq, 16);
+        sq += __shfl_xor(sq, 32);
+        if (cq == 0 && tok < a.M_pad) a.ssp_out[(size_t)tile * a.M_pad + tok] = sq;
+      }
+    }
+  } else {  // EPI_QKV
+    const int tph = a.dh / 16, half = a.dh / 2, nkb = a.dh / KBLK;
+    const int q_tiles = a.n_q * tph, k_tiles = a.n_kv * tph, gq = a.n_q / a.n_kv;
+    // this lane's 4 tokens (one per token tile j): sequence and chunk row, divided once
+    int sqj[4], tj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = min(tt0 * 16 + (wm * 4 + j) * 16 + tq, a.M - 1);
+      sqj[j] = tok / a.H;
+      tj[j] = tok - sqj[j] * a.H;
+    }
+    constexpr int PER = 16 / WK, GRP = PER < 4 ? PER : 4;
+#pragma unroll
+    for (int u0 = 0; u0 < PER; u0 += GRP) {
+      // (cos, sin) of the 4 head dims this lane rotates, for each tile of the group
+      float4 cs[GRP][2];
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = wk + WK * (u0 + u), i = q >> 2, j = q & 3;
+        const int tin = ct0 + wn * 4 + i, pair = (tin < q_tiles ? tin : tin - q_tiles) % tph;  // wave-uniform
+        const float4* cp = (const float4*)(a.rope_cs + ((size_t)tj[j] * half + pair * 8 + 4 * (cq & 1)) * 2);
+        cs[u][0] = cp[0];
+        cs[u][1] = cp[1];
+      }
+#pragma unroll
+      for (int u = 0; u < GRP; ++u) {
+        const int q = wk + WK * (u0 + u), i = q >> 2, j = q & 3;
+        const int tl = (wm * 4 + j) * 16 + tq, tok = tt0 * 16 + tl;
+        const int tin = ct0 + wn * 4 + i;  // wave-uniform
+        const float ir = inv_rms[tl];
+        const f32x4 v = tile_sum(i, j);
+        float x[4], xp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = v[e] * ir;
+          xp[e] = __shfl_xor(x[e], 32);  // channel c +- 8: the other half of the rotation pair
+        }
+        const bool valid = tok < a.M;
+        const int sq = sqj[j], t = tj[j];
+        if (tin < q_tiles + k_tiles) {
+          const bool is_q = tin < q_tiles;
+          const int tt2 = is_q ? tin : tin - q_tiles, head = tt2 / tph, pair = tt2 - head * tph;
+          const int hf = cq >> 1;
+          const float c4[4] = {cs[u][0].x, cs[u][0].z, cs[u][1].x, cs[u][1].z};
+          const float s4[4] = {cs[u][0].y, cs[u][0].w, cs[u][1].y, cs[u][1].w};
+          float out[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            out[e] = hf ? xp[e] * s4[e] + x[e] * c4[e] : x[e] * c4[e] - xp[e] * s4[e];
+          const int dfull = hf * half + pair * 8;
+          const int lgrp = ((dfull % KBLK) >> 3) << 4, kb = dfull / KBLK;
+          size_t off;
+          if (is_q) {
+            const int gg = head / gq, rr = (head - gg * gq) * a.H + t;
+            off = ((((size_t)sq * a.n_kv + gg) * a.n_qt + (rr >> 4)) * nkb + kb) * 512 + (lgrp + (rr & 15)) * 8;
+          } else {
+            const int kk = t & 31, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+            off = (((((size_t)sq * a.n_kv + head) * a.nbs + (t >> 5)) * 2 + kt) * nkb + kb) * 512 + (lgrp + m) * 8;
+          }
+          if (valid) {
+            uint2 o;
+            o.x = (uint32_t)f32_to_bf16(out[0]) | ((uint32_t)f32_to_bf16(out[1]) << 16);
+            o.y = (uint32_t)f32_to_bf16(out[2]) | ((uint32_t)f32_to_bf16(out[3]) << 16);
+            *(uint2*)((uint16_t*)(is_q ? a.q_out : a.k_out) + off + 4 * (cq & 1)) = o;
+          }
+        } else if (valid) {
+          // value A fragments (of V^T) of key block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e;
+          // this tile is head dims (tv % tph)*16 .. +16 of kv head tv / tph
+          const int tv = tin - q_tiles - k_tiles, hd = tv / tph, d16 = tv - hd * tph;
+          const int kk = t & 31;
+          const size_t fr = (((size_t)sq * a.n_kv + hd) * a.nbs + (t >> 5)) * (a.dh / 16) + d16;
+          uint16_t* vp = (uint16_t*)a.v_out + fr * 512 + (((kk >> 3) << 4) + cq * 4) * 8 + (kk & 7);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) vp[e * 8] = f32_to_bf16(x[e]);
+        }
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------ attention

@@ -119,6 +119,8 @@ struct ae_handle {
   // in-kernel partial exchanges (read from AE_ATTN_CORESIDENT / AE_EXCH_POLL at creation, 0 = off):
   // attention key splits merged by co-resident workgroups, split-K partials polled by split S-1
   bool coresident_attn = true, poll_splitk = true;
+  int tiled_roles = 0xf;  // GEMM roles (bit per Role) that may take the token-tiled kernel
+  int tiled_force = -1;   // token-tiled shape forced for every GEMM it fits (tests)
   float* rope_cs = nullptr;
   void *kcache = nullptr, *vcache = nullptr;
   size_t slot_elems = 0;     // elements of one slot's packed K (and V) cache
@@ -279,6 +281,52 @@ hipError_t set_gemm_attr() {
   if (e == hipSuccess) e = set_gemm_attr_k<WT, AT, ROLE, 1>();
   return e;
 }
+// Token-tiled GEMM shapes (WN, WM, WK): output tile 64 WN channels x 64 WM tokens, WK k-groups.
+constexpr int N_TILED = 4;
+template <int SH> struct TiledShape;
+template <> struct TiledShape<0> { typedef TileCfg<4, 2, 1> C; };
+template <> struct TiledShape<1> { typedef TileCfg<2, 2, 2> C; };
+template <> struct TiledShape<2> { typedef TileCfg<2, 1, 4> C; };
+template <> struct TiledShape<3> { typedef TileCfg<1, 1, 8> C; };
+constexpr int tiled_nt(int sh) { return sh == 0 ? 16 : sh == 3 ? 4 : 8; }  // 16-channel tiles
+constexpr int tiled_mt(int sh) { return sh == 0 || sh == 1 ? 8 : 4; }      // 16-token tiles
+constexpr int tiled_ck(int sh) {
+  return sh == 0 ? TiledShape<0>::C::CK : sh == 1 ? TiledShape<1>::C::CK : sh == 2 ? TiledShape<2>::C::CK : TiledShape<3>::C::CK;
+}
+static_assert(tiled_nt(0) == TiledShape<0>::C::NT && tiled_mt(0) == TiledShape<0>::C::MT, "shape 0");
+static_assert(tiled_nt(1) == TiledShape<1>::C::NT && tiled_mt(1) == TiledShape<1>::C::MT, "shape 1");
+static_assert(tiled_nt(2) == TiledShape<2>::C::NT && tiled_mt(2) == TiledShape<2>::C::MT, "shape 2");
+static_assert(tiled_nt(3) == TiledShape<3>::C::NT && tiled_mt(3) == TiledShape<3>::C::MT, "shape 3");
+
+template <int EPI, int WN, int WM, int WK>
+hipError_t launch_tiled_k(const GemmArgs& a, hipStream_t st, bool set_attr) {
+  typedef TileCfg<WN, WM, WK> C;
+  if (set_attr)
+    return hipFuncSetAttribute((const void*)gemm_tiled_kernel<EPI, WN, WM, WK>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)C::LDS);
+  AE_LAUNCH((gemm_tiled_kernel<EPI, WN, WM, WK>), dim3(a.tn_blocks * a.tm_blocks), dim3(GTHREADS), C::LDS, st, a);
+  return hipGetLastError();
+}
+template <int EPI>
+hipError_t launch_tiled(int shape, const GemmArgs& a, hipStream_t st, bool set_attr) {
+  switch (shape) {
+    case 0: return launch_tiled_k<EPI, 4, 2, 1>(a, st, set_attr);
+    case 1: return launch_tiled_k<EPI, 2, 2, 2>(a, st, set_attr);
+    case 2: return launch_tiled_k<EPI, 2, 1, 4>(a, st, set_attr);
+    default: return launch_tiled_k<EPI, 1, 1, 8>(a, st, set_attr);
+  }
+}
+hipError_t set_tiled_attrs() {
+  hipError_t e = hipSuccess;
+  for (int sh = 0; sh < N_TILED && e == hipSuccess; ++sh) {
+    GemmArgs a{};
+    e = launch_tiled<EPI_QKV>(sh, a, nullptr, true);
+    if (e == hipSuccess) e = launch_tiled<EPI_RESID>(sh, a, nullptr, true);
+    if (e == hipSuccess) e = launch_tiled<EPI_GEGLU>(sh, a, nullptr, true);
+  }
+  return e;
+}
+
 hipError_t set_all_gemm_attrs() {
   hipError_t e = hipSuccess;
   auto acc = [&](hipError_t r) { if (e == hipSuccess) e = r; };
@@ -289,6 +337,7 @@ hipError_t set_all_gemm_attrs() {
   acc(set_gemm_attr<WT_BF16, AT_BF16, R_GATE_UP>()); acc(set_gemm_attr<WT_BF16, AT_BF16, R_DOWN>());
   acc(set_gemm_attr<WT_BF16, AT_BF16, R_OUT_PROJ>());
   acc(set_gemm_attr<WT_FP8, AT_BF16, R_GATE_UP>()); acc(set_gemm_attr<WT_FP8, AT_BF16, R_DOWN>());
+  acc(set_tiled_attrs());
   return e;
 }
 
@@ -382,11 +431,54 @@ int poll_delay() {
   return n;
 }
 
+// Token-tiled shape for a GEMM role over n_tiles 16-channel tiles, K inputs and M tokens, or
+// -1 for the kernel above: one token group, fp32 or fp8 operands, an RMS input wider than the
+// tiled prologue reads, no shape dividing the tiles and k-blocks, or the role switched off
+// (AE_TILED, a bit per role; AE_TILED_SHAPE forces one shape wherever it fits). Among the
+// shapes that fit, the one with the least modelled time:
+// rounds of workgroups over the compute units x (the larger of its MFMA clocks and its operand
+// bytes at 64 B per clock per compute unit, + ~2 us per round). A shape whose launch would fill
+// under half the compute units is not taken (measured: slower than the kernel above there).
+int tiled_shape(const ae_handle* h, int role, int n_tiles, int K, int M, int Mp, int* tn_blocks, int* tm_blocks) {
+  if (role == R_OUT_PROJ || !((h->tiled_roles >> role) & 1) || Mp / TOKG < 2 || h->n_cu <= 0) return -1;
+  if (h->at != AT_BF16 || ((role == R_GATE_UP || role == R_DOWN) ? h->mt : h->wt) != WT_BF16) return -1;
+  if ((role == R_QKV_ROPE || role == R_GATE_UP) && h->c.width / 16 > TILED_MAX_GIN) return -1;
+  const int tok_tiles = (M + 15) / 16;
+  int best = -1;
+  double best_cost = 0;
+  for (int sh = 0; sh < N_TILED; ++sh) {
+    if (h->tiled_force >= 0 && sh != h->tiled_force) continue;
+    const int nt = tiled_nt(sh), mt = tiled_mt(sh);
+    if (n_tiles % nt || (K / KBLK) % tiled_ck(sh)) continue;
+    const int nb = n_tiles / nt, mb = (tok_tiles + mt - 1) / mt;
+    if (h->tiled_force < 0 && 2 * nb * mb < h->n_cu) continue;  // under half the compute units: the kernel above wins
+    const double mfma = (double)nt * 16 * mt * 16 * K * 2 / 4096, bytes = (double)(nt + mt) * 16 * K * 2 / 64;
+    const double cost = (double)((nb * mb + h->n_cu - 1) / h->n_cu) * (std::max(mfma, bytes) + 5000);
+    if (best < 0 || cost < best_cost) { best = sh; best_cost = cost; *tn_blocks = nb; *tm_blocks = mb; }
+  }
+  return best;
+}
+bool uses_tiled(const ae_handle* h, int role, int n_tiles, int K, int M, int Mp) {
+  int tn, tm;
+  return tiled_shape(h, role, n_tiles, K, M, Mp, &tn, &tm) >= 0;
+}
+
 struct Dispatch {
   // one launcher per role bound to the handle's dtypes (fp8 weights: MLP roles only)
   static hipError_t gemm(ae_handle* h, int role, GemmArgs a, int n_groups, int n_z, hipStream_t st) {
     // token groups per workgroup: enough that the launch fits one round of compute units
     // (each workgroup then loads its weights once for all its groups); split-K: one group
+    if (a.S == 1) {
+      const int nt = role == R_GATE_UP ? 2 : 1;
+      const int sh = tiled_shape(h, role, n_groups * nt, a.K, a.M, a.M_pad, &a.tn_blocks, &a.tm_blocks);
+      if (sh >= 0) {
+        switch (role) {
+          case R_QKV_ROPE: return launch_tiled<EPI_QKV>(sh, a, st, false);
+          case R_GATE_UP: return launch_tiled<EPI_GEGLU>(sh, a, st, false);
+          default: return launch_tiled<EPI_RESID>(sh, a, st, false);
+        }
+      }
+    }
     a.n_zt = n_z;
     a.zpw = 1;
     if (a.S == 1 && n_z > 1 && h->n_cu > 0 && tokens_per_wg_loop()) {
@@ -538,7 +630,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->o_p[l]; a.x = h->o; a.ssp_in = nullptr; a.K = nq * dh;
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
-      if (prefetch_mask() & 8) {  // gate/up's weights, tiled as gate/up is launched below
+      if ((prefetch_mask() & 8) && !uses_tiled(h, R_GATE_UP, h->gu_tiles, w, M, Mp)) {  // gate/up's weights, tiled as gate/up is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->gu_p[l];
         a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, splits().gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
@@ -553,7 +645,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb;
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
-      if (prefetch_mask() & 2) {  // down's weights, tiled as down is launched below
+      if ((prefetch_mask() & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
         a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, splits().down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
@@ -569,7 +661,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.S = pick(F / 32, splits().down, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
       a.ssp_out = h->ssp_a; a.N = w;
-      if ((prefetch_mask() & 16) && l + 1 < c.n_layers) {  // the next layer's QKV weights
+      if ((prefetch_mask() & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
         a.pf.kind = 2; a.pf.base = (const char*)h->qkv_p[l + 1];
         a.pf.next_groups = h->qkv_tiles; a.pf.next_S = pick(w / 32, splits().qkv, n_z).S; a.pf.NT = 1; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->wt == WT_F32 ? 2048 : 1024;
@@ -703,6 +795,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   if (hipDeviceGetAttribute(&h->n_cu, hipDeviceAttributeMultiprocessorCount, h->dev) != hipSuccess) h->n_cu = 0;
   if (const char* e = getenv("AE_ATTN_CORESIDENT")) h->coresident_attn = atoi(e) != 0;
   if (const char* e = getenv("AE_EXCH_POLL")) h->poll_splitk = atoi(e) != 0;
+  if (const char* e = getenv("AE_TILED")) h->tiled_roles = (int)strtol(e, nullptr, 0);
+  if (const char* e = getenv("AE_TILED_SHAPE")) h->tiled_force = atoi(e);
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
   hipEventCreate(&h->ev0);
   hipEventCreate(&h->ev1);

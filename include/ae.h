@@ -128,7 +128,10 @@ typedef struct ae_handle ae_handle;
  * merge in a separate launch instead of inside the attention launch) and
  * AE_EXCH_POLL=0 (split-K partials meet through arrival tickets instead of being
  * polled); AE_TOKEN_LOOP=0 (one GEMM workgroup per 64-token group instead of
- * workgroups that loop over several groups with their weights held); both in-kernel exchanges assume every workgroup of the launch is
+ * workgroups that loop over several groups with their weights held); AE_TILED=<mask>
+ * (GEMM roles, bit 0 qkv, 1 o_proj, 2 gate/up, 3 down, that may take the token-tiled
+ * kernel when a pass has 128 or more tokens; default 0xf) and AE_TILED_SHAPE=0..3 (force
+ * one tiled shape wherever it fits); both in-kernel exchanges assume every workgroup of the launch is
  * resident at once, which holds on an otherwise idle device. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 

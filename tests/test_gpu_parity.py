@@ -174,6 +174,47 @@ def test_error_codes():
     ex.close()
 
 
+# ------------------------------------------------------------------ token-tiled GEMMs (many tokens)
+
+# 7 robots x 20 rows = 140 tokens (3 token groups). With a shape forced (AE_TILED_SHAPE) every GEMM
+# but the output projection takes the token-tiled kernel: its 9 token tiles leave the last one
+# ragged, and 8-tile token panels reach past the 12 tiles the buffers hold (those loads are
+# clamped, their outputs dropped). The modelled choice keeps the 64-token kernel here (a tiled
+# launch would fill too few compute units), which the full-size batched and verify tests cover.
+SMALL_BF16_B7 = SMALL_BF16.with_(name="small_bf16_b7", max_batch=7)
+
+
+@pytest.mark.parametrize("shape", [None, 0, 1, 2, 3], ids=lambda s: "modelled" if s is None else f"shape{s}")
+def test_tiled_gemm_denoise_matches_oracle(shape, monkeypatch):
+    if shape is not None:
+        monkeypatch.setenv("AE_TILED_SHAPE", str(shape))
+    case = Case(SMALL_BF16_B7)
+    ex = _expert(case)
+    noise = case.noise(7)
+    got = ex.denoise(noise, 2)
+    ref = case.oracle_denoise(noise, 2)
+    err = rel_err(got, ref)
+    print(f"tiled shape={shape} rel_err={err:.3e}")
+    assert err <= tol_for(SMALL_BF16_B7), err
+    ex.close()
+
+
+def test_tiled_gemm_verify_matches_oracle(monkeypatch):
+    """8 flow times x 20 rows = 160 tokens in one verification pass (token-tiled GEMMs)."""
+    cfg = SMALL_BF16.with_(name="small_bf16_t8", max_taus=8)
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.linspace(0.1, 0.9, 8).astype(np.float32)
+    for seed in range(2):
+        draft = G.make_draft(cfg, seed)
+        noise = case.noise(1, 300 + seed)[0]
+        acc, sw, D = ex.verify(1, draft, noise, taus, 0.05)
+        acc_o, sw_o, D_o = case.oracle_verify(1, draft, noise, taus, 0.05)
+        assert (acc, sw) == (acc_o, sw_o)
+        assert rel_err(D, D_o) <= tol_for(cfg)
+    ex.close()
+
+
 # ------------------------------------------------------------------ full Pi0-scale shapes
 
 @pytest.fixture(scope="module")
