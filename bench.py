@@ -69,6 +69,17 @@ def step_bytes(cfg, batch):
     return cfg.n_layers * (per_layer + kv) + kb["in_proj"] + kb["out_proj_euler"]
 
 
+def step_flops(cfg, sequences):
+    """FLOPs of one velocity pass over `sequences` suffix sequences of H rows: 2 per weight per row
+    for every projection, plus Q.K^T and P.V of every query row over its P + H keys."""
+    w, F, dh, nq, nkv, A, H = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.action_dim, cfg.horizon
+    per_layer = (nq + 2 * nkv) * dh * w + w * nq * dh + 2 * F * w + w * F
+    rows = sequences * H
+    gemm = 2 * rows * (cfg.n_layers * per_layer + 2 * w * A)
+    attn = cfg.n_layers * sequences * 4 * nq * H * (cfg.prefix_len + H) * dh
+    return gemm + attn
+
+
 def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0):
     """The oracle as it stands, timed on this host: Euler steps of one robot until the budget is spent."""
     from oracle import ae_oracle as O
@@ -157,6 +168,8 @@ def bench_verify(args, cfg, W, kvs, ex, stream):
         "pass_ms_p90": round(float(np.percentile(pass_ms, 90)), 4),
         "pass_alg_bytes": sb,
         "pass_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "pass_flops": step_flops(cfg, n_tau),
+        "pass_mfma_frac": round(step_flops(cfg, n_tau) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
         "kernels": kernels,
@@ -308,6 +321,8 @@ def main():
         "step_alg_bytes": sb,
         "whole_chunk_GBs": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9, 1),
         "whole_chunk_hbm_frac": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "step_flops": step_flops(cfg, B),
+        "whole_chunk_mfma_frac": round(step_flops(cfg, B) * cfg.steps / (ms_per_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
                      "traffic": traffic.get(dom) if dom else None},

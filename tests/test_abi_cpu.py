@@ -119,3 +119,20 @@ def test_binding_raises_without_library(tmp_path):
             B.load_library(str(tmp_path / "missing.so"))
         finally:
             B._lib = saved
+
+
+def test_bench_work_figures_match_the_closed_forms():
+    """bench.py's algorithmic bytes and FLOPs per step, against the per-layer arithmetic of the
+    Pi0-scale shapes: 17.30 M weights per layer (qkv 2560 x 1024, o 1024 x 2048, gate/up
+    2 x 4096 x 1024, down 1024 x 4096), Q.K^T and P.V of 8 x 50 query rows over 866 keys x 256."""
+    import bench
+    per_layer = 2560 * 1024 + 1024 * 2048 + 2 * 4096 * 1024 + 1024 * 4096
+    assert per_layer == 17_301_504
+    attn = 4 * 8 * 50 * 866 * 256
+    io = 2 * 2 * 1024 * 32 * 50
+    assert bench.step_flops(C.PI0, 1) == 18 * (2 * 50 * per_layer + attn) + io
+    assert bench.step_flops(C.PI0_BATCH16, 16) == 16 * bench.step_flops(C.PI0, 1)
+    # bytes: bf16 weights once per step + the prefix K and V of every robot (suffix K/V excluded)
+    kv = 2 * 816 * 256 * 2
+    assert bench.step_bytes(C.PI0, 1) == 18 * (2 * per_layer + kv) + 2 * 2 * 1024 * 32
+    assert bench.step_bytes(C.PI0, 16) - bench.step_bytes(C.PI0, 1) == 15 * 18 * kv
