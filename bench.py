@@ -174,10 +174,34 @@ def bench_verify(args, cfg, W, kvs, ex, stream):
                      "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
         "kernels": kernels,
     }
+    result["rounds"] = bench_rounds(cfg, ex, args.steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline_verify(cfg, W, kvs[0][0], kvs[0][1])
     ex.close()
     print(json.dumps(result))
+
+
+def bench_rounds(cfg, ex, reps):
+    """Dual-path rounds (ae_round, synchronous, host buffers): a fast round (the verification
+    accepts: draft seed 0, no gripper switch, delta above every distance) and a full round (draft
+    seed 1 switches the gripper: verification, then the 10-step denoise). Wall clock per call and
+    the device-timeline figure of ae_last_gpu_ms, medians over `reps` rounds after one warm-up."""
+    from workload import gen as G
+    out = {}
+    for name, seed in (("fast", 0), ("full", 1)):
+        draft, noise, taus = G.make_verify_case(cfg, seed)
+        nf = G.make_noise(cfg, 500 + seed, 1)[0]
+        res = ex.round(0, draft, noise, taus, 1e9, nf, cfg.steps)  # captures the graphs
+        assert res[3] == (name == "full")
+        wall, gpu = [], []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            ex.round(0, draft, noise, taus, 1e9, nf, cfg.steps)
+            wall.append((time.perf_counter() - t0) * 1e3)
+            gpu.append(ex.last_gpu_ms())
+        out[name] = {"wall_ms": round(float(np.median(wall)), 4), "gpu_ms": round(float(np.median(gpu)), 4),
+                     "accept": int(res[1]), "full_path": int(res[3])}
+    return out
 
 
 def cpu_baseline_verify(cfg, W, k, v, budget_s=12.0):

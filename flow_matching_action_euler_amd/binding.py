@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libae.so")
 AE_OK = 0
 ERRORS = {-1: "AE_ERR_INVALID_ARG", -2: "AE_ERR_UNSUPPORTED", -3: "AE_ERR_NOT_READY", -4: "AE_ERR_OOM", -5: "AE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
-EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async",
+EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async", "ae_round",
            "ae_destroy", "ae_last_error", "ae_last_gpu_ms", "ae_kernel_times")
 
 
@@ -69,6 +69,7 @@ def load_library(path=LIB_PATH):
         "ae_denoise_async": (I, [P, I, P, I, P, P]),
         "ae_verify": (I, [P, I, P, P, P, I, F, P, P, P]),
         "ae_verify_async": (I, [P, I, P, P, P, I, F, P, P, P, P]),
+        "ae_round": (I, [P, I, P, P, P, I, F, P, I, P, P, P, P]),
         "ae_destroy": (V, [P]),
         "ae_last_error": (ctypes.c_char_p, [P]),
         "ae_last_gpu_ms": (I, [P, ctypes.POINTER(F)]),
@@ -184,6 +185,17 @@ class ActionExpert:
             self.h, slot, ctypes.c_void_p(d_draft), ctypes.c_void_p(d_noise), ctypes.c_void_p(d_taus), n_tau,
             ctypes.c_float(delta), ctypes.c_void_p(d_accept), ctypes.c_void_p(d_switch),
             ctypes.c_void_p(d_dist) if d_dist else None, ctypes.c_void_p(stream) if stream else None))
+
+    def round(self, slot, draft, noise_verify, taus, delta, noise_full, steps):
+        """One dual-path round: (actions [H][A], accept_len, gripper_switch, full_path)."""
+        draft, nv, taus, nf = (_c(draft, np.float32), _c(noise_verify, np.float32), _c(taus, np.float32),
+                               _c(noise_full, np.float32))
+        out = np.empty_like(draft)
+        acc, sw, full = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        self._check(self.lib.ae_round(self.h, slot, _ptr(draft), _ptr(nv), _ptr(taus), len(taus), ctypes.c_float(delta),
+                                      _ptr(nf), steps, _ptr(out), ctypes.byref(acc), ctypes.byref(sw),
+                                      ctypes.byref(full)))
+        return out, acc.value, sw.value, full.value
 
     def last_gpu_ms(self):
         ms = ctypes.c_float()

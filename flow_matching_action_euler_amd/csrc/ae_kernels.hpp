@@ -1103,7 +1103,8 @@ struct AttnArgs {
   const void* vs;         // packed suffix V
   const void* kcache;     // packed prefix K [slot][L][n_kv][nbp][2][dh/32][64][8]
   const void* vcache;     // packed prefix V [slot][L][n_kv][nbp][dh/16][64][8]
-  const int* seq_slot;    // prefix slot of each sequence; null: sequence s uses slot s (no load)
+  const int* seq_slot;    // prefix slot of each sequence; null: sequence s uses slot slot0 + s (no load)
+  int slot0;
   size_t slot_stride, layer_off;  // elements (same for K and V)
   int P, H, n_q, n_kv, dh;
   int nbp, nbs;           // 32-key prefix / suffix blocks
@@ -1162,7 +1163,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int gq = a.n_q / a.n_kv;
   const int R = gq * a.H;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int slot = a.seq_slot ? a.seq_slot[s] : s;
+  const int slot = a.seq_slot ? a.seq_slot[s] : a.slot0 + s;
   const int nb = a.nbp + a.nbs;
   const int bps = (nb + a.n_split - 1) / a.n_split;         // blocks per split
   const int b_begin = split * bps, b_end = min(nb, b_begin + bps);

@@ -558,7 +558,7 @@ int prefetch_down_lead() {
 
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
 // temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
-int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, float dt,
+int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, int slot0, float dt,
                      hipStream_t st, Timer* tm) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
@@ -578,6 +578,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   AttnArgs aa{};
   aa.q = h->q; aa.ks = h->ks; aa.vs = h->vs; aa.kcache = h->kcache; aa.vcache = h->vcache;
   aa.seq_slot = seq_slot;
+  aa.slot0 = slot0;
   aa.slot_stride = h->slot_elems;
   aa.P = c.prefix_len; aa.H = H; aa.n_q = nq; aa.n_kv = nkv; aa.dh = dh;
   aa.nbp = h->nbp; aa.nbs = h->nbs; aa.ntt = Mp / 16;
@@ -600,9 +601,9 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->qkv_p[l]; a.x = h->hb;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().qkv, n_z).S;
-      if ((prefetch_mask() & 1) && n_seq == 1 && h->slot_elems) {  // this layer's prefix K/V (one robot: slot 0)
+      if ((prefetch_mask() & 1) && n_seq == 1 && !seq_slot && h->slot_elems) {  // this layer's prefix K/V (one robot)
         const size_t kes = dtype_size(c.kv_dtype), lay = (size_t)nkv * h->nbp * ATT_KB * dh;
-        const size_t off = (size_t)l * lay * kes;
+        const size_t off = ((size_t)slot0 * h->slot_elems + (size_t)l * lay) * kes;
         a.pf.kind = 1; a.pf.bytes = lay * kes;
         a.pf.base = (const char*)h->kcache + off; a.pf.base2 = (const char*)h->vcache + off;
       }
@@ -724,11 +725,11 @@ int get_temb_steps(ae_handle* h, int steps, float** out) {
   return AE_OK;
 }
 
-int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t st, Timer* tm) {
+int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t st, Timer* tm, int slot0 = 0) {
   const float dt = 1.f / (float)steps;
   for (int k = 0; k < steps; ++k) {
     // robot b uses prefix slot b: no slot table (the attention then reads no slot from memory)
-    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, nullptr, dt, st, tm);
+    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, nullptr, slot0, dt, st, tm);
     if (rc) return rc;
   }
   return AE_OK;
@@ -741,7 +742,7 @@ int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
                                                       h->draft, h->vnoise, h->taus, n_tau, H, A, h->x));
   int rc = enqueue_temb(h, h->taus, n_tau, h->temb_tau, st, tm);
   if (rc) return rc;
-  rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0.f, st, tm);
+  rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm);
   if (rc) return rc;
   LAUNCH_CHECK(h, "verify_accept", AE_LAUNCH(verify_kernel, dim3(1), dim3(256), (size_t)n_tau * H * sizeof(float), st,
                                                       h->x, h->vout, h->draft, h->taus, n_tau, H, A, h->params,
@@ -753,13 +754,17 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
   auto key = std::make_tuple(mode, a, b);
   auto it = h->graphs.find(key);
   if (it != h->graphs.end()) { *out = it->second; return AE_OK; }
+  // mode 0: denoise (a steps, b robots on slots 0..b-1); 1: verify (a flow times);
+  // 2: denoise of one robot on prefix slot b (a steps)
   float* temb = nullptr;
-  if (mode == 0) {
+  if (mode == 0 || mode == 2) {
     int rc = get_temb_steps(h, a, &temb);
     if (rc) return rc;
   }
   HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
-  int rc = mode == 0 ? enqueue_denoise(h, b, a, temb, h->stream, nullptr) : enqueue_verify(h, a, h->stream, nullptr);
+  int rc = mode == 0   ? enqueue_denoise(h, b, a, temb, h->stream, nullptr)
+           : mode == 2 ? enqueue_denoise(h, 1, a, temb, h->stream, nullptr, b)
+                       : enqueue_verify(h, a, h->stream, nullptr);
   hipGraph_t graph = nullptr;
   hipError_t e = hipStreamEndCapture(h->stream, &graph);
   if (rc) { if (graph) hipGraphDestroy(graph); return rc; }
@@ -1135,6 +1140,57 @@ int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, co
   *accept_len = acc;
   *gripper_switch = sw;
   if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
+  return AE_OK;
+}
+
+int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_verify, const float* taus, int n_tau,
+             float delta, const float* noise_full, int steps, float* actions_out, int* accept_len, int* gripper_switch,
+             int* full_path) {
+  int rc = check_verify(h, slot, n_tau);
+  if (rc) return rc;
+  if (steps < 1 || steps > 1000) return fail(h, AE_ERR_INVALID_ARG, "steps out of range (1..1000)");
+  if (!draft || !noise_verify || !taus || !noise_full || !actions_out || !accept_len || !gripper_switch || !full_path)
+    return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  for (int j = 0; j < n_tau; ++j)
+    if (!(taus[j] >= 0.f && taus[j] < 1.f)) return fail(h, AE_ERR_INVALID_ARG, "tau must lie in [0, 1)");
+  // both graphs exist before the round starts (the first round of a shape captures them)
+  hipGraphExec_t gv, gd;
+  rc = get_graph(h, 1, n_tau, 1, &gv);
+  if (rc) return rc;
+  rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd) : get_graph(h, 2, steps, slot, &gd);
+  if (rc) return rc;
+  rc = verify_common(h, slot, n_tau, delta, h->stream, hipMemcpyHostToDevice, draft, noise_verify, taus);
+  if (rc) return rc;
+  const size_t ha = (size_t)h->c.horizon * h->c.action_dim * sizeof(float);
+  // fast path: the verification pass, then the host reads the decision
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(gv, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  int acc = 0, sw = 0;
+  HIP_TRY(h, hipMemcpyAsync(&acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipMemcpyAsync(&sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  rc = check_err_flag(h);
+  if (rc) return rc;
+  // an empty accepted prefix (a gripper switch forces it) falls back to the full denoise loop
+  const int full = acc == 0;
+  std::vector<float> out(ha / sizeof(float));
+  if (full) {
+    HIP_TRY(h, hipMemcpyAsync(h->x, noise_full, ha, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipGraphLaunch(gd, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(out.data(), h->x, ha, hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    rc = check_err_flag(h);
+    if (rc) return rc;
+  } else {
+    memcpy(out.data(), draft, ha);
+  }
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  memcpy(actions_out, out.data(), ha);
+  *accept_len = acc;
+  *gripper_switch = sw;
+  *full_path = full;
   return AE_OK;
 }
 

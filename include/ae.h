@@ -170,6 +170,27 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
                     int n_tau, float delta, int* d_accept_len, int* d_gripper_switch, float* d_dist_out,
                     void* stream);
 
+/* One round of the dual-path runtime ("Realtime-VLA FLASH" article, section 03:
+ * dual-path inference and phase-aware fallback). The fast path is ae_verify of
+ * `draft` on prefix slot `slot` at the n_tau flow times `taus` with the noise
+ * `noise_verify` and threshold `delta`. When its accepted prefix is empty -- which
+ * a gripper switch in the draft forces -- the round falls back to the full path:
+ * the denoise loop of `steps` uniform Euler steps (as ae_denoise, for this slot)
+ * from `noise_full`.
+ * Host buffers: draft, noise_verify, noise_full, actions_out [H][A] fp32;
+ * taus [n_tau]. actions_out receives the draft on the fast path (its first
+ * *accept_len rows are the accepted ones) and the denoised chunk on the full
+ * path; *full_path is 0 or 1. Synchronous: the host reads the verification's
+ * decision before the full path is launched. ae_last_gpu_ms then covers the
+ * round on the device timeline, from the verification's start to the end of
+ * the last pass it ran (the host decision included). The first round of a
+ * (n_tau, steps, slot) shape captures its graphs (slow). Errors as ae_verify,
+ * plus AE_ERR_INVALID_ARG for steps outside 1..1000; on error the outputs are
+ * not written. */
+int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_verify, const float* taus, int n_tau,
+             float delta, const float* noise_full, int steps, float* actions_out, int* accept_len,
+             int* gripper_switch, int* full_path);
+
 /* Free every device resource of the handle. NULL is a no-op. */
 void ae_destroy(ae_handle* h);
 

@@ -292,5 +292,16 @@ def verify(cfg, Wd, kv_k, kv_v, draft, noise, taus, delta):
     return accept_from_velocity(draft, x_tau, v_tau, taus, delta, cfg.gripper_dim)
 
 
+def dual_path_round(cfg, Wd, kv_k, kv_v, draft, noise_verify, taus, delta, noise_full, steps):
+    """One round of the dual-path runtime (FLASH section 03): the fast path verifies the draft;
+    when the accepted prefix is empty (a gripper switch in the draft forces that), the round falls
+    back to the full path, the denoise loop from noise_full. Returns (actions, accept, switch,
+    full_path): the draft on the fast path, the denoised chunk on the full path."""
+    accept, switch, _ = verify(cfg, Wd, kv_k, kv_v, draft, noise_verify, taus, delta)
+    if accept == 0:
+        return denoise(cfg, Wd, kv_k, kv_v, noise_full, steps), accept, switch, 1
+    return np.asarray(draft, np.float64), accept, switch, 0
+
+
 def decode_kv(cfg, k, v):
     return decode(k, cfg.kv_dtype), decode(v, cfg.kv_dtype)

@@ -174,6 +174,38 @@ def test_error_codes():
     ex.close()
 
 
+# ------------------------------------------------------------------ dual-path round
+
+def test_dual_path_round_matches_oracle():
+    """ae_round against the oracle's round: odd draft seeds switch the gripper (full path whatever
+    delta is), even seeds take the fast path at a delta above every distance and the full path at
+    delta 0 (nothing is < 0). Slot 0 and slot 2 (a graph of its own for that slot's prefix)."""
+    cfg = SMALL_BF16
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.array([0.2, 0.5, 0.8], np.float32)
+    seen = set()
+    for slot in (0, 2):
+        for seed in range(4):
+            draft = G.make_draft(cfg, seed)
+            nv = case.noise(1, 300 + seed)[0]
+            nf = case.noise(1, 400 + seed)[0]
+            _, _, D_o = case.oracle_verify(slot, draft, nv, taus, 0.05)
+            for delta in (float(D_o.max()) * 1.5 + 1e-3, 0.0):
+                act, acc, sw, full = ex.round(slot, draft, nv, taus, delta, nf, 2)
+                act_o, acc_o, sw_o, full_o = O.dual_path_round(cfg, case.Wd, case.kvd[slot][0], case.kvd[slot][1],
+                                                               draft, nv, taus, delta, nf, 2)
+                assert (acc, sw, full) == (acc_o, sw_o, full_o), (slot, seed, delta)
+                if full:
+                    assert rel_err(act, act_o) <= tol_for(cfg)
+                    assert rel_err(act, ex.denoise(np.stack([nf] * 3), 2)[0]) <= 1e-5 or slot != 0
+                else:
+                    assert np.array_equal(act, draft)
+                seen.add(full)
+    assert seen == {0, 1}
+    ex.close()
+
+
 # ------------------------------------------------------------------ token-tiled GEMMs (many tokens)
 
 # 7 robots x 20 rows = 140 tokens (3 token groups). With a shape forced (AE_TILED_SHAPE) every GEMM

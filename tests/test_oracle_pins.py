@@ -407,3 +407,28 @@ def test_suffix_rope_position_is_prefix_len_plus_row(P):
     expect = h0 + w_pre * np.array([[1.0, 2.0]])             # every prefix value row is (1, 2)
     got = O.decoder_layer(cfg, Wd, 0, h0, kp, vp)
     assert np.allclose(got, expect)
+
+
+def test_dual_path_round_branches_under_a_constant_velocity_field():
+    """With action_out_w = 0 the expert's velocity is its bias c everywhere. Then a rebuilt endpoint is
+    x_tau + (1 - tau) c = d + (1 - tau)(eps + c - d): noise eps = d - c rebuilds the draft exactly (every
+    row accepted, fast path, the draft returned), any other noise far from it rejects row 0 (full path:
+    Euler with constant velocity gives noise_full + c), and a gripper switch forces the full path."""
+    cfg = _tiny_cfg(gripper_dim=3)
+    Wd, kk, vv, noise_full = _tiny_inputs(cfg)
+    Wd["action_out_w"][:] = 0.0
+    c = np.array([0.5, -1.0, 2.0, 0.25])
+    Wd["action_out_b"] = c
+    taus = np.array([0.2, 0.5, 0.8])
+    rng = np.random.default_rng(4)
+    d = rng.standard_normal((cfg.horizon, cfg.action_dim))
+    d[:, 3] = 1.0                                   # gripper open throughout
+    act, acc, sw, full = O.dual_path_round(cfg, Wd, kk, vv, d, d - c, taus, 0.05, noise_full, 3)
+    assert (acc, sw, full) == (cfg.horizon, 0, 0) and np.array_equal(act, d)
+    far = d - c + 1.0                               # every rebuilt endpoint is (1 - tau) * 2 away from the draft
+    act, acc, sw, full = O.dual_path_round(cfg, Wd, kk, vv, d, far, taus, 0.05, noise_full, 3)
+    assert (acc, sw, full) == (0, 0, 1) and np.allclose(act, noise_full + c, atol=1e-12)
+    ds = d.copy()
+    ds[2:, 3] = -1.0                                # one switch: the full path although every row matches
+    act, acc, sw, full = O.dual_path_round(cfg, Wd, kk, vv, ds, ds - c, taus, 0.05, noise_full, 3)
+    assert (acc, sw, full) == (0, 1, 1) and np.allclose(act, noise_full + c, atol=1e-12)
