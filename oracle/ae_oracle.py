@@ -39,6 +39,13 @@ design notes):
   action_in/out and time_mlp_in/out have biases.
 * Verification: one noise draw shared by all tau; endpoint a_hat = x + (1 - tau) v;
   Euclidean distance per chunk row over all action dims; strict < delta.
+* Time-modulated expert (time_mode 1; the guide names time_mlp_in/out as the source of a
+  modulation signal and a time modulator per layer, without its form): per layer a linear map of
+  temb gives (scale, shift, gate) for each of the two sublayers, norm -> norm * (1 + scale) +
+  shift, residual += gate * sublayer; the final norm gets (scale, shift) the same way; temb is
+  then not added to the action tokens. QK-norm (qk_norm 1, Gemma3 text stack): RMSNorm of q and
+  k per head over head_dim with gains q_norm / k_norm, before RoPE; the cached prefix K is used
+  as given.
 """
 import numpy as np
 
@@ -195,34 +202,66 @@ def attention(q, k, v):
 # ----------------------------------------------------------------------------
 
 
-def decoder_layer(cfg, Wd, l, h, k_pre, v_pre):
-    """One Gemma-style block over one sequence. h: [H][w]; k_pre, v_pre: [P][n_kv][dh]."""
+def layer_modulation(cfg, Wd, l, temb):
+    """Per-layer time modulation (DM0.5 guide 5.2, "time_mlp_in / time_mlp_out turn the flow time into a
+    modulation signal" and "a time modulator in every layer"): a linear map of temb to
+    (scale1, shift1, gate1, scale2, shift2, gate2), each [w], for the attention and MLP sublayers."""
+    return np.split(linear(temb, Wd[f"layers.{l}.w_mod"], Wd[f"layers.{l}.b_mod"]), 6)
+
+
+def decoder_layer(cfg, Wd, l, h, k_pre, v_pre, mod=None):
+    """One Gemma-style block over one sequence. h: [H][w]; k_pre, v_pre: [P][n_kv][dh].
+
+    mod (time-modulated expert): (scale, shift, gate) per sublayer; the normalised input becomes
+    rmsnorm(h) * (1 + scale) + shift and the sublayer output enters the residual times gate.
+    With cfg.qk_norm, q and k are RMS-normalised per head over head_dim (gains q_norm, k_norm)
+    before RoPE, as in the Gemma3 text stack the guide builds the expert on.
+    """
     p = f"layers.{l}."
     H = h.shape[0]
     nq, nkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     n = rmsnorm(h, Wd[p + "ln1"], cfg.rms_eps)
+    if mod is not None:
+        n = n * (1.0 + mod[0]) + mod[1]
     q = linear(n, Wd[p + "wq"]).reshape(H, nq, dh)
     k = linear(n, Wd[p + "wk"]).reshape(H, nkv, dh)
     v = linear(n, Wd[p + "wv"]).reshape(H, nkv, dh)
+    if cfg.qk_norm:
+        q = rmsnorm(q, Wd[p + "q_norm"], cfg.rms_eps)
+        k = rmsnorm(k, Wd[p + "k_norm"], cfg.rms_eps)
     pos = cfg.prefix_len + np.arange(H)
     q = rope(q, pos, cfg.rope_base)
     k = rope(k, pos, cfg.rope_base)
     o = attention(q, np.concatenate([k_pre, k], axis=0), np.concatenate([v_pre, v], axis=0))
-    h = h + linear(o.reshape(H, nq * dh), Wd[p + "wo"])
+    a = linear(o.reshape(H, nq * dh), Wd[p + "wo"])
+    h = h + (a if mod is None else mod[2] * a)
     n2 = rmsnorm(h, Wd[p + "ln2"], cfg.rms_eps)
+    if mod is not None:
+        n2 = n2 * (1.0 + mod[3]) + mod[4]
     u = gelu_tanh(linear(n2, Wd[p + "wg"])) * linear(n2, Wd[p + "wu"])
-    return h + linear(u, Wd[p + "wd"])
+    m = linear(u, Wd[p + "wd"])
+    return h + (m if mod is None else mod[5] * m)
 
 
 def velocity(cfg, Wd, kv_k, kv_v, x, t):
     """v_theta(x_t, t | c) for one sequence (DM0.5 guide 5.2).
 
     x: [H][A] float64, t: scalar flow time, kv_k / kv_v: [L][P][n_kv][dh] float64.
+    cfg.time_mode 0: temb is added to every action_in_proj row; 1: temb modulates every layer's
+    norms and residual branches and the final norm (final scale and shift from final_mod).
     """
-    h = linear(x, Wd["action_in_w"], Wd["action_in_b"]) + time_embedding(Wd, t, cfg.width)[None, :]
+    temb = time_embedding(Wd, t, cfg.width)
+    h = linear(x, Wd["action_in_w"], Wd["action_in_b"])
+    if not cfg.time_mode:
+        h = h + temb[None, :]
     for l in range(cfg.n_layers):
-        h = decoder_layer(cfg, Wd, l, h, kv_k[l], kv_v[l])
-    return linear(rmsnorm(h, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
+        mod = layer_modulation(cfg, Wd, l, temb) if cfg.time_mode else None
+        h = decoder_layer(cfg, Wd, l, h, kv_k[l], kv_v[l], mod)
+    n = rmsnorm(h, Wd["final_ln"], cfg.rms_eps)
+    if cfg.time_mode:
+        scale, shift = np.split(linear(temb, Wd["final_mod_w"], Wd["final_mod_b"]), 2)
+        n = n * (1.0 + scale) + shift
+    return linear(n, Wd["action_out_w"], Wd["action_out_b"])
 
 
 def euler_integrate(x0, steps, vfield):

@@ -432,3 +432,106 @@ def test_dual_path_round_branches_under_a_constant_velocity_field():
     ds[2:, 3] = -1.0                                # one switch: the full path although every row matches
     act, acc, sw, full = O.dual_path_round(cfg, Wd, kk, vv, ds, ds - c, taus, 0.05, noise_full, 3)
     assert (acc, sw, full) == (0, 1, 1) and np.allclose(act, noise_full + c, atol=1e-12)
+
+
+# ---------------------------------------------------------------- time-modulated expert, QK-norm
+
+def _mod_cfg(**kw):
+    return _tiny_cfg(time_mode=1, **kw)
+
+
+def test_modulated_expert_with_identity_modulation_is_the_additive_one_without_temb():
+    """scale = shift = 0 and gate = 1 (zero modulation weights, bias thirds 0 / 0 / 1) leave every norm and
+    residual as in the plain block, so the velocity equals the additive expert's with temb = 0."""
+    cfg = _mod_cfg()
+    Wd, kk, vv, x = _tiny_inputs(cfg)
+    w = cfg.width
+    for l in range(cfg.n_layers):
+        Wd[f"layers.{l}.w_mod"][:] = 0.0
+        b = np.zeros(6 * w)
+        b[2 * w:3 * w] = b[5 * w:] = 1.0
+        Wd[f"layers.{l}.b_mod"] = b
+    Wd["final_mod_w"][:] = 0.0
+    Wd["final_mod_b"][:] = 0.0
+    base = cfg.with_(time_mode=0)
+    Wb = {k: v for k, v in Wd.items() if "mod" not in k}
+    Wb["time_out_w"] = np.zeros_like(Wd["time_out_w"])
+    Wb["time_out_b"] = np.zeros_like(Wd["time_out_b"])
+    for t in (0.0, 0.3, 0.9):
+        assert np.allclose(O.velocity(cfg, Wd, kk, vv, x, t), O.velocity(base, Wb, kk, vv, x, t), atol=1e-12)
+
+
+def test_modulation_gates_zero_make_every_layer_the_identity():
+    cfg = _mod_cfg()
+    Wd, kk, vv, x = _tiny_inputs(cfg)
+    for l in range(cfg.n_layers):
+        Wd[f"layers.{l}.w_mod"][:] = 0.0
+        Wd[f"layers.{l}.b_mod"][:] = 0.0
+    h0 = x @ Wd["action_in_w"].T + Wd["action_in_b"]
+    temb = O.time_embedding(Wd, 0.4, cfg.width)
+    fm = Wd["final_mod_w"] @ temb + Wd["final_mod_b"]
+    scale, shift = fm[:cfg.width], fm[cfg.width:]
+    n = h0 / np.sqrt(np.mean(h0 ** 2, axis=-1, keepdims=True) + cfg.rms_eps) * Wd["final_ln"]
+    want = (n * (1.0 + scale) + shift) @ Wd["action_out_w"].T + Wd["action_out_b"]
+    assert np.allclose(O.velocity(cfg, Wd, kk, vv, x, 0.4), want, atol=1e-12)
+
+
+def test_modulation_scale_is_a_gain_on_the_norm():
+    """A constant scale s on the attention norm equals the plain norm with gain ln1 * (1 + s)."""
+    cfg = _mod_cfg(n_layers=1)
+    Wd, kk, vv, x = _tiny_inputs(cfg)
+    w = cfg.width
+    s = np.linspace(-0.5, 0.7, w)
+    Wd["layers.0.w_mod"][:] = 0.0
+    b = np.zeros(6 * w)
+    b[:w] = s
+    b[2 * w:3 * w] = b[5 * w:] = 1.0
+    Wd["layers.0.b_mod"] = b
+    Wd["final_mod_w"][:] = 0.0
+    Wd["final_mod_b"][:] = 0.0
+    W2 = dict(Wd)
+    W2["layers.0.ln1"] = Wd["layers.0.ln1"] * (1.0 + s)
+    W2["layers.0.b_mod"] = b.copy()
+    W2["layers.0.b_mod"][:w] = 0.0
+    assert np.allclose(O.velocity(cfg, Wd, kk, vv, x, 0.2), O.velocity(cfg, W2, kk, vv, x, 0.2), atol=1e-12)
+
+
+def test_modulation_shift_enters_after_the_norm():
+    """With the MLP norm's gain 0 and scale 0, the MLP input is the shift alone: the MLP adds the
+    constant gate2 * Wd (gelu(Wg b2) * (Wu b2)) to every row, whatever h is."""
+    cfg = _mod_cfg(n_layers=1)
+    Wd, kk, vv, x = _tiny_inputs(cfg)
+    w = cfg.width
+    rng = np.random.default_rng(3)
+    b2 = rng.standard_normal(w)
+    g2 = rng.standard_normal(w)
+    Wd["layers.0.w_mod"][:] = 0.0
+    b = np.zeros(6 * w)
+    b[2 * w:3 * w] = 1.0
+    b[4 * w:5 * w] = b2
+    b[5 * w:] = g2
+    Wd["layers.0.b_mod"] = b
+    Wd["layers.0.ln2"] = np.zeros(w)
+    const = g2 * (Wd["layers.0.wd"] @ (O.gelu_tanh(Wd["layers.0.wg"] @ b2) * (Wd["layers.0.wu"] @ b2)))
+    W0 = dict(Wd)
+    W0["layers.0.b_mod"] = b.copy()
+    W0["layers.0.b_mod"][5 * w:] = 0.0   # no MLP branch
+    h_mlp = O.decoder_layer(cfg, Wd, 0, x @ Wd["action_in_w"].T, kk[0], vv[0], np.split(b, 6))
+    h_none = O.decoder_layer(cfg, W0, 0, x @ Wd["action_in_w"].T, kk[0], vv[0], np.split(W0["layers.0.b_mod"], 6))
+    assert np.allclose(h_mlp - h_none, np.broadcast_to(const, h_mlp.shape), atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["wq", "wk"])
+def test_qk_norm_is_per_head_and_scale_free(which):
+    """QK-norm normalises each head over head_dim: scaling the rows of one head of wq (or of the kv head of
+    wk) by c > 0 leaves the velocity unchanged, and without QK-norm it does not."""
+    cfg = _tiny_cfg(qk_norm=1, n_kv_heads=2, rms_eps=1e-30)  # eps would break exact scale invariance
+    Wd, kk, vv, x = _tiny_inputs(cfg)
+    dh = cfg.head_dim
+    W2 = dict(Wd)
+    W2[f"layers.0.{which}"] = Wd[f"layers.0.{which}"].copy()
+    W2[f"layers.0.{which}"][dh:2 * dh] *= 3.7   # head 1 only
+    v1, v2 = O.velocity(cfg, Wd, kk, vv, x, 0.5), O.velocity(cfg, W2, kk, vv, x, 0.5)
+    assert np.allclose(v1, v2, atol=1e-10)
+    off = cfg.with_(qk_norm=0)
+    assert not np.allclose(O.velocity(off, Wd, kk, vv, x, 0.5), O.velocity(off, W2, kk, vv, x, 0.5), atol=1e-6)

@@ -31,6 +31,8 @@ class AEConfig:
     mlp_dtype: str = "bf16"      # "f32" | "bf16" | "fp8": gate / up / down
     kv_dtype: str = "bf16"       # "f32" | "bf16": prefix cache storage
     gripper_dim: int = -1        # action dim holding the +-1 gripper channel, -1 = none
+    time_mode: int = 0           # 0: temb added to every action_in_proj row; 1: per-layer time modulation
+    qk_norm: int = 0             # 1: RMSNorm of q and k per head (gains q_norm, k_norm) before RoPE
     steps: int = 10
     batch: int = 1               # robots advanced together
     weight_std: float = 0.02
@@ -45,7 +47,9 @@ class AEConfig:
     def n_params(self):
         w, A, dh, F = self.width, self.action_dim, self.head_dim, self.mlp_dim
         per_layer = (self.n_q_heads + 2 * self.n_kv_heads) * dh * w + w * self.n_q_heads * dh + 3 * F * w + 2 * w
-        return self.n_layers * per_layer + 2 * (w * w + w) + (w * A + w) + (A * w + A) + w
+        per_layer += (6 * w * w + 6 * w if self.time_mode else 0) + (2 * dh if self.qk_norm else 0)
+        final = (2 * w * w + 2 * w) if self.time_mode else 0
+        return self.n_layers * per_layer + 2 * (w * w + w) + (w * A + w) + (A * w + A) + w + final
 
 
 TINY = AEConfig(
@@ -60,7 +64,11 @@ PI0_FP8 = PI0.with_(name="pi0_fp8mlp_2view", prefix_len=560, mlp_dtype="fp8")
 PI0_VERIFY = PI0.with_(name="pi0_verify", max_taus=4, gripper_dim=31)
 PI0_BATCH16 = PI0.with_(name="pi0_batch16", max_batch=16, batch=16)
 
-CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16]
+# DM0.5-style expert at the Pi0 shapes (DM0.5 guide, section 5.2: time_mlp_in/out turn the flow
+# time into a modulation signal, a per-layer time modulator, a Gemma3 text stack with QK-norm)
+DM05 = PI0.with_(name="dm05_bf16", time_mode=1, qk_norm=1)
+
+CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05]
 VERIFY_TAUS = (0.2, 0.4, 0.6, 0.8)
 VERIFY_DELTA = 0.05
 

@@ -62,23 +62,42 @@ def weight_names(cfg):
             (p + "ln2", (w,), "gain"),
             (p + "wg", (F, w), "mlp"), (p + "wu", (F, w), "mlp"), (p + "wd", (w, F), "mlp"),
         ]
+        if cfg.time_mode:  # [scale1 | shift1 | gate1 | scale2 | shift2 | gate2] from temb
+            out += [(p + "w_mod", (6 * w, w), "lin"), (p + "b_mod", (6 * w,), "modbias")]
+        if cfg.qk_norm:
+            out += [(p + "q_norm", (dh,), "normgain"), (p + "k_norm", (dh,), "normgain")]
     out += [("final_ln", (w,), "gain"), ("action_out_w", (A, w), "lin"), ("action_out_b", (A,), "bias")]
+    if cfg.time_mode:  # [scale | shift] of the final norm
+        out += [("final_mod_w", (2 * w, w), "lin"), ("final_mod_b", (2 * w,), "modbias")]
     return out
 
 
 def make_weights(cfg, seed=None):
     """Random-init expert weights.
 
-    Draw order: for each entry of ``weight_names`` that is not a gain, one
-    ``standard_normal(shape, float32) * weight_std`` draw. Gains are 1.
-    Biases stay float32; "lin" tensors use ``weight_dtype``; "mlp" tensors use
-    ``mlp_dtype`` (fp8 adds ``<name>.scale``).
+    Draw order: for each entry of ``weight_names`` that is not a gain or a
+    modulation bias, one ``standard_normal(shape, float32) * weight_std`` draw
+    ("normgain": ``1 + 0.1 * standard_normal``). Gains are 1; modulation biases
+    are 0 except their gate thirds (1), so the modulated block starts near the
+    plain one. Biases stay float32; "lin" tensors use ``weight_dtype``; "mlp"
+    tensors use ``mlp_dtype`` (fp8 adds ``<name>.scale``).
     """
     rng = np.random.default_rng(cfg.weight_seed if seed is None else seed)
     W = {}
     for name, shape, kind in weight_names(cfg):
         if kind == "gain":
             W[name] = np.ones(shape, np.float32)
+            continue
+        if kind == "modbias":
+            b = np.zeros(shape, np.float32)
+            w = cfg.width
+            if shape[0] == 6 * w:
+                b[2 * w:3 * w] = 1.0
+                b[5 * w:6 * w] = 1.0
+            W[name] = b
+            continue
+        if kind == "normgain":
+            W[name] = (1.0 + 0.1 * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
             continue
         a = rng.standard_normal(shape, dtype=np.float32) * np.float32(cfg.weight_std)
         if kind == "bias":
