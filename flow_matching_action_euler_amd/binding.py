@@ -30,12 +30,13 @@ class ae_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "n_layers", "width", "n_q_heads", "n_kv_heads", "head_dim", "mlp_dim", "action_dim", "horizon",
         "prefix_len", "max_batch", "max_taus")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
-        (n, ctypes.c_int) for n in ("weight_dtype", "mlp_dtype", "kv_dtype", "gripper_dim")]
+        (n, ctypes.c_int) for n in ("weight_dtype", "mlp_dtype", "kv_dtype", "gripper_dim", "time_mode", "qk_norm")]
 
 
 class ae_layer_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in (
-        "ln1", "wq", "wk", "wv", "wo", "ln2", "wg", "wu", "wd", "wg_scale", "wu_scale", "wd_scale")]
+        "ln1", "wq", "wk", "wv", "wo", "ln2", "wg", "wu", "wd", "wg_scale", "wu_scale", "wd_scale",
+        "w_mod", "b_mod", "q_norm", "k_norm")]
 
 
 class ae_weights(ctypes.Structure):
@@ -43,7 +44,8 @@ class ae_weights(ctypes.Structure):
                 ("time_out_w", ctypes.c_void_p), ("time_out_b", ctypes.c_void_p),
                 ("action_in_w", ctypes.c_void_p), ("action_in_b", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(ae_layer_weights)),
-                ("final_ln", ctypes.c_void_p), ("action_out_w", ctypes.c_void_p), ("action_out_b", ctypes.c_void_p)]
+                ("final_ln", ctypes.c_void_p), ("action_out_w", ctypes.c_void_p), ("action_out_b", ctypes.c_void_p),
+                ("final_mod_w", ctypes.c_void_p), ("final_mod_b", ctypes.c_void_p)]
 
 
 class ae_kernel_stat(ctypes.Structure):
@@ -98,7 +100,8 @@ def make_config(cfg):
         head_dim=cfg.head_dim, mlp_dim=cfg.mlp_dim, action_dim=cfg.action_dim, horizon=cfg.horizon,
         prefix_len=cfg.prefix_len, max_batch=cfg.max_batch, max_taus=cfg.max_taus, rope_base=cfg.rope_base,
         rms_eps=cfg.rms_eps, weight_dtype=DTYPES[cfg.weight_dtype], mlp_dtype=DTYPES[cfg.mlp_dtype],
-        kv_dtype=DTYPES[cfg.kv_dtype], gripper_dim=cfg.gripper_dim)
+        kv_dtype=DTYPES[cfg.kv_dtype], gripper_dim=cfg.gripper_dim, time_mode=getattr(cfg, "time_mode", 0),
+        qk_norm=getattr(cfg, "qk_norm", 0))
 
 
 class ActionExpert:
@@ -126,14 +129,14 @@ class ActionExpert:
         layers = (ae_layer_weights * L)()
         for l in range(L):
             pre = f"layers.{l}."
-            for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "wg", "wu", "wd"):
+            for f in ("ln1", "wq", "wk", "wv", "wo", "ln2", "wg", "wu", "wd", "w_mod", "b_mod", "q_norm", "k_norm"):
                 setattr(layers[l], f, p(pre + f))
             for f in ("wg", "wu", "wd"):
                 setattr(layers[l], f + "_scale", p(pre + f + ".scale"))
         w = ae_weights(time_in_w=p("time_in_w"), time_in_b=p("time_in_b"), time_out_w=p("time_out_w"),
                        time_out_b=p("time_out_b"), action_in_w=p("action_in_w"), action_in_b=p("action_in_b"),
                        layers=layers, final_ln=p("final_ln"), action_out_w=p("action_out_w"),
-                       action_out_b=p("action_out_b"))
+                       action_out_b=p("action_out_b"), final_mod_w=p("final_mod_w"), final_mod_b=p("final_mod_b"))
         self._cfg = make_config(cfg)
         h = ctypes.c_void_p()
         rc = self.lib.ae_create(ctypes.byref(self._cfg), ctypes.byref(w), ctypes.byref(h))

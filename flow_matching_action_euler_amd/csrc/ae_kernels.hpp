@@ -238,6 +238,11 @@ struct GemmArgs {
   int trace_id;          // kernel kind for the optional phase trace
   Prefetch pf;           // next kernel's operands to place in L2 (QKV and gate/up launches only)
   int tn_blocks, tm_blocks;  // token-tiled launches: channel and token panels of the output
+  // time-modulated expert and QK-norm (null when off; 64-token kernel only)
+  const float* shift_bias;  // EPI_QKV / EPI_GEGLU: W . shift per packed channel, added after the 1/rms scaling
+  const float* res_gate;    // EPI_RESID: gate per output channel on the sublayer's output
+  const float* qk_gain;     // EPI_QKV: QK-norm gain per packed q/k channel (applied before RoPE)
+  float* qk_ssp;            // EPI_QKV: [q and k tiles][M_pad] sums of squares of the q/k channels of a tile
 };
 
 constexpr int GW = 8;         // waves per GEMM workgroup
@@ -632,6 +637,21 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
           const int sq = tok / a.H, t = tok % a.H;
           const float ir = inv_rms[tl];
           const float* rr = res + tl * 16;
+          float xs[16];  // the tile's 16 channels of this token: dims pair*8 + c, then + dh/2
+#pragma unroll
+          for (int c = 0; c < 16; ++c) xs[c] = rr[c] * ir;
+          if (a.shift_bias) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) xs[c] += a.shift_bias[t_in * 16 + c];
+          }
+          if (a.qk_gain) {  // QK-norm: this tile's share of the head's sum of squares, then the gains
+            float sq2 = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) sq2 += xs[c] * xs[c];
+            if (hf == 0) a.qk_ssp[(size_t)t_in * a.M_pad + tok] = sq2;
+#pragma unroll
+            for (int c = 0; c < 16; ++c) xs[c] *= a.qk_gain[t_in * 16 + c];
+          }
           float out[8];
 #pragma unroll
           for (int j = 0; j < 8; j += 2) {
@@ -639,7 +659,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
               const float cs_c = u ? cs2.z : cs2.x, cs_s = u ? cs2.w : cs2.y;
-              const float x1 = rr[j + u] * ir, x2 = rr[8 + j + u] * ir;  // dims d and d + dh/2
+              const float x1 = xs[j + u], x2 = xs[8 + j + u];  // dims d and d + dh/2
               out[j + u] = hf ? x1 * cs_s + x2 * cs_c : x1 * cs_c - x2 * cs_s;
             }
           }
@@ -682,6 +702,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       }
       float val = res[e] * inv_rms[tl];
       if constexpr (WT == WT_FP8) val *= psc[i];
+      if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
+        if (a.shift_bias) val += a.shift_bias[tile * 16 + c];
       if constexpr (EPI == EPI_QKV) {
         // v tiles only (q and k tiles took the vectorised path above): value A fragments (of V^T)
         // of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
@@ -695,7 +717,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         const int n = (int)tile * 16 + c;
         float hn = 0.f;
         if (valid) {
-          hn = pre0[i] + val;
+          hn = pre0[i] + (a.res_gate ? a.res_gate[n] * val : val);
           a.h[(size_t)tok * a.N + n] = hn;
           Act<AT>::st((XT*)a.hb, act_idx(tok, n, a.M_pad / 16), hn * gn[i]);
         }
@@ -708,6 +730,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       } else if constexpr (EPI == EPI_GEGLU) {
         float up = res[e + 1024] * inv_rms[tl];
         if constexpr (WT == WT_FP8) up *= psc[(i + 2) & (2 * NT - 1)];  // the up tile of this gate element
+        if (a.shift_bias) up += a.shift_bias[(tile + 1) * 16 + c];
         const int f = (int)(tile / 2) * 16 + c;
         if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
       } else {  // EPI_OUT: bias (gn) and x (pre0) were loaded before the MFMAs
@@ -1118,6 +1141,12 @@ struct AttnArgs {
   int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
   void* o;                // output, fragment order (act_idx)
   int trace_id;
+  // QK-norm: per (q or k tile, token) sums of squares of the raw projections written by the QKV
+  // epilogue ([q tiles, then k tiles][qk_mpad]); a score is scaled by 1/rms of its query head row and,
+  // for suffix keys, of its key (the cached prefix keys come normalised)
+  const float* qk_ssp;
+  int qk_mpad;
+  float qk_inv_dh, qk_eps;
 };
 
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
@@ -1128,9 +1157,11 @@ constexpr int ATT_KB = 32;     // keys per wave block
 constexpr int ATT_WAVES_SPLIT = 8, ATT_IT_SPLIT = 1;
 constexpr int ATT_WAVES_WHOLE = 8, ATT_IT_WHOLE = 4;
 
-template <int DH, int NW>
-constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp32 at most)
-  return (size_t)NW * ATT_ROWS * (DH + 4) * 4 + (size_t)NW * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4;
+constexpr int ATT_QKN_KEYS = 256;  // suffix keys the QK-norm scales are staged for (horizon <= 256)
+template <int DH, int NW, bool QKN = false>
+constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp32 at most); QK-norm scales
+  return (size_t)NW * ATT_ROWS * (DH + 4) * 4 + (size_t)NW * ATT_ROWS * 2 * 4 + (size_t)ATT_ROWS * DH * 4 +
+         (QKN ? (size_t)(ATT_ROWS + ATT_QKN_KEYS) * 4 : 0);
 }
 
 // Attention of suffix query rows over [prefix ; suffix] keys. Grid (n_split,
@@ -1144,7 +1175,7 @@ constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp
 // the next block as soon as its S^T is done, its V fragments as soon as its
 // O^T is done. The waves merge (m, l, O) in LDS; with one split the workgroup
 // writes o, with several it stores its partial for attn_merge.
-template <int AT, int DH, int ATT_IT, int NW>
+template <int AT, int DH, int ATT_IT, int NW, bool QKN = false>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   typedef typename Act<AT>::T XT;
   typedef Frag<WT_BF16, AT> F;
@@ -1156,6 +1187,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   float* Ow = att_smem;                                    // [waves][16][LDO]
   float* MLw = Ow + NW * ATT_ROWS * LDO;                   // [waves][16][2]
   XT* Qs = (XT*)(MLw + NW * ATT_ROWS * 2);                 // [NKB][64][8] query fragments
+  float* rq_s = (float*)((char*)Qs + (size_t)ATT_ROWS * DH * 4);  // QK-norm: 1/rms of the 16 query rows
+  float* rk_s = rq_s + ATT_ROWS;                                  // and of the suffix keys
 
   AE_TR(0);
   const int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
@@ -1223,10 +1256,34 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     const int e = threadIdx.x + NW * 64 * i;
     if (e < QNV) *(i32x4*)(Qs + e * QVEC) = qtmp[i];
   }
+  if constexpr (QKN) {
+    // thread -> (row or key, one of the head's dh/16 tiles); a row's 16 lanes sum its tiles' partials
+    const int tph = DH / 16, q_tiles = a.n_q * tph;
+    for (int idx = threadIdx.x; idx < (ATT_ROWS + a.nbs * ATT_KB) * 16; idx += NW * 64) {
+      const int r = idx >> 4, i = idx & 15;
+      float v = 0.f;
+      if (r < ATT_ROWS) {
+        const int rg = qt * ATT_ROWS + r;
+        if (rg < R && i < tph) {
+          const int head = g * gq + rg / a.H, t = rg % a.H;
+          v = a.qk_ssp[(size_t)(head * tph + i) * a.qk_mpad + s * a.H + t];
+        }
+      } else {
+        const int key = r - ATT_ROWS;
+        if (key < a.H && i < tph) v = a.qk_ssp[(size_t)(q_tiles + g * tph + i) * a.qk_mpad + s * a.H + key];
+      }
+      v += __shfl_xor(v, 1, 16);
+      v += __shfl_xor(v, 2, 16);
+      v += __shfl_xor(v, 4, 16);
+      v += __shfl_xor(v, 8, 16);
+      if (i == 0) rq_s[r] = rsqrtf(v * a.qk_inv_dh + a.qk_eps);  // rk_s[key] = rq_s[ATT_ROWS + key]
+    }
+  }
   AE_TR(1);
   __syncthreads();  // query tile staged
 
   const int k8 = 8 * (lane >> 4);
+  const float row_scale = QKN ? a.scale_log2 * rq_s[lane & 15] : a.scale_log2;
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 oacc[NDT];
 #pragma unroll
@@ -1252,11 +1309,16 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     // online softmax over this block for row lane%16
     const int n_valid = nvs[it];
     float mb = -INFINITY;
+    // QK-norm: a suffix block's keys carry 1/rms of their own (prefix keys come normalised)
+    const int bb_it = b_begin + wave + NW * it, sk0 = (bb_it - a.nbp) * ATT_KB + k8;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float sv = (k8 + 4 * kt + v < n_valid) ? sacc[kt][v] * a.scale_log2 : -INFINITY;
+        float f = row_scale;
+        if constexpr (QKN)
+          if (bb_it >= a.nbp && k8 + 4 * kt + v < n_valid) f *= rk_s[sk0 + 4 * kt + v];
+        const float sv = (k8 + 4 * kt + v < n_valid) ? sacc[kt][v] * f : -INFINITY;
         sacc[kt][v] = sv;
         mb = fmaxf(mb, sv);
       }
@@ -1605,6 +1667,37 @@ __global__ void sinusoid_kernel(const float* t, int width, float* phi) {
 }
 
 // y[it][n] = act(W[n] . x[it] + b[n]); one wave per output row. act: 0 none, 1 silu.
+// y[step][ch] = sum_k W(ch, k) x[step][k] (+ add[ch] for ch < n_add) over packed bf16 weights
+// [n_tiles][KB][64][8] (the GEMMs' operand order: lane (k%32/8)*16 + ch%16 holds inputs k..k+7 of
+// channel ch). Grid (tiles, steps), one workgroup per 16-channel tile. It builds the time-modulated
+// expert's per-step biases W . shift, once per step count, outside the step loop.
+__global__ __launch_bounds__(256) void packed_gemv_kernel(const uint16_t* w, int KB, const float* x, int x_stride,
+                                                          const float* add, int n_add, float* y, int y_stride) {
+  __shared__ float part[16][16];
+  const int tile = blockIdx.x, step = blockIdx.y, c = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  const float* xs = x + (size_t)step * x_stride;
+  float acc = 0.f;
+  for (int kb = grp; kb < KB; kb += 16)
+    for (int q = 0; q < 4; ++q) {
+      const uint16_t* f = w + (((size_t)tile * KB + kb) * 64 + q * 16 + c) * 8;
+      for (int e = 0; e < 8; ++e) acc += bf16_to_f32(f[e]) * xs[kb * 32 + q * 8 + e];
+    }
+  part[grp][c] = acc;
+  __syncthreads();
+  if (threadIdx.x < 16) {
+    float sum = 0.f;
+    for (int g = 0; g < 16; ++g) sum += part[g][threadIdx.x];
+    const int ch = tile * 16 + threadIdx.x;
+    y[(size_t)step * y_stride + ch] = sum + ((add && ch < n_add) ? add[ch] : 0.f);
+  }
+}
+
+// g[step][i] = gain[i] * (1 + scale[step][i]): a modulated norm's gain for one step
+__global__ void mod_gain_kernel(const float* gain, const float* scale, int scale_stride, int w, float* g) {
+  const int step = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i < w) g[(size_t)step * w + i] = gain[i] * (1.f + scale[(size_t)step * scale_stride + i]);
+}
+
 template <int WT_>
 __global__ __launch_bounds__(256) void gemv_kernel(const void* w, const float* b, const float* x, int K, int N,
                                                    int act, float* y) {

@@ -131,6 +131,21 @@ struct ae_handle {
         *dist = nullptr, *params = nullptr;
   int *accept = nullptr, *gswitch = nullptr;
   std::map<int, float*> temb_steps;  // steps -> [steps][width]
+  // time-modulated expert (time_mode 1) and QK-norm
+  std::vector<void*> w_mod;          // [6w][w] row-major per layer (weight dtype)
+  std::vector<float*> b_mod;         // [6w]
+  void* final_mod_w = nullptr;       // [2w][w]
+  float* final_mod_b = nullptr;      // [2w]
+  std::vector<float*> qk_gain;       // QK-norm gains per packed q/k channel, per layer
+  float* qk_ssp = nullptr;           // [q and k tiles][Mp] per-tile sums of squares of q and k
+  float* zero_w = nullptr;           // [w] zeros: the additive temb of a modulated expert
+  struct ModTable {
+    float* mod = nullptr;                   // [L][steps][6w]: scale1 shift1 gate1 scale2 shift2 gate2
+    float *g1 = nullptr, *g2 = nullptr;     // [L][steps][w]: ln1 (1 + scale1), ln2 (1 + scale2)
+    float *bqkv = nullptr, *bgu = nullptr;  // [L][steps][tiles * 16], packed order: W . shift
+    float *fmod = nullptr, *gf = nullptr, *bout = nullptr;  // [steps][2w], [steps][w], [steps][out tiles * 16]
+  };
+  std::map<int, ModTable> mod_steps;
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
   float last_ms = 0.f;
   hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -227,12 +242,20 @@ int validate(const ae_config* c, const ae_weights* w) {
   if (!w->time_in_w || !w->time_in_b || !w->time_out_w || !w->time_out_b || !w->action_in_w || !w->action_in_b ||
       !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b)
     return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
+  if ((c->time_mode != 0 && c->time_mode != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
+    return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode and qk_norm are 0 or 1");
+  if ((c->time_mode || c->qk_norm) && (c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16))
+    return fail(nullptr, AE_ERR_UNSUPPORTED, "time modulation and QK-norm are built for bf16 weights and MLP");
+  if (c->time_mode && (!w->final_mod_w || !w->final_mod_b))
+    return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode 1 needs final_mod_w and final_mod_b");
   for (int l = 0; l < c->n_layers; ++l) {
     const ae_layer_weights& L = w->layers[l];
     if (!L.ln1 || !L.wq || !L.wk || !L.wv || !L.wo || !L.ln2 || !L.wg || !L.wu || !L.wd)
       return fail(nullptr, AE_ERR_INVALID_ARG, "null layer weight pointer");
     if (c->mlp_dtype == AE_FP8_E4M3 && (!L.wg_scale || !L.wu_scale || !L.wd_scale))
       return fail(nullptr, AE_ERR_INVALID_ARG, "fp8 MLP needs per-row scales");
+    if (c->time_mode && (!L.w_mod || !L.b_mod)) return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode 1 needs w_mod and b_mod");
+    if (c->qk_norm && (!L.q_norm || !L.k_norm)) return fail(nullptr, AE_ERR_INVALID_ARG, "qk_norm 1 needs q_norm and k_norm");
   }
   return AE_OK;
 }
@@ -355,25 +378,37 @@ const Splits& splits() { static Splits s; return s; }
 int attn_splits(int n_blocks, int it, int nw) { return std::max(1, (n_blocks + it * nw - 1) / (it * nw)); }
 
 // Attention kernels are instantiated per (activation type, head_dim, blocks per wave, waves).
-template <int AT, int IT, int NW>
-hipError_t attn_dispatch_it(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+template <int AT, int IT, int NW, bool QKN>
+hipError_t attn_dispatch_qkn(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   const void* fn = nullptr;
   size_t lds = 0;
   switch (dh) {
-    case 32: fn = (const void*)attn_kernel<AT, 32, IT, NW>; lds = attn_lds_size<32, NW>(); break;
-    case 64: fn = (const void*)attn_kernel<AT, 64, IT, NW>; lds = attn_lds_size<64, NW>(); break;
-    case 128: fn = (const void*)attn_kernel<AT, 128, IT, NW>; lds = attn_lds_size<128, NW>(); break;
-    case 256: fn = (const void*)attn_kernel<AT, 256, IT, NW>; lds = attn_lds_size<256, NW>(); break;
+    case 32: fn = (const void*)attn_kernel<AT, 32, IT, NW, QKN>; lds = attn_lds_size<32, NW, QKN>(); break;
+    case 64: fn = (const void*)attn_kernel<AT, 64, IT, NW, QKN>; lds = attn_lds_size<64, NW, QKN>(); break;
+    case 128: fn = (const void*)attn_kernel<AT, 128, IT, NW, QKN>; lds = attn_lds_size<128, NW, QKN>(); break;
+    case 256: fn = (const void*)attn_kernel<AT, 256, IT, NW, QKN>; lds = attn_lds_size<256, NW, QKN>(); break;
     default: return hipErrorInvalidValue;
   }
   if (set_attr) return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   switch (dh) {
-    case 32: AE_LAUNCH((attn_kernel<AT, 32, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
-    case 64: AE_LAUNCH((attn_kernel<AT, 64, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
-    case 128: AE_LAUNCH((attn_kernel<AT, 128, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
-    default: AE_LAUNCH((attn_kernel<AT, 256, IT, NW>), grid, dim3(NW * 64), lds, st, aa); break;
+    case 32: AE_LAUNCH((attn_kernel<AT, 32, IT, NW, QKN>), grid, dim3(NW * 64), lds, st, aa); break;
+    case 64: AE_LAUNCH((attn_kernel<AT, 64, IT, NW, QKN>), grid, dim3(NW * 64), lds, st, aa); break;
+    case 128: AE_LAUNCH((attn_kernel<AT, 128, IT, NW, QKN>), grid, dim3(NW * 64), lds, st, aa); break;
+    default: AE_LAUNCH((attn_kernel<AT, 256, IT, NW, QKN>), grid, dim3(NW * 64), lds, st, aa); break;
   }
   return hipGetLastError();
+}
+// QK-norm scaling is a separate instantiation (bf16 only), so the plain kernel is untouched by it
+template <int AT, int IT, int NW>
+hipError_t attn_dispatch_it(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  if constexpr (AT == AT_BF16) {
+    if (set_attr) {
+      hipError_t e = attn_dispatch_qkn<AT, IT, NW, false>(dh, true, grid, st, aa);
+      return e != hipSuccess ? e : attn_dispatch_qkn<AT, IT, NW, true>(dh, true, grid, st, aa);
+    }
+    if (aa.qk_ssp) return attn_dispatch_qkn<AT, IT, NW, true>(dh, false, grid, st, aa);
+  }
+  return attn_dispatch_qkn<AT, IT, NW, false>(dh, set_attr, grid, st, aa);
 }
 template <int AT>
 hipError_t attn_dispatch(int dh, bool set_attr, bool split_it, dim3 grid, hipStream_t st, const AttnArgs& aa) {
@@ -442,6 +477,7 @@ int poll_delay() {
 int tiled_shape(const ae_handle* h, int role, int n_tiles, int K, int M, int Mp, int* tn_blocks, int* tm_blocks) {
   if (role == R_OUT_PROJ || !((h->tiled_roles >> role) & 1) || Mp / TOKG < 2 || h->n_cu <= 0) return -1;
   if (h->at != AT_BF16 || ((role == R_GATE_UP || role == R_DOWN) ? h->mt : h->wt) != WT_BF16) return -1;
+  if (h->c.time_mode || h->c.qk_norm) return -1;  // its epilogues have no modulation or QK-norm
   if ((role == R_QKV_ROPE || role == R_GATE_UP) && h->c.width / 16 > TILED_MAX_GIN) return -1;
   const int tok_tiles = (M + 15) / 16;
   int best = -1;
@@ -558,20 +594,32 @@ int prefetch_down_lead() {
 
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
 // temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
+// Step k of a `steps`-step denoise of a time-modulated expert: where its modulation vectors live
+struct StepMod {
+  const ae_handle::ModTable* t;
+  int k, steps;
+};
+
 int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, int slot0, float dt,
-                     hipStream_t st, Timer* tm) {
+                     hipStream_t st, Timer* tm, const StepMod* sm = nullptr) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
   const int M = n_seq * H, Mp = (M + TOKG - 1) / TOKG * TOKG, n_z = Mp / TOKG;
+  const size_t nqkv = (size_t)h->qkv_tiles * 16, ngu = (size_t)h->gu_tiles * 16, nout = (size_t)h->out_tiles * 16;
+  // per-(layer, step) vector of a modulation table
+  auto modp = [&](const float* base, size_t per, int l) { return base + ((size_t)l * sm->steps + sm->k) * per; };
+  const float* temb_in = sm ? h->zero_w : temb;  // a modulated expert adds no temb to the tokens
+  const int temb_in_stride = sm ? 0 : temb_stride;
+  const float* g_first = sm ? modp(sm->t->g1, w, 0) : h->ln1[0];
 
   LAUNCH_CHECK(h, "in_proj", {
     if (h->at == AT_F32)
       AE_LAUNCH((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ln1[0], h->ssp_a);
+                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, h->ssp_a);
     else
       AE_LAUNCH((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb, temb_stride, M, Mp, A, H, w, h->h, h->hb, h->ln1[0], h->ssp_a);
+                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, h->ssp_a);
   });
 
   const int gq = nq / nkv, R = gq * H;
@@ -590,6 +638,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
   aa.trace_id = 1;
+  if (c.qk_norm) {
+    aa.qk_ssp = h->qk_ssp; aa.qk_mpad = Mp;
+    aa.qk_inv_dh = 1.f / (float)dh; aa.qk_eps = c.rms_eps;
+  }
 
   for (int l = 0; l < c.n_layers; ++l) {
     GemmArgs g{};
@@ -609,6 +661,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       }
       a.q_out = h->q; a.k_out = h->ks; a.v_out = h->vs; a.n_qt = h->n_qt; a.nbs = h->nbs; a.rope_cs = h->rope_cs;
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
+      if (sm) a.shift_bias = modp(sm->t->bqkv, nqkv, l);
+      if (c.qk_norm) { a.qk_gain = h->qk_gain[l]; a.qk_ssp = h->qk_ssp; }
       a.trace_id = 0;
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
@@ -630,7 +684,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       GemmArgs a = g;
       a.w = h->o_p[l]; a.x = h->o; a.ssp_in = nullptr; a.K = nq * dh;
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
-      a.h = h->h; a.hb = h->hb; a.gain_next = h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
+      a.h = h->h; a.hb = h->hb; a.gain_next = sm ? modp(sm->t->g2, w, l) : h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
+      if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 2 * w;
       if ((prefetch_mask() & 8) && !uses_tiled(h, R_GATE_UP, h->gu_tiles, w, M, Mp)) {  // gate/up's weights, tiled as gate/up is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->gu_p[l];
         a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, splits().gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
@@ -646,6 +701,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb;
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
+      if (sm) a.shift_bias = modp(sm->t->bgu, ngu, l);
       if ((prefetch_mask() & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
         a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, splits().down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
@@ -660,7 +716,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       GemmArgs a = g;
       a.w = h->d_p[l]; a.wscale = h->d_s[l]; a.x = h->u; a.ssp_in = nullptr; a.K = F;
       a.S = pick(F / 32, splits().down, n_z).S;
-      a.h = h->h; a.hb = h->hb; a.gain_next = (l + 1 < c.n_layers) ? h->ln1[l + 1] : h->final_ln;
+      a.h = h->h; a.hb = h->hb;
+      a.gain_next = (l + 1 < c.n_layers) ? (sm ? modp(sm->t->g1, w, l + 1) : h->ln1[l + 1])
+                                         : (sm ? sm->t->gf + (size_t)sm->k * w : h->final_ln);
+      if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 5 * w;
       a.ssp_out = h->ssp_a; a.N = w;
       if ((prefetch_mask() & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
         a.pf.kind = 2; a.pf.base = (const char*)h->qkv_p[l + 1];
@@ -678,7 +737,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.part = h->part; a.counters = h->counters;
     a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, splits().out, n_z).S;
-    a.bias = h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
+    a.bias = sm ? sm->t->bout + (size_t)sm->k * nout : h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
     a.trace_id = 5;
     LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, R_OUT_PROJ, a, h->out_tiles, n_z, st));
   }
@@ -696,6 +755,47 @@ int enqueue_temb(ae_handle* h, const float* t_dev, int n_t, float* out, hipStrea
     LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid));
     LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out));
   }
+  return AE_OK;
+}
+
+// The modulation vectors of every (layer, step) of a `steps`-step denoise of a time-modulated
+// expert, built once per step count from the step times' temb: the linear maps of temb, the
+// modulated norm gains, and the shift biases W . shift in the consumers' packed channel order.
+int build_mod_table(ae_handle* h, int steps, const float* temb) {
+  const ae_config& c = h->c;
+  const int w = c.width, L = c.n_layers;
+  const size_t nqkv = (size_t)h->qkv_tiles * 16, ngu = (size_t)h->gu_tiles * 16, nout = (size_t)h->out_tiles * 16;
+  ae_handle::ModTable t;
+  int rc = dalloc_t(h, &t.mod, (size_t)L * steps * 6 * w);
+  if (!rc) rc = dalloc_t(h, &t.g1, (size_t)L * steps * w);
+  if (!rc) rc = dalloc_t(h, &t.g2, (size_t)L * steps * w);
+  if (!rc) rc = dalloc_t(h, &t.bqkv, (size_t)L * steps * nqkv);
+  if (!rc) rc = dalloc_t(h, &t.bgu, (size_t)L * steps * ngu);
+  if (!rc) rc = dalloc_t(h, &t.fmod, (size_t)steps * 2 * w);
+  if (!rc) rc = dalloc_t(h, &t.gf, (size_t)steps * w);
+  if (!rc) rc = dalloc_t(h, &t.bout, (size_t)steps * nout);
+  if (rc) return rc;
+  hipStream_t st = h->stream;
+  const dim3 gw((w + 255) / 256, steps);
+  for (int l = 0; l < L; ++l) {
+    float* m = t.mod + (size_t)l * steps * 6 * w;
+    hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(6 * w / 4, steps), dim3(256), 0, st, h->w_mod[l], h->b_mod[l], temb, w,
+                       6 * w, 0, m);
+    hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln1[l], m, 6 * w, w, t.g1 + (size_t)l * steps * w);
+    hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln2[l], m + 3 * w, 6 * w, w, t.g2 + (size_t)l * steps * w);
+    hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->qkv_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->qkv_p[l],
+                       w / KBLK, m + w, 6 * w, nullptr, 0, t.bqkv + (size_t)l * steps * nqkv, (int)nqkv);
+    hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->gu_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->gu_p[l],
+                       w / KBLK, m + 4 * w, 6 * w, nullptr, 0, t.bgu + (size_t)l * steps * ngu, (int)ngu);
+  }
+  hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(2 * w / 4, steps), dim3(256), 0, st, h->final_mod_w, h->final_mod_b, temb,
+                     w, 2 * w, 0, t.fmod);
+  hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->final_ln, t.fmod, 2 * w, w, t.gf);
+  hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->out_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->action_out_p,
+                     w / KBLK, t.fmod + w, 2 * w, h->action_out_b, c.action_dim, t.bout, (int)nout);
+  HIP_TRY(h, hipGetLastError());
+  HIP_TRY(h, hipStreamSynchronize(st));
+  h->mod_steps[steps] = t;
   return AE_OK;
 }
 
@@ -721,6 +821,10 @@ int get_temb_steps(ae_handle* h, int steps, float** out) {
   if (rc) return rc;
   HIP_TRY(h, hipStreamSynchronize(h->stream));
   h->temb_steps[steps] = buf;
+  if (h->c.time_mode) {
+    rc = build_mod_table(h, steps, buf);
+    if (rc) return rc;
+  }
   *out = buf;
   return AE_OK;
 }
@@ -729,7 +833,14 @@ int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t
   const float dt = 1.f / (float)steps;
   for (int k = 0; k < steps; ++k) {
     // robot b uses prefix slot b: no slot table (the attention then reads no slot from memory)
-    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, nullptr, slot0, dt, st, tm);
+    StepMod sm{nullptr, k, steps};
+    if (h->c.time_mode) {
+      auto it = h->mod_steps.find(steps);
+      if (it == h->mod_steps.end()) return fail(h, AE_ERR_HIP, "modulation table missing for this step count");
+      sm.t = &it->second;
+    }
+    int rc = enqueue_velocity(h, batch, temb + (size_t)k * h->c.width, 0, nullptr, slot0, dt, st, tm,
+                              h->c.time_mode ? &sm : nullptr);
     if (rc) return rc;
   }
   return AE_OK;
@@ -902,7 +1013,34 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(upload(h, (void**)&g2, Lw.ln2, (size_t)w * 4));
     h->ln1.push_back(g1);
     h->ln2.push_back(g2);
+    if (c.time_mode) {
+      void* wm = nullptr;
+      float* bm = nullptr;
+      TRY(upload(h, &wm, Lw.w_mod, (size_t)6 * w * w * wes));
+      TRY(upload(h, (void**)&bm, Lw.b_mod, (size_t)6 * w * 4));
+      h->w_mod.push_back(wm);
+      h->b_mod.push_back(bm);
+    }
+    if (c.qk_norm) {  // gains in the packed q/k channel order (tile = dims p*8.. and their RoPE partners)
+      std::vector<float> gq;
+      auto head_gains = [&](const float* gain, int nh) {
+        for (int hh = 0; hh < nh; ++hh)
+          for (int pp = 0; pp < dh / 16; ++pp)
+            for (int cc = 0; cc < 16; ++cc) gq.push_back(gain[cc < 8 ? pp * 8 + cc : dh / 2 + pp * 8 + (cc - 8)]);
+      };
+      head_gains(Lw.q_norm, nq);
+      head_gains(Lw.k_norm, nkv);
+      float* gd = nullptr;
+      TRY(upload(h, (void**)&gd, gq.data(), gq.size() * 4));
+      h->qk_gain.push_back(gd);
+    }
   }
+  if (c.time_mode) {
+    TRY(upload(h, &h->final_mod_w, wts->final_mod_w, (size_t)2 * w * w * wes));
+    TRY(upload(h, (void**)&h->final_mod_b, wts->final_mod_b, (size_t)2 * w * 4));
+    TRY(dalloc_t(h, &h->zero_w, (size_t)w));
+  }
+  if (c.qk_norm) TRY(dalloc_t(h, &h->qk_ssp, (size_t)(nq + nkv) * dh / 16 * Mp));
   // ---- activations and scratch (padding rows stay zero)
   TRY(dalloc_t(h, &h->x, (size_t)Mp * A));
   TRY(dalloc_t(h, &h->vout, (size_t)Mp * A));
@@ -1073,6 +1211,7 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
 static int check_verify(ae_handle* h, int slot, int n_tau) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (h->c.max_taus < 1) return fail(h, AE_ERR_UNSUPPORTED, "handle created with max_taus = 0");
+  if (h->c.time_mode) return fail(h, AE_ERR_UNSUPPORTED, "verification of a time-modulated expert is not built");
   if (n_tau < 1 || n_tau > h->c.max_taus) return fail(h, AE_ERR_INVALID_ARG, "n_tau out of range");
   if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
   if (!h->slot_ready[slot]) return fail(h, AE_ERR_NOT_READY, "prefix slot not loaded");

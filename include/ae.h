@@ -83,10 +83,20 @@ typedef struct ae_config {
   int mlp_dtype;    /* AE_F32 | AE_BF16 | AE_FP8_E4M3: gate / up / down */
   int kv_dtype;     /* AE_F32 | AE_BF16: prefix cache */
   int gripper_dim;  /* action dim holding the +-1 gripper channel, -1 = none */
+  int time_mode;    /* 0: temb added to every action_in_proj row; 1: per-layer time modulation
+                       (see ae_layer_weights.w_mod; bf16 weights and MLP, no ae_verify / ae_round) */
+  int qk_norm;      /* 1: RMSNorm of q and k per head over head_dim (gains q_norm, k_norm)
+                       before RoPE; the cached prefix K is used as given */
 } ae_config;
 
 /* One decoder block. wq [n_q*dh][w], wk/wv [n_kv*dh][w], wo [w][n_q*dh],
- * wg/wu [F][w], wd [w][F]; *_scale are fp32 per output row, fp8 only (NULL otherwise). */
+ * wg/wu [F][w], wd [w][F]; *_scale are fp32 per output row, fp8 only (NULL otherwise).
+ * time_mode 1 ("DM0.5" guide, section 5.2: time_mlp_in/out turn the flow time into a
+ * modulation signal, and every layer has a time modulator; the form is this library's
+ * reading): w_mod [6w][w] (weight_dtype) and b_mod [6w] map temb to
+ * (scale1, shift1, gate1, scale2, shift2, gate2); the attention input is
+ * rmsnorm(h)*ln1*(1 + scale1) + shift1 and h += gate1 * o_proj(...), likewise for the MLP
+ * with the second triple. qk_norm 1: q_norm, k_norm [dh] fp32 gains. Unused pointers NULL. */
 typedef struct ae_layer_weights {
   const float* ln1;
   const void* wq;
@@ -100,9 +110,15 @@ typedef struct ae_layer_weights {
   const float* wg_scale;
   const float* wu_scale;
   const float* wd_scale;
+  const void* w_mod;
+  const float* b_mod;
+  const float* q_norm;
+  const float* k_norm;
 } ae_layer_weights;
 
-/* time_in_w/time_out_w [w][w], action_in_w [w][A], action_out_w [A][w], all host pointers. */
+/* time_in_w/time_out_w [w][w], action_in_w [w][A], action_out_w [A][w], all host pointers.
+ * time_mode 1: final_mod_w [2w][w] and final_mod_b [2w] give (scale, shift) of the final norm
+ * from temb: rmsnorm(h)*final_ln*(1 + scale) + shift; NULL otherwise. */
 typedef struct ae_weights {
   const void* time_in_w;
   const float* time_in_b;
@@ -114,6 +130,8 @@ typedef struct ae_weights {
   const float* final_ln;
   const void* action_out_w;
   const float* action_out_b;
+  const void* final_mod_w;
+  const float* final_mod_b;
 } ae_weights;
 
 typedef struct ae_handle ae_handle;

@@ -174,6 +174,67 @@ def test_error_codes():
     ex.close()
 
 
+# ------------------------------------------------------------------ time-modulated expert with QK-norm
+
+SMALL_DM05 = SMALL_BF16.with_(name="small_dm05", time_mode=1, qk_norm=1, max_taus=0)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_DM05, SMALL_DM05.with_(name="small_dm05_b7", max_batch=7),
+                                 SMALL_BF16.with_(name="small_qknorm", qk_norm=1)], ids=lambda c: c.name)
+def test_modulated_qknorm_denoise_matches_oracle(cfg):
+    """Per-layer time modulation (scale / shift / gate of both norms and the final norm) and per-head
+    QK-norm: 3 robots (one 64-token group) and 7 robots (the token-group loop), 1 and 3 steps."""
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(cfg.max_batch)
+    for steps in (1, cfg.steps):
+        got = ex.denoise(noise, steps)
+        ref = case.oracle_denoise(noise, steps)
+        err = rel_err(got, ref)
+        print(f"{cfg.name} steps={steps} rel_err={err:.3e}")
+        assert err <= tol_for(cfg), err
+    ex.close()
+
+
+def test_qknorm_verify_matches_oracle():
+    cfg = SMALL_BF16.with_(name="small_qknorm_v", qk_norm=1)
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.array([0.2, 0.5, 0.8], np.float32)
+    for seed in range(2):
+        draft = G.make_draft(cfg, seed)
+        noise = case.noise(1, 300 + seed)[0]
+        acc, sw, D = ex.verify(1, draft, noise, taus, 0.05)
+        acc_o, sw_o, D_o = case.oracle_verify(1, draft, noise, taus, 0.05)
+        assert (acc, sw) == (acc_o, sw_o)
+        assert rel_err(D, D_o) <= tol_for(cfg)
+    ex.close()
+
+
+def test_modulated_expert_rejects_verification():
+    case = Case(SMALL_DM05.with_(max_taus=2))
+    ex = _expert(case)
+    d = G.make_draft(case.cfg, 0)
+    with pytest.raises(AEError) as e:
+        ex.verify(0, d, d, np.array([0.3, 0.6], np.float32), 0.05)
+    assert e.value.code == -2
+    ex.close()
+
+
+def test_dm05_full_matches_oracle():
+    """DM0.5-style expert at the Pi0 shapes (18 layers, width 1024, 8q/1kv x 256, MLP 4096, P = 816), 10 steps."""
+    cfg = C.DM05
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(1)
+    got = ex.denoise(noise, 10)
+    ref = case.oracle_denoise(noise, 10)
+    err = rel_err(got, ref)
+    print(f"dm05 10 steps rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+    assert err <= 2e-2
+    ex.close()
+
+
 # ------------------------------------------------------------------ dual-path round
 
 def test_dual_path_round_matches_oracle():
