@@ -1147,6 +1147,9 @@ struct AttnArgs {
   const float* qk_ssp;
   int qk_mpad;
   float qk_inv_dh, qk_eps;
+  // 1: workgroup i (on XCD i % 8) takes the i-th of a contiguous run of (sequence, query tile, split)
+  // items per XCD, so the workgroups reading one sequence's K/V share one L2 (many sequences)
+  int xcd_group;
 };
 
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
@@ -1191,7 +1194,15 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   float* rk_s = rq_s + ATT_ROWS;                                  // and of the suffix keys
 
   AE_TR(0);
-  const int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
+  int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
+  if (a.xcd_group) {
+    const int T = gridDim.x * gridDim.y * gridDim.z;
+    const int L = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z), xcd = L & 7;
+    const int item = xcd * (T >> 3) + min(xcd, T & 7) + (L >> 3);
+    split = item % gridDim.x;
+    qt = (item / gridDim.x) % gridDim.y;
+    zz = item / (gridDim.x * gridDim.y);
+  }
   const int s = zz / a.n_kv, g = zz % a.n_kv;
   const int gq = a.n_q / a.n_kv;
   const int R = gq * a.H;

@@ -445,6 +445,16 @@ AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 
+// Whether attention workgroups of one sequence are grouped on one XCD when a launch covers 8 or
+// more (sequence, kv head) pairs; AE_ATTN_XCD=0 turns it off.
+bool attn_xcd_group() {
+  static bool on = [] {
+    const char* e = getenv("AE_ATTN_XCD");
+    return !e || atoi(e) != 0;
+  }();
+  return on;
+}
+
 // Whether a GEMM workgroup loops over several 64-token groups (M > 64) with its weights in
 // registers instead of one workgroup per group; AE_TOKEN_LOOP=0 turns it off.
 bool tokens_per_wg_loop() {
@@ -634,6 +644,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const AttnPlan plan = attn_plan(h, n_seq);
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
+  aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && attn_xcd_group();
   aa.err = h->err_flag;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;

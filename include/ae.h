@@ -148,8 +148,9 @@ typedef struct ae_handle ae_handle;
  * polled); AE_TOKEN_LOOP=0 (one GEMM workgroup per 64-token group instead of
  * workgroups that loop over several groups with their weights held); AE_TILED=<mask>
  * (GEMM roles, bit 0 qkv, 1 o_proj, 2 gate/up, 3 down, that may take the token-tiled
- * kernel when a pass has 128 or more tokens; default 0xf) and AE_TILED_SHAPE=0..3 (force
- * one tiled shape wherever it fits); both in-kernel exchanges assume every workgroup of the launch is
+ * kernel when a pass has 128 or more tokens; default 0xf), AE_TILED_SHAPE=0..3 (force
+ * one tiled shape wherever it fits) and AE_ATTN_XCD=0 (attention workgroups of one
+ * sequence not grouped on one XCD when a pass has 8 or more sequences); both in-kernel exchanges assume every workgroup of the launch is
  * resident at once, which holds on an otherwise idle device. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 
