@@ -1159,6 +1159,7 @@ constexpr int ATT_KB = 32;     // keys per wave block
 // exchange); otherwise 8 waves walk up to 4 blocks each (a split covers 32 blocks).
 constexpr int ATT_WAVES_SPLIT = 8, ATT_IT_SPLIT = 1;
 constexpr int ATT_WAVES_WHOLE = 8, ATT_IT_WHOLE = 4;
+constexpr int ATT_IT_MID = 2;  // co-resident splits of 8 waves x 2 blocks when 1-block splits would not fit
 
 constexpr int ATT_QKN_KEYS = 256;  // suffix keys the QK-norm scales are staged for (horizon <= 256)
 template <int DH, int NW, bool QKN = false>

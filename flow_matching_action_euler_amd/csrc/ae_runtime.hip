@@ -411,11 +411,13 @@ hipError_t attn_dispatch_it(int dh, bool set_attr, dim3 grid, hipStream_t st, co
   return attn_dispatch_qkn<AT, IT, NW, false>(dh, set_attr, grid, st, aa);
 }
 template <int AT>
-hipError_t attn_dispatch(int dh, bool set_attr, bool split_it, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+hipError_t attn_dispatch(int dh, bool set_attr, int split_it, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   if (set_attr) {
     hipError_t e = attn_dispatch_it<AT, ATT_IT_SPLIT, ATT_WAVES_SPLIT>(dh, true, grid, st, aa);
+    if (e == hipSuccess) e = attn_dispatch_it<AT, ATT_IT_MID, ATT_WAVES_SPLIT>(dh, true, grid, st, aa);
     return e != hipSuccess ? e : attn_dispatch_it<AT, ATT_IT_WHOLE, ATT_WAVES_WHOLE>(dh, true, grid, st, aa);
   }
+  if (split_it == ATT_IT_MID) return attn_dispatch_it<AT, ATT_IT_MID, ATT_WAVES_SPLIT>(dh, false, grid, st, aa);
   return split_it ? attn_dispatch_it<AT, ATT_IT_SPLIT, ATT_WAVES_SPLIT>(dh, false, grid, st, aa)
                   : attn_dispatch_it<AT, ATT_IT_WHOLE, ATT_WAVES_WHOLE>(dh, false, grid, st, aa);
 }
@@ -436,12 +438,24 @@ hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs
 // the device at once (one per compute unit); otherwise 8 waves walk up to 4 blocks each and
 // longer contexts fall back to attn_merge.
 struct AttnPlan {
-  int n_split, split_it, coresident;
+  int n_split, split_it, coresident;  // split_it: blocks per wave of a split plan (0: whole tile)
 };
+// AE_ATTN_MID=0 keeps several-sequence passes on whole-tile workgroups
+bool attn_mid_plan() {
+  static bool on = [] {
+    const char* e = getenv("AE_ATTN_MID");
+    return !e || atoi(e) != 0;
+  }();
+  return on;
+}
 AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
   const int ns = attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT);
-  if (h->coresident_attn && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, 1, 1};
+  if (h->coresident_attn && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, ATT_IT_SPLIT, 1};
+  // several sequences (verification): splits of 2 blocks per wave, if those fit on the device at once
+  const int nm = attn_splits(nb, ATT_IT_MID, ATT_WAVES_SPLIT);
+  if (h->coresident_attn && attn_mid_plan() && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
+    return {nm, ATT_IT_MID, 1};
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 

@@ -150,7 +150,8 @@ typedef struct ae_handle ae_handle;
  * (GEMM roles, bit 0 qkv, 1 o_proj, 2 gate/up, 3 down, that may take the token-tiled
  * kernel when a pass has 128 or more tokens; default 0xf), AE_TILED_SHAPE=0..3 (force
  * one tiled shape wherever it fits) and AE_ATTN_XCD=0 (attention workgroups of one
- * sequence not grouped on one XCD when a pass has 8 or more sequences); both in-kernel exchanges assume every workgroup of the launch is
+ * sequence not grouped on one XCD when a pass has 8 or more sequences) and AE_ATTN_MID=0
+ * (no co-resident 2-block attention splits for several-sequence passes); both in-kernel exchanges assume every workgroup of the launch is
  * resident at once, which holds on an otherwise idle device. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 
