@@ -39,6 +39,11 @@ design notes):
   action_in/out and time_mlp_in/out have biases.
 * Verification: one noise draw shared by all tau; endpoint a_hat = x + (1 - tau) v;
   Euclidean distance per chunk row over all action dims; strict < delta.
+* Draft model (FLASH section 03: one Gemma block and a linear action head, learnable action
+  queries over the current image features, one pass): the block's sequence is [features ;
+  queries]; queries attend to all of it, RoPE positions 0..P-1 for the features and P.. for the
+  queries; the head is the final RMSNorm then a linear map with bias. Features enter as tokens of
+  the block's width.
 * Time-modulated expert (time_mode 1; the guide names time_mlp_in/out as the source of a
   modulation signal and a time modulator per layer, without its form): per layer a linear map of
   temb gives (scale, shift, gate) for each of the two sublayers, norm -> norm * (1 + scale) +
@@ -340,6 +345,28 @@ def dual_path_round(cfg, Wd, kv_k, kv_v, draft, noise_verify, taus, delta, noise
     if accept == 0:
         return denoise(cfg, Wd, kv_k, kv_v, noise_full, steps), accept, switch, 1
     return np.asarray(draft, np.float64), accept, switch, 0
+
+
+def draft_feature_kv(cfg, Wd, feats):
+    """K/V that the draft block's attention reads for the image features (FLASH section 03, draft action
+    generation): the block's own RMSNorm and k / v projections of each feature token, K rotated at the
+    token's position 0..P-1. feats: [P][w] -> (k, v) each [P][n_kv][dh]."""
+    P = feats.shape[0]
+    n = rmsnorm(np.asarray(feats, np.float64), Wd["layers.0.ln1"], cfg.rms_eps)
+    k = linear(n, Wd["layers.0.wk"]).reshape(P, cfg.n_kv_heads, cfg.head_dim)
+    v = linear(n, Wd["layers.0.wv"]).reshape(P, cfg.n_kv_heads, cfg.head_dim)
+    return rope(k, np.arange(P), cfg.rope_base), v
+
+
+def draft_chunk(cfg, Wd, feats):
+    """Candidate chunk of the draft model (FLASH section 03): one Gemma block over [image features ;
+    learnable action queries] with every query attending to every feature and every query, then the
+    final RMSNorm and a linear action head on the query rows. Only the queries' rows are needed, so the
+    features enter as cached K/V (draft_feature_kv) and the queries as the suffix rows at positions
+    P .. P+H-1. feats: [P][w] -> chunk [H][A]."""
+    k_pre, v_pre = draft_feature_kv(cfg, Wd, feats)
+    h = decoder_layer(cfg, Wd, 0, np.asarray(Wd["queries"], np.float64), k_pre, v_pre)
+    return linear(rmsnorm(h, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
 
 
 def decode_kv(cfg, k, v):

@@ -535,3 +535,46 @@ def test_qk_norm_is_per_head_and_scale_free(which):
     assert np.allclose(v1, v2, atol=1e-10)
     off = cfg.with_(qk_norm=0)
     assert not np.allclose(O.velocity(off, Wd, kk, vv, x, 0.5), O.velocity(off, W2, kk, vv, x, 0.5), atol=1e-6)
+
+
+# ---------------------------------------------------------------- draft model
+
+def _draft_cfg():
+    return C.DRAFT.with_(width=64, n_q_heads=4, n_kv_heads=1, head_dim=16, mlp_dim=128, horizon=6, prefix_len=9,
+                         action_dim=4)
+
+
+def test_draft_equals_one_block_over_features_and_queries():
+    """The draft is one block over the whole sequence [features ; queries]: running that block on all P + H
+    tokens (every token attends to every token, RoPE at 0..P+H-1) and reading the query rows gives the same
+    chunk as the cached-feature form (features as prefix K/V, queries as suffix rows)."""
+    cfg = _draft_cfg()
+    Wd = O.dequantize_weights(cfg, G.make_weights(cfg, 5))
+    feats = G.make_features(cfg, 6).astype(np.float64)
+    P, H, nq, nkv, dh = cfg.prefix_len, cfg.horizon, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    seq = np.concatenate([feats, Wd["queries"]], axis=0)
+    p = "layers.0."
+    n = O.rmsnorm(seq, Wd[p + "ln1"], cfg.rms_eps)
+    pos = np.arange(P + H)
+    q = O.rope((n @ Wd[p + "wq"].T).reshape(P + H, nq, dh), pos, cfg.rope_base)
+    k = O.rope((n @ Wd[p + "wk"].T).reshape(P + H, nkv, dh), pos, cfg.rope_base)
+    v = (n @ Wd[p + "wv"].T).reshape(P + H, nkv, dh)
+    # attention through torch's scaled-dot-product routine, kv head repeated per query head
+    qt = torch.from_numpy(q.transpose(1, 0, 2))
+    kt = torch.from_numpy(np.repeat(k, nq // nkv, axis=1).transpose(1, 0, 2))
+    vt = torch.from_numpy(np.repeat(v, nq // nkv, axis=1).transpose(1, 0, 2))
+    o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt).numpy().transpose(1, 0, 2).reshape(P + H, nq * dh)
+    hs = seq + o @ Wd[p + "wo"].T
+    n2 = O.rmsnorm(hs, Wd[p + "ln2"], cfg.rms_eps)
+    hs = hs + (O.gelu_tanh(n2 @ Wd[p + "wg"].T) * (n2 @ Wd[p + "wu"].T)) @ Wd[p + "wd"].T
+    want = O.rmsnorm(hs[P:], Wd["final_ln"], cfg.rms_eps) @ Wd["action_out_w"].T + Wd["action_out_b"]
+    assert np.allclose(O.draft_chunk(cfg, Wd, feats), want, atol=1e-10)
+
+
+def test_draft_head_zero_gives_bias_and_features_matter():
+    cfg = _draft_cfg()
+    Wd = O.dequantize_weights(cfg, G.make_weights(cfg, 5))
+    f1, f2 = G.make_features(cfg, 6), G.make_features(cfg, 7)
+    assert not np.allclose(O.draft_chunk(cfg, Wd, f1), O.draft_chunk(cfg, Wd, f2))
+    Wd["action_out_w"][:] = 0.0
+    assert np.allclose(O.draft_chunk(cfg, Wd, f1), np.broadcast_to(Wd["action_out_b"], (cfg.horizon, cfg.action_dim)))

@@ -33,6 +33,7 @@ class AEConfig:
     gripper_dim: int = -1        # action dim holding the +-1 gripper channel, -1 = none
     time_mode: int = 0           # 0: temb added to every action_in_proj row; 1: per-layer time modulation
     qk_norm: int = 0             # 1: RMSNorm of q and k per head (gains q_norm, k_norm) before RoPE
+    draft: int = 0               # 1: draft model (one block, learnable queries over image features)
     steps: int = 10
     batch: int = 1               # robots advanced together
     weight_std: float = 0.02
@@ -49,6 +50,8 @@ class AEConfig:
         per_layer = (self.n_q_heads + 2 * self.n_kv_heads) * dh * w + w * self.n_q_heads * dh + 3 * F * w + 2 * w
         per_layer += (6 * w * w + 6 * w if self.time_mode else 0) + (2 * dh if self.qk_norm else 0)
         final = (2 * w * w + 2 * w) if self.time_mode else 0
+        if self.draft:  # queries replace the time MLP and action_in_proj
+            return self.n_layers * per_layer + self.horizon * w + (A * w + A) + w
         return self.n_layers * per_layer + 2 * (w * w + w) + (w * A + w) + (A * w + A) + w + final
 
 
@@ -68,7 +71,15 @@ PI0_BATCH16 = PI0.with_(name="pi0_batch16", max_batch=16, batch=16)
 # time into a modulation signal, a per-layer time modulator, a Gemma3 text stack with QK-norm)
 DM05 = PI0.with_(name="dm05_bf16", time_mode=1, qk_norm=1)
 
-CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05]
+# Draft model of the speculative round (FLASH article, section 03: one Gemma block and a linear action
+# head, ~110M parameters; learnable action queries over the current image features): a 2B-class Gemma
+# block (width 2048, 8q/1kv x 256, MLP 16384) over 3 views x 256 image tokens, 50 x 32 chunk
+DRAFT = AEConfig(
+    name="draft_bf16", n_layers=1, width=2048, n_q_heads=8, n_kv_heads=1, head_dim=256, mlp_dim=16384,
+    action_dim=32, horizon=50, prefix_len=768, draft=1, steps=1,
+)
+
+CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05, DRAFT]
 VERIFY_TAUS = (0.2, 0.4, 0.6, 0.8)
 VERIFY_DELTA = 0.05
 

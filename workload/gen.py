@@ -48,11 +48,14 @@ def weight_names(cfg):
     """(name, shape, kind) in draw order. Linear weights are row-major [out][in]."""
     w, A, dh, F = cfg.width, cfg.action_dim, cfg.head_dim, cfg.mlp_dim
     nq, nkv = cfg.n_q_heads, cfg.n_kv_heads
-    out = [
-        ("time_in_w", (w, w), "lin"), ("time_in_b", (w,), "bias"),
-        ("time_out_w", (w, w), "lin"), ("time_out_b", (w,), "bias"),
-        ("action_in_w", (w, A), "lin"), ("action_in_b", (w,), "bias"),
-    ]
+    if getattr(cfg, "draft", 0):  # learnable action queries instead of the time MLP and action_in_proj
+        out = [("queries", (cfg.horizon, w), "query")]
+    else:
+        out = [
+            ("time_in_w", (w, w), "lin"), ("time_in_b", (w,), "bias"),
+            ("time_out_w", (w, w), "lin"), ("time_out_b", (w,), "bias"),
+            ("action_in_w", (w, A), "lin"), ("action_in_b", (w,), "bias"),
+        ]
     for l in range(cfg.n_layers):
         p = f"layers.{l}."
         out += [
@@ -96,6 +99,9 @@ def make_weights(cfg, seed=None):
                 b[5 * w:6 * w] = 1.0
             W[name] = b
             continue
+        if kind == "query":  # N(0, 1) rows: an embedding table's scale
+            W[name] = rng.standard_normal(shape, dtype=np.float32)
+            continue
         if kind == "normgain":
             W[name] = (1.0 + 0.1 * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
             continue
@@ -122,6 +128,11 @@ def make_prefix_kv(cfg, seed=None):
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
     return store(k, cfg.kv_dtype), store(v, cfg.kv_dtype)
+
+
+def make_features(cfg, seed):
+    """Image features [P][w] float32 N(0, 1) for the draft model (3 views x 256 tokens at the block's width)."""
+    return np.random.default_rng(seed).standard_normal((cfg.prefix_len, cfg.width), dtype=np.float32)
 
 
 def make_noise(cfg, seed=None, batch=None):
