@@ -80,14 +80,19 @@ def step_flops(cfg, sequences):
     return gemm + attn
 
 
+def _cores():
+    """Threads the oracle's BLAS uses on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1]))
+    except Exception:
+        return int(os.cpu_count())
+
+
 def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0):
     """The oracle as it stands, timed on this host: Euler steps of one robot until the budget is spent."""
     from oracle import ae_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:
-        cores = os.cpu_count()
+    cores = _cores()
     Wd = O.dequantize_weights(cfg, W)
     kk, vv = O.decode_kv(cfg, k, v)
     x = noise[0].astype(np.float64)
@@ -204,6 +209,62 @@ def bench_rounds(cfg, ex, reps):
     return out
 
 
+def bench_draft(args, cfg, W):
+    """Draft-model passes (ae_draft: image features uploaded, one graph replay of the feature K/V
+    projection, the block over the action queries and the head, the chunk copied back), wall clock
+    per synchronous call and the device time of the replay, medians over `steps` after `warmup`."""
+    from flow_matching_action_euler_amd import ActionExpert
+    from workload import gen as G
+    ex = ActionExpert(cfg, W)
+    feats = G.make_features(cfg, 1)
+    for _ in range(max(1, args.warmup)):
+        ex.draft(feats)
+    wall, gpu = [], []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        t1 = time.perf_counter()
+        chunk = ex.draft(feats)
+        wall.append((time.perf_counter() - t1) * 1e3)
+        gpu.append(ex.last_gpu_ms())
+    elapsed = time.perf_counter() - t0
+    assert np.all(np.isfinite(chunk))
+    w, F, dh, nq, nkv, A = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.action_dim
+    block = ((nq + 2 * nkv) * dh * w + w * nq * dh + 3 * F * w) * 2 + A * w * 2
+    gpu_ms = float(np.median(gpu))
+    result = {
+        "metric": "draft passes/s (FLASH draft model: one 2B-class Gemma block over image features and action queries)",
+        "value": round(args.steps / elapsed, 2),
+        "unit": "draft passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(float(np.median(wall)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) image features and queries)",
+        "config": {"workload": cfg.name, "width": w, "heads": f"{nq}q/{nkv}kv", "head_dim": dh, "mlp_dim": F,
+                   "image_tokens": cfg.prefix_len, "queries": cfg.horizon, "params": cfg.n_params},
+        "gpu_ms_median": round(gpu_ms, 4),
+        "roofline": {"kernel": "whole draft pass", "bound": "hbm", "achieved": round(block / (gpu_ms * 1e-3) / 1e9, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(block / (gpu_ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_draft(cfg, W, feats)
+    ex.close()
+    print(json.dumps(result))
+
+
+def cpu_baseline_draft(cfg, W, feats, budget_s=12.0):
+    """The oracle's draft pass on the host (fp64 numpy), as many passes as fit in ~budget_s (at least one)."""
+    from oracle import ae_oracle as O
+    Wd = O.dequantize_weights(cfg, W)
+    n, t0 = 0, time.perf_counter()
+    while n == 0 or time.perf_counter() - t0 < budget_s:
+        O.draft_chunk(cfg, Wd, feats)
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 3), "unit": "draft passes/s", "cores": _cores(), "kind": "oracle",
+            "sample": f"{n} draft passes ({cfg.name}), fp64 numpy, {dt:.1f} s"}
+
+
 def cpu_baseline_verify(cfg, W, k, v, budget_s=12.0):
     """The oracle as it stands, timed on this host: verify passes (all flow times) of one draft."""
     from oracle import ae_oracle as O
@@ -255,6 +316,9 @@ def main():
     B = cfg.batch
     t_setup = time.perf_counter()
     W = G.make_weights(cfg)
+    if cfg.draft:
+        torch.cuda.set_device(0)
+        return bench_draft(args, cfg, W)
     kvs = [G.make_prefix_kv(cfg, cfg.kv_seed + r) for r in range(B)]
     noise = G.make_noise(cfg, batch=B)
     torch.cuda.set_device(0)

@@ -17,6 +17,7 @@ AE_OK = 0
 ERRORS = {-1: "AE_ERR_INVALID_ARG", -2: "AE_ERR_UNSUPPORTED", -3: "AE_ERR_NOT_READY", -4: "AE_ERR_OOM", -5: "AE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async", "ae_round",
+           "ae_draft",
            "ae_destroy", "ae_last_error", "ae_last_gpu_ms", "ae_kernel_times")
 
 
@@ -30,7 +31,8 @@ class ae_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in (
         "n_layers", "width", "n_q_heads", "n_kv_heads", "head_dim", "mlp_dim", "action_dim", "horizon",
         "prefix_len", "max_batch", "max_taus")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
-        (n, ctypes.c_int) for n in ("weight_dtype", "mlp_dtype", "kv_dtype", "gripper_dim", "time_mode", "qk_norm")]
+        (n, ctypes.c_int) for n in ("weight_dtype", "mlp_dtype", "kv_dtype", "gripper_dim", "time_mode", "qk_norm",
+                                    "draft")]
 
 
 class ae_layer_weights(ctypes.Structure):
@@ -45,7 +47,7 @@ class ae_weights(ctypes.Structure):
                 ("action_in_w", ctypes.c_void_p), ("action_in_b", ctypes.c_void_p),
                 ("layers", ctypes.POINTER(ae_layer_weights)),
                 ("final_ln", ctypes.c_void_p), ("action_out_w", ctypes.c_void_p), ("action_out_b", ctypes.c_void_p),
-                ("final_mod_w", ctypes.c_void_p), ("final_mod_b", ctypes.c_void_p)]
+                ("final_mod_w", ctypes.c_void_p), ("final_mod_b", ctypes.c_void_p), ("queries", ctypes.c_void_p)]
 
 
 class ae_kernel_stat(ctypes.Structure):
@@ -72,6 +74,7 @@ def load_library(path=LIB_PATH):
         "ae_verify": (I, [P, I, P, P, P, I, F, P, P, P]),
         "ae_verify_async": (I, [P, I, P, P, P, I, F, P, P, P, P]),
         "ae_round": (I, [P, I, P, P, P, I, F, P, I, P, P, P, P]),
+        "ae_draft": (I, [P, P, P]),
         "ae_destroy": (V, [P]),
         "ae_last_error": (ctypes.c_char_p, [P]),
         "ae_last_gpu_ms": (I, [P, ctypes.POINTER(F)]),
@@ -101,7 +104,7 @@ def make_config(cfg):
         prefix_len=cfg.prefix_len, max_batch=cfg.max_batch, max_taus=cfg.max_taus, rope_base=cfg.rope_base,
         rms_eps=cfg.rms_eps, weight_dtype=DTYPES[cfg.weight_dtype], mlp_dtype=DTYPES[cfg.mlp_dtype],
         kv_dtype=DTYPES[cfg.kv_dtype], gripper_dim=cfg.gripper_dim, time_mode=getattr(cfg, "time_mode", 0),
-        qk_norm=getattr(cfg, "qk_norm", 0))
+        qk_norm=getattr(cfg, "qk_norm", 0), draft=getattr(cfg, "draft", 0))
 
 
 class ActionExpert:
@@ -136,7 +139,8 @@ class ActionExpert:
         w = ae_weights(time_in_w=p("time_in_w"), time_in_b=p("time_in_b"), time_out_w=p("time_out_w"),
                        time_out_b=p("time_out_b"), action_in_w=p("action_in_w"), action_in_b=p("action_in_b"),
                        layers=layers, final_ln=p("final_ln"), action_out_w=p("action_out_w"),
-                       action_out_b=p("action_out_b"), final_mod_w=p("final_mod_w"), final_mod_b=p("final_mod_b"))
+                       action_out_b=p("action_out_b"), final_mod_w=p("final_mod_w"), final_mod_b=p("final_mod_b"),
+                       queries=p("queries"))
         self._cfg = make_config(cfg)
         h = ctypes.c_void_p()
         rc = self.lib.ae_create(ctypes.byref(self._cfg), ctypes.byref(w), ctypes.byref(h))
@@ -199,6 +203,13 @@ class ActionExpert:
                                       _ptr(nf), steps, _ptr(out), ctypes.byref(acc), ctypes.byref(sw),
                                       ctypes.byref(full)))
         return out, acc.value, sw.value, full.value
+
+    def draft(self, features):
+        """Candidate chunk [H][A] of a draft-model handle from image features [P][w]."""
+        features = _c(features, np.float32)
+        out = np.empty((self.cfg.horizon, self.cfg.action_dim), np.float32)
+        self._check(self.lib.ae_draft(self.h, _ptr(features), _ptr(out)))
+        return out
 
     def last_gpu_ms(self):
         ms = ctypes.c_float()

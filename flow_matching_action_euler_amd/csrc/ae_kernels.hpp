@@ -1704,6 +1704,25 @@ __global__ __launch_bounds__(256) void packed_gemv_kernel(const uint16_t* w, int
   }
 }
 
+// Rows x [M][w] fp32 as a GEMM input: hb = x * gain in fragment order (act_idx, M_pad / 16 token
+// tiles, bf16), the per-16-channel partial sums of x^2 [w/16][M_pad] the consumer's 1/rms needs,
+// and optionally x itself into the fp32 residual h [M_pad][w]. Padding rows are zero. Grid
+// (w / 16 / 4, M_pad / 64); thread -> (token, 16-channel group).
+__global__ __launch_bounds__(256) void stage_rows_kernel(const float* x, int M, int Mp, int w, const float* gain,
+                                                         float* h_out, uint16_t* hb, float* ssp) {
+  const int grp = blockIdx.x * 4 + (threadIdx.x >> 6), tok = blockIdx.y * 64 + (threadIdx.x & 63);
+  if (grp * 16 >= w || tok >= Mp) return;
+  float ss = 0.f;
+  for (int c = 0; c < 16; ++c) {
+    const int k = grp * 16 + c;
+    const float v = tok < M ? x[(size_t)tok * w + k] : 0.f;
+    ss += v * v;
+    if (h_out) h_out[(size_t)tok * w + k] = v;
+    hb[act_idx(tok, k, Mp / 16)] = f32_to_bf16(v * gain[k]);
+  }
+  ssp[(size_t)grp * Mp + tok] = ss;
+}
+
 // g[step][i] = gain[i] * (1 + scale[step][i]): a modulated norm's gain for one step
 __global__ void mod_gain_kernel(const float* gain, const float* scale, int scale_stride, int w, float* g) {
   const int step = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;

@@ -139,6 +139,9 @@ struct ae_handle {
   std::vector<float*> qk_gain;       // QK-norm gains per packed q/k channel, per layer
   float* qk_ssp = nullptr;           // [q and k tiles][Mp] per-tile sums of squares of q and k
   float* zero_w = nullptr;           // [w] zeros: the additive temb of a modulated expert
+  // draft model: the queries staged as block input rows, image features and their staging, RoPE of 0..P-1
+  float *q_h0 = nullptr, *q_ssp0 = nullptr, *feat = nullptr, *feat_ssp = nullptr, *rope_feat = nullptr;
+  void *q_hb0 = nullptr, *feat_hb = nullptr;
   struct ModTable {
     float* mod = nullptr;                   // [L][steps][6w]: scale1 shift1 gate1 scale2 shift2 gate2
     float *g1 = nullptr, *g2 = nullptr;     // [L][steps][w]: ln1 (1 + scale1), ln2 (1 + scale2)
@@ -239,9 +242,18 @@ int validate(const ae_config* c, const ae_weights* w) {
     return fail(nullptr, AE_ERR_UNSUPPORTED, "fp32 attention weights need fp32 MLP weights");
   if (c->weight_dtype == AE_BF16 && c->mlp_dtype == AE_F32)
     return fail(nullptr, AE_ERR_UNSUPPORTED, "bf16 attention weights need bf16 or fp8 MLP weights");
-  if (!w->time_in_w || !w->time_in_b || !w->time_out_w || !w->time_out_b || !w->action_in_w || !w->action_in_b ||
-      !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b)
+  if (c->draft != 0 && c->draft != 1) return fail(nullptr, AE_ERR_INVALID_ARG, "draft is 0 or 1");
+  if (c->draft) {
+    if (c->n_layers != 1 || c->max_batch != 1 || c->max_taus != 0 || c->time_mode || c->qk_norm ||
+        c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16 || c->prefix_len < 1)
+      return fail(nullptr, AE_ERR_UNSUPPORTED,
+                  "a draft model has 1 layer, max_batch 1, max_taus 0, bf16 weights, no modulation or QK-norm, prefix_len >= 1");
+    if (!w->queries || !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b)
+      return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
+  } else if (!w->time_in_w || !w->time_in_b || !w->time_out_w || !w->time_out_b || !w->action_in_w || !w->action_in_b ||
+             !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b) {
     return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
+  }
   if ((c->time_mode != 0 && c->time_mode != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
     return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode and qk_norm are 0 or 1");
   if ((c->time_mode || c->qk_norm) && (c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16))
@@ -625,7 +637,7 @@ struct StepMod {
 };
 
 int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, int slot0, float dt,
-                     hipStream_t st, Timer* tm, const StepMod* sm = nullptr) {
+                     hipStream_t st, Timer* tm, const StepMod* sm = nullptr, bool from_h = false) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
@@ -637,7 +649,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const int temb_in_stride = sm ? 0 : temb_stride;
   const float* g_first = sm ? modp(sm->t->g1, w, 0) : h->ln1[0];
 
-  LAUNCH_CHECK(h, "in_proj", {
+  // from_h: the block input rows are already in h / hb / ssp_a (the draft model's queries)
+  if (!from_h) LAUNCH_CHECK(h, "in_proj", {
     if (h->at == AT_F32)
       AE_LAUNCH((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
                          h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, h->ssp_a);
@@ -886,12 +899,44 @@ int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
   return AE_OK;
 }
 
+// The draft model's pass: stage the image features (h->feat) as GEMM input rows, write their K/V
+// through the block's own k/v projections (K rotated at positions 0..P-1) into prefix slot 0, put
+// the staged queries into h / hb / ssp_a, then the block and the head over the query rows.
+int enqueue_draft(ae_handle* h, hipStream_t st, Timer* tm) {
+  const ae_config& c = h->c;
+  const int w = c.width, P = c.prefix_len, H = c.horizon, nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
+  const int Pp = (P + TOKG - 1) / TOKG * TOKG, Mp = (H + TOKG - 1) / TOKG * TOKG;
+  LAUNCH_CHECK(h, "draft_stage_features", AE_LAUNCH(stage_rows_kernel, dim3(w / 64, Pp / 64), dim3(256), 0, st, h->feat,
+                                                    P, Pp, w, h->ln1[0], (float*)nullptr, (uint16_t*)h->feat_hb,
+                                                    h->feat_ssp));
+  {
+    // the k and v tiles of the packed QKV weights only (no query tiles): n_q = 0 makes every tile of
+    // the launch a key tile, then value tiles, in the QKV epilogue
+    const int tph = dh / 16, KB = w / KBLK;
+    GemmArgs a{};
+    a.w = (const uint16_t*)h->qkv_p[0] + (size_t)nq * tph * KB * 512;
+    a.x = h->feat_hb; a.ssp_in = h->feat_ssp; a.g_in = w / 16;
+    a.inv_width = 1.f / (float)w; a.eps = c.rms_eps;
+    a.M = P; a.M_pad = Pp; a.K = w; a.S = 1;
+    a.part = h->part; a.counters = h->counters;
+    a.n_q = 0; a.n_kv = nkv; a.dh = dh; a.H = P; a.nbs = h->nbp; a.n_qt = 0;
+    a.rope_cs = h->rope_feat;
+    a.k_out = h->kcache; a.v_out = h->vcache;  // slot 0, layer 0: the cache's own block layout
+    a.trace_id = 0;
+    LAUNCH_CHECK(h, "draft_feature_kv", (void)Dispatch::gemm(h, R_QKV_ROPE, a, 2 * nkv * tph, Pp / TOKG, st));
+  }
+  HIP_TRY(h, hipMemcpyAsync(h->h, h->q_h0, (size_t)Mp * w * 4, hipMemcpyDeviceToDevice, st));
+  HIP_TRY(h, hipMemcpyAsync(h->hb, h->q_hb0, (size_t)Mp * w * (h->at == AT_F32 ? 4 : 2), hipMemcpyDeviceToDevice, st));
+  HIP_TRY(h, hipMemcpyAsync(h->ssp_a, h->q_ssp0, (size_t)(w / 16) * Mp * 4, hipMemcpyDeviceToDevice, st));
+  return enqueue_velocity(h, 1, nullptr, 0, nullptr, 0, 0.f, st, tm, nullptr, true);
+}
+
 int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
   auto key = std::make_tuple(mode, a, b);
   auto it = h->graphs.find(key);
   if (it != h->graphs.end()) { *out = it->second; return AE_OK; }
   // mode 0: denoise (a steps, b robots on slots 0..b-1); 1: verify (a flow times);
-  // 2: denoise of one robot on prefix slot b (a steps)
+  // 2: denoise of one robot on prefix slot b (a steps); 3: the draft model's pass
   float* temb = nullptr;
   if (mode == 0 || mode == 2) {
     int rc = get_temb_steps(h, a, &temb);
@@ -900,6 +945,7 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
   HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
   int rc = mode == 0   ? enqueue_denoise(h, b, a, temb, h->stream, nullptr)
            : mode == 2 ? enqueue_denoise(h, 1, a, temb, h->stream, nullptr, b)
+           : mode == 3 ? enqueue_draft(h, h->stream, nullptr)
                        : enqueue_verify(h, a, h->stream, nullptr);
   hipGraph_t graph = nullptr;
   hipError_t e = hipStreamEndCapture(h->stream, &graph);
@@ -963,12 +1009,14 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
 #define TRY(x) do { int r_ = (x); if (r_) { msg = h->err; ae_destroy(h); return fail(nullptr, r_, msg); } } while (0)
 
   // ---- small weights (row-major, used by the time MLP and in_proj kernels)
-  TRY(upload(h, &h->time_in_w, wts->time_in_w, (size_t)w * w * wes));
-  TRY(upload(h, (void**)&h->time_in_b, wts->time_in_b, (size_t)w * 4));
-  TRY(upload(h, &h->time_out_w, wts->time_out_w, (size_t)w * w * wes));
-  TRY(upload(h, (void**)&h->time_out_b, wts->time_out_b, (size_t)w * 4));
-  TRY(upload(h, &h->action_in_w, wts->action_in_w, (size_t)w * A * wes));
-  TRY(upload(h, (void**)&h->action_in_b, wts->action_in_b, (size_t)w * 4));
+  if (!c.draft) {
+    TRY(upload(h, &h->time_in_w, wts->time_in_w, (size_t)w * w * wes));
+    TRY(upload(h, (void**)&h->time_in_b, wts->time_in_b, (size_t)w * 4));
+    TRY(upload(h, &h->time_out_w, wts->time_out_w, (size_t)w * w * wes));
+    TRY(upload(h, (void**)&h->time_out_b, wts->time_out_b, (size_t)w * 4));
+    TRY(upload(h, &h->action_in_w, wts->action_in_w, (size_t)w * A * wes));
+    TRY(upload(h, (void**)&h->action_in_b, wts->action_in_b, (size_t)w * 4));
+  }
   TRY(upload(h, (void**)&h->action_out_b, wts->action_out_b, (size_t)A * 4));
   TRY(upload(h, (void**)&h->final_ln, wts->final_ln, (size_t)w * 4));
   {
@@ -1130,6 +1178,30 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc_t(h, &h->params, 4));
   TRY(dalloc_t(h, &h->accept, 1));
   TRY(dalloc_t(h, &h->gswitch, 1));
+  if (c.draft) {
+    // the queries as the block's input rows (fixed: staged once), the feature buffers, and the RoPE
+    // table of the feature positions 0..P-1
+    const int Pp = (P + TOKG - 1) / TOKG * TOKG;
+    float* qrows = nullptr;
+    TRY(upload(h, (void**)&qrows, wts->queries, (size_t)H * w * 4));
+    TRY(dalloc_t(h, &h->q_h0, (size_t)Mp * w));
+    TRY(dalloc(h, &h->q_hb0, (size_t)Mp * w * aes));
+    TRY(dalloc_t(h, &h->q_ssp0, (size_t)(w / 16) * Mp));
+    hipLaunchKernelGGL(stage_rows_kernel, dim3(w / 64, Mp / 64), dim3(256), 0, h->stream, qrows, H, Mp, w, h->ln1[0],
+                       h->q_h0, (uint16_t*)h->q_hb0, h->q_ssp0);
+    TRY(dalloc_t(h, &h->feat, (size_t)P * w));
+    TRY(dalloc(h, &h->feat_hb, (size_t)Pp * w * aes));
+    TRY(dalloc_t(h, &h->feat_ssp, (size_t)(w / 16) * Pp));
+    std::vector<float> cs((size_t)P * (dh / 2) * 2);
+    for (int t = 0; t < P; ++t)
+      for (int d = 0; d < dh / 2; ++d) {
+        double ang = (double)t * std::pow((double)c.rope_base, -2.0 * d / dh);
+        cs[((size_t)t * (dh / 2) + d) * 2 + 0] = (float)std::cos(ang);
+        cs[((size_t)t * (dh / 2) + d) * 2 + 1] = (float)std::sin(ang);
+      }
+    TRY(upload(h, (void**)&h->rope_feat, cs.data(), cs.size() * 4));
+    if (hipGetLastError() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "query staging launch failed"); }
+  }
   if (hipDeviceSynchronize() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "device sync after upload failed"); }
 #undef TRY
   *out = h;
@@ -1187,6 +1259,7 @@ static int check_err_flag(ae_handle* h) {
 
 static int check_denoise(ae_handle* h, int batch, int steps) {
   if (!h) return AE_ERR_INVALID_ARG;
+  if (h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "a draft-model handle runs ae_draft only");
   if (batch < 1 || batch > h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "batch out of range");
   if (steps < 1 || steps > 1000) return fail(h, AE_ERR_INVALID_ARG, "steps out of range (1..1000)");
   for (int b = 0; b < batch; ++b)
@@ -1237,6 +1310,7 @@ static int check_verify(ae_handle* h, int slot, int n_tau) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (h->c.max_taus < 1) return fail(h, AE_ERR_UNSUPPORTED, "handle created with max_taus = 0");
   if (h->c.time_mode) return fail(h, AE_ERR_UNSUPPORTED, "verification of a time-modulated expert is not built");
+  if (h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "a draft-model handle runs ae_draft only");
   if (n_tau < 1 || n_tau > h->c.max_taus) return fail(h, AE_ERR_INVALID_ARG, "n_tau out of range");
   if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
   if (!h->slot_ready[slot]) return fail(h, AE_ERR_NOT_READY, "prefix slot not loaded");
@@ -1355,6 +1429,30 @@ int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_veri
   *accept_len = acc;
   *gripper_switch = sw;
   *full_path = full;
+  return AE_OK;
+}
+
+int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
+  if (!h) return AE_ERR_INVALID_ARG;
+  if (!h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "not a draft-model handle (ae_config.draft = 0)");
+  if (!features || !chunk_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  hipGraphExec_t g;
+  int rc = get_graph(h, 3, 0, 0, &g);
+  if (rc) return rc;
+  const ae_config& c = h->c;
+  HIP_TRY(h, hipMemcpyAsync(h->feat, features, (size_t)c.prefix_len * c.width * 4, hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(g, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  const size_t bytes = (size_t)c.horizon * c.action_dim * sizeof(float);
+  std::vector<float> tmp(bytes / sizeof(float));
+  HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->vout, bytes, hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  rc = check_err_flag(h);
+  if (rc) return rc;
+  h->slot_ready[0] = 1;
+  memcpy(chunk_out, tmp.data(), bytes);
   return AE_OK;
 }
 

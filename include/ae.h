@@ -87,6 +87,11 @@ typedef struct ae_config {
                        (see ae_layer_weights.w_mod; bf16 weights and MLP, no ae_verify / ae_round) */
   int qk_norm;      /* 1: RMSNorm of q and k per head over head_dim (gains q_norm, k_norm)
                        before RoPE; the cached prefix K is used as given */
+  int draft;        /* 1: a draft model for ae_draft ("Realtime-VLA FLASH" article, section 03:
+                       one Gemma block and a linear action head; learnable action queries read the
+                       current image features): n_layers 1, prefix_len = image tokens, max_batch 1,
+                       max_taus 0, time_mode 0, qk_norm 0, bf16; the time MLP and action_in weights
+                       are unused (may be NULL), ae_weights.queries is required */
 } ae_config;
 
 /* One decoder block. wq [n_q*dh][w], wk/wv [n_kv*dh][w], wo [w][n_q*dh],
@@ -132,6 +137,7 @@ typedef struct ae_weights {
   const float* action_out_b;
   const void* final_mod_w;
   const float* final_mod_b;
+  const float* queries;       /* draft 1: learnable action queries [H][w] fp32; NULL otherwise */
 } ae_weights;
 
 typedef struct ae_handle ae_handle;
@@ -210,6 +216,17 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
 int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_verify, const float* taus, int n_tau,
              float delta, const float* noise_full, int steps, float* actions_out, int* accept_len,
              int* gripper_switch, int* full_path);
+
+/* The draft model's candidate chunk ("Realtime-VLA FLASH" article, section 03, draft action
+ * generation) on a handle created with draft = 1. `features` is host [prefix_len][width] fp32:
+ * the current image features, as tokens of the block's width. The block's sequence is
+ * [features ; queries]: the features' K/V (RMSNorm ln1, k/v projections, K rotated at positions
+ * 0..prefix_len-1) are written to prefix slot 0, then the query rows run the block at positions
+ * prefix_len.. with every query attending to every feature and query, then final_ln and the
+ * action head (action_out_w, action_out_b). chunk_out: host [horizon][action_dim] fp32.
+ * Synchronous; ae_last_gpu_ms covers the device pass (features already uploaded). The first call
+ * captures the graph. AE_ERR_UNSUPPORTED on a handle that is not a draft model. */
+int ae_draft(ae_handle* h, const float* features, float* chunk_out);
 
 /* Free every device resource of the handle. NULL is a no-op. */
 void ae_destroy(ae_handle* h);

@@ -235,6 +235,41 @@ def test_dm05_full_matches_oracle():
     ex.close()
 
 
+# ------------------------------------------------------------------ draft model
+
+SMALL_DRAFT = C.DRAFT.with_(name="small_draft", width=256, n_q_heads=4, n_kv_heads=2, head_dim=64, mlp_dim=512,
+                            horizon=20, prefix_len=100, action_dim=24)
+
+
+@pytest.mark.parametrize("cfg", [SMALL_DRAFT, C.DRAFT], ids=lambda c: c.name)
+def test_draft_matches_oracle(cfg):
+    """The draft's candidate chunk against the oracle: small (100 feature tokens: a partial last key block,
+    2 kv heads) and full size (a 2B-class block, 768 feature tokens); two feature sets through one graph."""
+    W = G.make_weights(cfg)
+    Wd = O.dequantize_weights(cfg, W)
+    ex = ActionExpert(cfg, W)
+    for seed in (1, 2):
+        feats = G.make_features(cfg, seed)
+        got = ex.draft(feats)
+        ref = O.draft_chunk(cfg, Wd, feats)
+        err = rel_err(got, ref)
+        print(f"{cfg.name} seed={seed} rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+        assert err <= tol_for(cfg), err
+    with pytest.raises(AEError) as e:
+        ex.denoise(np.zeros((1, cfg.horizon, cfg.action_dim), np.float32), 1)
+    assert e.value.code == -2
+    ex.close()
+
+
+def test_draft_entry_rejects_an_expert_handle():
+    case = Case(SMALL_BF16)
+    ex = _expert(case)
+    with pytest.raises(AEError) as e:
+        ex.draft(np.zeros((SMALL_BF16.prefix_len, SMALL_BF16.width), np.float32))
+    assert e.value.code == -2
+    ex.close()
+
+
 # ------------------------------------------------------------------ dual-path round
 
 def test_dual_path_round_matches_oracle():
