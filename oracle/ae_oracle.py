@@ -39,6 +39,9 @@ design notes):
   action_in/out and time_mlp_in/out have biases.
 * Verification: one noise draw shared by all tau; endpoint a_hat = x + (1 - tau) v;
   Euclidean distance per chunk row over all action dims; strict < delta.
+* Prefix prefill (DM0.5 guide 5.1): the VLM's Gemma blocks over the prefix token embeddings
+  with full attention among the prefix tokens (a prefix is seen whole), RoPE at 0..P-1, no
+  embedding scale or logit softcap; each layer's K (rotated) and V form the cache.
 * Draft model (FLASH section 03: one Gemma block and a linear action head, learnable action
   queries over the current image features, one pass): the block's sequence is [features ;
   queries]; queries attend to all of it, RoPE positions 0..P-1 for the features and P.. for the
@@ -367,6 +370,30 @@ def draft_chunk(cfg, Wd, feats):
     k_pre, v_pre = draft_feature_kv(cfg, Wd, feats)
     h = decoder_layer(cfg, Wd, 0, np.asarray(Wd["queries"], np.float64), k_pre, v_pre)
     return linear(rmsnorm(h, Wd["final_ln"], cfg.rms_eps), Wd["action_out_w"], Wd["action_out_b"])
+
+
+def prefill_kv(cfg, Wd, emb):
+    """Per-layer prefix K/V cache from the prefix token embeddings (DM0.5 guide 5.1: the prefix is
+    encoded once by the VLM into a KV cache every step reuses): the VLM's Gemma blocks over the P
+    prefix tokens, every token attending to every prefix token, RoPE at positions 0..P-1. Returns
+    K (rotated, as the expert uses it) and V, each [L][P][n_kv][dh]. emb: [P][w]."""
+    P = emb.shape[0]
+    nq, nkv, dh = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    pos = np.arange(P)
+    h = np.asarray(emb, np.float64)
+    ks, vs = [], []
+    for l in range(cfg.n_layers):
+        p = f"layers.{l}."
+        n = rmsnorm(h, Wd[p + "ln1"], cfg.rms_eps)
+        q = rope(linear(n, Wd[p + "wq"]).reshape(P, nq, dh), pos, cfg.rope_base)
+        k = rope(linear(n, Wd[p + "wk"]).reshape(P, nkv, dh), pos, cfg.rope_base)
+        v = linear(n, Wd[p + "wv"]).reshape(P, nkv, dh)
+        ks.append(k)
+        vs.append(v)
+        h = h + linear(attention(q, k, v).reshape(P, nq * dh), Wd[p + "wo"])
+        n2 = rmsnorm(h, Wd[p + "ln2"], cfg.rms_eps)
+        h = h + linear(gelu_tanh(linear(n2, Wd[p + "wg"])) * linear(n2, Wd[p + "wu"]), Wd[p + "wd"])
+    return np.stack(ks), np.stack(vs)
 
 
 def decode_kv(cfg, k, v):

@@ -578,3 +578,45 @@ def test_draft_head_zero_gives_bias_and_features_matter():
     assert not np.allclose(O.draft_chunk(cfg, Wd, f1), O.draft_chunk(cfg, Wd, f2))
     Wd["action_out_w"][:] = 0.0
     assert np.allclose(O.draft_chunk(cfg, Wd, f1), np.broadcast_to(Wd["action_out_b"], (cfg.horizon, cfg.action_dim)))
+
+
+# ---------------------------------------------------------------- prefix prefill
+
+def _prefill_cfg(**kw):
+    base = dict(n_layers=2, width=64, n_q_heads=4, n_kv_heads=2, head_dim=16, mlp_dim=128, horizon=7,
+                mlp_dtype="f32", weight_dtype="f32", kv_dtype="f32")
+    base.update(kw)
+    return C.PREFILL.with_(**base)
+
+
+def test_prefill_attention_is_unmasked():
+    """Every prefix token attends to every prefix token: changing the last token's embedding changes the
+    first token's layer-1 K and V (a causal mask would not), while layer 0's K and V of the first token,
+    which come from its own embedding only, stay as they were."""
+    cfg = _prefill_cfg()
+    Wd = O.dequantize_weights(cfg, G.make_weights(cfg, 3))
+    emb = G.make_prefix_embeddings(cfg, 4).astype(np.float64)
+    e2 = emb.copy()
+    e2[-1] += 1.0
+    k, v = O.prefill_kv(cfg, Wd, emb)
+    k2, v2 = O.prefill_kv(cfg, Wd, e2)
+    assert np.allclose(k2[0, 0], k[0, 0], atol=1e-14) and np.allclose(v2[0, 0], v[0, 0], atol=1e-14)
+    assert not np.allclose(k2[1, 0], k[1, 0], atol=1e-6) and not np.allclose(v2[1, 0], v[1, 0], atol=1e-6)
+
+
+def test_prefill_first_layer_kv_and_single_token_closed_form():
+    """Layer 0's K/V come from the embeddings alone (the block's norm, projections, K rotated at 0..P-1),
+    and with one token the attention returns that token's V, so layer 1's input is closed form."""
+    cfg = _prefill_cfg(horizon=1)
+    Wd = O.dequantize_weights(cfg, G.make_weights(cfg, 3))
+    e = G.make_prefix_embeddings(cfg, 4).astype(np.float64)
+    k, v = O.prefill_kv(cfg, Wd, e)
+    n = e / np.sqrt(np.mean(e ** 2) + cfg.rms_eps) * Wd["layers.0.ln1"]
+    assert np.allclose(k[0].reshape(1, -1), n @ Wd["layers.0.wk"].T, atol=1e-12)  # position 0: no rotation
+    assert np.allclose(v[0].reshape(1, -1), n @ Wd["layers.0.wv"].T, atol=1e-12)
+    vh = np.repeat((n @ Wd["layers.0.wv"].T).reshape(cfg.n_kv_heads, -1), cfg.n_q_heads // cfg.n_kv_heads, axis=0)
+    h1 = e + vh.reshape(1, -1) @ Wd["layers.0.wo"].T
+    n2 = h1 / np.sqrt(np.mean(h1 ** 2) + cfg.rms_eps) * Wd["layers.0.ln2"]
+    h1 = h1 + (O.gelu_tanh(n2 @ Wd["layers.0.wg"].T) * (n2 @ Wd["layers.0.wu"].T)) @ Wd["layers.0.wd"].T
+    n1 = h1 / np.sqrt(np.mean(h1 ** 2) + cfg.rms_eps) * Wd["layers.1.ln1"]
+    assert np.allclose(v[1].reshape(1, -1), n1 @ Wd["layers.1.wv"].T, atol=1e-12)

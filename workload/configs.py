@@ -34,6 +34,7 @@ class AEConfig:
     time_mode: int = 0           # 0: temb added to every action_in_proj row; 1: per-layer time modulation
     qk_norm: int = 0             # 1: RMSNorm of q and k per head (gains q_norm, k_norm) before RoPE
     draft: int = 0               # 1: draft model (one block, learnable queries over image features)
+    prefill: int = 0             # 1: prefix prefill (the VLM's blocks over the prefix tokens -> KV cache)
     steps: int = 10
     batch: int = 1               # robots advanced together
     weight_std: float = 0.02
@@ -52,6 +53,8 @@ class AEConfig:
         final = (2 * w * w + 2 * w) if self.time_mode else 0
         if self.draft:  # queries replace the time MLP and action_in_proj
             return self.n_layers * per_layer + self.horizon * w + (A * w + A) + w
+        if self.prefill:  # the blocks only: no time MLP, action projections or final norm
+            return self.n_layers * per_layer
         return self.n_layers * per_layer + 2 * (w * w + w) + (w * A + w) + (A * w + A) + w + final
 
 
@@ -79,7 +82,15 @@ DRAFT = AEConfig(
     action_dim=32, horizon=50, prefix_len=768, draft=1, steps=1,
 )
 
-CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05, DRAFT]
+# Prefix prefill (DM0.5 guide 5.1 and 6.3: the VLM prefix is encoded once into the per-layer KV cache
+# the expert reads; the guide runs its MLP in FP8 E4M3): a 2B-class Gemma stack (18 layers, width
+# 2048, 8q/1kv x 256 -- the expert's kv heads and head_dim --, MLP 16384) over the 816 prefix tokens
+PREFILL = AEConfig(
+    name="prefill_fp8mlp", n_layers=18, width=2048, n_q_heads=8, n_kv_heads=1, head_dim=256, mlp_dim=16384,
+    action_dim=32, horizon=816, prefix_len=0, mlp_dtype="fp8", prefill=1, steps=1,
+)
+
+CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05, DRAFT, PREFILL]
 VERIFY_TAUS = (0.2, 0.4, 0.6, 0.8)
 VERIFY_DELTA = 0.05
 

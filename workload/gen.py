@@ -50,6 +50,8 @@ def weight_names(cfg):
     nq, nkv = cfg.n_q_heads, cfg.n_kv_heads
     if getattr(cfg, "draft", 0):  # learnable action queries instead of the time MLP and action_in_proj
         out = [("queries", (cfg.horizon, w), "query")]
+    elif getattr(cfg, "prefill", 0):  # the VLM's blocks only
+        out = []
     else:
         out = [
             ("time_in_w", (w, w), "lin"), ("time_in_b", (w,), "bias"),
@@ -69,7 +71,8 @@ def weight_names(cfg):
             out += [(p + "w_mod", (6 * w, w), "lin"), (p + "b_mod", (6 * w,), "modbias")]
         if cfg.qk_norm:
             out += [(p + "q_norm", (dh,), "normgain"), (p + "k_norm", (dh,), "normgain")]
-    out += [("final_ln", (w,), "gain"), ("action_out_w", (A, w), "lin"), ("action_out_b", (A,), "bias")]
+    if not getattr(cfg, "prefill", 0):
+        out += [("final_ln", (w,), "gain"), ("action_out_w", (A, w), "lin"), ("action_out_b", (A,), "bias")]
     if cfg.time_mode:  # [scale | shift] of the final norm
         out += [("final_mod_w", (2 * w, w), "lin"), ("final_mod_b", (2 * w,), "modbias")]
     return out
@@ -128,6 +131,11 @@ def make_prefix_kv(cfg, seed=None):
     k = rng.standard_normal(shape, dtype=np.float32)
     v = rng.standard_normal(shape, dtype=np.float32)
     return store(k, cfg.kv_dtype), store(v, cfg.kv_dtype)
+
+
+def make_prefix_embeddings(cfg, seed):
+    """Prefix token embeddings [P][w] float32 N(0, 1) for the prefill (P = cfg.horizon rows)."""
+    return np.random.default_rng(seed).standard_normal((cfg.horizon, cfg.width), dtype=np.float32)
 
 
 def make_features(cfg, seed):
