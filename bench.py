@@ -265,6 +265,75 @@ def cpu_baseline_draft(cfg, W, feats, budget_s=12.0):
             "sample": f"{n} draft passes ({cfg.name}), fp64 numpy, {dt:.1f} s"}
 
 
+def prefill_flops(cfg):
+    """FLOPs of one prefill pass: 2 per weight per prefix token for every projection of every layer, plus
+    Q.K^T and P.V of every token over all P prefix tokens."""
+    w, F, dh, nq, nkv, P = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.horizon
+    per_layer = (nq + 2 * nkv) * dh * w + w * nq * dh + 3 * F * w
+    return cfg.n_layers * (2 * P * per_layer + 4 * nq * P * P * dh)
+
+
+def bench_prefill(args, cfg, W):
+    """Prefill passes (ae_prefill: embeddings uploaded, one graph replay of the stack over the P prefix
+    tokens, every layer's K/V copied back), wall clock per synchronous call and the device time of the
+    replay, medians over `steps` after `warmup`."""
+    from flow_matching_action_euler_amd import ActionExpert
+    from workload import gen as G
+    ex = ActionExpert(cfg, W)
+    emb = G.make_prefix_embeddings(cfg, 1)
+    for _ in range(max(1, args.warmup)):
+        ex.prefill(emb)
+    wall, gpu = [], []
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        t1 = time.perf_counter()
+        k, v = ex.prefill(emb)
+        wall.append((time.perf_counter() - t1) * 1e3)
+        gpu.append(ex.last_gpu_ms())
+    elapsed = time.perf_counter() - t0
+    assert k.shape[0] == cfg.n_layers
+    gpu_ms = float(np.median(gpu))
+    fl = prefill_flops(cfg)
+    tflops = fl / (gpu_ms * 1e-3) / 1e12
+    result = {
+        "metric": "prefill passes/s (prefix KV cache of every layer from the prefix embeddings)",
+        "value": round(args.steps / elapsed, 2),
+        "unit": "prefill passes/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(float(np.median(wall)), 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if cfg.mlp_dtype == "bf16" else "bf16 (E4M3 MLP weights)",
+        "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix embeddings)",
+        "config": {"workload": cfg.name, "layers": cfg.n_layers, "width": cfg.width,
+                   "heads": f"{cfg.n_q_heads}q/{cfg.n_kv_heads}kv", "head_dim": cfg.head_dim, "mlp_dim": cfg.mlp_dim,
+                   "prefix_tokens": cfg.horizon, "params": cfg.n_params},
+        "gpu_ms_median": round(gpu_ms, 4),
+        "roofline": {"kernel": "whole prefill pass", "bound": "mfma", "achieved": round(tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline_prefill(cfg, emb)
+    ex.close()
+    print(json.dumps(result))
+
+
+def cpu_baseline_prefill(cfg, emb, layers=2):
+    """The oracle's prefill on the host (fp64 numpy) over the first `layers` layers of the stack, scaled
+    to whole passes (the layers have equal shapes and cost)."""
+    from oracle import ae_oracle as O
+    from workload import gen as G
+    sub = cfg.with_(n_layers=layers)
+    Wd = O.dequantize_weights(sub, G.make_weights(sub))
+    t0 = time.perf_counter()
+    O.prefill_kv(sub, Wd, emb)
+    dt = time.perf_counter() - t0
+    return {"value": round(layers / (dt * cfg.n_layers), 4), "unit": "prefill passes/s", "cores": _cores(),
+            "kind": "oracle",
+            "sample": f"{layers} of the {cfg.n_layers} layers over {cfg.horizon} prefix tokens ({cfg.name}), "
+                      f"fp64 numpy, {dt:.1f} s, scaled by {cfg.n_layers}/{layers}"}
+
+
 def cpu_baseline_verify(cfg, W, k, v, budget_s=12.0):
     """The oracle as it stands, timed on this host: verify passes (all flow times) of one draft."""
     from oracle import ae_oracle as O
@@ -319,6 +388,9 @@ def main():
     if cfg.draft:
         torch.cuda.set_device(0)
         return bench_draft(args, cfg, W)
+    if cfg.prefill:
+        torch.cuda.set_device(0)
+        return bench_prefill(args, cfg, W)
     kvs = [G.make_prefix_kv(cfg, cfg.kv_seed + r) for r in range(B)]
     noise = G.make_noise(cfg, batch=B)
     torch.cuda.set_device(0)

@@ -17,7 +17,7 @@ AE_OK = 0
 ERRORS = {-1: "AE_ERR_INVALID_ARG", -2: "AE_ERR_UNSUPPORTED", -3: "AE_ERR_NOT_READY", -4: "AE_ERR_OOM", -5: "AE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async", "ae_round",
-           "ae_draft",
+           "ae_draft", "ae_prefill",
            "ae_destroy", "ae_last_error", "ae_last_gpu_ms", "ae_kernel_times")
 
 
@@ -32,7 +32,7 @@ class ae_config(ctypes.Structure):
         "n_layers", "width", "n_q_heads", "n_kv_heads", "head_dim", "mlp_dim", "action_dim", "horizon",
         "prefix_len", "max_batch", "max_taus")] + [("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float)] + [
         (n, ctypes.c_int) for n in ("weight_dtype", "mlp_dtype", "kv_dtype", "gripper_dim", "time_mode", "qk_norm",
-                                    "draft")]
+                                    "draft", "prefill")]
 
 
 class ae_layer_weights(ctypes.Structure):
@@ -75,6 +75,7 @@ def load_library(path=LIB_PATH):
         "ae_verify_async": (I, [P, I, P, P, P, I, F, P, P, P, P]),
         "ae_round": (I, [P, I, P, P, P, I, F, P, I, P, P, P, P]),
         "ae_draft": (I, [P, P, P]),
+        "ae_prefill": (I, [P, P, P, P]),
         "ae_destroy": (V, [P]),
         "ae_last_error": (ctypes.c_char_p, [P]),
         "ae_last_gpu_ms": (I, [P, ctypes.POINTER(F)]),
@@ -104,7 +105,7 @@ def make_config(cfg):
         prefix_len=cfg.prefix_len, max_batch=cfg.max_batch, max_taus=cfg.max_taus, rope_base=cfg.rope_base,
         rms_eps=cfg.rms_eps, weight_dtype=DTYPES[cfg.weight_dtype], mlp_dtype=DTYPES[cfg.mlp_dtype],
         kv_dtype=DTYPES[cfg.kv_dtype], gripper_dim=cfg.gripper_dim, time_mode=getattr(cfg, "time_mode", 0),
-        qk_norm=getattr(cfg, "qk_norm", 0), draft=getattr(cfg, "draft", 0))
+        qk_norm=getattr(cfg, "qk_norm", 0), draft=getattr(cfg, "draft", 0), prefill=getattr(cfg, "prefill", 0))
 
 
 class ActionExpert:
@@ -210,6 +211,16 @@ class ActionExpert:
         out = np.empty((self.cfg.horizon, self.cfg.action_dim), np.float32)
         self._check(self.lib.ae_draft(self.h, _ptr(features), _ptr(out)))
         return out
+
+    def prefill(self, emb):
+        """Per-layer prefix (K, V) [L][P][n_kv][dh] in kv_dtype storage from embeddings [P][w]."""
+        emb = _c(emb, np.float32)
+        c = self.cfg
+        dt = np.float32 if c.kv_dtype == "f32" else np.uint16
+        k = np.empty((c.n_layers, c.horizon, c.n_kv_heads, c.head_dim), dt)
+        v = np.empty_like(k)
+        self._check(self.lib.ae_prefill(self.h, _ptr(emb), _ptr(k), _ptr(v)))
+        return k, v
 
     def last_gpu_ms(self):
         ms = ctypes.c_float()

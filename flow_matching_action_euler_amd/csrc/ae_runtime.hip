@@ -142,6 +142,9 @@ struct ae_handle {
   // draft model: the queries staged as block input rows, image features and their staging, RoPE of 0..P-1
   float *q_h0 = nullptr, *q_ssp0 = nullptr, *feat = nullptr, *feat_ssp = nullptr, *rope_feat = nullptr;
   void *q_hb0 = nullptr, *feat_hb = nullptr;
+  // prefill stack: every layer's K and V in the cache blocks' layout, [L][n_kv][nbs][32 keys x dh]
+  void *pf_k = nullptr, *pf_v = nullptr;
+  size_t pf_layer_elems = 0;
   struct ModTable {
     float* mod = nullptr;                   // [L][steps][6w]: scale1 shift1 gate1 scale2 shift2 gate2
     float *g1 = nullptr, *g2 = nullptr;     // [L][steps][w]: ln1 (1 + scale1), ln2 (1 + scale2)
@@ -235,7 +238,8 @@ int validate(const ae_config* c, const ae_weights* w) {
       c->mlp_dim % 256 || (c->n_q_heads * c->head_dim) % 256)
     return fail(nullptr, AE_ERR_UNSUPPORTED,
                 "width, mlp_dim and n_q_heads*head_dim must be multiples of 256; head_dim one of 32, 64, 128, 256");
-  if (c->action_dim > 64 || c->horizon > 256) return fail(nullptr, AE_ERR_UNSUPPORTED, "action_dim <= 64 and horizon <= 256");
+  if (c->action_dim > 64 || c->horizon > (c->prefill == 1 ? 1024 : 256))
+    return fail(nullptr, AE_ERR_UNSUPPORTED, "action_dim <= 64 and horizon <= 256 (prefill: <= 1024 tokens)");
   if (c->weight_dtype == AE_FP8_E4M3) return fail(nullptr, AE_ERR_UNSUPPORTED, "fp8 is supported for the MLP only");
   if (c->kv_dtype != c->weight_dtype) return fail(nullptr, AE_ERR_UNSUPPORTED, "kv_dtype must equal weight_dtype");
   if (c->weight_dtype == AE_F32 && c->mlp_dtype != AE_F32)
@@ -243,7 +247,14 @@ int validate(const ae_config* c, const ae_weights* w) {
   if (c->weight_dtype == AE_BF16 && c->mlp_dtype == AE_F32)
     return fail(nullptr, AE_ERR_UNSUPPORTED, "bf16 attention weights need bf16 or fp8 MLP weights");
   if (c->draft != 0 && c->draft != 1) return fail(nullptr, AE_ERR_INVALID_ARG, "draft is 0 or 1");
-  if (c->draft) {
+  if (c->prefill != 0 && c->prefill != 1) return fail(nullptr, AE_ERR_INVALID_ARG, "prefill is 0 or 1");
+  if (c->prefill) {
+    if (c->draft || c->prefix_len != 0 || c->max_batch != 1 || c->max_taus != 0 || c->time_mode || c->qk_norm ||
+        c->weight_dtype != AE_BF16 || c->mlp_dtype == AE_F32)
+      return fail(nullptr, AE_ERR_UNSUPPORTED,
+                  "a prefill stack has prefix_len 0, max_batch 1, max_taus 0, bf16 attention weights, no modulation or QK-norm");
+    if (!w->layers) return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
+  } else if (c->draft) {
     if (c->n_layers != 1 || c->max_batch != 1 || c->max_taus != 0 || c->time_mode || c->qk_norm ||
         c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16 || c->prefix_len < 1)
       return fail(nullptr, AE_ERR_UNSUPPORTED,
@@ -637,7 +648,7 @@ struct StepMod {
 };
 
 int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, int slot0, float dt,
-                     hipStream_t st, Timer* tm, const StepMod* sm = nullptr, bool from_h = false) {
+                     hipStream_t st, Timer* tm, const StepMod* sm = nullptr, bool from_h = false, bool head = true) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim, w = c.width, F = c.mlp_dim;
   const int nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
@@ -704,6 +715,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.trace_id = 0;
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
+    if (c.prefill) {  // this layer's K and V are the cache the expert will read
+      const size_t kes = dtype_size(c.kv_dtype), bytes = h->pf_layer_elems * kes;
+      HIP_TRY(h, hipMemcpyAsync((char*)h->pf_k + l * bytes, h->ks, bytes, hipMemcpyDeviceToDevice, st));
+      HIP_TRY(h, hipMemcpyAsync((char*)h->pf_v + l * bytes, h->vs, bytes, hipMemcpyDeviceToDevice, st));
+    }
     // --- attention over [prefix ; suffix]
     aa.layer_off = (size_t)l * nkv * h->nbp * ATT_KB * dh;
     const dim3 attn_grid(aa.n_split, aa.n_qt, n_seq * nkv);
@@ -756,7 +772,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.S = pick(F / 32, splits().down, n_z).S;
       a.h = h->h; a.hb = h->hb;
       a.gain_next = (l + 1 < c.n_layers) ? (sm ? modp(sm->t->g1, w, l + 1) : h->ln1[l + 1])
-                                         : (sm ? sm->t->gf + (size_t)sm->k * w : h->final_ln);
+                                         : (sm ? sm->t->gf + (size_t)sm->k * w : h->final_ln ? h->final_ln : h->ln1[0]);
       if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 5 * w;
       a.ssp_out = h->ssp_a; a.N = w;
       if ((prefetch_mask() & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
@@ -769,7 +785,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     }
   }
   // --- final norm + action_out_proj (+ Euler update)
-  {
+  if (head) {
     GemmArgs a{};
     a.inv_width = 1.f / (float)w; a.eps = c.rms_eps; a.M = M; a.M_pad = Mp;
     a.part = h->part; a.counters = h->counters;
@@ -931,12 +947,23 @@ int enqueue_draft(ae_handle* h, hipStream_t st, Timer* tm) {
   return enqueue_velocity(h, 1, nullptr, 0, nullptr, 0, 0.f, st, tm, nullptr, true);
 }
 
+// The prefill stack's pass: the embeddings (h->feat) staged as the block input rows (h, hb and the
+// RMS partials), then the blocks with every token attending to every token (the whole prefix is
+// the "suffix" of a prefix-free pass); each layer's K/V is copied out as its QKV kernel writes it.
+int enqueue_prefill(ae_handle* h, hipStream_t st, Timer* tm) {
+  const ae_config& c = h->c;
+  const int w = c.width, H = c.horizon, Mp = (H + TOKG - 1) / TOKG * TOKG;
+  LAUNCH_CHECK(h, "prefill_stage", AE_LAUNCH(stage_rows_kernel, dim3(w / 64, Mp / 64), dim3(256), 0, st, h->feat, H, Mp,
+                                             w, h->ln1[0], h->h, (uint16_t*)h->hb, h->ssp_a));
+  return enqueue_velocity(h, 1, nullptr, 0, nullptr, 0, 0.f, st, tm, nullptr, true, false);
+}
+
 int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
   auto key = std::make_tuple(mode, a, b);
   auto it = h->graphs.find(key);
   if (it != h->graphs.end()) { *out = it->second; return AE_OK; }
   // mode 0: denoise (a steps, b robots on slots 0..b-1); 1: verify (a flow times);
-  // 2: denoise of one robot on prefix slot b (a steps); 3: the draft model's pass
+  // 2: denoise of one robot on prefix slot b (a steps); 3: the draft model's pass; 4: prefill
   float* temb = nullptr;
   if (mode == 0 || mode == 2) {
     int rc = get_temb_steps(h, a, &temb);
@@ -946,6 +973,7 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
   int rc = mode == 0   ? enqueue_denoise(h, b, a, temb, h->stream, nullptr)
            : mode == 2 ? enqueue_denoise(h, 1, a, temb, h->stream, nullptr, b)
            : mode == 3 ? enqueue_draft(h, h->stream, nullptr)
+           : mode == 4 ? enqueue_prefill(h, h->stream, nullptr)
                        : enqueue_verify(h, a, h->stream, nullptr);
   hipGraph_t graph = nullptr;
   hipError_t e = hipStreamEndCapture(h->stream, &graph);
@@ -1009,7 +1037,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
 #define TRY(x) do { int r_ = (x); if (r_) { msg = h->err; ae_destroy(h); return fail(nullptr, r_, msg); } } while (0)
 
   // ---- small weights (row-major, used by the time MLP and in_proj kernels)
-  if (!c.draft) {
+  if (!c.draft && !c.prefill) {
     TRY(upload(h, &h->time_in_w, wts->time_in_w, (size_t)w * w * wes));
     TRY(upload(h, (void**)&h->time_in_b, wts->time_in_b, (size_t)w * 4));
     TRY(upload(h, &h->time_out_w, wts->time_out_w, (size_t)w * w * wes));
@@ -1017,10 +1045,10 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(upload(h, &h->action_in_w, wts->action_in_w, (size_t)w * A * wes));
     TRY(upload(h, (void**)&h->action_in_b, wts->action_in_b, (size_t)w * 4));
   }
-  TRY(upload(h, (void**)&h->action_out_b, wts->action_out_b, (size_t)A * 4));
-  TRY(upload(h, (void**)&h->final_ln, wts->final_ln, (size_t)w * 4));
-  {
-    h->out_tiles = (A + 15) / 16;
+  h->out_tiles = (A + 15) / 16;
+  if (!c.prefill) {  // the head (a prefill stack has none)
+    TRY(upload(h, (void**)&h->action_out_b, wts->action_out_b, (size_t)A * 4));
+    TRY(upload(h, (void**)&h->final_ln, wts->final_ln, (size_t)w * 4));
     std::vector<const unsigned char*> rows(h->out_tiles * 16, nullptr);
     for (int r = 0; r < A; ++r) rows[r] = (const unsigned char*)wts->action_out_w + (size_t)r * w * wes;
     std::vector<unsigned char> buf;
@@ -1202,6 +1230,12 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(upload(h, (void**)&h->rope_feat, cs.data(), cs.size() * 4));
     if (hipGetLastError() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "query staging launch failed"); }
   }
+  if (c.prefill) {  // the embeddings, and every layer's suffix K/V (the cache blocks' layout)
+    TRY(dalloc_t(h, &h->feat, (size_t)H * w));
+    h->pf_layer_elems = (size_t)nkv * h->nbs * ATT_KB * dh;
+    TRY(dalloc(h, &h->pf_k, (size_t)L * h->pf_layer_elems * kes));
+    TRY(dalloc(h, &h->pf_v, (size_t)L * h->pf_layer_elems * kes));
+  }
   if (hipDeviceSynchronize() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "device sync after upload failed"); }
 #undef TRY
   *out = h;
@@ -1260,6 +1294,7 @@ static int check_err_flag(ae_handle* h) {
 static int check_denoise(ae_handle* h, int batch, int steps) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "a draft-model handle runs ae_draft only");
+  if (h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "a prefill handle runs ae_prefill only");
   if (batch < 1 || batch > h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "batch out of range");
   if (steps < 1 || steps > 1000) return fail(h, AE_ERR_INVALID_ARG, "steps out of range (1..1000)");
   for (int b = 0; b < batch; ++b)
@@ -1311,6 +1346,7 @@ static int check_verify(ae_handle* h, int slot, int n_tau) {
   if (h->c.max_taus < 1) return fail(h, AE_ERR_UNSUPPORTED, "handle created with max_taus = 0");
   if (h->c.time_mode) return fail(h, AE_ERR_UNSUPPORTED, "verification of a time-modulated expert is not built");
   if (h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "a draft-model handle runs ae_draft only");
+  if (h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "a prefill handle runs ae_prefill only");
   if (n_tau < 1 || n_tau > h->c.max_taus) return fail(h, AE_ERR_INVALID_ARG, "n_tau out of range");
   if (slot < 0 || slot >= h->c.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
   if (!h->slot_ready[slot]) return fail(h, AE_ERR_NOT_READY, "prefix slot not loaded");
@@ -1453,6 +1489,46 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
   if (rc) return rc;
   h->slot_ready[0] = 1;
   memcpy(chunk_out, tmp.data(), bytes);
+  return AE_OK;
+}
+
+int ae_prefill(ae_handle* h, const float* emb, void* k_out, void* v_out) {
+  if (!h) return AE_ERR_INVALID_ARG;
+  if (!h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "not a prefill handle (ae_config.prefill = 0)");
+  if (!emb || !k_out || !v_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  hipGraphExec_t g;
+  int rc = get_graph(h, 4, 0, 0, &g);
+  if (rc) return rc;
+  const ae_config& c = h->c;
+  const int L = c.n_layers, P = c.horizon, nkv = c.n_kv_heads, dh = c.head_dim, nkb = dh / 32, nbs = h->nbs;
+  const size_t es = dtype_size(c.kv_dtype), all = (size_t)L * h->pf_layer_elems * es;
+  HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)P * c.width * 4, hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(g, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  std::vector<unsigned char> kp(all), vp(all);
+  HIP_TRY(h, hipMemcpyAsync(kp.data(), h->pf_k, all, hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipMemcpyAsync(vp.data(), h->pf_v, all, hipMemcpyDeviceToHost, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  rc = check_err_flag(h);
+  if (rc) return rc;
+  // from the cache blocks' fragment order back to [L][P][n_kv][dh] (the inverse of ae_load_prefix_kv)
+  unsigned char* ko = (unsigned char*)k_out;
+  unsigned char* vo = (unsigned char*)v_out;
+  for (int l = 0; l < L; ++l)
+    for (int j = 0; j < P; ++j)
+      for (int g2 = 0; g2 < nkv; ++g2) {
+        const size_t blk = (size_t)l * h->pf_layer_elems + ((size_t)g2 * nbs + j / 32) * 32 * dh;
+        const int kk = j % 32, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
+        const size_t drow = (((size_t)l * P + j) * nkv + g2) * dh;
+        for (int d = 0; d < dh; ++d) {
+          const size_t kidx = blk + ((size_t)(kt * nkb + d / 32) * 64 + ((d % 32) / 8) * 16 + m) * 8 + (d & 7);
+          const size_t vidx = blk + ((size_t)(d / 16) * 64 + (kk / 8) * 16 + (d & 15)) * 8 + (kk & 7);
+          memcpy(ko + (drow + d) * es, &kp[kidx * es], es);
+          memcpy(vo + (drow + d) * es, &vp[vidx * es], es);
+        }
+      }
   return AE_OK;
 }
 

@@ -92,6 +92,10 @@ typedef struct ae_config {
                        current image features): n_layers 1, prefix_len = image tokens, max_batch 1,
                        max_taus 0, time_mode 0, qk_norm 0, bf16; the time MLP and action_in weights
                        are unused (may be NULL), ae_weights.queries is required */
+  int prefill;      /* 1: a prefix-prefill stack for ae_prefill ("DM0.5" guide, section 5.1: the
+                       prefix is encoded once into the per-layer KV cache): horizon = prefix tokens
+                       (<= 1024), prefix_len 0, max_batch 1, max_taus 0, bf16 attention weights
+                       (MLP bf16 or fp8), no modulation or QK-norm; only the decoder blocks are used */
 } ae_config;
 
 /* One decoder block. wq [n_q*dh][w], wk/wv [n_kv*dh][w], wo [w][n_q*dh],
@@ -227,6 +231,15 @@ int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_veri
  * Synchronous; ae_last_gpu_ms covers the device pass (features already uploaded). The first call
  * captures the graph. AE_ERR_UNSUPPORTED on a handle that is not a draft model. */
 int ae_draft(ae_handle* h, const float* features, float* chunk_out);
+
+/* The per-layer prefix KV cache from the prefix token embeddings, on a handle created with
+ * prefill = 1 ("DM0.5" guide, section 5.1). emb: host [horizon][width] fp32. The handle's
+ * decoder blocks run over the horizon tokens with every token attending to every token and RoPE
+ * at positions 0..horizon-1. k_out, v_out: host [n_layers][horizon][n_kv_heads][head_dim] in
+ * kv_dtype, K rotated -- the layout and convention ae_load_prefix_kv takes, for an expert whose
+ * n_layers, n_kv_heads and head_dim match. Synchronous; ae_last_gpu_ms covers the device pass.
+ * AE_ERR_UNSUPPORTED on a handle that is not a prefill stack. */
+int ae_prefill(ae_handle* h, const float* emb, void* k_out, void* v_out);
 
 /* Free every device resource of the handle. NULL is a no-op. */
 void ae_destroy(ae_handle* h);

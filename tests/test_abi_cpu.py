@@ -25,7 +25,7 @@ def _declared():
 def test_library_exports_every_declared_function():
     lib = B.load_library()
     names = _declared()
-    assert len(names) == 12
+    assert len(names) == 13
     assert sorted(B.EXPORTS) == names
     for n in names:
         assert hasattr(lib, n), n
@@ -136,3 +136,14 @@ def test_bench_work_figures_match_the_closed_forms():
     kv = 2 * 816 * 256 * 2
     assert bench.step_bytes(C.PI0, 1) == 18 * (2 * per_layer + kv) + 2 * 2 * 1024 * 32
     assert bench.step_bytes(C.PI0, 16) - bench.step_bytes(C.PI0, 1) == 15 * 18 * kv
+
+
+def test_prefill_flops_match_the_closed_form():
+    """The 2B-class prefill stack: 110.1 M weights per layer (qkv 2560 x 2048, o 2048 x 2048, gate/up/down
+    3 x 16384 x 2048), 2 FLOPs per weight per token over 816 tokens, Q.K^T and P.V of 8 x 816 query rows
+    over 816 keys x 256; the weights are the stack's parameters less its two norm gains per layer."""
+    import bench
+    per_layer = 2560 * 2048 + 2048 * 2048 + 3 * 16384 * 2048
+    assert per_layer == 110_100_480
+    assert per_layer == C.PREFILL.n_params // 18 - 2 * 2048
+    assert bench.prefill_flops(C.PREFILL) == 18 * (2 * 816 * per_layer + 4 * 8 * 816 * 816 * 256)

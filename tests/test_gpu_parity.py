@@ -270,6 +270,73 @@ def test_draft_entry_rejects_an_expert_handle():
     ex.close()
 
 
+# ------------------------------------------------------------------ prefix prefill
+
+SMALL_PREFILL = C.PREFILL.with_(name="small_prefill", n_layers=2, width=256, n_q_heads=4, n_kv_heads=2, head_dim=64,
+                                mlp_dim=512, horizon=100)
+
+
+def _prefill_vs_oracle(cfg):
+    W = G.make_weights(cfg)
+    Wd = O.dequantize_weights(cfg, W)
+    ex = ActionExpert(cfg, W)
+    emb = G.make_prefix_embeddings(cfg, 11)
+    k, v = ex.prefill(emb)
+    k_o, v_o = O.prefill_kv(cfg, Wd, emb)
+    kd, vd = O.decode_kv(cfg, k, v)
+    for l in range(cfg.n_layers):
+        ek, ev = rel_err(kd[l], k_o[l]), rel_err(vd[l], v_o[l])
+        print(f"{cfg.name} layer {l}: K rel_err={ek:.3e} V rel_err={ev:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+        assert ek <= tol_for(cfg) and ev <= tol_for(cfg), (l, ek, ev)
+    ex.close()
+    return k, v
+
+
+def test_prefill_matches_oracle_small():
+    """100 prefix tokens (a partial last key block), 2 kv heads, E4M3 MLP."""
+    _prefill_vs_oracle(SMALL_PREFILL)
+
+
+def test_prefill_full_width_first_two_layers():
+    """The 2B-class stack's own per-layer shapes (width 2048, 8q/1kv x 256, E4M3 MLP 16384) over the 816
+    prefix tokens; the first two layers of the 18 (a stack's first layers' K/V do not depend on the rest)."""
+    _prefill_vs_oracle(C.PREFILL.with_(n_layers=2))
+
+
+def test_expert_denoises_on_a_prefilled_cache():
+    """The prefill output in ae_load_prefix_kv's format: an expert with the stack's kv heads, head_dim and
+    depth denoises on it as the oracle does on the same cache."""
+    pcfg = SMALL_PREFILL.with_(mlp_dtype="bf16")
+    W = G.make_weights(pcfg)
+    ex = ActionExpert(pcfg, W)
+    k, v = ex.prefill(G.make_prefix_embeddings(pcfg, 12))
+    ex.close()
+    cfg = SMALL_BF16  # 2 layers, 2 kv heads x 64, prefix 100
+    case = Case(cfg)
+    exp = ActionExpert(cfg, case.W)
+    exp.load_prefix_kv(0, k, v)
+    noise = case.noise(1)
+    got = exp.denoise(noise, 3)
+    kk, vv = O.decode_kv(cfg, k, v)
+    ref = O.denoise(cfg, case.Wd, kk, vv, noise[0].astype(np.float64), 3)
+    assert rel_err(got[0], ref) <= tol_for(cfg)
+    exp.close()
+
+
+def test_prefill_entry_rejects_other_handles():
+    case = Case(SMALL_BF16)
+    ex = _expert(case)
+    with pytest.raises(AEError) as e:
+        ex.prefill(np.zeros((SMALL_BF16.horizon, SMALL_BF16.width), np.float32))
+    assert e.value.code == -2
+    ex.close()
+    pf = ActionExpert(SMALL_PREFILL, G.make_weights(SMALL_PREFILL))
+    with pytest.raises(AEError) as e:
+        pf.denoise(np.zeros((1, SMALL_PREFILL.horizon, SMALL_PREFILL.action_dim), np.float32), 1)
+    assert e.value.code == -2
+    pf.close()
+
+
 # ------------------------------------------------------------------ dual-path round
 
 def test_dual_path_round_matches_oracle():
