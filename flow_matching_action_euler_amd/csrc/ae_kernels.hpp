@@ -806,7 +806,9 @@ constexpr void (*gemm_entry())(GemmArgs) {
 // k-group wk; with WK > 1 the partial sub-tiles meet in LDS and each wave finishes 1/WK of the
 // tiles. Operands are staged in LDS as whole 1 KB fragments in the packed order (lane-major, so
 // fragment reads are conflict-free), double-buffered: the next chunk's global loads are in flight
-// in registers while the MFMAs consume the current chunk. bf16 weights and activations.
+// in registers while the MFMAs consume the current chunk. bf16 activations; bf16 weights, or E4M3
+// weights (the MLP roles) widened to bf16 (exact) on their way into LDS and scaled per output
+// channel in the epilogue.
 template <int WN, int WM, int WK>
 struct TileCfg {
   static_assert(WN * WM * WK == GW, "8 waves");
@@ -823,11 +825,16 @@ struct TileCfg {
   static constexpr size_t LDS = STAGE + (size_t)MT * 16 * 4 + GTHREADS * 4;
   static_assert(NA % GW == 0 && NB % GW == 0 && 2 * CHUNK <= 128 * 1024, "chunk shape");
 };
-constexpr int TILED_MAX_GIN = 64;  // RMS partial groups the prologue reads (width <= 1024)
+constexpr int TILED_MAX_GIN = 128;  // RMS partial groups the prologue reads (width <= 2048)
+template <int WT> struct TiledWReg { typedef i32x4 T; };   // one lane's share of a weight fragment
+template <> struct TiledWReg<WT_FP8> { typedef i32x2 T; };
 
-template <int EPI, int WN, int WM, int WK>
+template <int EPI, int WN, int WM, int WK, int WT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_tiled_kernel(GemmArgs a) {
   typedef TileCfg<WN, WM, WK> C;
+  typedef typename TiledWReg<WT>::T WR;
+  static_assert(WT == WT_BF16 || (WT == WT_FP8 && EPI != EPI_QKV), "E4M3 weights: MLP roles");
+  constexpr int LW = C::NA / GW, LX = C::NB / GW;  // weight / activation loads per thread
   extern __shared__ __attribute__((aligned(16))) float smem[];
   char* stage = (char*)smem;                                  // [2][CHUNK] operands; then partials
   float* inv_rms = (float*)(stage + C::STAGE);                // [TM]
@@ -846,27 +853,36 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 
   // fragment f of chunk c: weights [ct][kk] for f < NA, then activations [kk][tt]; the token
   // tiles past the buffer's rows read its last tile (their outputs are never stored)
-  const i32x4* wsrc = (const i32x4*)a.w;
+  const WR* wsrc = (const WR*)a.w;
   const i32x4* xsrc = (const i32x4*)a.x;
-  // three chunks in flight in registers (a vector type: arrays of HIP's uint4 structs stayed in
-  // scratch memory); load i of a thread is fragment wave + 8 i, weights for i < NA / 8
-  i32x4 r0[C::LOADS], r1[C::LOADS], r2[C::LOADS];
-  auto gload = [&](i32x4 (&r)[C::LOADS], int c) __attribute__((always_inline)) {
+  // three chunks in flight in registers (vector types: arrays of HIP's uint4 structs stayed in
+  // scratch memory); weight load i of a thread is fragment wave + 8 i, activation load i fragment
+  // NA + wave + 8 i
+  WR w0[LW], w1[LW], w2[LW];
+  i32x4 x0[LX], x1[LX], x2[LX];
+  auto gload = [&](WR (&rw)[LW], i32x4 (&rx)[LX], int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < C::NA / GW; ++i) {
+    for (int i = 0; i < LW; ++i) {
       const int f = wave + GW * i;
-      r[i] = wsrc[((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane];
+      rw[i] = wsrc[((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane];
     }
 #pragma unroll
-    for (int i = C::NA / GW; i < C::LOADS; ++i) {
-      const int f = wave + GW * i - C::NA;
-      r[i] = xsrc[((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane];
+    for (int i = 0; i < LX; ++i) {
+      const int f = wave + GW * i;
+      rx[i] = xsrc[((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane];
     }
   };
-  auto lstore = [&](const i32x4 (&r)[C::LOADS], int b) __attribute__((always_inline)) {
+  auto lstore = [&](const WR (&rw)[LW], const i32x4 (&rx)[LX], int b) __attribute__((always_inline)) {
+    char* dst = stage + b * C::CHUNK + lane * 16;
 #pragma unroll
-    for (int i = 0; i < C::LOADS; ++i)
-      *(i32x4*)(stage + b * C::CHUNK + (size_t)(wave + GW * i) * 1024 + lane * 16) = r[i];
+    for (int i = 0; i < LW; ++i) {
+      if constexpr (WT == WT_FP8)
+        *(bf16x8*)(dst + (size_t)(wave + GW * i) * 1024) = fp8x8_to_bf16x8(make_uint2(rw[i][0], rw[i][1]));
+      else
+        *(i32x4*)(dst + (size_t)(wave + GW * i) * 1024) = rw[i];
+    }
+#pragma unroll
+    for (int i = 0; i < LX; ++i) *(i32x4*)(dst + (size_t)(C::NA + wave + GW * i) * 1024) = rx[i];
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -896,23 +912,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   };
 
   const int nc = KB / C::CK;
-  gload(r0, 0);
-  gload(r1, min(1, nc - 1));
-  gload(r2, min(2, nc - 1));
+  gload(w0, x0, 0);
+  gload(w1, x1, min(1, nc - 1));
+  gload(w2, x2, min(2, nc - 1));
   // 1/rms of this tile's tokens from the producer's partial sums of h^2 (QKV, gate/up):
   // thread -> token t % TM, partial groups t / TM + GPT * q; clamped loads, masked sums
   if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
     const int tl = threadIdx.x % (C::MT * 16), g0 = threadIdx.x / (C::MT * 16);
     const float* sp = a.ssp_in + min(tt0 * 16 + tl, a.M_pad - 1);
-    float sv[C::NRD];
-#pragma unroll
-    for (int q = 0; q < C::NRD; ++q) sv[q] = sp[(size_t)min(g0 + C::GPT * q, a.g_in - 1) * a.M_pad];
     float sum = 0.f;
+    for (int q0 = 0; q0 < a.g_in; q0 += C::GPT * C::NRD) {  // 64 groups a pass (width 1024 per pass)
+      float sv[C::NRD];
 #pragma unroll
-    for (int q = 0; q < C::NRD; ++q) sum += g0 + C::GPT * q < a.g_in ? sv[q] : 0.f;
+      for (int q = 0; q < C::NRD; ++q) sv[q] = sp[(size_t)min(q0 + g0 + C::GPT * q, a.g_in - 1) * a.M_pad];
+#pragma unroll
+      for (int q = 0; q < C::NRD; ++q) sum += q0 + g0 + C::GPT * q < a.g_in ? sv[q] : 0.f;
+    }
     ssq[threadIdx.x] = sum;
   }
-  lstore(r0, 0);
+  lstore(w0, x0, 0);
   __syncthreads();
   if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
     if (threadIdx.x < C::MT * 16) {
@@ -928,18 +946,19 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // what they store lands in a buffer nobody reads again): the compiler then sees the same loads
   // in flight on every path and waits only for the set it stores (a conditional load made it
   // wait for all of them).
-  auto step = [&](int c, i32x4 (&rf)[C::LOADS], const i32x4 (&rn)[C::LOADS]) __attribute__((always_inline)) {
-    gload(rf, min(c + 3, nc - 1));
+  auto step = [&](int c, WR (&wf)[LW], i32x4 (&xf)[LX], const WR (&wn_)[LW], const i32x4 (&xn)[LX])
+      __attribute__((always_inline)) {
+    gload(wf, xf, min(c + 3, nc - 1));
     __builtin_amdgcn_sched_barrier(0);  // the loads in flight before the MFMAs
     if (c < nc) compute(c & 1);
     __builtin_amdgcn_sched_barrier(0);
-    lstore(rn, (c + 1) & 1);
+    lstore(wn_, xn, (c + 1) & 1);
     __syncthreads();
   };
   for (int c = 0; c < nc; c += 3) {
-    step(c, r0, r1);
-    step(c + 1, r1, r2);
-    step(c + 2, r2, r0);
+    step(c, w0, x0, w1, x1);
+    step(c + 1, w1, x1, w2, x2);
+    step(c + 2, w2, x2, w0, x0);
   }
 
   // partial sub-tiles of the WK k-groups meet in LDS: [wave][tile q = 4 i + j][lane][4]
@@ -975,7 +994,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 #pragma unroll
     for (int u = 0; u < 8 / WK; ++u) {
       const int pq = wk + WK * u, p = pq >> 2, j = pq & 3;
-      const f32x4 gv = tile_sum(2 * p, j), uv = tile_sum(2 * p + 1, j);
+      f32x4 gv = tile_sum(2 * p, j), uv = tile_sum(2 * p + 1, j);
+      if constexpr (WT == WT_FP8) {  // per-channel scales of the gate and up rows
+        const int ch = (ct0 + wn * 4 + 2 * p) * 16 + cq * 4;
+        gv *= *(const f32x4*)(a.wscale + ch);
+        uv *= *(const f32x4*)(a.wscale + ch + 16);
+      }
       const int tl = (wm * 4 + j) * 16 + tq, tok = tt0 * 16 + tl;
       const float ir = inv_rms[tl];
       const int f = ((ct0 + wn * 4) / 2 + p) * 16 + cq * 4;
@@ -1003,6 +1027,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         hv[u] = *(const float4*)(a.h + (size_t)min(tok, a.M - 1) * a.N + n);
         gv[u] = *(const float4*)(a.gain_next + n);
         val[u] = tile_sum(i, j);
+        if constexpr (WT == WT_FP8) val[u] *= *(const f32x4*)(a.wscale + n);  // per-channel scales
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {

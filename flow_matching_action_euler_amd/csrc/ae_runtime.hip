@@ -344,22 +344,22 @@ static_assert(tiled_nt(1) == TiledShape<1>::C::NT && tiled_mt(1) == TiledShape<1
 static_assert(tiled_nt(2) == TiledShape<2>::C::NT && tiled_mt(2) == TiledShape<2>::C::MT, "shape 2");
 static_assert(tiled_nt(3) == TiledShape<3>::C::NT && tiled_mt(3) == TiledShape<3>::C::MT, "shape 3");
 
-template <int EPI, int WN, int WM, int WK>
+template <int EPI, int WT, int WN, int WM, int WK>
 hipError_t launch_tiled_k(const GemmArgs& a, hipStream_t st, bool set_attr) {
   typedef TileCfg<WN, WM, WK> C;
   if (set_attr)
-    return hipFuncSetAttribute((const void*)gemm_tiled_kernel<EPI, WN, WM, WK>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                               (int)C::LDS);
-  AE_LAUNCH((gemm_tiled_kernel<EPI, WN, WM, WK>), dim3(a.tn_blocks * a.tm_blocks), dim3(GTHREADS), C::LDS, st, a);
+    return hipFuncSetAttribute((const void*)gemm_tiled_kernel<EPI, WN, WM, WK, WT>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::LDS);
+  AE_LAUNCH((gemm_tiled_kernel<EPI, WN, WM, WK, WT>), dim3(a.tn_blocks * a.tm_blocks), dim3(GTHREADS), C::LDS, st, a);
   return hipGetLastError();
 }
-template <int EPI>
+template <int EPI, int WT = WT_BF16>
 hipError_t launch_tiled(int shape, const GemmArgs& a, hipStream_t st, bool set_attr) {
   switch (shape) {
-    case 0: return launch_tiled_k<EPI, 4, 2, 1>(a, st, set_attr);
-    case 1: return launch_tiled_k<EPI, 2, 2, 2>(a, st, set_attr);
-    case 2: return launch_tiled_k<EPI, 2, 1, 4>(a, st, set_attr);
-    default: return launch_tiled_k<EPI, 1, 1, 8>(a, st, set_attr);
+    case 0: return launch_tiled_k<EPI, WT, 4, 2, 1>(a, st, set_attr);
+    case 1: return launch_tiled_k<EPI, WT, 2, 2, 2>(a, st, set_attr);
+    case 2: return launch_tiled_k<EPI, WT, 2, 1, 4>(a, st, set_attr);
+    default: return launch_tiled_k<EPI, WT, 1, 1, 8>(a, st, set_attr);
   }
 }
 hipError_t set_tiled_attrs() {
@@ -369,6 +369,8 @@ hipError_t set_tiled_attrs() {
     e = launch_tiled<EPI_QKV>(sh, a, nullptr, true);
     if (e == hipSuccess) e = launch_tiled<EPI_RESID>(sh, a, nullptr, true);
     if (e == hipSuccess) e = launch_tiled<EPI_GEGLU>(sh, a, nullptr, true);
+    if (e == hipSuccess) e = launch_tiled<EPI_RESID, WT_FP8>(sh, a, nullptr, true);
+    if (e == hipSuccess) e = launch_tiled<EPI_GEGLU, WT_FP8>(sh, a, nullptr, true);
   }
   return e;
 }
@@ -514,8 +516,9 @@ int poll_delay() {
 }
 
 // Token-tiled shape for a GEMM role over n_tiles 16-channel tiles, K inputs and M tokens, or
-// -1 for the kernel above: one token group, fp32 or fp8 operands, an RMS input wider than the
-// tiled prologue reads, no shape dividing the tiles and k-blocks, or the role switched off
+// -1 for the kernel above: one token group, fp32 operands, E4M3 weights outside the MLP roles,
+// an RMS input wider than the tiled prologue reads, no shape dividing the tiles and k-blocks, or
+// the role switched off
 // (AE_TILED, a bit per role; AE_TILED_SHAPE forces one shape wherever it fits). Among the
 // shapes that fit, the one with the least modelled time:
 // rounds of workgroups over the compute units x (the larger of its MFMA clocks and its operand
@@ -523,7 +526,8 @@ int poll_delay() {
 // under half the compute units is not taken (measured: slower than the kernel above there).
 int tiled_shape(const ae_handle* h, int role, int n_tiles, int K, int M, int Mp, int* tn_blocks, int* tm_blocks) {
   if (role == R_OUT_PROJ || !((h->tiled_roles >> role) & 1) || Mp / TOKG < 2 || h->n_cu <= 0) return -1;
-  if (h->at != AT_BF16 || ((role == R_GATE_UP || role == R_DOWN) ? h->mt : h->wt) != WT_BF16) return -1;
+  const int wt = (role == R_GATE_UP || role == R_DOWN) ? h->mt : h->wt;
+  if (h->at != AT_BF16 || (wt != WT_BF16 && !(wt == WT_FP8 && (role == R_GATE_UP || role == R_DOWN)))) return -1;
   if (h->c.time_mode || h->c.qk_norm) return -1;  // its epilogues have no modulation or QK-norm
   if ((role == R_QKV_ROPE || role == R_GATE_UP) && h->c.width / 16 > TILED_MAX_GIN) return -1;
   const int tok_tiles = (M + 15) / 16;
@@ -555,10 +559,13 @@ struct Dispatch {
       const int nt = role == R_GATE_UP ? 2 : 1;
       const int sh = tiled_shape(h, role, n_groups * nt, a.K, a.M, a.M_pad, &a.tn_blocks, &a.tm_blocks);
       if (sh >= 0) {
+        const bool fp8 = (role == R_GATE_UP || role == R_DOWN) && h->mt == WT_FP8;
         switch (role) {
           case R_QKV_ROPE: return launch_tiled<EPI_QKV>(sh, a, st, false);
-          case R_GATE_UP: return launch_tiled<EPI_GEGLU>(sh, a, st, false);
-          default: return launch_tiled<EPI_RESID>(sh, a, st, false);
+          case R_GATE_UP: return fp8 ? launch_tiled<EPI_GEGLU, WT_FP8>(sh, a, st, false)
+                                     : launch_tiled<EPI_GEGLU>(sh, a, st, false);
+          default: return fp8 && role == R_DOWN ? launch_tiled<EPI_RESID, WT_FP8>(sh, a, st, false)
+                                                : launch_tiled<EPI_RESID>(sh, a, st, false);
         }
       }
     }
@@ -709,16 +716,16 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
         a.pf.base = (const char*)h->kcache + off; a.pf.base2 = (const char*)h->vcache + off;
       }
       a.q_out = h->q; a.k_out = h->ks; a.v_out = h->vs; a.n_qt = h->n_qt; a.nbs = h->nbs; a.rope_cs = h->rope_cs;
+      if (c.prefill) {  // this layer's K and V are written straight into the stack's output cache
+        const size_t off = l * h->pf_layer_elems * dtype_size(c.kv_dtype);
+        a.k_out = (char*)h->pf_k + off; a.v_out = (char*)h->pf_v + off;
+        aa.ks = a.k_out; aa.vs = a.v_out;
+      }
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
       if (sm) a.shift_bias = modp(sm->t->bqkv, nqkv, l);
       if (c.qk_norm) { a.qk_gain = h->qk_gain[l]; a.qk_ssp = h->qk_ssp; }
       a.trace_id = 0;
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
-    }
-    if (c.prefill) {  // this layer's K and V are the cache the expert will read
-      const size_t kes = dtype_size(c.kv_dtype), bytes = h->pf_layer_elems * kes;
-      HIP_TRY(h, hipMemcpyAsync((char*)h->pf_k + l * bytes, h->ks, bytes, hipMemcpyDeviceToDevice, st));
-      HIP_TRY(h, hipMemcpyAsync((char*)h->pf_v + l * bytes, h->vs, bytes, hipMemcpyDeviceToDevice, st));
     }
     // --- attention over [prefix ; suffix]
     aa.layer_off = (size_t)l * nkv * h->nbp * ATT_KB * dh;

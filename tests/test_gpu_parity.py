@@ -394,6 +394,25 @@ def test_tiled_gemm_denoise_matches_oracle(shape, monkeypatch):
     ex.close()
 
 
+SMALL_FP8_B7 = SMALL_FP8.with_(name="small_fp8_b7", max_batch=7)
+
+
+@pytest.mark.parametrize("shape", [0, 1, 2, 3], ids=lambda s: f"shape{s}")
+def test_tiled_gemm_fp8_mlp_denoise_matches_oracle(shape, monkeypatch):
+    """E4M3 gate/up and down weights in the token-tiled kernel (widened to bf16 in LDS, scaled per
+    output channel in the epilogue), every tile shape, 7 robots = 140 tokens."""
+    monkeypatch.setenv("AE_TILED_SHAPE", str(shape))
+    case = Case(SMALL_FP8_B7)
+    ex = _expert(case)
+    noise = case.noise(7)
+    got = ex.denoise(noise, 2)
+    ref = case.oracle_denoise(noise, 2)
+    err = rel_err(got, ref)
+    print(f"tiled fp8 shape={shape} rel_err={err:.3e}")
+    assert err <= tol_for(SMALL_FP8_B7), err
+    ex.close()
+
+
 def test_tiled_gemm_verify_matches_oracle(monkeypatch):
     """8 flow times x 20 rows = 160 tokens in one verification pass (token-tiled GEMMs)."""
     cfg = SMALL_BF16.with_(name="small_bf16_t8", max_taus=8)
