@@ -17,7 +17,7 @@ AE_OK = 0
 ERRORS = {-1: "AE_ERR_INVALID_ARG", -2: "AE_ERR_UNSUPPORTED", -3: "AE_ERR_NOT_READY", -4: "AE_ERR_OOM", -5: "AE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
 EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async", "ae_round",
-           "ae_draft", "ae_prefill",
+           "ae_draft", "ae_prefill", "ae_prefill_to_slot",
            "ae_destroy", "ae_last_error", "ae_last_gpu_ms", "ae_kernel_times")
 
 
@@ -76,6 +76,7 @@ def load_library(path=LIB_PATH):
         "ae_round": (I, [P, I, P, P, P, I, F, P, I, P, P, P, P]),
         "ae_draft": (I, [P, P, P]),
         "ae_prefill": (I, [P, P, P, P]),
+        "ae_prefill_to_slot": (I, [P, P, P, I]),
         "ae_destroy": (V, [P]),
         "ae_last_error": (ctypes.c_char_p, [P]),
         "ae_last_gpu_ms": (I, [P, ctypes.POINTER(F)]),
@@ -221,6 +222,12 @@ class ActionExpert:
         v = np.empty_like(k)
         self._check(self.lib.ae_prefill(self.h, _ptr(emb), _ptr(k), _ptr(v)))
         return k, v
+
+    def prefill_to_slot(self, emb, expert, slot):
+        """Run this prefill stack over embeddings [P][w] and copy every layer's K/V on the device into
+        prefix slot `slot` of the expert handle `expert` (an ActionExpert)."""
+        emb = _c(emb, np.float32)
+        self._check(self.lib.ae_prefill_to_slot(self.h, _ptr(emb), expert.h, slot))
 
     def last_gpu_ms(self):
         ms = ctypes.c_float()

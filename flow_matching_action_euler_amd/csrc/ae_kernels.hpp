@@ -798,23 +798,24 @@ constexpr void (*gemm_entry())(GemmArgs) {
 
 // ------------------------------------------------------------------ GEMM, many tokens
 
-// For a few hundred tokens and more (verification passes, batched robots) a workgroup owns an
-// output tile of TN = 64*WN channels x TM = 64*WM tokens, so that each operand byte it brings in
-// feeds TM (weights) or TN (activations) outputs; the kernel above re-reads every activation in
-// each 16- or 32-channel group. The 8 waves are WN x WM x WK: wave (wn, wm, wk) accumulates the
-// 64 x 64 sub-tile (wn, wm) (4 x 4 MFMA tiles) over the k-blocks of each chunk that belong to its
-// k-group wk; with WK > 1 the partial sub-tiles meet in LDS and each wave finishes 1/WK of the
-// tiles. Operands are staged in LDS as whole 1 KB fragments in the packed order (lane-major, so
-// fragment reads are conflict-free), double-buffered: the next chunk's global loads are in flight
-// in registers while the MFMAs consume the current chunk. bf16 activations; bf16 weights, or E4M3
-// weights (the MLP roles) widened to bf16 (exact) on their way into LDS and scaled per output
-// channel in the epilogue.
+// For a few hundred tokens and more (verification passes, batched robots, prefill) a workgroup
+// owns an output tile of TN = 64*WN channels x TM = 64*WM tokens, so that each operand byte it
+// brings in feeds TM (weights) or TN (activations) outputs; the kernel above re-reads every
+// activation in each 16- or 32-channel group. The 8 waves are WN x WM x WK: wave (wn, wm, wk)
+// accumulates the 64 x 64 sub-tile (wn, wm) (4 x 4 MFMA tiles) over the k-blocks of its k-group
+// wk (one k-block of each chunk); with WK > 1 the partial sub-tiles meet in LDS and each wave
+// finishes 1/WK of the tiles. Operands are staged in LDS as whole 1 KB fragments in the packed
+// order (lane-major, so fragment reads are conflict-free) in two buffers; each wave holds the
+// fragments of two chunks in registers, so the MFMAs of one chunk run while the next chunk's
+// fragments are read and the one after is stored (measured on a stand-alone step: the LDS reads
+// hide completely under the MFMAs, the per-step barrier costs ~20% and the LDS writes ~50%).
+// bf16 activations; bf16 weights, or E4M3 weights (the MLP roles) widened to bf16 (exact) on
+// their way into LDS and scaled per output channel in the epilogue.
 template <int WN, int WM, int WK>
 struct TileCfg {
   static_assert(WN * WM * WK == GW, "8 waves");
   static constexpr int NT = 4 * WN, MT = 4 * WM;                   // 16-channel, 16-token tiles
-  static constexpr int KPT = 64 / ((NT + MT) * WK) >= 2 ? 2 : 1;  // k-blocks per wave per chunk
-  static constexpr int CK = WK * KPT;                              // k-blocks per chunk
+  static constexpr int CK = WK;                                    // k-blocks per chunk: one per k-group
   static constexpr int NA = NT * CK, NB = MT * CK;                 // fragments per chunk
   static constexpr int LOADS = (NA + NB) / GW;                     // 16-byte loads per thread
   static constexpr size_t CHUNK = (size_t)(NA + NB) * 1024;
@@ -855,11 +856,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // tiles past the buffer's rows read its last tile (their outputs are never stored)
   const WR* wsrc = (const WR*)a.w;
   const i32x4* xsrc = (const i32x4*)a.x;
-  // three chunks in flight in registers (vector types: arrays of HIP's uint4 structs stayed in
+  // two chunks in flight in registers (vector types: arrays of HIP's uint4 structs stayed in
   // scratch memory); weight load i of a thread is fragment wave + 8 i, activation load i fragment
   // NA + wave + 8 i
-  WR w0[LW], w1[LW], w2[LW];
-  i32x4 x0[LX], x1[LX], x2[LX];
+  WR w0[LW], w1[LW];
+  i32x4 x0[LX], x1[LX];
   auto gload = [&](WR (&rw)[LW], i32x4 (&rx)[LX], int c) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < LW; ++i) {
@@ -889,32 +890,25 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // every fragment of the chunk is read before the first MFMA (LDS returns in order, so the
-  // MFMAs of k-block 0 wait only for their own fragments)
-  auto compute = [&](int b) __attribute__((always_inline)) {
+
+  // fragments of this wave's k-block of the chunk in LDS buffer b, and their 16 MFMAs
+  auto rd = [&](bf16x8 (&af)[4], bf16x8 (&bf)[4], int b) __attribute__((always_inline)) {
     const char* buf = stage + b * C::CHUNK + lane * 16;
-    bf16x8 af[C::KPT][4], bfr[C::KPT][4];
 #pragma unroll
-    for (int kp = 0; kp < C::KPT; ++kp) {
-      const int kk = wk * C::KPT + kp;
+    for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(buf + (size_t)((wn * 4 + i) * C::CK + wk) * 1024);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[kp][i] = *(const bf16x8*)(buf + (size_t)((wn * 4 + i) * C::CK + kk) * 1024);
+    for (int j = 0; j < 4; ++j) bf[j] = *(const bf16x8*)(buf + (size_t)(C::NA + wk * C::MT + wm * 4 + j) * 1024);
+  };
+  auto mm = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) bfr[kp][j] = *(const bf16x8*)(buf + (size_t)(C::NA + kk * C::MT + wm * 4 + j) * 1024);
-    }
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int kp = 0; kp < C::KPT; ++kp)
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[kp][i], bfr[kp][j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
   };
 
   const int nc = KB / C::CK;
   gload(w0, x0, 0);
   gload(w1, x1, min(1, nc - 1));
-  gload(w2, x2, min(2, nc - 1));
   // 1/rms of this tile's tokens from the producer's partial sums of h^2 (QKV, gate/up):
   // thread -> token t % TM, partial groups t / TM + GPT * q; clamped loads, masked sums
   if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
@@ -930,7 +924,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
     ssq[threadIdx.x] = sum;
   }
+  bf16x8 fa[4], fb[4], ga[4], gb[4];  // fragments of two chunks: the one in the MFMAs, the next
   lstore(w0, x0, 0);
+  gload(w0, x0, min(2, nc - 1));
   __syncthreads();
   if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
     if (threadIdx.x < C::MT * 16) {
@@ -940,27 +936,31 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       inv_rms[threadIdx.x] = rsqrtf(t * a.inv_width + a.eps);
     }
   }
-  // chunk c: LDS buffer c % 2 holds it and registers hold chunks c + 1 and c + 2. Chunk c + 1 is
-  // stored first, into the other buffer (every wave finished reading it before the previous
-  // barrier), so that its LDS writes run under this chunk's MFMAs (measured: 3-4% faster than
-  // storing after them); then chunk c + 3 is loaded into the set chunk c came from. Every step
-  // issues the same loads and stores (chunk indices clamped; steps past the end skip only the
-  // MFMAs, and what they store lands in a buffer nobody reads again): the compiler then sees the
-  // same loads in flight on every path and waits only for the set it stores (a conditional load
-  // made it wait for all of them).
-  auto step = [&](int c, WR (&wf)[LW], i32x4 (&xf)[LX], const WR (&wn_)[LW], const i32x4 (&xn)[LX])
-      __attribute__((always_inline)) {
-    lstore(wn_, xn, (c + 1) & 1);
-    __builtin_amdgcn_sched_barrier(0);
-    gload(wf, xf, min(c + 3, nc - 1));
-    __builtin_amdgcn_sched_barrier(0);  // the loads in flight before the MFMAs
-    if (c < nc) compute(c & 1);
+  rd(fa, fb, 0);
+  lstore(w1, x1, 1);
+  gload(w1, x1, min(3, nc - 1));
+  __syncthreads();
+  // step c: the fragments of chunk c are in registers, LDS buffer (c + 1) % 2 holds chunk c + 1
+  // and register set c % 2 holds chunk c + 2 (the other set: chunk c + 3). The MFMAs of chunk c
+  // run while this wave reads chunk c + 1's fragments and stores chunk c + 2 into buffer c % 2
+  // (chunk c's fragments left it before the previous barrier); that set then takes chunk c + 4
+  // (a third set measured no faster). One barrier a step, and the MFMA unit never waits on the
+  // step's own LDS reads. Chunk indices are clamped (what lands past the end is never read).
+  auto step = [&](int c, const bf16x8 (&fc)[4], const bf16x8 (&gc)[4], bf16x8 (&fn)[4], bf16x8 (&gn)[4],
+                  WR (&ws)[LW], i32x4 (&xs)[LX]) __attribute__((always_inline)) {
+    rd(fn, gn, (c + 1) & 1);
+    mm(fc, gc);
+    lstore(ws, xs, c & 1);
+    gload(ws, xs, min(c + 4, nc - 1));
     __syncthreads();
   };
-  for (int c = 0; c < nc; c += 3) {
-    step(c, w0, x0, w1, x1);
-    step(c + 1, w1, x1, w2, x2);
-    step(c + 2, w2, x2, w0, x0);
+  int c = 0;
+  {
+    for (; c + 2 <= nc; c += 2) {
+      step(c, fa, fb, ga, gb, w0, x0);
+      step(c + 1, ga, gb, fa, fb, w1, x1);
+    }
+    if (c < nc) step(c, fa, fb, ga, gb, w0, x0);
   }
 
   // partial sub-tiles of the WK k-groups meet in LDS: [wave][tile q = 4 i + j][lane][4]

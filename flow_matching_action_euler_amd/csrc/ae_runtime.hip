@@ -1499,6 +1499,40 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
   return AE_OK;
 }
 
+int ae_prefill_to_slot(ae_handle* h, const float* emb, ae_handle* expert, int slot) {
+  if (!h || !expert) return AE_ERR_INVALID_ARG;
+  if (!h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "not a prefill handle (ae_config.prefill = 0)");
+  if (!emb) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  const ae_config& c = h->c;
+  const ae_config& e = expert->c;
+  if (expert->c.prefill || expert->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "the target is not an expert handle");
+  if (slot < 0 || slot >= e.max_batch) return fail(h, AE_ERR_INVALID_ARG, "slot out of range");
+  if (e.prefix_len != c.horizon || e.n_layers != c.n_layers || e.n_kv_heads != c.n_kv_heads ||
+      e.head_dim != c.head_dim || e.kv_dtype != c.kv_dtype || expert->dev != h->dev)
+    return fail(h, AE_ERR_UNSUPPORTED,
+                "expert prefix_len, n_layers, n_kv_heads, head_dim, kv_dtype and device must match the prefill stack");
+  // the two layouts coincide: [L][n_kv][32-key blocks][block fragments], ceil(P/32) blocks, keys
+  // past P zero in both (never written here, zeroed at allocation)
+  const size_t bytes = expert->slot_elems * dtype_size(e.kv_dtype);
+  if (bytes != (size_t)c.n_layers * h->pf_layer_elems * dtype_size(c.kv_dtype))
+    return fail(h, AE_ERR_UNSUPPORTED, "cache layouts differ");
+  hipGraphExec_t g;
+  int rc = get_graph(h, 4, 0, 0, &g);
+  if (rc) return rc;
+  HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)c.horizon * c.width * 4, hipMemcpyHostToDevice, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+  HIP_TRY(h, hipGraphLaunch(g, h->stream));
+  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  HIP_TRY(h, hipMemcpyAsync((char*)expert->kcache + slot * bytes, h->pf_k, bytes, hipMemcpyDeviceToDevice, h->stream));
+  HIP_TRY(h, hipMemcpyAsync((char*)expert->vcache + slot * bytes, h->pf_v, bytes, hipMemcpyDeviceToDevice, h->stream));
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  rc = check_err_flag(h);
+  if (rc) return rc;
+  expert->slot_ready[slot] = 1;
+  return AE_OK;
+}
+
 int ae_prefill(ae_handle* h, const float* emb, void* k_out, void* v_out) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (!h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "not a prefill handle (ae_config.prefill = 0)");

@@ -241,6 +241,15 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out);
  * AE_ERR_UNSUPPORTED on a handle that is not a prefill stack. */
 int ae_prefill(ae_handle* h, const float* emb, void* k_out, void* v_out);
 
+/* ae_prefill with the cache left on the device: the prefill stack h runs over emb (host
+ * [horizon][width] fp32) and its per-layer K/V are copied device to device into prefix slot
+ * `slot` of the expert handle `expert` (the packed layout ae_load_prefix_kv builds; no host
+ * round trip). The expert's prefix_len must equal h's horizon and its n_layers, n_kv_heads,
+ * head_dim and kv_dtype must match h's, else AE_ERR_UNSUPPORTED; both handles on one device.
+ * Marks the slot loaded. Synchronous (h's stream drained before return); ae_last_gpu_ms(h) covers
+ * the prefill pass. */
+int ae_prefill_to_slot(ae_handle* h, const float* emb, ae_handle* expert, int slot);
+
 /* Free every device resource of the handle. NULL is a no-op. */
 void ae_destroy(ae_handle* h);
 

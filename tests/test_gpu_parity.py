@@ -323,6 +323,34 @@ def test_expert_denoises_on_a_prefilled_cache():
     exp.close()
 
 
+def test_prefill_to_slot_equals_the_host_round_trip():
+    """ae_prefill_to_slot copies the stack's K/V on the device into an expert's slot: two robots with
+    the same noise, one on a slot loaded through ae_prefill + ae_load_prefix_kv and one on a slot
+    filled on the device from the same embeddings, denoise bit for bit alike (and as the oracle);
+    mismatched shapes are rejected."""
+    pcfg = SMALL_PREFILL.with_(mlp_dtype="bf16")
+    pf = ActionExpert(pcfg, G.make_weights(pcfg))
+    emb = G.make_prefix_embeddings(pcfg, 13)
+    k, v = pf.prefill(emb)
+    cfg = SMALL_BF16.with_(max_batch=2)
+    case = Case(cfg, n_slots=0)
+    exp = ActionExpert(cfg, case.W)
+    exp.load_prefix_kv(0, k, v)
+    pf.prefill_to_slot(emb, exp, 1)
+    noise = case.noise(1)
+    x = exp.denoise(np.concatenate([noise, noise]), 3)
+    assert np.array_equal(x[0], x[1])
+    kk, vv = O.decode_kv(cfg, k, v)
+    assert rel_err(x[1], O.denoise(cfg, case.Wd, kk, vv, noise[0].astype(np.float64), 3)) <= tol_for(cfg)
+    bcfg = SMALL_BF16.with_(prefix_len=96)
+    bad = ActionExpert(bcfg, G.make_weights(bcfg))
+    with pytest.raises(AEError) as e:
+        pf.prefill_to_slot(emb, bad, 0)
+    assert e.value.code == -2
+    for h in (pf, exp, bad):
+        h.close()
+
+
 def test_prefill_entry_rejects_other_handles():
     case = Case(SMALL_BF16)
     ex = _expert(case)
