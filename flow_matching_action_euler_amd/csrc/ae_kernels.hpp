@@ -809,8 +809,8 @@ constexpr void (*gemm_entry())(GemmArgs) {
 // fragments of two chunks in registers, so the MFMAs of one chunk run while the next chunk's
 // fragments are read and the one after is stored (measured on a stand-alone step: the LDS reads
 // hide completely under the MFMAs, the per-step barrier costs ~20% and the LDS writes ~50%).
-// bf16 activations; bf16 weights, or E4M3 weights (the MLP roles) widened to bf16 (exact) on
-// their way into LDS and scaled per output channel in the epilogue.
+// bf16 activations; bf16 weights, or E4M3 weights (the MLP roles) kept as bytes in LDS, widened
+// to bf16 (exact) after the fragment read and scaled per output channel in the epilogue.
 template <int WN, int WM, int WK>
 struct TileCfg {
   static_assert(WN * WM * WK == GW, "8 waves");
@@ -836,6 +836,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   typedef typename TiledWReg<WT>::T WR;
   static_assert(WT == WT_BF16 || (WT == WT_FP8 && EPI != EPI_QKV), "E4M3 weights: MLP roles");
   constexpr int LW = C::NA / GW, LX = C::NB / GW;  // weight / activation loads per thread
+  // E4M3 weight fragments stay 512-byte runs in LDS (widened to bf16 after the fragment read):
+  // a quarter fewer LDS bytes stored and read per step than widening them before the store
+  constexpr size_t AFB = WT == WT_FP8 ? 512 : 1024, CHUNKB = (size_t)C::NA * AFB + (size_t)C::NB * 1024;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   char* stage = (char*)smem;                                  // [2][CHUNK] operands; then partials
   float* inv_rms = (float*)(stage + C::STAGE);                // [TM]
@@ -874,16 +877,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   };
   auto lstore = [&](const WR (&rw)[LW], const i32x4 (&rx)[LX], int b) __attribute__((always_inline)) {
-    char* dst = stage + b * C::CHUNK + lane * 16;
+    char* dst = stage + b * CHUNKB;
 #pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      if constexpr (WT == WT_FP8)
-        *(bf16x8*)(dst + (size_t)(wave + GW * i) * 1024) = fp8x8_to_bf16x8(make_uint2(rw[i][0], rw[i][1]));
-      else
-        *(i32x4*)(dst + (size_t)(wave + GW * i) * 1024) = rw[i];
-    }
+    for (int i = 0; i < LW; ++i) *(WR*)(dst + (size_t)(wave + GW * i) * AFB + lane * (AFB / 64)) = rw[i];
 #pragma unroll
-    for (int i = 0; i < LX; ++i) *(i32x4*)(dst + (size_t)(C::NA + wave + GW * i) * 1024) = rx[i];
+    for (int i = 0; i < LX; ++i) *(i32x4*)(dst + C::NA * AFB + (size_t)(wave + GW * i) * 1024 + lane * 16) = rx[i];
   };
   f32x4 acc[4][4];
 #pragma unroll
@@ -893,11 +891,20 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
 
   // fragments of this wave's k-block of the chunk in LDS buffer b, and their 16 MFMAs
   auto rd = [&](bf16x8 (&af)[4], bf16x8 (&bf)[4], int b) __attribute__((always_inline)) {
-    const char* buf = stage + b * C::CHUNK + lane * 16;
+    const char* buf = stage + b * CHUNKB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) af[i] = *(const bf16x8*)(buf + (size_t)((wn * 4 + i) * C::CK + wk) * 1024);
+    for (int i = 0; i < 4; ++i) {
+      const char* src = buf + (size_t)((wn * 4 + i) * C::CK + wk) * AFB + lane * (AFB / 64);
+      if constexpr (WT == WT_FP8) {
+        const i32x2 v = *(const i32x2*)src;
+        af[i] = fp8x8_to_bf16x8(make_uint2(v[0], v[1]));
+      } else {
+        af[i] = *(const bf16x8*)src;
+      }
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *(const bf16x8*)(buf + (size_t)(C::NA + wk * C::MT + wm * 4 + j) * 1024);
+    for (int j = 0; j < 4; ++j)
+      bf[j] = *(const bf16x8*)(buf + C::NA * AFB + (size_t)(wk * C::MT + wm * 4 + j) * 1024 + lane * 16);
   };
   auto mm = [&](const bf16x8 (&af)[4], const bf16x8 (&bf)[4]) __attribute__((always_inline)) {
 #pragma unroll
