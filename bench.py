@@ -89,24 +89,48 @@ def _cores():
         return int(os.cpu_count())
 
 
-def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0):
-    """The oracle as it stands, timed on this host: Euler steps of one robot until the budget is spent."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0, single_core_s=5.0):
+    """The oracle as it stands, timed on this host: Euler steps of one robot until the budget is spent,
+    with every BLAS thread, then again (a shorter budget) on one thread."""
     from oracle import ae_oracle as O
     cores = _cores()
     Wd = O.dequantize_weights(cfg, W)
     kk, vv = O.decode_kv(cfg, k, v)
-    x = noise[0].astype(np.float64)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        x = x + (1.0 / cfg.steps) * O.velocity(cfg, Wd, kk, vv, x, (n % cfg.steps) / cfg.steps)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 40:
-            break
-    return {"value": n / el, "unit": "denoise steps/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"{n} Euler steps of one robot ({cfg.name}, P={cfg.prefix_len}, H={cfg.horizon}), fp64 numpy, "
-                      f"{el:.1f} s"}
+
+    def run(budget, cap):
+        x = noise[0].astype(np.float64)
+        n = 0
+        t0 = time.perf_counter()
+        while True:
+            x = x + (1.0 / cfg.steps) * O.velocity(cfg, Wd, kk, vv, x, (n % cfg.steps) / cfg.steps)
+            n += 1
+            el = time.perf_counter() - t0
+            if el >= budget or n >= cap:
+                return n, el
+
+    n, el = run(budget_s, 40)
+    out = {"value": n / el, "unit": "denoise steps/s", "cores": int(cores), "kind": "oracle",
+           "sample": f"{n} Euler steps of one robot ({cfg.name}, P={cfg.prefix_len}, H={cfg.horizon}), fp64 numpy, "
+                     f"{el:.1f} s", "cpu_model": _cpu_model()}
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            n1, el1 = run(single_core_s, 10)
+        out["single_core"] = {"value": n1 / el1, "sample": f"{n1} Euler steps, one BLAS thread, {el1:.1f} s"}
+    except ImportError:
+        pass
+    return out
 
 
 def bench_verify(args, cfg, W, kvs, ex, stream):
