@@ -174,6 +174,40 @@ def test_error_codes():
     ex.close()
 
 
+SMALL_MAX = SMALL_BF16.with_(name="small_max", horizon=256, action_dim=64, prefix_len=64, max_batch=2, max_taus=1,
+                             gripper_dim=63, steps=2)
+
+
+def test_largest_chunk_and_action_width_match_oracle():
+    """The largest suffix the kernels take (horizon 256, action_dim 64), two robots, then one flow
+    time: delta 0 accepts nothing (the test is strict), a huge delta accepts every row of a draft
+    without a switch."""
+    cfg = SMALL_MAX
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(2)
+    got = ex.denoise(noise, cfg.steps)
+    err = rel_err(got, case.oracle_denoise(noise, cfg.steps))
+    print(f"small_max rel_err={err:.3e}")
+    assert err <= tol_for(cfg), err
+    draft = G.make_draft(cfg, 0)  # even seed: no gripper switch
+    tau = np.array([0.5], np.float32)
+    acc0, sw0, D = ex.verify(0, draft, noise[0], tau, 0.0)
+    accH, swH, _ = ex.verify(0, draft, noise[0], tau, 1e30)
+    assert (acc0, sw0) == (0, 0) and (accH, swH) == (cfg.horizon, 0)
+    _, _, D_o = case.oracle_verify(0, draft, noise[0], tau, 0.0)
+    assert rel_err(D, D_o) <= tol_for(cfg)
+    ex.close()
+
+
+@pytest.mark.parametrize("over", [dict(horizon=257), dict(action_dim=65)], ids=["horizon257", "action65"])
+def test_sizes_past_the_kernels_are_rejected_at_create(over):
+    cfg = SMALL_BF16.with_(**over)
+    with pytest.raises(AEError) as e:
+        ActionExpert(cfg, G.make_weights(cfg))
+    assert e.value.code == -2
+
+
 # ------------------------------------------------------------------ time-modulated expert with QK-norm
 
 SMALL_DM05 = SMALL_BF16.with_(name="small_dm05", time_mode=1, qk_norm=1, max_taus=0)
