@@ -913,36 +913,74 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[i], bf[j], acc[i][j], 0, 0, 0);
   };
 
-  const int nc = KB / C::CK;
-  gload(w0, x0, 0);
-  gload(w1, x1, min(1, nc - 1));
   // 1/rms of this tile's tokens from the producer's partial sums of h^2 (QKV, gate/up):
   // thread -> token t % TM, partial groups t / TM + GPT * q; clamped loads, masked sums
-  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
-    const int tl = threadIdx.x % (C::MT * 16), g0 = threadIdx.x / (C::MT * 16);
-    const float* sp = a.ssp_in + min(tt0 * 16 + tl, a.M_pad - 1);
-    float sum = 0.f;
-    for (int q0 = 0; q0 < a.g_in; q0 += C::GPT * C::NRD) {  // 64 groups a pass (width 1024 per pass)
-      float sv[C::NRD];
-#pragma unroll
-      for (int q = 0; q < C::NRD; ++q) sv[q] = sp[(size_t)min(q0 + g0 + C::GPT * q, a.g_in - 1) * a.M_pad];
-#pragma unroll
-      for (int q = 0; q < C::NRD; ++q) sum += q0 + g0 + C::GPT * q < a.g_in ? sv[q] : 0.f;
+  auto rms_partial = [&]() __attribute__((always_inline)) {
+    if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
+      const int tl = threadIdx.x % (C::MT * 16), g0 = threadIdx.x / (C::MT * 16);
+      const float* sp = a.ssp_in + min(tt0 * 16 + tl, a.M_pad - 1);
+      float sum = 0.f;
+      for (int q0 = 0; q0 < a.g_in; q0 += C::GPT * C::NRD) {  // 64 groups a pass (width 1024 per pass)
+        float sv[C::NRD];
+  #pragma unroll
+        for (int q = 0; q < C::NRD; ++q) sv[q] = sp[(size_t)min(q0 + g0 + C::GPT * q, a.g_in - 1) * a.M_pad];
+  #pragma unroll
+        for (int q = 0; q < C::NRD; ++q) sum += q0 + g0 + C::GPT * q < a.g_in ? sv[q] : 0.f;
+      }
+      ssq[threadIdx.x] = sum;
     }
-    ssq[threadIdx.x] = sum;
-  }
+  };
+  auto rms_final = [&]() __attribute__((always_inline)) {  // after a barrier
+    if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
+      if (threadIdx.x < C::MT * 16) {
+        float t = 0.f;
+  #pragma unroll
+        for (int q = 0; q < C::GPT; ++q) t += ssq[q * C::MT * 16 + threadIdx.x];
+        inv_rms[threadIdx.x] = rsqrtf(t * a.inv_width + a.eps);
+      }
+    }
+  };
+  const int nc = KB / C::CK;
+  if constexpr (WN == 1 && WM == 1) {
+    // one 64 x 64 tile per workgroup, one k-group per wave: no fragment is shared between waves,
+    // so each wave loads its own straight into registers (three k-blocks in flight) and the loop
+    // has no LDS traffic and no barrier; LDS only meets the k-groups' partial tiles afterwards
+    auto ld = [&](bf16x8 (&af)[4], bf16x8 (&bf)[4], int c) __attribute__((always_inline)) {
+      const int kb = min(c, nc - 1) * WK + wk;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const WR v = wsrc[((size_t)(ct0 + i) * KB + kb) * 64 + lane];
+        if constexpr (WT == WT_FP8) af[i] = fp8x8_to_bf16x8(make_uint2(v[0], v[1]));
+        else af[i] = __builtin_bit_cast(bf16x8, v);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        bf[j] = __builtin_bit_cast(bf16x8, xsrc[((size_t)kb * ntt + min(tt0 + j, ntt - 1)) * 64 + lane]);
+    };
+    bf16x8 a0[4], b0[4], a1[4], b1[4], a2[4], b2[4];
+    ld(a0, b0, 0);
+    ld(a1, b1, 1);
+    ld(a2, b2, 2);
+    rms_partial();
+    __syncthreads();
+    rms_final();
+    for (int c = 0; c < nc; c += 3) {
+      mm(a0, b0);
+      ld(a0, b0, c + 3);
+      if (c + 1 < nc) mm(a1, b1);
+      ld(a1, b1, c + 4);
+      if (c + 2 < nc) mm(a2, b2);
+      ld(a2, b2, c + 5);
+    }
+  } else {
+  gload(w0, x0, 0);
+  gload(w1, x1, min(1, nc - 1));
+  rms_partial();
   bf16x8 fa[4], fb[4], ga[4], gb[4];  // fragments of two chunks: the one in the MFMAs, the next
   lstore(w0, x0, 0);
   gload(w0, x0, min(2, nc - 1));
   __syncthreads();
-  if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
-    if (threadIdx.x < C::MT * 16) {
-      float t = 0.f;
-#pragma unroll
-      for (int q = 0; q < C::GPT; ++q) t += ssq[q * C::MT * 16 + threadIdx.x];
-      inv_rms[threadIdx.x] = rsqrtf(t * a.inv_width + a.eps);
-    }
-  }
+  rms_final();
   rd(fa, fb, 0);
   lstore(w1, x1, 1);
   gload(w1, x1, min(3, nc - 1));
@@ -968,6 +1006,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       step(c + 1, ga, gb, fa, fb, w1, x1);
     }
     if (c < nc) step(c, fa, fb, ga, gb, w0, x0);
+  }
+
   }
 
   // partial sub-tiles of the WK k-groups meet in LDS: [wave][tile q = 4 i + j][lane][4]
