@@ -40,36 +40,6 @@ enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2, EPI_OUT = 3 };
 
 constexpr int TOKG = 64;   // tokens per workgroup (4 MFMA column tiles of 16)
 
-// Optional phase timestamps (compile with -DAE_TRACE): thread 0 of every
-// workgroup records the 100 MHz wall clock at numbered points of a kernel.
-#ifdef AE_TRACE
-__device__ unsigned long long ae_trace_buf[8][2048][8];  // [kernel kind][workgroup][point]
-#define AE_TR(i)                                                                                         \
-  do {                                                                                                   \
-    if (threadIdx.x == 0) {                                                                              \
-      const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);               \
-      if (wg_ < 2048) ae_trace_buf[a.trace_id & 7][wg_][i] = wall_clock64();                             \
-    }                                                                                                    \
-  } while (0)
-#define AE_TRC(i)                                                                                        \
-  do {                                                                                                   \
-    if (threadIdx.x == 0) {                                                                              \
-      const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);               \
-      if (wg_ < 2048) ae_trace_buf[a.trace_id & 7][wg_][i] = clock64();                                  \
-    }                                                                                                    \
-  } while (0)
-#define AE_TRV(i, v)                                                                                     \
-  do {                                                                                                   \
-    if (threadIdx.x == 0) {                                                                              \
-      const unsigned wg_ = blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z);               \
-      if (wg_ < 2048) ae_trace_buf[a.trace_id & 7][wg_][i] = (v);                                        \
-    }                                                                                                    \
-  } while (0)
-#else
-#define AE_TR(i) do { } while (0)
-#define AE_TRC(i) do { } while (0)
-#define AE_TRV(i, v) do { } while (0)
-#endif
 constexpr int KBLK = 32;   // inputs per k-block
 
 // Activations passed between kernels (hb, o, u: M_pad tokens x K inputs) are stored in the
@@ -235,7 +205,6 @@ struct GemmArgs {
   float* xio;            // denoise: x [M_pad][A] updated in place; verify: v out
   int A;
   float dt;              // > 0: x += dt * v; 0: store v
-  int trace_id;          // kernel kind for the optional phase trace
   Prefetch pf;           // next kernel's operands to place in L2 (QKV and gate/up launches only)
   int tn_blocks, tm_blocks;  // token-tiled launches: channel and token panels of the output
   // time-modulated expert and QK-norm (null when off; 64-token kernel only)
@@ -359,8 +328,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   float* ssq8 = inv_rms + 64;                                 // [8][64]
   unsigned* ticket = (unsigned*)(ssq8 + 512);                 // split-K arrival ticket
 
-  AE_TR(0);
-  AE_TRC(6);
   const int g = blockIdx.x, s = blockIdx.y;
   const int n_groups = gridDim.x;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -482,18 +449,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       if (zi == 0)
         pf_acc = prefetch_issue<2>(a.pf, blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z),
                                    gridDim.x * gridDim.y * gridDim.z, threadIdx.x, GTHREADS);
-    AE_TR(1);
     float ssq = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) ssq += (has_ssp && (int)(threadIdx.x >> 6) + 8 * i < a.g_in) ? ssv[i] : 0.f;
     if (a.ssp_in != nullptr)
       for (int gi = (threadIdx.x >> 6) + 64; gi < a.g_in; gi += 8) ssq += sp[(size_t)gi * a.M_pad];  // width > 1024
-#ifdef AE_TRACE
-    if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU) {
-      asm volatile("" ::"v"(ssq));
-      AE_TR(5);
-    }
-#endif
     // cross-wave reduction: red[wave][nt][tt][channel quad][token % 16][4], so the 16 lanes of a
     // write phase cover 256 consecutive bytes (no bank conflicts); res is [nt][token][channel]
 #pragma unroll
@@ -527,7 +487,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     }
     __syncthreads();
 
-    AE_TR(2);
     if (a.S > 1) {  // one token group (zpw = 1)
       const int n_z = a.n_zt;
       const int tile_elems = NT * 1024;
@@ -560,8 +519,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
           if (qd < NT * 256) {
             f32x4 v[3];
             const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
-            int polls = 0;
-            for (;; ++polls) {
+            for (;;) {
               bool ok = true;
 #pragma unroll
               for (int ss = 0; ss < 3; ++ss) {
@@ -572,7 +530,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
               if (wall_clock64() > t_end) { gave_up = true; break; }
               __builtin_amdgcn_s_sleep(1);
             }
-            if (i == 0) AE_TRV(5, polls + 1);
             const f32x4 own = *(const f32x4*)(res + qd * 4);
             const f32x4 zero = f32x4{0.f, 0.f, 0.f, 0.f};
             f32x4 sum = v[0] + (a.S == 2 ? own : v[1]);
@@ -621,7 +578,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       }
     }
 
-    AE_TR(3);
     if constexpr (EPI == EPI_QKV) {
       // q and k tiles: thread -> (token, half of the tile's 16 channels) = 8 consecutive head dims,
       // rotated and stored as one 16-byte run of a fragment row
@@ -758,11 +714,6 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     return;
   }
   prefetch_done(pf_acc);
-#ifdef AE_TRACE
-  wait_mem();
-  AE_TR(4);
-  AE_TRC(7);
-#endif
 }
 
 // One entry point per role, so that profiles name the phase: same body,
@@ -1214,7 +1165,6 @@ struct AttnArgs {
   unsigned* err;          // set if a co-resident merge poll gave up
   int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
   void* o;                // output, fragment order (act_idx)
-  int trace_id;
   // QK-norm: per (q or k tile, token) sums of squares of the raw projections written by the QKV
   // epilogue ([q tiles, then k tiles][qk_mpad]); a score is scaled by 1/rms of its query head row and,
   // for suffix keys, of its key (the cached prefix keys come normalised)
@@ -1268,7 +1218,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   float* rq_s = (float*)((char*)Qs + (size_t)ATT_ROWS * DH * 4);  // QK-norm: 1/rms of the 16 query rows
   float* rk_s = rq_s + ATT_ROWS;                                  // and of the suffix keys
 
-  AE_TR(0);
   int split = blockIdx.x, qt = blockIdx.y, zz = blockIdx.z;
   if (a.xcd_group) {
     const int T = gridDim.x * gridDim.y * gridDim.z;
@@ -1365,7 +1314,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       if (i == 0) rq_s[r] = rsqrtf(v * a.qk_inv_dh + a.qk_eps);  // rk_s[key] = rq_s[ATT_ROWS + key]
     }
   }
-  AE_TR(1);
   __syncthreads();  // query tile staged
 
   const int k8 = 8 * (lane >> 4);
@@ -1449,7 +1397,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(ow + dt * 16) = oacc[dt];
   if (lane < 16) *(float2*)(MLw + (wave * ATT_ROWS + lane) * 2) = make_float2(m_run, l_run);
   __syncthreads();
-  AE_TR(2);
 
   // ---- merge the waves: thread -> (row, 4-dim chunk) pairs q = t + 64 NW i; a wave reads whole
   // 1 KB rows of the wave partials, so the LDS reads have no bank conflicts
@@ -1484,7 +1431,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     Lq[i] = L;
     Oq[i] = O;
   }
-  AE_TR(3);
 
   auto pair_row = [&](int i) { return (int)(threadIdx.x + NTH * i) / CPR; };
   auto pair_ok = [&](int i) { return (int)(threadIdx.x + NTH * i) < ATT_ROWS * CPR; };
@@ -1513,10 +1459,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         *(f32x4*)(a.opart + (prow + pair_row(i)) * DH + 4 * c4) = Oq[i];
         if (c4 == 0) *(float2*)(a.mlpart + (prow + pair_row(i)) * 2) = make_float2(Mq[i], Lq[i]);
       }
-#ifdef AE_TRACE
-    wait_mem();
-    AE_TR(4);
-#endif
     return;
   }
 
@@ -1537,7 +1479,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   if (threadIdx.x < ATT_ROWS)
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(i32x2, MLs[threadIdx.x]), rm,
                                           (unsigned)((prow + threadIdx.x) * 8), 0, 0x10);
-  AE_TR(6);
   const int rps = (ATT_ROWS + a.n_split - 1) / a.n_split;
   constexpr int TPC = DH / 4;            // consumer threads per row, one 16-byte chunk each
   constexpr int RPP = NW * 64 / TPC;     // rows per pass
@@ -1557,8 +1498,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       auto moff = [&](int c) { return (unsigned)(((tile * a.n_split + c) * ATT_ROWS + rr) * 8); };
       auto ooff = [&](int c) { return (unsigned)((((tile * a.n_split + c) * ATT_ROWS + rr) * DH + kc * 4) * 4); };
       const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
-      int polls = 0;
-      for (;; ++polls) {
+      for (;;) {
         bool ok = true;
 #pragma unroll
         for (int c = 0; c < 8; ++c)
@@ -1571,8 +1511,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
         if (wall_clock64() > t_end) { gave_up = true; break; }
         __builtin_amdgcn_s_sleep(1);
       }
-      AE_TR(4);
-      if (c0 == 0) AE_TRV(7, polls + 1);
       float Mn = M2;
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -1605,10 +1543,6 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   }
   if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-#ifdef AE_TRACE
-  wait_mem();
-  AE_TR(5);
-#endif
 }
 
 // Merge of the key-split partials of attn_kernel: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
@@ -1621,7 +1555,6 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   constexpr int TPR = DH / DPT;
   const int qt = blockIdx.x, zz = blockIdx.y;
   if ((int)threadIdx.x >= ATT_ROWS * TPR) return;
-  AE_TR(0);
   const int row = threadIdx.x / TPR, d0 = (threadIdx.x % TPR) * DPT;
   const int s = zz / a.n_kv, g = zz % a.n_kv, gq = a.n_q / a.n_kv;
   const int r = qt * ATT_ROWS + row;
@@ -1679,10 +1612,6 @@ __global__ __launch_bounds__(256) void attn_merge(AttnArgs a) {
   const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
   for (int i = 0; i < DPT; ++i) Act<AT>::st((XT*)a.o, act_idx(tok, col + i, a.ntt), O[i] * inv);
-#ifdef AE_TRACE
-  wait_mem();
-  AE_TR(1);
-#endif
 }
 
 // ------------------------------------------------------------------ in_proj, time embedding, verify

@@ -121,6 +121,7 @@ struct ae_handle {
   bool coresident_attn = true, poll_splitk = true;
   int tiled_roles = 0xf;  // GEMM roles (bit per Role) that may take the token-tiled kernel
   int tiled_force = -1;   // token-tiled shape forced for every GEMM it fits (tests)
+  bool attn_xcd = true;   // attention workgroups of one sequence grouped on one XCD (8+ sequences)
   float* rope_cs = nullptr;
   void *kcache = nullptr, *vcache = nullptr;
   size_t slot_elems = 0;     // elements of one slot's packed K (and V) cache
@@ -389,15 +390,12 @@ hipError_t set_all_gemm_attrs() {
   return e;
 }
 
-// k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group;
-// AE_SPLITS="q,o,g,d,u" overrides them for tuning.
+// k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group (measured for Pi0:
+// o_proj and down gain from 4 splits, the others from none)
 struct Splits {
   int qkv = 1, o = 4, gu = 1, down = 4, out = 1;
-  Splits() {
-    if (const char* e = getenv("AE_SPLITS")) sscanf(e, "%d,%d,%d,%d,%d", &qkv, &o, &gu, &down, &out);
-  }
 };
-const Splits& splits() { static Splits s; return s; }
+const Splits& splits() { static const Splits s; return s; }
 
 // Key splits when each of nw waves walks `it` blocks of ATT_KB keys.
 int attn_splits(int n_blocks, int it, int nw) { return std::max(1, (n_blocks + it * nw - 1) / (it * nw)); }
@@ -465,55 +463,21 @@ hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs
 struct AttnPlan {
   int n_split, split_it, coresident;  // split_it: blocks per wave of a split plan (0: whole tile)
 };
-// AE_ATTN_MID=0 keeps several-sequence passes on whole-tile workgroups
-bool attn_mid_plan() {
-  static bool on = [] {
-    const char* e = getenv("AE_ATTN_MID");
-    return !e || atoi(e) != 0;
-  }();
-  return on;
-}
 AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
   const int ns = attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT);
   if (h->coresident_attn && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, ATT_IT_SPLIT, 1};
   // several sequences (verification): splits of 2 blocks per wave, if those fit on the device at once
   const int nm = attn_splits(nb, ATT_IT_MID, ATT_WAVES_SPLIT);
-  if (h->coresident_attn && attn_mid_plan() && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
+  if (h->coresident_attn && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
     return {nm, ATT_IT_MID, 1};
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
 
-// Whether attention workgroups of one sequence are grouped on one XCD when a launch covers 8 or
-// more (sequence, kv head) pairs; AE_ATTN_XCD=0 turns it off.
-bool attn_xcd_group() {
-  static bool on = [] {
-    const char* e = getenv("AE_ATTN_XCD");
-    return !e || atoi(e) != 0;
-  }();
-  return on;
-}
-
-// Whether a GEMM workgroup loops over several 64-token groups (M > 64) with its weights in
-// registers instead of one workgroup per group; AE_TOKEN_LOOP=0 turns it off.
-bool tokens_per_wg_loop() {
-  static bool on = [] {
-    const char* e = getenv("AE_TOKEN_LOOP");
-    return !e || atoi(e) != 0;
-  }();
-  return on;
-}
-
 // Steps of ~0.2 us that a split-K consumer sleeps before its first poll, so that the poll
 // finds the other splits' partials landed instead of costing a second round trip (measured
-// for Pi0: 1 step saves 0.16 ms per chunk, 2-6 steps less); AE_POLL_DELAY overrides it.
-int poll_delay() {
-  static int n = [] {
-    const char* e = getenv("AE_POLL_DELAY");
-    return e ? atoi(e) : 1;
-  }();
-  return n;
-}
+// for Pi0: 1 step saves 0.16 ms per chunk, 2-6 steps less).
+constexpr int POLL_DELAY = 1;
 
 // Token-tiled shape for a GEMM role over n_tiles 16-channel tiles, K inputs and M tokens, or
 // -1 for the kernel above: one token group, fp32 operands, E4M3 weights outside the MLP roles,
@@ -571,12 +535,12 @@ struct Dispatch {
     }
     a.n_zt = n_z;
     a.zpw = 1;
-    if (a.S == 1 && n_z > 1 && h->n_cu > 0 && tokens_per_wg_loop()) {
+    if (a.S == 1 && n_z > 1 && h->n_cu > 0) {
       const int gz = std::max(1, std::min(n_z, h->n_cu / std::max(n_groups, 1)));
       a.zpw = (n_z + gz - 1) / gz;
     }
     a.exch_poll = h->poll_splitk && (long long)n_groups * a.S * n_z <= h->n_cu;  // one workgroup per CU fits them all
-    a.poll_delay = poll_delay();
+    a.poll_delay = POLL_DELAY;
     a.err = h->err_flag;
     if (h->at == AT_F32) {
       switch (role) {
@@ -615,36 +579,15 @@ struct Dispatch {
 // bit 0 saves 0.32 ms, bit 4 0.19 ms, bit 3 (half of each k-range) 0.1 ms, bit 1 0.04 ms (it
 // moves ~1.3 us per layer from down to gate/up). The attention placing o_proj's weights
 // costs it ~1 us per launch (its exchange shares the memory path) and is not offered.
-// Default 1 | 2 | 8 | 16; AE_PREFETCH=mask overrides it.
-int prefetch_mask() {
-  static int m = [] {
-    const char* e = getenv("AE_PREFETCH");
-    return e ? atoi(e) : 1 | 2 | 8 | 16;
-  }();
-  return m;
-}
+constexpr int PREFETCH_MASK = 1 | 2 | 8 | 16;
 
 // Leading k-blocks of each gate/up tile that o_proj's producers place in L2 (bit 3): half the
 // k-range, so that the prefetch ends within o_proj's own tail (measured for Pi0: all of it
-// lengthens o_proj as much as it shortens gate/up; 12-16 of 32 blocks gain 0.1 ms per chunk);
-// AE_PF_GU_LEAD overrides it.
-int prefetch_gu_lead(int kb) {
-  static int n = [] {
-    const char* e = getenv("AE_PF_GU_LEAD");
-    return e ? atoi(e) : -1;
-  }();
-  return n >= 0 ? n : kb / 2;
-}
+// lengthens o_proj as much as it shortens gate/up; 12-16 of 32 blocks gain 0.1 ms per chunk).
+int prefetch_gu_lead(int kb) { return kb / 2; }
 
-// Leading k-blocks of each down tile that gate/up places in L2 (bit 1; 0 = all);
-// AE_PF_DOWN_LEAD overrides it.
-int prefetch_down_lead() {
-  static int n = [] {
-    const char* e = getenv("AE_PF_DOWN_LEAD");
-    return e ? atoi(e) : 0;
-  }();
-  return n;
-}
+// Leading k-blocks of each down tile that gate/up places in L2 (bit 1; 0 = all of them).
+constexpr int PREFETCH_DOWN_LEAD = 0;
 
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
 // temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
@@ -689,11 +632,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const AttnPlan plan = attn_plan(h, n_seq);
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
-  aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && attn_xcd_group();
+  aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && h->attn_xcd;
   aa.err = h->err_flag;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
-  aa.trace_id = 1;
   if (c.qk_norm) {
     aa.qk_ssp = h->qk_ssp; aa.qk_mpad = Mp;
     aa.qk_inv_dh = 1.f / (float)dh; aa.qk_eps = c.rms_eps;
@@ -709,7 +651,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.w = h->qkv_p[l]; a.x = h->hb;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().qkv, n_z).S;
-      if ((prefetch_mask() & 1) && n_seq == 1 && !seq_slot && h->slot_elems) {  // this layer's prefix K/V (one robot)
+      if ((PREFETCH_MASK & 1) && n_seq == 1 && !seq_slot && h->slot_elems) {  // this layer's prefix K/V (one robot)
         const size_t kes = dtype_size(c.kv_dtype), lay = (size_t)nkv * h->nbp * ATT_KB * dh;
         const size_t off = ((size_t)slot0 * h->slot_elems + (size_t)l * lay) * kes;
         a.pf.kind = 1; a.pf.bytes = lay * kes;
@@ -724,7 +666,6 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
       if (sm) a.shift_bias = modp(sm->t->bqkv, nqkv, l);
       if (c.qk_norm) { a.qk_gain = h->qk_gain[l]; a.qk_ssp = h->qk_ssp; }
-      a.trace_id = 0;
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
     // --- attention over [prefix ; suffix]
@@ -747,13 +688,12 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.S = pick(nq * dh / 32, splits().o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = sm ? modp(sm->t->g2, w, l) : h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
       if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 2 * w;
-      if ((prefetch_mask() & 8) && !uses_tiled(h, R_GATE_UP, h->gu_tiles, w, M, Mp)) {  // gate/up's weights, tiled as gate/up is launched below
+      if ((PREFETCH_MASK & 8) && !uses_tiled(h, R_GATE_UP, h->gu_tiles, w, M, Mp)) {  // gate/up's weights, tiled as gate/up is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->gu_p[l];
         a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, splits().gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
         a.pf.kb_lead = prefetch_gu_lead(w / KBLK / a.pf.next_S);
       }
-      a.trace_id = 2;
       LAUNCH_CHECK(h, "o_proj_resid", (void)Dispatch::gemm(h, R_O_PROJ, a, w / 16, n_z, st));
     }
     // --- norm2 + gate/up + GeGLU
@@ -763,13 +703,12 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
       if (sm) a.shift_bias = modp(sm->t->bgu, ngu, l);
-      if ((prefetch_mask() & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
+      if ((PREFETCH_MASK & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
         a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, splits().down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
-        a.pf.kb_lead = prefetch_down_lead();
+        a.pf.kb_lead = PREFETCH_DOWN_LEAD;
       }
-      a.trace_id = 3;
       LAUNCH_CHECK(h, "gate_up_geglu", (void)Dispatch::gemm(h, R_GATE_UP, a, h->gu_tiles / 2, n_z, st));
     }
     // --- down + residual; hb <- h * next gain
@@ -782,12 +721,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
                                          : (sm ? sm->t->gf + (size_t)sm->k * w : h->final_ln ? h->final_ln : h->ln1[0]);
       if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 5 * w;
       a.ssp_out = h->ssp_a; a.N = w;
-      if ((prefetch_mask() & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
+      if ((PREFETCH_MASK & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
         a.pf.kind = 2; a.pf.base = (const char*)h->qkv_p[l + 1];
         a.pf.next_groups = h->qkv_tiles; a.pf.next_S = pick(w / 32, splits().qkv, n_z).S; a.pf.NT = 1; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->wt == WT_F32 ? 2048 : 1024;
       }
-      a.trace_id = 4;
       LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, R_DOWN, a, w / 16, n_z, st));
     }
   }
@@ -799,7 +737,6 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, splits().out, n_z).S;
     a.bias = sm ? sm->t->bout + (size_t)sm->k * nout : h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
-    a.trace_id = 5;
     LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, R_OUT_PROJ, a, h->out_tiles, n_z, st));
   }
   return AE_OK;
@@ -945,7 +882,6 @@ int enqueue_draft(ae_handle* h, hipStream_t st, Timer* tm) {
     a.n_q = 0; a.n_kv = nkv; a.dh = dh; a.H = P; a.nbs = h->nbp; a.n_qt = 0;
     a.rope_cs = h->rope_feat;
     a.k_out = h->kcache; a.v_out = h->vcache;  // slot 0, layer 0: the cache's own block layout
-    a.trace_id = 0;
     LAUNCH_CHECK(h, "draft_feature_kv", (void)Dispatch::gemm(h, R_QKV_ROPE, a, 2 * nkv * tph, Pp / TOKG, st));
   }
   HIP_TRY(h, hipMemcpyAsync(h->h, h->q_h0, (size_t)Mp * w * 4, hipMemcpyDeviceToDevice, st));
@@ -1019,6 +955,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   if (const char* e = getenv("AE_EXCH_POLL")) h->poll_splitk = atoi(e) != 0;
   if (const char* e = getenv("AE_TILED")) h->tiled_roles = (int)strtol(e, nullptr, 0);
   if (const char* e = getenv("AE_TILED_SHAPE")) h->tiled_force = atoi(e);
+  if (const char* e = getenv("AE_ATTN_XCD")) h->attn_xcd = atoi(e) != 0;
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
   hipEventCreate(&h->ev0);
   hipEventCreate(&h->ev1);
@@ -1737,16 +1674,5 @@ int ae_kernel_times(ae_handle* h, int mode, int batch, int steps, int iters, ae_
   return rc ? rc : rc2;
 }
 
-#ifdef AE_TRACE
-// Debug export of the traced build only: copies the per-workgroup timestamps.
-int ae_debug_trace(unsigned long long* out) {
-  if (!out) return AE_ERR_INVALID_ARG;
-  return hipMemcpyFromSymbol(out, HIP_SYMBOL(ae_trace_buf), sizeof(unsigned long long) * 8 * 2048 * 8) == hipSuccess ? AE_OK : AE_ERR_HIP;
-}
-int ae_debug_trace_clear() {
-  static unsigned long long zeros[8][2048][8];
-  return hipMemcpyToSymbol(HIP_SYMBOL(ae_trace_buf), zeros, sizeof(zeros)) == hipSuccess ? AE_OK : AE_ERR_HIP;
-}
-#endif
 
 }  // extern "C"

@@ -67,21 +67,22 @@ enum ae_dtype { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 };
 
 typedef struct ae_config {
   int n_layers;     /* L decoder blocks */
-  int width;        /* hidden size w (multiple of 64) */
-  int n_q_heads;    /* query heads */
+  int width;        /* hidden size w (multiple of 256) */
+  int n_q_heads;    /* query heads (n_q_heads * head_dim a multiple of 256) */
   int n_kv_heads;   /* key/value heads (divides n_q_heads) */
-  int head_dim;     /* dh (multiple of 32) */
-  int mlp_dim;      /* GeGLU inner size F (multiple of 32) */
+  int head_dim;     /* dh: 32, 64, 128 or 256 */
+  int mlp_dim;      /* GeGLU inner size F (multiple of 256) */
   int action_dim;   /* A (1..64) */
-  int horizon;      /* H chunk rows (1..256) */
+  int horizon;      /* H chunk rows (1..256; a prefill stack: 1..1024 tokens) */
   int prefix_len;   /* P cached prefix tokens (>= 0) */
   int max_batch;    /* prefix slots = robots advanced together by ae_denoise (>= 1) */
-  int max_taus;     /* verification times per ae_verify call (0 disables ae_verify) */
+  int max_taus;     /* verification times per ae_verify call (0..64; 0 disables ae_verify) */
   float rope_base;  /* e.g. 10000 */
-  float rms_eps;    /* e.g. 1e-6 */
+  float rms_eps;    /* e.g. 1e-6 (>= 0) */
   int weight_dtype; /* AE_F32 | AE_BF16: q/k/v/o, action in/out, time MLP */
-  int mlp_dtype;    /* AE_F32 | AE_BF16 | AE_FP8_E4M3: gate / up / down */
-  int kv_dtype;     /* AE_F32 | AE_BF16: prefix cache */
+  int mlp_dtype;    /* AE_F32 | AE_BF16 | AE_FP8_E4M3: gate / up / down; AE_F32 exactly when
+                       weight_dtype is AE_F32 */
+  int kv_dtype;     /* prefix cache: equal to weight_dtype */
   int gripper_dim;  /* action dim holding the +-1 gripper channel, -1 = none */
   int time_mode;    /* 0: temb added to every action_in_proj row; 1: per-layer time modulation
                        (see ae_layer_weights.w_mod; bf16 weights and MLP, no ae_verify / ae_round) */
@@ -100,9 +101,9 @@ typedef struct ae_config {
 
 /* One decoder block. wq [n_q*dh][w], wk/wv [n_kv*dh][w], wo [w][n_q*dh],
  * wg/wu [F][w], wd [w][F]; *_scale are fp32 per output row, fp8 only (NULL otherwise).
- * time_mode 1 ("DM0.5" guide, section 5.2: time_mlp_in/out turn the flow time into a
- * modulation signal, and every layer has a time modulator; the form is this library's
- * reading): w_mod [6w][w] (weight_dtype) and b_mod [6w] map temb to
+ * time_mode 1 ("DM0.5" guide, section 5.2, where the time MLP conditions every layer; the
+ * linear scale/shift/gate form is this library's reading): w_mod [6w][w] (weight_dtype) and
+ * b_mod [6w] map temb to
  * (scale1, shift1, gate1, scale2, shift2, gate2); the attention input is
  * rmsnorm(h)*ln1*(1 + scale1) + shift1 and h += gate1 * o_proj(...), likewise for the MLP
  * with the second triple. qk_norm 1: q_norm, k_norm [dh] fp32 gains. Unused pointers NULL. */

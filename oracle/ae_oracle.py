@@ -47,8 +47,8 @@ design notes):
   queries]; queries attend to all of it, RoPE positions 0..P-1 for the features and P.. for the
   queries; the head is the final RMSNorm then a linear map with bias. Features enter as tokens of
   the block's width.
-* Time-modulated expert (time_mode 1; the guide names time_mlp_in/out as the source of a
-  modulation signal and a time modulator per layer, without its form): per layer a linear map of
+* Time-modulated expert (time_mode 1; the guide derives a per-layer conditioning signal from the
+  time MLP and leaves its form open): per layer a linear map of
   temb gives (scale, shift, gate) for each of the two sublayers, norm -> norm * (1 + scale) +
   shift, residual += gate * sublayer; the final norm gets (scale, shift) the same way; temb is
   then not added to the action tokens. QK-norm (qk_norm 1, Gemma3 text stack): RMSNorm of q and
@@ -211,9 +211,9 @@ def attention(q, k, v):
 
 
 def layer_modulation(cfg, Wd, l, temb):
-    """Per-layer time modulation (DM0.5 guide 5.2, "time_mlp_in / time_mlp_out turn the flow time into a
-    modulation signal" and "a time modulator in every layer"): a linear map of temb to
-    (scale1, shift1, gate1, scale2, shift2, gate2), each [w], for the attention and MLP sublayers."""
+    """Per-layer scale/shift/gate taken linearly from temb (DM0.5 guide 5.2, which derives a per-layer
+    conditioning signal from the time MLP without fixing its form): (scale1, shift1, gate1, scale2,
+    shift2, gate2), each [w], for the attention and MLP sublayers."""
     return np.split(linear(temb, Wd[f"layers.{l}.w_mod"], Wd[f"layers.{l}.b_mod"]), 6)
 
 

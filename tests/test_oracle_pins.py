@@ -49,6 +49,70 @@ def test_fp8_rows_roundtrip_within_half_ulp():
     assert np.all(np.abs(deq - w)[big] <= np.abs(w)[big] * 2.0 ** -4 + 1e-12)
 
 
+# An fp8-MLP config and its fp32 twin draw the same float32 weights (same seed, shapes and draw order;
+# only the storage format differs), so the fp32 twin's tensors are the unquantised originals.
+_FP8_CFG = C.TINY.with_(name="pin_fp8", n_layers=2, width=64, n_q_heads=2, n_kv_heads=1, head_dim=32, mlp_dim=128,
+                        action_dim=8, horizon=6, prefix_len=10, weight_dtype="bf16", mlp_dtype="fp8",
+                        kv_dtype="bf16")
+_F32_TWIN = _FP8_CFG.with_(name="pin_f32", weight_dtype="f32", mlp_dtype="f32", kv_dtype="f32")
+
+
+def test_dequantize_routes_mlp_through_e4m3_with_row_scales():
+    """DM0.5 guide 6.3 (E4M3 MLP weights with scales): gate/up/down decode as E4M3 codes times one
+    scale per output row, checked against torch's float8_e4m3fn decoder and against the unquantised
+    draw within E4M3's half-ulp; every other linear decodes as weight_dtype (torch's bfloat16 view),
+    and biases and gains stay as drawn."""
+    W = G.make_weights(_FP8_CFG)
+    Wd = O.dequantize_weights(_FP8_CFG, W)
+    W32 = G.make_weights(_F32_TWIN)
+    assert not any(n.endswith(".scale") for n in Wd)
+    for l in range(_FP8_CFG.n_layers):
+        for nm in ("wg", "wu", "wd"):
+            key = f"layers.{l}.{nm}"
+            codes, scale = W[key], W[key + ".scale"]
+            assert codes.dtype == np.uint8 and scale.shape == (codes.shape[0],)
+            ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * scale[:, None]
+            assert np.array_equal(Wd[key], ref), key
+            # against the float32 draw: relative error <= 2^-4 above the subnormal range, absolute
+            # <= 2^-10 * scale below it (per row: a column scale or a bf16 decode of the codes fails)
+            a = W32[key].astype(np.float64)
+            bound = np.maximum(np.abs(a) * 2.0 ** -4, scale[:, None].astype(np.float64) * 2.0 ** -10) * (1 + 1e-6)
+            assert np.all(np.abs(Wd[key] - a) <= bound), key
+            # each row's largest magnitude lands on +-448 * scale
+            assert np.allclose(np.abs(Wd[key]).max(axis=1), np.abs(a).max(axis=1), rtol=1e-6), key
+        for nm in ("wq", "wk", "wv", "wo"):
+            key = f"layers.{l}.{nm}"
+            assert W[key].dtype == np.uint16, key
+            ref = torch.from_numpy(W[key].view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+            assert np.array_equal(Wd[key], ref), key
+            a = W32[key].astype(np.float64)
+            assert np.all(np.abs(Wd[key] - a) <= np.abs(a) * 2.0 ** -8 * (1 + 1e-6)), key
+        for nm in ("ln1", "ln2"):
+            assert np.array_equal(Wd[f"layers.{l}.{nm}"], W[f"layers.{l}.{nm}"].astype(np.float64))
+    for key in ("time_in_w", "time_out_w", "action_in_w", "action_out_w"):
+        ref = torch.from_numpy(W[key].view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+        assert np.array_equal(Wd[key], ref), key
+    for key in ("time_in_b", "time_out_b", "action_in_b", "action_out_b", "final_ln"):
+        assert np.array_equal(Wd[key], W32[key].astype(np.float64)), key
+
+
+def test_fp8_velocity_is_the_fp32_velocity_of_the_dequantised_weights():
+    """The storage format enters the velocity only through dequantisation: the fp8 config's velocity
+    equals the fp32 twin's velocity when the twin is fed the fp8 config's dequantised tensors, and
+    differs from the twin's own (unquantised) velocity by about the E4M3 rounding."""
+    W = G.make_weights(_FP8_CFG)
+    Wd = O.dequantize_weights(_FP8_CFG, W)
+    k, v = G.make_prefix_kv(_FP8_CFG, 100)
+    kk, vv = O.decode_kv(_FP8_CFG, k, v)
+    x = G.make_noise(_FP8_CFG, 200, 1)[0].astype(np.float64)
+    got = O.velocity(_FP8_CFG, Wd, kk, vv, x, 0.3)
+    twin = O.velocity(_F32_TWIN, dict(Wd), kk, vv, x, 0.3)
+    assert np.array_equal(got, twin)
+    own = O.velocity(_F32_TWIN, O.dequantize_weights(_F32_TWIN, G.make_weights(_F32_TWIN)), kk, vv, x, 0.3)
+    rel = np.max(np.abs(got - own)) / np.sqrt(np.mean(own ** 2))
+    assert 0 < rel < 6e-2, rel
+
+
 # ---------------------------------------------------------------- elementwise
 
 def test_gelu_tanh_against_erf_gelu():

@@ -70,8 +70,8 @@ PI0_FP8 = PI0.with_(name="pi0_fp8mlp_2view", prefix_len=560, mlp_dtype="fp8")
 PI0_VERIFY = PI0.with_(name="pi0_verify", max_taus=4, gripper_dim=31)
 PI0_BATCH16 = PI0.with_(name="pi0_batch16", max_batch=16, batch=16)
 
-# DM0.5-style expert at the Pi0 shapes (DM0.5 guide, section 5.2: time_mlp_in/out turn the flow
-# time into a modulation signal, a per-layer time modulator, a Gemma3 text stack with QK-norm)
+# DM0.5-style expert at the Pi0 shapes (DM0.5 guide, section 5.2: the time MLP conditions every
+# layer, and the expert sits on a Gemma3 text stack, which normalises q and k per head)
 DM05 = PI0.with_(name="dm05_bf16", time_mode=1, qk_norm=1)
 
 # Draft model of the speculative round (FLASH article, section 03: one Gemma block and a linear action
