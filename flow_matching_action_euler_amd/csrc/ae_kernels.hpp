@@ -185,7 +185,8 @@ struct GemmArgs {
   unsigned* counters;   // [n_z][n_groups], zero between launches (arrival tickets)
   int exch_poll;        // 1: every workgroup is resident at once; split S-1 polls the others' partials
   int poll_delay;       // ~0.2 us steps split S-1 waits before its first poll (the partials' flight time)
-  unsigned* err;        // set if a poll gave up
+  unsigned* err;        // set if a poll gave up (host-visible)
+  unsigned long long wait;  // constant-clock ticks (100 MHz) a poll waits before it gives up
   // EPI_QKV
   void* q_out; void* k_out; void* v_out;   // attention operands in fragment order (see the attention section)
   const float* rope_cs;                    // [H][dh/2][2] cos, sin at positions P + t
@@ -254,7 +255,7 @@ __device__ __forceinline__ void st4_coherent(__amdgpu_buffer_rsrc_t r, unsigned 
 // arithmetic on finite inputs produces; a word is tested on its own, so a
 // 16-byte store seen half-written still reads as not arrived.
 constexpr unsigned EXCH_EMPTY = 0xffffffffu;
-constexpr unsigned long long EXCH_WAIT = 2000000;  // constant-clock ticks (100 MHz: 20 ms) before a poll gives up
+constexpr unsigned long long EXCH_WAIT = 2000000;  // default wait: constant-clock ticks (100 MHz: 20 ms) before a poll gives up
 __device__ __forceinline__ bool exch_arrived(float v) { return __float_as_uint(v) != EXCH_EMPTY; }
 __device__ __forceinline__ bool exch_arrived(f32x4 v) {
   return exch_arrived(v[0]) && exch_arrived(v[1]) && exch_arrived(v[2]) && exch_arrived(v[3]);
@@ -518,7 +519,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
           const int qd = threadIdx.x + GTHREADS * i;
           if (qd < NT * 256) {
             f32x4 v[3];
-            const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
+            const unsigned long long t_end = wall_clock64() + a.wait;
             for (;;) {
               bool ok = true;
 #pragma unroll
@@ -541,7 +542,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
               if (ss < a.S - 1) st16_empty(rp, poff(ss, qd));
           }
         }
-        if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         __syncthreads();
       } else {
         // split-K, more workgroups than fit at once: publish the partial, count arrivals; the
@@ -1162,7 +1163,8 @@ struct AttnArgs {
   float scale_log2;       // log2(e) / sqrt(dh)
   float* opart;           // [zz][qt][split][16][dh] split partials, EXCH_EMPTY between launches
   float* mlpart;          // [zz][qt][split][16][2]  (row max in log2 units, row sum), same
-  unsigned* err;          // set if a co-resident merge poll gave up
+  unsigned* err;          // set if a co-resident merge poll gave up (host-visible)
+  unsigned long long wait;  // constant-clock ticks (100 MHz) a merge poll waits before it gives up
   int coresident;         // 1: every workgroup is resident at once; splits merge in-kernel
   void* o;                // output, fragment order (act_idx)
   // QK-norm: per (q or k tile, token) sums of squares of the raw projections written by the QKV
@@ -1497,7 +1499,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       f32x4 oc[8];
       auto moff = [&](int c) { return (unsigned)(((tile * a.n_split + c) * ATT_ROWS + rr) * 8); };
       auto ooff = [&](int c) { return (unsigned)((((tile * a.n_split + c) * ATT_ROWS + rr) * DH + kc * 4) * 4); };
-      const unsigned long long t_end = wall_clock64() + EXCH_WAIT;
+      const unsigned long long t_end = wall_clock64() + a.wait;
       for (;;) {
         bool ok = true;
 #pragma unroll
@@ -1542,7 +1544,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       Act<AT>::st((XT*)a.o, act_idx(tok, col + 3, a.ntt), O2.w * inv);
     }
   }
-  if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (gave_up) __hip_atomic_store(a.err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
 }
 
 // Merge of the key-split partials of attn_kernel: o = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.

@@ -21,6 +21,7 @@
 
 #include "../../include/ae.h"
 #include "ae_kernels.hpp"
+#include "ae_fused.hpp"
 
 using namespace ae;
 
@@ -113,7 +114,26 @@ struct ae_handle {
   size_t n_counters = 0;
   float *opart = nullptr, *mlpart = nullptr;
   size_t opart_floats = 0, mlpart_floats = 0;
-  unsigned* err_flag = nullptr;     // set by a kernel whose bounded poll gave up
+  unsigned long long wait_ticks = EXCH_WAIT;  // bound of every in-kernel wait (100 MHz ticks)
+  unsigned* flag_host = nullptr;    // pinned host word, set by a kernel whose bounded wait gave up
+  unsigned* flag_dev = nullptr;     // its device address
+  // capture variant of the pass being enqueued: 0 = the persistent step kernel where eligible,
+  // 1 = one launch per phase, 2 = one launch per phase with no in-kernel waits (no co-resident
+  // exchanges: the pass a failed one is repeated with)
+  int variant = 0;
+  // persistent step kernel (batch-1 denoise)
+  bool fused_ok = false;            // shape, dtypes, occupancy and AE_FUSED allow it
+  std::string fused_why;            // why not, when fused_ok is false
+  int fused_fail = 0;               // consecutive passes whose persistent launch gave up
+  void (*fused_fn)(FusedArgs) = nullptr;
+  size_t fused_lds = 0;
+  FusedLayer* fused_layers = nullptr;  // device [L]
+  char* ring[2] = {nullptr, nullptr};  // activation rings of alternating launches
+  unsigned layer_bytes = 0, off_ssp = 0, off_q = 0, off_k = 0, off_v = 0, off_o = 0, off_hb2 = 0, off_ssp2 = 0, off_u = 0;
+  float *fpart_o = nullptr, *fpart_ml = nullptr;
+  size_t fpart_o_floats = 0, fpart_ml_floats = 0;
+  unsigned* abort_dev = nullptr;
+  int f_nsplit = 0, f_natt = 0;
   int n_qt = 0, nbp = 0, nbs = 0;  // 16-row query tiles, 32-key prefix / suffix blocks
   int n_cu = 0;
   // in-kernel partial exchanges (read from AE_ATTN_CORESIDENT / AE_EXCH_POLL at creation, 0 = off):
@@ -155,7 +175,7 @@ struct ae_handle {
   std::map<int, ModTable> mod_steps;
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
   float last_ms = 0.f;
-  hipEvent_t ev0 = nullptr, ev1 = nullptr;
+  hipEvent_t ev0 = nullptr, ev1 = nullptr, ev_round = nullptr;
   // inputs of the last call per mode, for ae_kernel_times
   int last_verify_slot = 0;
   float last_delta = 0.f;
@@ -196,11 +216,18 @@ int dalloc_t(ae_handle* h, T** p, size_t count) {
 // The split partial buffers hold EXCH_EMPTY in every word between launches (all bytes 0xff);
 // the GEMM arrival tickets hold zero. Synchronous.
 int reset_exchange(ae_handle* h) {
+  HIP_TRY(h, hipDeviceSynchronize());
   if (h->part) HIP_TRY(h, hipMemset(h->part, 0xff, h->part_floats * sizeof(float)));
+  for (int r = 0; r < 2; ++r)
+    if (h->ring[r]) HIP_TRY(h, hipMemset(h->ring[r], 0xff, (size_t)(h->c.n_layers + 1) * h->layer_bytes));
+  if (h->fpart_o) HIP_TRY(h, hipMemset(h->fpart_o, 0xff, h->fpart_o_floats * sizeof(float)));
+  if (h->fpart_ml) HIP_TRY(h, hipMemset(h->fpart_ml, 0xff, h->fpart_ml_floats * sizeof(float)));
+  if (h->abort_dev) HIP_TRY(h, hipMemset(h->abort_dev, 0, sizeof(unsigned)));
   if (h->opart) HIP_TRY(h, hipMemset(h->opart, 0xff, h->opart_floats * sizeof(float)));
   if (h->mlpart) HIP_TRY(h, hipMemset(h->mlpart, 0xff, h->mlpart_floats * sizeof(float)));
   if (h->counters) HIP_TRY(h, hipMemset(h->counters, 0, h->n_counters * sizeof(unsigned)));
   HIP_TRY(h, hipDeviceSynchronize());
+  if (h->flag_host) __atomic_store_n(h->flag_host, 0u, __ATOMIC_RELEASE);
   return AE_OK;
 }
 
@@ -466,10 +493,11 @@ struct AttnPlan {
 AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
   const int ns = attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT);
-  if (h->coresident_attn && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, ATT_IT_SPLIT, 1};
+  const bool may_wait = h->coresident_attn && h->variant != 2;
+  if (may_wait && ns >= 2 && ns <= 16 && ns * h->n_qt * zz <= h->n_cu) return {ns, ATT_IT_SPLIT, 1};
   // several sequences (verification): splits of 2 blocks per wave, if those fit on the device at once
   const int nm = attn_splits(nb, ATT_IT_MID, ATT_WAVES_SPLIT);
-  if (h->coresident_attn && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
+  if (may_wait && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
     return {nm, ATT_IT_MID, 1};
   return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
 }
@@ -539,9 +567,11 @@ struct Dispatch {
       const int gz = std::max(1, std::min(n_z, h->n_cu / std::max(n_groups, 1)));
       a.zpw = (n_z + gz - 1) / gz;
     }
-    a.exch_poll = h->poll_splitk && (long long)n_groups * a.S * n_z <= h->n_cu;  // one workgroup per CU fits them all
+    // one workgroup per CU fits them all (and the pass may wait inside a kernel)
+    a.exch_poll = h->poll_splitk && h->variant != 2 && (long long)n_groups * a.S * n_z <= h->n_cu;
     a.poll_delay = POLL_DELAY;
-    a.err = h->err_flag;
+    a.err = h->flag_dev;
+    a.wait = h->wait_ticks;
     if (h->at == AT_F32) {
       switch (role) {
         case R_QKV_ROPE: return launch_gemm<WT_F32, AT_F32, R_QKV_ROPE>(a, n_groups, n_z, st);
@@ -633,7 +663,8 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
   aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && h->attn_xcd;
-  aa.err = h->err_flag;
+  aa.err = h->flag_dev;
+  aa.wait = h->wait_ticks;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
   aa.opart = h->opart; aa.mlpart = h->mlpart; aa.o = h->o;
   if (c.qk_norm) {
@@ -827,7 +858,143 @@ int get_temb_steps(ae_handle* h, int steps, float** out) {
   return AE_OK;
 }
 
+// The persistent step kernel of batch-1 denoise passes: the instantiation for the handle's shapes
+// and dtypes, every workgroup of its grid resident at once (one per compute unit), the activation
+// rings, the attention split partials and the per-layer table. fused_ok stays false, and the passes
+// take one launch per phase, when any of it does not hold.
+int setup_fused(ae_handle* h) {
+  const ae_config& c = h->c;
+  const int w = c.width, F = c.mlp_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim, H = c.horizon;
+  const int L = c.n_layers;
+  auto no = [&](const char* why) {
+    h->fused_why = why;
+    return AE_OK;
+  };
+  if (c.draft || c.prefill || c.time_mode || c.qk_norm || c.weight_dtype != AE_BF16 || c.kv_dtype != AE_BF16 ||
+      (c.mlp_dtype != AE_BF16 && c.mlp_dtype != AE_FP8_E4M3))
+    return no("model variant or dtypes");
+  if (H > 64 || c.prefix_len < 1 || h->n_cu < 32 || h->n_cu % 32) return no("horizon, prefix or compute-unit count");
+  // instantiated shapes: head_dim 256, width 1024, n_q_heads * head_dim 2048, mlp_dim 4096
+  const bool fp8 = c.mlp_dtype == AE_FP8_E4M3;
+  if (dh == 256 && w == 1024 && nq * dh == 2048 && F == 4096) {
+    h->fused_fn = fp8 ? fused_step_kernel<256, WT_FP8, 4, 8, 16> : fused_step_kernel<256, WT_BF16, 4, 8, 16>;
+    h->fused_lds = fused_lds_bytes<256>();
+  } else {
+    return no("shapes without an instantiation");
+  }
+  const int ntt = (H + 15) / 16, ntp = ntt <= 1 ? 1 : ntt <= 2 ? 2 : 4, G = h->n_cu;
+  const int nb = h->nbp + h->nbs;
+  h->f_nsplit = (nb + FW - 1) / FW;
+  if (const char* e = getenv("AE_FUSED_SPLITS")) h->f_nsplit = std::max(h->f_nsplit, std::min(nb, atoi(e)));
+  h->f_natt = h->f_nsplit * h->n_qt * nkv;
+  if (w / 16 > F_SLOTS * (G / ntp) || h->f_natt > 4 * G || h->out_tiles > G / ntp || h->nbp < 1)
+    return no("work split does not fit the grid");
+  // a failed query leaves its error for the next hipGetLastError: read it back here
+  const hipError_t ea = hipFuncSetAttribute((const void*)h->fused_fn, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                            (int)h->fused_lds);
+  (void)hipGetLastError();
+  if (ea != hipSuccess) return no("dynamic LDS attribute refused");
+  // one workgroup per compute unit: its threads, registers (2 waves per SIMD: at most 256 VGPRs) and
+  // LDS must fit one compute unit (the kernel's own attributes against the device's)
+  hipFuncAttributes fat{};
+  int lds_cu = 0;
+  const hipError_t ef = hipFuncGetAttributes(&fat, (const void*)h->fused_fn);
+  const hipError_t ed = hipDeviceGetAttribute(&lds_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, h->dev);
+  (void)hipGetLastError();
+  if (ef != hipSuccess || ed != hipSuccess) return no("kernel or device attribute query failed");
+  if (fat.maxThreadsPerBlock < FT || fat.numRegs > 256 || fat.localSizeBytes > 0 ||
+      fat.sharedSizeBytes + h->fused_lds > (size_t)lds_cu)
+    return no("a workgroup does not fit a compute unit");
+  // one block of the ring per layer (and one for the final norm's input), each buffer 256-byte aligned
+  const size_t Mp = (size_t)ntt * 16;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) / 256 * 256;
+    return (unsigned)o;
+  };
+  take(Mp * w * 2);  // hb_in: the layer's input rows * ln1, fragment order
+  h->off_ssp = take((size_t)(w / 16) * Mp * 4);
+  h->off_q = take((size_t)nkv * h->n_qt * ATT_ROWS * dh * 2);
+  h->off_k = take((size_t)nkv * h->nbs * ATT_KB * dh * 2);
+  h->off_v = take((size_t)nkv * h->nbs * ATT_KB * dh * 2);
+  h->off_o = take(Mp * nq * dh * 2);
+  h->off_hb2 = take(Mp * w * 2);
+  h->off_ssp2 = take((size_t)(w / 16) * Mp * 4);
+  h->off_u = take(Mp * F * 2);
+  h->layer_bytes = (unsigned)off;
+  for (int r = 0; r < 2; ++r) {
+    const int rc = dalloc(h, (void**)&h->ring[r], (size_t)(L + 1) * off);
+    if (rc) return rc;
+  }
+  h->fpart_o_floats = (size_t)L * h->f_natt * ATT_ROWS * dh;
+  h->fpart_ml_floats = (size_t)L * h->f_natt * ATT_ROWS * 2;
+  int rc = dalloc_t(h, &h->fpart_o, h->fpart_o_floats);
+  if (!rc) rc = dalloc_t(h, &h->fpart_ml, h->fpart_ml_floats);
+  if (!rc) rc = dalloc_t(h, &h->abort_dev, 1);
+  if (rc) return rc;
+  std::vector<FusedLayer> ly(L);
+  const size_t lay = (size_t)nkv * h->nbp * ATT_KB * dh;  // elements of one layer of a slot's packed cache
+  for (int l = 0; l < L; ++l) {
+    ly[l].qkv = (const uint16_t*)h->qkv_p[l];
+    ly[l].o = (const uint16_t*)h->o_p[l];
+    ly[l].gu = h->gu_p[l];
+    ly[l].d = h->d_p[l];
+    ly[l].gu_s = h->gu_s[l];
+    ly[l].d_s = h->d_s[l];
+    ly[l].ln2 = h->ln2[l];
+    ly[l].g_next = l + 1 < L ? h->ln1[l + 1] : h->final_ln;
+    ly[l].kc = (const uint16_t*)h->kcache + (size_t)l * lay;
+    ly[l].vc = (const uint16_t*)h->vcache + (size_t)l * lay;
+  }
+  rc = upload(h, (void**)&h->fused_layers, ly.data(), L * sizeof(FusedLayer));
+  if (rc) return rc;
+  h->fused_ok = true;
+  return AE_OK;
+}
+
+// The batch-1 denoise as `steps` launches of the persistent step kernel (one per Euler step) on
+// prefix slot slot0. Launch k polls activation ring k % 2 and empties ring (k + 1) % 2, which the
+// previous launch used; ring 0 is empty when a pass starts, so a pass with an odd step count ends
+// with a fill of ring 0 (its last launch used it).
+int enqueue_fused(ae_handle* h, int steps, const float* temb, hipStream_t st, Timer* tm, int slot0) {
+  const ae_config& c = h->c;
+  FusedArgs fa{};
+  fa.layers = h->fused_layers;
+  fa.L = c.n_layers; fa.w = c.width; fa.F = c.mlp_dim; fa.nq = c.n_q_heads; fa.nkv = c.n_kv_heads; fa.dh = c.head_dim;
+  fa.H = c.horizon; fa.P = c.prefix_len; fa.A = c.action_dim;
+  fa.ntt = (c.horizon + 15) / 16;
+  fa.ntp = fa.ntt <= 1 ? 1 : fa.ntt <= 2 ? 2 : 4;
+  fa.G = h->n_cu;
+  fa.eps = c.rms_eps; fa.inv_w = 1.f / (float)c.width;
+  fa.x = h->x;
+  fa.w_in = (const uint16_t*)h->action_in_w; fa.b_in = h->action_in_b; fa.ln1_0 = h->ln1[0];
+  fa.w_out = (const uint16_t*)h->action_out_p; fa.b_out = h->action_out_b; fa.out_tiles = h->out_tiles;
+  fa.dt = 1.f / (float)steps;
+  fa.rope_cs = h->rope_cs;
+  fa.n_qt = h->n_qt; fa.nbp = h->nbp; fa.nbs = h->nbs; fa.n_split = h->f_nsplit; fa.n_att = h->f_natt;
+  fa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)c.head_dim));
+  fa.part_o = h->fpart_o; fa.part_ml = h->fpart_ml;
+  fa.layer_bytes = h->layer_bytes;
+  fa.off_ssp = h->off_ssp; fa.off_q = h->off_q; fa.off_k = h->off_k; fa.off_v = h->off_v; fa.off_o = h->off_o;
+  fa.off_hb2 = h->off_hb2; fa.off_ssp2 = h->off_ssp2; fa.off_u = h->off_u;
+  fa.abort = h->abort_dev; fa.host_flag = h->flag_dev; fa.wait_ticks = h->wait_ticks;
+  fa.slot_off = (size_t)slot0 * h->slot_elems;
+  for (int k = 0; k < steps; ++k) {
+    fa.temb = temb + (size_t)k * c.width;
+    fa.ring = h->ring[k & 1];
+    fa.ring_other = h->ring[(k + 1) & 1];
+    LAUNCH_CHECK(h, "fused_step", AE_LAUNCH(h->fused_fn, dim3(h->n_cu), dim3(FT), h->fused_lds, st, fa));
+  }
+  if (steps & 1) {
+    const size_t n16 = (size_t)(c.n_layers + 1) * h->layer_bytes / 16;
+    LAUNCH_CHECK(h, "fill_empty", AE_LAUNCH(fill_empty_kernel, dim3(1024), dim3(256), 0, st, (uint4*)h->ring[0], n16));
+  }
+  return AE_OK;
+}
+
 int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t st, Timer* tm, int slot0 = 0) {
+  if (batch == 1 && h->variant == 0 && h->fused_ok) return enqueue_fused(h, steps, temb, st, tm, slot0);
   const float dt = 1.f / (float)steps;
   for (int k = 0; k < steps; ++k) {
     // robot b uses prefix slot b: no slot table (the attention then reads no slot from memory)
@@ -901,8 +1068,12 @@ int enqueue_prefill(ae_handle* h, hipStream_t st, Timer* tm) {
   return enqueue_velocity(h, 1, nullptr, 0, nullptr, 0, 0.f, st, tm, nullptr, true, false);
 }
 
-int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
-  auto key = std::make_tuple(mode, a, b);
+// The capture variant a call starts with: the persistent step kernel unless it gave up on three
+// passes in a row (the device is shared, say), then one launch per phase.
+int pref_variant(const ae_handle* h) { return h->fused_fail >= 3 ? 1 : 0; }
+
+int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out, int variant) {
+  auto key = std::make_tuple(mode + 16 * variant, a, b);
   auto it = h->graphs.find(key);
   if (it != h->graphs.end()) { *out = it->second; return AE_OK; }
   // mode 0: denoise (a steps, b robots on slots 0..b-1); 1: verify (a flow times);
@@ -913,11 +1084,13 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out) {
     if (rc) return rc;
   }
   HIP_TRY(h, hipStreamBeginCapture(h->stream, hipStreamCaptureModeThreadLocal));
+  h->variant = variant;
   int rc = mode == 0   ? enqueue_denoise(h, b, a, temb, h->stream, nullptr)
            : mode == 2 ? enqueue_denoise(h, 1, a, temb, h->stream, nullptr, b)
            : mode == 3 ? enqueue_draft(h, h->stream, nullptr)
            : mode == 4 ? enqueue_prefill(h, h->stream, nullptr)
                        : enqueue_verify(h, a, h->stream, nullptr);
+  h->variant = 0;
   hipGraph_t graph = nullptr;
   hipError_t e = hipStreamEndCapture(h->stream, &graph);
   if (rc) { if (graph) hipGraphDestroy(graph); return rc; }
@@ -956,9 +1129,13 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   if (const char* e = getenv("AE_TILED")) h->tiled_roles = (int)strtol(e, nullptr, 0);
   if (const char* e = getenv("AE_TILED_SHAPE")) h->tiled_force = atoi(e);
   if (const char* e = getenv("AE_ATTN_XCD")) h->attn_xcd = atoi(e) != 0;
+  if (const char* e = getenv("AE_WAIT_TICKS")) h->wait_ticks = strtoull(e, nullptr, 0);
+  bool want_fused = true;
+  if (const char* e = getenv("AE_FUSED")) want_fused = atoi(e) != 0;
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
   hipEventCreate(&h->ev0);
   hipEventCreate(&h->ev1);
+  hipEventCreate(&h->ev_round);
   h->at = c.weight_dtype == AE_F32 ? AT_F32 : AT_BF16;
   h->wt = c.weight_dtype == AE_F32 ? WT_F32 : WT_BF16;
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
@@ -1121,8 +1298,12 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     h->mlpart_floats = n_zz * n_qt * n_split * ATT_ROWS * 2;
     TRY(dalloc_t(h, &h->opart, h->opart_floats));
     TRY(dalloc_t(h, &h->mlpart, h->mlpart_floats));
-    TRY(dalloc_t(h, &h->err_flag, 1));
-    TRY(reset_exchange(h));
+    if (hipHostMalloc((void**)&h->flag_host, sizeof(unsigned), hipHostMallocMapped) != hipSuccess ||
+        hipHostGetDevicePointer((void**)&h->flag_dev, h->flag_host, 0) != hipSuccess) {
+      ae_destroy(h);
+      return fail(nullptr, AE_ERR_HIP, "pinned host flag allocation failed");
+    }
+    *h->flag_host = 0;
   }
   {
     std::vector<float> cs((size_t)H * (dh / 2) * 2);
@@ -1180,6 +1361,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc(h, &h->pf_k, (size_t)L * h->pf_layer_elems * kes));
     TRY(dalloc(h, &h->pf_v, (size_t)L * h->pf_layer_elems * kes));
   }
+  if (want_fused) TRY(setup_fused(h));
+  TRY(reset_exchange(h));
   if (hipDeviceSynchronize() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "device sync after upload failed"); }
 #undef TRY
   *out = h;
@@ -1221,18 +1404,24 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   return AE_OK;
 }
 
-// A kernel whose poll for another workgroup's partial gave up (the workgroups of the launch
-// were not all resident) leaves a flag: report it and restore the exchange buffers, which
-// may then hold partials nobody consumed.
-static int check_err_flag(ae_handle* h) {
-  unsigned e = 0;
-  HIP_TRY(h, hipMemcpy(&e, h->err_flag, sizeof(e), hipMemcpyDeviceToHost));
-  if (!e) return AE_OK;
-  HIP_TRY(h, hipMemset(h->err_flag, 0, sizeof(e)));
-  const int rc = reset_exchange(h);
-  if (rc) return rc;
-  return fail(h, AE_ERR_HIP, "split partial exchange: workgroups were not co-resident (poll gave up); "
-                             "set AE_ATTN_CORESIDENT=0 and AE_EXCH_POLL=0");
+// A kernel whose bounded wait gave up (not every workgroup of its launch was resident, say) sets the
+// host-visible flag. A synchronous call that finds it set after its pass waits for the device,
+// restores every exchange buffer and repeats the pass with launches that wait for nothing inside a
+// kernel (variant 2); its outputs are then those of the repeated pass. An asynchronous call cannot
+// repeat its pass: the next call on the handle finds the flag and reports it (failed_async).
+static bool take_failure(ae_handle* h) {
+  if (!h->flag_host || !__atomic_load_n(h->flag_host, __ATOMIC_ACQUIRE)) return false;
+  reset_exchange(h);
+  return true;
+}
+
+static int failed_async(ae_handle* h) {
+  if (!take_failure(h)) return AE_OK;
+  ++h->fused_fail;
+  return fail(h, AE_ERR_HIP,
+              "an earlier asynchronous pass on this handle gave up waiting for another workgroup of its launch "
+              "(not all were resident); the outputs of the asynchronous passes enqueued since the last successful "
+              "call are invalid; the exchange buffers are restored");
 }
 
 static int check_denoise(ae_handle* h, int batch, int steps) {
@@ -1246,13 +1435,21 @@ static int check_denoise(ae_handle* h, int batch, int steps) {
   return AE_OK;
 }
 
+// Count the outcome of a pass that used the persistent step kernel.
+static void note_fused(ae_handle* h, int variant, int batch, bool failed) {
+  if (variant != 0 || batch != 1 || !h->fused_ok) return;
+  h->fused_fail = failed ? h->fused_fail + 1 : 0;
+}
+
 int ae_denoise_async(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out, void* stream) {
   int rc = check_denoise(h, batch, steps);
   if (rc) return rc;
   if (!d_noise || !d_actions_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  rc = failed_async(h);
+  if (rc) return rc;
   hipStream_t st = stream ? (hipStream_t)stream : h->stream;
   hipGraphExec_t g;
-  rc = get_graph(h, 0, steps, batch, &g);
+  rc = get_graph(h, 0, steps, batch, &g, pref_variant(h));
   if (rc) return rc;
   const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
   HIP_TRY(h, hipMemcpyAsync(h->x, d_noise, bytes, hipMemcpyDeviceToDevice, st));
@@ -1265,22 +1462,25 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   int rc = check_denoise(h, batch, steps);
   if (rc) return rc;
   if (!noise || !actions_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
-  hipGraphExec_t g;
-  rc = get_graph(h, 0, steps, batch, &g);
+  rc = failed_async(h);
   if (rc) return rc;
   const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
-  HIP_TRY(h, hipMemcpyAsync(h->x, noise, bytes, hipMemcpyHostToDevice, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(g, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
   std::vector<float> tmp(bytes / sizeof(float));
-  HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipStreamSynchronize(h->stream));
-  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  {
-    const int rc_err = check_err_flag(h);
-    if (rc_err) return rc_err;
+  for (int variant = pref_variant(h);; variant = 2) {
+    hipGraphExec_t g;
+    rc = get_graph(h, 0, steps, batch, &g, variant);
+    if (rc) return rc;
+    HIP_TRY(h, hipMemcpyAsync(h->x, noise, bytes, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    const bool failed = take_failure(h);
+    note_fused(h, variant, batch, failed);
+    if (!failed || variant == 2) break;
   }
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
   memcpy(actions_out, tmp.data(), bytes);
   return AE_OK;
 }
@@ -1315,9 +1515,11 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
   int rc = check_verify(h, slot, n_tau);
   if (rc) return rc;
   if (!d_draft || !d_noise || !d_taus || !d_accept_len || !d_gripper_switch) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  rc = failed_async(h);
+  if (rc) return rc;
   hipStream_t st = stream ? (hipStream_t)stream : h->stream;
   hipGraphExec_t g;
-  rc = get_graph(h, 1, n_tau, 1, &g);
+  rc = get_graph(h, 1, n_tau, 1, &g, pref_variant(h));
   if (rc) return rc;
   rc = verify_common(h, slot, n_tau, delta, st, hipMemcpyDeviceToDevice, d_draft, d_noise, d_taus);
   if (rc) return rc;
@@ -1329,6 +1531,24 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
   return AE_OK;
 }
 
+// The verification pass on the library's stream, repeated with no in-kernel waits if a wait gave up;
+// the inputs are on the device already (verify_common). Reads back the decision (and D).
+static int run_verify(ae_handle* h, int n_tau, int* acc, int* sw, float* dist) {
+  for (int variant = pref_variant(h);; variant = 2) {
+    hipGraphExec_t g;
+    int rc = get_graph(h, 1, n_tau, 1, &g, variant);
+    if (rc) return rc;
+    HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
+    if (dist) HIP_TRY(h, hipMemcpyAsync(dist, h->dist, (size_t)n_tau * h->c.horizon * sizeof(float), hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    if (!take_failure(h) || variant == 2) return AE_OK;
+  }
+}
+
 int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, const float* taus, int n_tau, float delta,
               int* accept_len, int* gripper_switch, float* dist_out) {
   int rc = check_verify(h, slot, n_tau);
@@ -1336,25 +1556,15 @@ int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, co
   if (!draft || !noise || !taus || !accept_len || !gripper_switch) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
   for (int j = 0; j < n_tau; ++j)
     if (!(taus[j] >= 0.f && taus[j] < 1.f)) return fail(h, AE_ERR_INVALID_ARG, "tau must lie in [0, 1)");
-  hipGraphExec_t g;
-  rc = get_graph(h, 1, n_tau, 1, &g);
+  rc = failed_async(h);
   if (rc) return rc;
   rc = verify_common(h, slot, n_tau, delta, h->stream, hipMemcpyHostToDevice, draft, noise, taus);
   if (rc) return rc;
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(g, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
   int acc = 0, sw = 0;
   std::vector<float> d((size_t)n_tau * h->c.horizon);
-  HIP_TRY(h, hipMemcpyAsync(&acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipMemcpyAsync(&sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipMemcpyAsync(d.data(), h->dist, d.size() * sizeof(float), hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  rc = run_verify(h, n_tau, &acc, &sw, d.data());
+  if (rc) return rc;
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  {
-    const int rc_err = check_err_flag(h);
-    if (rc_err) return rc_err;
-  }
   *accept_len = acc;
   *gripper_switch = sw;
   if (dist_out) memcpy(dist_out, d.data(), d.size() * sizeof(float));
@@ -1371,40 +1581,47 @@ int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_veri
     return fail(h, AE_ERR_INVALID_ARG, "null pointer");
   for (int j = 0; j < n_tau; ++j)
     if (!(taus[j] >= 0.f && taus[j] < 1.f)) return fail(h, AE_ERR_INVALID_ARG, "tau must lie in [0, 1)");
+  rc = failed_async(h);
+  if (rc) return rc;
   // both graphs exist before the round starts (the first round of a shape captures them)
   hipGraphExec_t gv, gd;
-  rc = get_graph(h, 1, n_tau, 1, &gv);
+  const int var = pref_variant(h);
+  rc = get_graph(h, 1, n_tau, 1, &gv, var);
   if (rc) return rc;
-  rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd) : get_graph(h, 2, steps, slot, &gd);
+  rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd, var) : get_graph(h, 2, steps, slot, &gd, var);
   if (rc) return rc;
   rc = verify_common(h, slot, n_tau, delta, h->stream, hipMemcpyHostToDevice, draft, noise_verify, taus);
   if (rc) return rc;
   const size_t ha = (size_t)h->c.horizon * h->c.action_dim * sizeof(float);
   // fast path: the verification pass, then the host reads the decision
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(gv, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
   int acc = 0, sw = 0;
-  HIP_TRY(h, hipMemcpyAsync(&acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipMemcpyAsync(&sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipStreamSynchronize(h->stream));
-  rc = check_err_flag(h);
+  HIP_TRY(h, hipEventRecord(h->ev_round, h->stream));
+  rc = run_verify(h, n_tau, &acc, &sw, nullptr);
   if (rc) return rc;
   // an empty accepted prefix (a gripper switch forces it) falls back to the full denoise loop
   const int full = acc == 0;
   std::vector<float> out(ha / sizeof(float));
   if (full) {
-    HIP_TRY(h, hipMemcpyAsync(h->x, noise_full, ha, hipMemcpyHostToDevice, h->stream));
-    HIP_TRY(h, hipGraphLaunch(gd, h->stream));
-    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
-    HIP_TRY(h, hipMemcpyAsync(out.data(), h->x, ha, hipMemcpyDeviceToHost, h->stream));
-    HIP_TRY(h, hipStreamSynchronize(h->stream));
-    rc = check_err_flag(h);
-    if (rc) return rc;
+    for (int variant = var;; variant = 2) {
+      if (variant != var) {
+        rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd, variant) : get_graph(h, 2, steps, slot, &gd, variant);
+        if (rc) return rc;
+      }
+      HIP_TRY(h, hipMemcpyAsync(h->x, noise_full, ha, hipMemcpyHostToDevice, h->stream));
+      HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+      HIP_TRY(h, hipGraphLaunch(gd, h->stream));
+      HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+      HIP_TRY(h, hipMemcpyAsync(out.data(), h->x, ha, hipMemcpyDeviceToHost, h->stream));
+      HIP_TRY(h, hipStreamSynchronize(h->stream));
+      const bool failed = take_failure(h);
+      note_fused(h, variant, 1, failed);
+      if (!failed || variant == 2) break;
+    }
   } else {
     memcpy(out.data(), draft, ha);
   }
-  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
+  // the round on the device timeline: verification, the host decision and the full pass if any
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev_round, h->ev1));
   memcpy(actions_out, out.data(), ha);
   *accept_len = acc;
   *gripper_switch = sw;
@@ -1416,23 +1633,45 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (!h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "not a draft-model handle (ae_config.draft = 0)");
   if (!features || !chunk_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
-  hipGraphExec_t g;
-  int rc = get_graph(h, 3, 0, 0, &g);
+  int rc = failed_async(h);
   if (rc) return rc;
   const ae_config& c = h->c;
-  HIP_TRY(h, hipMemcpyAsync(h->feat, features, (size_t)c.prefix_len * c.width * 4, hipMemcpyHostToDevice, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(g, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
   const size_t bytes = (size_t)c.horizon * c.action_dim * sizeof(float);
   std::vector<float> tmp(bytes / sizeof(float));
-  HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->vout, bytes, hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipStreamSynchronize(h->stream));
+  for (int variant = 0;; variant = 2) {
+    hipGraphExec_t g;
+    rc = get_graph(h, 3, 0, 0, &g, variant);
+    if (rc) return rc;
+    HIP_TRY(h, hipMemcpyAsync(h->feat, features, (size_t)c.prefix_len * c.width * 4, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+    HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->vout, bytes, hipMemcpyDeviceToHost, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    if (!take_failure(h) || variant == 2) break;
+  }
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  rc = check_err_flag(h);
-  if (rc) return rc;
   h->slot_ready[0] = 1;
   memcpy(chunk_out, tmp.data(), bytes);
+  return AE_OK;
+}
+
+// The prefill stack's pass over host embeddings emb, on the library's stream, repeated with no
+// in-kernel waits if a wait gave up; every layer's K/V is then in pf_k / pf_v.
+static int run_prefill(ae_handle* h, const float* emb) {
+  const ae_config& c = h->c;
+  for (int variant = 0;; variant = 2) {
+    hipGraphExec_t g;
+    int rc = get_graph(h, 4, 0, 0, &g, variant);
+    if (rc) return rc;
+    HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)c.horizon * c.width * 4, hipMemcpyHostToDevice, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
+    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+    HIP_TRY(h, hipStreamSynchronize(h->stream));
+    if (!take_failure(h) || variant == 2) break;
+  }
+  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
   return AE_OK;
 }
 
@@ -1453,19 +1692,13 @@ int ae_prefill_to_slot(ae_handle* h, const float* emb, ae_handle* expert, int sl
   const size_t bytes = expert->slot_elems * dtype_size(e.kv_dtype);
   if (bytes != (size_t)c.n_layers * h->pf_layer_elems * dtype_size(c.kv_dtype))
     return fail(h, AE_ERR_UNSUPPORTED, "cache layouts differ");
-  hipGraphExec_t g;
-  int rc = get_graph(h, 4, 0, 0, &g);
+  int rc = failed_async(h);
   if (rc) return rc;
-  HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)c.horizon * c.width * 4, hipMemcpyHostToDevice, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(g, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
+  rc = run_prefill(h, emb);
+  if (rc) return rc;
   HIP_TRY(h, hipMemcpyAsync((char*)expert->kcache + slot * bytes, h->pf_k, bytes, hipMemcpyDeviceToDevice, h->stream));
   HIP_TRY(h, hipMemcpyAsync((char*)expert->vcache + slot * bytes, h->pf_v, bytes, hipMemcpyDeviceToDevice, h->stream));
   HIP_TRY(h, hipStreamSynchronize(h->stream));
-  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  rc = check_err_flag(h);
-  if (rc) return rc;
   expert->slot_ready[slot] = 1;
   return AE_OK;
 }
@@ -1474,23 +1707,16 @@ int ae_prefill(ae_handle* h, const float* emb, void* k_out, void* v_out) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (!h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "not a prefill handle (ae_config.prefill = 0)");
   if (!emb || !k_out || !v_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
-  hipGraphExec_t g;
-  int rc = get_graph(h, 4, 0, 0, &g);
+  int rc = failed_async(h);
   if (rc) return rc;
   const ae_config& c = h->c;
   const int L = c.n_layers, P = c.horizon, nkv = c.n_kv_heads, dh = c.head_dim, nkb = dh / 32, nbs = h->nbs;
   const size_t es = dtype_size(c.kv_dtype), all = (size_t)L * h->pf_layer_elems * es;
-  HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)P * c.width * 4, hipMemcpyHostToDevice, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-  HIP_TRY(h, hipGraphLaunch(g, h->stream));
-  HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
-  std::vector<unsigned char> kp(all), vp(all);
-  HIP_TRY(h, hipMemcpyAsync(kp.data(), h->pf_k, all, hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipMemcpyAsync(vp.data(), h->pf_v, all, hipMemcpyDeviceToHost, h->stream));
-  HIP_TRY(h, hipStreamSynchronize(h->stream));
-  HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
-  rc = check_err_flag(h);
+  rc = run_prefill(h, emb);
   if (rc) return rc;
+  std::vector<unsigned char> kp(all), vp(all);
+  HIP_TRY(h, hipMemcpy(kp.data(), h->pf_k, all, hipMemcpyDeviceToHost));
+  HIP_TRY(h, hipMemcpy(vp.data(), h->pf_v, all, hipMemcpyDeviceToHost));
   // from the cache blocks' fragment order back to [L][P][n_kv][dh] (the inverse of ae_load_prefix_kv)
   unsigned char* ko = (unsigned char*)k_out;
   unsigned char* vo = (unsigned char*)v_out;
@@ -1515,8 +1741,10 @@ void ae_destroy(ae_handle* h) {
   if (h->stream) hipStreamSynchronize(h->stream);
   for (auto& kv : h->graphs) hipGraphExecDestroy(kv.second);
   for (void* p : h->allocs) hipFree(p);
+  if (h->flag_host) hipHostFree(h->flag_host);
   if (h->ev0) hipEventDestroy(h->ev0);
   if (h->ev1) hipEventDestroy(h->ev1);
+  if (h->ev_round) hipEventDestroy(h->ev_round);
   if (h->stream) hipStreamDestroy(h->stream);
   delete h;
 }
@@ -1608,6 +1836,7 @@ static int kernel_times_impl(ae_handle* h, int mode, int batch, int steps, int i
   }
   float* temb = nullptr;
   if (mode == 0) { rc = get_temb_steps(h, steps, &temb); if (rc) return rc; }
+  h->variant = pref_variant(h);
   auto enqueue = [&](Timer* tm) {
     return mode == 0 ? enqueue_denoise(h, batch, steps, temb, h->stream, tm) : enqueue_verify(h, batch, h->stream, tm);
   };
