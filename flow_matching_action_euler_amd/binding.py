@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libae.so")
 AE_OK = 0
 ERRORS = {-1: "AE_ERR_INVALID_ARG", -2: "AE_ERR_UNSUPPORTED", -3: "AE_ERR_NOT_READY", -4: "AE_ERR_OOM", -5: "AE_ERR_HIP"}
 DTYPES = {"f32": 0, "bf16": 1, "fp8": 2}
-EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_verify", "ae_verify_async", "ae_round",
+EXPORTS = ("ae_create", "ae_load_prefix_kv", "ae_denoise", "ae_denoise_async", "ae_denoise_static", "ae_verify", "ae_verify_async", "ae_round",
            "ae_draft", "ae_prefill", "ae_prefill_to_slot",
            "ae_destroy", "ae_last_error", "ae_last_gpu_ms", "ae_kernel_times")
 
@@ -71,6 +71,7 @@ def load_library(path=LIB_PATH):
         "ae_load_prefix_kv": (I, [P, I, P, P]),
         "ae_denoise": (I, [P, I, P, I, P]),
         "ae_denoise_async": (I, [P, I, P, I, P, P]),
+        "ae_denoise_static": (I, [P, I, P, I, P, P]),
         "ae_verify": (I, [P, I, P, P, P, I, F, P, P, P]),
         "ae_verify_async": (I, [P, I, P, P, P, I, F, P, P, P, P]),
         "ae_round": (I, [P, I, P, P, P, I, F, P, I, P, P, P, P]),
@@ -180,6 +181,12 @@ class ActionExpert:
         """Device-pointer variant (ints from e.g. torch ``tensor.data_ptr()``)."""
         self._check(self.lib.ae_denoise_async(self.h, batch, ctypes.c_void_p(d_noise), steps,
                                               ctypes.c_void_p(d_out), ctypes.c_void_p(stream) if stream else None))
+
+    def denoise_static(self, batch, d_noise, steps, d_out, stream=None):
+        """ae_denoise_static: as denoise_async, with the pass's scratch in the library's static
+        device array instead of the handle's buffers (no allocation)."""
+        self._check(self.lib.ae_denoise_static(self.h, batch, ctypes.c_void_p(d_noise), steps,
+                                               ctypes.c_void_p(d_out), ctypes.c_void_p(stream) if stream else None))
 
     def verify(self, slot, draft, noise, taus, delta, want_dist=True):
         draft, noise, taus = _c(draft, np.float32), _c(noise, np.float32), _c(taus, np.float32)

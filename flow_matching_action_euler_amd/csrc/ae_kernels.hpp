@@ -1670,6 +1670,17 @@ __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void
   }
 }
 
+// t[k] = k / steps, the Euler step times (rounded from fp64, as the host computes them).
+__global__ void step_times_kernel(float* t, int steps) {
+  for (int k = threadIdx.x; k < steps; k += blockDim.x) t[k] = (float)((double)k / (double)steps);
+}
+
+// v in every 32-bit word of n16 16-byte units (a clear that graph capture records as a kernel).
+__global__ void fill16_kernel(uint4* p, size_t n16, unsigned v) {
+  for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < n16; e += (size_t)gridDim.x * blockDim.x)
+    p[e] = make_uint4(v, v, v, v);
+}
+
 // phi(t) for n_t times: [sin(2 pi t / p_i) | cos(2 pi t / p_i)], p_i geometric 4e-3 .. 4 (fp64 math).
 __global__ void sinusoid_kernel(const float* t, int width, float* phi) {
   const int it = blockIdx.y;

@@ -15,6 +15,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <map>
+#include <mutex>
 #include <string>
 #include <tuple>
 #include <vector>
@@ -136,6 +137,8 @@ struct ae_handle {
   int f_nsplit = 0, f_natt = 0;
   int n_qt = 0, nbp = 0, nbs = 0;  // 16-row query tiles, 32-key prefix / suffix blocks
   int n_cu = 0;
+  void* static_scratch = nullptr;   // device address of this device's `scratch` array (ae_denoise_static)
+  std::string static_err;           // why it is null
   // in-kernel partial exchanges (read from AE_ATTN_CORESIDENT / AE_EXCH_POLL at creation, 0 = off):
   // attention key splits merged by co-resident workgroups, split-K partials polled by split S-1
   bool coresident_attn = true, poll_splitk = true;
@@ -1107,6 +1110,109 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out, int var
 }  // namespace
 
 // =====================================================================================
+// Scratch of the no-allocation entry point (ae_denoise_static): every activation, partial, counter
+// and time table of one pass, carved from this file-scope array. Each device holds its own copy
+// from the load of the code object to the end of the process. Host code never passes the array's
+// name to a kernel or a copy (on the host it is a stand-in, not a device address): it uses the
+// address hipGetSymbolAddress returns, looked up once per device with that device current.
+static __device__ __align__(256) unsigned char scratch[AE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_addr;  // per device ordinal: the address of `scratch` there
+
+// The device address of `scratch` on h's device (the current one, at ae_create).
+int scratch_address(ae_handle* h) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_addr.size() <= (size_t)h->dev) g_scratch_addr.resize((size_t)h->dev + 1, nullptr);
+  if (!g_scratch_addr[h->dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      h->static_err = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return AE_ERR_HIP;
+    }
+    g_scratch_addr[h->dev] = p;
+  }
+  h->static_scratch = g_scratch_addr[h->dev];
+  return AE_OK;
+}
+
+// Byte offsets in `scratch` of one ae_denoise_static pass over `batch` robots and `steps` steps:
+// the buffers a handle allocates for its passes, sized for this batch (the kernels index them by the
+// pass's own padded token count), plus the step-time table and its time-MLP staging.
+struct StaticLayout {
+  size_t x, h, hb, ssp_a, ssp_b, q, ks, vs, o, u, part, counters, opart, mlpart, qk_ssp, t, phi, hid, temb;
+  size_t total;
+};
+
+StaticLayout static_layout(const ae_handle* h, int batch, int steps) {
+  const ae_config& c = h->c;
+  const int w = c.width, A = c.action_dim, F = c.mlp_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
+  const size_t M = (size_t)batch * c.horizon, Mp = (M + TOKG - 1) / TOKG * TOKG, n_z = Mp / TOKG;
+  const size_t aes = h->at == AT_F32 ? 4 : 2;
+  StaticLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += (std::max<size_t>(bytes, 16) + 255) / 256 * 256;
+    return o;
+  };
+  L.x = take(Mp * A * 4);
+  L.h = take(Mp * w * 4);
+  L.hb = take(Mp * w * aes);
+  L.ssp_a = take((size_t)(w / 16) * Mp * 4);
+  L.ssp_b = take((size_t)(w / 16) * Mp * 4);
+  L.q = take((size_t)batch * nkv * h->n_qt * ATT_ROWS * dh * aes);
+  L.ks = take((size_t)batch * nkv * h->nbs * ATT_KB * dh * aes);
+  L.vs = take((size_t)batch * nkv * h->nbs * ATT_KB * dh * aes);
+  L.o = take(Mp * nq * dh * aes);
+  L.u = take(Mp * F * aes);
+  const size_t maxg = std::max({(size_t)h->qkv_tiles, (size_t)(w / 16), (size_t)h->gu_tiles, (size_t)h->out_tiles});
+  L.part = take(4 * maxg * 2 * TOKG * 16 * n_z * 4);
+  L.counters = take(maxg * n_z * 4);
+  const int nb = h->nbp + h->nbs;
+  const size_t n_split = std::max(attn_splits(nb, ATT_IT_SPLIT, ATT_WAVES_SPLIT), attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE));
+  const size_t zz = (size_t)batch * nkv;
+  L.opart = take(zz * h->n_qt * n_split * ATT_ROWS * dh * 4);
+  L.mlpart = take(zz * h->n_qt * n_split * ATT_ROWS * 2 * 4);
+  L.qk_ssp = c.qk_norm ? take((size_t)(nq + nkv) * dh / 16 * Mp * 4) : 0;
+  L.t = take((size_t)steps * 4);
+  L.phi = take((size_t)steps * w * 4);
+  L.hid = take((size_t)steps * w * 4);
+  L.temb = take((size_t)steps * w * 4);
+  L.total = off;
+  return L;
+}
+
+// The handle's per-pass buffers and capture variant, set aside while a pass runs in the static
+// scratch and put back when the call returns (on every path).
+class PassBuffers {
+ public:
+  explicit PassBuffers(ae_handle* h)
+      : h_(h), x_(h->x), h_buf_(h->h), ssp_a_(h->ssp_a), ssp_b_(h->ssp_b), part_(h->part), opart_(h->opart),
+        mlpart_(h->mlpart), qk_ssp_(h->qk_ssp), phi_(h->phi), hid_(h->hid), hb_(h->hb), o_(h->o), u_(h->u),
+        q_(h->q), ks_(h->ks), vs_(h->vs), counters_(h->counters), variant_(h->variant) {}
+  ~PassBuffers() {
+    h_->x = x_; h_->h = h_buf_; h_->ssp_a = ssp_a_; h_->ssp_b = ssp_b_; h_->part = part_; h_->opart = opart_;
+    h_->mlpart = mlpart_; h_->qk_ssp = qk_ssp_; h_->phi = phi_; h_->hid = hid_; h_->hb = hb_; h_->o = o_;
+    h_->u = u_; h_->q = q_; h_->ks = ks_; h_->vs = vs_; h_->counters = counters_; h_->variant = variant_;
+  }
+  PassBuffers(const PassBuffers&) = delete;
+  PassBuffers& operator=(const PassBuffers&) = delete;
+
+ private:
+  ae_handle* h_;
+  float *x_, *h_buf_, *ssp_a_, *ssp_b_, *part_, *opart_, *mlpart_, *qk_ssp_, *phi_, *hid_;
+  void *hb_, *o_, *u_, *q_, *ks_, *vs_;
+  unsigned* counters_;
+  int variant_;
+};
+
+}  // namespace
+
 extern "C" {
 
 int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
@@ -1362,6 +1468,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc(h, &h->pf_v, (size_t)L * h->pf_layer_elems * kes));
   }
   if (want_fused) TRY(setup_fused(h));
+  (void)scratch_address(h);  // a failure is reported by ae_denoise_static
   TRY(reset_exchange(h));
   if (hipDeviceSynchronize() != hipSuccess) { ae_destroy(h); return fail(nullptr, AE_ERR_HIP, "device sync after upload failed"); }
 #undef TRY
@@ -1482,6 +1589,48 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   }
   HIP_TRY(h, hipEventElapsedTime(&h->last_ms, h->ev0, h->ev1));
   memcpy(actions_out, tmp.data(), bytes);
+  return AE_OK;
+}
+
+int ae_denoise_static(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out, void* stream) {
+  int rc = check_denoise(h, batch, steps);
+  if (rc) return rc;
+  if (!d_noise || !d_actions_out) return fail(h, AE_ERR_INVALID_ARG, "null pointer");
+  if (h->c.time_mode)
+    return fail(h, AE_ERR_UNSUPPORTED, "a time-modulated expert builds its modulation tables per step count in "
+                                       "allocated memory: use ae_denoise_async");
+  if (!h->static_scratch) return fail(h, AE_ERR_HIP, h->static_err);
+  const StaticLayout L = static_layout(h, batch, steps);
+  if (L.total > (size_t)AE_STATIC_SCRATCH_BYTES)
+    return fail(h, AE_ERR_INVALID_ARG, "batch " + std::to_string(batch) + " x " + std::to_string(steps) +
+                                           " steps needs " + std::to_string(L.total) +
+                                           " bytes of scratch; the static scratch holds " +
+                                           std::to_string((size_t)AE_STATIC_SCRATCH_BYTES) + " (ae_denoise_async has no such limit)");
+  hipStream_t st = stream ? (hipStream_t)stream : h->stream;
+  Timer* tm = nullptr;
+  char* base = (char*)h->static_scratch;
+  PassBuffers keep(h);
+  h->x = (float*)(base + L.x); h->h = (float*)(base + L.h); h->hb = base + L.hb;
+  h->ssp_a = (float*)(base + L.ssp_a); h->ssp_b = (float*)(base + L.ssp_b);
+  h->q = base + L.q; h->ks = base + L.ks; h->vs = base + L.vs; h->o = base + L.o; h->u = base + L.u;
+  h->part = (float*)(base + L.part); h->counters = (unsigned*)(base + L.counters);
+  h->opart = (float*)(base + L.opart); h->mlpart = (float*)(base + L.mlpart);
+  h->qk_ssp = h->c.qk_norm ? (float*)(base + L.qk_ssp) : nullptr;
+  h->phi = (float*)(base + L.phi); h->hid = (float*)(base + L.hid);
+  // launches that wait for nothing inside a kernel: nothing can give up, so nothing is repeated
+  h->variant = 2;
+  // the previous call's contents (any handle, any size) go: padding rows and counters start at zero
+  LAUNCH_CHECK(h, "static_clear", AE_LAUNCH(fill16_kernel, dim3(1024), dim3(256), 0, st, (uint4*)base, L.total / 16, 0u));
+  float* t = (float*)(base + L.t);
+  float* temb = (float*)(base + L.temb);
+  LAUNCH_CHECK(h, "step_times", AE_LAUNCH(step_times_kernel, dim3(1), dim3(256), 0, st, t, steps));
+  rc = enqueue_temb(h, t, steps, temb, st, tm);
+  if (rc) return rc;
+  const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
+  HIP_TRY(h, hipMemcpyAsync(h->x, d_noise, bytes, hipMemcpyDeviceToDevice, st));
+  rc = enqueue_denoise(h, batch, steps, temb, st, tm);
+  if (rc) return rc;
+  HIP_TRY(h, hipMemcpyAsync(d_actions_out, h->x, bytes, hipMemcpyDeviceToDevice, st));
   return AE_OK;
 }
 

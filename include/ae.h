@@ -183,6 +183,32 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
 int ae_denoise_async(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out,
                      void* stream);
 
+/* Bytes of the static device scratch behind ae_denoise_static (64 MiB per device). */
+#define AE_STATIC_SCRATCH_BYTES (64u << 20)
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): ae_denoise_async with
+ * every activation, partial, counter and time table of the pass taken from one
+ * file-scope device array of AE_STATIC_SCRATCH_BYTES (each device holds its own
+ * copy until the process ends) instead of the handle's buffers. The call makes
+ * no hipMalloc / hipFree / allocating library call and no hipMemsetAsync: it
+ * enqueues on `stream` (NULL = the library's stream) a clear kernel over the
+ * bytes the pass uses, the step-time table, the time MLP, the copy of d_noise
+ * in, the denoise pass (one launch per phase, no waits inside a kernel, so no
+ * pass ever needs repeating) and the copy out to d_actions_out (device
+ * [batch][H][A] fp32); it returns after enqueueing. Every call on a device
+ * shares that device's array and it keeps the last call's contents: calls
+ * that overlap on one device (two streams, two handles) race and their outputs
+ * are undefined. AE_ERR_INVALID_ARG, before anything is enqueued, when the
+ * pass needs more than AE_STATIC_SCRATCH_BYTES (about 20 MB per Pi0-shaped
+ * robot at 10 steps: three fit, four do not); AE_ERR_UNSUPPORTED for a time-modulated
+ * expert (its modulation tables are built in allocated memory); otherwise the
+ * errors of ae_denoise_async. The result equals ae_denoise_async's within the
+ * bf16 tolerance of the path (its batch-1 passes run the persistent step
+ * kernel, whose sums are split differently). */
+int ae_denoise_static(ae_handle* h, int batch, const float* d_noise, int steps, float* d_actions_out,
+                      void* stream);
+
 /* Speculative verification of a draft chunk against the expert (Realtime-VLA
  * FLASH, sections 02-03). Host inputs: draft [H][A], noise [H][A] (one draw
  * shared by every tau), taus [n_tau] in [0, 1). The expert velocity v_j is
