@@ -21,6 +21,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
+RIDGE_BF16 = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # FLOP per HBM byte where the two roofs meet
 
 
 def kernel_bytes(cfg):
@@ -30,7 +31,7 @@ def kernel_bytes(cfg):
     mb = {"bf16": 2, "fp8": 1, "f32": 4}[cfg.mlp_dtype]
     sc = 4 if cfg.mlp_dtype == "fp8" else 0
     kvb = 2 if cfg.kv_dtype == "bf16" else 4
-    return {
+    kb = {
         "qkv_rope": (nq + 2 * nkv) * dh * w * wb,
         "attn": 2 * (cfg.prefix_len + cfg.horizon) * nkv * dh * kvb,
         "o_proj_resid": w * nq * dh * wb,
@@ -39,6 +40,52 @@ def kernel_bytes(cfg):
         "in_proj": w * A * wb,
         "out_proj_euler": A * w * wb,
     }
+    # the persistent step kernel: one launch is one whole Euler step of one robot (every layer's
+    # weights, the robot's prefix K/V, in/out projections)
+    prefix_kv = 2 * cfg.prefix_len * nkv * dh * kvb
+    kb["fused_step"] = (cfg.n_layers * (kb["qkv_rope"] + kb["o_proj_resid"] + kb["gate_up_geglu"] + kb["down_resid"]
+                                        + prefix_kv) + kb["in_proj"] + kb["out_proj_euler"])
+    return kb
+
+
+def kernel_flops(cfg, seqs):
+    """Algorithmic FLOPs per launch of each kernel over `seqs` suffix sequences of H rows."""
+    w, F, dh, nq, nkv, A, H = cfg.width, cfg.mlp_dim, cfg.head_dim, cfg.n_q_heads, cfg.n_kv_heads, cfg.action_dim, cfg.horizon
+    rows = seqs * H
+    return {
+        "qkv_rope": 2 * rows * (nq + 2 * nkv) * dh * w,
+        "attn": seqs * 4 * nq * H * (cfg.prefix_len + H) * dh,
+        "o_proj_resid": 2 * rows * w * nq * dh,
+        "gate_up_geglu": 2 * rows * 2 * F * w,
+        "down_resid": 2 * rows * w * F,
+        "in_proj": 2 * rows * w * A,
+        "out_proj_euler": 2 * rows * A * w,
+        "fused_step": step_flops(cfg, seqs),
+    }
+
+
+def annotate(entry, alg_bytes, alg_flops, avg_us):
+    """Both roofs of one kernel: HBM bytes and FLOPs per launch over its average duration; `bound` is the
+    roof its arithmetic intensity puts it under (MFMA above the bf16 ridge), `frac` the fraction of it."""
+    gbs = alg_bytes / (avg_us * 1e-6) / 1e9
+    tfl = alg_flops / (avg_us * 1e-6) / 1e12
+    entry.update({"alg_bytes": alg_bytes, "alg_flops": alg_flops, "GBs": round(gbs, 1), "TFLOPs": round(tfl, 2),
+                  "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "mfma_frac": round(tfl / PEAK_BF16_TFLOPS, 4)})
+    entry["bound"] = "mfma" if alg_flops > RIDGE_BF16 * alg_bytes else "hbm"
+    entry["frac"] = entry["mfma_frac"] if entry["bound"] == "mfma" else entry["hbm_frac"]
+    return entry
+
+
+def roofline_of(kernels, dom, traffic=None):
+    if not dom or "bound" not in kernels[dom]:
+        return {"kernel": dom, "bound": "hbm", "achieved": None, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": None,
+                "traffic": None}
+    e = kernels[dom]
+    mfma = e["bound"] == "mfma"
+    return {"kernel": dom, "bound": e["bound"], "achieved": e["TFLOPs"] if mfma else e["GBs"],
+            "peak": PEAK_BF16_TFLOPS if mfma else PEAK_HBM_GBS, "unit": "TFLOP/s" if mfma else "GB/s",
+            "frac": e["frac"], "hbm_frac": e["hbm_frac"], "mfma_frac": e["mfma_frac"],
+            "traffic": (traffic or {}).get(dom)}
 
 
 def measured_traffic():
@@ -49,7 +96,7 @@ def measured_traffic():
     if not os.path.exists(path):
         return {}
     sha = hashlib.sha256()
-    for f in ("ae_kernels.hpp", "ae_runtime.hip"):
+    for f in ("ae_kernels.hpp", "ae_fused.hpp", "ae_runtime.hip"):
         with open(os.path.join(ROOT, "flow_matching_action_euler_amd", "csrc", f), "rb") as fh:
             sha.update(fh.read())
     want, table = None, {}
@@ -90,14 +137,21 @@ def _cores():
 
 
 def _cpu_model():
+    """The host CPU as /proc/cpuinfo names it, with family / model / stepping and the logical CPU count
+    (some hosts give only a marketing name)."""
+    info = {}
     try:
         with open("/proc/cpuinfo") as fh:
             for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+                if ":" in line:
+                    k, v = line.split(":", 1)
+                    info.setdefault(k.strip(), v.strip())
     except OSError:
-        pass
-    return "unknown"
+        return "unknown"
+    name = info.get("model name", "unknown")
+    return (f"{name} (vendor {info.get('vendor_id', '?')}, family {info.get('cpu family', '?')}, model "
+            f"{info.get('model', '?')}, stepping {info.get('stepping', '?')}, {os.cpu_count()} logical CPUs visible, "
+            f"{info.get('cpu MHz', '?')} MHz)")
 
 
 def cpu_baseline(cfg, W, k, v, noise, budget_s=12.0, single_core_s=5.0):
@@ -176,11 +230,9 @@ def bench_verify(args, cfg, W, kvs, ex, stream):
                 kvb = 2 if cfg.kv_dtype == "bf16" else 4
                 suffix = 2 * cfg.horizon * cfg.n_kv_heads * cfg.head_dim * kvb  # every flow time shares the prefix
                 per_launch = kb[name] + (n_tau - 1) * suffix if name == "attn" else kb[name]
-                entry["alg_bytes"] = per_launch
-                entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+                annotate(entry, per_launch, kernel_flops(cfg, n_tau)[name], avg_us)
             kernels[name] = entry
     dom = max(kernels, key=lambda n: kernels[n]["ms_per_pass"]) if kernels else None
-    achieved = kernels[dom].get("GBs") if dom else None
     sb = step_bytes(cfg, 1)
     ms = elapsed * 1e3 / args.steps
     result = {
@@ -189,6 +241,7 @@ def bench_verify(args, cfg, W, kvs, ex, stream):
         "unit": "verify passes/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4),
+        "ms_per_step_is": "ms per bench step = one verify pass (every flow time of one draft)",
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weights, N(0,1) prefix KV, random-walk draft, N(0,1) noise)",
         "config": {"workload": cfg.name, "layers": cfg.n_layers, "width": cfg.width, "prefix_len": cfg.prefix_len,
@@ -199,8 +252,7 @@ def bench_verify(args, cfg, W, kvs, ex, stream):
         "pass_hbm_frac": round(sb / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "pass_flops": step_flops(cfg, n_tau),
         "pass_mfma_frac": round(step_flops(cfg, n_tau) / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None, "traffic": None},
+        "roofline": roofline_of(kernels, dom),
         "kernels": kernels,
     }
     result["rounds"] = bench_rounds(cfg, ex, args.steps)
@@ -478,8 +530,7 @@ def main():
                 entry["isolated_avg_us"] = round(iso[name][1] * 1e3 / iso[name][0], 3)
             if name in kb:
                 per_launch = kb[name] * (B if name == "attn" else 1)
-                entry["alg_bytes"] = per_launch
-                entry["GBs"] = round(per_launch / (avg_us * 1e-6) / 1e9, 1)
+                annotate(entry, per_launch, kernel_flops(cfg, 1 if name == "fused_step" else B)[name], avg_us)
             kernels[name] = entry
     traffic = measured_traffic() if cfg.name == "pi0_bf16" else {}
     for name, entry in kernels.items():
@@ -487,7 +538,6 @@ def main():
             entry["traffic_bytes"] = traffic[name]
     dom = max(kernels, key=lambda n: kernels[n]["ms_per_chunk"]) if kernels else None
     sb = step_bytes(cfg, B)
-    achieved = kernels[dom].get("GBs") if dom else None
     result = {
         "metric": "ms per 10-step action chunk & denoise steps/s (Pi0-scale expert, bs1)",
         "value": round(args.steps * cfg.steps / elapsed, 2),
@@ -496,6 +546,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_chunk, 4),
+        "ms_per_step_is": f"ms per bench step = one whole {cfg.steps}-Euler-step action chunk",
+        "ms_per_euler_step": round(ms_per_chunk / cfg.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -512,9 +564,7 @@ def main():
         "whole_chunk_hbm_frac": round(sb * cfg.steps / (ms_per_chunk * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "step_flops": step_flops(cfg, B),
         "whole_chunk_mfma_frac": round(step_flops(cfg, B) * cfg.steps / (ms_per_chunk * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4) if achieved else None,
-                     "traffic": traffic.get(dom) if dom else None},
+        "roofline": roofline_of(kernels, dom, traffic),
         "kernels": kernels,
     }
     if not args.no_cpu_baseline:

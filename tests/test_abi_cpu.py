@@ -136,6 +136,16 @@ def test_bench_work_figures_match_the_closed_forms():
     kv = 2 * 816 * 256 * 2
     assert bench.step_bytes(C.PI0, 1) == 18 * (2 * per_layer + kv) + 2 * 2 * 1024 * 32
     assert bench.step_bytes(C.PI0, 16) - bench.step_bytes(C.PI0, 1) == 15 * 18 * kv
+    # one persistent step-kernel launch is one whole Euler step of one robot
+    assert bench.kernel_bytes(C.PI0)["fused_step"] == bench.step_bytes(C.PI0, 1)
+    assert bench.kernel_flops(C.PI0, 1)["fused_step"] == bench.step_flops(C.PI0, 1)
+    # the attention of one robot: 354.7 MFLOP over 886,784 B of K/V = 400 FLOP/B, above the bf16
+    # ridge (2.5 PFLOP/s over 8 TB/s = 312.5 FLOP/B): its roof is the MFMA one; a GEMM's is HBM
+    e = bench.annotate({}, bench.kernel_bytes(C.PI0)["attn"], bench.kernel_flops(C.PI0, 1)["attn"], 10.0)
+    assert e["alg_bytes"] == 886_784 and e["alg_flops"] == attn and e["bound"] == "mfma"
+    assert e["frac"] == e["mfma_frac"] == round(attn / 10e-6 / 2.5e15, 4)
+    e = bench.annotate({}, bench.kernel_bytes(C.PI0)["down_resid"], bench.kernel_flops(C.PI0, 1)["down_resid"], 10.0)
+    assert e["bound"] == "hbm" and e["frac"] == e["hbm_frac"]
 
 
 def test_prefill_flops_match_the_closed_form():
