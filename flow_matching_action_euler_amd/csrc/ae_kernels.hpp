@@ -1775,40 +1775,66 @@ __global__ void interp_kernel(const float* draft, const float* noise, const floa
   }
 }
 
-// Endpoints, distances, prefix scan and gripper check (one workgroup).
-__global__ __launch_bounds__(256) void verify_kernel(const float* x, const float* v, const float* draft, const float* taus,
-                                                     int n_tau, int H, int A, const float* params, int gripper_dim,
-                                                     float* dist_out, int* accept_out, int* switch_out) {
+// The verification tail (FLASH article, section 03): endpoints a_j[i] = x_j[i] + (1 - tau_j) v_j[i] and
+// distances D[j][i] = ||a_j[i] - draft[i]||_2, one lane per action dim in a power-of-two lane group per
+// (j, i) and a shuffle reduction; then per row i "rejected" (D[j][i] >= delta or NaN at some tau) and
+// "gripper flips" (sign change from row i-1), each gathered with one ballot per wave: the accepted length
+// is the first rejected row (H when none), forced to 0 when any row flips. One workgroup of 1024 threads;
+// A <= 64, dynamic LDS n_tau * H floats.
+constexpr int VERIFY_THREADS = 1024;
+__global__ __launch_bounds__(VERIFY_THREADS) void verify_kernel(const float* x, const float* v, const float* draft,
+                                                                const float* taus, int n_tau, int H, int A,
+                                                                const float* params, int gripper_dim, float* dist_out,
+                                                                int* accept_out, int* switch_out) {
   extern __shared__ float dsh[];  // [n_tau][H]
+  __shared__ int w_first[VERIFY_THREADS / 64], w_flip[VERIFY_THREADS / 64];
   const float delta = params[0];
-  for (int e = threadIdx.x; e < n_tau * H; e += blockDim.x) {
-    int j = e / H, i = e % H;
-    float om = 1.f - taus[j];
-    float acc = 0.f;
-    for (int k = 0; k < A; ++k) {
-      size_t idx = ((size_t)j * H + i) * A + k;
-      float diff = x[idx] + om * v[idx] - draft[(size_t)i * A + k];
-      acc += diff * diff;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int S = 1;
+  while (S < A) S <<= 1;
+  const int sub = lane & (S - 1), rows = n_tau * H, per_pass = VERIFY_THREADS / S;
+  for (int r0 = 0; r0 < rows; r0 += per_pass) {
+    const int r = r0 + (int)threadIdx.x / S;
+    float d2 = 0.f;
+    if (r < rows && sub < A) {
+      const int j = r / H, i = r % H;
+      const size_t idx = (size_t)r * A + sub;
+      const float diff = x[idx] + (1.f - taus[j]) * v[idx] - draft[(size_t)i * A + sub];
+      d2 = diff * diff;
     }
-    float dd = sqrtf(acc);
-    dsh[e] = dd;
-    if (dist_out) dist_out[e] = dd;
+    for (int o = S >> 1; o > 0; o >>= 1) d2 += __shfl_xor(d2, o, 64);
+    if (r < rows && sub == 0) {
+      const float dd = sqrtf(d2);
+      dsh[r] = dd;
+      if (dist_out) dist_out[r] = dd;
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int sw = 0;
-    if (gripper_dim >= 0)
-      for (int i = 1; i < H; ++i)
-        if (draft[(size_t)i * A + gripper_dim] * draft[(size_t)(i - 1) * A + gripper_dim] < 0.f) sw = 1;
-    int acc = 0;
-    while (acc < H) {
-      bool ok = true;
-      for (int j = 0; j < n_tau; ++j) ok = ok && (dsh[j * H + acc] < delta);
-      if (!ok) break;
-      ++acc;
+  int first = H, flip = 0;
+  for (int i0 = 0; i0 < H; i0 += VERIFY_THREADS) {
+    const int i = i0 + (int)threadIdx.x;
+    bool bad = false, fl = false;
+    if (i < H) {
+      for (int j = 0; j < n_tau; ++j) bad = bad || !(dsh[j * H + i] < delta);
+      if (gripper_dim >= 0 && i > 0) fl = draft[(size_t)i * A + gripper_dim] * draft[(size_t)(i - 1) * A + gripper_dim] < 0.f;
     }
-    *accept_out = sw ? 0 : acc;
-    *switch_out = sw;
+    const unsigned long long mb = __ballot(bad), mf = __ballot(fl);
+    if (lane == 0) {
+      w_first[wave] = mb ? i0 + wave * 64 + (__ffsll((long long)mb) - 1) : H;
+      w_flip[wave] = mf != 0ull;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      for (int w = 0; w < VERIFY_THREADS / 64; ++w) {
+        first = min(first, w_first[w]);
+        flip |= w_flip[w];
+      }
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    *accept_out = flip ? 0 : first;
+    *switch_out = flip;
   }
 }
 

@@ -85,6 +85,12 @@ struct PhaseCfg {
 
 }  // namespace
 
+// Split-K factor of each GEMM role when a pass has one token group (at most 4; pick() lowers it to what
+// divides the role's k-blocks). AE_SPLITK=<o>,<down> sets the o_proj and down factors at ae_create.
+struct Splits {
+  int qkv = 1, o = 4, gu = 1, down = 4, out = 1;
+};
+
 struct ae_handle {
   ae_config c{};
   int dev = 0;
@@ -122,6 +128,8 @@ struct ae_handle {
   // 1 = one launch per phase, 2 = one launch per phase with no in-kernel waits (no co-resident
   // exchanges: the pass a failed one is repeated with)
   int variant = 0;
+  bool eager = false;               // AE_GRAPH=0: passes enqueue their launches instead of replaying a graph
+  Splits sk;                        // split-K factors of the launch-per-phase GEMMs
   // persistent step kernel (batch-1 denoise)
   bool fused_ok = false;            // shape, dtypes, occupancy and AE_FUSED allow it
   std::string fused_why;            // why not, when fused_ok is false
@@ -422,10 +430,6 @@ hipError_t set_all_gemm_attrs() {
 
 // k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group (measured for Pi0:
 // o_proj and down gain from 4 splits, the others from none)
-struct Splits {
-  int qkv = 1, o = 4, gu = 1, down = 4, out = 1;
-};
-const Splits& splits() { static const Splits s; return s; }
 
 // Key splits when each of nw waves walks `it` blocks of ATT_KB keys.
 int attn_splits(int n_blocks, int it, int nw) { return std::max(1, (n_blocks + it * nw - 1) / (it * nw)); }
@@ -684,7 +688,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       GemmArgs a = g;
       a.w = h->qkv_p[l]; a.x = h->hb;
       a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
-      a.S = pick(w / 32, splits().qkv, n_z).S;
+      a.S = pick(w / 32, h->sk.qkv, n_z).S;
       if ((PREFETCH_MASK & 1) && n_seq == 1 && !seq_slot && h->slot_elems) {  // this layer's prefix K/V (one robot)
         const size_t kes = dtype_size(c.kv_dtype), lay = (size_t)nkv * h->nbp * ATT_KB * dh;
         const size_t off = ((size_t)slot0 * h->slot_elems + (size_t)l * lay) * kes;
@@ -719,12 +723,12 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     {
       GemmArgs a = g;
       a.w = h->o_p[l]; a.x = h->o; a.ssp_in = nullptr; a.K = nq * dh;
-      a.S = pick(nq * dh / 32, splits().o, n_z).S;
+      a.S = pick(nq * dh / 32, h->sk.o, n_z).S;
       a.h = h->h; a.hb = h->hb; a.gain_next = sm ? modp(sm->t->g2, w, l) : h->ln2[l]; a.ssp_out = h->ssp_b; a.N = w;
       if (sm) a.res_gate = modp(sm->t->mod, 6 * (size_t)w, l) + 2 * w;
       if ((PREFETCH_MASK & 8) && !uses_tiled(h, R_GATE_UP, h->gu_tiles, w, M, Mp)) {  // gate/up's weights, tiled as gate/up is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->gu_p[l];
-        a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, splits().gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
+        a.pf.next_groups = h->gu_tiles / 2; a.pf.next_S = pick(w / 32, h->sk.gu, n_z).S; a.pf.NT = 2; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
         a.pf.kb_lead = prefetch_gu_lead(w / KBLK / a.pf.next_S);
       }
@@ -735,11 +739,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       GemmArgs a = g;
       a.w = h->gu_p[l]; a.wscale = h->gu_s[l]; a.x = h->hb;
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
-      a.S = pick(w / 32, splits().gu, n_z).S; a.u_out = h->u; a.N = F;
+      a.S = pick(w / 32, h->sk.gu, n_z).S; a.u_out = h->u; a.N = F;
       if (sm) a.shift_bias = modp(sm->t->bgu, ngu, l);
       if ((PREFETCH_MASK & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
-        a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, splits().down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
+        a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, h->sk.down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
         a.pf.frag_bytes = h->mt == WT_F32 ? 2048 : h->mt == WT_BF16 ? 1024 : 512;
         a.pf.kb_lead = PREFETCH_DOWN_LEAD;
       }
@@ -749,7 +753,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     {
       GemmArgs a = g;
       a.w = h->d_p[l]; a.wscale = h->d_s[l]; a.x = h->u; a.ssp_in = nullptr; a.K = F;
-      a.S = pick(F / 32, splits().down, n_z).S;
+      a.S = pick(F / 32, h->sk.down, n_z).S;
       a.h = h->h; a.hb = h->hb;
       a.gain_next = (l + 1 < c.n_layers) ? (sm ? modp(sm->t->g1, w, l + 1) : h->ln1[l + 1])
                                          : (sm ? sm->t->gf + (size_t)sm->k * w : h->final_ln ? h->final_ln : h->ln1[0]);
@@ -757,7 +761,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.ssp_out = h->ssp_a; a.N = w;
       if ((PREFETCH_MASK & 16) && l + 1 < c.n_layers && !uses_tiled(h, R_QKV_ROPE, h->qkv_tiles, w, M, Mp)) {  // the next layer's QKV weights
         a.pf.kind = 2; a.pf.base = (const char*)h->qkv_p[l + 1];
-        a.pf.next_groups = h->qkv_tiles; a.pf.next_S = pick(w / 32, splits().qkv, n_z).S; a.pf.NT = 1; a.pf.KB = w / KBLK;
+        a.pf.next_groups = h->qkv_tiles; a.pf.next_S = pick(w / 32, h->sk.qkv, n_z).S; a.pf.NT = 1; a.pf.KB = w / KBLK;
         a.pf.frag_bytes = h->wt == WT_F32 ? 2048 : 1024;
       }
       LAUNCH_CHECK(h, "down_resid", (void)Dispatch::gemm(h, R_DOWN, a, w / 16, n_z, st));
@@ -769,7 +773,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.inv_width = 1.f / (float)w; a.eps = c.rms_eps; a.M = M; a.M_pad = Mp;
     a.part = h->part; a.counters = h->counters;
     a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
-    a.S = pick(w / 32, splits().out, n_z).S;
+    a.S = pick(w / 32, h->sk.out, n_z).S;
     a.bias = sm ? sm->t->bout + (size_t)sm->k * nout : h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
     LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, R_OUT_PROJ, a, h->out_tiles, n_z, st));
   }
@@ -887,8 +891,12 @@ int setup_fused(ae_handle* h) {
   }
   const int ntt = (H + 15) / 16, ntp = ntt <= 1 ? 1 : ntt <= 2 ? 2 : 4, G = h->n_cu;
   const int nb = h->nbp + h->nbs;
+  // key splits of 4 blocks (half the waves of a unit busy, half the K/V bytes per workgroup of 8-block
+  // splits: measured for Pi0, 7 splits of 4 blocks take 0.685 ms per step, 4 splits of 7 blocks 0.694 ms),
+  // as long as every unit still has a workgroup of its own
   h->f_nsplit = (nb + FW - 1) / FW;
-  if (const char* e = getenv("AE_FUSED_SPLITS")) h->f_nsplit = std::max(h->f_nsplit, std::min(nb, atoi(e)));
+  const int ns4 = (nb + 3) / 4;
+  if (ns4 <= FW && ns4 * h->n_qt * nkv <= G) h->f_nsplit = std::max(h->f_nsplit, ns4);
   h->f_natt = h->f_nsplit * h->n_qt * nkv;
   if (w / 16 > F_SLOTS * (G / ntp) || h->f_natt > 4 * G || h->out_tiles > G / ntp || h->nbp < 1)
     return no("work split does not fit the grid");
@@ -1023,7 +1031,7 @@ int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
   if (rc) return rc;
   rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm);
   if (rc) return rc;
-  LAUNCH_CHECK(h, "verify_accept", AE_LAUNCH(verify_kernel, dim3(1), dim3(256), (size_t)n_tau * H * sizeof(float), st,
+  LAUNCH_CHECK(h, "verify_accept", AE_LAUNCH(verify_kernel, dim3(1), dim3(VERIFY_THREADS), (size_t)n_tau * H * sizeof(float), st,
                                                       h->x, h->vout, h->draft, h->taus, n_tau, H, A, h->params,
                                                       c.gripper_dim, h->dist, h->accept, h->gswitch));
   return AE_OK;
@@ -1105,6 +1113,40 @@ int get_graph(ae_handle* h, int mode, int a, int b, hipGraphExec_t* out, int var
   h->graphs[key] = exec;
   *out = exec;
   return AE_OK;
+}
+
+// A pass of `mode` (as in get_graph): its captured graph, replayed by launch_pass, or on an eager
+// handle (AE_GRAPH=0) the same launches enqueued by launch_pass directly on its stream.
+struct Pass {
+  hipGraphExec_t g = nullptr;
+  int mode = 0, a = 0, b = 0, variant = 0;
+};
+
+int get_pass(ae_handle* h, int mode, int a, int b, Pass* p, int variant) {
+  *p = Pass{nullptr, mode, a, b, variant};
+  if (!h->eager) return get_graph(h, mode, a, b, &p->g, variant);
+  float* temb = nullptr;
+  return mode == 0 || mode == 2 ? get_temb_steps(h, a, &temb) : AE_OK;  // built before the pass, as for a graph
+}
+
+int launch_pass(ae_handle* h, const Pass& p, hipStream_t st) {
+  if (p.g) {
+    HIP_TRY(h, hipGraphLaunch(p.g, st));
+    return AE_OK;
+  }
+  float* temb = nullptr;
+  if (p.mode == 0 || p.mode == 2) {
+    const int rc = get_temb_steps(h, p.a, &temb);
+    if (rc) return rc;
+  }
+  h->variant = p.variant;
+  const int rc = p.mode == 0   ? enqueue_denoise(h, p.b, p.a, temb, st, nullptr)
+                 : p.mode == 2 ? enqueue_denoise(h, 1, p.a, temb, st, nullptr, p.b)
+                 : p.mode == 3 ? enqueue_draft(h, st, nullptr)
+                 : p.mode == 4 ? enqueue_prefill(h, st, nullptr)
+                               : enqueue_verify(h, p.a, st, nullptr);
+  h->variant = 0;
+  return rc;
 }
 
 }  // namespace
@@ -1236,6 +1278,14 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   if (const char* e = getenv("AE_TILED_SHAPE")) h->tiled_force = atoi(e);
   if (const char* e = getenv("AE_ATTN_XCD")) h->attn_xcd = atoi(e) != 0;
   if (const char* e = getenv("AE_WAIT_TICKS")) h->wait_ticks = strtoull(e, nullptr, 0);
+  if (const char* e = getenv("AE_GRAPH")) h->eager = atoi(e) == 0;
+  if (const char* e = getenv("AE_SPLITK")) {
+    int so = 0, sd = 0;
+    if (sscanf(e, "%d,%d", &so, &sd) == 2 && so >= 1 && so <= 4 && sd >= 1 && sd <= 4) {
+      h->sk.o = so;
+      h->sk.down = sd;
+    }
+  }
   bool want_fused = true;
   if (const char* e = getenv("AE_FUSED")) want_fused = atoi(e) != 0;
   if (hipStreamCreateWithFlags(&h->stream, hipStreamNonBlocking) != hipSuccess) { delete h; return fail(nullptr, AE_ERR_HIP, "hipStreamCreate failed"); }
@@ -1247,7 +1297,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
   if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})
                         : attn_dispatch<AT_F32>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
-      set_all_gemm_attrs() != hipSuccess) {
+      set_all_gemm_attrs() != hipSuccess ||
+      hipFuncSetAttribute((const void*)verify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 256 * 4) != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
     return fail(nullptr, AE_ERR_HIP, m);
@@ -1555,12 +1606,13 @@ int ae_denoise_async(ae_handle* h, int batch, const float* d_noise, int steps, f
   rc = failed_async(h);
   if (rc) return rc;
   hipStream_t st = stream ? (hipStream_t)stream : h->stream;
-  hipGraphExec_t g;
-  rc = get_graph(h, 0, steps, batch, &g, pref_variant(h));
+  Pass g;
+  rc = get_pass(h, 0, steps, batch, &g, pref_variant(h));
   if (rc) return rc;
   const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
   HIP_TRY(h, hipMemcpyAsync(h->x, d_noise, bytes, hipMemcpyDeviceToDevice, st));
-  HIP_TRY(h, hipGraphLaunch(g, st));
+  rc = launch_pass(h, g, st);
+  if (rc) return rc;
   HIP_TRY(h, hipMemcpyAsync(d_actions_out, h->x, bytes, hipMemcpyDeviceToDevice, st));
   return AE_OK;
 }
@@ -1574,12 +1626,13 @@ int ae_denoise(ae_handle* h, int batch, const float* noise, int steps, float* ac
   const size_t bytes = (size_t)batch * h->c.horizon * h->c.action_dim * sizeof(float);
   std::vector<float> tmp(bytes / sizeof(float));
   for (int variant = pref_variant(h);; variant = 2) {
-    hipGraphExec_t g;
-    rc = get_graph(h, 0, steps, batch, &g, variant);
+    Pass g;
+    rc = get_pass(h, 0, steps, batch, &g, variant);
     if (rc) return rc;
     HIP_TRY(h, hipMemcpyAsync(h->x, noise, bytes, hipMemcpyHostToDevice, h->stream));
     HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    rc = launch_pass(h, g, h->stream);
+    if (rc) return rc;
     HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
     HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->x, bytes, hipMemcpyDeviceToHost, h->stream));
     HIP_TRY(h, hipStreamSynchronize(h->stream));
@@ -1667,12 +1720,13 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
   rc = failed_async(h);
   if (rc) return rc;
   hipStream_t st = stream ? (hipStream_t)stream : h->stream;
-  hipGraphExec_t g;
-  rc = get_graph(h, 1, n_tau, 1, &g, pref_variant(h));
+  Pass g;
+  rc = get_pass(h, 1, n_tau, 1, &g, pref_variant(h));
   if (rc) return rc;
   rc = verify_common(h, slot, n_tau, delta, st, hipMemcpyDeviceToDevice, d_draft, d_noise, d_taus);
   if (rc) return rc;
-  HIP_TRY(h, hipGraphLaunch(g, st));
+  rc = launch_pass(h, g, st);
+  if (rc) return rc;
   HIP_TRY(h, hipMemcpyAsync(d_accept_len, h->accept, sizeof(int), hipMemcpyDeviceToDevice, st));
   HIP_TRY(h, hipMemcpyAsync(d_gripper_switch, h->gswitch, sizeof(int), hipMemcpyDeviceToDevice, st));
   if (d_dist_out)
@@ -1684,11 +1738,12 @@ int ae_verify_async(ae_handle* h, int slot, const float* d_draft, const float* d
 // the inputs are on the device already (verify_common). Reads back the decision (and D).
 static int run_verify(ae_handle* h, int n_tau, int* acc, int* sw, float* dist) {
   for (int variant = pref_variant(h);; variant = 2) {
-    hipGraphExec_t g;
-    int rc = get_graph(h, 1, n_tau, 1, &g, variant);
+    Pass g;
+    int rc = get_pass(h, 1, n_tau, 1, &g, variant);
     if (rc) return rc;
     HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    rc = launch_pass(h, g, h->stream);
+    if (rc) return rc;
     HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
     HIP_TRY(h, hipMemcpyAsync(acc, h->accept, sizeof(int), hipMemcpyDeviceToHost, h->stream));
     HIP_TRY(h, hipMemcpyAsync(sw, h->gswitch, sizeof(int), hipMemcpyDeviceToHost, h->stream));
@@ -1733,11 +1788,11 @@ int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_veri
   rc = failed_async(h);
   if (rc) return rc;
   // both graphs exist before the round starts (the first round of a shape captures them)
-  hipGraphExec_t gv, gd;
+  Pass gv, gd;
   const int var = pref_variant(h);
-  rc = get_graph(h, 1, n_tau, 1, &gv, var);
+  rc = get_pass(h, 1, n_tau, 1, &gv, var);
   if (rc) return rc;
-  rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd, var) : get_graph(h, 2, steps, slot, &gd, var);
+  rc = slot == 0 ? get_pass(h, 0, steps, 1, &gd, var) : get_pass(h, 2, steps, slot, &gd, var);
   if (rc) return rc;
   rc = verify_common(h, slot, n_tau, delta, h->stream, hipMemcpyHostToDevice, draft, noise_verify, taus);
   if (rc) return rc;
@@ -1753,12 +1808,13 @@ int ae_round(ae_handle* h, int slot, const float* draft, const float* noise_veri
   if (full) {
     for (int variant = var;; variant = 2) {
       if (variant != var) {
-        rc = slot == 0 ? get_graph(h, 0, steps, 1, &gd, variant) : get_graph(h, 2, steps, slot, &gd, variant);
+        rc = slot == 0 ? get_pass(h, 0, steps, 1, &gd, variant) : get_pass(h, 2, steps, slot, &gd, variant);
         if (rc) return rc;
       }
       HIP_TRY(h, hipMemcpyAsync(h->x, noise_full, ha, hipMemcpyHostToDevice, h->stream));
       HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-      HIP_TRY(h, hipGraphLaunch(gd, h->stream));
+      rc = launch_pass(h, gd, h->stream);
+      if (rc) return rc;
       HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
       HIP_TRY(h, hipMemcpyAsync(out.data(), h->x, ha, hipMemcpyDeviceToHost, h->stream));
       HIP_TRY(h, hipStreamSynchronize(h->stream));
@@ -1788,12 +1844,13 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
   const size_t bytes = (size_t)c.horizon * c.action_dim * sizeof(float);
   std::vector<float> tmp(bytes / sizeof(float));
   for (int variant = 0;; variant = 2) {
-    hipGraphExec_t g;
-    rc = get_graph(h, 3, 0, 0, &g, variant);
+    Pass g;
+    rc = get_pass(h, 3, 0, 0, &g, variant);
     if (rc) return rc;
     HIP_TRY(h, hipMemcpyAsync(h->feat, features, (size_t)c.prefix_len * c.width * 4, hipMemcpyHostToDevice, h->stream));
     HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    rc = launch_pass(h, g, h->stream);
+    if (rc) return rc;
     HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
     HIP_TRY(h, hipMemcpyAsync(tmp.data(), h->vout, bytes, hipMemcpyDeviceToHost, h->stream));
     HIP_TRY(h, hipStreamSynchronize(h->stream));
@@ -1810,12 +1867,13 @@ int ae_draft(ae_handle* h, const float* features, float* chunk_out) {
 static int run_prefill(ae_handle* h, const float* emb) {
   const ae_config& c = h->c;
   for (int variant = 0;; variant = 2) {
-    hipGraphExec_t g;
-    int rc = get_graph(h, 4, 0, 0, &g, variant);
+    Pass g;
+    int rc = get_pass(h, 4, 0, 0, &g, variant);
     if (rc) return rc;
     HIP_TRY(h, hipMemcpyAsync(h->feat, emb, (size_t)c.horizon * c.width * 4, hipMemcpyHostToDevice, h->stream));
     HIP_TRY(h, hipEventRecord(h->ev0, h->stream));
-    HIP_TRY(h, hipGraphLaunch(g, h->stream));
+    rc = launch_pass(h, g, h->stream);
+    if (rc) return rc;
     HIP_TRY(h, hipEventRecord(h->ev1, h->stream));
     HIP_TRY(h, hipStreamSynchronize(h->stream));
     if (!take_failure(h) || variant == 2) break;

@@ -44,9 +44,12 @@
  * Errors. Every int-returning call returns AE_OK (0) or a negative AE_ERR_*
  * code and never throws; ae_last_error() describes the last failure. On error
  * the outputs are not written. A bounded wait inside a kernel that gave up
- * (partials of other workgroups never arrived) is reported as AE_ERR_HIP by the
- * synchronous ae_denoise / ae_verify of that pass, or by the next one after an
- * asynchronous call. A handle is not re-entrant: calls on one
+ * (data of another workgroup never arrived: not all of the launch was resident)
+ * does not fail a synchronous call: it restores the exchange buffers and repeats
+ * its pass with launches that have no in-kernel waits, and returns that pass's
+ * outputs. An asynchronous call cannot repeat its pass: the next call on the
+ * handle reports AE_ERR_HIP (the outputs of the asynchronous passes since the last
+ * successful call are invalid) and restores the buffers. A handle is not re-entrant: calls on one
  * handle must not overlap. Separate handles are independent.
  */
 #ifndef AE_H_
@@ -153,17 +156,31 @@ typedef struct ae_handle ae_handle;
  * 6.5: fixed image count, token length and chunk shape). Returns
  * AE_ERR_INVALID_ARG / AE_ERR_UNSUPPORTED before touching the GPU when cfg is
  * not covered, AE_ERR_HIP if no device is usable, AE_ERR_OOM on allocation failure.
- * Read here from the environment: AE_ATTN_CORESIDENT=0 (attention key splits
- * merge in a separate launch instead of inside the attention launch) and
- * AE_EXCH_POLL=0 (split-K partials meet through arrival tickets instead of being
- * polled); AE_TOKEN_LOOP=0 (one GEMM workgroup per 64-token group instead of
- * workgroups that loop over several groups with their weights held); AE_TILED=<mask>
- * (GEMM roles, bit 0 qkv, 1 o_proj, 2 gate/up, 3 down, that may take the token-tiled
- * kernel when a pass has 128 or more tokens; default 0xf), AE_TILED_SHAPE=0..3 (force
- * one tiled shape wherever it fits) and AE_ATTN_XCD=0 (attention workgroups of one
- * sequence not grouped on one XCD when a pass has 8 or more sequences) and AE_ATTN_MID=0
- * (no co-resident 2-block attention splits for several-sequence passes); both in-kernel exchanges assume every workgroup of the launch is
- * resident at once, which holds on an otherwise idle device. */
+ * Read here from the environment, once, for the handle's lifetime (all optional):
+ *   AE_FUSED=0         batch-1 denoise passes use one launch per phase instead of the
+ *                      persistent step kernel (one launch per Euler step);
+ *   AE_ATTN_CORESIDENT=0  attention key splits merge in a separate launch instead of
+ *                      inside the attention launch;
+ *   AE_EXCH_POLL=0     split-K partials meet through arrival tickets instead of being
+ *                      polled;
+ *   AE_SPLITK=<o>,<d>  split-K factors (1..4) of o_proj and down in passes of one
+ *                      64-token group (default 4,4; lowered to what divides K);
+ *   AE_TILED=<mask>    GEMM roles (bit 0 qkv, 1 o_proj, 2 gate/up, 3 down) that may take
+ *                      the token-tiled kernel when a pass has 128 or more tokens (0xf);
+ *   AE_TILED_SHAPE=0..3  force one tiled shape wherever it fits;
+ *   AE_ATTN_XCD=0      attention workgroups of one sequence not grouped on one XCD when
+ *                      a pass has 8 or more sequences;
+ *   AE_WAIT_TICKS=<n>  bound of every in-kernel wait in ticks of the 100 MHz clock
+ *                      (default 2e6 = 20 ms; 0 makes every wait give up at once);
+ *   AE_GRAPH=0         passes enqueue their launches directly instead of replaying a
+ *                      captured graph (same kernels, same arguments, same results).
+ * The persistent step kernel and the in-kernel exchanges assume every workgroup of
+ * their launch is resident at once (one workgroup per compute unit for the step
+ * kernel, checked against the kernel's registers and LDS at ae_create). When another
+ * process or stream holds compute units, a bounded wait gives up, sets a host-visible
+ * flag, and the call repeats its pass with launches that wait for nothing inside a
+ * kernel (see Errors); after three such passes in a row a handle stops trying the
+ * step kernel. */
 int ae_create(const ae_config* cfg, const ae_weights* w, ae_handle** out);
 
 /* Copy one robot's prefix cache into slot (0 <= slot < max_batch). k and v are
