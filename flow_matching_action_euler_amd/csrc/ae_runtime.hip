@@ -21,6 +21,7 @@
 #include <vector>
 
 #include "../../include/ae.h"
+#include "ae_host.hpp"
 #include "ae_kernels.hpp"
 #include "ae_fused.hpp"
 
@@ -77,7 +78,7 @@ struct Timer {
   }
 };
 
-size_t dtype_size(int dt) { return dt == AE_F32 ? 4 : dt == AE_BF16 ? 2 : 1; }
+using ae_host::dtype_size;
 
 struct PhaseCfg {
   int S;  // k-splits
@@ -251,75 +252,14 @@ int upload(ae_handle* h, void** dst, const void* src, size_t bytes) {
 
 // Pack rows (row_ptr[p] = source row of packed channel p, or null for a zero row)
 // of K elements of size es into [tiles][K/32][64 lanes][8].
-void pack_rows(const std::vector<const unsigned char*>& row_ptr, int K, size_t es, std::vector<unsigned char>& out) {
-  const int tiles = (int)row_ptr.size() / 16, KB = K / 32;
-  out.assign((size_t)tiles * KB * 64 * 8 * es, 0);
-  for (int t = 0; t < tiles; ++t)
-    for (int kb = 0; kb < KB; ++kb)
-      for (int lane = 0; lane < 64; ++lane) {
-        const unsigned char* src = row_ptr[t * 16 + (lane & 15)];
-        unsigned char* dst = out.data() + (((size_t)t * KB + kb) * 64 + lane) * 8 * es;
-        if (src) memcpy(dst, src + ((size_t)kb * 32 + (lane >> 4) * 8) * es, 8 * es);
-      }
-}
+using ae_host::pack_rows;
 
+// ae_create's checks of the config and the weight pointers (ae_host::validate_config), as an AE_* code
+// with the reason for ae_last_error.
 int validate(const ae_config* c, const ae_weights* w) {
-  if (!c || !w) return fail(nullptr, AE_ERR_INVALID_ARG, "null config or weights");
-  if (c->n_layers < 1 || c->width <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 ||
-      c->mlp_dim <= 0 || c->action_dim <= 0 || c->horizon <= 0 || c->prefix_len < 0 || c->max_batch < 1 ||
-      c->max_taus < 0 || c->max_taus > 64 || !(c->rms_eps >= 0.f) || !(c->rope_base > 0.f))
-    return fail(nullptr, AE_ERR_INVALID_ARG, "non-positive size in ae_config");
-  if (c->n_q_heads % c->n_kv_heads) return fail(nullptr, AE_ERR_INVALID_ARG, "n_kv_heads must divide n_q_heads");
-  if (c->gripper_dim >= c->action_dim || c->gripper_dim < -1) return fail(nullptr, AE_ERR_INVALID_ARG, "gripper_dim out of range");
-  for (int d : {c->weight_dtype, c->mlp_dtype, c->kv_dtype})
-    if (d != AE_F32 && d != AE_BF16 && d != AE_FP8_E4M3) return fail(nullptr, AE_ERR_INVALID_ARG, "unknown dtype");
-  if (c->width % 256 || (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128 && c->head_dim != 256) ||
-      c->mlp_dim % 256 || (c->n_q_heads * c->head_dim) % 256)
-    return fail(nullptr, AE_ERR_UNSUPPORTED,
-                "width, mlp_dim and n_q_heads*head_dim must be multiples of 256; head_dim one of 32, 64, 128, 256");
-  if (c->action_dim > 64 || c->horizon > (c->prefill == 1 ? 1024 : 256))
-    return fail(nullptr, AE_ERR_UNSUPPORTED, "action_dim <= 64 and horizon <= 256 (prefill: <= 1024 tokens)");
-  if (c->weight_dtype == AE_FP8_E4M3) return fail(nullptr, AE_ERR_UNSUPPORTED, "fp8 is supported for the MLP only");
-  if (c->kv_dtype != c->weight_dtype) return fail(nullptr, AE_ERR_UNSUPPORTED, "kv_dtype must equal weight_dtype");
-  if (c->weight_dtype == AE_F32 && c->mlp_dtype != AE_F32)
-    return fail(nullptr, AE_ERR_UNSUPPORTED, "fp32 attention weights need fp32 MLP weights");
-  if (c->weight_dtype == AE_BF16 && c->mlp_dtype == AE_F32)
-    return fail(nullptr, AE_ERR_UNSUPPORTED, "bf16 attention weights need bf16 or fp8 MLP weights");
-  if (c->draft != 0 && c->draft != 1) return fail(nullptr, AE_ERR_INVALID_ARG, "draft is 0 or 1");
-  if (c->prefill != 0 && c->prefill != 1) return fail(nullptr, AE_ERR_INVALID_ARG, "prefill is 0 or 1");
-  if (c->prefill) {
-    if (c->draft || c->prefix_len != 0 || c->max_batch != 1 || c->max_taus != 0 || c->time_mode || c->qk_norm ||
-        c->weight_dtype != AE_BF16 || c->mlp_dtype == AE_F32)
-      return fail(nullptr, AE_ERR_UNSUPPORTED,
-                  "a prefill stack has prefix_len 0, max_batch 1, max_taus 0, bf16 attention weights, no modulation or QK-norm");
-    if (!w->layers) return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
-  } else if (c->draft) {
-    if (c->n_layers != 1 || c->max_batch != 1 || c->max_taus != 0 || c->time_mode || c->qk_norm ||
-        c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16 || c->prefix_len < 1)
-      return fail(nullptr, AE_ERR_UNSUPPORTED,
-                  "a draft model has 1 layer, max_batch 1, max_taus 0, bf16 weights, no modulation or QK-norm, prefix_len >= 1");
-    if (!w->queries || !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b)
-      return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
-  } else if (!w->time_in_w || !w->time_in_b || !w->time_out_w || !w->time_out_b || !w->action_in_w || !w->action_in_b ||
-             !w->layers || !w->final_ln || !w->action_out_w || !w->action_out_b) {
-    return fail(nullptr, AE_ERR_INVALID_ARG, "null weight pointer");
-  }
-  if ((c->time_mode != 0 && c->time_mode != 1) || (c->qk_norm != 0 && c->qk_norm != 1))
-    return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode and qk_norm are 0 or 1");
-  if ((c->time_mode || c->qk_norm) && (c->weight_dtype != AE_BF16 || c->mlp_dtype != AE_BF16))
-    return fail(nullptr, AE_ERR_UNSUPPORTED, "time modulation and QK-norm are built for bf16 weights and MLP");
-  if (c->time_mode && (!w->final_mod_w || !w->final_mod_b))
-    return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode 1 needs final_mod_w and final_mod_b");
-  for (int l = 0; l < c->n_layers; ++l) {
-    const ae_layer_weights& L = w->layers[l];
-    if (!L.ln1 || !L.wq || !L.wk || !L.wv || !L.wo || !L.ln2 || !L.wg || !L.wu || !L.wd)
-      return fail(nullptr, AE_ERR_INVALID_ARG, "null layer weight pointer");
-    if (c->mlp_dtype == AE_FP8_E4M3 && (!L.wg_scale || !L.wu_scale || !L.wd_scale))
-      return fail(nullptr, AE_ERR_INVALID_ARG, "fp8 MLP needs per-row scales");
-    if (c->time_mode && (!L.w_mod || !L.b_mod)) return fail(nullptr, AE_ERR_INVALID_ARG, "time_mode 1 needs w_mod and b_mod");
-    if (c->qk_norm && (!L.q_norm || !L.k_norm)) return fail(nullptr, AE_ERR_INVALID_ARG, "qk_norm 1 needs q_norm and k_norm");
-  }
-  return AE_OK;
+  std::string why;
+  const int rc = ae_host::validate_config(c, w, why);
+  return rc ? fail(nullptr, rc, why) : AE_OK;
 }
 
 PhaseCfg pick(int KB, int want, int n_z) {
@@ -1327,10 +1267,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   if (!c.prefill) {  // the head (a prefill stack has none)
     TRY(upload(h, (void**)&h->action_out_b, wts->action_out_b, (size_t)A * 4));
     TRY(upload(h, (void**)&h->final_ln, wts->final_ln, (size_t)w * 4));
-    std::vector<const unsigned char*> rows(h->out_tiles * 16, nullptr);
-    for (int r = 0; r < A; ++r) rows[r] = (const unsigned char*)wts->action_out_w + (size_t)r * w * wes;
     std::vector<unsigned char> buf;
-    pack_rows(rows, w, wes, buf);
+    pack_rows(ae_host::plain_rows(wts->action_out_w, A, w, wes, h->out_tiles * 16), w, wes, buf);
     TRY(upload(h, &h->action_out_p, buf.data(), buf.size()));
   }
   // ---- decoder layers, packed
@@ -1340,44 +1278,24 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     const ae_layer_weights& Lw = wts->layers[l];
     std::vector<unsigned char> buf;
     // q heads, k heads: tile = 8 channels d..d+7 and their RoPE partners d+dh/2..; then v
-    std::vector<const unsigned char*> rows;
-    auto head_rows = [&](const void* base, int nh) {
-      for (int hh = 0; hh < nh; ++hh)
-        for (int p = 0; p < dh / 16; ++p)
-          for (int cc = 0; cc < 16; ++cc) {
-            int d = cc < 8 ? p * 8 + cc : dh / 2 + p * 8 + (cc - 8);
-            rows.push_back((const unsigned char*)base + ((size_t)hh * dh + d) * w * wes);
-          }
-    };
-    head_rows(Lw.wq, nq);
-    head_rows(Lw.wk, nkv);
-    for (int r = 0; r < nkv * dh; ++r) rows.push_back((const unsigned char*)Lw.wv + (size_t)r * w * wes);
-    pack_rows(rows, w, wes, buf);
+    pack_rows(ae_host::qkv_rows(Lw.wq, Lw.wk, Lw.wv, nq, nkv, dh, w, wes), w, wes, buf);
     void* p = nullptr;
     TRY(upload(h, &p, buf.data(), buf.size()));
     h->qkv_p.push_back(p);
-    rows.clear();
-    for (int r = 0; r < w; ++r) rows.push_back((const unsigned char*)Lw.wo + (size_t)r * nq * dh * wes);
-    pack_rows(rows, nq * dh, wes, buf);
+    pack_rows(ae_host::plain_rows(Lw.wo, w, nq * dh, wes), nq * dh, wes, buf);
     TRY(upload(h, &p, buf.data(), buf.size()));
     h->o_p.push_back(p);
-    // gate/up interleaved by 16-row tiles
-    rows.clear();
+    // gate/up interleaved by 16-row tiles (their E4M3 scales likewise)
     std::vector<float> gus;
-    for (int j = 0; j < F / 16; ++j) {
-      for (int cc = 0; cc < 16; ++cc) rows.push_back((const unsigned char*)Lw.wg + ((size_t)j * 16 + cc) * w * mes);
-      for (int cc = 0; cc < 16; ++cc) rows.push_back((const unsigned char*)Lw.wu + ((size_t)j * 16 + cc) * w * mes);
-      if (c.mlp_dtype == AE_FP8_E4M3) {
+    if (c.mlp_dtype == AE_FP8_E4M3)
+      for (int j = 0; j < F / 16; ++j) {
         for (int cc = 0; cc < 16; ++cc) gus.push_back(Lw.wg_scale[j * 16 + cc]);
         for (int cc = 0; cc < 16; ++cc) gus.push_back(Lw.wu_scale[j * 16 + cc]);
       }
-    }
-    pack_rows(rows, w, mes, buf);
+    pack_rows(ae_host::gate_up_rows(Lw.wg, Lw.wu, F, w, mes), w, mes, buf);
     TRY(upload(h, &p, buf.data(), buf.size()));
     h->gu_p.push_back(p);
-    rows.clear();
-    for (int r = 0; r < w; ++r) rows.push_back((const unsigned char*)Lw.wd + (size_t)r * F * mes);
-    pack_rows(rows, F, mes, buf);
+    pack_rows(ae_host::plain_rows(Lw.wd, w, F, mes), F, mes, buf);
     TRY(upload(h, &p, buf.data(), buf.size()));
     h->d_p.push_back(p);
     float *gs = nullptr, *ds = nullptr;
@@ -1405,7 +1323,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
       auto head_gains = [&](const float* gain, int nh) {
         for (int hh = 0; hh < nh; ++hh)
           for (int pp = 0; pp < dh / 16; ++pp)
-            for (int cc = 0; cc < 16; ++cc) gq.push_back(gain[cc < 8 ? pp * 8 + cc : dh / 2 + pp * 8 + (cc - 8)]);
+            for (int cc = 0; cc < 16; ++cc) gq.push_back(gain[ae_host::rope_tile_dim(dh, pp, cc)]);
       };
       head_gains(Lw.q_norm, nq);
       head_gains(Lw.k_norm, nkv);
@@ -1535,26 +1453,11 @@ int ae_load_prefix_kv(ae_handle* h, int slot, const void* k, const void* v) {
   const size_t es = dtype_size(c.kv_dtype);
   const size_t bytes = h->slot_elems * es;
   if (bytes) {
-    // repack into the attention's fragment order (see the attention section of the kernels):
-    // per layer and kv head, 32-key blocks; keys past prefix_len stay zero
-    const int L = c.n_layers, P = c.prefix_len, nkv = c.n_kv_heads, dh = c.head_dim, nbp = h->nbp;
-    const int nkb = dh / 32;
-    std::vector<unsigned char> kp(bytes, 0), vp(bytes, 0);
-    const unsigned char* ksrc = (const unsigned char*)k;
-    const unsigned char* vsrc = (const unsigned char*)v;
-    for (int l = 0; l < L; ++l)
-      for (int j = 0; j < P; ++j)
-        for (int g = 0; g < nkv; ++g) {
-          const size_t blk = (((size_t)l * nkv + g) * nbp + j / 32) * 32 * dh;  // block base (elements)
-          const int kk = j % 32, kt = (kk & 7) >> 2, m = 4 * (kk >> 3) + (kk & 3);
-          const size_t srow = (((size_t)l * P + j) * nkv + g) * dh;
-          for (int d = 0; d < dh; ++d) {
-            const size_t kidx = blk + ((size_t)(kt * nkb + d / 32) * 64 + ((d % 32) / 8) * 16 + m) * 8 + (d & 7);
-            const size_t vidx = blk + ((size_t)(d / 16) * 64 + (kk / 8) * 16 + (d & 15)) * 8 + (kk & 7);
-            memcpy(&kp[kidx * es], ksrc + (srow + d) * es, es);
-            memcpy(&vp[vidx * es], vsrc + (srow + d) * es, es);
-          }
-        }
+    // repack into the attention's fragment order: per layer and kv head, 32-key blocks; keys past
+    // prefix_len stay zero
+    std::vector<unsigned char> kp, vp;
+    ae_host::repack_prefix_kv((const unsigned char*)k, (const unsigned char*)v, c.n_layers, c.prefix_len, c.n_kv_heads,
+                              c.head_dim, h->nbp, es, kp, vp);
     HIP_TRY(h, hipMemcpy((char*)h->kcache + slot * bytes, kp.data(), bytes, hipMemcpyHostToDevice));
     HIP_TRY(h, hipMemcpy((char*)h->vcache + slot * bytes, vp.data(), bytes, hipMemcpyHostToDevice));
   }

@@ -94,8 +94,8 @@ def tiny_weights():
     (dict(width=0), -1),
     (dict(n_kv_heads=3), -1),           # does not divide n_q_heads
     (dict(gripper_dim=8), -1),           # outside action_dim
-    (dict(width=200), -2),               # not a multiple of 64
-    (dict(head_dim=48), -2),             # not a multiple of 32
+    (dict(width=200), -2),               # not a multiple of 256
+    (dict(head_dim=48), -2),             # not one of 32, 64, 128, 256
     (dict(action_dim=65), -2),
     (dict(kv_dtype="bf16"), -2),         # cache type differs from the attention weights
     (dict(mlp_dtype="fp8"), -2),         # fp8 MLP needs bf16 attention weights
@@ -157,3 +157,22 @@ def test_prefill_flops_match_the_closed_form():
     assert per_layer == 110_100_480
     assert per_layer == C.PREFILL.n_params // 18 - 2 * 2048
     assert bench.prefill_flops(C.PREFILL) == 18 * (2 * 816 * per_layer + 4 * 8 * 816 * 816 * 256)
+
+
+def test_host_code_under_address_and_ub_sanitizers(tmp_path):
+    """The library's host code (config checks, weight packing, prefix-cache repacking: csrc/ae_host.hpp)
+    built with g++ -fsanitize=address,undefined and run by tests/host/ae_host_check.cpp on varied
+    shapes and on configs whose sizes would overflow int; any sanitizer report or layout mismatch fails."""
+    import shutil
+    import subprocess
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    exe = tmp_path / "ae_host_check"
+    src = os.path.join(ROOT, "tests", "host", "ae_host_check.cpp")
+    build = subprocess.run([gxx, "-std=c++17", "-O1", "-g", "-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                            "-fno-omit-frame-pointer", src, "-o", str(exe)], capture_output=True, text=True)
+    assert build.returncode == 0, build.stderr[-2000:]
+    env = dict(os.environ, ASAN_OPTIONS="detect_leaks=1:verify_asan_link_order=0", UBSAN_OPTIONS="print_stacktrace=1")
+    run = subprocess.run([str(exe)], capture_output=True, text=True, env=env, timeout=300)
+    assert run.returncode == 0 and run.stdout.strip() == "ok", (run.stdout[-2000:], run.stderr[-2000:])
