@@ -69,16 +69,16 @@ extern "C" {
 enum ae_dtype { AE_F32 = 0, AE_BF16 = 1, AE_FP8_E4M3 = 2 };
 
 typedef struct ae_config {
-  int n_layers;     /* L decoder blocks */
-  int width;        /* hidden size w (multiple of 256) */
-  int n_q_heads;    /* query heads (n_q_heads * head_dim a multiple of 256) */
-  int n_kv_heads;   /* key/value heads (divides n_q_heads) */
+  int n_layers;     /* L decoder blocks (1..1024) */
+  int width;        /* hidden size w (multiple of 256, <= 65536) */
+  int n_q_heads;    /* query heads (n_q_heads * head_dim a multiple of 256; <= 1024) */
+  int n_kv_heads;   /* key/value heads (divides n_q_heads; <= 1024) */
   int head_dim;     /* dh: 32, 64, 128 or 256 */
-  int mlp_dim;      /* GeGLU inner size F (multiple of 256) */
+  int mlp_dim;      /* GeGLU inner size F (multiple of 256, <= 2^20) */
   int action_dim;   /* A (1..64) */
   int horizon;      /* H chunk rows (1..256; a prefill stack: 1..1024 tokens) */
-  int prefix_len;   /* P cached prefix tokens (>= 0) */
-  int max_batch;    /* prefix slots = robots advanced together by ae_denoise (>= 1) */
+  int prefix_len;   /* P cached prefix tokens (0..2^20) */
+  int max_batch;    /* prefix slots = robots advanced together by ae_denoise (1..4096) */
   int max_taus;     /* verification times per ae_verify call (0..64; 0 disables ae_verify) */
   float rope_base;  /* e.g. 10000 */
   float rms_eps;    /* e.g. 1e-6 (>= 0) */
