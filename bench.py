@@ -89,24 +89,27 @@ def roofline_of(kernels, dom, traffic=None):
 
 
 def measured_traffic():
-    """HBM bytes per launch of each kernel from the committed rocprofv3 counter summary, or {} when
-    the kernel sources have changed since the counters were taken."""
+    """HBM bytes per launch of each kernel from the committed rocprofv3 counter summaries (profiles/*.md
+    with a machine-readable table), keeping only those taken from the kernel sources as they are now."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "traffic_pi0_bf16_kernels.md")
-    if not os.path.exists(path):
-        return {}
     sha = hashlib.sha256()
     for f in ("ae_kernels.hpp", "ae_fused.hpp", "ae_runtime.hip"):
         with open(os.path.join(ROOT, "flow_matching_action_euler_amd", "csrc", f), "rb") as fh:
             sha.update(fh.read())
-    want, table = None, {}
-    with open(path) as fh:
-        for line in fh:
-            if line.startswith("traffic_source_sha256_16:"):
-                want = line.split(":", 1)[1].strip()
-            elif line.startswith("traffic_bytes_per_launch:"):
-                table = json.loads(line.split(":", 1)[1])
-    return table if want == sha.hexdigest()[:16] else {}
+    now = sha.hexdigest()[:16]
+    out = {}
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        want, table = None, {}
+        with open(path) as fh:
+            for line in fh:
+                if line.startswith("traffic_source_sha256_16:"):
+                    want = line.split(":", 1)[1].strip()
+                elif line.startswith("traffic_bytes_per_launch:"):
+                    table = json.loads(line.split(":", 1)[1])
+        if want == now:
+            out.update(table)
+    return out
 
 
 def step_bytes(cfg, batch):

@@ -1793,20 +1793,36 @@ __global__ __launch_bounds__(VERIFY_THREADS) void verify_kernel(const float* x, 
   int S = 1;
   while (S < A) S <<= 1;
   const int sub = lane & (S - 1), rows = n_tau * H, per_pass = VERIFY_THREADS / S;
-  for (int r0 = 0; r0 < rows; r0 += per_pass) {
-    const int r = r0 + (int)threadIdx.x / S;
-    float d2 = 0.f;
-    if (r < rows && sub < A) {
-      const int j = r / H, i = r % H;
-      const size_t idx = (size_t)r * A + sub;
-      const float diff = x[idx] + (1.f - taus[j]) * v[idx] - draft[(size_t)i * A + sub];
-      d2 = diff * diff;
+  // VP passes at a time, every load of them issued before the first is used (one memory round trip
+  // per VP passes instead of one per pass)
+  constexpr int VP = 8;
+  for (int r00 = 0; r00 < rows; r00 += VP * per_pass) {
+    float xv[VP], vv[VP], dv[VP], om[VP];
+#pragma unroll
+    for (int p = 0; p < VP; ++p) {
+      const int r = r00 + p * per_pass + (int)threadIdx.x / S;
+      const bool in = r < rows && sub < A;
+      const int rc = in ? r : 0, j = rc / H, i = rc % H;
+      const size_t idx = (size_t)rc * A + (in ? sub : 0);
+      xv[p] = x[idx];
+      vv[p] = v[idx];
+      dv[p] = draft[(size_t)i * A + (in ? sub : 0)];
+      om[p] = 1.f - taus[j];
     }
-    for (int o = S >> 1; o > 0; o >>= 1) d2 += __shfl_xor(d2, o, 64);
-    if (r < rows && sub == 0) {
-      const float dd = sqrtf(d2);
-      dsh[r] = dd;
-      if (dist_out) dist_out[r] = dd;
+#pragma unroll
+    for (int p = 0; p < VP; ++p) {
+      const int r = r00 + p * per_pass + (int)threadIdx.x / S;
+      float d2 = 0.f;
+      if (r < rows && sub < A) {
+        const float diff = xv[p] + om[p] * vv[p] - dv[p];
+        d2 = diff * diff;
+      }
+      for (int o = S >> 1; o > 0; o >>= 1) d2 += __shfl_xor(d2, o, 64);
+      if (r < rows && sub == 0) {
+        const float dd = sqrtf(d2);
+        dsh[r] = dd;
+        if (dist_out) dist_out[r] = dd;
+      }
     }
   }
   __syncthreads();
