@@ -725,12 +725,6 @@ struct FusedStep {
             O2 += wt * oc[c];
           }
         M2 = Mn;
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          if (c < nc && act) {
-            st16_empty(ro, ooff(c));
-            if (kc == 0) __builtin_amdgcn_raw_buffer_store_b64(i32x2{-1, -1}, rm, moff(c), 0, 0x10);
-          }
       }
       if (!ok) break;
       const int r2 = qt * ATT_ROWS + rr2;
@@ -740,6 +734,14 @@ struct FusedStep {
         const uint2 o = make_uint2(pack_bf16x2(O2[0] * inv, O2[1] * inv), pack_bf16x2(O2[2] * inv, O2[3] * inv));
         st8_coherent(rr, blk(l) + a.off_o + (unsigned)(act_idx(tok, col, a.ntt) * 2), o);
       }
+      // the partials read go back to the empty pattern after o is out (o_proj waits for o; the partials
+      // of layer l are next used by the next launch)
+      if (act)
+        for (int c = 0; c < a.n_split; ++c) {
+          const size_t prow = ((size_t)l * a.n_att + (size_t)c * upsp + rest) * ATT_ROWS + rr2;
+          st16_empty(ro, (unsigned)((prow * DH + kc * 4) * 4));
+          if (kc == 0) __builtin_amdgcn_raw_buffer_store_b64(i32x2{-1, -1}, rm, (unsigned)(prow * 8), 0, 0x10);
+        }
     }
     return settle(ok);
   }
