@@ -555,10 +555,9 @@ struct FusedStep {
     constexpr int NKV = 2 * NKB + NDT;  // K fragments [kt][kb], then V fragments [dt]
     i32x4 kv[NKV];
     bool ok = true;
-    if (!has || pre) {  // prefix block (or the split's first block, masked): plain loads
-      const int bq = pre ? bb : (b_begin < a.nbp ? b_begin : 0);
-      const uint16_t* kf = Ly.kc + a.slot_off + ((size_t)g * a.nbp + bq) * (2 * NKB * FR);
-      const uint16_t* vf = Ly.vc + a.slot_off + ((size_t)g * a.nbp + bq) * (2 * NKB * FR);
+    if (pre) {  // a prefix block: plain loads (a wave with no block of the split loads nothing)
+      const uint16_t* kf = Ly.kc + a.slot_off + ((size_t)g * a.nbp + bb) * (2 * NKB * FR);
+      const uint16_t* vf = Ly.vc + a.slot_off + ((size_t)g * a.nbp + bb) * (2 * NKB * FR);
 #pragma unroll
       for (int i = 0; i < 2 * NKB; ++i) kv[i] = *(const i32x4*)(kf + i * FR + lane * 8);
 #pragma unroll
@@ -596,6 +595,7 @@ struct FusedStep {
            ok;
     }
     if (!settle(ok)) return false;
+    if (has) {
     // S^T = K Q^T, online softmax over the block, O^T = V^T P^T (as the stand-alone attention)
     const int k8 = 8 * (lane >> 4);
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -638,6 +638,9 @@ struct FusedStep {
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) *(f32x4*)(ow + dt * 16) = oacc[dt];
     if (lane < 16) *(float2*)(MLw + (wave * ATT_ROWS + lane) * 2) = make_float2(mb, lb);
+    } else if (lane < 16) {  // no block: m = -inf marks the wave's O (never written) as absent
+      *(float2*)(MLw + (wave * ATT_ROWS + lane) * 2) = make_float2(-INFINITY, 0.f);
+    }
     lds_barrier();
     // merge the waves: thread -> (row, 16-byte chunk), published as this unit's partial
     constexpr int CPR = DH / 4;
@@ -653,9 +656,11 @@ struct FusedStep {
 #pragma unroll
       for (int wv = 0; wv < FW; ++wv) {
         const float mw = MLw[(wv * ATT_ROWS + row) * 2];
-        const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
-        Lsum += wt * MLw[(wv * ATT_ROWS + row) * 2 + 1];
-        O += wt * *(const f32x4*)(Ow + ((size_t)wv * ATT_ROWS + row) * LDO + 4 * c4);
+        if (mw != -INFINITY) {
+          const float wt = exp2f(mw - M);
+          Lsum += wt * MLw[(wv * ATT_ROWS + row) * 2 + 1];
+          O += wt * *(const f32x4*)(Ow + ((size_t)wv * ATT_ROWS + row) * LDO + 4 * c4);
+        }
       }
       st16_coherent(ro, (unsigned)(((prow + row) * DH + 4 * c4) * 4), make_float4(O[0], O[1], O[2], O[3]));
       if (c4 == 0)

@@ -123,3 +123,26 @@ def test_zero_tick_async_give_up_is_reported_by_the_next_call(monkeypatch):
         assert rel_err(got, ref) <= tol_for(cfg)
     assert reported >= 1, "a zero-tick wait inside the step kernel gives up"
     ex.close()
+
+
+def test_step_kernel_on_another_prefix_slot():
+    """A dual-path round on prefix slot 1 whose draft switches the gripper runs the full path: the
+    batch-1 denoise of slot 1 on the persistent step kernel (its cache offset is the slot's)."""
+    from oracle import ae_oracle as O
+    from workload import gen as G
+    cfg = STEP_BF16.with_(name="step_bf16_round", max_batch=2, max_taus=3, gripper_dim=23)
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.array([0.2, 0.5, 0.8], np.float32)
+    draft = G.make_draft(cfg, 1)  # odd seeds switch the gripper
+    nv = case.noise(1, 301)[0]
+    nf = case.noise(1, 401)[0]
+    for slot in (1, 0, 1):
+        act, acc, sw, full = ex.round(slot, draft, nv, taus, 0.05, nf, 3)
+        act_o, acc_o, sw_o, full_o = O.dual_path_round(cfg, case.Wd, case.kvd[slot][0], case.kvd[slot][1], draft, nv,
+                                                       taus, 0.05, nf, 3)
+        assert (acc, sw, full) == (acc_o, sw_o, full_o) == (0, 1, 1), slot
+        err = rel_err(act, act_o)
+        print(f"slot {slot} full-path rel_err={err:.3e}")
+        assert err <= tol_for(cfg), (slot, err)
+    ex.close()
