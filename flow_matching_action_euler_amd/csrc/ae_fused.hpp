@@ -49,6 +49,7 @@ struct FusedLayer {
   const float* g_next;   // gain of the next norm (next layer's ln1, or the final norm)
   const uint16_t* kc;    // this layer's packed prefix K of slot 0 (a pass on slot s adds FusedArgs::slot_off)
   const uint16_t* vc;    // and V
+  const float* qk_gain;  // QK-norm: gain per packed q/k channel; else null
 };
 
 struct FusedArgs {
@@ -80,6 +81,20 @@ struct FusedArgs {
   unsigned* host_flag;   // host-visible copy of abort
   unsigned long long wait_ticks;
   size_t slot_off;       // elements from slot 0's prefix cache to the pass's slot
+  // time-modulated expert (null otherwise; DM0.5 guide, section 5.2): this step's vectors of layer l at
+  // base + l * stride: norm gains ln1 (1 + scale1) and ln2 (1 + scale2), the shift biases of QKV and
+  // gate/up in their packed channel order, the modulation rows [6w] (gates at 2w and 5w), the final gain
+  const float* m_g1;
+  const float* m_g2;
+  const float* m_bqkv;
+  const float* m_bgu;
+  const float* m_mod;
+  const float* m_gf;
+  size_t m_sw, m_sqkv, m_sgu, m_smod;
+  // QK-norm: byte offset in a ring block of the per-tile sums of squares of q and k ([(nq + nkv) dh/16]
+  // [ntt * 16] fp32), 0 without QK-norm
+  unsigned off_qks;
+  float qk_inv_dh, qk_eps;
 };
 
 constexpr int FW = 8;            // waves per workgroup
@@ -94,8 +109,11 @@ constexpr size_t fused_scratch_bytes() {
   constexpr size_t gemm = (size_t)FW * F_NQ * 1024 + (size_t)F_NQ * 1024 + 64 * 4 + FW * 64 * 4;
   return att > gemm ? att : gemm;
 }
+// after the scratch: the residual slots, the abort word (16 bytes), QK-norm's 1/rms of the 16 query rows
+// and of each wave's 32 suffix keys
+constexpr size_t F_QKN_FLOATS = ATT_ROWS + FW * ATT_KB;
 template <int DH>
-constexpr size_t fused_lds_bytes() { return fused_scratch_bytes<DH>() + (size_t)F_SLOTS * 1024 + 16; }
+constexpr size_t fused_lds_bytes() { return fused_scratch_bytes<DH>() + (size_t)F_SLOTS * 1024 + 16 + F_QKN_FLOATS * 4; }
 
 // ------------------------------------------------------------------ polling
 
@@ -419,7 +437,7 @@ struct FusedStep {
         slot[e] = h;
       }
       lds_barrier();
-      resid_store(tid, a, slot, tile, tt, a.ln1_0, rr, blk(0), blk(0) + a.off_ssp);
+      resid_store(tid, a, slot, tile, tt, a.m_g1 ? a.m_g1 : a.ln1_0, rr, blk(0), blk(0) + a.off_ssp);
     }
   }
 
@@ -445,16 +463,17 @@ struct FusedStep {
       unit_reduce<F_QKV_NT>(tid, accq, red, res);
 #pragma unroll
       for (int t = 0; t < F_QKV_NT; ++t)
-        if (tile[t] >= 0) qkv_epilogue(l, tile[t], tt, res + t * 256);
+        if (tile[t] >= 0) qkv_epilogue(l, tile[t], tt, res + t * 256, Ly.qk_gain);
       lds_barrier();
     }
     return true;
   }
 
-  __device__ void qkv_epilogue(int l, int tin, int tt, const float* r) {
+  __device__ void qkv_epilogue(int l, int tin, int tt, const float* r, const float* qk_gain) {
     const int dh = a.dh, tph = dh / 16, half = dh / 2, nkb = dh / KBLK;
     const int q_tiles = a.nq * tph, k_tiles = a.nkv * tph, gq = a.nq / a.nkv;
     const int t = tid;
+    const float* sb = a.m_bqkv ? a.m_bqkv + (size_t)l * a.m_sqkv + tin * 16 : nullptr;  // shift bias of the tile
     if (tin < q_tiles + k_tiles) {
       if (t >= 32) return;
       const int tok = t >> 1, hf = t & 1, tg = tt * 16 + tok;  // (token, half of the tile's channels)
@@ -464,7 +483,17 @@ struct FusedStep {
       const float ir = inv_rms[tok];
       float xs[16];
 #pragma unroll
-      for (int c = 0; c < 16; ++c) xs[c] = r[mfma_idx(c, tok)] * ir;
+      for (int c = 0; c < 16; ++c) xs[c] = r[mfma_idx(c, tok)] * ir + (sb ? sb[c] : 0.f);
+      if (qk_gain) {  // QK-norm: the tile's share of the head's sum of squares, then the gains (before RoPE)
+        float sq2 = 0.f;
+#pragma unroll
+        for (int c = 0; c < 16; ++c) sq2 += xs[c] * xs[c];
+        if (hf == 0)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_int(sq2), rr,
+                                                blk(l) + a.off_qks + (unsigned)(((size_t)tin * a.ntt * 16 + tg) * 4), 0, 0x10);
+#pragma unroll
+        for (int c = 0; c < 16; ++c) xs[c] *= qk_gain[tin * 16 + c];
+      }
       const float4* csp = (const float4*)(a.rope_cs + ((size_t)tg * half + pair * 8) * 2);
       float out[8];
 #pragma unroll
@@ -501,7 +530,7 @@ struct FusedStep {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int tok = g8 * 8 + e;
-        vv[e] = t0 + e < a.H ? r[mfma_idx(c, tok)] * inv_rms[tok] : 0.f;
+        vv[e] = t0 + e < a.H ? r[mfma_idx(c, tok)] * inv_rms[tok] + (sb ? sb[c] : 0.f) : 0.f;
       }
       const size_t fr = ((size_t)hd * a.nbs + (t0 >> 5)) * tph + d16;
       const unsigned off = a.off_v + (unsigned)((fr * 512 + ((((t0 & 31) >> 3) << 4) + c) * 8) * 2);
@@ -594,6 +623,48 @@ struct FusedStep {
                kv, a) &&
            ok;
     }
+    // QK-norm: 1/rms of the 16 query rows and of this wave's suffix keys, from the QKV tiles' sums of
+    // squares (prefix keys come normalised)
+    float* rq_s = (float*)(lds + fused_scratch_bytes<DH>() + (size_t)F_SLOTS * 1024 + 16);
+    float* rk_s = rq_s + ATT_ROWS + wave * ATT_KB;
+    if (a.off_qks) {
+      constexpr int TPH = DH / 16;
+      static_assert(TPH <= 16, "16 lanes per query row");
+      const int Mp = a.ntt * 16, q_tiles = a.nq * TPH;
+      if (tid < ATT_ROWS * 16) {  // thread -> (row, tile of the row's head)
+        const int row = tid >> 4, i = tid & 15, rg = qt * ATT_ROWS + row;
+        const bool need = rg < R && i < TPH;
+        const int head = g * gq + (rg < R ? rg / a.H : 0), t = rg < R ? rg % a.H : 0;
+        float v[1];
+        ok = poll4<1>(rr, {blk(l) + a.off_qks + (unsigned)((((size_t)head * TPH + (need ? i : 0)) * Mp + t) * 4)}, {need}, v, a) &&
+             ok;
+        float sum = v[0];
+        sum += __shfl_xor(sum, 1);
+        sum += __shfl_xor(sum, 2);
+        sum += __shfl_xor(sum, 4);
+        sum += __shfl_xor(sum, 8);
+        if (i == 0) rq_s[row] = rg < R ? rsqrtf(sum * a.qk_inv_dh + a.qk_eps) : 0.f;
+      }
+      if (has && !pre) {  // lane -> (key lane % 32, tiles 8 (lane / 32) ..): 8 partial sums each
+        const int kk = lane & 31, t = (bb - a.nbp) * ATT_KB + kk, i0 = (lane >> 5) * 8;
+        const bool kv_ok = t < a.H;
+        float v[8];
+        unsigned offs[8];
+        bool needs[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          needs[j] = kv_ok && i0 + j < TPH;
+          offs[j] = blk(l) + a.off_qks +
+                    (unsigned)((((size_t)q_tiles + g * TPH + (needs[j] ? i0 + j : 0)) * Mp + (kv_ok ? t : 0)) * 4);
+        }
+        ok = poll4<8>(rr, offs, needs, v, a) && ok;
+        float sum = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) sum += v[j];
+        sum += __shfl_xor(sum, 32);
+        if (lane < ATT_KB) rk_s[kk] = kv_ok ? rsqrtf(sum * a.qk_inv_dh + a.qk_eps) : 0.f;
+      }
+    }
     if (!settle(ok)) return false;
     if (has) {
     // S^T = K Q^T, online softmax over the block, O^T = V^T P^T (as the stand-alone attention)
@@ -607,11 +678,14 @@ struct FusedStep {
         sacc[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(B8, kv[kt * NKB + kb]), qb, sacc[kt], 0, 0, 0);
     }
     float mb = -INFINITY;
+    const float row_scale = a.off_qks ? a.scale_log2 * rq_s[lane & 15] : a.scale_log2;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const float sv = (k8 + 4 * kt + v < n_valid) ? sacc[kt][v] * a.scale_log2 : -INFINITY;
+        float f = row_scale;
+        if (a.off_qks && !pre && k8 + 4 * kt + v < n_valid) f *= rk_s[k8 + 4 * kt + v];
+        const float sv = (k8 + 4 * kt + v < n_valid) ? sacc[kt][v] * f : -INFINITY;
         sacc[kt][v] = sv;
         mb = fmaxf(mb, sv);
       }
@@ -766,9 +840,14 @@ struct FusedStep {
       const f32x4 accq[1] = {acc[0][0]};
       unit_reduce<1>(tid, accq, red, res);
       float* slot = slots + i * 256;
-      if (tid < 256) slot[tid] += res[tid];
+      const float* gate = a.m_mod ? a.m_mod + (size_t)l * a.m_smod + 2 * a.w : nullptr;  // time modulation
+      if (tid < 256) {
+        const int ln = tid >> 2, c = ((ln >> 4) << 2) + (tid & 3);
+        slot[tid] += gate ? gate[tile * 16 + c] * res[tid] : res[tid];
+      }
       lds_barrier();
-      resid_store(tid, a, slot, tile, tt, Ly.ln2, rr, blk(l) + a.off_hb2, blk(l) + a.off_ssp2);
+      resid_store(tid, a, slot, tile, tt, a.m_g2 ? a.m_g2 + (size_t)l * a.m_sw : Ly.ln2, rr, blk(l) + a.off_hb2,
+                  blk(l) + a.off_ssp2);
     }
     return true;
   }
@@ -816,8 +895,17 @@ struct FusedStep {
               gv = make_float4(gv.x * sg.x, gv.y * sg.y, gv.z * sg.z, gv.w * sg.w);
               uv = make_float4(uv.x * su.x, uv.y * su.y, uv.z * su.z, uv.w * su.w);
             }
-            const uint2 o = make_uint2(pack_bf16x2(gelu_tanh_fast(gv.x * ir) * (uv.x * ir), gelu_tanh_fast(gv.y * ir) * (uv.y * ir)),
-                                       pack_bf16x2(gelu_tanh_fast(gv.z * ir) * (uv.z * ir), gelu_tanh_fast(gv.w * ir) * (uv.w * ir)));
+            gv = make_float4(gv.x * ir, gv.y * ir, gv.z * ir, gv.w * ir);
+            uv = make_float4(uv.x * ir, uv.y * ir, uv.z * ir, uv.w * ir);
+            if (a.m_bgu) {  // time modulation: the shift biases of the gate and up channels
+              const float* sb = a.m_bgu + (size_t)l * a.m_sgu;
+              const float4 bg = *(const float4*)(sb + (size_t)(2 * p) * 16 + cq * 4);
+              const float4 bu = *(const float4*)(sb + (size_t)(2 * p + 1) * 16 + cq * 4);
+              gv = make_float4(gv.x + bg.x, gv.y + bg.y, gv.z + bg.z, gv.w + bg.w);
+              uv = make_float4(uv.x + bu.x, uv.y + bu.y, uv.z + bu.z, uv.w + bu.w);
+            }
+            const uint2 o = make_uint2(pack_bf16x2(gelu_tanh_fast(gv.x) * uv.x, gelu_tanh_fast(gv.y) * uv.y),
+                                       pack_bf16x2(gelu_tanh_fast(gv.z) * uv.z, gelu_tanh_fast(gv.w) * uv.w));
             st8_coherent(rr, blk(l) + a.off_u + (unsigned)(act_idx(tg, p * 16 + cq * 4, a.ntt) * 2), o);
           }
         }
@@ -842,16 +930,16 @@ struct FusedStep {
       const f32x4 accq[1] = {acc[0][0]};
       unit_reduce<1>(tid, accq, red, res);
       float* slot = slots + i * 256;
+      const float* gate = a.m_mod ? a.m_mod + (size_t)l * a.m_smod + 5 * a.w : nullptr;  // time modulation
       if (tid < 256) {
+        const int ln = tid >> 2, c = ((ln >> 4) << 2) + (tid & 3);
         float v = res[tid];
-        if constexpr (MT == WT_FP8) {
-          const int ln = tid >> 2, c = ((ln >> 4) << 2) + (tid & 3);
-          v *= Ly.d_s[tile * 16 + c];
-        }
-        slot[tid] += v;
+        if constexpr (MT == WT_FP8) v *= Ly.d_s[tile * 16 + c];
+        slot[tid] += gate ? gate[tile * 16 + c] * v : v;
       }
       lds_barrier();
-      resid_store(tid, a, slot, tile, tt, Ly.g_next, rr, blk(l + 1), blk(l + 1) + a.off_ssp);
+      const float* gn = !a.m_g1 ? Ly.g_next : l + 1 < a.L ? a.m_g1 + (size_t)(l + 1) * a.m_sw : a.m_gf;
+      resid_store(tid, a, slot, tile, tt, gn, rr, blk(l + 1), blk(l + 1) + a.off_ssp);
     }
     return true;
   }

@@ -140,6 +140,7 @@ struct ae_handle {
   FusedLayer* fused_layers = nullptr;  // device [L]
   char* ring[2] = {nullptr, nullptr};  // activation rings of alternating launches
   unsigned layer_bytes = 0, off_ssp = 0, off_q = 0, off_k = 0, off_v = 0, off_o = 0, off_hb2 = 0, off_ssp2 = 0, off_u = 0;
+  unsigned off_qks = 0;              // QK-norm partials in a ring block (0: none)
   float *fpart_o = nullptr, *fpart_ml = nullptr;
   size_t fpart_o_floats = 0, fpart_ml_floats = 0;
   unsigned* abort_dev = nullptr;
@@ -817,7 +818,7 @@ int setup_fused(ae_handle* h) {
     h->fused_why = why;
     return AE_OK;
   };
-  if (c.draft || c.prefill || c.time_mode || c.qk_norm || c.weight_dtype != AE_BF16 || c.kv_dtype != AE_BF16 ||
+  if (c.draft || c.prefill || c.weight_dtype != AE_BF16 || c.kv_dtype != AE_BF16 ||
       (c.mlp_dtype != AE_BF16 && c.mlp_dtype != AE_FP8_E4M3))
     return no("model variant or dtypes");
   if (H > 64 || c.prefix_len < 1 || h->n_cu < 32 || h->n_cu % 32) return no("horizon, prefix or compute-unit count");
@@ -873,6 +874,7 @@ int setup_fused(ae_handle* h) {
   h->off_hb2 = take(Mp * w * 2);
   h->off_ssp2 = take((size_t)(w / 16) * Mp * 4);
   h->off_u = take(Mp * F * 2);
+  if (c.qk_norm) h->off_qks = take((size_t)(nq + nkv) * (dh / 16) * Mp * 4);
   h->layer_bytes = (unsigned)off;
   for (int r = 0; r < 2; ++r) {
     const int rc = dalloc(h, (void**)&h->ring[r], (size_t)(L + 1) * off);
@@ -897,6 +899,7 @@ int setup_fused(ae_handle* h) {
     ly[l].g_next = l + 1 < L ? h->ln1[l + 1] : h->final_ln;
     ly[l].kc = (const uint16_t*)h->kcache + (size_t)l * lay;
     ly[l].vc = (const uint16_t*)h->vcache + (size_t)l * lay;
+    ly[l].qk_gain = c.qk_norm ? h->qk_gain[l] : nullptr;
   }
   rc = upload(h, (void**)&h->fused_layers, ly.data(), L * sizeof(FusedLayer));
   if (rc) return rc;
@@ -931,8 +934,33 @@ int enqueue_fused(ae_handle* h, int steps, const float* temb, hipStream_t st, Ti
   fa.off_hb2 = h->off_hb2; fa.off_ssp2 = h->off_ssp2; fa.off_u = h->off_u;
   fa.abort = h->abort_dev; fa.host_flag = h->flag_dev; fa.wait_ticks = h->wait_ticks;
   fa.slot_off = (size_t)slot0 * h->slot_elems;
+  fa.off_qks = h->off_qks;
+  fa.qk_inv_dh = 1.f / (float)c.head_dim;
+  fa.qk_eps = c.rms_eps;
+  const ae_handle::ModTable* mt = nullptr;  // time modulation: this step count's table
+  if (c.time_mode) {
+    auto it = h->mod_steps.find(steps);
+    if (it == h->mod_steps.end()) return fail(h, AE_ERR_HIP, "modulation table missing for this step count");
+    mt = &it->second;
+    const size_t w = c.width;
+    fa.m_sw = (size_t)steps * w;
+    fa.m_sqkv = (size_t)steps * h->qkv_tiles * 16;
+    fa.m_sgu = (size_t)steps * h->gu_tiles * 16;
+    fa.m_smod = (size_t)steps * 6 * w;
+  }
   for (int k = 0; k < steps; ++k) {
     fa.temb = temb + (size_t)k * c.width;
+    if (mt) {  // step k's vectors; the tokens get no temb, the head this step's bias
+      const size_t w = c.width;
+      fa.temb = h->zero_w;
+      fa.m_g1 = mt->g1 + (size_t)k * w;
+      fa.m_g2 = mt->g2 + (size_t)k * w;
+      fa.m_bqkv = mt->bqkv + (size_t)k * h->qkv_tiles * 16;
+      fa.m_bgu = mt->bgu + (size_t)k * h->gu_tiles * 16;
+      fa.m_mod = mt->mod + (size_t)k * 6 * w;
+      fa.m_gf = mt->gf + (size_t)k * w;
+      fa.b_out = mt->bout + (size_t)k * h->out_tiles * 16;
+    }
     fa.ring = h->ring[k & 1];
     fa.ring_other = h->ring[(k + 1) & 1];
     LAUNCH_CHECK(h, "fused_step", AE_LAUNCH(h->fused_fn, dim3(h->n_cu), dim3(FT), h->fused_lds, st, fa));

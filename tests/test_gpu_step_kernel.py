@@ -24,6 +24,10 @@ STEP_BF16 = C.PI0.with_(name="step_bf16", n_layers=2, horizon=20, prefix_len=100
 STEP_FP8 = STEP_BF16.with_(name="step_fp8", mlp_dtype="fp8")
 STEP_LONG = STEP_BF16.with_(name="step_bf16_long_prefix", prefix_len=1100, horizon=50, action_dim=32)
 STEP_H64 = STEP_BF16.with_(name="step_bf16_h64", horizon=64, prefix_len=300)
+# time modulation and QK-norm (the DM0.5-style expert): per-step gains, shift biases and gates, and the
+# per-head 1/rms of q and k exchanged between the QKV and attention phases
+STEP_DM05 = STEP_BF16.with_(name="step_dm05", time_mode=1, qk_norm=1)
+STEP_DM05_LONG = STEP_LONG.with_(name="step_dm05_long_prefix", time_mode=1, qk_norm=1)
 
 
 def _uses_step_kernel(ex, steps):
@@ -38,7 +42,8 @@ def _expert(case):
     return ex
 
 
-@pytest.mark.parametrize("cfg", [STEP_BF16, STEP_FP8, STEP_LONG, STEP_H64], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", [STEP_BF16, STEP_FP8, STEP_LONG, STEP_H64, STEP_DM05, STEP_DM05_LONG],
+                         ids=lambda c: c.name)
 def test_step_kernel_matches_oracle(cfg):
     case = Case(cfg)
     ex = _expert(case)
@@ -55,9 +60,10 @@ def test_step_kernel_matches_oracle(cfg):
     ex.close()
 
 
-def test_step_kernel_agrees_with_launch_per_phase(monkeypatch):
+@pytest.mark.parametrize("cfg", [STEP_LONG, STEP_DM05_LONG], ids=lambda c: c.name)
+def test_step_kernel_agrees_with_launch_per_phase(cfg, monkeypatch):
     """Same GEMM splits, different attention key splits and reduction order: bf16-level agreement."""
-    case = Case(STEP_LONG)
+    case = Case(cfg)
     noise = case.noise(1)
     outs = {}
     for fused in ("1", "0"):
@@ -69,8 +75,8 @@ def test_step_kernel_agrees_with_launch_per_phase(monkeypatch):
         ex.close()
     ref = case.oracle_denoise(noise, 3)
     for k, v in outs.items():
-        assert rel_err(v, ref) <= tol_for(STEP_LONG), k
-    assert rel_err(outs["1"], outs["0"]) <= tol_for(STEP_LONG)
+        assert rel_err(v, ref) <= tol_for(cfg), k
+    assert rel_err(outs["1"], outs["0"]) <= tol_for(cfg)
 
 
 @pytest.mark.parametrize("cfg", [STEP_BF16, SMALL_BF16.with_(name="small_bf16_long_prefix", prefix_len=1100)],
