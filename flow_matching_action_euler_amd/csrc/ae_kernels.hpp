@@ -1788,13 +1788,17 @@ __global__ __launch_bounds__(VERIFY_THREADS) void verify_kernel(const float* x, 
                                                                 int* accept_out, int* switch_out) {
   extern __shared__ float dsh[];  // [n_tau][H]
   __shared__ int w_first[VERIFY_THREADS / 64], w_flip[VERIFY_THREADS / 64];
-  const float delta = params[0];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int S = 1;
   while (S < A) S <<= 1;
   const int sub = lane & (S - 1), rows = n_tau * H, per_pass = VERIFY_THREADS / S;
-  // VP passes at a time, every load of them issued before the first is used (one memory round trip
-  // per VP passes instead of one per pass)
+  // every global load of the kernel goes out first (one memory round trip): the gripper column of
+  // rows i and i-1 for thread i (rows up to 1024), delta, then VP passes of endpoint operands
+  const int gi = (int)threadIdx.x;
+  const bool g_row = gripper_dim >= 0 && gi > 0 && gi < H;
+  const float g_cur = g_row ? draft[(size_t)gi * A + gripper_dim] : 0.f;
+  const float g_prev = g_row ? draft[(size_t)(gi - 1) * A + gripper_dim] : 0.f;
+  const float delta = params[0];
   constexpr int VP = 8;
   for (int r00 = 0; r00 < rows; r00 += VP * per_pass) {
     float xv[VP], vv[VP], dv[VP], om[VP];
@@ -1826,31 +1830,27 @@ __global__ __launch_bounds__(VERIFY_THREADS) void verify_kernel(const float* x, 
     }
   }
   __syncthreads();
-  int first = H, flip = 0;
-  for (int i0 = 0; i0 < H; i0 += VERIFY_THREADS) {
-    const int i = i0 + (int)threadIdx.x;
-    bool bad = false, fl = false;
-    if (i < H) {
-      for (int j = 0; j < n_tau; ++j) bad = bad || !(dsh[j * H + i] < delta);
-      if (gripper_dim >= 0 && i > 0) fl = draft[(size_t)i * A + gripper_dim] * draft[(size_t)(i - 1) * A + gripper_dim] < 0.f;
-    }
-    const unsigned long long mb = __ballot(bad), mf = __ballot(fl);
-    if (lane == 0) {
-      w_first[wave] = mb ? i0 + wave * 64 + (__ffsll((long long)mb) - 1) : H;
-      w_flip[wave] = mf != 0ull;
-    }
-    __syncthreads();
-    if (threadIdx.x == 0) {
-      for (int w = 0; w < VERIFY_THREADS / 64; ++w) {
-        first = min(first, w_first[w]);
-        flip |= w_flip[w];
-      }
-    }
-    __syncthreads();
+  // row i is rejected when some flow time has D >= delta (or D is NaN); rows up to 1024
+  bool bad = false;
+  if (gi < H)
+    for (int j = 0; j < n_tau; ++j) bad = bad || !(dsh[j * H + gi] < delta);
+  const unsigned long long mb = __ballot(bad), mf = __ballot(g_row && g_cur * g_prev < 0.f);
+  if (lane == 0) {
+    w_first[wave] = mb ? wave * 64 + (__ffsll((long long)mb) - 1) : H;
+    w_flip[wave] = mf != 0ull;
   }
-  if (threadIdx.x == 0) {
-    *accept_out = flip ? 0 : first;
-    *switch_out = flip;
+  __syncthreads();
+  if (wave == 0) {  // the first rejected row and any flip over the 16 waves, by shuffles
+    int first = lane < VERIFY_THREADS / 64 ? w_first[lane] : H;
+    int flip = lane < VERIFY_THREADS / 64 ? w_flip[lane] : 0;
+    for (int o = 8; o > 0; o >>= 1) {
+      first = min(first, __shfl_xor(first, o, 64));
+      flip |= __shfl_xor(flip, o, 64);
+    }
+    if (lane == 0) {
+      *accept_out = flip ? 0 : first;
+      *switch_out = flip;
+    }
   }
 }
 
