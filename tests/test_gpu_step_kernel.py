@@ -152,3 +152,24 @@ def test_step_kernel_on_another_prefix_slot():
         print(f"slot {slot} full-path rel_err={err:.3e}")
         assert err <= tol_for(cfg), (slot, err)
     ex.close()
+
+
+# the work split's edge cases: 1 and 16 rows (one token tile, ntp 1), 17 and 33 rows (2 and 3 token tiles,
+# ragged), a one-key prefix (one block, 31 masked keys), a 31-key prefix, and a 2,000-key prefix (65 blocks:
+# 9 key splits of 8 blocks, more units than the XCD grouping covers)
+EDGE = [STEP_BF16.with_(name=f"step_h{H}_p{P}", horizon=H, prefix_len=P, steps=2)
+        for H, P in ((1, 100), (16, 1), (17, 31), (33, 2000))]
+
+
+@pytest.mark.parametrize("cfg", EDGE, ids=lambda c: c.name)
+def test_step_kernel_work_split_edges(cfg):
+    case = Case(cfg)
+    ex = _expert(case)
+    assert _uses_step_kernel(ex, 2)
+    noise = case.noise(1)
+    for steps in (1, 2):
+        got = ex.denoise(noise, steps)
+        err = rel_err(got, case.oracle_denoise(noise, steps))
+        print(f"{cfg.name} steps={steps} rel_err={err:.3e}")
+        assert err <= tol_for(cfg), (steps, err)
+    ex.close()
