@@ -596,3 +596,26 @@ def test_pi0_batch16_every_robot(pi0_case, robots):
         print(f"batch16 robot {r} rel_err={err:.3e}")
         assert err <= 2e-2
     ex.close()
+
+
+# ------------------------------------------------------------------ several robots at the Pi0 widths
+
+# Pi0 widths, two layers, several robots (launch per phase: the step kernel is for batch 1): a 100-key
+# prefix and a 1,100-key prefix (37 blocks), 50 rows x 8 heads = 25 query tiles
+PI0W = [C.PI0.with_(name="pi0w_p100_b3", n_layers=2, prefix_len=100, max_batch=3, batch=3, steps=2),
+          C.PI0.with_(name="pi0w_p1100_b2", n_layers=2, prefix_len=1100, max_batch=2, batch=2, steps=2)]
+
+
+@pytest.mark.parametrize("cfg", PI0W, ids=lambda c: c.name)
+def test_batched_robots_at_pi0_widths_match_oracle(cfg):
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(cfg.max_batch)
+    for steps in (1, 2):
+        got = ex.denoise(noise, steps)
+        ref = case.oracle_denoise(noise, steps)
+        for r in range(cfg.max_batch):
+            err = rel_err(got[r], ref[r])
+            print(f"{cfg.name} steps={steps} robot {r} rel_err={err:.3e}")
+            assert err <= tol_for(cfg), (steps, r, err)
+    ex.close()
