@@ -771,16 +771,30 @@ struct TileCfg {
   static constexpr int NA = NT * CK, NB = MT * CK;                 // fragments per chunk
   static constexpr int LOADS = (NA + NB) / GW;                     // 16-byte loads per thread
   static constexpr size_t CHUNK = (size_t)(NA + NB) * 1024;
-  // operand double buffer; with WK > 1 it then holds the 8 waves' partial sub-tiles (16 KB each)
-  static constexpr size_t STAGE = WK > 1 && 2 * CHUNK < (size_t)GW * 16384 ? (size_t)GW * 16384 : 2 * CHUNK;
+  // shapes that share fragments between waves stage them in LDS; with bf16 weights NBUF chunk
+  // buffers are filled straight from global memory, NBUF - 1 chunks in flight
+  static constexpr bool SHARED = !(WN == 1 && WM == 1);
+  static constexpr int NBUF = !SHARED ? 2 : (int)((144 * 1024) / CHUNK) < 3 ? 3 : (int)((144 * 1024) / CHUNK);
+  // operand buffers; with WK > 1 they then hold the 8 waves' partial sub-tiles (16 KB each)
+  static constexpr size_t OPER = (size_t)NBUF * CHUNK > 2 * CHUNK ? (size_t)NBUF * CHUNK : 2 * CHUNK;
+  static constexpr size_t STAGE = WK > 1 && OPER < (size_t)GW * 16384 ? (size_t)GW * 16384 : OPER;
   static constexpr int GPT = GTHREADS / (MT * 16);                 // RMS partial groups per token
   static constexpr int NRD = 64 / GPT;                             // RMS partial loads per thread
   static constexpr size_t LDS = STAGE + (size_t)MT * 16 * 4 + GTHREADS * 4;
-  static_assert(NA % GW == 0 && NB % GW == 0 && 2 * CHUNK <= 128 * 1024, "chunk shape");
+  static_assert(NA % GW == 0 && NB % GW == 0 && 2 * CHUNK <= 128 * 1024 && LDS <= 160 * 1024, "chunk shape");
 };
 constexpr int TILED_MAX_GIN = 128;  // RMS partial groups the prologue reads (width <= 2048)
 template <int WT> struct TiledWReg { typedef i32x4 T; };   // one lane's share of a weight fragment
 template <> struct TiledWReg<WT_FP8> { typedef i32x2 T; };
+
+// Wait until at most N of this wave's vector memory operations are outstanding and its LDS
+// operations are done, then meet the workgroup. Loads return in order, so this waits for every
+// load but the N youngest, including loads that write LDS directly.
+template <int N>
+__device__ __forceinline__ void vm_wait_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 template <int EPI, int WN, int WM, int WK, int WT>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) void gemm_tiled_kernel(GemmArgs a) {
@@ -893,6 +907,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   };
   const int nc = KB / C::CK;
+  bf16x8 fa_d[4], fb_d[4], ga_d[4], gb_d[4];  // the LDS-staged forms' fragments of two chunks
   if constexpr (WN == 1 && WM == 1) {
     // one 64 x 64 tile per workgroup, one k-group per wave: no fragment is shared between waves,
     // so each wave loads its own straight into registers (three k-blocks in flight) and the loop
@@ -924,6 +939,65 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (c + 2 < nc) mm(a2, b2);
       ld(a2, b2, c + 5);
     }
+  } else if constexpr (WT == WT_BF16) {
+    // Operands go from global memory straight into LDS: one global_load_lds_dwordx4 of a wave writes
+    // a whole 1 KB fragment (lane l's 16 bytes at l * 16), so no register carries them and no LDS
+    // store is issued. Chunk c goes to buffer c % NBUF and D = NBUF - 1 chunks are in flight; a
+    // wave waits for its own loads of a chunk (vmcnt), and the barrier after that makes every
+    // wave's loads of it visible. Fragments of the next chunk are read into registers while the
+    // MFMAs of the current one run, as in the register-staged form below.
+    constexpr int NB_ = C::NBUF, D = NB_ - 1, LPC = C::LOADS;
+    const char* wb = (const char*)a.w;
+    const char* xb = (const char*)a.x;
+    auto dma = [&](int c) __attribute__((always_inline)) {
+      char* dst = stage + (size_t)(c % NB_) * C::CHUNK;
+#pragma unroll
+      for (int i = 0; i < LW; ++i) {
+        const int f = wave + GW * i;
+        const char* src = wb + (((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane) * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + (size_t)f * 1024),
+                                         16, 0, 0);
+      }
+#pragma unroll
+      for (int i = 0; i < LX; ++i) {
+        const int f = wave + GW * i;
+        const char* src = xb + (((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane) * 16;
+        __builtin_amdgcn_global_load_lds((const void*)src,
+                                         (__attribute__((address_space(3))) void*)(dst + (size_t)(C::NA + f) * 1024), 16, 0, 0);
+      }
+    };
+    // issue chunk `last` (when it exists) and wait until chunk last - D + 1 has landed everywhere: D - 1
+    // chunks of this wave's loads may stay in flight; with nothing issued, wait for all of them
+    auto issue_wait = [&](int last) __attribute__((always_inline)) {
+      if (last < nc) {
+        dma(last);
+        vm_wait_barrier<(D - 1) * LPC>();
+      } else {
+        vm_wait_barrier<0>();
+      }
+    };
+#pragma unroll
+    for (int c = 0; c < D - 1; ++c)
+      if (c < nc) dma(c);
+    rms_partial();           // its loads are the youngest: the compiler's wait for them waits for these too
+    issue_wait(D - 1);       // chunk 0 landed
+    rms_final();
+    rd(fa_d, fb_d, 0);
+    issue_wait(D);           // chunk 1 landed; every wave's reads of buffer 0 are done
+    // step c: chunk c's fragments in registers; read chunk c + 1's, MFMAs of chunk c, then chunk
+    // c + D + 1 into buffer c % NBUF (chunk c's, read before the last barrier)
+    auto dstep = [&](int c, const bf16x8 (&fc)[4], const bf16x8 (&gc)[4], bf16x8 (&fn)[4], bf16x8 (&gn)[4])
+                     __attribute__((always_inline)) {
+      rd(fn, gn, (c + 1) % NB_);
+      mm(fc, gc);
+      issue_wait(c + D + 1);
+    };
+    int c = 0;
+    for (; c + 2 <= nc; c += 2) {
+      dstep(c, fa_d, fb_d, ga_d, gb_d);
+      dstep(c + 1, ga_d, gb_d, fa_d, fb_d);
+    }
+    if (c < nc) dstep(c, fa_d, fb_d, ga_d, gb_d);
   } else {
   gload(w0, x0, 0);
   gload(w1, x1, min(1, nc - 1));
