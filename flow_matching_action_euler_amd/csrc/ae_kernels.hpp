@@ -206,6 +206,19 @@ struct GemmArgs {
   float* xio;            // denoise: x [M_pad][A] updated in place; verify: v out
   int A;
   float dt;              // > 0: x += dt * v; 0: store v
+  // EPI_OUT of a verification pass (vx non-null; FLASH article, section 03, parallel verification):
+  // the endpoints x + (1 - tau) v, their distances to the draft and the accepted length are formed here
+  const float* vx;       // [n_tau * H][A] the interpolated points the velocities are taken at
+  const float* draft;    // [H][A]
+  const float* taus;     // [n_tau] (sequence j of the pass is flow time taus[j])
+  const float* vparams;  // [0] = delta
+  float* vpart;          // [ceil(A / 16)][M_pad] per 16-dim tile: sums of squared endpoint errors
+  unsigned* vcount;      // arrival ticket, zero between launches
+  int v_epi;             // epilogues of the launch (output tile groups x token groups)
+  int gripper_dim;       // < 0: none
+  float* dist;           // [n_tau][H] distances
+  int* accept;           // accepted length
+  int* gswitch;          // 1 when the draft's gripper column changes sign between rows
   Prefetch pf;           // next kernel's operands to place in L2 (QKV and gate/up launches only)
   int tn_blocks, tm_blocks;  // token-tiled launches: channel and token panels of the output
   // time-modulated expert and QK-norm (null when off; 64-token kernel only)
@@ -311,6 +324,67 @@ constexpr size_t gemm_lds_size() {
   return need > 81 * 1024 ? need : 81 * 1024;
 }
 
+// End of a verification pass (FLASH article, section 03: a prefix of the draft is accepted while every
+// flow time reconstructs it within delta): each output-projection epilogue has stored, per 16-dim tile
+// and row, the sum of squared endpoint errors with write-through stores; it counts its arrival, and
+// the last one forms D[j][i] = sqrt(sum over tiles, in tile order), writes the distances, and takes the
+// accepted length (first row rejected at some flow time: D >= delta or NaN; H when none, 0 when the
+// draft's gripper column changes sign between two rows) and the switch flag with one ballot per wave.
+// Rows up to GTHREADS; n_tau * H <= M.
+__device__ __forceinline__ void verify_tail(const GemmArgs& a, unsigned* ticket, int* wsh) {
+  wait_mem();  // this workgroup's partial stores have been acknowledged
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *ticket = __hip_atomic_fetch_add(a.vcount, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (*ticket == (unsigned)a.v_epi - 1) __hip_atomic_store(a.vcount, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (*ticket != (unsigned)a.v_epi - 1) return;
+  const int H = a.H, n_tau = a.M / H, n_tiles = (a.A + 15) / 16, i = threadIdx.x;
+  const int lane = i & 63, wave = i >> 6;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(a.vpart);
+  const bool row = i < H;
+  const int gd = a.gripper_dim;
+  const bool g_row = gd >= 0 && i > 0 && row;
+  const float g_cur = a.draft[g_row ? (size_t)i * a.A + gd : 0], g_prev = a.draft[g_row ? (size_t)(i - 1) * a.A + gd : 0];
+  const float delta = a.vparams[0];
+  bool bad = false;
+  for (int j0 = 0; j0 < n_tau; j0 += 4) {
+    float s[4][4];  // [flow time][tile]: every load of the group in flight before the sums
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const bool in = row && j0 + q < n_tau && t < n_tiles;
+        s[q][t] = ld_coherent_buf(rp, in ? (unsigned)((t * a.M_pad + (j0 + q) * H + i) * 4) : 0u);
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (row && j0 + q < n_tau) {
+        float sum = s[q][0];
+        for (int t = 1; t < n_tiles; ++t) sum += s[q][t];
+        const float D = sqrtf(sum);
+        a.dist[(size_t)(j0 + q) * H + i] = D;
+        bad = bad || !(D < delta);
+      }
+  }
+  const unsigned long long mb = __ballot(row && bad), mf = __ballot(g_row && g_cur * g_prev < 0.f);
+  if (lane == 0) {
+    wsh[wave] = mb ? wave * 64 + (__ffsll((long long)mb) - 1) : H;
+    wsh[GW + wave] = mf != 0ull;
+  }
+  __syncthreads();
+  if (i == 0) {
+    int first = H, flip = 0;
+    for (int w = 0; w < GW; ++w) {
+      first = min(first, wsh[w]);
+      flip |= wsh[GW + w];
+    }
+    *a.accept = flip ? 0 : first;
+    *a.gswitch = flip;
+  }
+}
+
 // Y = X W^T over the workgroup's channel tiles [g*NT, g*NT+NT), k-split s and
 // token group z (64 rows), then the epilogue EPI. Block = 8 waves. In each
 // pass wave w owns KPW consecutive k-blocks: it issues its weight fragments
@@ -404,7 +478,8 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     // product for ssv (its register pair overlapped a load in flight), hence 32-bit offsets there.
     float ssv[8];
     const float* sp = has_ssp ? a.ssp_in + tok0 + (threadIdx.x & 63) : (const float*)a.w;
-    float pre0[2 * NT];  // EPI_RESID: h; EPI_OUT: x
+    float pre0[2 * NT];  // EPI_RESID: h; EPI_OUT: x (denoise), the interpolated point (verification)
+    float vom[2 * NT], vdr[2 * NT];  // verification: 1 - tau of the row's sequence, the draft's value
     float4 cs_pre[4];
     {
       typename F::A wa[NT][KPW];
@@ -423,7 +498,14 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         const int n = (int)((size_t)g * NT + (e >> 10)) * 16 + (e & 15);
         pre0[i] = 0.f;
         if constexpr (EPI == EPI_RESID) pre0[i] = a.h[(size_t)tok * a.N + n];
-        else if constexpr (EPI == EPI_OUT) pre0[i] = a.dt > 0.f ? a.xio[(size_t)tok * a.A + (n < a.A ? n : 0)] : 0.f;
+        else if constexpr (EPI == EPI_OUT) {
+          const bool ver = a.vx != nullptr;
+          const int nn = n < a.A ? n : 0;
+          const float* xs = a.dt > 0.f ? a.xio : ver ? a.vx : a.bias;
+          pre0[i] = xs[xs == a.bias ? 0 : (size_t)tok * a.A + nn];
+          vom[i] = 1.f - (ver ? a.taus : a.bias)[ver ? tok / a.H : 0];
+          vdr[i] = (ver ? a.draft : a.bias)[ver ? (size_t)(tok % a.H) * a.A + nn : 0];
+        }
       }
       if constexpr (EPI == EPI_QKV) {
         const int tok = min(tok0 + ((threadIdx.x >> 1) & (TOKG - 1)), a.M - 1);
@@ -692,11 +774,25 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
       } else {  // EPI_OUT: bias (gn) and x (pre0) were loaded before the MFMAs
         const int n = (int)tile * 16 + c;
-        if (valid && n < a.A) {
-          const float v = val + gn[i];
-          a.xio[(size_t)tok * a.A + n] = a.dt > 0.f ? pre0[i] + a.dt * v : v;
+        const float v = val + gn[i];
+        if (valid && n < a.A) a.xio[(size_t)tok * a.A + n] = a.dt > 0.f ? pre0[i] + a.dt * v : v;
+        if (a.vx) {  // the squared endpoint error summed over the tile's 16 dims (16 lanes), device-scope
+          float d2 = 0.f;
+          if (valid && n < a.A) {
+            const float d = pre0[i] + vom[i] * v - vdr[i];
+            d2 = d * d;
+          }
+          d2 += __shfl_xor(d2, 1, 16);
+          d2 += __shfl_xor(d2, 2, 16);
+          d2 += __shfl_xor(d2, 4, 16);
+          d2 += __shfl_xor(d2, 8, 16);
+          if (c == 0 && valid)
+            st4_coherent(make_rsrc(a.vpart), (unsigned)((tile * a.M_pad + tok) * 4), __float_as_uint(d2));
         }
       }
+    }
+    if constexpr (EPI == EPI_OUT) {
+      if (a.vx) verify_tail(a, ticket, (int*)red);
     }
     return false;
   };
@@ -1846,85 +1942,6 @@ __global__ void interp_kernel(const float* draft, const float* noise, const floa
     int j = e / (H * A), ia = e % (H * A);
     float tau = taus[j];
     x[e] = (1.f - tau) * noise[ia] + tau * draft[ia];
-  }
-}
-
-// The verification tail (FLASH article, section 03): endpoints a_j[i] = x_j[i] + (1 - tau_j) v_j[i] and
-// distances D[j][i] = ||a_j[i] - draft[i]||_2, one lane per action dim in a power-of-two lane group per
-// (j, i) and a shuffle reduction; then per row i "rejected" (D[j][i] >= delta or NaN at some tau) and
-// "gripper flips" (sign change from row i-1), each gathered with one ballot per wave: the accepted length
-// is the first rejected row (H when none), forced to 0 when any row flips. One workgroup of 1024 threads;
-// A <= 64, dynamic LDS n_tau * H floats.
-constexpr int VERIFY_THREADS = 1024;
-__global__ __launch_bounds__(VERIFY_THREADS) void verify_kernel(const float* x, const float* v, const float* draft,
-                                                                const float* taus, int n_tau, int H, int A,
-                                                                const float* params, int gripper_dim, float* dist_out,
-                                                                int* accept_out, int* switch_out) {
-  extern __shared__ float dsh[];  // [n_tau][H]
-  __shared__ int w_first[VERIFY_THREADS / 64], w_flip[VERIFY_THREADS / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int S = 1;
-  while (S < A) S <<= 1;
-  const int sub = lane & (S - 1), rows = n_tau * H, per_pass = VERIFY_THREADS / S;
-  // every global load of the kernel goes out first (one memory round trip): the gripper column of
-  // rows i and i-1 for thread i (rows up to 1024), delta, then VP passes of endpoint operands
-  const int gi = (int)threadIdx.x;
-  const bool g_row = gripper_dim >= 0 && gi > 0 && gi < H;
-  const float g_cur = g_row ? draft[(size_t)gi * A + gripper_dim] : 0.f;
-  const float g_prev = g_row ? draft[(size_t)(gi - 1) * A + gripper_dim] : 0.f;
-  const float delta = params[0];
-  constexpr int VP = 8;
-  for (int r00 = 0; r00 < rows; r00 += VP * per_pass) {
-    float xv[VP], vv[VP], dv[VP], om[VP];
-#pragma unroll
-    for (int p = 0; p < VP; ++p) {
-      const int r = r00 + p * per_pass + (int)threadIdx.x / S;
-      const bool in = r < rows && sub < A;
-      const int rc = in ? r : 0, j = rc / H, i = rc % H;
-      const size_t idx = (size_t)rc * A + (in ? sub : 0);
-      xv[p] = x[idx];
-      vv[p] = v[idx];
-      dv[p] = draft[(size_t)i * A + (in ? sub : 0)];
-      om[p] = 1.f - taus[j];
-    }
-#pragma unroll
-    for (int p = 0; p < VP; ++p) {
-      const int r = r00 + p * per_pass + (int)threadIdx.x / S;
-      float d2 = 0.f;
-      if (r < rows && sub < A) {
-        const float diff = xv[p] + om[p] * vv[p] - dv[p];
-        d2 = diff * diff;
-      }
-      for (int o = S >> 1; o > 0; o >>= 1) d2 += __shfl_xor(d2, o, 64);
-      if (r < rows && sub == 0) {
-        const float dd = sqrtf(d2);
-        dsh[r] = dd;
-        if (dist_out) dist_out[r] = dd;
-      }
-    }
-  }
-  __syncthreads();
-  // row i is rejected when some flow time has D >= delta (or D is NaN); rows up to 1024
-  bool bad = false;
-  if (gi < H)
-    for (int j = 0; j < n_tau; ++j) bad = bad || !(dsh[j * H + gi] < delta);
-  const unsigned long long mb = __ballot(bad), mf = __ballot(g_row && g_cur * g_prev < 0.f);
-  if (lane == 0) {
-    w_first[wave] = mb ? wave * 64 + (__ffsll((long long)mb) - 1) : H;
-    w_flip[wave] = mf != 0ull;
-  }
-  __syncthreads();
-  if (wave == 0) {  // the first rejected row and any flip over the 16 waves, by shuffles
-    int first = lane < VERIFY_THREADS / 64 ? w_first[lane] : H;
-    int flip = lane < VERIFY_THREADS / 64 ? w_flip[lane] : 0;
-    for (int o = 8; o > 0; o >>= 1) {
-      first = min(first, __shfl_xor(first, o, 64));
-      flip |= __shfl_xor(flip, o, 64);
-    }
-    if (lane == 0) {
-      *accept_out = flip ? 0 : first;
-      *switch_out = flip;
-    }
   }
 }
 

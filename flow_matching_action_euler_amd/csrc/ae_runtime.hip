@@ -164,6 +164,9 @@ struct ae_handle {
   float *draft = nullptr, *vnoise = nullptr, *taus = nullptr, *temb_tau = nullptr, *phi = nullptr, *hid = nullptr,
         *dist = nullptr, *params = nullptr;
   int *accept = nullptr, *gswitch = nullptr;
+  float* vpart = nullptr;       // [out tiles][Mp_max] the verification's squared endpoint errors per 16-dim tile
+  unsigned* vcount = nullptr;   // its arrival ticket (zero between launches)
+  bool verify_head = false;     // set while a verification pass is enqueued: the head forms its distances
   std::map<int, float*> temb_steps;  // steps -> [steps][width]
   // time-modulated expert (time_mode 1) and QK-norm
   std::vector<void*> w_mod;          // [6w][w] row-major per layer (weight dtype)
@@ -716,6 +719,11 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, h->sk.out, n_z).S;
     a.bias = sm ? sm->t->bout + (size_t)sm->k * nout : h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
+    if (h->verify_head) {  // the endpoints, distances and accepted length in the epilogue
+      a.H = H; a.vx = h->x; a.draft = h->draft; a.taus = h->taus; a.vparams = h->params;
+      a.vpart = h->vpart; a.vcount = h->vcount; a.v_epi = h->out_tiles * n_z; a.gripper_dim = c.gripper_dim;
+      a.dist = h->dist; a.accept = h->accept; a.gswitch = h->gswitch;
+    }
     LAUNCH_CHECK(h, "out_proj_euler", (void)Dispatch::gemm(h, R_OUT_PROJ, a, h->out_tiles, n_z, st));
   }
   return AE_OK;
@@ -997,12 +1005,10 @@ int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
                                                       h->draft, h->vnoise, h->taus, n_tau, H, A, h->x));
   int rc = enqueue_temb(h, h->taus, n_tau, h->temb_tau, st, tm);
   if (rc) return rc;
+  h->verify_head = true;  // the output projection forms the distances and the accepted length
   rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm);
-  if (rc) return rc;
-  LAUNCH_CHECK(h, "verify_accept", AE_LAUNCH(verify_kernel, dim3(1), dim3(VERIFY_THREADS), (size_t)n_tau * H * sizeof(float), st,
-                                                      h->x, h->vout, h->draft, h->taus, n_tau, H, A, h->params,
-                                                      c.gripper_dim, h->dist, h->accept, h->gswitch));
-  return AE_OK;
+  h->verify_head = false;
+  return rc;
 }
 
 // The draft model's pass: stage the image features (h->feat) as GEMM input rows, write their K/V
@@ -1265,8 +1271,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
   if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})
                         : attn_dispatch<AT_F32>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
-      set_all_gemm_attrs() != hipSuccess ||
-      hipFuncSetAttribute((const void*)verify_kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 64 * 256 * 4) != hipSuccess) {
+      set_all_gemm_attrs() != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
     return fail(nullptr, AE_ERR_HIP, m);
@@ -1434,6 +1439,8 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   TRY(dalloc_t(h, &h->params, 4));
   TRY(dalloc_t(h, &h->accept, 1));
   TRY(dalloc_t(h, &h->gswitch, 1));
+  TRY(dalloc_t(h, &h->vpart, (size_t)h->out_tiles * Mp));
+  TRY(dalloc_t(h, &h->vcount, 4));
   if (c.draft) {
     // the queries as the block's input rows (fixed: staged once), the feature buffers, and the RoPE
     // table of the feature positions 0..P-1
