@@ -1915,28 +1915,67 @@ __global__ void mod_gain_kernel(const float* gain, const float* scale, int scale
   if (i < w) g[(size_t)step * w + i] = gain[i] * (1.f + scale[(size_t)step * scale_stride + i]);
 }
 
+// y[it][n] = act(W[n] . x[it] + b[n]) for it < n_t; act: 0 none, 1 silu. One wave per output row n,
+// 4 consecutive inputs per lane per 256-input step (K is a multiple of 256), the weight row read once
+// for every 8 inputs x[it] (their dot products accumulate side by side), then one wave reduction each.
 template <int WT_>
 __global__ __launch_bounds__(256) void gemv_kernel(const void* w, const float* b, const float* x, int K, int N,
-                                                   int act, float* y) {
-  const int it = blockIdx.y;
+                                                   int act, float* y, int n_t) {
   const int n = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (n >= N) return;
-  float acc = 0.f;
-  for (int k = lane; k < K; k += 64) {
-    float wv = (WT_ == WT_BF16) ? bf16_to_f32(((const uint16_t*)w)[(size_t)n * K + k]) : ((const float*)w)[(size_t)n * K + k];
-    acc += wv * x[(size_t)it * K + k];
-  }
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) {
-    float v = acc + b[n];
-    if (act == 1) v = v / (1.f + expf(-v));
-    y[(size_t)it * N + n] = v;
+  for (int it0 = 0; it0 < n_t; it0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int k = lane * 4; k < K; k += 256) {
+      float wv[4];
+      if constexpr (WT_ == WT_BF16) {
+        const uint2 p = *(const uint2*)((const uint16_t*)w + (size_t)n * K + k);
+        wv[0] = bf16_to_f32((uint16_t)(p.x & 0xffffu));
+        wv[1] = bf16_to_f32((uint16_t)(p.x >> 16));
+        wv[2] = bf16_to_f32((uint16_t)(p.y & 0xffffu));
+        wv[3] = bf16_to_f32((uint16_t)(p.y >> 16));
+      } else {
+        const float4 p = *(const float4*)((const float*)w + (size_t)n * K + k);
+        wv[0] = p.x; wv[1] = p.y; wv[2] = p.z; wv[3] = p.w;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (it0 + j < n_t) {
+          const float4 xv = *(const float4*)(x + (size_t)(it0 + j) * K + k);
+          acc[j] += wv[0] * xv.x + wv[1] * xv.y + wv[2] * xv.z + wv[3] * xv.w;
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float v = acc[j];
+      for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+      if (lane == 0 && it0 + j < n_t) {
+        v += b[n];
+        if (act == 1) v = v / (1.f + expf(-v));
+        y[(size_t)(it0 + j) * N + n] = v;
+      }
+    }
   }
 }
 
-// x_j = (1 - tau_j) noise + tau_j draft into rows j*H + i.
-__global__ void interp_kernel(const float* draft, const float* noise, const float* taus, int n_tau, int H, int A, float* x) {
+// The start of a verification pass in one launch: rows y < n_tau of the grid write phi(tau_y) as
+// sinusoid_kernel does, row n_tau writes x_j = (1 - tau_j) noise + tau_j draft into rows j*H + i.
+__global__ void verify_start_kernel(const float* draft, const float* noise, const float* taus, int n_tau, int H, int A,
+                                    float* x, int width, float* phi) {
+  const int it = blockIdx.y;
+  if (it < n_tau) {
+    const int half = width / 2;
+    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < half; i += gridDim.x * blockDim.x) {
+      double frac = (half > 1) ? (double)i / (double)(half - 1) : 0.0;
+      double period = 4e-3 * pow(4.0 / 4e-3, frac);
+      double ang = 2.0 * 3.14159265358979323846 * (double)taus[it] / period;
+      phi[(size_t)it * width + i] = (float)sin(ang);
+      phi[(size_t)it * width + half + i] = (float)cos(ang);
+    }
+    return;
+  }
   const int total = n_tau * H * A;
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < total; e += gridDim.x * blockDim.x) {
     int j = e / (H * A), ia = e % (H * A);

@@ -730,17 +730,23 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
 }
 
 // temb for n_t times in device array t_dev -> out [n_t][width].
+// The time MLP over the n_t sinusoid rows in h->phi -> out [n_t][width].
+int enqueue_time_mlp(ae_handle* h, int n_t, float* out, hipStream_t st, Timer* tm) {
+  const int w = h->c.width;
+  if (h->at == AT_F32) {
+    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid, n_t));
+    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out, n_t));
+  } else {
+    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid, n_t));
+    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out, n_t));
+  }
+  return AE_OK;
+}
+
 int enqueue_temb(ae_handle* h, const float* t_dev, int n_t, float* out, hipStream_t st, Timer* tm) {
   const int w = h->c.width;
   LAUNCH_CHECK(h, "time_sinusoid", AE_LAUNCH(sinusoid_kernel, dim3(std::max(1, w / 2 / 256), n_t), dim3(256), 0, st, t_dev, w, h->phi));
-  if (h->at == AT_F32) {
-    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid));
-    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_F32>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out));
-  } else {
-    LAUNCH_CHECK(h, "time_mlp_in", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_in_w, h->time_in_b, h->phi, w, w, 1, h->hid));
-    LAUNCH_CHECK(h, "time_mlp_out", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(w / 4, n_t), dim3(256), 0, st, h->time_out_w, h->time_out_b, h->hid, w, w, 0, out));
-  }
-  return AE_OK;
+  return enqueue_time_mlp(h, n_t, out, st, tm);
 }
 
 // The modulation vectors of every (layer, step) of a `steps`-step denoise of a time-modulated
@@ -764,8 +770,8 @@ int build_mod_table(ae_handle* h, int steps, const float* temb) {
   const dim3 gw((w + 255) / 256, steps);
   for (int l = 0; l < L; ++l) {
     float* m = t.mod + (size_t)l * steps * 6 * w;
-    hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(6 * w / 4, steps), dim3(256), 0, st, h->w_mod[l], h->b_mod[l], temb, w,
-                       6 * w, 0, m);
+    hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(6 * w / 4), dim3(256), 0, st, h->w_mod[l], h->b_mod[l], temb, w,
+                       6 * w, 0, m, steps);
     hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln1[l], m, 6 * w, w, t.g1 + (size_t)l * steps * w);
     hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln2[l], m + 3 * w, 6 * w, w, t.g2 + (size_t)l * steps * w);
     hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->qkv_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->qkv_p[l],
@@ -773,8 +779,8 @@ int build_mod_table(ae_handle* h, int steps, const float* temb) {
     hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->gu_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->gu_p[l],
                        w / KBLK, m + 4 * w, 6 * w, nullptr, 0, t.bgu + (size_t)l * steps * ngu, (int)ngu);
   }
-  hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(2 * w / 4, steps), dim3(256), 0, st, h->final_mod_w, h->final_mod_b, temb,
-                     w, 2 * w, 0, t.fmod);
+  hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(2 * w / 4), dim3(256), 0, st, h->final_mod_w, h->final_mod_b, temb,
+                     w, 2 * w, 0, t.fmod, steps);
   hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->final_ln, t.fmod, 2 * w, w, t.gf);
   hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->out_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->action_out_p,
                      w / KBLK, t.fmod + w, 2 * w, h->action_out_b, c.action_dim, t.bout, (int)nout);
@@ -1001,9 +1007,11 @@ int enqueue_denoise(ae_handle* h, int batch, int steps, float* temb, hipStream_t
 int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
   const ae_config& c = h->c;
   const int H = c.horizon, A = c.action_dim;
-  LAUNCH_CHECK(h, "verify_interp", AE_LAUNCH(interp_kernel, dim3((n_tau * H * A + 255) / 256), dim3(256), 0, st,
-                                                      h->draft, h->vnoise, h->taus, n_tau, H, A, h->x));
-  int rc = enqueue_temb(h, h->taus, n_tau, h->temb_tau, st, tm);
+  // x_j and phi(tau_j) in one launch, then the time MLP
+  LAUNCH_CHECK(h, "verify_start", AE_LAUNCH(verify_start_kernel, dim3(std::max((n_tau * H * A + 255) / 256, std::max(1, c.width / 2 / 256)), n_tau + 1),
+                                             dim3(256), 0, st, h->draft, h->vnoise, h->taus, n_tau, H, A, h->x, c.width,
+                                             h->phi));
+  int rc = enqueue_time_mlp(h, n_tau, h->temb_tau, st, tm);
   if (rc) return rc;
   h->verify_head = true;  // the output projection forms the distances and the accepted length
   rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm);
