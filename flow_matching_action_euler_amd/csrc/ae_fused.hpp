@@ -14,8 +14,8 @@
 // Buffers. Every activation a phase polls lives in a per-layer block of an activation ring; two
 // rings alternate between consecutive launches, and each launch writes EXCH_EMPTY over the ring the
 // previous launch used (that launch has ended, the next one has not begun), spread over the
-// workgroups at the start of each layer. Attention split partials have one consumer, which empties
-// what it read. The residual h of a (16-channel tile, 16-token tile) never leaves the workgroup that
+// workgroups at the start of each layer. Attention split partials alternate the same way (two sets,
+// the other emptied in the same reset phases). The residual h of a (16-channel tile, 16-token tile) never leaves the workgroup that
 // owns it: in_proj, o_proj and down give the same workgroup the same tile, which keeps h in LDS.
 //
 // Work split (G workgroups; workgroup g runs on XCD g % 8). The token-split phases give the ntp
@@ -71,8 +71,10 @@ struct FusedArgs {
   const float* rope_cs;  // [H][dh/2][2] (cos, sin) at positions P + t
   int n_qt, nbp, nbs, n_split, n_att;  // attention: query tiles, prefix / suffix 32-key blocks, key splits, units
   float scale_log2;
-  float* part_o;         // [L][n_att][16][dh] split partials (EXCH_EMPTY between uses)
+  float* part_o;         // [L][n_att][16][dh] split partials of this launch (EXCH_EMPTY before it)
   float* part_ml;        // [L][n_att][16][2]
+  float* part_o_other;   // the partials of the previous launch, emptied here (as the other ring)
+  float* part_ml_other;
   char* ring;            // this launch's activation ring: (L + 1) blocks of layer_bytes
   char* ring_other;      // the ring of the previous launch, emptied here
   unsigned layer_bytes;
@@ -408,13 +410,28 @@ struct FusedStep {
     return *lds_abort == 0;
   }
 
-  // EXCH_EMPTY over this workgroup's share of block l of the other launch's ring (plain stores: the
-  // other launch's polls read memory after this launch has ended)
+  // EXCH_EMPTY over this workgroup's share of block l of the other launch's ring and of layer l of the
+  // other launch's attention partials (plain stores: the other launch's polls read memory after this
+  // launch has ended)
   __device__ void reset_other(int l) {
-    const unsigned n16 = a.layer_bytes / 16, per = (n16 + a.G - 1) / a.G;
-    uint4* dst = (uint4*)(a.ring_other + (size_t)l * a.layer_bytes);
-    const unsigned e0 = blockIdx.x * per, e1 = min(e0 + per, n16);
-    for (unsigned e = e0 + tid; e < e1; e += FT) dst[e] = make_uint4(EXCH_EMPTY, EXCH_EMPTY, EXCH_EMPTY, EXCH_EMPTY);
+    const uint4 e4 = make_uint4(EXCH_EMPTY, EXCH_EMPTY, EXCH_EMPTY, EXCH_EMPTY);
+    {
+      const unsigned n16 = a.layer_bytes / 16, per = (n16 + a.G - 1) / a.G;
+      uint4* dst = (uint4*)(a.ring_other + (size_t)l * a.layer_bytes);
+      const unsigned e0 = blockIdx.x * per, e1 = min(e0 + per, n16);
+      for (unsigned e = e0 + tid; e < e1; e += FT) dst[e] = e4;
+    }
+    if (l < a.L) {
+      const size_t rows = (size_t)a.n_att * ATT_ROWS;
+      const unsigned n16 = (unsigned)(rows * a.dh / 4), per = (n16 + a.G - 1) / a.G;
+      uint4* dst = (uint4*)(a.part_o_other + (size_t)l * rows * a.dh);
+      const unsigned e0 = blockIdx.x * per, e1 = min(e0 + per, n16);
+      for (unsigned e = e0 + tid; e < e1; e += FT) dst[e] = e4;
+      const unsigned m16 = (unsigned)(rows * 2 / 4), mper = (m16 + a.G - 1) / a.G;  // (m, l) pairs, 16 bytes = 2 rows
+      uint4* mdst = (uint4*)(a.part_ml_other + (size_t)l * rows * 2);
+      const unsigned m0 = blockIdx.x * mper, m1 = min(m0 + mper, m16);
+      for (unsigned e = m0 + tid; e < m1; e += FT) mdst[e] = e4;
+    }
   }
 
   // ---- in_proj: h = x W_in^T + b_in + temb for (tile, token tile); h stays in the slot
@@ -744,8 +761,8 @@ struct FusedStep {
     return true;
   }
 
-  // Merge of one unit's share of its query tile (rows split * rps .. + rps) from every split's partial,
-  // which it empties; o in fragment order (act_idx), four dims per 8-byte store.
+  // Merge of one unit's share of its query tile (rows split * rps .. + rps) from every split's partial;
+  // o in fragment order (act_idx), four dims per 8-byte store.
   __device__ bool merge_unit(int l, int u) {
     const int upsp = a.n_qt * a.nkv;
     const int split = u / upsp, rest = u % upsp, qt = rest / a.nkv, g = rest % a.nkv;
@@ -813,14 +830,8 @@ struct FusedStep {
         const uint2 o = make_uint2(pack_bf16x2(O2[0] * inv, O2[1] * inv), pack_bf16x2(O2[2] * inv, O2[3] * inv));
         st8_coherent(rr, blk(l) + a.off_o + (unsigned)(act_idx(tok, col, a.ntt) * 2), o);
       }
-      // the partials read go back to the empty pattern after o is out (o_proj waits for o; the partials
-      // of layer l are next used by the next launch)
-      if (act)
-        for (int c = 0; c < a.n_split; ++c) {
-          const size_t prow = ((size_t)l * a.n_att + (size_t)c * upsp + rest) * ATT_ROWS + rr2;
-          st16_empty(ro, (unsigned)((prow * DH + kc * 4) * 4));
-          if (kc == 0) __builtin_amdgcn_raw_buffer_store_b64(i32x2{-1, -1}, rm, (unsigned)(prow * 8), 0, 0x10);
-        }
+      // the partials read stay as they are: the next launch (which uses the other partial buffers)
+      // writes the empty pattern over them
     }
     return settle(ok);
   }

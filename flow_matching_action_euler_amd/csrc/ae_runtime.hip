@@ -894,8 +894,9 @@ int setup_fused(ae_handle* h) {
     const int rc = dalloc(h, (void**)&h->ring[r], (size_t)(L + 1) * off);
     if (rc) return rc;
   }
-  h->fpart_o_floats = (size_t)L * h->f_natt * ATT_ROWS * dh;
-  h->fpart_ml_floats = (size_t)L * h->f_natt * ATT_ROWS * 2;
+  // two sets of attention partials, used by alternating launches as the rings are
+  h->fpart_o_floats = 2 * (size_t)L * h->f_natt * ATT_ROWS * dh;
+  h->fpart_ml_floats = 2 * (size_t)L * h->f_natt * ATT_ROWS * 2;
   int rc = dalloc_t(h, &h->fpart_o, h->fpart_o_floats);
   if (!rc) rc = dalloc_t(h, &h->fpart_ml, h->fpart_ml_floats);
   if (!rc) rc = dalloc_t(h, &h->abort_dev, 1);
@@ -977,11 +978,19 @@ int enqueue_fused(ae_handle* h, int steps, const float* temb, hipStream_t st, Ti
     }
     fa.ring = h->ring[k & 1];
     fa.ring_other = h->ring[(k + 1) & 1];
+    fa.part_o = h->fpart_o + (k & 1) * (h->fpart_o_floats / 2);
+    fa.part_ml = h->fpart_ml + (k & 1) * (h->fpart_ml_floats / 2);
+    fa.part_o_other = h->fpart_o + ((k + 1) & 1) * (h->fpart_o_floats / 2);
+    fa.part_ml_other = h->fpart_ml + ((k + 1) & 1) * (h->fpart_ml_floats / 2);
     LAUNCH_CHECK(h, "fused_step", AE_LAUNCH(h->fused_fn, dim3(h->n_cu), dim3(FT), h->fused_lds, st, fa));
   }
-  if (steps & 1) {
+  if (steps & 1) {  // the last launch used ring 0 and partial set 0: the next call starts on them
     const size_t n16 = (size_t)(c.n_layers + 1) * h->layer_bytes / 16;
     LAUNCH_CHECK(h, "fill_empty", AE_LAUNCH(fill_empty_kernel, dim3(1024), dim3(256), 0, st, (uint4*)h->ring[0], n16));
+    LAUNCH_CHECK(h, "fill_empty", AE_LAUNCH(fill_empty_kernel, dim3(1024), dim3(256), 0, st, (uint4*)h->fpart_o,
+                                            h->fpart_o_floats / 2 / 4));
+    LAUNCH_CHECK(h, "fill_empty", AE_LAUNCH(fill_empty_kernel, dim3(1024), dim3(256), 0, st, (uint4*)h->fpart_ml,
+                                            h->fpart_ml_floats / 2 / 4));
   }
   return AE_OK;
 }
