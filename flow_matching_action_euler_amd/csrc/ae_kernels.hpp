@@ -1375,8 +1375,14 @@ constexpr size_t attn_lds_size() {  // per-wave O and (m, l), the query tile (fp
 // the next block as soon as its S^T is done, its V fragments as soon as its
 // O^T is done. The waves merge (m, l, O) in LDS; with one split the workgroup
 // writes o, with several it stores its partial for attn_merge.
-template <int AT, int DH, int ATT_IT, int NW, bool QKN = false>
+// TPW = 2 (bf16, one split, no QK-norm): the workgroup takes query tiles 2y and 2y + 1 of its
+// sequence, 4 waves each; the waves of the two tiles walk the same key blocks in the same order, so
+// the second reader of each K/V fragment finds it in the compute unit's L1 and a sequence's K/V
+// crosses from L2 once per pair of tiles (and the launch is one round of half as many workgroups).
+template <int AT, int DH, int ATT_IT, int NW, bool QKN = false, int TPW = 1>
 __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
+  static_assert(TPW == 1 || (TPW == 2 && !QKN && AT == AT_BF16), "two query tiles: bf16 without QK-norm");
+  constexpr int NWT = NW / TPW;    // waves per query tile
   typedef typename Act<AT>::T XT;
   typedef Frag<WT_BF16, AT> F;
   constexpr int NKB = DH / KBLK;   // 32-dim blocks of a head
@@ -1402,7 +1408,8 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   const int s = zz / a.n_kv, g = zz % a.n_kv;
   const int gq = a.n_q / a.n_kv;
   const int R = gq * a.H;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;  // wave: scalar
+  const int qt0 = qt * TPW, tq = wave / NWT, wv = wave % NWT;  // this wave's tile qt0 + tq
   const int slot = a.seq_slot ? a.seq_slot[s] : a.slot0 + s;
   const int nb = a.nbp + a.nbs;
   const int bps = (nb + a.n_split - 1) / a.n_split;         // blocks per split
@@ -1423,18 +1430,21 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
       n_valid = min(ATT_KB, a.H - (b - a.nbp) * ATT_KB);
     }
   };
-  const XT* qf = (const XT*)a.q + (((size_t)s * a.n_kv + g) * a.n_qt + qt) * NKB * FR;
+  const XT* qf = (const XT*)a.q + (((size_t)s * a.n_kv + g) * a.n_qt) * NKB * FR;  // the sequence's first tile
 
-  // the query tile goes to LDS once (it is the same for every wave and block): its loads are
-  // issued first, the LDS stores wait only for them while the K/V loads below stay in flight
+  // the query tile(s) go to LDS once (the same for every wave and block): their loads are issued
+  // first, the LDS stores wait only for them while the K/V loads below stay in flight; a second
+  // tile past the sequence's last one reads the last one (its rows are never stored)
   constexpr int QVEC = 16 / sizeof(XT);  // elements per 16-byte vector
-  constexpr int QNV = NKB * FR / QVEC;
+  constexpr int QNV1 = NKB * FR / QVEC, QNV = TPW * QNV1;
   constexpr int QIT = (QNV + NW * 64 - 1) / (NW * 64);
+  static_assert((size_t)QNV * 16 <= (size_t)ATT_ROWS * DH * 4, "query tiles fit their LDS region");
   i32x4 qtmp[QIT];
 #pragma unroll
   for (int i = 0; i < QIT; ++i) {
     const int e = threadIdx.x + NW * 64 * i;
-    qtmp[i] = e < QNV ? *(const i32x4*)(qf + e * QVEC) : i32x4{0, 0, 0, 0};
+    const int tile = min(qt0 + e / QNV1, a.n_qt - 1);
+    qtmp[i] = e < QNV ? *(const i32x4*)(qf + (size_t)tile * NKB * FR + (e % QNV1) * QVEC) : i32x4{0, 0, 0, 0};
   }
   __builtin_amdgcn_sched_barrier(0);
   // this wave's blocks: b_begin + wave + NW it for it < ATT_IT (the runtime keeps a split within
@@ -1445,7 +1455,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   int nvs[ATT_IT];
 #pragma unroll
   for (int it = 0; it < ATT_IT; ++it) {
-    const int bb = b_begin + wave + NW * it;
+    const int bb = b_begin + wv + NWT * it;
     block_src(bb < b_end ? bb : b_begin, kfs[it], vfs[it], nvs[it]);
     if (bb >= b_end) nvs[it] = 0;
   }
@@ -1500,7 +1510,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const typename F::B qb = F::load_b(Qs + kb * FR + lane * 8);
+      const typename F::B qb = F::load_b(Qs + (tq * NKB + kb) * FR + lane * 8);
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) sacc[kt] = F::mma(ka[kt][kb], qb, sacc[kt]);
     }
@@ -1516,7 +1526,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     const int n_valid = nvs[it];
     float mb = -INFINITY;
     // QK-norm: a suffix block's keys carry 1/rms of their own (prefix keys come normalised)
-    const int bb_it = b_begin + wave + NW * it, sk0 = (bb_it - a.nbp) * ATT_KB + k8;
+    const int bb_it = b_begin + wv + NWT * it, sk0 = (bb_it - a.nbp) * ATT_KB + k8;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -1574,8 +1584,35 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
   // 1 KB rows of the wave partials, so the LDS reads have no bank conflicts
   constexpr int CPR = DH / 4;                              // 16-byte chunks per row
   constexpr int NTH = NW * 64;
-  constexpr int PPT = (ATT_ROWS * CPR + NTH - 1) / NTH;    // pairs per thread
+  constexpr int PPT = (TPW * ATT_ROWS * CPR + NTH - 1) / NTH;  // pairs per thread
   const int c4 = threadIdx.x % CPR;                        // same chunk for every pair of a thread
+  if constexpr (TPW > 1) {
+    // two tiles, one split: each pair merged from its tile's waves and stored at once
+#pragma unroll
+    for (int i = 0; i < PPT; ++i) {
+      const int q = threadIdx.x + NTH * i;
+      const int row2 = q / CPR, row = row2 % ATT_ROWS, w0 = (row2 / ATT_ROWS) * NWT;
+      const int tile = qt0 + row2 / ATT_ROWS, r = tile * ATT_ROWS + row;
+      if (q >= TPW * ATT_ROWS * CPR || tile >= a.n_qt || r >= R) continue;
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NWT; ++w) M = fmaxf(M, MLw[((w0 + w) * ATT_ROWS + row) * 2]);
+      float L = 0.f;
+      f32x4 O = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int w = 0; w < NWT; ++w) {
+        const float mw = MLw[((w0 + w) * ATT_ROWS + row) * 2];
+        const float wt = (mw == -INFINITY) ? 0.f : exp2f(mw - M);
+        L += wt * MLw[((w0 + w) * ATT_ROWS + row) * 2 + 1];
+        O += wt * *(const f32x4*)(Ow + ((size_t)(w0 + w) * ATT_ROWS + row) * LDO + 4 * c4);
+      }
+      const int tok = s * a.H + r % a.H, col = (g * gq + r / a.H) * DH + 4 * c4;
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Act<AT>::st((XT*)a.o, act_idx(tok, col + j, a.ntt), O[j] * inv);
+    }
+    return;
+  }
   float Mq[PPT], Lq[PPT];
   f32x4 Oq[PPT];
 #pragma unroll

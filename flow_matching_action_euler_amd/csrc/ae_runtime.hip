@@ -423,6 +423,27 @@ hipError_t attn_dispatch(int dh, bool set_attr, int split_it, dim3 grid, hipStre
                   : attn_dispatch_it<AT, ATT_IT_WHOLE, ATT_WAVES_WHOLE>(dh, false, grid, st, aa);
 }
 
+// Two query tiles per workgroup (bf16, one split, no QK-norm): 4 waves per tile x up to 7 blocks each
+// (896 keys; more blocks per wave spill registers at head_dim 256).
+constexpr int ATT_IT_PAIR = 7;
+template <int DH>
+hipError_t attn_pair_k(bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  constexpr size_t lds = attn_lds_size<DH, ATT_WAVES_WHOLE, false>();
+  if (set_attr)
+    return hipFuncSetAttribute((const void*)attn_kernel<AT_BF16, DH, ATT_IT_PAIR, ATT_WAVES_WHOLE, false, 2>,
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  AE_LAUNCH((attn_kernel<AT_BF16, DH, ATT_IT_PAIR, ATT_WAVES_WHOLE, false, 2>), grid, dim3(ATT_WAVES_WHOLE * 64), lds, st, aa);
+  return hipGetLastError();
+}
+hipError_t attn_pair_dispatch(int dh, bool set_attr, dim3 grid, hipStream_t st, const AttnArgs& aa) {
+  switch (dh) {
+    case 32: return attn_pair_k<32>(set_attr, grid, st, aa);
+    case 64: return attn_pair_k<64>(set_attr, grid, st, aa);
+    case 128: return attn_pair_k<128>(set_attr, grid, st, aa);
+    default: return attn_pair_k<256>(set_attr, grid, st, aa);
+  }
+}
+
 template <int AT>
 hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs& aa) {
   switch (dh) {
@@ -440,6 +461,7 @@ hipError_t attn_merge_dispatch(int dh, dim3 grid, hipStream_t st, const AttnArgs
 // longer contexts fall back to attn_merge.
 struct AttnPlan {
   int n_split, split_it, coresident;  // split_it: blocks per wave of a split plan (0: whole tile)
+  int pair;                           // whole tile, two query tiles per workgroup
 };
 AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   const int nb = h->nbp + h->nbs, zz = n_seq * h->c.n_kv_heads;
@@ -449,8 +471,12 @@ AttnPlan attn_plan(const ae_handle* h, int n_seq) {
   // several sequences (verification): splits of 2 blocks per wave, if those fit on the device at once
   const int nm = attn_splits(nb, ATT_IT_MID, ATT_WAVES_SPLIT);
   if (may_wait && nm >= 2 && nm <= 16 && nm * h->n_qt * zz <= h->n_cu)
-    return {nm, ATT_IT_MID, 1};
-  return {attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE), 0, 0};
+    return {nm, ATT_IT_MID, 1, 0};
+  const int nw = attn_splits(nb, ATT_IT_WHOLE, ATT_WAVES_WHOLE);
+  // many sequences (a launch of more than one round): two query tiles per workgroup share each K/V load
+  const bool pair = nw == 1 && h->at == AT_BF16 && !h->c.qk_norm && nb <= ATT_IT_PAIR * ATT_WAVES_WHOLE / 2 &&
+                    h->n_qt * zz > h->n_cu;
+  return {nw, 0, 0, pair ? 1 : 0};
 }
 
 // Steps of ~0.2 us that a split-K consumer sleeps before its first poll, so that the poll
@@ -652,9 +678,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     }
     // --- attention over [prefix ; suffix]
     aa.layer_off = (size_t)l * nkv * h->nbp * ATT_KB * dh;
-    const dim3 attn_grid(aa.n_split, aa.n_qt, n_seq * nkv);
+    const dim3 attn_grid(aa.n_split, plan.pair ? (aa.n_qt + 1) / 2 : aa.n_qt, n_seq * nkv);
     LAUNCH_CHECK(h, "attn", {
-      if (h->at == AT_BF16) (void)attn_dispatch<AT_BF16>(dh, false, plan.split_it, attn_grid, st, aa);
+      if (plan.pair) (void)attn_pair_dispatch(dh, false, attn_grid, st, aa);
+      else if (h->at == AT_BF16) (void)attn_dispatch<AT_BF16>(dh, false, plan.split_it, attn_grid, st, aa);
       else (void)attn_dispatch<AT_F32>(dh, false, plan.split_it, attn_grid, st, aa);
     });
     if (aa.n_split > 1 && !aa.coresident) {
@@ -1288,6 +1315,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
   h->mt = c.mlp_dtype == AE_F32 ? WT_F32 : c.mlp_dtype == AE_BF16 ? WT_BF16 : WT_FP8;
   if ((h->at == AT_BF16 ? attn_dispatch<AT_BF16>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})
                         : attn_dispatch<AT_F32>(cfg->head_dim, true, false, dim3(), nullptr, AttnArgs{})) != hipSuccess ||
+      (h->at == AT_BF16 && attn_pair_dispatch(cfg->head_dim, true, dim3(), nullptr, AttnArgs{}) != hipSuccess) ||
       set_all_gemm_attrs() != hipSuccess) {
     std::string m = "hipFuncSetAttribute failed";
     ae_destroy(h);
