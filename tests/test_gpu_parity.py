@@ -619,3 +619,25 @@ def test_batched_robots_at_pi0_widths_match_oracle(cfg):
             print(f"{cfg.name} steps={steps} robot {r} rel_err={err:.3e}")
             assert err <= tol_for(cfg), (steps, r, err)
     ex.close()
+
+
+# Many robots at the Pi0 widths: more query tiles than compute units, so the attention takes two query
+# tiles per workgroup. 32 robots x 17 rows: 9 query tiles per robot (odd: the last workgroup of each
+# robot has one tile); 40 robots x 16 rows with an 850-key prefix: 8 tiles, 28 key blocks (the most the
+# two-tile workgroup walks)
+PAIRS = [C.PI0.with_(name="pi0w_h17_b32", n_layers=2, horizon=17, prefix_len=100, max_batch=32, batch=32, steps=2),
+         C.PI0.with_(name="pi0w_h16_p850_b40", n_layers=2, horizon=16, prefix_len=850, max_batch=40, batch=40,
+                     steps=2)]
+
+
+@pytest.mark.parametrize("cfg", PAIRS, ids=lambda c: c.name)
+def test_two_tile_attention_matches_oracle(cfg):
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(cfg.max_batch)
+    got = ex.denoise(noise, 2)
+    ref = case.oracle_denoise(noise, 2)
+    errs = [rel_err(got[r], ref[r]) for r in range(cfg.max_batch)]
+    print(f"{cfg.name} worst robot rel_err={max(errs):.3e}")
+    assert max(errs) <= tol_for(cfg), errs
+    ex.close()
