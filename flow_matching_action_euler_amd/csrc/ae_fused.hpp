@@ -139,20 +139,32 @@ __device__ __forceinline__ void fused_give_up(const FusedArgs& a) {
 // them in registers). False when the wait gave up or another workgroup's did.
 // While the data is far from ready only the first piece of each lane is polled (1 KB per wave instead of
 // the whole operand set), so that waiting workgroups do not crowd the fabric the producers need.
+// With lead (an LDS word; every wave of the workgroup calls together), only wave 0 polls its first
+// piece while the others wait at a barrier: an eighth of the polling traffic.
 template <int N, class Off, class Need>
-__device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t r, Off off, Need need, i32x4 (&v)[N], const FusedArgs& a) {
+__device__ __forceinline__ bool poll16(__amdgpu_buffer_rsrc_t r, Off off, Need need, i32x4 (&v)[N], const FusedArgs& a,
+                                       int* lead = nullptr) {
   const unsigned long long t_end = wall_clock64() + a.wait_ticks;
   if constexpr (N > 1) {
-    for (;;) {
+    const bool poll_first = !lead || __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+    bool first_ok = true;
+    if (poll_first) for (;;) {
       const i32x4 w0 = __builtin_amdgcn_raw_buffer_load_b128(r, off(0), 0, 0x10);
       const unsigned ab = __hip_atomic_load(a.abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       if (__all(!need(0) || !is_empty4(w0))) break;
       if (ab != 0u || wall_clock64() > t_end) {
         if (ab == 0u) fused_give_up(a);
-        return false;
+        first_ok = false;
+        break;
       }
       __builtin_amdgcn_s_sleep(1);
     }
+    if (lead) {
+      if (poll_first && (threadIdx.x & 63) == 0) *lead = first_ok ? 0 : 1;
+      lds_barrier();
+      first_ok = *lead == 0;
+    }
+    if (!first_ok) return false;
   }
   for (;;) {
 #pragma unroll
@@ -242,7 +254,7 @@ template <int WT, int KBW, int NT, int TT, bool RMS = false>
 __device__ __forceinline__ bool unit_mma(int tid, const FusedArgs& a, const void* w, const int (&tile)[NT], int KB,
                                          __amdgpu_buffer_rsrc_t rr, unsigned x_off, const int (&tt)[TT], int M,
                                          f32x4 (&acc)[NT][TT], unsigned ssp_off = 0, float* ssq = nullptr,
-                                         float* inv_rms = nullptr) {
+                                         float* inv_rms = nullptr, int* lead = nullptr) {
   typedef typename FWReg<WT>::T WR;
   const int wave = tid >> 6, lane = tid & 63;
   const int kb0 = wave * KBW;
@@ -268,7 +280,7 @@ __device__ __forceinline__ bool unit_mma(int tid, const FusedArgs& a, const void
     return tt[j] >= 0 && tt[j] * 16 + (lane & 15) < M;
   };
   i32x4 xv[NX + (RMS ? 1 : 0)];
-  const bool ok = poll16<NX + (RMS ? 1 : 0)>(rr, off, need, xv, a);
+  const bool ok = poll16<NX + (RMS ? 1 : 0)>(rr, off, need, xv, a, lead);
   if constexpr (RMS) {
     // sum this wave's channel groups per 4-token quad (lanes q_rms, q_rms + QPG, ...), then the waves in LDS
     f32x4 r = __builtin_bit_cast(f32x4, xv[NX]);
@@ -403,6 +415,7 @@ struct FusedStep {
 
   __device__ unsigned blk(int l) const { return (unsigned)l * a.layer_bytes; }
 
+
   // A phase result: every thread of the workgroup leaves together when any wave's wait gave up.
   __device__ bool settle(bool ok) {
     if (!ok) *lds_abort = 1;
@@ -472,7 +485,7 @@ struct FusedStep {
       for (int t = 0; t < F_QKV_NT; ++t) tile[t] = t0 + t * ts.n_groups < n_tiles ? t0 + t * ts.n_groups : -1;
       f32x4 acc[F_QKV_NT][1];
       const bool ok = unit_mma<WT_BF16, KW, F_QKV_NT, 1, true>(tid, a, Ly.qkv, tile, a.w / 32, rr, blk(l), ttv, a.H, acc,
-                                                               blk(l) + a.off_ssp, ssq, inv_rms);
+                                                               blk(l) + a.off_ssp, ssq, inv_rms, lds_abort + 1);
       f32x4 accq[F_QKV_NT];
 #pragma unroll
       for (int t = 0; t < F_QKV_NT; ++t) accq[t] = acc[t][0];
@@ -846,7 +859,8 @@ struct FusedStep {
     for (int i = 0, tile = ts.gid; tile < a.w / 16 && i < F_SLOTS; ++i, tile += ts.n_groups) {
       const int tl[1] = {tile};
       f32x4 acc[1][1];
-      const bool ok = unit_mma<WT_BF16, KO, 1, 1>(tid, a, Ly.o, tl, a.nq * a.dh / 32, rr, blk(l) + a.off_o, ttv, a.H, acc);
+      const bool ok = unit_mma<WT_BF16, KO, 1, 1>(tid, a, Ly.o, tl, a.nq * a.dh / 32, rr, blk(l) + a.off_o, ttv, a.H, acc,
+                                                  0, nullptr, nullptr, lds_abort + 1);
       if (!settle(ok)) return false;
       const f32x4 accq[1] = {acc[0][0]};
       unit_reduce<1>(tid, accq, red, res);
@@ -881,7 +895,7 @@ struct FusedStep {
       const int tile[4] = {2 * p0, 2 * p0 + 1, p1 < n_pairs ? 2 * p1 : -1, p1 < n_pairs ? 2 * p1 + 1 : -1};
       f32x4 acc[4][2];
       const bool ok = unit_mma<MT, KW, 4, 2, true>(tid, a, Ly.gu, tile, a.w / 32, rr, blk(l) + a.off_hb2, ttv, a.H, acc,
-                                                   blk(l) + a.off_ssp2, ssq, inv_rms);
+                                                   blk(l) + a.off_ssp2, ssq, inv_rms, lds_abort + 1);
       if (!settle(ok)) return false;
       f32x4 accq[8];
 #pragma unroll
@@ -936,7 +950,8 @@ struct FusedStep {
     for (int i = 0, tile = ts.gid; tile < a.w / 16 && i < F_SLOTS; ++i, tile += ts.n_groups) {
       const int tl[1] = {tile};
       f32x4 acc[1][1];
-      const bool ok = unit_mma<MT, KF, 1, 1>(tid, a, Ly.d, tl, a.F / 32, rr, blk(l) + a.off_u, ttv, a.H, acc);
+      const bool ok = unit_mma<MT, KF, 1, 1>(tid, a, Ly.d, tl, a.F / 32, rr, blk(l) + a.off_u, ttv, a.H, acc, 0, nullptr,
+                                             nullptr, lds_abort + 1);
       if (!settle(ok)) return false;
       const f32x4 accq[1] = {acc[0][0]};
       unit_reduce<1>(tid, accq, red, res);
