@@ -226,6 +226,10 @@ struct GemmArgs {
   const float* res_gate;    // EPI_RESID: gate per output channel on the sublayer's output
   const float* qk_gain;     // EPI_QKV: QK-norm gain per packed q/k channel (applied before RoPE)
   float* qk_ssp;            // EPI_QKV: [q and k tiles][M_pad] sums of squares of the q/k channels of a tile
+  // modulation per sequence (a verification pass of a time-modulated expert: each flow time has its
+  // own vectors): row r takes sequence r / mod_rows's vectors, ms_* elements apart; 0: one set for all
+  int mod_rows;
+  size_t ms_gain, ms_shift, ms_gate, ms_bias;
 };
 
 constexpr int GW = 8;         // waves per GEMM workgroup
@@ -452,9 +456,10 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
     for (int i = 0; i < 2 * NT; ++i) {
       const int e = threadIdx.x + GTHREADS * i;
       const int n = (int)((size_t)g * NT + (e >> 10)) * 16 + (e & 15);
+      const int sq = a.mod_rows ? min(tok0 + ((e >> 4) & 63), a.M - 1) / a.mod_rows : 0;
       gn[i] = 0.f;
-      if constexpr (EPI == EPI_RESID) gn[i] = a.gain_next[n];
-      else if constexpr (EPI == EPI_OUT) gn[i] = a.bias[n < a.A ? n : 0];
+      if constexpr (EPI == EPI_RESID) gn[i] = a.gain_next[sq * a.ms_gain + n];
+      else if constexpr (EPI == EPI_OUT) gn[i] = a.bias[sq * a.ms_bias + (n < a.A ? n : 0)];
     }
     // fp8 weights: the per-row scale of each epilogue element, loaded now
     float psc[2 * NT];
@@ -680,8 +685,9 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
 #pragma unroll
           for (int c = 0; c < 16; ++c) xs[c] = rr[c] * ir;
           if (a.shift_bias) {
+            const float* sb = a.shift_bias + (a.mod_rows ? (size_t)(tok / a.mod_rows) * a.ms_shift : 0) + t_in * 16;
 #pragma unroll
-            for (int c = 0; c < 16; ++c) xs[c] += a.shift_bias[t_in * 16 + c];
+            for (int c = 0; c < 16; ++c) xs[c] += sb[c];
           }
           if (a.qk_gain) {  // QK-norm: this tile's share of the head's sum of squares, then the gains
             float sq2 = 0.f;
@@ -739,10 +745,11 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       if constexpr (EPI == EPI_GEGLU) {
         if (nt & 1) continue;
       }
+      const size_t msq = a.mod_rows ? (size_t)(min(tok, a.M - 1) / a.mod_rows) : 0;  // modulation set of this row
       float val = res[e] * inv_rms[tl];
       if constexpr (WT == WT_FP8) val *= psc[i];
       if constexpr (EPI == EPI_QKV || EPI == EPI_GEGLU)
-        if (a.shift_bias) val += a.shift_bias[tile * 16 + c];
+        if (a.shift_bias) val += a.shift_bias[msq * a.ms_shift + tile * 16 + c];
       if constexpr (EPI == EPI_QKV) {
         // v tiles only (q and k tiles took the vectorised path above): value A fragments (of V^T)
         // of block t/32: dims dt*16 + lane%16, keys (lane/16)*8 + e
@@ -756,7 +763,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
         const int n = (int)tile * 16 + c;
         float hn = 0.f;
         if (valid) {
-          hn = pre0[i] + (a.res_gate ? a.res_gate[n] * val : val);
+          hn = pre0[i] + (a.res_gate ? a.res_gate[msq * a.ms_gate + n] * val : val);
           a.h[(size_t)tok * a.N + n] = hn;
           Act<AT>::st((XT*)a.hb, act_idx(tok, n, a.M_pad / 16), hn * gn[i]);
         }
@@ -769,7 +776,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
       } else if constexpr (EPI == EPI_GEGLU) {
         float up = res[e + 1024] * inv_rms[tl];
         if constexpr (WT == WT_FP8) up *= psc[(i + 2) & (2 * NT - 1)];  // the up tile of this gate element
-        if (a.shift_bias) up += a.shift_bias[(tile + 1) * 16 + c];
+        if (a.shift_bias) up += a.shift_bias[msq * a.ms_shift + (tile + 1) * 16 + c];
         const int f = (int)(tile / 2) * 16 + c;
         if (valid) Act<AT>::st((XT*)a.u_out, act_idx(tok, f, a.M_pad / 16), gelu_tanh(val) * up);
       } else {  // EPI_OUT: bias (gn) and x (pre0) were loaded before the MFMAs
@@ -1346,6 +1353,9 @@ struct AttnArgs {
   // 1: workgroup i (on XCD i % 8) takes the i-th of a contiguous run of (sequence, query tile, split)
   // items per XCD, so the workgroups reading one sequence's K/V share one L2 (many sequences)
   int xcd_group;
+  // 1 (passes over several sequences): each workgroup first touches its share of its sequence's prefix
+  // K/V lines, one dword per 128-byte line, so that all of them are asked from HBM at once
+  int touch;
 };
 
 constexpr int ATT_ROWS = 16;   // query rows per workgroup
@@ -1431,6 +1441,25 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
   };
   const XT* qf = (const XT*)a.q + (((size_t)s * a.n_kv + g) * a.n_qt) * NKB * FR;  // the sequence's first tile
+
+  // Several sequences: the blocks below reach each wave one at a time (a block's loads go out once the
+  // previous block's are in), and the first reader of a line of the sequence's prefix waits out HBM
+  // latency for it, block after block. The workgroups of one (sequence, kv head) therefore touch its
+  // prefix K and V first, line by line (rank split + n_split * tile of n_split * tiles), so that every
+  // line is asked for at once and the chained loads find them in L2. The values are only consumed after
+  // the block loop (loads complete in order: the first block's wait covers them).
+  int tch[2] = {0, 0};
+  if (a.touch) {
+    const unsigned n_grp = gridDim.x * gridDim.y, rk = split + gridDim.x * qt;
+    const unsigned lines = (unsigned)((size_t)a.nbp * 2 * NKB * FR * sizeof(XT) / 128);  // of K (and of V)
+    const char* kb0 = (const char*)((const XT*)a.kcache + pre_base);
+    const char* vb0 = (const char*)((const XT*)a.vcache + pre_base);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const unsigned L = rk + n_grp * (threadIdx.x + NW * 64 * i);
+      if (L < 2 * lines) tch[i] = *(const int*)((L < lines ? kb0 : vb0) + (size_t)(L % lines) * 128);
+    }
+  }
 
   // the query tile(s) go to LDS once (the same for every wave and block): their loads are issued
   // first, the LDS stores wait only for them while the K/V loads below stay in flight; a second
@@ -1573,6 +1602,7 @@ __global__ __launch_bounds__(NW * 64) void attn_kernel(AttnArgs a) {
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  asm volatile("" ::"v"(tch[0] ^ tch[1]));  // the touches, long since in
   // this wave's (m, l, O) to LDS: O[row lane%16][dt*16 + 4*(lane/16) + v]
   float* ow = Ow + (size_t)wave * ATT_ROWS * LDO + (lane & 15) * LDO + 4 * (lane >> 4);
 #pragma unroll
@@ -1832,7 +1862,7 @@ template <int WT_IN, int AT>
 __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void* w_in, const float* b_in,
                                                       const float* temb, int temb_stride, int M, int M_pad,
                                                       int A, int H, int width, float* h, void* hb,
-                                                      const float* gain, float* ssp) {
+                                                      const float* gain, size_t gain_stride, float* ssp) {
   typedef typename Act<AT>::T XT;
   __shared__ float xs[16][65];
   __shared__ float ws[64][65];
@@ -1849,12 +1879,13 @@ __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void
     ws[r][k] = (WT_IN == WT_BF16) ? bf16_to_f32(((const uint16_t*)w_in)[idx]) : ((const float*)w_in)[idx];
   }
   const int nl = threadIdx.x & 63, n = n0 + nl;
-  const float bias = b_in[n], gn = gain[n];
-  float tv[4];
+  const float bias = b_in[n];
+  float tv[4], gn[4];  // per row: its sequence's temb and norm gain (gain_stride 0: one gain for all rows)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int tok = t0 + (threadIdx.x >> 6) * 4 + i;
     tv[i] = tok < M ? temb[(size_t)(tok / H) * temb_stride + n] : 0.f;
+    gn[i] = gain[(size_t)(min(tok, M - 1) / H) * gain_stride + n];
   }
   __syncthreads();
 #pragma unroll
@@ -1866,7 +1897,7 @@ __global__ __launch_bounds__(256) void in_proj_kernel(const float* x, const void
       acc = bias + tv[i];
       for (int k = 0; k < A; ++k) acc += xs[rl][k] * ws[nl][k];
       h[(size_t)tok * width + n] = acc;
-      Act<AT>::st((XT*)hb, act_idx(tok, n, M_pad / 16), acc * gn);
+      Act<AT>::st((XT*)hb, act_idx(tok, n, M_pad / 16), acc * gn[i]);
     }
     float sq = acc * acc;
     sq += __shfl_xor(sq, 1, 16);
@@ -2018,6 +2049,125 @@ __global__ void verify_start_kernel(const float* draft, const float* noise, cons
     int j = e / (H * A), ia = e % (H * A);
     float tau = taus[j];
     x[e] = (1.f - tau) * noise[ia] + tau * draft[ia];
+  }
+}
+
+// ------------------------------------------------------------------ modulation vectors of a verification pass
+// A time-modulated expert's verification pass (one flow time per sequence) forms every layer's
+// modulation vectors from the flow times' temb inside the pass, in three launches over job tables
+// built at create: the linear maps of temb, the modulated norm gains, and the shift biases W . shift.
+
+// y[it][n] = W[n] . x[it] + b[n] for it < n_t, job blockIdx.y, bf16 weights. One wave per 4 output rows
+// (grid.x = N / 16 for 4 waves): every 256-input step loads each input's 4 values once for the 4 rows
+// and each row's 4 weights once for 4 inputs (inputs 4 at a time), then one wave reduction per sum.
+struct GemvJob {
+  const uint16_t* w;
+  const float* b;
+  const float* x;
+  float* y;
+  int K, N;
+};
+__global__ __launch_bounds__(256) void gemv_jobs_kernel(const GemvJob* jobs, int n_t) {
+  const GemvJob jb = jobs[blockIdx.y];
+  const int n0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 4;
+  const int lane = threadIdx.x & 63;
+  if (n0 >= jb.N) return;
+  for (int it0 = 0; it0 < n_t; it0 += 4) {
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[r][j] = 0.f;
+    for (int k = lane * 4; k < jb.K; k += 256) {
+      float4 xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        xv[j] = it0 + j < n_t ? *(const float4*)(jb.x + (size_t)(it0 + j) * jb.K + k) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint2 p = *(const uint2*)(jb.w + (size_t)(n0 + r) * jb.K + k);
+        const float w0 = bf16_to_f32((uint16_t)(p.x & 0xffffu)), w1 = bf16_to_f32((uint16_t)(p.x >> 16));
+        const float w2 = bf16_to_f32((uint16_t)(p.y & 0xffffu)), w3 = bf16_to_f32((uint16_t)(p.y >> 16));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[r][j] += w0 * xv[j].x + w1 * xv[j].y + w2 * xv[j].z + w3 * xv[j].w;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float v = acc[r][j];
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+        if (lane == 0 && it0 + j < n_t) jb.y[(size_t)(it0 + j) * jb.N + n0 + r] = v + jb.b[n0 + r];
+      }
+  }
+}
+
+// g[it][i] = gain[i] (1 + scale[it][i]) for it < n_t, job blockIdx.z (grid (w / 256, n_t, jobs))
+struct GainJob {
+  const float* gain;
+  const float* scale;
+  float* g;
+  int scale_stride;
+};
+__global__ void mod_gain_jobs_kernel(const GainJob* jobs, int w) {
+  const GainJob jb = jobs[blockIdx.z];
+  const int it = blockIdx.y, i = blockIdx.x * 256 + threadIdx.x;
+  if (i < w) jb.g[(size_t)it * w + i] = jb.gain[i] * (1.f + jb.scale[(size_t)it * jb.scale_stride + i]);
+}
+
+// y[it][ch] = sum_k W(ch, k) x[it][k] (+ add[ch] for ch < n_add) over packed bf16 weights (the layout
+// packed_gemv_kernel reads) for it < n_t, job blockIdx.y, tile blockIdx.x: each 16-byte piece of the
+// tile is loaded once for all n_t inputs (8 at a time).
+struct PackedGemvJob {
+  const uint16_t* w;
+  const float* x;
+  const float* add;
+  float* y;
+  int KB, tiles, x_stride, y_stride, n_add;
+};
+__global__ __launch_bounds__(256) void packed_gemv_jobs_kernel(const PackedGemvJob* jobs, int n_t) {
+  __shared__ float part[16][8][17];
+  const PackedGemvJob jb = jobs[blockIdx.y];
+  const int tile = blockIdx.x, c = threadIdx.x & 15, grp = threadIdx.x >> 4;
+  if (tile >= jb.tiles) return;
+  for (int it0 = 0; it0 < n_t; it0 += 8) {
+    float acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
+    for (int kb = grp; kb < jb.KB; kb += 16)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 p = *(const uint4*)(jb.w + (((size_t)tile * jb.KB + kb) * 64 + q * 16 + c) * 8);
+        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+        float wv[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          wv[2 * e] = bf16_to_f32((uint16_t)(pw[e] & 0xffffu));
+          wv[2 * e + 1] = bf16_to_f32((uint16_t)(pw[e] >> 16));
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (it0 + j < n_t) {
+            const float* xs = jb.x + (size_t)(it0 + j) * jb.x_stride + kb * 32 + q * 8;
+            const float4 x0 = *(const float4*)xs, x1 = *(const float4*)(xs + 4);
+            acc[j] += wv[0] * x0.x + wv[1] * x0.y + wv[2] * x0.z + wv[3] * x0.w + wv[4] * x1.x + wv[5] * x1.y +
+                      wv[6] * x1.z + wv[7] * x1.w;
+          }
+      }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) part[grp][j][c] = acc[j];
+    __syncthreads();
+    if (threadIdx.x < 128) {
+      const int j = threadIdx.x >> 4, cc = threadIdx.x & 15;
+      if (it0 + j < n_t) {
+        float sum = 0.f;
+        for (int g = 0; g < 16; ++g) sum += part[g][j][cc];
+        const int ch = tile * 16 + cc;
+        jb.y[(size_t)(it0 + j) * jb.y_stride + ch] = sum + ((jb.add && ch < jb.n_add) ? jb.add[ch] : 0.f);
+      }
+    }
+    __syncthreads();
   }
 }
 

@@ -152,6 +152,7 @@ struct ae_handle {
   // in-kernel partial exchanges (read from AE_ATTN_CORESIDENT / AE_EXCH_POLL at creation, 0 = off):
   // attention key splits merged by co-resident workgroups, split-K partials polled by split S-1
   bool coresident_attn = true, poll_splitk = true;
+  int occ_attn = 0, occ_gemm = 0, occ_fused = 0;  // workgroups per CU of the kernels that may wait in-kernel
   int tiled_roles = 0xf;  // GEMM roles (bit per Role) that may take the token-tiled kernel
   int tiled_force = -1;   // token-tiled shape forced for every GEMM it fits (tests)
   bool attn_xcd = true;   // attention workgroups of one sequence grouped on one XCD (8+ sequences)
@@ -189,6 +190,11 @@ struct ae_handle {
     float *fmod = nullptr, *gf = nullptr, *bout = nullptr;  // [steps][2w], [steps][w], [steps][out tiles * 16]
   };
   std::map<int, ModTable> mod_steps;
+  ModTable mod_tau;  // time-modulated expert with max_taus > 0: the verification times' vectors, filled per pass
+  GemvJob* mt_gemv = nullptr;          // and the job tables that fill it: L + 1 linear maps of temb,
+  GainJob* mt_gain = nullptr;          // 2 L + 1 modulated gains,
+  PackedGemvJob* mt_shift = nullptr;   // 2 L + 1 shift biases
+  int mt_max_n = 0, mt_max_tiles = 0;
   std::map<std::tuple<int, int, int>, hipGraphExec_t> graphs;
   float last_ms = 0.f;
   hipEvent_t ev0 = nullptr, ev1 = nullptr, ev_round = nullptr;
@@ -370,6 +376,43 @@ hipError_t set_all_gemm_attrs() {
   acc(set_gemm_attr<WT_FP8, AT_BF16, R_GATE_UP>()); acc(set_gemm_attr<WT_FP8, AT_BF16, R_DOWN>());
   acc(set_tiled_attrs());
   return e;
+}
+
+// Workgroups of fn (threads each, lds bytes of dynamic LDS) one compute unit holds at once, from the
+// runtime's occupancy calculator (registers, LDS, waves); 0 when the query fails.
+int blocks_per_cu(const void* fn, int threads, size_t lds) {
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return nb;
+}
+// The kernels that may wait inside a launch for other workgroups of it assume every workgroup is
+// resident at once, one per compute unit (the runtime sizes their grids to at most the CU count):
+// the smallest occupancy among the split attention kernels of this head size ...
+template <int AT, int IT, bool QKN>
+int attn_split_occ_k(int dh) {
+  constexpr int NW = ATT_WAVES_SPLIT;
+  switch (dh) {
+    case 32: return blocks_per_cu((const void*)attn_kernel<AT, 32, IT, NW, QKN>, NW * 64, attn_lds_size<32, NW, QKN>());
+    case 64: return blocks_per_cu((const void*)attn_kernel<AT, 64, IT, NW, QKN>, NW * 64, attn_lds_size<64, NW, QKN>());
+    case 128: return blocks_per_cu((const void*)attn_kernel<AT, 128, IT, NW, QKN>, NW * 64, attn_lds_size<128, NW, QKN>());
+    default: return blocks_per_cu((const void*)attn_kernel<AT, 256, IT, NW, QKN>, NW * 64, attn_lds_size<256, NW, QKN>());
+  }
+}
+template <int AT, bool QKN>
+int attn_split_occ(int dh) { return std::min(attn_split_occ_k<AT, ATT_IT_SPLIT, QKN>(dh), attn_split_occ_k<AT, ATT_IT_MID, QKN>(dh)); }
+// ... and among the one-group GEMM kernels of a role (their split-K partials are polled in-kernel)
+template <int WT, int AT, int ROLE, int KPW>
+int gemm_occ_k() {
+  return blocks_per_cu((const void*)gemm_entry<ROLE, WT, AT, KPW, false>(), GTHREADS, gemm_lds_size<AT, RoleTraits<ROLE>::NT, KPW>());
+}
+template <int WT, int AT, int ROLE>
+int gemm_occ() {
+  int nb = std::min(gemm_occ_k<WT, AT, ROLE, 2>(), gemm_occ_k<WT, AT, ROLE, 1>());
+  if constexpr (AT == AT_BF16) nb = std::min(nb, gemm_occ_k<WT, AT, ROLE, 4>());
+  return nb;
 }
 
 // k-splits per GEMM phase (qkv, o, gate/up, down, out) for one token group (measured for Pi0:
@@ -599,9 +642,11 @@ constexpr int PREFETCH_DOWN_LEAD = 0;
 // One velocity pass over M = n_seq * H rows in h->x (temb per sequence from
 // temb[seq * temb_stride]); dt > 0 updates x in place, dt == 0 writes h->vout.
 // Step k of a `steps`-step denoise of a time-modulated expert: where its modulation vectors live
+// (per_seq: a verification pass, sequence j of the pass takes row j of the table; k = 0)
 struct StepMod {
   const ae_handle::ModTable* t;
   int k, steps;
+  bool per_seq = false;
 };
 
 int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride, const int* seq_slot, int slot0, float dt,
@@ -616,15 +661,16 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   const float* temb_in = sm ? h->zero_w : temb;  // a modulated expert adds no temb to the tokens
   const int temb_in_stride = sm ? 0 : temb_stride;
   const float* g_first = sm ? modp(sm->t->g1, w, 0) : h->ln1[0];
+  const bool mseq = sm && sm->per_seq;  // each sequence its own modulation vectors, one table row apart
 
   // from_h: the block input rows are already in h / hb / ssp_a (the draft model's queries)
   if (!from_h) LAUNCH_CHECK(h, "in_proj", {
     if (h->at == AT_F32)
       AE_LAUNCH((in_proj_kernel<WT_F32, AT_F32>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, h->ssp_a);
+                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, mseq ? (size_t)w : 0, h->ssp_a);
     else
       AE_LAUNCH((in_proj_kernel<WT_BF16, AT_BF16>), dim3(w / 64, Mp / 16), dim3(256), 0, st, h->x, h->action_in_w,
-                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, h->ssp_a);
+                         h->action_in_b, temb_in, temb_in_stride, M, Mp, A, H, w, h->h, h->hb, g_first, mseq ? (size_t)w : 0, h->ssp_a);
   });
 
   const int gq = nq / nkv, R = gq * H;
@@ -640,6 +686,10 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
   aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && h->attn_xcd;
+#ifndef ATT_TOUCH
+#define ATT_TOUCH 1
+#endif
+  aa.touch = ATT_TOUCH && n_seq >= 2;
   aa.err = h->flag_dev;
   aa.wait = h->wait_ticks;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
@@ -653,6 +703,9 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     GemmArgs g{};
     g.inv_width = 1.f / (float)w; g.eps = c.rms_eps; g.M = M; g.M_pad = Mp;
     g.part = h->part; g.counters = h->counters;
+    if (mseq) {  // gains, gates and shift biases of row r from sequence r / H's table row
+      g.mod_rows = H; g.ms_gain = w; g.ms_gate = 6 * (size_t)w;
+    }
     // --- norm1 + QKV + RoPE
     {
       GemmArgs a = g;
@@ -673,6 +726,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       }
       a.n_q = nq; a.n_kv = nkv; a.dh = dh; a.H = H;
       if (sm) a.shift_bias = modp(sm->t->bqkv, nqkv, l);
+      a.ms_shift = nqkv;
       if (c.qk_norm) { a.qk_gain = h->qk_gain[l]; a.qk_ssp = h->qk_ssp; }
       LAUNCH_CHECK(h, "qkv_rope", (void)Dispatch::gemm(h, R_QKV_ROPE, a, h->qkv_tiles, n_z, st));
     }
@@ -712,6 +766,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
       a.ssp_in = h->ssp_b; a.g_in = w / 16; a.K = w;
       a.S = pick(w / 32, h->sk.gu, n_z).S; a.u_out = h->u; a.N = F;
       if (sm) a.shift_bias = modp(sm->t->bgu, ngu, l);
+      a.ms_shift = ngu;
       if ((PREFETCH_MASK & 2) && !uses_tiled(h, R_DOWN, w / 16, F, M, Mp)) {  // down's weights, tiled as down is launched below
         a.pf.kind = 2; a.pf.base = (const char*)h->d_p[l];
         a.pf.next_groups = w / 16; a.pf.next_S = pick(F / 32, h->sk.down, n_z).S; a.pf.NT = 1; a.pf.KB = F / KBLK;
@@ -746,6 +801,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
     a.w = h->action_out_p; a.x = h->hb; a.ssp_in = h->ssp_a; a.g_in = w / 16; a.K = w;
     a.S = pick(w / 32, h->sk.out, n_z).S;
     a.bias = sm ? sm->t->bout + (size_t)sm->k * nout : h->action_out_b; a.A = A; a.dt = dt; a.xio = dt > 0.f ? h->x : h->vout;
+    if (mseq) { a.mod_rows = H; a.ms_bias = nout; }
     if (h->verify_head) {  // the endpoints, distances and accepted length in the epilogue
       a.H = H; a.vx = h->x; a.draft = h->draft; a.taus = h->taus; a.vparams = h->params;
       a.vpart = h->vpart; a.vcount = h->vcount; a.v_epi = h->out_tiles * n_z; a.gripper_dim = c.gripper_dim;
@@ -779,11 +835,10 @@ int enqueue_temb(ae_handle* h, const float* t_dev, int n_t, float* out, hipStrea
 // The modulation vectors of every (layer, step) of a `steps`-step denoise of a time-modulated
 // expert, built once per step count from the step times' temb: the linear maps of temb, the
 // modulated norm gains, and the shift biases W . shift in the consumers' packed channel order.
-int build_mod_table(ae_handle* h, int steps, const float* temb) {
+int alloc_mod_table(ae_handle* h, int steps, ae_handle::ModTable& t) {
   const ae_config& c = h->c;
   const int w = c.width, L = c.n_layers;
   const size_t nqkv = (size_t)h->qkv_tiles * 16, ngu = (size_t)h->gu_tiles * 16, nout = (size_t)h->out_tiles * 16;
-  ae_handle::ModTable t;
   int rc = dalloc_t(h, &t.mod, (size_t)L * steps * 6 * w);
   if (!rc) rc = dalloc_t(h, &t.g1, (size_t)L * steps * w);
   if (!rc) rc = dalloc_t(h, &t.g2, (size_t)L * steps * w);
@@ -792,27 +847,89 @@ int build_mod_table(ae_handle* h, int steps, const float* temb) {
   if (!rc) rc = dalloc_t(h, &t.fmod, (size_t)steps * 2 * w);
   if (!rc) rc = dalloc_t(h, &t.gf, (size_t)steps * w);
   if (!rc) rc = dalloc_t(h, &t.bout, (size_t)steps * nout);
-  if (rc) return rc;
-  hipStream_t st = h->stream;
-  const dim3 gw((w + 255) / 256, steps);
+  return rc;
+}
+
+// Fill rows 0 .. n - 1 of table t (laid out for `steps` rows per layer) from the n time embeddings
+// temb [n][w]: no allocation and no synchronisation, so that a verification graph can hold it.
+int enqueue_mod_table(ae_handle* h, const ae_handle::ModTable& t, int steps, int n, const float* temb, hipStream_t st,
+                      Timer* tm) {
+  const ae_config& c = h->c;
+  const int w = c.width, L = c.n_layers;
+  const size_t nqkv = (size_t)h->qkv_tiles * 16, ngu = (size_t)h->gu_tiles * 16, nout = (size_t)h->out_tiles * 16;
+  const dim3 gw((w + 255) / 256, n);
   for (int l = 0; l < L; ++l) {
     float* m = t.mod + (size_t)l * steps * 6 * w;
-    hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(6 * w / 4), dim3(256), 0, st, h->w_mod[l], h->b_mod[l], temb, w,
-                       6 * w, 0, m, steps);
-    hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln1[l], m, 6 * w, w, t.g1 + (size_t)l * steps * w);
-    hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->ln2[l], m + 3 * w, 6 * w, w, t.g2 + (size_t)l * steps * w);
-    hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->qkv_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->qkv_p[l],
-                       w / KBLK, m + w, 6 * w, nullptr, 0, t.bqkv + (size_t)l * steps * nqkv, (int)nqkv);
-    hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->gu_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->gu_p[l],
-                       w / KBLK, m + 4 * w, 6 * w, nullptr, 0, t.bgu + (size_t)l * steps * ngu, (int)ngu);
+    LAUNCH_CHECK(h, "mod_rows", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(6 * w / 4), dim3(256), 0, st, h->w_mod[l], h->b_mod[l],
+                                         temb, w, 6 * w, 0, m, n));
+    LAUNCH_CHECK(h, "mod_gain", AE_LAUNCH(mod_gain_kernel, gw, dim3(256), 0, st, h->ln1[l], m, 6 * w, w,
+                                         t.g1 + (size_t)l * steps * w));
+    LAUNCH_CHECK(h, "mod_gain", AE_LAUNCH(mod_gain_kernel, gw, dim3(256), 0, st, h->ln2[l], m + 3 * w, 6 * w, w,
+                                         t.g2 + (size_t)l * steps * w));
+    LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_kernel, dim3(h->qkv_tiles, n), dim3(256), 0, st,
+                                          (const uint16_t*)h->qkv_p[l], w / KBLK, m + w, 6 * w, nullptr, 0,
+                                          t.bqkv + (size_t)l * steps * nqkv, (int)nqkv));
+    LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_kernel, dim3(h->gu_tiles, n), dim3(256), 0, st,
+                                          (const uint16_t*)h->gu_p[l], w / KBLK, m + 4 * w, 6 * w, nullptr, 0,
+                                          t.bgu + (size_t)l * steps * ngu, (int)ngu));
   }
-  hipLaunchKernelGGL(gemv_kernel<WT_BF16>, dim3(2 * w / 4), dim3(256), 0, st, h->final_mod_w, h->final_mod_b, temb,
-                     w, 2 * w, 0, t.fmod, steps);
-  hipLaunchKernelGGL(mod_gain_kernel, gw, dim3(256), 0, st, h->final_ln, t.fmod, 2 * w, w, t.gf);
-  hipLaunchKernelGGL(packed_gemv_kernel, dim3(h->out_tiles, steps), dim3(256), 0, st, (const uint16_t*)h->action_out_p,
-                     w / KBLK, t.fmod + w, 2 * w, h->action_out_b, c.action_dim, t.bout, (int)nout);
-  HIP_TRY(h, hipGetLastError());
-  HIP_TRY(h, hipStreamSynchronize(st));
+  LAUNCH_CHECK(h, "mod_rows", AE_LAUNCH(gemv_kernel<WT_BF16>, dim3(2 * w / 4), dim3(256), 0, st, h->final_mod_w,
+                                       h->final_mod_b, temb, w, 2 * w, 0, t.fmod, n));
+  LAUNCH_CHECK(h, "mod_gain", AE_LAUNCH(mod_gain_kernel, gw, dim3(256), 0, st, h->final_ln, t.fmod, 2 * w, w, t.gf));
+  LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_kernel, dim3(h->out_tiles, n), dim3(256), 0, st,
+                                        (const uint16_t*)h->action_out_p, w / KBLK, t.fmod + w, 2 * w, h->action_out_b,
+                                        c.action_dim, t.bout, (int)nout));
+  return AE_OK;
+}
+
+// The job tables of a verification pass's modulation vectors (mod_tau, from temb_tau), built once.
+int setup_mod_tau_jobs(ae_handle* h) {
+  const ae_config& c = h->c;
+  const int w = c.width, L = c.n_layers, S = c.max_taus;
+  const ae_handle::ModTable& t = h->mod_tau;
+  const size_t nqkv = (size_t)h->qkv_tiles * 16, ngu = (size_t)h->gu_tiles * 16, nout = (size_t)h->out_tiles * 16;
+  std::vector<GemvJob> gj;
+  std::vector<GainJob> nj;
+  std::vector<PackedGemvJob> pj;
+  for (int l = 0; l < L; ++l) {
+    float* m = t.mod + (size_t)l * S * 6 * w;
+    gj.push_back({(const uint16_t*)h->w_mod[l], h->b_mod[l], h->temb_tau, m, w, 6 * w});
+    nj.push_back({h->ln1[l], m, t.g1 + (size_t)l * S * w, 6 * w});
+    nj.push_back({h->ln2[l], m + 3 * w, t.g2 + (size_t)l * S * w, 6 * w});
+    pj.push_back({(const uint16_t*)h->qkv_p[l], m + w, nullptr, t.bqkv + (size_t)l * S * nqkv, w / KBLK, h->qkv_tiles,
+                  6 * w, (int)nqkv, 0});
+    pj.push_back({(const uint16_t*)h->gu_p[l], m + 4 * w, nullptr, t.bgu + (size_t)l * S * ngu, w / KBLK, h->gu_tiles,
+                  6 * w, (int)ngu, 0});
+  }
+  gj.push_back({(const uint16_t*)h->final_mod_w, h->final_mod_b, h->temb_tau, t.fmod, w, 2 * w});
+  nj.push_back({h->final_ln, t.fmod, t.gf, 2 * w});
+  pj.push_back({(const uint16_t*)h->action_out_p, t.fmod + w, h->action_out_b, t.bout, w / KBLK, h->out_tiles, 2 * w,
+                (int)nout, c.action_dim});
+  h->mt_max_n = 6 * w;
+  h->mt_max_tiles = std::max({h->qkv_tiles, h->gu_tiles, h->out_tiles});
+  int rc = upload(h, (void**)&h->mt_gemv, gj.data(), gj.size() * sizeof(GemvJob));
+  if (!rc) rc = upload(h, (void**)&h->mt_gain, nj.data(), nj.size() * sizeof(GainJob));
+  if (!rc) rc = upload(h, (void**)&h->mt_shift, pj.data(), pj.size() * sizeof(PackedGemvJob));
+  return rc;
+}
+
+// mod_tau rows 0 .. n - 1 from temb_tau: three launches over the job tables
+int enqueue_mod_tau(ae_handle* h, int n, hipStream_t st, Timer* tm) {
+  const int w = h->c.width, L = h->c.n_layers;
+  LAUNCH_CHECK(h, "mod_rows", AE_LAUNCH(gemv_jobs_kernel, dim3(h->mt_max_n / 16, L + 1), dim3(256), 0, st, h->mt_gemv, n));
+  LAUNCH_CHECK(h, "mod_gain", AE_LAUNCH(mod_gain_jobs_kernel, dim3((w + 255) / 256, n, 2 * L + 1), dim3(256), 0, st,
+                                       h->mt_gain, w));
+  LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_jobs_kernel, dim3(h->mt_max_tiles, 2 * L + 1), dim3(256), 0, st,
+                                        h->mt_shift, n));
+  return AE_OK;
+}
+
+int build_mod_table(ae_handle* h, int steps, const float* temb) {
+  ae_handle::ModTable t;
+  int rc = alloc_mod_table(h, steps, t);
+  if (!rc) rc = enqueue_mod_table(h, t, steps, steps, temb, h->stream, nullptr);
+  if (rc) return rc;
+  HIP_TRY(h, hipStreamSynchronize(h->stream));
   h->mod_steps[steps] = t;
   return AE_OK;
 }
@@ -898,6 +1015,8 @@ int setup_fused(ae_handle* h) {
   if (fat.maxThreadsPerBlock < FT || fat.numRegs > 256 || fat.localSizeBytes > 0 ||
       fat.sharedSizeBytes + h->fused_lds > (size_t)lds_cu)
     return no("a workgroup does not fit a compute unit");
+  h->occ_fused = blocks_per_cu((const void*)h->fused_fn, FT, h->fused_lds);
+  if (h->occ_fused < 1) return no("the occupancy calculator puts no workgroup on a compute unit");
   // one block of the ring per layer (and one for the final norm's input), each buffer 256-byte aligned
   const size_t Mp = (size_t)ntt * 16;
   size_t off = 0;
@@ -1049,8 +1168,13 @@ int enqueue_verify(ae_handle* h, int n_tau, hipStream_t st, Timer* tm) {
                                              h->phi));
   int rc = enqueue_time_mlp(h, n_tau, h->temb_tau, st, tm);
   if (rc) return rc;
+  StepMod sm{&h->mod_tau, 0, std::max(1, c.max_taus), true};
+  if (c.time_mode) {  // each flow time's modulation vectors, from its temb
+    rc = enqueue_mod_tau(h, n_tau, st, tm);
+    if (rc) return rc;
+  }
   h->verify_head = true;  // the output projection forms the distances and the accepted length
-  rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm);
+  rc = enqueue_velocity(h, n_tau, h->temb_tau, c.width, h->verify_slots, 0, 0.f, st, tm, c.time_mode ? &sm : nullptr);
   h->verify_head = false;
   return rc;
 }
@@ -1321,6 +1445,24 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     ae_destroy(h);
     return fail(nullptr, AE_ERR_HIP, m);
   }
+  // in-kernel waits only where the occupancy calculator puts at least one workgroup on every compute unit
+  {
+    int occ_a, occ_g;
+    if (h->at == AT_F32) {
+      occ_a = attn_split_occ<AT_F32, false>(cfg->head_dim);
+      occ_g = std::min(std::min(gemm_occ<WT_F32, AT_F32, R_QKV_ROPE>(), gemm_occ<WT_F32, AT_F32, R_O_PROJ>()),
+                       std::min(gemm_occ<WT_F32, AT_F32, R_GATE_UP>(), gemm_occ<WT_F32, AT_F32, R_DOWN>()));
+    } else {
+      occ_a = cfg->qk_norm ? attn_split_occ<AT_BF16, true>(cfg->head_dim) : attn_split_occ<AT_BF16, false>(cfg->head_dim);
+      occ_g = std::min(gemm_occ<WT_BF16, AT_BF16, R_QKV_ROPE>(), gemm_occ<WT_BF16, AT_BF16, R_O_PROJ>());
+      occ_g = std::min(occ_g, h->mt == WT_FP8 ? std::min(gemm_occ<WT_FP8, AT_BF16, R_GATE_UP>(), gemm_occ<WT_FP8, AT_BF16, R_DOWN>())
+                                              : std::min(gemm_occ<WT_BF16, AT_BF16, R_GATE_UP>(), gemm_occ<WT_BF16, AT_BF16, R_DOWN>()));
+    }
+    h->occ_attn = occ_a;
+    h->occ_gemm = occ_g;
+    if (occ_a < 1) h->coresident_attn = false;
+    if (occ_g < 1) h->poll_splitk = false;
+  }
 
   const int w = c.width, A = c.action_dim, F = c.mlp_dim, nq = c.n_q_heads, nkv = c.n_kv_heads, dh = c.head_dim;
   const int L = c.n_layers, H = c.horizon, P = c.prefix_len;
@@ -1414,6 +1556,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(upload(h, &h->final_mod_w, wts->final_mod_w, (size_t)2 * w * w * wes));
     TRY(upload(h, (void**)&h->final_mod_b, wts->final_mod_b, (size_t)2 * w * 4));
     TRY(dalloc_t(h, &h->zero_w, (size_t)w));
+    if (c.max_taus > 0) TRY(alloc_mod_table(h, c.max_taus, h->mod_tau));
   }
   if (c.qk_norm) TRY(dalloc_t(h, &h->qk_ssp, (size_t)(nq + nkv) * dh / 16 * Mp));
   // ---- activations and scratch (padding rows stay zero)
@@ -1516,6 +1659,7 @@ int ae_create(const ae_config* cfg, const ae_weights* wts, ae_handle** out) {
     TRY(dalloc(h, &h->pf_k, (size_t)L * h->pf_layer_elems * kes));
     TRY(dalloc(h, &h->pf_v, (size_t)L * h->pf_layer_elems * kes));
   }
+  if (c.time_mode && c.max_taus > 0) TRY(setup_mod_tau_jobs(h));
   if (want_fused) TRY(setup_fused(h));
   (void)scratch_address(h);  // a failure is reported by ae_denoise_static
   TRY(reset_exchange(h));
@@ -1673,7 +1817,6 @@ int ae_denoise_static(ae_handle* h, int batch, const float* d_noise, int steps, 
 static int check_verify(ae_handle* h, int slot, int n_tau) {
   if (!h) return AE_ERR_INVALID_ARG;
   if (h->c.max_taus < 1) return fail(h, AE_ERR_UNSUPPORTED, "handle created with max_taus = 0");
-  if (h->c.time_mode) return fail(h, AE_ERR_UNSUPPORTED, "verification of a time-modulated expert is not built");
   if (h->c.draft) return fail(h, AE_ERR_UNSUPPORTED, "a draft-model handle runs ae_draft only");
   if (h->c.prefill) return fail(h, AE_ERR_UNSUPPORTED, "a prefill handle runs ae_prefill only");
   if (n_tau < 1 || n_tau > h->c.max_taus) return fail(h, AE_ERR_INVALID_ARG, "n_tau out of range");

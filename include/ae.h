@@ -88,7 +88,8 @@ typedef struct ae_config {
   int kv_dtype;     /* prefix cache: equal to weight_dtype */
   int gripper_dim;  /* action dim holding the +-1 gripper channel, -1 = none */
   int time_mode;    /* 0: temb added to every action_in_proj row; 1: per-layer time modulation
-                       (see ae_layer_weights.w_mod; bf16 weights and MLP, no ae_verify / ae_round) */
+                       (see ae_layer_weights.w_mod; bf16 weights and MLP; ae_verify / ae_round form
+                       each verification time's modulation vectors inside the pass) */
   int qk_norm;      /* 1: RMSNorm of q and k per head over head_dim (gains q_norm, k_norm)
                        before RoPE; the cached prefix K is used as given */
   int draft;        /* 1: a draft model for ae_draft ("Realtime-VLA FLASH" article, section 03:
@@ -175,8 +176,11 @@ typedef struct ae_handle ae_handle;
  *   AE_GRAPH=0         passes enqueue their launches directly instead of replaying a
  *                      captured graph (same kernels, same arguments, same results).
  * The persistent step kernel and the in-kernel exchanges assume every workgroup of
- * their launch is resident at once (one workgroup per compute unit for the step
- * kernel, checked against the kernel's registers and LDS at ae_create). When another
+ * their launch is resident at once (one workgroup per compute unit). ae_create asks
+ * the runtime's occupancy calculator (hipOccupancyMaxActiveBlocksPerMultiprocessor)
+ * for each kernel that may wait: the step kernel, the split attention kernels and the
+ * split-K GEMM kernels of the handle's dtypes; a kernel with no workgroup per compute
+ * unit is never launched in a form that waits. When another
  * process or stream holds compute units, a bounded wait gives up, sets a host-visible
  * flag, and the call repeats its pass with launches that wait for nothing inside a
  * kernel (see Errors); after three such passes in a row a handle stops trying the
@@ -234,7 +238,9 @@ int ae_denoise_static(ae_handle* h, int batch, const float* d_noise, int steps, 
  * D[j][i] = ||a_j[i] - draft[i]||_2. *accept_len = longest k with D[j][i] < delta
  * for all i < k and all j, forced to 0 when *gripper_switch = 1 (the gripper
  * channel changes sign between consecutive rows). dist_out (nullable) receives
- * D [n_tau][H]. Synchronous. Requires 1 <= n_tau <= max_taus. */
+ * D [n_tau][H]. Synchronous. Requires 1 <= n_tau <= max_taus. A time-modulated
+ * expert (time_mode 1) conditions sequence j on tau_j alone: its layer and final-norm
+ * modulation vectors are computed from temb(tau_j) at the start of the pass. */
 int ae_verify(ae_handle* h, int slot, const float* draft, const float* noise, const float* taus, int n_tau,
               float delta, int* accept_len, int* gripper_switch, float* dist_out);
 

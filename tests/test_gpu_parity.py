@@ -245,13 +245,60 @@ def test_qknorm_verify_matches_oracle():
     ex.close()
 
 
-def test_modulated_expert_rejects_verification():
-    case = Case(SMALL_DM05.with_(max_taus=2))
+def _delta_sweep(ex, slot, draft, noise, taus, D, D_o, horizon):
+    """Every accept length k whose deciding half-gap (between the running maxima of D over rows
+    k - 1 and k) exceeds twice the largest measured |D - D_o|: the kernel must take each such
+    decision exactly as the oracle does (FLASH article, section 03: a row is accepted only when every
+    flow time reconstructs it within delta). Returns the lengths checked."""
+    e = float(np.max(np.abs(D.astype(np.float64) - D_o)))
+    run = np.maximum.accumulate(D_o.max(axis=0))
+    checked = []
+    for k in range(1, horizon):
+        if 0.5 * (run[k] - run[k - 1]) > 2.0 * e:
+            delta = float(0.5 * (run[k] + run[k - 1]))
+            assert O.accept_from_distances(D_o, delta, 0) == k
+            acc_k, _, _ = ex.verify(slot, draft, noise, taus, delta)
+            assert acc_k == k, (k, acc_k)
+            checked.append(k)
+    return checked
+
+
+def test_modulated_verify_matches_oracle():
+    """Verification with the time-modulated QK-norm expert: each flow time's sequence takes the layer
+    and final-norm modulation of its own tau (per-row vectors in every epilogue), against the oracle's
+    independent velocity per tau; 3 flow times, two prefix slots, draft seeds with and without a
+    gripper switch, and the accept decisions of a delta sweep."""
+    cfg = SMALL_DM05.with_(name="small_dm05_v", max_taus=3)
+    case = Case(cfg)
     ex = _expert(case)
-    d = G.make_draft(case.cfg, 0)
-    with pytest.raises(AEError) as e:
-        ex.verify(0, d, d, np.array([0.3, 0.6], np.float32), 0.05)
-    assert e.value.code == -2
+    taus = np.array([0.15, 0.5, 0.85], np.float32)
+    checked = []
+    for slot in (0, 2):
+        for seed in range(3):
+            draft = G.make_draft(cfg, seed)
+            noise = case.noise(1, 500 + seed)[0]
+            acc, sw, D = ex.verify(slot, draft, noise, taus, 0.05)
+            acc_o, sw_o, D_o = case.oracle_verify(slot, draft, noise, taus, 0.05)
+            assert (acc, sw) == (acc_o, sw_o), (slot, seed)
+            err = rel_err(D, D_o)
+            print(f"dm05 verify slot {slot} seed {seed} D rel_err={err:.3e}")
+            assert err <= tol_for(cfg), err
+            if sw == 0:
+                checked += _delta_sweep(ex, slot, draft, noise, taus, D, D_o, cfg.horizon)
+    print(f"accept lengths checked: {sorted(set(checked))}")
+    assert len(set(checked)) >= 3
+    # a round: the fast path, or the full modulated denoise on a switching draft
+    nf = case.noise(1, 600)[0]
+    for seed in (0, 1):
+        draft = G.make_draft(cfg, seed)
+        nv = case.noise(1, 700 + seed)[0]
+        _, _, D_o = case.oracle_verify(0, draft, nv, taus, 0.05)
+        delta = float(D_o.max()) * 1.5 + 1e-3
+        act, acc, sw, full = ex.round(0, draft, nv, taus, delta, nf, 2)
+        act_o, acc_o, sw_o, full_o = O.dual_path_round(cfg, case.Wd, case.kvd[0][0], case.kvd[0][1], draft, nv, taus,
+                                                       delta, nf, 2)
+        assert (acc, sw, full) == (acc_o, sw_o, full_o), seed
+        assert rel_err(act, act_o) <= tol_for(cfg) if full else np.array_equal(act, draft)
     ex.close()
 
 
@@ -266,6 +313,30 @@ def test_dm05_full_matches_oracle():
     err = rel_err(got, ref)
     print(f"dm05 10 steps rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
     assert err <= 2e-2
+    ex.close()
+
+
+def test_dm05_verify_full():
+    """Verification with the DM0.5-style expert at the Pi0 verify shape (18 layers, width 1024, 8q/1kv x
+    256, MLP 4096, P = 816, 4 flow times): accepted length, switch and distances against the oracle, and
+    the accept decisions of a delta sweep."""
+    cfg = C.DM05_VERIFY
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.asarray(C.VERIFY_TAUS, np.float32)
+    checked = []
+    for seed in range(8):
+        draft, noise, _ = G.make_verify_case(cfg, seed)
+        acc, sw, D = ex.verify(0, draft, noise, taus, C.VERIFY_DELTA)
+        acc_o, sw_o, D_o = case.oracle_verify(0, draft, noise, taus, C.VERIFY_DELTA)
+        assert (acc, sw) == (acc_o, sw_o), seed
+        err = rel_err(D, D_o)
+        print(f"dm05 verify seed {seed} D rel_err={err:.3e} gpu_ms={ex.last_gpu_ms():.3f}")
+        assert err <= 2e-2, (seed, err)
+        if sw == 0:
+            checked += _delta_sweep(ex, 0, draft, noise, taus, D, D_o, cfg.horizon)
+    print(f"{len(checked)} accept decisions checked, lengths {sorted(set(checked))}")
+    assert len(set(checked)) >= 4
     ex.close()
 
 

@@ -73,6 +73,8 @@ PI0_BATCH16 = PI0.with_(name="pi0_batch16", max_batch=16, batch=16)
 # DM0.5-style expert at the Pi0 shapes (DM0.5 guide, section 5.2: the time MLP conditions every
 # layer, and the expert sits on a Gemma3 text stack, which normalises q and k per head)
 DM05 = PI0.with_(name="dm05_bf16", time_mode=1, qk_norm=1)
+# and its speculative verification (FLASH article, section 03) at the Pi0 verify shape
+DM05_VERIFY = DM05.with_(name="dm05_verify", max_taus=4, gripper_dim=31)
 
 # Draft model of the speculative round (FLASH article, section 03: one Gemma block and a linear action
 # head, ~110M parameters; learnable action queries over the current image features): a 2B-class Gemma
@@ -90,7 +92,7 @@ PREFILL = AEConfig(
     action_dim=32, horizon=816, prefix_len=0, mlp_dtype="fp8", prefill=1, steps=1,
 )
 
-CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05, DRAFT, PREFILL]
+CONFIGS = [TINY, PI0, PI0_FP8, PI0_VERIFY, PI0_BATCH16, DM05, DM05_VERIFY, DRAFT, PREFILL]
 VERIFY_TAUS = (0.2, 0.4, 0.6, 0.8)
 VERIFY_DELTA = 0.05
 
