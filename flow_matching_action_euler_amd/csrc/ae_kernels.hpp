@@ -1244,12 +1244,17 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       const int tl = (wm * 4 + j) * 16 + tq, tok = tt0 * 16 + tl;
       const float ir = inv_rms[tl];
       const int f = ((ct0 + wn * 4) / 2 + p) * 16 + cq * 4;
+      f32x4 g2 = gv * ir, u2 = uv * ir;
+      if (a.shift_bias) {  // time-modulated expert: W . shift of the row's sequence, after the 1/rms scaling
+        const float* sb = a.shift_bias + (a.mod_rows ? (size_t)(min(tok, a.M - 1) / a.mod_rows) * a.ms_shift : 0) +
+                          (ct0 + wn * 4 + 2 * p) * 16 + cq * 4;
+        g2 += *(const f32x4*)sb;
+        u2 += *(const f32x4*)(sb + 16);
+      }
       if (tok < a.M) {
         uint2 o;
-        o.x = (uint32_t)f32_to_bf16(gelu_tanh_fast(gv[0] * ir) * (uv[0] * ir)) |
-              ((uint32_t)f32_to_bf16(gelu_tanh_fast(gv[1] * ir) * (uv[1] * ir)) << 16);
-        o.y = (uint32_t)f32_to_bf16(gelu_tanh_fast(gv[2] * ir) * (uv[2] * ir)) |
-              ((uint32_t)f32_to_bf16(gelu_tanh_fast(gv[3] * ir) * (uv[3] * ir)) << 16);
+        o.x = (uint32_t)f32_to_bf16(gelu_tanh_fast(g2[0]) * u2[0]) | ((uint32_t)f32_to_bf16(gelu_tanh_fast(g2[1]) * u2[1]) << 16);
+        o.y = (uint32_t)f32_to_bf16(gelu_tanh_fast(g2[2]) * u2[2]) | ((uint32_t)f32_to_bf16(gelu_tanh_fast(g2[3]) * u2[3]) << 16);
         *(uint2*)((uint16_t*)a.u_out + act_idx(tok, f, ntt)) = o;
       }
     }
@@ -1322,14 +1327,28 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const int tin = ct0 + wn * 4 + i;  // wave-uniform
         const float ir = inv_rms[tl];
         const f32x4 v = tile_sum(i, j);
-        float x[4], xp[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = v[e] * ir;
-          xp[e] = __shfl_xor(x[e], 32);  // channel c +- 8: the other half of the rotation pair
-        }
         const bool valid = tok < a.M;
         const int sq = sqj[j], t = tj[j];
+        float x[4], xp[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = v[e] * ir;
+        if (a.shift_bias) {  // time-modulated expert: W . shift of the row's sequence
+          const f32x4 sb = *(const f32x4*)(a.shift_bias + (a.mod_rows ? (size_t)sq * a.ms_shift : 0) + tin * 16 + cq * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] += sb[e];
+        }
+        if (a.qk_gain && tin < q_tiles + k_tiles) {  // QK-norm (wave-uniform): the tile's share of its head's
+          // sum of squares for this token (its 16 channels sit in lanes tq + 16 cq), then the per-dim gains
+          float s2 = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+          s2 += __shfl_xor(s2, 16);
+          s2 += __shfl_xor(s2, 32);
+          if (cq == 0 && valid) a.qk_ssp[(size_t)tin * a.M_pad + tok] = s2;
+          const f32x4 qg = *(const f32x4*)(a.qk_gain + tin * 16 + cq * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] *= qg[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) xp[e] = __shfl_xor(x[e], 32);  // channel c +- 8: the other half of the rotation pair
         if (tin < q_tiles + k_tiles) {
           const bool is_q = tin < q_tiles;
           const int tt2 = is_q ? tin : tin - q_tiles, head = tt2 / tph, pair = tt2 - head * tph;

@@ -546,6 +546,49 @@ def test_tiled_gemm_fp8_mlp_denoise_matches_oracle(shape, monkeypatch):
     ex.close()
 
 
+SMALL_DM05_B7 = SMALL_DM05.with_(name="small_dm05_b7t", max_batch=7)
+SMALL_QKN_B7 = SMALL_BF16_B7.with_(name="small_qknorm_b7", qk_norm=1)
+
+
+@pytest.mark.parametrize("shape", [0, 1, 2, 3], ids=lambda s: f"shape{s}")
+@pytest.mark.parametrize("cfg", [SMALL_DM05_B7, SMALL_QKN_B7], ids=lambda c: c.name)
+def test_tiled_gemm_modulated_qknorm_matches_oracle(cfg, shape, monkeypatch):
+    """The token-tiled QKV and gate/up epilogues with the time-modulated expert's shift biases and the
+    QK-norm sums of squares and gains (o_proj and down of a modulated expert keep the 64-token kernel),
+    every tile shape, 7 robots = 140 tokens."""
+    monkeypatch.setenv("AE_TILED_SHAPE", str(shape))
+    case = Case(cfg)
+    ex = _expert(case)
+    noise = case.noise(7)
+    got = ex.denoise(noise, 2)
+    ref = case.oracle_denoise(noise, 2)
+    err = rel_err(got, ref)
+    print(f"tiled {cfg.name} shape={shape} rel_err={err:.3e}")
+    assert err <= tol_for(cfg), err
+    ex.close()
+
+
+@pytest.mark.parametrize("shape", [1, 3], ids=lambda s: f"shape{s}")
+def test_tiled_gemm_modulated_verify_matches_oracle(shape, monkeypatch):
+    """A time-modulated verification pass of 8 flow times (160 rows) through the token-tiled QKV and
+    gate/up epilogues: each row takes its own flow time's shift biases."""
+    monkeypatch.setenv("AE_TILED_SHAPE", str(shape))
+    cfg = SMALL_DM05.with_(name="small_dm05_t8", max_taus=8)
+    case = Case(cfg)
+    ex = _expert(case)
+    taus = np.linspace(0.1, 0.9, 8).astype(np.float32)
+    for seed in range(2):
+        draft = G.make_draft(cfg, seed)
+        noise = case.noise(1, 300 + seed)[0]
+        acc, sw, D = ex.verify(1, draft, noise, taus, 0.05)
+        acc_o, sw_o, D_o = case.oracle_verify(1, draft, noise, taus, 0.05)
+        assert (acc, sw) == (acc_o, sw_o)
+        err = rel_err(D, D_o)
+        print(f"tiled dm05 verify shape={shape} seed={seed} D rel_err={err:.3e}")
+        assert err <= tol_for(cfg), err
+    ex.close()
+
+
 def test_tiled_gemm_verify_matches_oracle(monkeypatch):
     """8 flow times x 20 rows = 160 tokens in one verification pass (token-tiled GEMMs)."""
     cfg = SMALL_BF16.with_(name="small_bf16_t8", max_taus=8)
