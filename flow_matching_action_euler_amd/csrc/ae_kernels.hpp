@@ -2199,8 +2199,10 @@ __global__ void mod_gain_jobs_kernel(const GainJob* jobs, int w) {
 }
 
 // y[it][ch] = sum_k W(ch, k) x[it][k] (+ add[ch] for ch < n_add) over packed bf16 weights (the layout
-// packed_gemv_kernel reads) for it < n_t, job blockIdx.y, tile blockIdx.x: each 16-byte piece of the
-// tile is loaded once for all n_t inputs (8 at a time).
+// packed_gemv_kernel reads) for it < n_t, job blockIdx.y, tiles 8 blockIdx.x .. + 8. Thread -> (k-group
+// wave, lane = 16 q + c): for each of its k-blocks it loads the 8 inputs k-block * 32 + 8 q .. + 8 of 4
+// rows once and reuses them for the 8 tiles' pieces of channel c, so input loads do not outnumber weight
+// loads; partial sums meet across q by shuffles and across the 4 waves in LDS.
 struct PackedGemvJob {
   const uint16_t* w;
   const float* x;
@@ -2208,44 +2210,58 @@ struct PackedGemvJob {
   float* y;
   int KB, tiles, x_stride, y_stride, n_add;
 };
+constexpr int PGJ_TILES = 8;
+constexpr int PGJ_ROWS = 4;
 __global__ __launch_bounds__(256) void packed_gemv_jobs_kernel(const PackedGemvJob* jobs, int n_t) {
-  __shared__ float part[16][8][17];
+  __shared__ float part[4][PGJ_TILES][PGJ_ROWS][16];
   const PackedGemvJob jb = jobs[blockIdx.y];
-  const int tile = blockIdx.x, c = threadIdx.x & 15, grp = threadIdx.x >> 4;
-  if (tile >= jb.tiles) return;
-  for (int it0 = 0; it0 < n_t; it0 += 8) {
-    float acc[8];
+  const int t0 = blockIdx.x * PGJ_TILES;
+  if (t0 >= jb.tiles) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, q = lane >> 4, c = lane & 15;
+  for (int it0 = 0; it0 < n_t; it0 += PGJ_ROWS) {
+    float acc[PGJ_TILES][PGJ_ROWS];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[j] = 0.f;
-    for (int kb = grp; kb < jb.KB; kb += 16)
+    for (int u = 0; u < PGJ_TILES; ++u)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 p = *(const uint4*)(jb.w + (((size_t)tile * jb.KB + kb) * 64 + q * 16 + c) * 8);
-        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
-        float wv[8];
+      for (int j = 0; j < PGJ_ROWS; ++j) acc[u][j] = 0.f;
+    for (int kb = wave; kb < jb.KB; kb += 4) {
+      float xv[PGJ_ROWS][8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          wv[2 * e] = bf16_to_f32((uint16_t)(pw[e] & 0xffffu));
-          wv[2 * e + 1] = bf16_to_f32((uint16_t)(pw[e] >> 16));
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          if (it0 + j < n_t) {
-            const float* xs = jb.x + (size_t)(it0 + j) * jb.x_stride + kb * 32 + q * 8;
-            const float4 x0 = *(const float4*)xs, x1 = *(const float4*)(xs + 4);
-            acc[j] += wv[0] * x0.x + wv[1] * x0.y + wv[2] * x0.z + wv[3] * x0.w + wv[4] * x1.x + wv[5] * x1.y +
-                      wv[6] * x1.z + wv[7] * x1.w;
-          }
+      for (int j = 0; j < PGJ_ROWS; ++j) {
+        const int row = min(it0 + j, n_t - 1);
+        const float* xs = jb.x + (size_t)row * jb.x_stride + kb * 32 + q * 8;
+        const float4 x0 = *(const float4*)xs, x1 = *(const float4*)(xs + 4);
+        xv[j][0] = x0.x; xv[j][1] = x0.y; xv[j][2] = x0.z; xv[j][3] = x0.w;
+        xv[j][4] = x1.x; xv[j][5] = x1.y; xv[j][6] = x1.z; xv[j][7] = x1.w;
       }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) part[grp][j][c] = acc[j];
+      for (int u = 0; u < PGJ_TILES; ++u) {
+        const int tile = min(t0 + u, jb.tiles - 1);
+        const uint4 p = *(const uint4*)(jb.w + (((size_t)tile * jb.KB + kb) * 64 + lane) * 8);
+        const uint32_t pw[4] = {p.x, p.y, p.z, p.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float w0 = bf16_to_f32((uint16_t)(pw[e] & 0xffffu)), w1 = bf16_to_f32((uint16_t)(pw[e] >> 16));
+#pragma unroll
+          for (int j = 0; j < PGJ_ROWS; ++j) acc[u][j] += w0 * xv[j][2 * e] + w1 * xv[j][2 * e + 1];
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PGJ_TILES; ++u)
+#pragma unroll
+      for (int j = 0; j < PGJ_ROWS; ++j) {
+        float v = acc[u][j];
+        v += __shfl_xor(v, 16);
+        v += __shfl_xor(v, 32);
+        if (q == 0) part[wave][u][j][c] = v;
+      }
     __syncthreads();
-    if (threadIdx.x < 128) {
-      const int j = threadIdx.x >> 4, cc = threadIdx.x & 15;
-      if (it0 + j < n_t) {
-        float sum = 0.f;
-        for (int g = 0; g < 16; ++g) sum += part[g][j][cc];
-        const int ch = tile * 16 + cc;
+    for (int o = threadIdx.x; o < PGJ_TILES * PGJ_ROWS * 16; o += 256) {  // (tile u, row j, channel) sums over the waves
+      const int u = o >> 6, j = (o >> 4) & 3, cc = o & 15;
+      if (t0 + u < jb.tiles && it0 + j < n_t) {
+        const float sum = part[0][u][j][cc] + part[1][u][j][cc] + part[2][u][j][cc] + part[3][u][j][cc];
+        const int ch = (t0 + u) * 16 + cc;
         jb.y[(size_t)(it0 + j) * jb.y_stride + ch] = sum + ((jb.add && ch < jb.n_add) ? jb.add[ch] : 0.f);
       }
     }

@@ -920,7 +920,7 @@ int enqueue_mod_tau(ae_handle* h, int n, hipStream_t st, Timer* tm) {
   LAUNCH_CHECK(h, "mod_rows", AE_LAUNCH(gemv_jobs_kernel, dim3(h->mt_max_n / 16, L + 1), dim3(256), 0, st, h->mt_gemv, n));
   LAUNCH_CHECK(h, "mod_gain", AE_LAUNCH(mod_gain_jobs_kernel, dim3((w + 255) / 256, n, 2 * L + 1), dim3(256), 0, st,
                                        h->mt_gain, w));
-  LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_jobs_kernel, dim3(h->mt_max_tiles, 2 * L + 1), dim3(256), 0, st,
+  LAUNCH_CHECK(h, "mod_shift", AE_LAUNCH(packed_gemv_jobs_kernel, dim3((h->mt_max_tiles + PGJ_TILES - 1) / PGJ_TILES, 2 * L + 1), dim3(256), 0, st,
                                         h->mt_shift, n));
   return AE_OK;
 }

@@ -302,6 +302,51 @@ def test_modulated_verify_matches_oracle():
     ex.close()
 
 
+def _strong_modulation(cfg, W, seed=7):
+    """W with every modulation map scaled 30x and random shift biases: the generated maps move the
+    norms by a few percent only, which would let a wrong row-to-sequence index or a lost shift bias
+    pass at small widths."""
+    rng = np.random.default_rng(seed)
+    W = dict(W)
+    w = cfg.width
+    for name in [f"layers.{l}.w_mod" for l in range(cfg.n_layers)] + ["final_mod_w"]:
+        W[name] = G.store(O.decode(W[name], cfg.weight_dtype).astype(np.float32) * np.float32(30.0), cfg.weight_dtype)
+    for l in range(cfg.n_layers):
+        b = W[f"layers.{l}.b_mod"].copy()
+        b[w:2 * w] = 0.5 * rng.standard_normal(w)      # shift1
+        b[4 * w:5 * w] = 0.5 * rng.standard_normal(w)  # shift2
+        W[f"layers.{l}.b_mod"] = b.astype(np.float32)
+    fb = W["final_mod_b"].copy()
+    fb[w:] = 0.5 * rng.standard_normal(w)
+    W["final_mod_b"] = fb.astype(np.float32)
+    return W
+
+
+@pytest.mark.parametrize("shape", [None, 1, 3], ids=lambda s: "modelled" if s is None else f"shape{s}")
+def test_modulated_verify_strong_modulation(shape, monkeypatch):
+    """Verification of a time-modulated expert whose modulation is large (30x maps, random shifts), so
+    that every flow time's rows differ in their gains, gates and shift biases: the 64-token kernel and
+    two token-tiled shapes against the oracle."""
+    if shape is not None:
+        monkeypatch.setenv("AE_TILED_SHAPE", str(shape))
+    cfg = SMALL_DM05.with_(name="small_dm05_strong", max_taus=4)
+    case = Case(cfg)
+    case.W = _strong_modulation(cfg, case.W)
+    case.Wd = O.dequantize_weights(cfg, case.W)
+    ex = _expert(case)
+    taus = np.array([0.1, 0.4, 0.6, 0.9], np.float32)
+    for seed in range(2):
+        draft = G.make_draft(cfg, seed)
+        noise = case.noise(1, 800 + seed)[0]
+        acc, sw, D = ex.verify(0, draft, noise, taus, 0.05)
+        acc_o, sw_o, D_o = case.oracle_verify(0, draft, noise, taus, 0.05)
+        assert (acc, sw) == (acc_o, sw_o), seed
+        err = rel_err(D, D_o)
+        print(f"strong modulation shape={shape} seed={seed} D rel_err={err:.3e}")
+        assert err <= tol_for(cfg), err
+    ex.close()
+
+
 def test_dm05_full_matches_oracle():
     """DM0.5-style expert at the Pi0 shapes (18 layers, width 1024, 8q/1kv x 256, MLP 4096, P = 816), 10 steps."""
     cfg = C.DM05
