@@ -38,12 +38,6 @@ enum WType { WT_BF16 = 0, WT_FP8 = 1, WT_F32 = 2 };
 enum AType { AT_BF16 = 0, AT_F32 = 1 };
 enum Epi { EPI_QKV = 0, EPI_RESID = 1, EPI_GEGLU = 2, EPI_OUT = 3 };
 
-#ifndef GEMM_TOUCH
-#define GEMM_TOUCH 1
-#endif
-#ifndef TILED_TOUCH
-#define TILED_TOUCH 1
-#endif
 constexpr int TOKG = 64;   // tokens per workgroup (4 MFMA column tiles of 16)
 
 constexpr int KBLK = 32;   // inputs per k-block
@@ -818,7 +812,7 @@ __device__ __forceinline__ void gemm_body(const GemmArgs& a) {
   // 6.7 us, down 10.7 -> 10.0 us): with one (batch-1 passes) the touches duplicate the previous
   // kernel's L2 placement of these weights and made the launch-per-phase chunk 6.94 -> 7.33 ms.
   int tch[2] = {0, 0};
-  if (GEMM_TOUCH && gridDim.z > 1) {
+  if (gridDim.z > 1) {
     constexpr size_t FB = WT == WT_FP8 ? 512 : WT == WT_F32 ? 2048 : 1024;  // bytes per fragment
     const int kbs = KB / a.S;
     const unsigned lpt = (unsigned)(kbs * FB / 128), wl = NT * lpt;
@@ -962,7 +956,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
   // chunk's wait covers them). Measured at batch 16: o_proj 12.5 -> 11.6 us, down 19.9 -> 18.3 us;
   // the shapes that stage shared fragments in LDS got slower with it (gate/up 19.0 -> 20.8 us).
   int tch[4] = {0, 0, 0, 0};
-  if (TILED_TOUCH && !C::SHARED) {
+  if constexpr (!C::SHARED) {
     constexpr size_t AFB_ = WT == WT_FP8 ? 512 : 1024;
     const unsigned wl = (unsigned)((size_t)C::NT * KB * AFB_ / 128);  // weight panel lines, contiguous
     const char* wpan = (const char*)a.w + (size_t)ct0 * KB * AFB_;

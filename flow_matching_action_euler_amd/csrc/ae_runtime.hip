@@ -687,10 +687,7 @@ int enqueue_velocity(ae_handle* h, int n_seq, const float* temb, int temb_stride
   aa.n_split = plan.n_split;
   aa.coresident = plan.coresident;
   aa.xcd_group = n_seq * nkv >= 8 && !plan.coresident && h->attn_xcd;
-#ifndef ATT_TOUCH
-#define ATT_TOUCH 1
-#endif
-  aa.touch = ATT_TOUCH && n_seq >= 2;
+  aa.touch = n_seq >= 2;  // several sequences: each touches its prefix K/V into L2 first
   aa.err = h->flag_dev;
   aa.wait = h->wait_ticks;
   aa.scale_log2 = (float)(1.4426950408889634 / std::sqrt((double)dh));
