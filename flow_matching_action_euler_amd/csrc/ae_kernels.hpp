@@ -882,13 +882,13 @@ constexpr void (*gemm_entry())(GemmArgs) {
 // activation in each 16- or 32-channel group. The 8 waves are WN x WM x WK: wave (wn, wm, wk)
 // accumulates the 64 x 64 sub-tile (wn, wm) (4 x 4 MFMA tiles) over the k-blocks of its k-group
 // wk (one k-block of each chunk); with WK > 1 the partial sub-tiles meet in LDS and each wave
-// finishes 1/WK of the tiles. Operands are staged in LDS as whole 1 KB fragments in the packed
-// order (lane-major, so fragment reads are conflict-free) in two buffers; each wave holds the
-// fragments of two chunks in registers, so the MFMAs of one chunk run while the next chunk's
-// fragments are read and the one after is stored (measured on a stand-alone step: the LDS reads
-// hide completely under the MFMAs, the per-step barrier costs ~20% and the LDS writes ~50%).
-// bf16 activations; bf16 weights, or E4M3 weights (the MLP roles) kept as bytes in LDS, widened
-// to bf16 (exact) after the fragment read and scaled per output channel in the epilogue.
+// finishes 1/WK of the tiles. Operands go from global memory straight into LDS as whole fragments
+// in the packed order (lane-major, so fragment reads are conflict-free), several chunks in flight;
+// each wave holds the fragments of two chunks in registers, so the MFMAs of one chunk run while the
+// next chunk's fragments are read. bf16 activations; bf16 weights, or E4M3 weights (the MLP roles)
+// kept as bytes in LDS (512-byte fragments), widened to bf16 (exact) after the fragment read and
+// scaled per output channel in the epilogue. (Staging through registers and LDS stores, the form
+// this replaced, cost the prefill 4%: 6.73 -> 6.44 ms per pass once its E4M3 weights loaded direct.)
 template <int WN, int WM, int WK>
 struct TileCfg {
   static_assert(WN * WM * WK == GW, "8 waves");
@@ -980,34 +980,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   }
 
-  // fragment f of chunk c: weights [ct][kk] for f < NA, then activations [kk][tt]; the token
+  // weight fragments [ct][kk] and activation fragments [kk][tt] of the packed operands; the token
   // tiles past the buffer's rows read its last tile (their outputs are never stored)
   const WR* wsrc = (const WR*)a.w;
   const i32x4* xsrc = (const i32x4*)a.x;
-  // two chunks in flight in registers (vector types: arrays of HIP's uint4 structs stayed in
-  // scratch memory); weight load i of a thread is fragment wave + 8 i, activation load i fragment
-  // NA + wave + 8 i
-  WR w0[LW], w1[LW];
-  i32x4 x0[LX], x1[LX];
-  auto gload = [&](WR (&rw)[LW], i32x4 (&rx)[LX], int c) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < LW; ++i) {
-      const int f = wave + GW * i;
-      rw[i] = wsrc[((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane];
-    }
-#pragma unroll
-    for (int i = 0; i < LX; ++i) {
-      const int f = wave + GW * i;
-      rx[i] = xsrc[((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane];
-    }
-  };
-  auto lstore = [&](const WR (&rw)[LW], const i32x4 (&rx)[LX], int b) __attribute__((always_inline)) {
-    char* dst = stage + b * CHUNKB;
-#pragma unroll
-    for (int i = 0; i < LW; ++i) *(WR*)(dst + (size_t)(wave + GW * i) * AFB + lane * (AFB / 64)) = rw[i];
-#pragma unroll
-    for (int i = 0; i < LX; ++i) *(i32x4*)(dst + C::NA * AFB + (size_t)(wave + GW * i) * 1024 + lane * 16) = rx[i];
-  };
   f32x4 acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -1066,7 +1042,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
     }
   };
   const int nc = KB / C::CK;
-  bf16x8 fa_d[4], fb_d[4], ga_d[4], gb_d[4];  // the LDS-staged forms' fragments of two chunks
+  bf16x8 fa_d[4], fb_d[4], ga_d[4], gb_d[4];  // the LDS-staged shapes' fragments of two chunks
   if constexpr (WN == 1 && WM == 1) {
     // one 64 x 64 tile per workgroup, one k-group per wave: no fragment is shared between waves,
     // so each wave loads its own straight into registers (three k-blocks in flight) and the loop
@@ -1098,31 +1074,46 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       if (c + 2 < nc) mm(a2, b2);
       ld(a2, b2, c + 5);
     }
-  } else if constexpr (WT == WT_BF16) {
+  } else if constexpr (WT == WT_BF16 || WT == WT_FP8) {
     // Operands go from global memory straight into LDS: one global_load_lds_dwordx4 of a wave writes
     // a whole 1 KB fragment (lane l's 16 bytes at l * 16), so no register carries them and no LDS
-    // store is issued. Chunk c goes to buffer c % NBUF and D = NBUF - 1 chunks are in flight; a
+    // store is issued; an E4M3 weight fragment (512 bytes) takes two dword loads (bytes l * 4 and
+    // 256 + l * 4). Chunk c goes to buffer c % NBUF and D = NBUF - 1 chunks are in flight; a
     // wave waits for its own loads of a chunk (vmcnt), and the barrier after that makes every
-    // wave's loads of it visible. Fragments of the next chunk are read into registers while the
-    // MFMAs of the current one run, as in the register-staged form below.
-    constexpr int NB_ = C::NBUF, D = NB_ - 1, LPC = C::LOADS;
+    // wave's loads of it visible. Fragments of the next chunk are read from LDS into registers while
+    // the MFMAs of the current one run (the LDS reads hide under the MFMAs).
+    constexpr int AL = WT == WT_FP8 ? 2 : 1;  // loads per weight fragment
+    // (E4M3 chunks are smaller than the bf16 ones the stage is sized for; filling it with more of them
+    // measured the same on the prefill)
+    constexpr int NB_ = C::NBUF, D = NB_ - 1, LPC = AL * LW + LX;
+    static_assert((D - 1) * LPC < 64 && (size_t)NB_ * CHUNKB <= C::STAGE, "chunk buffers");
     const char* wb = (const char*)a.w;
     const char* xb = (const char*)a.x;
     auto dma = [&](int c) __attribute__((always_inline)) {
-      char* dst = stage + (size_t)(c % NB_) * C::CHUNK;
+      char* dst = stage + (size_t)(c % NB_) * CHUNKB;
 #pragma unroll
       for (int i = 0; i < LW; ++i) {
         const int f = wave + GW * i;
-        const char* src = wb + (((size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK) * 64 + lane) * 16;
-        __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + (size_t)f * 1024),
-                                         16, 0, 0);
+        const size_t frag = (size_t)(ct0 + f / C::CK) * KB + c * C::CK + f % C::CK;
+        if constexpr (WT == WT_FP8) {
+          const char* src = wb + frag * 512 + lane * 4;
+          __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + (size_t)f * 512),
+                                           4, 0, 0);
+          __builtin_amdgcn_global_load_lds((const void*)(src + 256),
+                                           (__attribute__((address_space(3))) void*)(dst + (size_t)f * 512 + 256), 4, 0, 0);
+        } else {
+          const char* src = wb + (frag * 64 + lane) * 16;
+          __builtin_amdgcn_global_load_lds((const void*)src, (__attribute__((address_space(3))) void*)(dst + (size_t)f * 1024),
+                                           16, 0, 0);
+        }
       }
 #pragma unroll
       for (int i = 0; i < LX; ++i) {
         const int f = wave + GW * i;
         const char* src = xb + (((size_t)(c * C::CK + f / C::MT) * ntt + min(tt0 + f % C::MT, ntt - 1)) * 64 + lane) * 16;
         __builtin_amdgcn_global_load_lds((const void*)src,
-                                         (__attribute__((address_space(3))) void*)(dst + (size_t)(C::NA + f) * 1024), 16, 0, 0);
+                                         (__attribute__((address_space(3))) void*)(dst + (size_t)C::NA * AFB + (size_t)f * 1024),
+                                         16, 0, 0);
       }
     };
     // issue chunk `last` (when it exists) and wait until chunk last - D + 1 has landed everywhere: D - 1
@@ -1157,42 +1148,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
       dstep(c + 1, ga_d, gb_d, fa_d, fb_d);
     }
     if (c < nc) dstep(c, fa_d, fb_d, ga_d, gb_d);
-  } else {
-  gload(w0, x0, 0);
-  gload(w1, x1, min(1, nc - 1));
-  rms_partial();
-  bf16x8 fa[4], fb[4], ga[4], gb[4];  // fragments of two chunks: the one in the MFMAs, the next
-  lstore(w0, x0, 0);
-  gload(w0, x0, min(2, nc - 1));
-  __syncthreads();
-  rms_final();
-  rd(fa, fb, 0);
-  lstore(w1, x1, 1);
-  gload(w1, x1, min(3, nc - 1));
-  __syncthreads();
-  // step c: the fragments of chunk c are in registers, LDS buffer (c + 1) % 2 holds chunk c + 1
-  // and register set c % 2 holds chunk c + 2 (the other set: chunk c + 3). The MFMAs of chunk c
-  // run while this wave reads chunk c + 1's fragments and stores chunk c + 2 into buffer c % 2
-  // (chunk c's fragments left it before the previous barrier); that set then takes chunk c + 4
-  // (a third set measured no faster). One barrier a step, and the MFMA unit never waits on the
-  // step's own LDS reads. Chunk indices are clamped (what lands past the end is never read).
-  auto step = [&](int c, const bf16x8 (&fc)[4], const bf16x8 (&gc)[4], bf16x8 (&fn)[4], bf16x8 (&gn)[4],
-                  WR (&ws)[LW], i32x4 (&xs)[LX]) __attribute__((always_inline)) {
-    rd(fn, gn, (c + 1) & 1);
-    mm(fc, gc);
-    lstore(ws, xs, c & 1);
-    gload(ws, xs, min(c + 4, nc - 1));
-    __syncthreads();
-  };
-  int c = 0;
-  {
-    for (; c + 2 <= nc; c += 2) {
-      step(c, fa, fb, ga, gb, w0, x0);
-      step(c + 1, ga, gb, fa, fb, w1, x1);
-    }
-    if (c < nc) step(c, fa, fb, ga, gb, w0, x0);
-  }
-
   }
 
   asm volatile("" ::"v"(tch[0] ^ tch[1] ^ tch[2] ^ tch[3]));  // the touches, long since in
