@@ -1219,10 +1219,13 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(1, 2))) voi
         const int q = wk + WK * (u0 + u), i = q >> 2, j = q & 3;
         const int tok = tt0 * 16 + (wm * 4 + j) * 16 + tq;
         const int n = (ct0 + wn * 4 + i) * 16 + cq * 4;
+        // time-modulated expert: the next gain and this sublayer's residual gate of the row's sequence
+        const size_t msq = a.mod_rows ? (size_t)(min(tok, a.M - 1) / a.mod_rows) : 0;
         hv[u] = *(const float4*)(a.h + (size_t)min(tok, a.M - 1) * a.N + n);
-        gv[u] = *(const float4*)(a.gain_next + n);
+        gv[u] = *(const float4*)(a.gain_next + msq * a.ms_gain + n);
         val[u] = tile_sum(i, j);
         if constexpr (WT == WT_FP8) val[u] *= *(const f32x4*)(a.wscale + n);  // per-channel scales
+        if (a.res_gate) val[u] *= *(const f32x4*)(a.res_gate + msq * a.ms_gate + n);
       }
 #pragma unroll
       for (int u = 0; u < GRP; ++u) {

@@ -540,8 +540,6 @@ int tiled_shape(const ae_handle* h, int role, int n_tiles, int K, int M, int Mp,
   if (role == R_OUT_PROJ || !((h->tiled_roles >> role) & 1) || Mp / TOKG < 2 || h->n_cu <= 0) return -1;
   const int wt = (role == R_GATE_UP || role == R_DOWN) ? h->mt : h->wt;
   if (h->at != AT_BF16 || (wt != WT_BF16 && !(wt == WT_FP8 && (role == R_GATE_UP || role == R_DOWN)))) return -1;
-  // its residual epilogue has no per-row gates: o_proj and down of a time-modulated expert stay on the 64-token kernel
-  if (h->c.time_mode && (role == R_O_PROJ || role == R_DOWN)) return -1;
   if ((role == R_QKV_ROPE || role == R_GATE_UP) && h->c.width / 16 > TILED_MAX_GIN) return -1;
   const int tok_tiles = (M + 15) / 16;
   int best = -1;
